@@ -1,0 +1,137 @@
+"""CPU oracle for the GQA decode attention-times-V contraction (test infrastructure).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package. The product package
+``gqa_reuse_attn_amd`` never imports it, and the two share no code.
+
+``gqa_av_oracle.c`` holds the definition (ExecuTorch PR #21063, "...GEMV",
+introduction, with a batch index added): fp64 sums over context positions c of
+exact fp32 x V products, kv_h = floor(q_h / G). ``brute.py`` holds a
+pure-Python correctly rounded version for tiny shapes. Every function here is
+pinned by ``tests/test_oracle_pins.py``; none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_HERE, "gqa_av_oracle.c")
+LIB = os.path.join(_HERE, "libgqa_av_oracle.so")
+
+DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
+
+# Plain, portable flags: no -march (the library may run on another host),
+# no contraction or reassociation of the fp64 sum.
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+          "-fno-fast-math", "-Wall", "-Wextra"]
+
+
+def build(src: str = SRC, out: str = LIB, extra_flags: Optional[list] = None) -> str:
+    """Compile the oracle with gcc into a shared library; returns its path."""
+    cmd = ["gcc", *CFLAGS, *(extra_flags or []), "-o", out, src, "-lm", "-lpthread"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+class Oracle:
+    """ctypes view of one compiled oracle library (the real one or a test mutant)."""
+
+    def __init__(self, path: str = LIB):
+        if not os.path.exists(path):
+            raise FileNotFoundError(f"oracle library {path} is not built; call oracle.build()")
+        self.path = path
+        lib = ctypes.CDLL(path)
+        i64, vp, ip = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        lib.gqa_av_oracle.argtypes = [vp, vp, ip, i64, i64, i64, i64, i64, vp, ip]
+        lib.gqa_av_oracle.restype = ip
+        lib.gqa_av_oracle_points.argtypes = [vp, vp, ip, i64, i64, i64, i64, i64, vp, i64, vp, ip]
+        lib.gqa_av_oracle_points.restype = ip
+        lib.gqa_av_oracle_decode.argtypes = [vp, ip, i64, vp]
+        lib.gqa_av_oracle_decode.restype = ip
+        self.lib = lib
+
+    @staticmethod
+    def _np_inputs(attn, V, v_dtype: str):
+        a = _as_numpy(attn, np.float32)
+        if v_dtype == "f32":
+            v = _as_numpy(V, np.float32)
+        else:
+            v = _as_numpy(V, np.uint16)
+        return np.ascontiguousarray(a), np.ascontiguousarray(v)
+
+    def full(self, attn, V, v_dtype: str, nthreads: int = 0) -> np.ndarray:
+        """out[B, Hq, D] (float64) for attn [B,C,Hq] fp32 and V [B,C,Hkv,D]."""
+        a, v = self._np_inputs(attn, V, v_dtype)
+        B, C, Hq = a.shape
+        _, C2, Hkv, D = v.shape
+        assert C2 == C and v.shape[0] == B
+        out = np.empty((B, Hq, D), dtype=np.float64)
+        rc = self.lib.gqa_av_oracle(a.ctypes.data, v.ctypes.data, DTYPE_CODE[v_dtype],
+                                    B, C, Hq, Hkv, D, out.ctypes.data, nthreads)
+        if rc != 0:
+            raise ValueError(f"oracle rejected the arguments (status {rc})")
+        return out
+
+    def points(self, attn, V, v_dtype: str, idx: np.ndarray, nthreads: int = 0) -> np.ndarray:
+        """Selected elements out[b, q, d] for idx rows (b, q, d)."""
+        a, v = self._np_inputs(attn, V, v_dtype)
+        B, C, Hq = a.shape
+        _, _, Hkv, D = v.shape
+        idx = np.ascontiguousarray(idx, dtype=np.int64)
+        out = np.empty(idx.shape[0], dtype=np.float64)
+        rc = self.lib.gqa_av_oracle_points(a.ctypes.data, v.ctypes.data, DTYPE_CODE[v_dtype],
+                                           B, C, Hq, Hkv, D, idx.ctypes.data, idx.shape[0],
+                                           out.ctypes.data, nthreads)
+        if rc != 0:
+            raise ValueError(f"oracle rejected the arguments (status {rc})")
+        return out
+
+    def decode(self, raw: np.ndarray, v_dtype: str) -> np.ndarray:
+        """Widen raw V elements (uint16 bits or float32) to float64."""
+        raw = np.ascontiguousarray(raw)
+        out = np.empty(raw.size, dtype=np.float64)
+        rc = self.lib.gqa_av_oracle_decode(raw.ctypes.data, DTYPE_CODE[v_dtype], raw.size,
+                                           out.ctypes.data)
+        if rc != 0:
+            raise ValueError("bad dtype")
+        return out.reshape(raw.shape)
+
+
+def _as_numpy(x, np_dtype):
+    """torch CPU tensor or numpy array -> numpy array of the given bit type."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu().contiguous()
+            if np_dtype == np.uint16 and x.dtype in (torch.float16, torch.bfloat16):
+                return x.view(torch.int16).numpy().view(np.uint16)
+            if np_dtype == np.float32:
+                assert x.dtype == torch.float32, x.dtype
+            return x.numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    x = np.asarray(x)
+    if np_dtype == np.uint16 and x.dtype == np.float16:
+        return x.view(np.uint16)
+    return x
+
+
+_DEFAULT: Optional[Oracle] = None
+
+
+def get(build_if_missing: bool = True) -> Oracle:
+    """The compiled oracle (built on first use when missing or older than its source)."""
+    global _DEFAULT
+    if _DEFAULT is None:
+        stale = (not os.path.exists(LIB)) or os.path.getmtime(LIB) < os.path.getmtime(SRC)
+        if stale:
+            if not build_if_missing:
+                raise FileNotFoundError(LIB)
+            build()
+        _DEFAULT = Oracle(LIB)
+    return _DEFAULT

@@ -1,0 +1,177 @@
+/*
+ * CPU oracle for the GQA decode attention-times-V contraction.
+ *
+ * TEST INFRASTRUCTURE. Only tests/, __graft_entry__.smoke() and the
+ * cpu_baseline leg of bench.py may load or call this library. The product
+ * path (gqa_reuse_attn_amd/) never links, imports or executes it, and it
+ * shares no code, header or table with the HIP kernels.
+ *
+ * What it computes -- ExecuTorch PR #21063, "...GEMV" (GQA-reuse AV coop GEMV
+ * for the Vulkan backend), introduction: query heads come in groups of
+ * G = Hq / Hkv that share one KV head, and each output element is the sum
+ * over context positions c of attn[c, q_h] * V[c, kv_h, d]. A batch index b
+ * of independent sequences is added in front of every tensor:
+ *
+ *   out[b, q_h, d] = sum_{c=0}^{C-1} attn[b, c, q_h] * V[b, c, kv_h(q_h), d]
+ *   kv_h(q_h)      = floor(q_h / G)      (contiguous groups of G heads)
+ *
+ * The page never states which KV head a query head reads. Contiguous groups
+ * are taken: the page has G query heads sharing one KV head and one workgroup
+ * per KV head producing that group's G outputs, and consecutive query heads
+ * are the plain grouping for that.
+ *
+ * How: every input element is widened exactly to double with decoders written
+ * here from the IEEE-754 binary16 and bfloat16 bit layouts; each product of a
+ * float32 weight and a V value is exact in double (at most 24 x 24 significand
+ * bits); the products are added in double in increasing c. The only rounding
+ * is that summation, bounded by gamma_{C-1} * sum_c |attn * V|.
+ *
+ * Layouts are dense row-major: attn [B][C][Hq] float32, V [B][C][Hkv][D] of
+ * the given dtype, out [B][Hq][D] double.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2 };
+enum { ORC_OK = 0, ORC_BAD_ARG = 1 };
+
+/* bfloat16 is the upper half of an IEEE binary32: shift into place. */
+static double orc_bf16(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+static double orc_f16(uint16_t h)
+{
+    const int sign = (h >> 15) & 1;
+    const int e = (h >> 10) & 0x1f;
+    const int m = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);               /* subnormal: m * 2^(1-15-10) */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(m + 1024), e - 25);   /* (1 + m/2^10) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+static double orc_f32(const float *p)
+{
+    return (double)*p;
+}
+
+static double orc_load(const void *V, int dtype, int64_t i)
+{
+    switch (dtype) {
+    case ORC_F32: return orc_f32((const float *)V + i);
+    case ORC_F16: return orc_f16(((const uint16_t *)V)[i]);
+    default:      return orc_bf16(((const uint16_t *)V)[i]);
+    }
+}
+
+static int orc_check(int dtype, int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D)
+{
+    if (dtype != ORC_F32 && dtype != ORC_F16 && dtype != ORC_BF16) return ORC_BAD_ARG;
+    if (B < 0 || C < 0 || Hq < 1 || Hkv < 1 || D < 1) return ORC_BAD_ARG;
+    if (Hq % Hkv != 0) return ORC_BAD_ARG;
+    return ORC_OK;
+}
+
+/* Widen n elements of V to double (exposed so tests can pin the decoders). */
+int gqa_av_oracle_decode(const void *V, int dtype, int64_t n, double *out)
+{
+    if (dtype != ORC_F32 && dtype != ORC_F16 && dtype != ORC_BF16) return ORC_BAD_ARG;
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_load(V, dtype, i);
+    return ORC_OK;
+}
+
+/* All 65536 binary16 values, filled once from orc_f16 (a speed-up only). */
+static double orc_f16_table[65536];
+static pthread_once_t orc_f16_once = PTHREAD_ONCE_INIT;
+static void orc_f16_fill(void)
+{
+    for (uint32_t h = 0; h < 65536u; ++h) orc_f16_table[h] = orc_f16((uint16_t)h);
+}
+
+/* One output row out[b, q, 0:D]: the definition, summed in increasing c. */
+static void orc_row(const float *attn, const void *V, int dtype,
+                    int64_t C, int64_t Hq, int64_t Hkv, int64_t D,
+                    int64_t b, int64_t q, double *acc)
+{
+    const int64_t G = Hq / Hkv;
+    const int64_t kv = q / G;
+    for (int64_t d = 0; d < D; ++d) acc[d] = 0.0;
+    for (int64_t c = 0; c < C; ++c) {
+        const double a = (double)attn[(b * C + c) * Hq + q];
+        const int64_t row = ((b * C + c) * Hkv + kv) * D;
+        if (dtype == ORC_F32) {
+            const float *r = (const float *)V + row;
+            for (int64_t d = 0; d < D; ++d) acc[d] += a * orc_f32(r + d);
+        } else if (dtype == ORC_F16) {
+            const uint16_t *r = (const uint16_t *)V + row;
+            for (int64_t d = 0; d < D; ++d) acc[d] += a * orc_f16_table[r[d]];
+        } else {
+            const uint16_t *r = (const uint16_t *)V + row;
+            for (int64_t d = 0; d < D; ++d) acc[d] += a * orc_bf16(r[d]);
+        }
+    }
+}
+
+/* Full output: out[B][Hq][D] in double. nthreads <= 0 uses the OpenMP default. */
+int gqa_av_oracle(const float *attn, const void *V, int dtype,
+                  int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D,
+                  double *out, int nthreads)
+{
+    int rc = orc_check(dtype, B, C, Hq, Hkv, D);
+    if (rc != ORC_OK) return rc;
+    pthread_once(&orc_f16_once, orc_f16_fill);
+    const int64_t rows = B * Hq;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int64_t i = 0; i < rows; ++i)
+        orc_row(attn, V, dtype, C, Hq, Hkv, D, i / Hq, i % Hq, out + i * D);
+    (void)nthreads;
+    return ORC_OK;
+}
+
+/* Selected outputs: idx holds npts triples (b, q_h, d); out[k] is that element. */
+int gqa_av_oracle_points(const float *attn, const void *V, int dtype,
+                         int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D,
+                         const int64_t *idx, int64_t npts, double *out, int nthreads)
+{
+    int rc = orc_check(dtype, B, C, Hq, Hkv, D);
+    if (rc != ORC_OK) return rc;
+    for (int64_t k = 0; k < npts; ++k) {
+        const int64_t b = idx[3 * k], q = idx[3 * k + 1], d = idx[3 * k + 2];
+        if (b < 0 || b >= B || q < 0 || q >= Hq || d < 0 || d >= D) return ORC_BAD_ARG;
+    }
+    const int64_t G = Hq / Hkv;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 16) num_threads(nthreads)
+#endif
+    for (int64_t k = 0; k < npts; ++k) {
+        const int64_t b = idx[3 * k], q = idx[3 * k + 1], d = idx[3 * k + 2];
+        const int64_t kv = q / G;
+        double acc = 0.0;
+        for (int64_t c = 0; c < C; ++c)
+            acc += (double)attn[(b * C + c) * Hq + q] *
+                   orc_load(V, dtype, ((b * C + c) * Hkv + kv) * D + d);
+        out[k] = acc;
+    }
+    (void)nthreads;
+    return ORC_OK;
+}

@@ -1,0 +1,220 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each pin is a plain function taking an ``oracle.Oracle`` and raising
+AssertionError when the oracle disagrees. ``test_oracle_pins.py`` runs them on
+the real oracle and on deliberately broken copies of its source, which must
+each fail at least one pin.
+
+What pins what:
+  * decode_table      IEEE-754 binary16 / bfloat16 bit patterns with closed-form
+                      values, and every 16-bit pattern against torch's own
+                      conversion (an independent library routine).
+  * brute_force       tiny shapes, all dtypes, against the correctly rounded
+                      exact sum (oracle/brute.py), within the oracle's a-priori
+                      bound gamma_{C-1} * sum|a*v| + one rounding.
+  * mha_einsum        G = 1 equals numpy's einsum 'bch,bchd->bhd' in fp64.
+  * repeat_mha        GQA equals MHA over V repeated G times along the head
+                      axis: pins kv_h = floor(q_h / G).
+  * constant_v        V constant along c gives u * sum_c attn; with softmax
+                      weights (columns summing to 1) that is u itself.
+  * one_hot           one-hot weights return that V row exactly.
+  * linearity, permutation, batch independence: algebraic properties.
+  * points            the sampled entry point equals brute force.
+  * edges             C = 0 gives zeros; B = 0 gives an empty result;
+                      Hq % Hkv != 0 is rejected.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from oracle.brute import abs_sum, brute_force
+from workloads import make_random
+
+U64 = 2.0 ** -53
+
+
+def gamma(n: int) -> float:
+    nu = n * U64
+    return nu / (1.0 - nu)
+
+
+def _within_bound(o: np.ndarray, exact: np.ndarray, scale: np.ndarray, C: int, what: str):
+    bound = gamma(max(C - 1, 0)) * scale + U64 * np.abs(exact) + 1e-300
+    err = np.abs(o - exact)
+    bad = err > bound
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements outside the bound, worst {float((err - bound).max()):.3e}"
+
+
+def _tiny_cases():
+    return [
+        # B, C, Hq, Hkv, D, dtype, attn kind
+        (1, 1, 1, 1, 1, "f32", "signed"),
+        (2, 17, 6, 2, 5, "f32", "signed"),
+        (2, 13, 5, 1, 8, "bf16", "signed"),
+        (1, 9, 6, 3, 7, "f16", "signed"),
+        (2, 11, 4, 4, 3, "bf16", "softmax"),
+        (1, 16, 10, 2, 4, "f16", "softmax"),
+    ]
+
+
+def pin_decode_table(orc):
+    f16_known = {
+        0x0000: 0.0, 0x3C00: 1.0, 0xC000: -2.0, 0x7BFF: 65504.0, 0x0400: 2.0 ** -14,
+        0x0001: 2.0 ** -24, 0x03FF: 1023 * 2.0 ** -24, 0x3555: (1 + 0x155 / 1024) * 0.25,
+        0x8001: -(2.0 ** -24), 0x7C00: math.inf, 0xFC00: -math.inf,
+    }
+    bf16_known = {
+        0x0000: 0.0, 0x3F80: 1.0, 0xC000: -2.0, 0x0080: 2.0 ** -126, 0x0001: 2.0 ** -133,
+        0x3EAB: (1 + 0x2B / 128) * 0.25, 0x7F7F: (2 - 2.0 ** -7) * 2.0 ** 127,
+        0x8080: -(2.0 ** -126), 0x7F80: math.inf, 0xFF80: -math.inf,
+    }
+    for dt, known in (("f16", f16_known), ("bf16", bf16_known)):
+        bits = np.array(list(known.keys()), dtype=np.uint16)
+        got = orc.decode(bits, dt)
+        for b, g in zip(bits.tolist(), got.tolist()):
+            assert g == known[b], f"{dt} 0x{b:04x}: {g!r} != {known[b]!r}"
+    nan_f16 = orc.decode(np.array([0x7E00, 0xFE01], np.uint16), "f16")
+    nan_bf16 = orc.decode(np.array([0x7FC0, 0xFF81], np.uint16), "bf16")
+    assert np.isnan(nan_f16).all() and np.isnan(nan_bf16).all()
+    # every 16-bit pattern against torch's conversion
+    allbits = np.arange(65536, dtype=np.uint16)
+    t = torch.from_numpy(allbits.view(np.int16).copy())
+    for dt, tdt in (("f16", torch.float16), ("bf16", torch.bfloat16)):
+        ref = t.view(tdt).to(torch.float64).numpy()
+        got = orc.decode(allbits, dt)
+        same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+        assert same.all(), f"{dt}: {int((~same).sum())} patterns decode differently from torch"
+        # signed zero
+        assert np.array_equal(np.signbit(got[~np.isnan(got)]), np.signbit(ref[~np.isnan(ref)]))
+    f = np.array([1.5, -0.0, 3.4e38, 1e-45, -7.25], dtype=np.float32)
+    assert np.array_equal(orc.decode(f, "f32"), f.astype(np.float64))
+
+
+def pin_brute_force(orc):
+    for i, (B, C, Hq, Hkv, D, dt, kind) in enumerate(_tiny_cases()):
+        attn, V = make_random(B, C, Hq, Hkv, D, dt, seed=100 + i, attn_kind=kind)
+        exact = brute_force(attn, V)
+        o = orc.full(attn, V, dt)
+        _within_bound(o, exact, abs_sum(attn, V), C, f"brute {B,C,Hq,Hkv,D,dt}")
+
+
+def pin_mha_einsum(orc):
+    for dt in ("f32", "bf16", "f16"):
+        attn, V = make_random(2, 37, 3, 3, 6, dt, seed=7, attn_kind="signed")
+        ref = np.einsum("bch,bchd->bhd", attn.double().numpy(), V.double().numpy())
+        o = orc.full(attn, V, dt)
+        _within_bound(o, ref, abs_sum(attn, V), 2 * 37, f"einsum {dt}")
+
+
+def pin_repeat_mha(orc):
+    for dt, (Hq, Hkv) in (("bf16", (8, 2)), ("f16", (6, 3)), ("f32", (5, 1))):
+        attn, V = make_random(2, 23, Hq, Hkv, 4, dt, seed=11, attn_kind="signed")
+        G = Hq // Hkv
+        Vrep = V.repeat_interleave(G, dim=2).contiguous()
+        a = orc.full(attn, V, dt)
+        b = orc.full(attn, Vrep, dt)
+        assert np.array_equal(a, b), f"GQA != MHA over repeated V ({dt}, G={G})"
+        # and the repeated form agrees with the textbook einsum
+        ref = np.einsum("bch,bchd->bhd", attn.double().numpy(), Vrep.double().numpy())
+        _within_bound(a, ref, abs_sum(attn, V), 2 * 23, f"repeat-einsum {dt}")
+
+
+def pin_constant_v(orc):
+    B, C, Hq, Hkv, D = 2, 300, 6, 2, 5
+    g = torch.Generator().manual_seed(5)
+    u = torch.randn(B, 1, Hkv, D, generator=g).to(torch.bfloat16)
+    V = u.expand(B, C, Hkv, D).contiguous()
+    logits = torch.randn(B, C, Hq, generator=g, dtype=torch.float64)
+    attn = torch.softmax(logits, dim=1).to(torch.float32)
+    o = orc.full(attn, V, "bf16")
+    G = Hq // Hkv
+    ud = u.double().numpy()[:, 0]                             # [B, Hkv, D]
+    colsum = np.array([[math.fsum(attn[b, :, q].double().tolist()) for q in range(Hq)] for b in range(B)])
+    expect = colsum[:, :, None] * np.repeat(ud, G, axis=1)
+    _within_bound(o, expect, np.abs(expect), C, "constant V")
+    # columns sum to one up to fp32 rounding of the weights: out ~ u
+    assert np.allclose(o, np.repeat(ud, G, axis=1), rtol=C * 2.0 ** -23, atol=0.0), "constant V, unit columns"
+
+
+def pin_one_hot(orc):
+    B, C, Hq, Hkv, D = 3, 41, 8, 4, 6
+    for dt in ("f32", "f16", "bf16"):
+        _, V = make_random(B, C, Hq, Hkv, D, dt, seed=3)
+        attn = torch.zeros(B, C, Hq)
+        G = Hq // Hkv
+        picks = {}
+        for b in range(B):
+            for q in range(Hq):
+                c = (7 * b + 5 * q + 1) % C
+                attn[b, c, q] = 1.0
+                picks[b, q] = c
+        o = orc.full(attn, V, dt)
+        Vd = V.double().numpy()
+        for (b, q), c in picks.items():
+            assert np.array_equal(o[b, q], Vd[b, c, q // G]), f"one-hot {dt} b={b} q={q}"
+
+
+def pin_linearity(orc):
+    B, C, Hq, Hkv, D = 2, 40, 6, 3, 4
+    attn, V = make_random(B, C, Hq, Hkv, D, "bf16", seed=21, attn_kind="signed")
+    a1 = attn.clone(); a1[:, C // 2:] = 0
+    a2 = attn.clone(); a2[:, :C // 2] = 0
+    o = orc.full(attn, V, "bf16")
+    o12 = orc.full(a1, V, "bf16") + orc.full(a2, V, "bf16")
+    _within_bound(o, o12, 2 * abs_sum(attn, V), C, "linearity")
+    o2 = orc.full(attn * 2.0, V, "bf16")
+    assert np.array_equal(o2, 2.0 * o), "scaling by 2"
+
+
+def pin_permutation(orc):
+    B, C, Hq, Hkv, D = 2, 33, 4, 2, 5
+    attn, V = make_random(B, C, Hq, Hkv, D, "f16", seed=31, attn_kind="signed")
+    perm = torch.randperm(C, generator=torch.Generator().manual_seed(1))
+    o = orc.full(attn, V, "f16")
+    op = orc.full(attn[:, perm].contiguous(), V[:, perm].contiguous(), "f16")
+    _within_bound(op, o, 2 * abs_sum(attn, V), C, "permutation")
+
+
+def pin_batch_independence(orc):
+    B, C, Hq, Hkv, D = 3, 19, 6, 2, 4
+    attn, V = make_random(B, C, Hq, Hkv, D, "bf16", seed=41, attn_kind="signed")
+    o = orc.full(attn, V, "bf16")
+    for b in range(B):
+        ob = orc.full(attn[b:b + 1].contiguous(), V[b:b + 1].contiguous(), "bf16")
+        assert np.array_equal(o[b:b + 1], ob), f"batch {b} depends on other batches"
+
+
+def pin_points(orc):
+    B, C, Hq, Hkv, D = 2, 21, 6, 3, 5
+    for dt in ("f32", "f16", "bf16"):
+        attn, V = make_random(B, C, Hq, Hkv, D, dt, seed=51, attn_kind="signed")
+        exact = brute_force(attn, V)
+        rng = np.random.default_rng(0)
+        idx = np.stack([rng.integers(0, B, 40), rng.integers(0, Hq, 40), rng.integers(0, D, 40)], 1)
+        p = orc.points(attn, V, dt, idx)
+        e = exact[idx[:, 0], idx[:, 1], idx[:, 2]]
+        s = abs_sum(attn, V)[idx[:, 0], idx[:, 1], idx[:, 2]]
+        _within_bound(p, e, s, C, f"points {dt}")
+
+
+def pin_edges(orc):
+    attn = torch.zeros(2, 0, 4)
+    V = torch.zeros(2, 0, 2, 3, dtype=torch.bfloat16)
+    o = orc.full(attn, V, "bf16")
+    assert o.shape == (2, 4, 3) and not o.any(), "C = 0 must give zeros"
+    o = orc.full(torch.zeros(0, 5, 4), torch.zeros(0, 5, 2, 3), "f32")
+    assert o.shape == (0, 4, 3)
+    try:
+        orc.full(torch.zeros(1, 2, 5), torch.zeros(1, 2, 2, 3), "f32")
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("Hq % Hkv != 0 must be rejected")
+
+
+ALL_PINS = [pin_decode_table, pin_brute_force, pin_mha_einsum, pin_repeat_mha, pin_constant_v,
+            pin_one_hot, pin_linearity, pin_permutation, pin_batch_independence, pin_points,
+            pin_edges]

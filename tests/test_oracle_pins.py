@@ -1,0 +1,102 @@
+"""CPU tests: the oracle against its pins, and planted mistakes that the pins catch.
+
+A planted mistake is a textual edit of the oracle's C source, compiled into a
+temporary library. Each one is a plausible slip (wrong head mapping, a dropped
+row, a wrong decoder constant, a sign, a transposed or batch-less index) and
+must fail at least one pin; the pins are useless otherwise.
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests import oracle_pins
+from tests.parity import gate
+from workloads import WORKLOADS, make_inputs
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin, oracle_lib):
+    pin(oracle_lib)
+
+
+# (name, original text, planted text) -- every original must occur in the source.
+PLANTS = [
+    ("kv_mod_mapping", "const int64_t kv = q / G;", "const int64_t kv = q % Hkv;"),
+    ("drop_last_row", "for (int64_t c = 0; c < C; ++c) {", "for (int64_t c = 0; c < C - 1; ++c) {"),
+    ("bf16_shift", "uint32_t u = (uint32_t)h << 16;", "uint32_t u = (uint32_t)h << 15;"),
+    ("f16_subnormal_scale", "v = ldexp((double)m, -24);", "v = ldexp((double)m, -25);"),
+    ("f16_bias", "v = ldexp((double)(m + 1024), e - 25);", "v = ldexp((double)(m + 1024), e - 24);"),
+    ("f16_no_sign", "return sign ? -v : v;", "return v;"),
+    ("sign_flip", "acc[d] += a * orc_bf16(r[d]);", "acc[d] -= a * orc_bf16(r[d]);"),
+    ("attn_transposed", "const double a = (double)attn[(b * C + c) * Hq + q];",
+     "const double a = (double)attn[(b * Hq + q) * C + c];"),
+    ("v_ignores_batch", "const int64_t row = ((b * C + c) * Hkv + kv) * D;",
+     "const int64_t row = ((0 * C + c) * Hkv + kv) * D;"),
+    ("f32_as_float_sum", "for (int64_t d = 0; d < D; ++d) acc[d] += a * orc_f32(r + d);",
+     "for (int64_t d = 0; d < D; ++d) acc[d] += (float)(a * orc_f32(r + d));"),
+    ("points_wrong_head", "const int64_t kv = q / G;\n        double acc = 0.0;",
+     "const int64_t kv = q / G + (q % G == 1);\n        double acc = 0.0;"),
+]
+
+
+@pytest.mark.parametrize("name,orig,planted", PLANTS, ids=[p[0] for p in PLANTS])
+def test_planted_mistake_is_caught(name, orig, planted, tmp_path):
+    src = open(oracle.SRC).read()
+    assert orig in src, f"plant {name}: pattern no longer in the oracle source"
+    # kv_mod_mapping touches both places the mapping is written
+    mutated = src.replace(orig, planted) if name == "kv_mod_mapping" else src.replace(orig, planted, 1)
+    if name == "points_wrong_head":
+        assert mutated != src
+    p_src = tmp_path / f"{name}.c"
+    p_src.write_text(mutated)
+    lib = oracle.build(str(p_src), str(tmp_path / f"lib{name}.so"))
+    mutant = oracle.Oracle(lib)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(mutant)
+        except (AssertionError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, f"planted mistake {name} passed every pin"
+
+
+def _drop_one_row_per_split(attn: torch.Tensor, nsplit: int) -> torch.Tensor:
+    """Zero the last context row of each of nsplit equal C-splits."""
+    a = attn.clone()
+    C = a.shape[1]
+    step = max(1, -(-C // nsplit))
+    last = [min(s + step, C) - 1 for s in range(0, C, step)]
+    a[:, last, :] = 0.0
+    return a
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("wname", list(WORKLOADS))
+def test_gate_bites_on_dropped_row(wname, oracle_lib):
+    """A result missing one context row per split must fail the acceptance gate.
+
+    Planted in the oracle's input on the CPU. The large-batch workload is cut to
+    8 sequences: the relative error of a dropped row depends on C, not on B.
+    """
+    w = WORKLOADS[wname]
+    if w.B > 8:
+        w = w.replace(B=8)
+    attn, V = make_inputs(w, seed=0)
+    ref = oracle_lib.full(attn, V, w.v_dtype)
+    bad = oracle_lib.full(_drop_one_row_per_split(attn, 1), V, w.v_dtype)
+    ok, msg = gate(bad.astype(np.float32), ref, w.v_dtype)
+    assert not ok, f"{wname}: dropping one row passed the gate ({msg})"
+    ok, msg = gate(ref.astype(np.float32), ref, w.v_dtype)
+    assert ok, f"{wname}: the exact result rounded to fp32 fails the gate ({msg})"
+
+
+def test_oracle_header_declares_test_infrastructure():
+    head = open(oracle.SRC).read(600)
+    assert "TEST INFRASTRUCTURE" in head
+    assert "TEST INFRASTRUCTURE" in open(os.path.join(os.path.dirname(oracle.SRC), "__init__.py")).read() or \
+        "test infrastructure" in open(os.path.join(os.path.dirname(oracle.SRC), "__init__.py")).read()

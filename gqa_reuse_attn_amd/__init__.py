@@ -1,0 +1,231 @@
+"""Python binding of libgqa_av.so: GQA decode attention-times-V on MI355X.
+
+    out[b, q_h, d] = sum_c attn[b, c, q_h] * V[b, c, q_h // G, d],   G = Hq // Hkv
+
+(ExecuTorch PR #21063, "...GEMV", introduction; batch index added.) Every
+step runs in the HIP library; this module only checks tensors and marshals
+pointers, sizes and the stream through ctypes. PyTorch provides device memory
+and streams. There is no CPU fallback: if the library is missing, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Union
+
+__all__ = [
+    "LIB_PATH", "GqaAvError", "Hint", "Plan", "load", "resolve_mode", "make_plan",
+    "gqa_av_decode", "gqa_av_decode_plan", "bind", "BoundCall", "release", "status_string", "MODES", "DTYPES",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_av.so")
+
+MODES = {"auto": -1, "per_head": 0, "reuse": 1}
+ENGINES = {"auto": -1, "valu": 0, "mfma": 1}
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
+STATUS = {0: "OK", 1: "INVALID_ARG", 2: "INELIGIBLE", 3: "UNSUPPORTED", 4: "HIP"}
+
+
+class GqaAvError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        super().__init__(f"gqa_av: {self.name}: {detail}")
+
+
+class Hint(ctypes.Structure):
+    _fields_ = [("engine", ctypes.c_int32), ("nsplit", ctypes.c_int32), ("cu_count", ctypes.c_int32),
+                ("v_align", ctypes.c_int32), ("reserved", ctypes.c_int32 * 4)]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("engine", ctypes.c_int32), ("heads_per_tile", ctypes.c_int32),
+                ("subgroups", ctypes.c_int32), ("vec_bytes", ctypes.c_int32), ("lanes_per_row", ctypes.c_int32),
+                ("row_slots", ctypes.c_int32), ("d_tiles", ctypes.c_int32), ("nsplit", ctypes.c_int32),
+                ("threads", ctypes.c_int32), ("rows_per_split", ctypes.c_int64), ("grid", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_int64), ("v_bytes_read", ctypes.c_int64),
+                ("reserved", ctypes.c_int32 * 4)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+
+    def __repr__(self) -> str:
+        return f"Plan({self.as_dict()})"
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m gqa_reuse_attn_amd.build` "
+                           "(or __graft_entry__.build()); there is no CPU fallback")
+    lib = ctypes.CDLL(path)
+    i64, i32, vp, ip = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int
+    lib.gqa_av_resolve_mode.argtypes = [i64, i64, ip]
+    lib.gqa_av_resolve_mode.restype = ip
+    lib.gqa_av_make_plan.argtypes = [i64, i64, i64, i64, i64, ip, ip, ctypes.POINTER(Hint), ctypes.POINTER(Plan)]
+    lib.gqa_av_make_plan.restype = ip
+    lib.gqa_av_decode.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ip, ip, vp]
+    lib.gqa_av_decode.restype = ip
+    lib.gqa_av_decode_plan.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ip, ctypes.POINTER(Plan), vp]
+    lib.gqa_av_decode_plan.restype = ip
+    lib.gqa_av_status_string.argtypes = [ip]
+    lib.gqa_av_status_string.restype = ctypes.c_char_p
+    lib.gqa_av_last_error.argtypes = []
+    lib.gqa_av_last_error.restype = ctypes.c_char_p
+    lib.gqa_av_release.argtypes = []
+    lib.gqa_av_release.restype = ip
+    del i32
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().gqa_av_status_string(status).decode()
+
+
+def _raise(status: int):
+    detail = load().gqa_av_last_error().decode()
+    raise GqaAvError(status, detail or status_string(status))
+
+
+def _mode(mode: Union[str, int]) -> int:
+    if isinstance(mode, str):
+        if mode not in MODES:
+            raise ValueError(f"mode must be one of {sorted(MODES)}, got {mode!r}")
+        return MODES[mode]
+    return int(mode)
+
+
+def resolve_mode(Hq: int, Hkv: int, mode: Union[str, int] = "auto") -> str:
+    """'reuse' or 'per_head' for this head shape (host only, no GPU needed)."""
+    r = load().gqa_av_resolve_mode(Hq, Hkv, _mode(mode))
+    if r < 0:
+        _raise(-r)
+    return "reuse" if r == 1 else "per_head"
+
+
+def make_plan(B: int, C: int, Hq: int, Hkv: int, D: int, v_dtype: str, mode: Union[str, int] = "auto",
+              engine: Union[str, int] = "auto", nsplit: int = 0, cu_count: int = 0, v_align: int = 0) -> Plan:
+    """Host-only planning (no GPU needed). nsplit/cu_count/v_align <= 0 mean automatic."""
+    h = Hint()
+    h.engine = ENGINES[engine] if isinstance(engine, str) else int(engine)
+    h.nsplit, h.cu_count, h.v_align = int(nsplit), int(cu_count), int(v_align)
+    p = Plan()
+    rc = load().gqa_av_make_plan(B, C, Hq, Hkv, D, DTYPES[v_dtype], _mode(mode), ctypes.byref(h), ctypes.byref(p))
+    if rc != 0:
+        _raise(rc)
+    return p
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _check(attn, V, out):
+    torch = _torch()
+    vmap = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
+    if attn.dim() != 3 or V.dim() != 4:
+        raise ValueError(f"attn must be [B,C,Hq] and V [B,C,Hkv,D]; got {tuple(attn.shape)} and {tuple(V.shape)}")
+    B, C, Hq = attn.shape
+    if V.shape[0] != B or V.shape[1] != C:
+        raise ValueError(f"V {tuple(V.shape)} does not match attn {tuple(attn.shape)} in B or C")
+    Hkv, D = V.shape[2], V.shape[3]
+    if attn.dtype != torch.float32:
+        raise TypeError(f"attn must be float32, got {attn.dtype}")
+    if V.dtype not in vmap:
+        raise TypeError(f"V must be float32, float16 or bfloat16, got {V.dtype}")
+    if not (attn.is_cuda and V.is_cuda):
+        raise ValueError("attn and V must be GPU tensors")
+    if attn.device != V.device:
+        raise ValueError("attn and V must be on the same device")
+    if not (attn.is_contiguous() and V.is_contiguous()):
+        raise ValueError("attn and V must be contiguous")
+    if out is not None:
+        if out.dtype != torch.float32 or tuple(out.shape) != (B, Hq, D) or not out.is_contiguous() \
+                or out.device != attn.device:
+            raise ValueError(f"out must be a contiguous float32 [{B},{Hq},{D}] tensor on {attn.device}")
+    return B, C, Hq, Hkv, D, vmap[V.dtype]
+
+
+def gqa_av_decode(attn, V, out=None, mode: Union[str, int] = "auto", stream=None, plan: Optional[Plan] = None):
+    """out[b,q_h,d] = sum_c attn[b,c,q_h] * V[b,c,q_h//G,d] on the GPU; returns out.
+
+    attn: float32 [B,C,Hq]; V: float32/float16/bfloat16 [B,C,Hkv,D]; both
+    contiguous on one GPU. mode: "auto" | "per_head" | "reuse" (or -1/0/1).
+    stream: a torch.cuda.Stream (default: the current stream). plan: an
+    explicit Plan from make_plan for the same problem (tests, sweeps).
+    """
+    torch = _torch()
+    B, C, Hq, Hkv, D, vdt = _check(attn, V, out)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=attn.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(attn.device)
+    lib = load()
+    with torch.cuda.device(attn.device):
+        if plan is None:
+            rc = lib.gqa_av_decode(attn.data_ptr(), V.data_ptr(), out.data_ptr(), B, C, Hq, Hkv, D,
+                                   DTYPES[vdt], _mode(mode), stream.cuda_stream)
+        else:
+            rc = lib.gqa_av_decode_plan(attn.data_ptr(), V.data_ptr(), out.data_ptr(), B, C, Hq, Hkv, D,
+                                        DTYPES[vdt], ctypes.byref(plan), stream.cuda_stream)
+    if rc != 0:
+        _raise(rc)
+    return out
+
+
+def gqa_av_decode_plan(attn, V, plan: Plan, out=None, stream=None):
+    """gqa_av_decode with an explicit plan."""
+    return gqa_av_decode(attn, V, out=out, stream=stream, plan=plan)
+
+
+class BoundCall:
+    """One problem's arguments, checked once, for repeated calls (decode loops, benchmarks).
+
+    Calling the object enqueues the kernels on the bound stream through the C
+    ABI with no per-call Python checks. The bound tensors are referenced here
+    and must not be resized or freed while the object is used.
+    """
+
+    def __init__(self, attn, V, out=None, plan: Optional[Plan] = None, mode: Union[str, int] = "auto",
+                 stream=None):
+        torch = _torch()
+        B, C, Hq, Hkv, D, vdt = _check(attn, V, out)
+        if out is None:
+            out = torch.empty((B, Hq, D), dtype=torch.float32, device=attn.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(attn.device)
+        if plan is None:
+            props = torch.cuda.get_device_properties(attn.device)
+            addr = V.data_ptr()
+            align = 16 if addr % 16 == 0 else (addr & -addr)
+            plan = make_plan(B, C, Hq, Hkv, D, vdt, mode, cu_count=props.multi_processor_count, v_align=align)
+        self.attn, self.V, self.out, self.plan, self.stream = attn, V, out, plan, stream
+        self._fn = load().gqa_av_decode_plan
+        self._args = (attn.data_ptr(), V.data_ptr(), out.data_ptr(), B, C, Hq, Hkv, D, DTYPES[vdt],
+                      ctypes.byref(plan), stream.cuda_stream)
+
+    def __call__(self):
+        rc = self._fn(*self._args)
+        if rc != 0:
+            _raise(rc)
+        return self.out
+
+
+def bind(attn, V, out=None, plan: Optional[Plan] = None, mode: Union[str, int] = "auto", stream=None) -> BoundCall:
+    """A BoundCall for (attn, V, out): see BoundCall."""
+    return BoundCall(attn, V, out=out, plan=plan, mode=mode, stream=stream)
+
+
+def release() -> None:
+    """Free the library's cached split-C workspaces."""
+    rc = load().gqa_av_release()
+    if rc != 0:
+        _raise(rc)

@@ -1,0 +1,501 @@
+// Device code of the GQA decode attention-times-V path for gfx950 (MI355X).
+//
+// Operation (ExecuTorch PR #21063, "...GEMV", introduction), batch index added:
+//   out[b, q_h, d] = sum_c attn[b, c, q_h] * V[b, c, kv_h, d],  kv_h = q_h / G.
+// The page's GQA-reuse variant gives one workgroup a whole KV head and makes
+// it produce the G outputs of that head's group from one read of each V row;
+// its per-query-head shader (kept here as the baseline) reads V once per head.
+//
+// A workgroup (256 threads = 4 wave64) owns a tile = (b, kv_h, head
+// sub-group, D-tile) -- or (b, q_h, D-tile) for the per-head baseline -- and
+// one context split [cb, ce). It streams the tile's V rows of that split once
+// and keeps fp32 accumulators for every query head of the tile. Without a
+// context split it writes `out` directly; otherwise it writes its split's
+// plane of partial sums and a second kernel adds the planes in increasing
+// split order (the kernel boundary makes the partials visible across the
+// XCDs' separate L2 caches without any cache maintenance inside pass 1). No
+// atomics anywhere: a plan gives bitwise-identical results run to run.
+//
+// Two inner-product engines, both fp32 FMA arithmetic:
+//  * VALU  -- any G and D. Lc lanes cover a D-row with VB-byte loads (one
+//             16-byte global_load_dwordx4 each when D allows); rps row slots
+//             load different rows side by side. Each lane widens its V chunk
+//             once and applies it to the GT query heads of the tile, whose
+//             weights are staged in LDS per stage of rps * U rows
+//             (double-buffered) and read as broadcasts. Row slots are summed
+//             through LDS at the end.
+//  * MFMA  -- G >= 5: the group's weights form a 16 x 4 A operand and four V
+//             rows a 4 x 16 B operand of v_mfma_f32_16x16x4_f32, so the matrix
+//             core does the G-fold reuse and the sum over four rows at once.
+//             Lane 16k + n loads row k's D-chunk n (D/16 elements) and the
+//             weight of head n of row k; nothing goes through LDS until the
+//             four waves' tiles are added at the end.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa_av {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kXcds = 8;          // MI355X: 8 accelerator complex dies, one L2 each
+constexpr int kMaxRowSlots = 64;  // rows a VALU workgroup loads side by side, at most
+
+enum : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+template <int DT>
+constexpr int esize() { return DT == kF32 ? 4 : 2; }
+
+// Workgroups are handed to the XCDs round-robin (block i -> XCD i % 8). Remap
+// so that each XCD walks a contiguous range of logical tiles: the KV heads of
+// one (b, split) -- which share the cache lines of their attn rows -- then run
+// on one XCD at about the same time and share its L2.
+__device__ inline uint32_t xcd_remap(uint32_t i, uint32_t n) {
+    const uint32_t per = n / kXcds, rem = n % kXcds;
+    const uint32_t x = i % kXcds, k = i / kXcds;
+    return x < rem ? x * (per + 1) + k : rem * (per + 1) + (x - rem) * per + k;
+}
+
+struct Pass1Args {
+    const float* attn;      // [B][C][Hq]
+    const uint8_t* V;       // [B][C][Hkv][D] of DT
+    float* out;             // [B][Hq][D]
+    float* part;            // [nsplit][B][Hq][D]   (nsplit > 1)
+    int64_t C;
+    int64_t rows_per_split;
+    int32_t B, Hq, Hkv, D;
+    int32_t G;              // Hq / Hkv
+    int32_t per_head;       // 0: reuse tiles, 1: one query head per tile
+    int32_t nsg;            // head sub-groups per KV head (reuse)
+    int32_t ndt;            // D-tiles (VALU)
+    int32_t nsplit;
+    int32_t L;              // VALU: lanes per full D-row
+    int32_t Lc;             // VALU: lanes per D-row inside a workgroup (<= 256)
+    int32_t rps;            // VALU: row slots = min(256 / Lc, kMaxRowSlots)
+    uint32_t nblocks;
+};
+
+// ---- V loads and conversion -------------------------------------------------
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int NB>
+struct Raw {
+    uint32_t w[NB >= 4 ? NB / 4 : 1];
+};
+
+// Load NB bytes (2, 4, 8, 12, 16 or 32) from p, which is NB-aligned (12: 4-aligned).
+// V is read exactly once per call, so the loads carry the non-temporal cache
+// policy: on MI355X this streams at about 7 TB/s against about 6.1 TB/s for
+// default-policy loads of the same pattern.
+template <int NB>
+__device__ inline Raw<NB> load_raw(const uint8_t* p) {
+    Raw<NB> r;
+    if constexpr (NB == 32) {
+        const u32x4 v0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        const u32x4 v1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + 1);
+        r.w[0] = v0.x; r.w[1] = v0.y; r.w[2] = v0.z; r.w[3] = v0.w;
+        r.w[4] = v1.x; r.w[5] = v1.y; r.w[6] = v1.z; r.w[7] = v1.w;
+    } else if constexpr (NB == 16) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+    } else if constexpr (NB == 12) {
+        const u32x3 v = __builtin_nontemporal_load(reinterpret_cast<const u32x3*>(p));
+        r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z;
+    } else if constexpr (NB == 8) {
+        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+        r.w[0] = v.x; r.w[1] = v.y;
+    } else if constexpr (NB == 4) {
+        r.w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+    } else {
+        r.w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
+    }
+    return r;
+}
+
+template <int NB>
+__device__ inline Raw<NB> zero_raw() {
+    Raw<NB> r;
+#pragma unroll
+    for (int i = 0; i < (NB >= 4 ? NB / 4 : 1); ++i) r.w[i] = 0u;
+    return r;
+}
+
+__device__ inline float f16_bits_to_f32(uint32_t h) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+}
+
+// Widen the NB / esize elements of one lane-load to fp32 (exact for all three types).
+template <int DT, int NB>
+__device__ inline void widen(const Raw<NB>& r, float* f) {
+    if constexpr (DT == kF32) {
+#pragma unroll
+        for (int i = 0; i < NB / 4; ++i) f[i] = __uint_as_float(r.w[i]);
+    } else if constexpr (NB == 2) {
+        f[0] = DT == kBF16 ? __uint_as_float(r.w[0] << 16) : f16_bits_to_f32(r.w[0]);
+    } else if constexpr (DT == kBF16) {
+#pragma unroll
+        for (int i = 0; i < NB / 4; ++i) {
+            f[2 * i] = __uint_as_float(r.w[i] << 16);
+            f[2 * i + 1] = __uint_as_float(r.w[i] & 0xffff0000u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NB / 4; ++i) {
+            f[2 * i] = f16_bits_to_f32(r.w[i] & 0xffffu);
+            f[2 * i + 1] = f16_bits_to_f32(r.w[i] >> 16);
+        }
+    }
+}
+
+// ---- tile decode ------------------------------------------------------------
+
+struct Tile {
+    int b, kv, s, dt, q_first, nq;
+};
+
+// Logical order, fastest first: (sub-group, D-tile), kv_h, split, b, and for
+// the per-head baseline the head's position g inside its group slowest, so the
+// G re-reads of one V row are far apart in time and not merged by the caches.
+__device__ inline Tile decode_tile(const Pass1Args& a, int GT) {
+    uint32_t t = xcd_remap(blockIdx.x, a.nblocks);
+    Tile T;
+    const uint32_t nminor = a.per_head ? a.ndt : a.nsg * a.ndt;
+    const uint32_t minor = t % nminor; t /= nminor;
+    T.kv = t % a.Hkv; t /= a.Hkv;
+    T.s = t % a.nsplit; t /= a.nsplit;
+    T.b = t % a.B; t /= a.B;
+    const uint32_t major = t;
+    if (a.per_head) {
+        T.dt = minor;
+        T.q_first = T.kv * a.G + major;
+        T.nq = 1;
+    } else {
+        const int sg = minor / a.ndt;
+        T.dt = minor % a.ndt;
+        T.q_first = T.kv * a.G + sg * GT;
+        T.nq = min(GT, a.G - sg * GT);
+    }
+    return T;
+}
+
+// ---- pass 1: VALU engine ----------------------------------------------------
+
+// GP: padded LDS row of staged weights (GT = 3 -> 4 so rows stay 16-byte aligned).
+template <int GT>
+constexpr int padded_heads() { return GT <= 2 ? GT : (GT + 3) / 4 * 4; }
+
+template <int DT, int VB, int GT, int U>
+__global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
+    constexpr int ES = esize<DT>();
+    constexpr int E = VB / ES;
+    constexpr int NACC = GT * E;
+    constexpr int CH = NACC < 32 ? NACC : 32;       // accumulator slots per LDS reduction pass
+    constexpr int GP = padded_heads<GT>();
+    constexpr int RMAX = kMaxRowSlots * U;           // rows per stage is rps * U
+    constexpr int WBUF = 2 * RMAX * GP;              // staged weights, double-buffered (worst case)
+    constexpr int RED = CH * kThreads;
+    constexpr int SMEM = WBUF > RED ? WBUF : RED;
+    __shared__ float smem[SMEM];
+
+    const Tile T = decode_tile(a, GT);
+    const int tid = threadIdx.x;
+    const int Lc = a.Lc, rps = a.rps;
+    const int r = tid / Lc;
+    const int j = tid - r * Lc;
+    const int lane_d = T.dt * Lc + j;                // which VB-chunk of the D-row
+    const bool active = (r < rps) && (lane_d < a.L);
+
+    const int64_t cb = static_cast<int64_t>(T.s) * a.rows_per_split;
+    const int64_t ce = min(a.C, cb + a.rows_per_split);
+    const int R = rps * U;                           // rows per stage
+    const int64_t nstage = ce > cb ? (ce - cb + R - 1) / R : 0;
+
+    const size_t vrow = static_cast<size_t>(a.Hkv) * a.D * ES;   // bytes from row c to c+1
+    const uint8_t* vbase = a.V + (static_cast<size_t>(T.b) * a.C * a.Hkv + T.kv) * a.D * ES
+                               + static_cast<size_t>(lane_d) * VB;
+    const float* abase = a.attn + static_cast<size_t>(T.b) * a.C * a.Hq + T.q_first;
+
+    float acc[GT][E];
+#pragma unroll
+    for (int g = 0; g < GT; ++g)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[g][e] = 0.0f;
+
+    // Weight staging: element k of a stage is (row i = k / GT, head g = k % GT).
+    const int nstage_elems = R * GT;
+    constexpr int SPT = (RMAX * GT + kThreads - 1) / kThreads;  // staged words per thread (bound)
+    float wreg[SPT];
+    auto stage_load = [&](int64_t c0) {
+#pragma unroll
+        for (int k = 0; k < SPT; ++k) {
+            const int idx = tid + k * kThreads;
+            float v = 0.0f;
+            if (idx < nstage_elems) {
+                const int i = idx / GT, g = idx - (idx / GT) * GT;
+                const int64_t c = c0 + i;
+                if (g < T.nq && c < ce) v = abase[c * a.Hq + g];
+            }
+            wreg[k] = v;
+        }
+    };
+    auto stage_store = [&](int buf) {
+        float* w = smem + buf * (RMAX * GP);
+#pragma unroll
+        for (int k = 0; k < SPT; ++k) {
+            const int idx = tid + k * kThreads;
+            if (idx < nstage_elems) {
+                const int i = idx / GT, g = idx - (idx / GT) * GT;
+                w[i * GP + g] = wreg[k];
+            }
+        }
+    };
+    // V rows of the stage starting at c0: this lane's rows are c0 + r + u * rps.
+    auto load_v = [&](Raw<VB> (&raw)[U], int64_t c0) {
+        if (!active) return;
+        const uint8_t* p = vbase + static_cast<size_t>(c0 + r) * vrow;
+        const size_t step = static_cast<size_t>(rps) * vrow;
+        if (c0 + R <= ce) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) raw[u] = load_raw<VB>(p + u * step);
+        } else {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                raw[u] = (c0 + r + u * rps < ce) ? load_raw<VB>(p + u * step) : zero_raw<VB>();
+        }
+    };
+    auto compute = [&](const Raw<VB> (&raw)[U], int buf) {
+        if (!active) return;
+        const float* w = smem + buf * (RMAX * GP);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float* wr = w + (r + u * rps) * GP;
+            float wv[GT];
+#pragma unroll
+            for (int g = 0; g < GT; ++g) wv[g] = wr[g];
+            float f[E];
+            widen<DT, VB>(raw[u], f);
+#pragma unroll
+            for (int g = 0; g < GT; ++g)
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[g][e] = __builtin_fmaf(wv[g], f[e], acc[g][e]);
+        }
+    };
+
+    // Software pipeline over stages: the next stage's V rows and weights are in
+    // flight while the current stage is computed. Stage st uses weight buffer st & 1.
+    Raw<VB> rA[U], rB[U];
+    if (nstage > 0) {
+        load_v(rA, cb);
+        stage_load(cb);
+        stage_store(0);
+    }
+    __syncthreads();
+    int64_t st = 0;
+    for (; st + 1 < nstage; st += 2) {
+        const int64_t c1 = cb + (st + 1) * R;
+        load_v(rB, c1);
+        stage_load(c1);
+        compute(rA, 0);
+        stage_store(1);
+        __syncthreads();
+        const bool more = st + 2 < nstage;
+        if (more) {
+            load_v(rA, c1 + R);
+            stage_load(c1 + R);
+        }
+        compute(rB, 1);
+        if (more) stage_store(0);
+        __syncthreads();
+    }
+    if (st < nstage) compute(rA, 0);
+    __syncthreads();                                  // weight buffers are reused below
+
+    // Sum the row slots: slot kk of thread tid lives at smem[kk * 256 + tid].
+    float* const dst = a.nsplit > 1 ? a.part + static_cast<size_t>(T.s) * a.B * a.Hq * a.D : a.out;
+    const int nout = Lc * CH;
+#pragma unroll
+    for (int k0 = 0; k0 < NACC; k0 += CH) {
+#pragma unroll
+        for (int kk = 0; kk < CH; ++kk) {
+            const int k = k0 + kk;
+            smem[kk * kThreads + tid] = acc[k / E][k % E];
+        }
+        __syncthreads();
+        for (int idx = tid; idx < nout; idx += kThreads) {
+            const int kk = idx / Lc, jj = idx - (idx / Lc) * Lc;
+            float sum = 0.0f;
+            for (int rr = 0; rr < rps; ++rr) sum += smem[kk * kThreads + rr * Lc + jj];
+            const int k = k0 + kk;
+            const int g = k / E, e = k - (k / E) * E;
+            const int ld = T.dt * Lc + jj;
+            if (g < T.nq && ld < a.L)
+                dst[(static_cast<size_t>(T.b) * a.Hq + T.q_first + g) * a.D + static_cast<size_t>(ld) * E + e] = sum;
+        }
+        __syncthreads();
+    }
+}
+
+// ---- pass 1: MFMA engine ----------------------------------------------------
+
+// NSET sets of 16 query heads; DE = D / 16 elements of V per lane and row.
+// Rows are taken in groups of four (the K of one MFMA); wave w of the
+// workgroup handles groups w, w + 4, w + 8, ... of its split, U groups per
+// step, with the next step's loads in flight during the current step.
+template <int DT, int DE, int NSET, int U>
+__global__ __launch_bounds__(kThreads) void av_pass1_mfma(Pass1Args a) {
+    constexpr int ES = esize<DT>();
+    constexpr int NB = DE * ES;                      // V bytes per lane and row
+    constexpr int NREG = NSET * DE * 4;              // accumulator floats per lane
+    constexpr int TO = NREG * 64;                    // outputs of the tile (= 16 * NSET * D)
+    __shared__ float red[kWaves * TO];
+
+    const Tile T = decode_tile(a, 16 * NSET);
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int k = lane >> 4;                         // row inside a group of four
+    const int n = lane & 15;                         // D-chunk / head index inside a set
+
+    const int64_t cb = static_cast<int64_t>(T.s) * a.rows_per_split;
+    const int64_t ce = min(a.C, cb + a.rows_per_split);
+    const size_t vrow = static_cast<size_t>(a.Hkv) * a.D * ES;
+    const uint8_t* vbase = a.V + (static_cast<size_t>(T.b) * a.C * a.Hkv + T.kv) * a.D * ES
+                               + static_cast<size_t>(n) * NB;
+    const float* abase = a.attn + static_cast<size_t>(T.b) * a.C * a.Hq + T.q_first + n;
+    bool hv[NSET];
+#pragma unroll
+    for (int s = 0; s < NSET; ++s) hv[s] = n + 16 * s < T.nq;
+
+    f32x4 acc[NSET][DE];
+#pragma unroll
+    for (int s = 0; s < NSET; ++s)
+#pragma unroll
+        for (int e = 0; e < DE; ++e) acc[s][e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    constexpr int RSTEP = 4 * kWaves * U;            // rows per workgroup step
+    const int64_t nsteps = ce > cb ? (ce - cb + RSTEP - 1) / RSTEP : 0;
+
+    // Row of group u of the step starting at c0, for this lane.
+    auto row_of = [&](int64_t c0, int u) -> int64_t { return c0 + 4 * (u * kWaves + wave) + k; };
+    auto load = [&](Raw<NB> (&rv)[U], float (&rw)[U][NSET], int64_t c0) {
+        if (c0 + RSTEP <= ce) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t c = row_of(c0, u);
+                rv[u] = load_raw<NB>(vbase + static_cast<size_t>(c) * vrow);
+#pragma unroll
+                for (int s = 0; s < NSET; ++s) rw[u][s] = hv[s] ? abase[c * a.Hq + 16 * s] : 0.0f;
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t c = row_of(c0, u);
+                const bool in = c < ce;
+                rv[u] = in ? load_raw<NB>(vbase + static_cast<size_t>(c) * vrow) : zero_raw<NB>();
+#pragma unroll
+                for (int s = 0; s < NSET; ++s) rw[u][s] = (in && hv[s]) ? abase[c * a.Hq + 16 * s] : 0.0f;
+            }
+        }
+    };
+    auto compute = [&](const Raw<NB> (&rv)[U], const float (&rw)[U][NSET]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float f[DE];
+            widen<DT, NB>(rv[u], f);
+#pragma unroll
+            for (int s = 0; s < NSET; ++s)
+#pragma unroll
+                for (int e = 0; e < DE; ++e)
+                    acc[s][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(rw[u][s], f[e], acc[s][e], 0, 0, 0);
+        }
+    };
+
+    Raw<NB> vA[U], vB[U];
+    float wA[U][NSET], wB[U][NSET];
+    int64_t st = 0;
+    if (nsteps > 0) load(vA, wA, cb);
+    for (; st + 1 < nsteps; st += 2) {
+        const int64_t c1 = cb + (st + 1) * RSTEP;
+        load(vB, wB, c1);
+        compute(vA, wA);
+        if (st + 2 < nsteps) load(vA, wA, c1 + RSTEP);
+        compute(vB, wB);
+    }
+    if (st < nsteps) compute(vA, wA);
+
+    // Add the four waves' 16 x D tiles. Register i of acc[s][e] in lane l is
+    // head 16 s + 4 (l / 16) + i, element d = (l % 16) * DE + e; as a tile
+    // output index: ((s * DE + e) * 4 + i) * 64 + l.
+#pragma unroll
+    for (int s = 0; s < NSET; ++s)
+#pragma unroll
+        for (int e = 0; e < DE; ++e)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[wave * TO + ((s * DE + e) * 4 + i) * 64 + lane] = acc[s][e][i];
+    __syncthreads();
+    float* const dst = a.nsplit > 1 ? a.part + static_cast<size_t>(T.s) * a.B * a.Hq * a.D : a.out;
+    for (int idx = threadIdx.x; idx < TO; idx += kThreads) {
+        float sum = red[idx];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) sum += red[w * TO + idx];
+        const int l = idx & 63, reg = idx >> 6;
+        const int i = reg & 3, se = reg >> 2;
+        const int e = se % DE, s = se / DE;
+        const int g = 16 * s + 4 * (l >> 4) + i;
+        if (g < T.nq)
+            dst[(static_cast<size_t>(T.b) * a.Hq + T.q_first + g) * a.D + (l & 15) * DE + e] = sum;
+    }
+}
+
+// ---- pass 2: split-C combine -------------------------------------------------
+
+// out[i] = sum over s of part[s][i] for the `plane` outputs, in a fixed order:
+// the splits are cut into kSplitGroups contiguous ranges, each summed in
+// increasing s by its own thread, and the range sums are then added in
+// increasing range order. Each thread covers four consecutive outputs.
+constexpr int kSplitGroups = 8;
+constexpr int kQuadsPerBlock = kThreads / kSplitGroups;
+
+__global__ __launch_bounds__(kThreads) void av_pass2_combine(const float* __restrict__ part,
+                                                             float* __restrict__ out,
+                                                             int64_t plane, int32_t nsplit) {
+    __shared__ f32x4 red[kSplitGroups][kQuadsPerBlock];
+    const int q = threadIdx.x % kQuadsPerBlock;
+    const int sg = threadIdx.x / kQuadsPerBlock;
+    const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * kQuadsPerBlock + q) * 4;
+    const int s0 = static_cast<int>((static_cast<int64_t>(nsplit) * sg) / kSplitGroups);
+    const int s1 = static_cast<int>((static_cast<int64_t>(nsplit) * (sg + 1)) / kSplitGroups);
+    // Whole float4 loads need a plane of whole quads; the store needs `out` 16-byte aligned.
+    const bool quads = (plane & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15u) == 0;
+    f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (quads && i0 + 3 < plane) {
+#pragma unroll 4
+        for (int s = s0; s < s1; ++s)
+            sum += *reinterpret_cast<const f32x4*>(part + static_cast<size_t>(s) * plane + i0);
+    } else {
+        for (int s = s0; s < s1; ++s)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (i0 + c < plane) sum[c] += part[static_cast<size_t>(s) * plane + i0 + c];
+    }
+    red[sg][q] = sum;
+    __syncthreads();
+    if (sg == 0) {
+        f32x4 t = red[0][q];
+#pragma unroll
+        for (int k = 1; k < kSplitGroups; ++k) t += red[k][q];
+        if (quads && i0 + 3 < plane) {
+            *reinterpret_cast<f32x4*>(out + i0) = t;
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (i0 + c < plane) out[i0 + c] = t[c];
+        }
+    }
+}
+
+}  // namespace gqa_av

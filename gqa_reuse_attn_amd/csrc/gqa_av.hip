@@ -1,0 +1,529 @@
+// Host side of libgqa_av.so: argument checks, mode resolution, planning,
+// workspace management and kernel launches behind the C ABI in include/gqa_av.h.
+//
+// Mode resolution and eligibility follow the dispatch and override bullets of
+// ExecuTorch PR #21063, "...GEMV", implementation section: the reuse variant
+// is picked when Hq > Hkv and Hq divides evenly by Hkv, the per-head kernel
+// otherwise, and a forced reuse on an ineligible shape is an error. The page
+// also caps G at 8 and sends larger groups to the per-head kernel; that cap
+// is not kept: any G takes the reuse path (G > 16 in sub-groups of 16 heads).
+#include "gqa_av.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "av_kernels.hpp"
+
+namespace {
+
+using gqa_av::Pass1Args;
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int elem_bytes(int dt) { return dt == GQA_AV_F32 ? 4 : 2; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Compile-time head capacity of a reuse tile for a group of G heads.
+int head_capacity(int64_t G) {
+    if (G <= 4) return static_cast<int>(G);
+    if (G <= 8) return 8;
+    return 16;
+}
+
+// Unroll depth: rows each lane keeps in flight per stage.
+int unroll_for(int GT) { return GT <= 4 ? 8 : (GT <= 8 ? 4 : 2); }
+
+constexpr int kDefaultCUs = 256;
+constexpr int64_t kMinRowsPerSplit = 256;     // below this a split's epilogue dominates
+constexpr int64_t kTargetWgPerCU = 8;
+
+// Split-C workspace of one (device, stream): the partial-sum planes.
+struct Workspace {
+    void* part = nullptr;
+    size_t bytes = 0;
+};
+
+std::mutex g_ws_mutex;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+std::mutex g_cu_mutex;
+std::map<int, int> g_cu_count;
+
+int device_cus(int dev, int* cus) {
+    std::lock_guard<std::mutex> lock(g_cu_mutex);
+    auto it = g_cu_count.find(dev);
+    if (it != g_cu_count.end()) {
+        *cus = it->second;
+        return GQA_AV_OK;
+    }
+    int n = 0;
+    hipError_t e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
+    g_cu_count[dev] = n;
+    *cus = n;
+    return GQA_AV_OK;
+}
+
+// The workspace of (dev, stream), grown to at least `bytes`. Earlier calls on
+// the stream may still use the old buffer, so the stream is synchronised
+// before it is freed.
+int get_workspace(int dev, hipStream_t stream, size_t bytes, float** part) {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace& ws = g_ws[{dev, stream}];
+    if (ws.bytes < bytes) {
+        if (ws.part) {
+            hipError_t e = hipStreamSynchronize(stream);
+            if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
+            e = hipFree(ws.part);
+            ws = Workspace();
+            if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "hipFree: %s", hipGetErrorString(e));
+        }
+        void* p = nullptr;
+        hipError_t e = hipMalloc(&p, bytes);
+        if (e != hipSuccess)
+            return fail(GQA_AV_ERR_HIP, "hipMalloc(%zu) for split-C workspace: %s", bytes, hipGetErrorString(e));
+        ws.part = p;
+        ws.bytes = bytes;
+    }
+    *part = static_cast<float*>(ws.part);
+    return GQA_AV_OK;
+}
+
+int check_sizes(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dtype) {
+    if (B < 0 || C < 0) return fail(GQA_AV_ERR_INVALID_ARG, "B=%lld and C=%lld must be >= 0", (long long)B, (long long)C);
+    if (Hq < 1 || Hkv < 1 || D < 1)
+        return fail(GQA_AV_ERR_INVALID_ARG, "Hq=%lld, Hkv=%lld and D=%lld must be >= 1", (long long)Hq, (long long)Hkv, (long long)D);
+    if (Hq % Hkv != 0)
+        return fail(GQA_AV_ERR_INVALID_ARG, "Hq=%lld is not a multiple of Hkv=%lld", (long long)Hq, (long long)Hkv);
+    if (v_dtype != GQA_AV_F32 && v_dtype != GQA_AV_F16 && v_dtype != GQA_AV_BF16)
+        return fail(GQA_AV_ERR_INVALID_ARG, "unknown v_dtype %d", v_dtype);
+    // Index arithmetic inside the kernels keeps these in 32 bits.
+    if (B > INT32_MAX || Hq > INT32_MAX || D > INT32_MAX)
+        return fail(GQA_AV_ERR_UNSUPPORTED, "B, Hq and D must each fit in 31 bits");
+    return GQA_AV_OK;
+}
+
+// ---- kernel dispatch ----------------------------------------------------------
+
+template <int DT, int VB, int GT>
+hipError_t launch_valu(const Pass1Args& a, hipStream_t s) {
+    constexpr int U = GT <= 4 ? 8 : (GT <= 8 ? 4 : 2);
+    hipLaunchKernelGGL((gqa_av::av_pass1_valu<DT, VB, GT, U>), dim3(a.nblocks), dim3(gqa_av::kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int DT, int VB>
+hipError_t launch_valu_gt(int GT, const Pass1Args& a, hipStream_t s) {
+    switch (GT) {
+    case 1: return launch_valu<DT, VB, 1>(a, s);
+    case 2: return launch_valu<DT, VB, 2>(a, s);
+    case 3: return launch_valu<DT, VB, 3>(a, s);
+    case 4: return launch_valu<DT, VB, 4>(a, s);
+    case 8: return launch_valu<DT, VB, 8>(a, s);
+    case 16: return launch_valu<DT, VB, 16>(a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int DT>
+hipError_t launch_valu_vb(int VB, int GT, const Pass1Args& a, hipStream_t s) {
+    switch (VB) {
+    case 16: return launch_valu_gt<DT, 16>(GT, a, s);
+    case 8: return launch_valu_gt<DT, 8>(GT, a, s);
+    case 4: return launch_valu_gt<DT, 4>(GT, a, s);
+    case 2:
+        if constexpr (DT != gqa_av::kF32) return launch_valu_gt<DT, 2>(GT, a, s);
+        return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int DT, int DE, int NSET>
+hipError_t launch_mfma(const Pass1Args& a, hipStream_t s) {
+    constexpr int U = DE * gqa_av::esize<DT>() > 16 ? 2 : 4;
+    hipLaunchKernelGGL((gqa_av::av_pass1_mfma<DT, DE, NSET, U>), dim3(a.nblocks), dim3(gqa_av::kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int DT, int DE>
+hipError_t launch_mfma_set(int nset, const Pass1Args& a, hipStream_t s) {
+    if (nset == 1) return launch_mfma<DT, DE, 1>(a, s);
+    if constexpr (DE <= 8) {
+        if (nset == 2) return launch_mfma<DT, DE, 2>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int DT>
+hipError_t launch_mfma_de(int DE, int nset, const Pass1Args& a, hipStream_t s) {
+    switch (DE) {
+    case 2: return launch_mfma_set<DT, 2>(nset, a, s);
+    case 4: return launch_mfma_set<DT, 4>(nset, a, s);
+    case 6:
+        if constexpr (DT != gqa_av::kF32) return launch_mfma_set<DT, 6>(nset, a, s);
+        return hipErrorInvalidValue;
+    case 8: return launch_mfma_set<DT, 8>(nset, a, s);
+    case 16:
+        if constexpr (DT != gqa_av::kF32) return launch_mfma_set<DT, 16>(nset, a, s);
+        return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_pass1(int v_dtype, const gqa_av_plan& p, int64_t D, const Pass1Args& a, hipStream_t s) {
+    if (p.engine == GQA_AV_ENGINE_MFMA) {
+        const int DE = static_cast<int>(D / 16), nset = p.heads_per_tile / 16;
+        switch (v_dtype) {
+        case GQA_AV_F32: return launch_mfma_de<gqa_av::kF32>(DE, nset, a, s);
+        case GQA_AV_F16: return launch_mfma_de<gqa_av::kF16>(DE, nset, a, s);
+        case GQA_AV_BF16: return launch_mfma_de<gqa_av::kBF16>(DE, nset, a, s);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    switch (v_dtype) {
+    case GQA_AV_F32: return launch_valu_vb<gqa_av::kF32>(p.vec_bytes, p.heads_per_tile, a, s);
+    case GQA_AV_F16: return launch_valu_vb<gqa_av::kF16>(p.vec_bytes, p.heads_per_tile, a, s);
+    case GQA_AV_BF16: return launch_valu_vb<gqa_av::kBF16>(p.vec_bytes, p.heads_per_tile, a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// Address alignment a lane load of `vec_bytes` needs: its own size up to 16
+// bytes (a 32-byte load is two 16-byte ones); 12-byte loads need 4.
+int load_alignment(int vec_bytes) {
+    if (vec_bytes == 12) return 4;
+    return vec_bytes > 16 ? 16 : vec_bytes;
+}
+
+// Can the MFMA engine take this problem? D splits into 16 lane chunks whose
+// byte size is one of the engine's load widths, V is aligned for that width,
+// and the four waves' 16 x D tiles fit the 64 KB LDS reduction buffer.
+bool mfma_fits(int64_t D, int es, int v_align, int nset) {
+    if (D % 16 != 0) return false;
+    const int64_t DE = D / 16, NB = DE * es;
+    if (!(NB == 4 || NB == 8 || NB == 12 || NB == 16 || NB == 32)) return false;
+    if (v_align % load_alignment(static_cast<int>(NB)) != 0) return false;
+    return nset * DE <= 16 && (nset == 1 || DE <= 8);
+}
+
+constexpr int64_t kMfmaMinGroup = 5;     // below this the VALU engine does less work
+
+int64_t workspace_bytes(int64_t B, int64_t Hq, int64_t D, int64_t nsplit) {
+    return nsplit > 1 ? nsplit * B * Hq * D * 4 : 0;   // one fp32 plane of out per split
+}
+
+int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dtype, int mode,
+              const gqa_av_hint* hint, int cu_default, gqa_av_plan* plan) {
+    int rc = check_sizes(B, C, Hq, Hkv, D, v_dtype);
+    if (rc != GQA_AV_OK) return rc;
+    const int resolved = gqa_av_resolve_mode(Hq, Hkv, mode);
+    if (resolved < 0) return -resolved;
+    if (!plan) return fail(GQA_AV_ERR_INVALID_ARG, "plan is NULL");
+
+    gqa_av_hint h;
+    std::memset(&h, 0, sizeof h);
+    h.engine = GQA_AV_ENGINE_AUTO;
+    if (hint) h = *hint;
+    if (h.engine != GQA_AV_ENGINE_AUTO && h.engine != GQA_AV_ENGINE_VALU && h.engine != GQA_AV_ENGINE_MFMA)
+        return fail(GQA_AV_ERR_INVALID_ARG, "unknown engine %d", h.engine);
+    const int cus = h.cu_count > 0 ? h.cu_count : cu_default;
+    const int v_align = h.v_align > 0 ? h.v_align : 16;
+
+    const int es = elem_bytes(v_dtype);
+    const int64_t G = Hq / Hkv;
+
+    // Engine. The matrix-core engine always computes 16 (or 32) heads per
+    // tile, so it only pays off for larger groups; the per-head baseline is
+    // always the VALU engine with one head per tile.
+    const int nset = (G > 16 && mfma_fits(D, es, v_align, 2)) ? 2 : 1;
+    const bool mfma_ok = resolved == GQA_AV_REUSE && mfma_fits(D, es, v_align, nset);
+    int engine = h.engine;
+    if (engine == GQA_AV_ENGINE_AUTO) engine = (mfma_ok && G >= kMfmaMinGroup) ? GQA_AV_ENGINE_MFMA : GQA_AV_ENGINE_VALU;
+    if (engine == GQA_AV_ENGINE_MFMA && !mfma_ok)
+        return fail(GQA_AV_ERR_UNSUPPORTED,
+                    "MFMA engine needs reuse mode, D %% 16 == 0 with a 4/8/12/16/32-byte lane chunk and matching V alignment");
+
+    int VB, GT, nsg;
+    int64_t Lc, rps, ndt, rows_per_step;
+    int64_t heads_major;  // tiles along the head axis per KV head
+    if (engine == GQA_AV_ENGINE_MFMA) {
+        const int64_t DE = D / 16;
+        VB = static_cast<int>(DE * es);
+        GT = 16 * nset;
+        nsg = static_cast<int>(ceil_div(G, GT));
+        heads_major = nsg;
+        Lc = 16;
+        rps = 16;                       // 4 waves x 4 rows per MFMA
+        ndt = 1;
+        rows_per_step = 4 * gqa_av::kWaves * (VB > 16 ? 2 : 4);
+    } else {
+        // Widest lane load that divides a D-row and respects V's alignment.
+        VB = 0;
+        for (int cand = 16; cand >= es; cand /= 2) {
+            if ((D * es) % cand == 0 && v_align % cand == 0) { VB = cand; break; }
+        }
+        if (VB == 0)
+            return fail(GQA_AV_ERR_UNSUPPORTED, "V must be aligned to its element size (%d bytes)", es);
+        const int64_t E = VB / es;
+        const int64_t L = D / E;
+        Lc = L < gqa_av::kThreads ? L : gqa_av::kThreads;
+        ndt = ceil_div(L, Lc);
+        rps = gqa_av::kThreads / Lc;
+        if (rps > gqa_av::kMaxRowSlots) rps = gqa_av::kMaxRowSlots;
+        if (resolved == GQA_AV_REUSE) {
+            GT = head_capacity(G);
+            nsg = static_cast<int>(ceil_div(G, GT));
+            heads_major = nsg;
+        } else {
+            GT = 1;
+            nsg = 1;
+            heads_major = G;
+        }
+        rows_per_step = rps * unroll_for(GT);
+    }
+    const int64_t tiles = B * Hkv * heads_major * ndt;
+
+    int64_t nsplit = 1, rows_per_split = C;
+    if (C > 0) {
+        if (h.nsplit > 0) {
+            nsplit = h.nsplit < C ? h.nsplit : C;
+            rows_per_split = ceil_div(C, nsplit);
+        } else {
+            const int64_t target = kTargetWgPerCU * cus;
+            nsplit = tiles > 0 ? ceil_div(target, tiles) : 1;
+            const int64_t cap = ceil_div(C, kMinRowsPerSplit);
+            if (nsplit > cap) nsplit = cap;
+            if (nsplit < 1) nsplit = 1;
+            rows_per_split = ceil_div(ceil_div(C, nsplit), rows_per_step) * rows_per_step;
+        }
+        nsplit = ceil_div(C, rows_per_split);
+    }
+    if (nsplit > INT32_MAX) return fail(GQA_AV_ERR_UNSUPPORTED, "too many context splits");
+    const int64_t grid = tiles * nsplit;
+    if (grid > INT32_MAX) return fail(GQA_AV_ERR_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)grid);
+
+    std::memset(plan, 0, sizeof *plan);
+    plan->mode = resolved;
+    plan->engine = engine;
+    plan->heads_per_tile = GT;
+    plan->subgroups = nsg;
+    plan->vec_bytes = VB;
+    plan->lanes_per_row = static_cast<int32_t>(Lc);
+    plan->row_slots = static_cast<int32_t>(rps);
+    plan->d_tiles = static_cast<int32_t>(ndt);
+    plan->nsplit = static_cast<int32_t>(nsplit);
+    plan->threads = gqa_av::kThreads;
+    plan->rows_per_split = rows_per_split;
+    plan->grid = grid;
+    plan->workspace_bytes = workspace_bytes(B, Hq, D, nsplit);
+    plan->v_bytes_read = B * C * Hkv * D * es * heads_major;
+    return GQA_AV_OK;
+}
+
+bool same_plan(const gqa_av_plan& a, const gqa_av_plan& b) {
+    return a.mode == b.mode && a.engine == b.engine && a.heads_per_tile == b.heads_per_tile &&
+           a.subgroups == b.subgroups && a.vec_bytes == b.vec_bytes && a.lanes_per_row == b.lanes_per_row &&
+           a.row_slots == b.row_slots && a.d_tiles == b.d_tiles && a.nsplit == b.nsplit &&
+           a.threads == b.threads && a.rows_per_split == b.rows_per_split && a.grid == b.grid &&
+           a.workspace_bytes == b.workspace_bytes;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_av_resolve_mode(int64_t Hq, int64_t Hkv, int mode) {
+    if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) {
+        fail(GQA_AV_ERR_INVALID_ARG, "head shape Hq=%lld, Hkv=%lld: need Hq, Hkv >= 1 and Hq %% Hkv == 0",
+             (long long)Hq, (long long)Hkv);
+        return -GQA_AV_ERR_INVALID_ARG;
+    }
+    const bool eligible = Hq / Hkv >= 2;
+    switch (mode) {
+    case GQA_AV_AUTO: return eligible ? GQA_AV_REUSE : GQA_AV_PER_HEAD;
+    case GQA_AV_PER_HEAD: return GQA_AV_PER_HEAD;
+    case GQA_AV_REUSE:
+        if (!eligible) {
+            fail(GQA_AV_ERR_INELIGIBLE, "reuse forced with Hq=%lld, Hkv=%lld: group size %lld < 2",
+                 (long long)Hq, (long long)Hkv, (long long)(Hq / Hkv));
+            return -GQA_AV_ERR_INELIGIBLE;
+        }
+        return GQA_AV_REUSE;
+    default:
+        fail(GQA_AV_ERR_INVALID_ARG, "unknown mode %d", mode);
+        return -GQA_AV_ERR_INVALID_ARG;
+    }
+}
+
+int gqa_av_make_plan(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dtype, int mode,
+                     const gqa_av_hint* hint, gqa_av_plan* plan) {
+    return plan_impl(B, C, Hq, Hkv, D, v_dtype, mode, hint, kDefaultCUs, plan);
+}
+
+int gqa_av_decode_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C, int64_t Hq,
+                       int64_t Hkv, int64_t D, int v_dtype, const gqa_av_plan* plan, void* stream) {
+    if (!plan) return fail(GQA_AV_ERR_INVALID_ARG, "plan is NULL");
+    int rc = check_sizes(B, C, Hq, Hkv, D, v_dtype);
+    if (rc != GQA_AV_OK) return rc;
+    // Re-derive the plan from its own choices and insist it matches.
+    gqa_av_hint h;
+    std::memset(&h, 0, sizeof h);
+    h.engine = plan->engine;
+    h.nsplit = plan->nsplit;
+    h.v_align = plan->vec_bytes;
+    gqa_av_plan check;
+    const int mode = plan->mode;
+    // Re-plan with the split count fixed: rows_per_split then follows from C.
+    rc = plan_impl(B, C, Hq, Hkv, D, v_dtype, mode, &h, kDefaultCUs, &check);
+    if (rc != GQA_AV_OK) return rc;
+    check.rows_per_split = plan->rows_per_split;
+    check.nsplit = plan->nsplit;
+    check.grid = plan->grid;
+    check.workspace_bytes = plan->workspace_bytes;
+    if (!same_plan(check, *plan)) return fail(GQA_AV_ERR_INVALID_ARG, "plan does not belong to this problem");
+    // The split fields must still tile [0, C) exactly.
+    if (C > 0) {
+        if (plan->nsplit < 1 || plan->rows_per_split < 1 ||
+            ceil_div(C, plan->rows_per_split) != plan->nsplit)
+            return fail(GQA_AV_ERR_INVALID_ARG, "plan splits do not cover C=%lld", (long long)C);
+    } else if (plan->nsplit != 1) {
+        return fail(GQA_AV_ERR_INVALID_ARG, "C == 0 needs nsplit == 1");
+    }
+    const int64_t tiles_per_split = plan->grid / plan->nsplit;
+    const int64_t heads_major = plan->mode == GQA_AV_REUSE ? plan->subgroups : Hq / Hkv;
+    if (plan->grid % plan->nsplit != 0 || tiles_per_split != B * Hkv * heads_major * plan->d_tiles)
+        return fail(GQA_AV_ERR_INVALID_ARG, "plan grid does not match the problem");
+    if (plan->workspace_bytes != workspace_bytes(B, Hq, D, plan->nsplit))
+        return fail(GQA_AV_ERR_INVALID_ARG, "plan workspace does not match the problem");
+
+    if (B == 0) return GQA_AV_OK;
+    if (!attn && C > 0) return fail(GQA_AV_ERR_INVALID_ARG, "attn is NULL");
+    if (!V && C > 0) return fail(GQA_AV_ERR_INVALID_ARG, "V is NULL");
+    if (!out) return fail(GQA_AV_ERR_INVALID_ARG, "out is NULL");
+    if ((reinterpret_cast<uintptr_t>(attn) & 3u) || (reinterpret_cast<uintptr_t>(out) & 3u))
+        return fail(GQA_AV_ERR_INVALID_ARG, "attn and out must be 4-byte aligned");
+    if (reinterpret_cast<uintptr_t>(V) % static_cast<uintptr_t>(load_alignment(plan->vec_bytes)))
+        return fail(GQA_AV_ERR_UNSUPPORTED, "V is not aligned to the plan's %d-byte loads", plan->vec_bytes);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+
+    float* part = nullptr;
+    if (plan->nsplit > 1) {
+        rc = get_workspace(dev, s, static_cast<size_t>(plan->workspace_bytes), &part);
+        if (rc != GQA_AV_OK) return rc;
+    }
+
+    Pass1Args a;
+    a.attn = attn;
+    a.V = static_cast<const uint8_t*>(V);
+    a.out = out;
+    a.part = part;
+    a.C = C;
+    a.rows_per_split = plan->rows_per_split;
+    a.B = static_cast<int32_t>(B);
+    a.Hq = static_cast<int32_t>(Hq);
+    a.Hkv = static_cast<int32_t>(Hkv);
+    a.D = static_cast<int32_t>(D);
+    a.G = static_cast<int32_t>(Hq / Hkv);
+    a.per_head = plan->mode == GQA_AV_PER_HEAD;
+    a.nsg = plan->subgroups;
+    a.ndt = plan->d_tiles;
+    a.nsplit = plan->nsplit;
+    a.L = static_cast<int32_t>(D * elem_bytes(v_dtype) / plan->vec_bytes);
+    a.Lc = plan->lanes_per_row;
+    a.rps = plan->row_slots;
+    a.nblocks = static_cast<uint32_t>(plan->grid);
+
+    e = launch_pass1(v_dtype, *plan, D, a, s);
+    if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "pass-1 launch: %s", hipGetErrorString(e));
+    if (plan->nsplit > 1) {
+        const int64_t plane = B * Hq * D;
+        const int64_t per_block = 4 * gqa_av::kQuadsPerBlock;
+        const int64_t blocks = ceil_div(plane, per_block);
+        if (blocks > INT32_MAX) return fail(GQA_AV_ERR_UNSUPPORTED, "output too large for the split-C combine");
+        hipLaunchKernelGGL(gqa_av::av_pass2_combine, dim3(static_cast<uint32_t>(blocks)), dim3(gqa_av::kThreads),
+                           0, s, static_cast<const float*>(part), out, plane, a.nsplit);
+        e = hipGetLastError();
+        if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "pass-2 launch: %s", hipGetErrorString(e));
+    }
+    return GQA_AV_OK;
+}
+
+int gqa_av_decode(const float* attn, const void* V, float* out, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
+                  int64_t D, int v_dtype, int mode, void* stream) {
+    int rc = check_sizes(B, C, Hq, Hkv, D, v_dtype);
+    if (rc != GQA_AV_OK) return rc;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    int cus = kDefaultCUs;
+    rc = device_cus(dev, &cus);
+    if (rc != GQA_AV_OK) return rc;
+    gqa_av_hint h;
+    std::memset(&h, 0, sizeof h);
+    h.engine = GQA_AV_ENGINE_AUTO;
+    h.cu_count = cus;
+    // Alignment of V's address: its lowest set bit, at most 16.
+    const uintptr_t addr = reinterpret_cast<uintptr_t>(V);
+    const uintptr_t low = addr & (~addr + 1);
+    h.v_align = (addr == 0 || low >= 16) ? 16 : static_cast<int32_t>(low);
+    gqa_av_plan plan;
+    rc = plan_impl(B, C, Hq, Hkv, D, v_dtype, mode, &h, cus, &plan);
+    if (rc != GQA_AV_OK) return rc;
+    return gqa_av_decode_plan(attn, V, out, B, C, Hq, Hkv, D, v_dtype, &plan, stream);
+}
+
+const char* gqa_av_status_string(int status) {
+    switch (status) {
+    case GQA_AV_OK: return "ok";
+    case GQA_AV_ERR_INVALID_ARG: return "invalid argument";
+    case GQA_AV_ERR_INELIGIBLE: return "shape not eligible for GQA reuse (group size < 2)";
+    case GQA_AV_ERR_UNSUPPORTED: return "unsupported by this build";
+    case GQA_AV_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+const char* gqa_av_last_error(void) { return g_last_error.c_str(); }
+
+int gqa_av_release(void) {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    int prev = 0;
+    bool have_prev = hipGetDevice(&prev) == hipSuccess;
+    int status = GQA_AV_OK;
+    for (auto& kv : g_ws) {
+        Workspace& ws = kv.second;
+        if (!ws.part) continue;
+        hipError_t e = hipSetDevice(kv.first.first);
+        if (e == hipSuccess) e = hipDeviceSynchronize();
+        if (e == hipSuccess) e = hipFree(ws.part);
+        if (e != hipSuccess) status = fail(GQA_AV_ERR_HIP, "release: %s", hipGetErrorString(e));
+        ws = Workspace();
+    }
+    g_ws.clear();
+    if (have_prev) (void)hipSetDevice(prev);
+    return status;
+}
+
+}  // extern "C"

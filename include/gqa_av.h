@@ -1,0 +1,166 @@
+/*
+ * gqa_av.h -- C ABI of the MI355X (gfx950) GQA decode attention-times-V library
+ * (libgqa_av.so, built from gqa_reuse_attn_amd/csrc/).
+ *
+ * The operation (ExecuTorch PR #21063, "...GEMV" -- GQA-reuse AV coop GEMV for
+ * the Vulkan backend -- introduction): in grouped-query attention the
+ * Hq = G * Hkv query heads come in groups of G that share one KV head, and the
+ * decode step's attention-times-V product is
+ *
+ *     out[b, q_h, d] = sum_{c < C} attn[b, c, q_h] * V[b, c, kv_h, d]
+ *     kv_h           = q_h / G            (integer division)
+ *
+ * for every sequence b < B, query head q_h < Hq and d < D. The page writes it
+ * without the batch index; b indexes independent sequences of equal length C.
+ * attn holds already-normalised weights: no softmax, scale or mask is applied.
+ *
+ * Two ways to compute it, chosen by `mode` (the page's override knob, in its
+ * implementation section, with the same three values):
+ *   GQA_AV_REUSE     each V row is read once and used for all G query heads of
+ *                    its group (the page's GQA-reuse variant).
+ *   GQA_AV_PER_HEAD  each query head reads its KV head's V rows itself, so V
+ *                    is read G times (the page's per-query-head shader; kept
+ *                    as the measured baseline).
+ *   GQA_AV_AUTO      reuse when the shape is eligible (G >= 2), per-head
+ *                    otherwise (the page's dispatch bullet, without its cap of
+ *                    8 on G: any G is accepted here).
+ *
+ * Memory layout: dense, row-major, no padding or strides.
+ *   attn  [B][C][Hq]      float32
+ *   V     [B][C][Hkv][D]  float32, float16 or bfloat16 (v_dtype)
+ *   out   [B][Hq][D]      float32, fully overwritten
+ * All three are DEVICE pointers on the current HIP device, owned by the
+ * caller; the library keeps no pointer to them after a call returns.
+ * Accumulation is in float32 (fused multiply-add, round to nearest even).
+ *
+ * Asynchrony: gqa_av_decode* enqueue work on `stream` (a hipStream_t; NULL is
+ * the default stream) and return without synchronising. The buffers must stay
+ * valid until the stream has passed the call. A fault inside a kernel shows up
+ * at the caller's next synchronisation, not as a return value.
+ *
+ * Errors: every entry point returns an int status (enum gqa_av_status) and
+ * never throws. Arguments are validated before anything is launched; on an
+ * error `out` is left untouched. gqa_av_last_error() gives a one-line detail
+ * for the calling thread's last failing call.
+ *
+ * Workspace: when a plan splits the context (nsplit > 1) the library needs one
+ * block of partial sums per (tile, split) and one uint32 counter per tile
+ * (plan->workspace_bytes in total). It allocates them itself (hipMalloc) per
+ * (device, stream) in two buffers, keeps them for reuse, grows them on demand
+ * (synchronising that stream first) and frees them in gqa_av_release(). The
+ * counters are zeroed when allocated and every call leaves them at zero.
+ * Calls on different streams never share a workspace; calls on one stream are
+ * ordered by the stream.
+ *
+ * Thread safety: all entry points may be called from several host threads.
+ */
+#ifndef GQA_AV_H
+#define GQA_AV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of V. attn and out are always float32. */
+typedef enum gqa_av_dtype {
+    GQA_AV_F32 = 0,
+    GQA_AV_F16 = 1,   /* IEEE binary16 */
+    GQA_AV_BF16 = 2   /* bfloat16: the upper 16 bits of a binary32 */
+} gqa_av_dtype;
+
+/* How V is shared across the query heads of a group (see above). */
+typedef enum gqa_av_mode {
+    GQA_AV_AUTO = -1,
+    GQA_AV_PER_HEAD = 0,
+    GQA_AV_REUSE = 1
+} gqa_av_mode;
+
+typedef enum gqa_av_status {
+    GQA_AV_OK = 0,
+    GQA_AV_ERR_INVALID_ARG = 1,  /* negative/zero sizes, Hq % Hkv != 0, bad enum, null pointer */
+    GQA_AV_ERR_INELIGIBLE = 2,   /* GQA_AV_REUSE forced on a shape with G < 2 */
+    GQA_AV_ERR_UNSUPPORTED = 3,  /* valid request this build cannot run (e.g. misaligned pointer for a forced plan) */
+    GQA_AV_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
+} gqa_av_status;
+
+/* Inner-product engine of the reuse kernel. */
+typedef enum gqa_av_engine {
+    GQA_AV_ENGINE_AUTO = -1,
+    GQA_AV_ENGINE_VALU = 0,      /* per-lane fp32 FMAs, any G, any D */
+    GQA_AV_ENGINE_MFMA = 1       /* fp32 matrix-core tiles over 16 query heads */
+} gqa_av_engine;
+
+/* Optional planning hints. Zero-initialise, then set what you want to force:
+ * a value <= 0 (or -1 for enums) means "choose automatically". */
+typedef struct gqa_av_hint {
+    int32_t engine;     /* gqa_av_engine; -1 = auto */
+    int32_t nsplit;     /* number of context splits; <= 0 = auto */
+    int32_t cu_count;   /* compute units to plan for; <= 0 = the device's (decode) or 256 (make_plan) */
+    int32_t v_align;    /* byte alignment of V's base address; <= 0 = assume 16 */
+    int32_t reserved[4];
+} gqa_av_hint;
+
+/* A launch plan: what gqa_av_decode_plan will run. Produced by gqa_av_make_plan. */
+typedef struct gqa_av_plan {
+    int32_t mode;            /* resolved: GQA_AV_PER_HEAD or GQA_AV_REUSE */
+    int32_t engine;          /* resolved gqa_av_engine */
+    int32_t heads_per_tile;  /* query heads one workgroup computes (reuse: VALU 1-4, 8 or 16; MFMA 16 or 32; per-head: 1) */
+    int32_t subgroups;       /* workgroups that share one KV head's rows (ceil(G / heads_per_tile)) */
+    int32_t vec_bytes;       /* bytes of V each lane loads per row (VALU: 16, 8, 4, 2; MFMA: D/16 elements) */
+    int32_t lanes_per_row;   /* lanes covering one D-row of V inside a workgroup */
+    int32_t row_slots;       /* rows a workgroup loads side by side */
+    int32_t d_tiles;         /* workgroups along D */
+    int32_t nsplit;          /* context splits (1 = no partial sums) */
+    int32_t threads;         /* threads per workgroup */
+    int64_t rows_per_split;  /* context rows per split (last split may be shorter) */
+    int64_t grid;            /* workgroups launched by the first kernel */
+    int64_t workspace_bytes; /* device workspace the plan needs (0 if nsplit == 1) */
+    int64_t v_bytes_read;    /* V bytes the plan reads from memory (G x more for per-head) */
+    int32_t reserved[4];
+} gqa_av_plan;
+
+/* Resolve `mode` for a head shape. Host-only: needs no GPU.
+ * Returns GQA_AV_PER_HEAD or GQA_AV_REUSE (>= 0) on success, or the negated
+ * gqa_av_status on error: -GQA_AV_ERR_INVALID_ARG for Hq < 1, Hkv < 1,
+ * Hq % Hkv != 0 or an unknown mode; -GQA_AV_ERR_INELIGIBLE for GQA_AV_REUSE
+ * with G = Hq / Hkv < 2 (the page checks forced reuse against eligibility). */
+int gqa_av_resolve_mode(int64_t Hq, int64_t Hkv, int mode);
+
+/* Build the launch plan for a problem. Host-only: needs no GPU.
+ * hint may be NULL. Returns a gqa_av_status; fills *plan on success. */
+int gqa_av_make_plan(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D,
+                     int v_dtype, int mode, const gqa_av_hint *hint, gqa_av_plan *plan);
+
+/* out = attn x V as defined above, with an automatic plan for the current
+ * device. Sizes: B >= 0, C >= 0, Hq >= 1, Hkv >= 1, D >= 1, Hq % Hkv == 0.
+ * C == 0 writes zeros (empty sum); B == 0 does nothing. Pointers may be NULL
+ * only when B * Hq * D == 0. attn and out must be 4-byte aligned; V needs only
+ * its element alignment (the plan narrows its loads to what V allows). */
+int gqa_av_decode(const float *attn, const void *V, float *out,
+                  int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D,
+                  int v_dtype, int mode, void *stream);
+
+/* Same, with an explicit plan from gqa_av_make_plan for the same sizes, dtype
+ * and mode. Returns GQA_AV_ERR_INVALID_ARG if the plan does not match the
+ * problem and GQA_AV_ERR_UNSUPPORTED if V is not aligned to plan->vec_bytes. */
+int gqa_av_decode_plan(const float *attn, const void *V, float *out,
+                       int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D,
+                       int v_dtype, const gqa_av_plan *plan, void *stream);
+
+/* Static description of a status code. */
+const char *gqa_av_status_string(int status);
+
+/* Detail of the calling thread's last failing call ("" if none). */
+const char *gqa_av_last_error(void);
+
+/* Free every cached workspace, after synchronising the devices that hold one.
+ * Returns a gqa_av_status. Safe to call at any time; later calls allocate again. */
+int gqa_av_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_AV_H */

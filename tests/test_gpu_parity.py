@@ -1,0 +1,268 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Every test here needs an MI355X and the built libgqa_av.so; all are marked
+``gpu``. Inputs are seeded and synthetic (workloads.py). The comparison is the
+acceptance gate of tests/parity.py (max-abs for fp32 V, relative L2 for
+bf16/fp16 V) plus the fp32-accumulation bound.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import gqa_reuse_attn_amd as ga
+from tests.parity import assert_parity, gate, rel_l2
+from workloads import WORKLOADS, Workload, make_inputs, make_random
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _say(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ga.load()
+    yield
+    torch.cuda.synchronize()
+    ga.release()
+
+
+def _run(attn, V, mode="auto", plan=None, out=None):
+    a = attn.to(DEV)
+    v = V.to(DEV)
+    o = ga.gqa_av_decode(a, v, out=out, mode=mode, plan=plan)
+    torch.cuda.synchronize()
+    return o.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("wname", list(WORKLOADS))
+@pytest.mark.parametrize("mode", ["auto", "per_head"])
+def test_workload_full_size(wname, mode, oracle_lib):
+    """Full-size decode workloads, in the plan the bench times (auto) and per-head."""
+    w = WORKLOADS[wname]
+    _say(f"[parity] {wname} mode={mode}")
+    attn, V = make_inputs(w, seed=0)
+    ref = oracle_lib.full(attn, V, w.v_dtype)
+    plan = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, mode,
+                        cu_count=torch.cuda.get_device_properties(0).multi_processor_count)
+    out = _run(attn, V, mode)
+    assert_parity(out, ref, w.v_dtype, w.C, f"{wname}/{mode} plan={plan.as_dict()}")
+    _say(f"[parity] {wname} mode={mode} relL2={rel_l2(out, ref):.2e} nsplit={plan.nsplit}")
+
+
+def _sweep_cases():
+    Gs = [1, 2, 3, 4, 5, 7, 8, 9, 12, 16, 17, 32]
+    Ds = [64, 96, 128, 256]
+    Cs = [1, 2, 63, 64, 65, 1000]
+    dts = ["bf16", "f16", "f32"]
+    cases = []
+    k = 0
+    for G in Gs:
+        for C in Cs:
+            D = Ds[k % len(Ds)]
+            dt = dts[k % len(dts)]
+            Hkv = 1 + (k % 3)
+            ns = [1, 2, 7, 0, 10 ** 6][k % 5]      # 0 = automatic, 10**6 = one row per split
+            cases.append((2, C, G * Hkv, Hkv, D, dt, ns))
+            k += 1
+    return cases
+
+
+def _plans(B, C, Hq, Hkv, D, dt, ns):
+    """The automatic plan, per-head, and each reuse engine that can take the shape."""
+    plans = [("auto", ga.make_plan(B, C, Hq, Hkv, D, dt, "auto", nsplit=ns))]
+    if Hq // Hkv >= 2:
+        plans.append(("per_head", ga.make_plan(B, C, Hq, Hkv, D, dt, "per_head", nsplit=ns)))
+        for eng in ("valu", "mfma"):
+            try:
+                plans.append((eng, ga.make_plan(B, C, Hq, Hkv, D, dt, "reuse", engine=eng, nsplit=ns)))
+            except ga.GqaAvError as e:
+                assert e.name == "UNSUPPORTED"
+    return plans
+
+
+@pytest.mark.parametrize("B,C,Hq,Hkv,D,dt,ns", _sweep_cases())
+def test_sweep_small(B, C, Hq, Hkv, D, dt, ns, oracle_lib):
+    """Small shapes: G from 1 to 32, ragged C, several D, dtypes, forced splits, both engines."""
+    attn, V = make_random(B, C, Hq, Hkv, D, dt, seed=B * 1000 + C + Hq, attn_kind="signed")
+    ref = oracle_lib.full(attn, V, dt)
+    scale = np.abs(attn.double().numpy()).sum(1).max() * np.abs(V.double().numpy()).max()
+    for name, plan in _plans(B, C, Hq, Hkv, D, dt, ns):
+        out = _run(attn, V, plan=plan)
+        ok, msg = gate(out, ref, dt)
+        assert ok, f"{(B, C, Hq, Hkv, D, dt, name)} plan={plan.as_dict()}: {msg}"
+        # signed weights cancel; hold the elementwise error to fp32 accumulation
+        assert np.abs(out - ref).max() <= 4 * C * 2.0 ** -24 * scale + 1e-30, \
+            f"{(B, C, Hq, Hkv, D, dt, name)} plan={plan.as_dict()}"
+
+
+@pytest.mark.parametrize("wname,engine", [
+    ("llama3-8b-b1-c4096-hq32-hkv8-d128-bf16", "mfma"),
+    ("g2-b4-c32768-hq16-hkv8-d128-bf16", "mfma"),
+    ("mqa16-b4-c32768-hq16-hkv1-d128-bf16", "valu"),
+    ("batch64-b64-c8192-hq64-hkv8-d128-bf16", "valu"),
+])
+def test_workload_other_engine(wname, engine, oracle_lib):
+    """Full-size workloads on the engine the automatic plan does not pick."""
+    w = WORKLOADS[wname]
+    _say(f"[parity] {wname} engine={engine}")
+    attn, V = make_inputs(w, seed=0)
+    ref = oracle_lib.full(attn, V, w.v_dtype)
+    plan = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, "reuse", engine=engine,
+                        cu_count=torch.cuda.get_device_properties(0).multi_processor_count)
+    out = _run(attn, V, plan=plan)
+    assert_parity(out, ref, w.v_dtype, w.C, f"{wname}/{engine} plan={plan.as_dict()}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_one_hot_is_exact(dt):
+    """One-hot weights return the selected V row bit for bit, through splits too."""
+    B, C, Hq, Hkv, D = 2, 777, 12, 3, 128
+    _, V = make_random(B, C, Hq, Hkv, D, dt, seed=5)
+    attn = torch.zeros(B, C, Hq)
+    G = Hq // Hkv
+    sel = {}
+    for b in range(B):
+        for q in range(Hq):
+            c = (97 * b + 31 * q + 13) % C
+            attn[b, c, q] = 1.0
+            sel[b, q] = c
+    Vd = V.to(torch.float32).numpy()
+    for mode, ns, eng in (("auto", 0, "auto"), ("auto", 5, "auto"), ("per_head", 3, "auto"), ("auto", 1, "auto"),
+                          ("reuse", 0, "mfma"), ("reuse", 4, "mfma"), ("reuse", 1, "mfma")):
+        plan = ga.make_plan(B, C, Hq, Hkv, D, dt, mode, nsplit=ns, engine=eng)
+        out = _run(attn, V, plan=plan).astype(np.float32)
+        for (b, q), c in sel.items():
+            assert np.array_equal(out[b, q], Vd[b, c, q // G]), (mode, ns, b, q)
+
+
+def test_deterministic_run_to_run():
+    w = WORKLOADS["mqa16-b4-c32768-hq16-hkv1-d128-bf16"]
+    attn, V = make_inputs(w, seed=1)
+    a, v = attn.to(DEV), V.to(DEV)
+    outs = [ga.gqa_av_decode(a, v).cpu() for _ in range(3)]
+    torch.cuda.synchronize()
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+
+
+def test_zero_context_writes_zeros():
+    B, Hq, Hkv, D = 3, 8, 2, 128
+    attn = torch.zeros(B, 0, Hq, device=DEV)
+    V = torch.zeros(B, 0, Hkv, D, dtype=torch.bfloat16, device=DEV)
+    out = torch.full((B, Hq, D), float("nan"), device=DEV)
+    ga.gqa_av_decode(attn, V, out=out)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0
+
+
+def test_zero_batch_is_noop():
+    attn = torch.zeros(0, 16, 8, device=DEV)
+    V = torch.zeros(0, 16, 2, 64, dtype=torch.float16, device=DEV)
+    out = ga.gqa_av_decode(attn, V)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 8, 64)
+
+
+@pytest.mark.parametrize("B,C,Hq,Hkv,D,dt", [
+    (1, 300, 4, 2, 127, "bf16"),     # odd D: 2-byte loads
+    (2, 129, 6, 3, 1, "f16"),        # D = 1
+    (1, 200, 1, 1, 64, "f32"),       # Hq = Hkv = 1
+    (2, 150, 64, 1, 64, "bf16"),     # G = 64: four sub-groups of 16
+    (1, 90, 4, 2, 2048, "f32"),      # D-row of 8 KB: two D-tiles
+    (3, 257, 10, 5, 80, "f16"),      # D = 80
+])
+def test_edge_shapes(B, C, Hq, Hkv, D, dt, oracle_lib):
+    attn, V = make_random(B, C, Hq, Hkv, D, dt, seed=C + D, attn_kind="softmax")
+    ref = oracle_lib.full(attn, V, dt)
+    for mode in (["auto", "per_head"] if Hq // Hkv >= 2 else ["auto"]):
+        out = _run(attn, V, mode)
+        assert_parity(out, ref, dt, C, f"{(B, C, Hq, Hkv, D, dt, mode)}")
+
+
+def test_misaligned_v_narrows_loads(oracle_lib):
+    """V starting 2 bytes past a 16-byte boundary still works (auto plan uses 2-byte loads)."""
+    B, C, Hq, Hkv, D = 2, 333, 8, 2, 128
+    attn, V = make_random(B, C, Hq, Hkv, D, "bf16", seed=9)
+    ref = oracle_lib.full(attn, V, "bf16")
+    buf = torch.empty(V.numel() + 8, dtype=torch.bfloat16, device=DEV)
+    v_off = buf[1:1 + V.numel()].view(B, C, Hkv, D)
+    v_off.copy_(V.to(DEV))
+    assert v_off.data_ptr() % 16 == 2
+    out = ga.gqa_av_decode(attn.to(DEV), v_off)
+    torch.cuda.synchronize()
+    assert_parity(out.cpu().numpy().astype(np.float64), ref, "bf16", C, "misaligned V")
+    # a forced 16-byte plan on that pointer is refused, not run
+    plan = ga.make_plan(B, C, Hq, Hkv, D, "bf16")
+    with pytest.raises(ga.GqaAvError) as ei:
+        ga.gqa_av_decode(attn.to(DEV), v_off, plan=plan)
+    assert ei.value.name == "UNSUPPORTED"
+
+
+def test_side_stream_and_reuse_of_out(oracle_lib):
+    w = WORKLOADS["llama3-8b-b1-c4096-hq32-hkv8-d128-bf16"]
+    attn, V = make_inputs(w, seed=3)
+    ref = oracle_lib.full(attn, V, w.v_dtype)
+    s = torch.cuda.Stream()
+    a, v = attn.to(DEV), V.to(DEV)
+    out = torch.full((w.B, w.Hq, w.D), 7.0, device=DEV)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            ga.gqa_av_decode(a, v, out=out)
+    s.synchronize()
+    assert_parity(out.cpu().numpy().astype(np.float64), ref, w.v_dtype, w.C, "side stream")
+
+
+def test_bf16_rounded_weights_would_fail_accumulation_bound(oracle_lib):
+    """The extra fp32-accumulation check catches what the 2e-3 gate lets through."""
+    w = WORKLOADS["g2-b4-c32768-hq16-hkv8-d128-bf16"]
+    attn, V = make_inputs(w.replace(B=1), seed=0)
+    ref = oracle_lib.full(attn, V, w.v_dtype)
+    rounded = attn.to(torch.bfloat16).to(torch.float32)
+    out = _run(rounded, V)
+    ok, _ = gate(out, ref, w.v_dtype)
+    assert ok                                  # the official gate passes it ...
+    with pytest.raises(AssertionError):
+        assert_parity(out, ref, w.v_dtype, w.C)  # ... the accumulation bound does not
+
+
+def test_workspace_reuse_across_plans(oracle_lib):
+    """Plans with different tile counts share one cached workspace: each must find
+    its split counters at zero, whatever partial sums the previous plans wrote."""
+    shapes = [(4, 3000, 64, 8, 128, "bf16", "auto"),     # large workspace first
+              (1, 3000, 8, 2, 128, "bf16", "per_head"),  # few tiles, many partials
+              (2, 3000, 24, 8, 96, "f16", "per_head"),   # more tiles than the previous call
+              (1, 3000, 32, 2, 128, "bf16", "auto"),
+              (3, 3000, 12, 4, 64, "f32", "per_head")]
+    cases = []
+    for k, (B, C, Hq, Hkv, D, dt, mode) in enumerate(shapes):
+        attn, V = make_random(B, C, Hq, Hkv, D, dt, seed=300 + k)
+        cases.append((attn, V, dt, C, mode, oracle_lib.full(attn, V, dt)))
+    for rnd in range(2):
+        for attn, V, dt, C, mode, ref in cases:
+            plan = ga.make_plan(*attn.shape[:2], attn.shape[2], V.shape[2], V.shape[3], dt, mode, nsplit=9)
+            out = _run(attn, V, plan=plan)
+            assert_parity(out, ref, dt, C, f"round {rnd} {tuple(V.shape)} {mode} plan={plan.as_dict()}")
+
+
+def test_bound_call_matches_decode(oracle_lib):
+    w = WORKLOADS["llama3-8b-b1-c4096-hq32-hkv8-d128-bf16"]
+    attn, V = make_inputs(w, seed=4)
+    ref = oracle_lib.full(attn, V, w.v_dtype)
+    a, v = attn.to(DEV), V.to(DEV)
+    call = ga.bind(a, v)
+    for _ in range(3):
+        out = call()
+    torch.cuda.synchronize()
+    assert_parity(out.cpu().numpy().astype(np.float64), ref, w.v_dtype, w.C, "bound call")
+    assert torch.equal(out, ga.gqa_av_decode(a, v))

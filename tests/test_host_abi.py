@@ -1,0 +1,250 @@
+"""CPU tests of the C ABI: the library loads, exports what the header declares,
+and its host-only logic (mode resolution, planning, argument checks) behaves.
+No kernel is launched here.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import gqa_reuse_attn_amd as ga
+from workloads import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa_av.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gqa_av_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = ga.load()
+    names = declared_functions()
+    assert len(names) >= 7, names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in gqa_av.h but not exported"
+
+
+def test_exports_are_c_symbols():
+    # extern "C": no mangled gqa_av names in the dynamic symbol table
+    out = os.popen(f"nm -D --defined-only {ga.LIB_PATH}").read()
+    exported = set(re.findall(r"\s(gqa_av_\w+)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
+
+
+@pytest.mark.parametrize("Hq,Hkv,mode,expect", [
+    (32, 8, "auto", "reuse"),          # Llama-style G=4
+    (24, 8, "auto", "reuse"),          # G=3
+    (16, 8, "auto", "reuse"),          # G=2
+    (16, 1, "auto", "reuse"),          # MQA G=16: the page's cap of 8 is not kept
+    (64, 1, "auto", "reuse"),          # G=64
+    (8, 1, "auto", "reuse"),           # low-ratio MQA
+    (8, 8, "auto", "per_head"),        # MHA
+    (1, 1, "auto", "per_head"),
+    (32, 8, "per_head", "per_head"),   # forced per-head always runs
+    (8, 8, "per_head", "per_head"),
+    (32, 8, "reuse", "reuse"),
+])
+def test_resolve_mode(Hq, Hkv, mode, expect):
+    assert ga.resolve_mode(Hq, Hkv, mode) == expect
+
+
+@pytest.mark.parametrize("Hq,Hkv,mode,status", [
+    (8, 8, "reuse", "INELIGIBLE"),     # forced reuse with G = 1
+    (1, 1, "reuse", "INELIGIBLE"),
+    (12, 8, "auto", "INVALID_ARG"),    # not divisible
+    (12, 8, "per_head", "INVALID_ARG"),
+    (0, 1, "auto", "INVALID_ARG"),
+    (8, 0, "auto", "INVALID_ARG"),
+    (8, 2, 5, "INVALID_ARG"),          # unknown mode
+    (8, 2, -2, "INVALID_ARG"),
+])
+def test_resolve_mode_errors(Hq, Hkv, mode, status):
+    with pytest.raises(ga.GqaAvError) as ei:
+        ga.resolve_mode(Hq, Hkv, mode)
+    assert ei.value.name == status
+    assert str(ei.value)
+
+
+def _check_plan(p, B, C, Hq, Hkv, D, v_dtype, mode):
+    es = 4 if v_dtype == "f32" else 2
+    G = Hq // Hkv
+    assert p.threads == 256
+    if p.engine == 1:                                   # MFMA: 16 lanes x D/16 elements per row
+        assert p.mode == 1 and D % 16 == 0
+        assert p.vec_bytes == D // 16 * es and p.lanes_per_row == 16 and p.row_slots == 16 and p.d_tiles == 1
+        assert p.heads_per_tile in (16, 32)
+    else:
+        assert p.vec_bytes in (16, 8, 4, 2) and (D * es) % p.vec_bytes == 0 and p.vec_bytes >= es
+        L = D * es // p.vec_bytes
+        assert p.lanes_per_row == min(L, 256)
+        assert p.d_tiles == -(-L // p.lanes_per_row)
+        assert p.row_slots == min(256 // p.lanes_per_row, 64)
+    if C == 0:
+        assert p.nsplit == 1
+    else:
+        assert p.nsplit >= 1 and p.rows_per_split >= 1
+        assert -(-C // p.rows_per_split) == p.nsplit       # splits tile [0, C) exactly
+    if p.mode == 1:
+        assert p.heads_per_tile >= min(G, 16) and p.subgroups == -(-G // p.heads_per_tile)
+        tiles = B * Hkv * p.subgroups * p.d_tiles
+        assert p.v_bytes_read == B * C * Hkv * D * es * p.subgroups
+    else:
+        assert p.heads_per_tile == 1
+        tiles = B * Hq * p.d_tiles
+        assert p.v_bytes_read == B * C * Hkv * D * es * G
+    assert p.grid == tiles * p.nsplit
+    assert p.workspace_bytes == (p.nsplit * B * Hq * D * 4 if p.nsplit > 1 else 0)
+
+
+@pytest.mark.parametrize("wname", list(WORKLOADS))
+@pytest.mark.parametrize("mode", ["auto", "per_head"])
+def test_plan_for_workloads(wname, mode):
+    w = WORKLOADS[wname]
+    p = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, mode)
+    _check_plan(p, w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, mode)
+    assert p.vec_bytes == 16                         # every decode workload allows 16-byte loads
+    if mode == "auto":
+        assert p.mode == 1                           # all six have G >= 2
+        assert p.v_bytes_read == w.v_bytes()         # V read once
+    else:
+        assert p.v_bytes_read == w.G * w.v_bytes()
+
+
+@pytest.mark.parametrize("B,C,Hq,Hkv,D,dt", [
+    (1, 1, 1, 1, 1, "bf16"), (2, 0, 4, 2, 8, "f16"), (0, 10, 4, 2, 8, "f32"), (3, 1000, 40, 2, 96, "bf16"),
+    (1, 77, 17, 1, 3, "f16"), (2, 65, 9, 3, 2000, "f32"), (1, 5000, 64, 2, 256, "bf16"), (4, 3, 6, 6, 5, "f32"),
+])
+def test_plan_edges(B, C, Hq, Hkv, D, dt):
+    for mode in ("auto", "per_head"):
+        p = ga.make_plan(B, C, Hq, Hkv, D, dt, mode)
+        _check_plan(p, B, C, Hq, Hkv, D, dt, mode)
+
+
+@pytest.mark.parametrize("nsplit", [1, 2, 7, 64, 10 ** 6])
+def test_forced_nsplit(nsplit):
+    C = 1000
+    p = ga.make_plan(2, C, 8, 2, 128, "bf16", "auto", nsplit=nsplit)
+    assert p.nsplit <= min(nsplit, C)
+    assert -(-C // p.rows_per_split) == p.nsplit
+    if nsplit <= 64:
+        assert p.nsplit == nsplit or C % nsplit != 0
+
+
+def test_alignment_narrows_loads():
+    assert ga.make_plan(1, 64, 8, 2, 128, "bf16", v_align=16).vec_bytes == 16
+    assert ga.make_plan(1, 64, 8, 2, 128, "bf16", v_align=8).vec_bytes == 8
+    assert ga.make_plan(1, 64, 8, 2, 128, "bf16", v_align=2).vec_bytes == 2
+    assert ga.make_plan(1, 64, 8, 2, 127, "bf16").vec_bytes == 2     # odd D
+    assert ga.make_plan(1, 64, 8, 2, 6, "bf16").vec_bytes == 4       # 12-byte rows
+    assert ga.make_plan(1, 64, 8, 2, 3, "f32").vec_bytes == 4
+    with pytest.raises(ga.GqaAvError) as ei:
+        ga.make_plan(1, 64, 8, 2, 64, "f32", v_align=2)
+    assert ei.value.name == "UNSUPPORTED"
+
+
+def test_large_groups_use_subgroups():
+    p = ga.make_plan(1, 4096, 40, 1, 128, "bf16", engine="valu")
+    assert p.mode == 1 and p.heads_per_tile == 16 and p.subgroups == 3
+    p = ga.make_plan(1, 4096, 40, 1, 128, "bf16")
+    assert p.mode == 1 and p.engine == 1 and p.heads_per_tile == 32 and p.subgroups == 2
+
+
+@pytest.mark.parametrize("args,status", [
+    ((-1, 4, 8, 2, 16, "bf16"), "INVALID_ARG"),
+    ((1, -4, 8, 2, 16, "bf16"), "INVALID_ARG"),
+    ((1, 4, 8, 2, 0, "bf16"), "INVALID_ARG"),
+    ((1, 4, 9, 2, 16, "bf16"), "INVALID_ARG"),
+])
+def test_plan_errors(args, status):
+    with pytest.raises(ga.GqaAvError) as ei:
+        ga.make_plan(*args)
+    assert ei.value.name == status
+
+
+def test_unknown_dtype_and_engine():
+    lib = ga.load()
+    p = ga.Plan()
+    assert lib.gqa_av_make_plan(1, 4, 8, 2, 16, 7, -1, None, ctypes.byref(p)) == 1
+    h = ga.Hint(); h.engine = 9
+    assert lib.gqa_av_make_plan(1, 4, 8, 2, 16, 2, -1, ctypes.byref(h), ctypes.byref(p)) == 1
+
+
+def test_decode_plan_rejects_before_launch():
+    """Argument errors are returned before any HIP call (so this runs without a GPU)."""
+    lib = ga.load()
+    B, C, Hq, Hkv, D = 2, 100, 8, 2, 128
+    p = ga.make_plan(B, C, Hq, Hkv, D, "bf16")
+    fake = ctypes.c_void_p(1 << 20)
+    # a plan for another problem
+    assert lib.gqa_av_decode_plan(fake, fake, fake, B, C + 5000, Hq, Hkv, D, 2, ctypes.byref(p), None) == 1
+    bad = ga.Plan.from_buffer_copy(p); bad.grid += 1
+    assert lib.gqa_av_decode_plan(fake, fake, fake, B, C, Hq, Hkv, D, 2, ctypes.byref(bad), None) == 1
+    bad = ga.Plan.from_buffer_copy(p); bad.rows_per_split = 1
+    assert lib.gqa_av_decode_plan(fake, fake, fake, B, C, Hq, Hkv, D, 2, ctypes.byref(bad), None) == 1
+    # null and misaligned pointers
+    assert lib.gqa_av_decode_plan(None, fake, fake, B, C, Hq, Hkv, D, 2, ctypes.byref(p), None) == 1
+    assert lib.gqa_av_decode_plan(fake, fake, None, B, C, Hq, Hkv, D, 2, ctypes.byref(p), None) == 1
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    assert lib.gqa_av_decode_plan(odd, fake, fake, B, C, Hq, Hkv, D, 2, ctypes.byref(p), None) == 1
+    assert lib.gqa_av_decode_plan(fake, odd, fake, B, C, Hq, Hkv, D, 2, ctypes.byref(p), None) == 3
+    assert "aligned" in ga.load().gqa_av_last_error().decode()
+    # B == 0 is a no-op that needs no device
+    p0 = ga.make_plan(0, C, Hq, Hkv, D, "bf16")
+    assert lib.gqa_av_decode_plan(None, None, None, 0, C, Hq, Hkv, D, 2, ctypes.byref(p0), None) == 0
+    assert lib.gqa_av_decode_plan(fake, fake, fake, B, C, Hq, Hkv, D, 2, None, None) == 1
+
+
+def test_status_strings():
+    for s in range(5):
+        assert ga.status_string(s)
+    assert ga.status_string(99) == "unknown status"
+
+
+def test_product_path_does_not_touch_the_oracle():
+    pkg = os.path.join(ROOT, "gqa_reuse_attn_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, flags=re.M), f
+                assert "gqa_av_oracle" not in text, f
+    deps = os.popen(f"ldd {ga.LIB_PATH} 2>/dev/null").read()
+    assert "oracle" not in deps
+
+
+@pytest.mark.parametrize("wname,engine", [
+    ("tiny-f32-b1-c256-hq8-hkv2-d64", 0), ("llama3-8b-b1-c4096-hq32-hkv8-d128-bf16", 0),
+    ("g3-b8-c16384-hq24-hkv8-d96-f16", 0), ("g2-b4-c32768-hq16-hkv8-d128-bf16", 0),
+    ("mqa16-b4-c32768-hq16-hkv1-d128-bf16", 1), ("batch64-b64-c8192-hq64-hkv8-d128-bf16", 1),
+])
+def test_auto_engine(wname, engine):
+    """Groups of 5 or more heads take the matrix-core engine, smaller ones the VALU engine."""
+    w = WORKLOADS[wname]
+    assert ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype).engine == engine
+    assert ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, "per_head").engine == 0
+
+
+def test_forced_engines():
+    p = ga.make_plan(1, 300, 4, 2, 128, "bf16", engine="mfma")          # G = 2 on MFMA: allowed
+    assert p.engine == 1 and p.heads_per_tile == 16 and p.subgroups == 1
+    _check_plan(p, 1, 300, 4, 2, 128, "bf16", "auto")
+    p = ga.make_plan(1, 300, 64, 1, 128, "bf16")                        # G = 64: 32-head sets
+    assert p.engine == 1 and p.heads_per_tile == 32 and p.subgroups == 2
+    p = ga.make_plan(1, 300, 64, 1, 256, "bf16")                        # D = 256: 16-head sets
+    assert p.engine == 1 and p.heads_per_tile == 16 and p.subgroups == 4
+    assert ga.make_plan(1, 300, 16, 1, 128, "bf16", engine="valu").engine == 0
+    for args, kw in [((1, 300, 16, 1, 127, "bf16"), {}), ((1, 300, 16, 1, 128, "bf16", "per_head"), {}),
+                     ((1, 300, 16, 1, 96, "f32"), {}), ((1, 300, 16, 1, 128, "bf16"), {"v_align": 8})]:
+        with pytest.raises(ga.GqaAvError) as ei:
+            ga.make_plan(*args, engine="mfma", **kw)
+        assert ei.value.name == "UNSUPPORTED"
+    # without the engine forced, shapes the MFMA engine cannot take fall back to VALU
+    assert ga.make_plan(1, 300, 16, 1, 127, "bf16").engine == 0
+    assert ga.make_plan(1, 300, 16, 1, 128, "bf16", v_align=8).engine == 0

@@ -18,7 +18,8 @@ __all__ = [
     "gqa_av_decode", "gqa_av_decode_plan", "bind", "BoundCall", "release", "status_string", "MODES", "DTYPES",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_av.so")
+# GQA_AV_LIBRARY may name another build of the same library (tuning variants).
+LIB_PATH = os.environ.get("GQA_AV_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_av.so")
 
 MODES = {"auto": -1, "per_head": 0, "reuse": 1}
 ENGINES = {"auto": -1, "valu": 0, "mfma": 1}

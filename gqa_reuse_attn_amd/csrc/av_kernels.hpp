@@ -42,6 +42,24 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kXcds = 8;          // MI355X: 8 accelerator complex dies, one L2 each
 constexpr int kMaxRowSlots = 64;  // rows a VALU workgroup loads side by side, at most
 
+// Tuning constants (compile-time; -D overrides build variants for sweeps).
+#ifndef GQA_AV_VALU_UNROLL
+#define GQA_AV_VALU_UNROLL 8      // rows per lane per stage, groups of up to 4 heads
+#endif
+#ifndef GQA_AV_VALU_PIPELINE
+#define GQA_AV_VALU_PIPELINE 0    // staged weights only: next stage's loads in flight during the current one
+#endif
+#ifndef GQA_AV_VALU_STAGE_WEIGHTS
+#define GQA_AV_VALU_STAGE_WEIGHTS 0  // 1: weights staged in LDS per stage; 0: each lane loads its row's weights
+#endif
+#ifndef GQA_AV_MFMA_UNROLL
+#define GQA_AV_MFMA_UNROLL 4      // row groups of four per wave and step (16-byte lanes)
+#endif
+constexpr int valu_unroll(int GT) {
+    return GT <= 4 ? GQA_AV_VALU_UNROLL : (GT <= 8 ? (GQA_AV_VALU_UNROLL + 1) / 2 : (GQA_AV_VALU_UNROLL + 3) / 4);
+}
+constexpr int mfma_unroll(int NB) { return NB > 16 ? (GQA_AV_MFMA_UNROLL + 1) / 2 : GQA_AV_MFMA_UNROLL; }
+
 enum : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
 template <int DT>
@@ -195,11 +213,15 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
     constexpr int E = VB / ES;
     constexpr int NACC = GT * E;
     constexpr int CH = NACC < 32 ? NACC : 32;       // accumulator slots per LDS reduction pass
+    constexpr int RED = CH * kThreads;
+#if GQA_AV_VALU_STAGE_WEIGHTS
     constexpr int GP = padded_heads<GT>();
     constexpr int RMAX = kMaxRowSlots * U;           // rows per stage is rps * U
     constexpr int WBUF = 2 * RMAX * GP;              // staged weights, double-buffered (worst case)
-    constexpr int RED = CH * kThreads;
     constexpr int SMEM = WBUF > RED ? WBUF : RED;
+#else
+    constexpr int SMEM = RED;
+#endif
     __shared__ float smem[SMEM];
 
     const Tile T = decode_tile(a, GT);
@@ -213,18 +235,22 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
     const int64_t cb = static_cast<int64_t>(T.s) * a.rows_per_split;
     const int64_t ce = min(a.C, cb + a.rows_per_split);
     const int R = rps * U;                           // rows per stage
-    const int64_t nstage = ce > cb ? (ce - cb + R - 1) / R : 0;
 
     const size_t vrow = static_cast<size_t>(a.Hkv) * a.D * ES;   // bytes from row c to c+1
     const uint8_t* vbase = a.V + (static_cast<size_t>(T.b) * a.C * a.Hkv + T.kv) * a.D * ES
                                + static_cast<size_t>(lane_d) * VB;
-    const float* abase = a.attn + static_cast<size_t>(T.b) * a.C * a.Hq + T.q_first;
 
     float acc[GT][E];
 #pragma unroll
     for (int g = 0; g < GT; ++g)
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[g][e] = 0.0f;
+
+#if GQA_AV_VALU_STAGE_WEIGHTS
+    const int q_lo = T.q_first;                      // accumulator g is head q_lo + g
+    const int g_off = 0;
+    const float* abase = a.attn + static_cast<size_t>(T.b) * a.C * a.Hq + T.q_first;
+    const int64_t nstage = ce > cb ? (ce - cb + R - 1) / R : 0;
 
     // Weight staging: element k of a stage is (row i = k / GT, head g = k % GT).
     const int nstage_elems = R * GT;
@@ -288,13 +314,17 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
 
     // Software pipeline over stages: the next stage's V rows and weights are in
     // flight while the current stage is computed. Stage st uses weight buffer st & 1.
-    Raw<VB> rA[U], rB[U];
+    Raw<VB> rA[U];
+#if GQA_AV_VALU_PIPELINE
+    Raw<VB> rB[U];
+#endif
     if (nstage > 0) {
         load_v(rA, cb);
         stage_load(cb);
         stage_store(0);
     }
     __syncthreads();
+#if GQA_AV_VALU_PIPELINE
     int64_t st = 0;
     for (; st + 1 < nstage; st += 2) {
         const int64_t c1 = cb + (st + 1) * R;
@@ -313,7 +343,64 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
         __syncthreads();
     }
     if (st < nstage) compute(rA, 0);
-    __syncthreads();                                  // weight buffers are reused below
+#else
+    for (int64_t st = 0; st < nstage; ++st) {
+        const int buf = static_cast<int>(st & 1);
+        if (st > 0) load_v(rA, cb + st * R);
+        if (st + 1 < nstage) stage_load(cb + (st + 1) * R);
+        compute(rA, buf);
+        if (st + 1 < nstage) stage_store(buf ^ 1);
+        __syncthreads();
+    }
+#endif
+
+#else
+    // The tile's weights are read as a window of GT consecutive heads starting at
+    // q_lo, shifted down when the tile's last sub-group is short, so every lane
+    // loads GT words at constant offsets and the window never leaves the attn
+    // row (the planner keeps GT <= Hq). Accumulators outside the tile's own
+    // heads are computed and dropped.
+    const int q_lo = min(T.q_first, a.Hq - GT);
+    const int g_off = T.q_first - q_lo;
+    const float* wbase = a.attn + static_cast<size_t>(T.b) * a.C * a.Hq + q_lo;
+    if (active) {
+        int64_t c0 = cb;
+        for (; c0 + R <= ce; c0 += R) {
+            Raw<VB> raw[U];
+            float w[U][GT];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t c = c0 + r + u * rps;
+                raw[u] = load_raw<VB>(vbase + static_cast<size_t>(c) * vrow);
+                const float* wr = wbase + c * a.Hq;
+#pragma unroll
+                for (int g = 0; g < GT; ++g) w[u][g] = wr[g];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float f[E];
+                widen<DT, VB>(raw[u], f);
+#pragma unroll
+                for (int g = 0; g < GT; ++g)
+#pragma unroll
+                    for (int e = 0; e < E; ++e) acc[g][e] = __builtin_fmaf(w[u][g], f[e], acc[g][e]);
+            }
+        }
+        for (int64_t c = c0 + r; c < ce; c += rps) {
+            const Raw<VB> raw = load_raw<VB>(vbase + static_cast<size_t>(c) * vrow);
+            const float* wr = wbase + c * a.Hq;
+            float f[E];
+            widen<DT, VB>(raw, f);
+#pragma unroll
+            for (int g = 0; g < GT; ++g) {
+                const float wg = wr[g];
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[g][e] = __builtin_fmaf(wg, f[e], acc[g][e]);
+            }
+        }
+    }
+#endif
+    __syncthreads();                                  // LDS is reused below
 
     // Sum the row slots: slot kk of thread tid lives at smem[kk * 256 + tid].
     float* const dst = a.nsplit > 1 ? a.part + static_cast<size_t>(T.s) * a.B * a.Hq * a.D : a.out;
@@ -333,8 +420,8 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
             const int k = k0 + kk;
             const int g = k / E, e = k - (k / E) * E;
             const int ld = T.dt * Lc + jj;
-            if (g < T.nq && ld < a.L)
-                dst[(static_cast<size_t>(T.b) * a.Hq + T.q_first + g) * a.D + static_cast<size_t>(ld) * E + e] = sum;
+            if (g >= g_off && g < g_off + T.nq && ld < a.L)
+                dst[(static_cast<size_t>(T.b) * a.Hq + q_lo + g) * a.D + static_cast<size_t>(ld) * E + e] = sum;
         }
         __syncthreads();
     }

@@ -41,15 +41,15 @@ int elem_bytes(int dt) { return dt == GQA_AV_F32 ? 4 : 2; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Compile-time head capacity of a reuse tile for a group of G heads.
+// Compile-time head capacity of a VALU reuse tile for a group of G heads:
+// exactly G up to 8, two tiles of 8 for 9..15, tiles of 16 beyond. Never more
+// than Hq (>= G), so a tile's weight window fits inside an attn row.
 int head_capacity(int64_t G) {
-    if (G <= 4) return static_cast<int>(G);
-    if (G <= 8) return 8;
+    if (G <= 8) return static_cast<int>(G);
+    if (G < 16) return 8;
     return 16;
 }
 
-// Unroll depth: rows each lane keeps in flight per stage.
-int unroll_for(int GT) { return GT <= 4 ? 8 : (GT <= 8 ? 4 : 2); }
 
 constexpr int kDefaultCUs = 256;
 constexpr int64_t kMinRowsPerSplit = 256;     // below this a split's epilogue dominates
@@ -125,7 +125,7 @@ int check_sizes(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_
 
 template <int DT, int VB, int GT>
 hipError_t launch_valu(const Pass1Args& a, hipStream_t s) {
-    constexpr int U = GT <= 4 ? 8 : (GT <= 8 ? 4 : 2);
+    constexpr int U = gqa_av::valu_unroll(GT);
     hipLaunchKernelGGL((gqa_av::av_pass1_valu<DT, VB, GT, U>), dim3(a.nblocks), dim3(gqa_av::kThreads), 0, s, a);
     return hipGetLastError();
 }
@@ -137,6 +137,9 @@ hipError_t launch_valu_gt(int GT, const Pass1Args& a, hipStream_t s) {
     case 2: return launch_valu<DT, VB, 2>(a, s);
     case 3: return launch_valu<DT, VB, 3>(a, s);
     case 4: return launch_valu<DT, VB, 4>(a, s);
+    case 5: return launch_valu<DT, VB, 5>(a, s);
+    case 6: return launch_valu<DT, VB, 6>(a, s);
+    case 7: return launch_valu<DT, VB, 7>(a, s);
     case 8: return launch_valu<DT, VB, 8>(a, s);
     case 16: return launch_valu<DT, VB, 16>(a, s);
     default: return hipErrorInvalidValue;
@@ -158,7 +161,7 @@ hipError_t launch_valu_vb(int VB, int GT, const Pass1Args& a, hipStream_t s) {
 
 template <int DT, int DE, int NSET>
 hipError_t launch_mfma(const Pass1Args& a, hipStream_t s) {
-    constexpr int U = DE * gqa_av::esize<DT>() > 16 ? 2 : 4;
+    constexpr int U = gqa_av::mfma_unroll(DE * gqa_av::esize<DT>());
     hipLaunchKernelGGL((gqa_av::av_pass1_mfma<DT, DE, NSET, U>), dim3(a.nblocks), dim3(gqa_av::kThreads), 0, s, a);
     return hipGetLastError();
 }
@@ -273,7 +276,7 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
         Lc = 16;
         rps = 16;                       // 4 waves x 4 rows per MFMA
         ndt = 1;
-        rows_per_step = 4 * gqa_av::kWaves * (VB > 16 ? 2 : 4);
+        rows_per_step = 4 * gqa_av::kWaves * gqa_av::mfma_unroll(VB);
     } else {
         // Widest lane load that divides a D-row and respects V's alignment.
         VB = 0;
@@ -297,7 +300,7 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
             nsg = 1;
             heads_major = G;
         }
-        rows_per_step = rps * unroll_for(GT);
+        rows_per_step = rps * gqa_av::valu_unroll(GT);
     }
     const int64_t tiles = B * Hkv * heads_major * ndt;
 

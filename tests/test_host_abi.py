@@ -92,7 +92,8 @@ def _check_plan(p, B, C, Hq, Hkv, D, v_dtype, mode):
         assert p.nsplit >= 1 and p.rows_per_split >= 1
         assert -(-C // p.rows_per_split) == p.nsplit       # splits tile [0, C) exactly
     if p.mode == 1:
-        assert p.heads_per_tile >= min(G, 16) and p.subgroups == -(-G // p.heads_per_tile)
+        assert p.heads_per_tile >= min(G, 8) and (p.engine == 1 or p.heads_per_tile <= Hq)
+        assert p.subgroups == -(-G // p.heads_per_tile)
         tiles = B * Hkv * p.subgroups * p.d_tiles
         assert p.v_bytes_read == B * C * Hkv * D * es * p.subgroups
     else:

@@ -1,22 +1,33 @@
 """Benchmark of the GQA decode attention-times-V path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--mode auto|per_head]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--mode auto|per_head|reuse]
 
-A step is one call of the whole path (pass 1, and pass 2 when the context is
-split) over one batch of synthetic decode input already resident in HBM.
-Several copies of the inputs are rotated so that the total exceeds twice the
-256 MB Infinity Cache and every step reads V and attn from HBM.
+A step is one call of the whole path (pass 1, and the split combine when the
+context is split) over one batch of synthetic decode input already resident in
+HBM. Several copies of the inputs are rotated so that the total exceeds twice
+the 256 MB Infinity Cache and every step reads V and attn from HBM.
 
 Prints ONE JSON line: µs per call and achieved GB/s over the algorithmic bytes
-(V + attn + out, each once), the roofline fraction against 8 TB/s HBM, and the
-CPU oracle timed on this host as a baseline.
+(V + attn + out, each once); a roofline for the dominant kernel (pass 1, timed
+alone with HIP events around each of its launches on the launch stream) against
+8 TB/s HBM; and the CPU oracle timed on this host as a baseline.
+
+Other modes (measurement plumbing, no JSON line):
+    --copy-calibration MB   device-to-device copy of MB MiB three times, to scale
+                            the FETCH_SIZE / WRITE_SIZE counters
+    --summarize-trace DIR   write a kernel-trace summary from rocprofv3 CSV output
+    --summarize-pmc ...     write a traffic summary from four rocprofv3 --pmc runs
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -28,6 +39,17 @@ METRIC = "GQA decode AV: µs/call and achieved HBM GB/s (% of MI355X peak)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 ROTATE_BYTES = 512 * 2 ** 20   # 2 x the 256 MB Infinity Cache
 DEFAULT_WORKLOAD = "g2-b4-c32768-hq16-hkv8-d128-bf16"
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = [os.path.join(ROOT, "gqa_reuse_attn_amd", "csrc", f) for f in ("av_kernels.hpp", "gqa_av.hip")]
+
+
+def source_hash() -> str:
+    """SHA-256 over the kernel sources: identifies the kernels a profile was taken on."""
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def parse():
@@ -38,11 +60,107 @@ def parse():
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--mode", default="auto", choices=["auto", "per_head", "reuse"])
     p.add_argument("--nsplit", type=int, default=0, help="force the number of context splits (0 = plan)")
+    p.add_argument("--engine", default="auto", choices=["auto", "valu", "mfma"])
+    p.add_argument("--combine", default="auto", choices=["auto", "kernel", "last"],
+                   help="how split partials are added (plan default: auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle time budget")
     p.add_argument("--rotate-mb", type=float, default=ROTATE_BYTES / 2 ** 20)
+    p.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB")
+    p.add_argument("--summarize-trace", metavar="DIR")
+    p.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
+    p.add_argument("--copy-bytes", type=float, default=1024.0, help="MiB per copy in the calibration runs")
+    p.add_argument("--out", help="summary file to write (with --summarize-*)")
+    p.add_argument("--command", default="", help="the command line the summarized data came from")
     return p.parse_args()
 
+
+# ---- measurement plumbing ------------------------------------------------------
+
+def _rows(d: str, suffix: str):
+    files = glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    with open(files[0]) as fh:
+        return list(csv.DictReader(fh))
+
+
+def summarize_trace(d: str, out: str, command: str):
+    rows = _rows(d, "kernel_stats.csv")
+    lines = ["# rocprofv3 kernel trace summary", f"command: {command}", f"kernel_sources_sha256: {source_hash()}", "",
+             "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
+                     f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} | {float(r['Percentage']):.1f} |")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def _counter_medians(d: str):
+    vals = {}
+    for r in _rows(d, "counter_collection.csv"):
+        vals.setdefault((r["Kernel_Name"], r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    return {k: statistics.median(v) for k, v in vals.items()}
+
+
+def summarize_pmc(dirs, copy_mib: float, out: str, command: str):
+    fetch, write, cfetch, cwrite = (_counter_medians(d) for d in dirs)
+    copy_bytes = copy_mib * 2 ** 20
+
+    def copy_factor(m, counter):
+        vals = [v for (k, c), v in m.items() if c == counter and "copyBuffer" in k]
+        return copy_bytes / (max(vals) * 1024.0)
+    ff, wf = copy_factor(cfetch, "FETCH_SIZE"), copy_factor(cwrite, "WRITE_SIZE")
+    lines = ["# rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE summary", f"command: {command}",
+             f"kernel_sources_sha256: {source_hash()}",
+             f"copy_calibration: {copy_mib:.0f} MiB device-to-device copy (__amd_rocclr_copyBuffer)",
+             f"fetch_scale: {ff:.4f}", f"write_scale: {wf:.4f}", "",
+             "| kernel | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | scaled HBM bytes/dispatch |",
+             "|---|---|---|---|"]
+    extra = []
+    for (k, c), v in sorted(fetch.items()):
+        if "gqa_av" not in k:
+            continue
+        w = write.get((k, "WRITE_SIZE"), 0.0)
+        traffic = v * 1024 * ff + w * 1024 * wf
+        lines.append(f"| {k[:90]} | {v:.1f} | {w:.1f} | {traffic:.0f} |")
+        if "pass1" in k:
+            extra.append(f"pass1_traffic_bytes: {traffic:.0f}")
+    lines += [""] + extra
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def recorded_traffic(workload: str, mode: str):
+    """Pass-1 HBM bytes per launch from the committed PMC summary, if it was
+    taken on the current kernel sources (else None)."""
+    f = os.path.join(PROFILES, f"pass1_{workload}_{mode}_traffic.md")
+    if not os.path.exists(f):
+        return None
+    kv = {}
+    for line in open(f):
+        if ":" in line and not line.startswith("|"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_sources_sha256") != source_hash() or "pass1_traffic_bytes" not in kv:
+        return None
+    return float(kv["pass1_traffic_bytes"])
+
+
+def copy_calibration(mib: float):
+    import torch
+    n = int(mib * 2 ** 20)
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copied {n} bytes x3", flush=True)
+
+
+# ---- CPU baseline ---------------------------------------------------------------
 
 def cpu_baseline(w, attn, V, budget_s: float):
     """The CPU oracle (fp64, OpenMP) on the same workload, repeated for ~budget_s."""
@@ -59,21 +177,32 @@ def cpu_baseline(w, attn, V, budget_s: float):
             break
     per_call = el / reps
     return {
-        "value": w.algorithmic_bytes() / per_call / 1e9,
+        "value": round(w.algorithmic_bytes() / per_call / 1e9, 3),
         "unit": "GB/s",
-        "us_per_call": per_call * 1e6,
+        "us_per_call": round(per_call * 1e6, 1),
         "cores": threads,
         "kind": "oracle",
         "sample": f"full workload {w.name}, {reps} calls in {el:.1f} s (fp64 C oracle, OpenMP)",
     }
 
 
+# ---- benchmark --------------------------------------------------------------------
+
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.out, args.command)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc, args.copy_bytes, args.out, args.command)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this path has no "
               "multi-GPU code; see DESIGN.md for how it would shard.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import torch
 
@@ -92,7 +221,7 @@ def main():
 
     attn_h, V_h = make_inputs(w, seed=0)
     plan = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, args.mode, nsplit=args.nsplit,
-                        cu_count=props.multi_processor_count)
+                        engine=args.engine, combine=args.combine, cu_count=props.multi_processor_count)
     per_set = w.v_bytes() + w.attn_bytes() + w.out_bytes()
     nrot = max(1, math.ceil(args.rotate_mb * 2 ** 20 / per_set))
     sets = []
@@ -102,32 +231,46 @@ def main():
         v = v0 if i == 0 else v0.clone()
         sets.append((a, v, torch.empty(w.B, w.Hq, w.D, device=dev)))
     torch.cuda.synchronize()
-
     calls = [ga.bind(a, v, o, plan=plan) for a, v, o in sets]
-
-    def step(i):
-        calls[i % nrot]()
+    stream = torch.cuda.current_stream(dev)
 
     for i in range(args.warmup):
-        step(i)
+        calls[i % nrot]()
     torch.cuda.synchronize()
+
+    # Whole calls: the metric.
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
+    start.record(stream)
     for i in range(args.steps):
-        step(i)
-    end.record()
+        calls[i % nrot]()
+    end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
     gbs = w.algorithmic_bytes() / (ms / 1e3) / 1e9
-    print(f"[bench] {ms * 1e3:.2f} us/call, {gbs:.1f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of peak), "
-          f"{nrot} rotation sets, plan {plan.as_dict()}", file=sys.stderr, flush=True)
+
+    # The dominant kernel alone: the same steps, with events around each pass-1 launch.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        c = calls[i % nrot]
+        ev[i][0].record(stream)
+        c.pass1()
+        ev[i][1].record(stream)
+        c.combine()
+    torch.cuda.synchronize()
+    p1_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / args.steps
+    p1_gbs = w.algorithmic_bytes() / (p1_ms / 1e3) / 1e9
+    print(f"[bench] {ms * 1e3:.2f} us/call, {gbs:.1f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of peak); "
+          f"pass 1 {p1_ms * 1e3:.2f} us = {p1_gbs:.1f} GB/s; {nrot} rotation sets, plan {plan.as_dict()}",
+          file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, attn_h, V_h, args.cpu_seconds)
 
-    kernels = 1   # pass 1 and the split-C combine are one kernel
+    split_kernel = plan.nsplit > 1 and plan.combine == 1
+    traffic = recorded_traffic(w.name, args.mode) if (args.nsplit == 0 and args.engine == "auto"
+                                                      and args.combine == "auto") else None
     line = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -145,16 +288,18 @@ def main():
         "config": {
             "workload": w.name, "B": w.B, "C": w.C, "Hq": w.Hq, "Hkv": w.Hkv, "G": w.G, "D": w.D,
             "v_dtype": w.v_dtype, "mode": args.mode, "algorithmic_bytes": w.algorithmic_bytes(),
-            "rotation_sets": nrot, "kernels_per_call": kernels, "plan": plan.as_dict(),
+            "rotation_sets": nrot, "kernels_per_call": 2 if split_kernel else 1, "plan": plan.as_dict(),
         },
         "roofline": {
             "bound": "hbm",
-            "achieved": round(gbs, 2),
+            "achieved": round(p1_gbs, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "timing": "HIP events around the timed calls on the launch stream; one kernel per call",
+            "frac": round(p1_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "pass 1 (V streaming)",
+            "us_per_launch": round(p1_ms * 1e3, 3),
+            "timing": "HIP events around each pass-1 launch on the launch stream",
         },
         "cpu_baseline": cpu,
     }

@@ -22,7 +22,8 @@ __all__ = [
 LIB_PATH = os.environ.get("GQA_AV_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_av.so")
 
 MODES = {"auto": -1, "per_head": 0, "reuse": 1}
-ENGINES = {"auto": -1, "valu": 0, "mfma": 1}
+ENGINES = {"auto": 0, "valu": 1, "mfma": 2}
+COMBINES = {"auto": 0, "kernel": 1, "last": 2}
 DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "INELIGIBLE", 3: "UNSUPPORTED", 4: "HIP"}
 
@@ -36,7 +37,7 @@ class GqaAvError(RuntimeError):
 
 class Hint(ctypes.Structure):
     _fields_ = [("engine", ctypes.c_int32), ("nsplit", ctypes.c_int32), ("cu_count", ctypes.c_int32),
-                ("v_align", ctypes.c_int32), ("reserved", ctypes.c_int32 * 4)]
+                ("v_align", ctypes.c_int32), ("combine", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
 
 
 class Plan(ctypes.Structure):
@@ -45,7 +46,7 @@ class Plan(ctypes.Structure):
                 ("row_slots", ctypes.c_int32), ("d_tiles", ctypes.c_int32), ("nsplit", ctypes.c_int32),
                 ("threads", ctypes.c_int32), ("rows_per_split", ctypes.c_int64), ("grid", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_int64), ("v_bytes_read", ctypes.c_int64),
-                ("reserved", ctypes.c_int32 * 4)]
+                ("combine", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
@@ -73,8 +74,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gqa_av_make_plan.restype = ip
     lib.gqa_av_decode.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ip, ip, vp]
     lib.gqa_av_decode.restype = ip
-    lib.gqa_av_decode_plan.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ip, ctypes.POINTER(Plan), vp]
-    lib.gqa_av_decode_plan.restype = ip
+    for fn in ("gqa_av_decode_plan", "gqa_av_decode_pass1", "gqa_av_decode_combine"):
+        getattr(lib, fn).argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ip, ctypes.POINTER(Plan), vp]
+        getattr(lib, fn).restype = ip
     lib.gqa_av_status_string.argtypes = [ip]
     lib.gqa_av_status_string.restype = ctypes.c_char_p
     lib.gqa_av_last_error.argtypes = []
@@ -112,10 +114,15 @@ def resolve_mode(Hq: int, Hkv: int, mode: Union[str, int] = "auto") -> str:
 
 
 def make_plan(B: int, C: int, Hq: int, Hkv: int, D: int, v_dtype: str, mode: Union[str, int] = "auto",
-              engine: Union[str, int] = "auto", nsplit: int = 0, cu_count: int = 0, v_align: int = 0) -> Plan:
-    """Host-only planning (no GPU needed). nsplit/cu_count/v_align <= 0 mean automatic."""
+              engine: Union[str, int] = "auto", nsplit: int = 0, cu_count: int = 0, v_align: int = 0,
+              combine: Union[str, int] = "auto") -> Plan:
+    """Host-only planning (no GPU needed). nsplit/cu_count/v_align <= 0 mean automatic.
+
+    engine: "auto" | "valu" | "mfma"; combine: "auto" | "kernel" | "last".
+    """
     h = Hint()
     h.engine = ENGINES[engine] if isinstance(engine, str) else int(engine)
+    h.combine = COMBINES[combine] if isinstance(combine, str) else int(combine)
     h.nsplit, h.cu_count, h.v_align = int(nsplit), int(cu_count), int(v_align)
     p = Plan()
     rc = load().gqa_av_make_plan(B, C, Hq, Hkv, D, DTYPES[v_dtype], _mode(mode), ctypes.byref(h), ctypes.byref(p))
@@ -209,12 +216,28 @@ class BoundCall:
             align = 16 if addr % 16 == 0 else (addr & -addr)
             plan = make_plan(B, C, Hq, Hkv, D, vdt, mode, cu_count=props.multi_processor_count, v_align=align)
         self.attn, self.V, self.out, self.plan, self.stream = attn, V, out, plan, stream
-        self._fn = load().gqa_av_decode_plan
+        lib = load()
+        self._fn = lib.gqa_av_decode_plan
+        self._pass1 = lib.gqa_av_decode_pass1
+        self._combine = lib.gqa_av_decode_combine
         self._args = (attn.data_ptr(), V.data_ptr(), out.data_ptr(), B, C, Hq, Hkv, D, DTYPES[vdt],
                       ctypes.byref(plan), stream.cuda_stream)
 
     def __call__(self):
         rc = self._fn(*self._args)
+        if rc != 0:
+            _raise(rc)
+        return self.out
+
+    def pass1(self):
+        """Only the V-streaming launch (see gqa_av_decode_pass1); combine() must follow."""
+        rc = self._pass1(*self._args)
+        if rc != 0:
+            _raise(rc)
+
+    def combine(self):
+        """The split combine launch (see gqa_av_decode_combine); completes `out`."""
+        rc = self._combine(*self._args)
         if rc != 0:
             _raise(rc)
         return self.out

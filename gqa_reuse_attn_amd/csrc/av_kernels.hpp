@@ -10,11 +10,18 @@
 // sub-group, D-tile) -- or (b, q_h, D-tile) for the per-head baseline -- and
 // one context split [cb, ce). It streams the tile's V rows of that split once
 // and keeps fp32 accumulators for every query head of the tile. Without a
-// context split it writes `out` directly; otherwise it writes its split's
-// plane of partial sums and a second kernel adds the planes in increasing
-// split order (the kernel boundary makes the partials visible across the
-// XCDs' separate L2 caches without any cache maintenance inside pass 1). No
-// atomics anywhere: a plan gives bitwise-identical results run to run.
+// context split it writes `out` directly. With one, the split partial sums
+// are added in increasing split order, either
+//  * in the same kernel: every workgroup stores its partials with
+//    agent-scope (device-coherent) stores, waits for them to complete, and
+//    counts itself in on a per-tile counter; the workgroup that arrives last
+//    reads the tile's partials back with agent-scope loads and writes `out`.
+//    Because the partials themselves are coherent at device scope, no L2
+//    write-back or invalidate is needed (a release/acquire fence at agent
+//    scope costs a whole-L2 maintenance operation per workgroup on the
+//    per-XCD L2s of MI355X), or
+//  * in a second kernel over split planes (the kernel boundary orders them).
+// Both sum in the same fixed order, so a plan is bitwise reproducible.
 //
 // Two inner-product engines, both fp32 FMA arithmetic:
 //  * VALU  -- any G and D. Lc lanes cover a D-row with VB-byte loads (one
@@ -79,7 +86,9 @@ struct Pass1Args {
     const float* attn;      // [B][C][Hq]
     const uint8_t* V;       // [B][C][Hkv][D] of DT
     float* out;             // [B][Hq][D]
-    float* part;            // [nsplit][B][Hq][D]   (nsplit > 1)
+    float* part;            // combine in kernel: [tiles][nsplit][tile outputs]; else [nsplit][B][Hq][D]
+    uint32_t* counters;     // combine in kernel: [tiles], zero between calls
+    int32_t combine;        // 1: last workgroup of a tile adds the splits; 0: second kernel
     int64_t C;
     int64_t rows_per_split;
     int32_t B, Hq, Hkv, D;
@@ -174,6 +183,7 @@ __device__ inline void widen(const Raw<NB>& r, float* f) {
 
 struct Tile {
     int b, kv, s, dt, q_first, nq;
+    uint32_t id;    // tile index without the split: counter and partial block
 };
 
 // Logical order, fastest first: (sub-group, D-tile), kv_h, split, b, and for
@@ -188,6 +198,7 @@ __device__ inline Tile decode_tile(const Pass1Args& a, int GT) {
     T.s = t % a.nsplit; t /= a.nsplit;
     T.b = t % a.B; t /= a.B;
     const uint32_t major = t;
+    T.id = ((major * a.B + T.b) * a.Hkv + T.kv) * nminor + minor;
     if (a.per_head) {
         T.dt = minor;
         T.q_first = T.kv * a.G + major;
@@ -199,6 +210,83 @@ __device__ inline Tile decode_tile(const Pass1Args& a, int GT) {
         T.nq = min(GT, a.G - sg * GT);
     }
     return T;
+}
+
+// ---- in-kernel split combine ------------------------------------------------
+
+// Split partials are added as kSplitGroups contiguous ranges of splits (see
+// combine_last and av_pass2_combine).
+constexpr int kSplitGroups = 8;
+
+// Agent-scope relaxed atomics: on gfx950 these are plain loads and stores with
+// the device-coherence cache policy, so they bypass the XCD-private cache state.
+__device__ inline void store_coherent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float load_coherent(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Floats of one (tile, split) block of partials: the tile's outputs rounded up
+// to whole float4s, so every block starts 16-byte aligned.
+__device__ __host__ constexpr int padded_outputs(int TO) { return (TO + 3) / 4 * 4; }
+
+constexpr int kQuadsPerBlock = kThreads / kSplitGroups;
+// Buffer-resource word 3 for raw (untyped) buffer access on gfx9-family parts.
+constexpr int kRawBufferFlags = 0x00020000;
+constexpr int kCachePolicySc1 = 16;   // device-scope coherence (same policy as agent-scope atomics)
+
+// Called by all threads of a workgroup after each stored its share of the
+// split's TO partial sums with store_coherent() into blk = the tile's block
+// [nsplit][padded_outputs(TO)]. In the one workgroup that arrives last, every
+// tile output k is summed over the splits in the fixed association of
+// av_pass2_combine (kSplitGroups contiguous split ranges, each in increasing
+// split order, then the range sums in range order) and handed to emit(k, sum).
+template <typename Emit>
+__device__ inline void combine_last(const Pass1Args& a, const Tile& T, const float* blk, int TO, Emit emit) {
+    __shared__ uint32_t s_last;
+    __shared__ f32x4 red[kSplitGroups][kQuadsPerBlock];
+    // The partials must have reached device scope before this workgroup counts
+    // itself in: wait for every outstanding store of this wave, then barrier.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(a.counters + T.id, 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        s_last = prev == static_cast<uint32_t>(a.nsplit - 1);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    const int ns = a.nsplit;
+    const int TOP = padded_outputs(TO), nquads = TOP / 4;
+    // Device-coherent float4 reads of the tile's block; the resource bounds
+    // every access to the block.
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(blk), 0, ns * TOP * 4, kRawBufferFlags);
+    const int q = threadIdx.x % kQuadsPerBlock, g = threadIdx.x / kQuadsPerBlock;
+    const int s0 = static_cast<int>((static_cast<int64_t>(ns) * g) / kSplitGroups);
+    const int s1 = static_cast<int>((static_cast<int64_t>(ns) * (g + 1)) / kSplitGroups);
+    for (int q0 = 0; q0 < nquads; q0 += kQuadsPerBlock) {
+        const int quad = q0 + q;
+        f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (quad < nquads) {
+#pragma unroll 8
+            for (int s = s0; s < s1; ++s)
+                sum += __builtin_amdgcn_raw_buffer_load_b128(rsrc, (s * TOP + quad * 4) * 4, 0, kCachePolicySc1);
+        }
+        red[g][q] = sum;
+        __syncthreads();
+        if (g == 0 && quad < nquads) {
+            f32x4 t = red[0][q];
+#pragma unroll
+            for (int k = 1; k < kSplitGroups; ++k) t += red[k][q];
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (quad * 4 + c < TO) emit(quad * 4 + c, t[c]);
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(a.counters + T.id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---- pass 1: VALU engine ----------------------------------------------------
@@ -403,27 +491,49 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
     __syncthreads();                                  // LDS is reused below
 
     // Sum the row slots: slot kk of thread tid lives at smem[kk * 256 + tid].
-    float* const dst = a.nsplit > 1 ? a.part + static_cast<size_t>(T.s) * a.B * a.Hq * a.D : a.out;
-    const int nout = Lc * CH;
+    // Output slot k = g * E + e of lane chunk jj is tile output k * Lc + jj.
+    const int TO = NACC * Lc;
+    const bool in_kernel = a.nsplit > 1 && a.combine;
+    const int TOP = padded_outputs(TO);
+    float* const blk = in_kernel ? a.part + static_cast<size_t>(T.id) * a.nsplit * TOP : nullptr;
+    float* const plane = (a.nsplit > 1 && !a.combine) ? a.part + static_cast<size_t>(T.s) * a.B * a.Hq * a.D : a.out;
+    auto out_index = [&](int k, int jj, size_t* o) -> bool {
+        const int g = k / E, e = k - (k / E) * E;
+        const int ld = T.dt * Lc + jj;
+        *o = (static_cast<size_t>(T.b) * a.Hq + q_lo + g) * a.D + static_cast<size_t>(ld) * E + e;
+        return g >= g_off && g < g_off + T.nq && ld < a.L;
+    };
 #pragma unroll
     for (int k0 = 0; k0 < NACC; k0 += CH) {
+        // The last chunk may be short (NACC need not be a multiple of CH).
+        const int nk = NACC - k0 < CH ? NACC - k0 : CH;
 #pragma unroll
         for (int kk = 0; kk < CH; ++kk) {
             const int k = k0 + kk;
-            smem[kk * kThreads + tid] = acc[k / E][k % E];
+            if (k < NACC) smem[kk * kThreads + tid] = acc[k / E][k % E];
         }
         __syncthreads();
+        const int nout = Lc * nk;
         for (int idx = tid; idx < nout; idx += kThreads) {
             const int kk = idx / Lc, jj = idx - (idx / Lc) * Lc;
             float sum = 0.0f;
             for (int rr = 0; rr < rps; ++rr) sum += smem[kk * kThreads + rr * Lc + jj];
             const int k = k0 + kk;
-            const int g = k / E, e = k - (k / E) * E;
-            const int ld = T.dt * Lc + jj;
-            if (g >= g_off && g < g_off + T.nq && ld < a.L)
-                dst[(static_cast<size_t>(T.b) * a.Hq + q_lo + g) * a.D + static_cast<size_t>(ld) * E + e] = sum;
+            if (in_kernel) {
+                store_coherent(blk + static_cast<size_t>(T.s) * TOP + k * Lc + jj, sum);
+            } else {
+                size_t o;
+                if (out_index(k, jj, &o)) plane[o] = sum;
+            }
         }
         __syncthreads();
+    }
+    if (in_kernel) {
+        combine_last(a, T, blk, TO, [&](int idx, float v) {
+            const int k = idx / Lc, jj = idx - (idx / Lc) * Lc;
+            size_t o;
+            if (out_index(k, jj, &o)) a.out[o] = v;
+        });
     }
 }
 
@@ -524,17 +634,34 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma(Pass1Args a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) red[wave * TO + ((s * DE + e) * 4 + i) * 64 + lane] = acc[s][e][i];
     __syncthreads();
-    float* const dst = a.nsplit > 1 ? a.part + static_cast<size_t>(T.s) * a.B * a.Hq * a.D : a.out;
-    for (int idx = threadIdx.x; idx < TO; idx += kThreads) {
-        float sum = red[idx];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) sum += red[w * TO + idx];
+    const bool in_kernel = a.nsplit > 1 && a.combine;
+    static_assert(TO % 4 == 0, "MFMA tile outputs come in whole float4s");
+    float* const blk = in_kernel ? a.part + static_cast<size_t>(T.id) * a.nsplit * TO : nullptr;
+    float* const plane = (a.nsplit > 1 && !a.combine) ? a.part + static_cast<size_t>(T.s) * a.B * a.Hq * a.D : a.out;
+    auto out_index = [&](int idx, size_t* o) -> bool {
         const int l = idx & 63, reg = idx >> 6;
         const int i = reg & 3, se = reg >> 2;
         const int e = se % DE, s = se / DE;
         const int g = 16 * s + 4 * (l >> 4) + i;
-        if (g < T.nq)
-            dst[(static_cast<size_t>(T.b) * a.Hq + T.q_first + g) * a.D + (l & 15) * DE + e] = sum;
+        *o = (static_cast<size_t>(T.b) * a.Hq + T.q_first + g) * a.D + (l & 15) * DE + e;
+        return g < T.nq;
+    };
+    for (int idx = threadIdx.x; idx < TO; idx += kThreads) {
+        float sum = red[idx];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) sum += red[w * TO + idx];
+        if (in_kernel) {
+            store_coherent(blk + static_cast<size_t>(T.s) * TO + idx, sum);
+        } else {
+            size_t o;
+            if (out_index(idx, &o)) plane[o] = sum;
+        }
+    }
+    if (in_kernel) {
+        combine_last(a, T, blk, TO, [&](int idx, float v) {
+            size_t o;
+            if (out_index(idx, &o)) a.out[o] = v;
+        });
     }
 }
 
@@ -544,9 +671,6 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma(Pass1Args a) {
 // the splits are cut into kSplitGroups contiguous ranges, each summed in
 // increasing s by its own thread, and the range sums are then added in
 // increasing range order. Each thread covers four consecutive outputs.
-constexpr int kSplitGroups = 8;
-constexpr int kQuadsPerBlock = kThreads / kSplitGroups;
-
 __global__ __launch_bounds__(kThreads) void av_pass2_combine(const float* __restrict__ part,
                                                              float* __restrict__ out,
                                                              int64_t plane, int32_t nsplit) {

@@ -55,10 +55,15 @@ constexpr int kDefaultCUs = 256;
 constexpr int64_t kMinRowsPerSplit = 256;     // below this a split's epilogue dominates
 constexpr int64_t kTargetWgPerCU = 8;
 
-// Split-C workspace of one (device, stream): the partial-sum planes.
+// Split-C workspace of one (device, stream). The per-tile counters live in a
+// buffer of their own: they must be zero before a call, every call leaves the
+// ones it used at zero again, and no partial sum may ever land on them,
+// whatever the next plan's layout.
 struct Workspace {
+    void* counters = nullptr;
+    size_t counter_bytes = 0;
     void* part = nullptr;
-    size_t bytes = 0;
+    size_t part_bytes = 0;
 };
 
 std::mutex g_ws_mutex;
@@ -82,27 +87,43 @@ int device_cus(int dev, int* cus) {
     return GQA_AV_OK;
 }
 
-// The workspace of (dev, stream), grown to at least `bytes`. Earlier calls on
-// the stream may still use the old buffer, so the stream is synchronised
-// before it is freed.
-int get_workspace(int dev, hipStream_t stream, size_t bytes, float** part) {
+// Grow `*buf` to at least `bytes`. Earlier calls on `stream` may still use the
+// old buffer, so the stream is synchronised before it is freed. A new counter
+// buffer is zeroed on the stream.
+int grow(void** buf, size_t* have, size_t bytes, hipStream_t stream, bool zero) {
+    if (*have >= bytes) return GQA_AV_OK;
+    if (*buf) {
+        hipError_t e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
+        e = hipFree(*buf);
+        *buf = nullptr;
+        *have = 0;
+        if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "hipFree: %s", hipGetErrorString(e));
+    }
+    void* p = nullptr;
+    hipError_t e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "hipMalloc(%zu) for split-C workspace: %s", bytes, hipGetErrorString(e));
+    if (zero) {
+        e = hipMemsetAsync(p, 0, bytes, stream);
+        if (e != hipSuccess) {
+            (void)hipFree(p);
+            return fail(GQA_AV_ERR_HIP, "hipMemsetAsync: %s", hipGetErrorString(e));
+        }
+    }
+    *buf = p;
+    *have = bytes;
+    return GQA_AV_OK;
+}
+
+int get_workspace(int dev, hipStream_t stream, size_t counter_bytes, size_t part_bytes, uint32_t** counters,
+                  float** part) {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace& ws = g_ws[{dev, stream}];
-    if (ws.bytes < bytes) {
-        if (ws.part) {
-            hipError_t e = hipStreamSynchronize(stream);
-            if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
-            e = hipFree(ws.part);
-            ws = Workspace();
-            if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "hipFree: %s", hipGetErrorString(e));
-        }
-        void* p = nullptr;
-        hipError_t e = hipMalloc(&p, bytes);
-        if (e != hipSuccess)
-            return fail(GQA_AV_ERR_HIP, "hipMalloc(%zu) for split-C workspace: %s", bytes, hipGetErrorString(e));
-        ws.part = p;
-        ws.bytes = bytes;
-    }
+    int rc = GQA_AV_OK;
+    if (counter_bytes > 0) rc = grow(&ws.counters, &ws.counter_bytes, counter_bytes, stream, true);
+    if (rc == GQA_AV_OK) rc = grow(&ws.part, &ws.part_bytes, part_bytes, stream, false);
+    if (rc != GQA_AV_OK) return rc;
+    *counters = static_cast<uint32_t*>(ws.counters);
     *part = static_cast<float*>(ws.part);
     return GQA_AV_OK;
 }
@@ -229,8 +250,18 @@ bool mfma_fits(int64_t D, int es, int v_align, int nset) {
 
 constexpr int64_t kMfmaMinGroup = 5;     // below this the VALU engine does less work
 
-int64_t workspace_bytes(int64_t B, int64_t Hq, int64_t D, int64_t nsplit) {
-    return nsplit > 1 ? nsplit * B * Hq * D * 4 : 0;   // one fp32 plane of out per split
+constexpr int64_t kCounterBytes = 256;          // the counter block is padded to this
+
+int64_t counter_bytes(int64_t tiles) { return ceil_div(tiles * 4, kCounterBytes) * kCounterBytes; }
+
+// KERNEL: one fp32 plane of `out` per split. LAST: [tiles][nsplit][tile outputs]
+// partials plus one counter per tile.
+int64_t workspace_bytes(int64_t B, int64_t Hq, int64_t D, int64_t tiles, int64_t nsplit, int64_t tile_outputs,
+                        int combine) {
+    if (nsplit <= 1) return 0;
+    if (combine == GQA_AV_COMBINE_LAST)
+        return counter_bytes(tiles) + tiles * nsplit * gqa_av::padded_outputs(static_cast<int>(tile_outputs)) * 4;
+    return nsplit * B * Hq * D * 4;
 }
 
 int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dtype, int mode,
@@ -243,10 +274,11 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
 
     gqa_av_hint h;
     std::memset(&h, 0, sizeof h);
-    h.engine = GQA_AV_ENGINE_AUTO;
     if (hint) h = *hint;
-    if (h.engine != GQA_AV_ENGINE_AUTO && h.engine != GQA_AV_ENGINE_VALU && h.engine != GQA_AV_ENGINE_MFMA)
+    if (h.engine < GQA_AV_ENGINE_AUTO || h.engine > GQA_AV_ENGINE_MFMA)
         return fail(GQA_AV_ERR_INVALID_ARG, "unknown engine %d", h.engine);
+    if (h.combine < GQA_AV_COMBINE_AUTO || h.combine > GQA_AV_COMBINE_LAST)
+        return fail(GQA_AV_ERR_INVALID_ARG, "unknown combine %d", h.combine);
     const int cus = h.cu_count > 0 ? h.cu_count : cu_default;
     const int v_align = h.v_align > 0 ? h.v_align : 16;
 
@@ -265,7 +297,7 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
                     "MFMA engine needs reuse mode, D %% 16 == 0 with a 4/8/12/16/32-byte lane chunk and matching V alignment");
 
     int VB, GT, nsg;
-    int64_t Lc, rps, ndt, rows_per_step;
+    int64_t Lc, rps, ndt, rows_per_step, tile_outputs;
     int64_t heads_major;  // tiles along the head axis per KV head
     if (engine == GQA_AV_ENGINE_MFMA) {
         const int64_t DE = D / 16;
@@ -277,6 +309,7 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
         rps = 16;                       // 4 waves x 4 rows per MFMA
         ndt = 1;
         rows_per_step = 4 * gqa_av::kWaves * gqa_av::mfma_unroll(VB);
+        tile_outputs = static_cast<int64_t>(GT) * D;
     } else {
         // Widest lane load that divides a D-row and respects V's alignment.
         VB = 0;
@@ -301,6 +334,7 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
             heads_major = G;
         }
         rows_per_step = rps * gqa_av::valu_unroll(GT);
+        tile_outputs = static_cast<int64_t>(GT) * E * Lc;
     }
     const int64_t tiles = B * Hkv * heads_major * ndt;
 
@@ -336,7 +370,19 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
     plan->threads = gqa_av::kThreads;
     plan->rows_per_split = rows_per_split;
     plan->grid = grid;
-    plan->workspace_bytes = workspace_bytes(B, Hq, D, nsplit);
+    int combine = GQA_AV_COMBINE_AUTO;
+    if (nsplit > 1) {
+        combine = h.combine;
+        // Measured on MI355X: the second kernel is faster on every decode
+        // workload (the last-workgroup combine pays for device-coherent
+        // stores and loads of the partials), so it is the automatic choice.
+        if (combine == GQA_AV_COMBINE_AUTO) combine = GQA_AV_COMBINE_KERNEL;
+        // One tile's block is addressed through a 32-bit buffer offset.
+        if (combine == GQA_AV_COMBINE_LAST && nsplit * gqa_av::padded_outputs(static_cast<int>(tile_outputs)) * 4 > INT32_MAX)
+            return fail(GQA_AV_ERR_UNSUPPORTED, "a tile's split partials exceed 2 GB; use the kernel combine");
+    }
+    plan->combine = combine;
+    plan->workspace_bytes = workspace_bytes(B, Hq, D, tiles, nsplit, tile_outputs, combine);
     plan->v_bytes_read = B * C * Hkv * D * es * heads_major;
     return GQA_AV_OK;
 }
@@ -381,8 +427,17 @@ int gqa_av_make_plan(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, i
     return plan_impl(B, C, Hq, Hkv, D, v_dtype, mode, hint, kDefaultCUs, plan);
 }
 
-int gqa_av_decode_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C, int64_t Hq,
-                       int64_t Hkv, int64_t D, int v_dtype, const gqa_av_plan* plan, void* stream) {
+}  // extern "C"
+
+namespace {
+
+constexpr int kRunPass1 = 1, kRunCombine = 2;
+
+// Validate (attn, V, out, sizes, plan) and launch the parts of the call named
+// by `which`. Validation is the same for every part, so a caller splitting
+// the call gets the same errors as gqa_av_decode_plan.
+int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
+             int64_t D, int v_dtype, const gqa_av_plan* plan, void* stream, int which) {
     if (!plan) return fail(GQA_AV_ERR_INVALID_ARG, "plan is NULL");
     int rc = check_sizes(B, C, Hq, Hkv, D, v_dtype);
     if (rc != GQA_AV_OK) return rc;
@@ -392,6 +447,7 @@ int gqa_av_decode_plan(const float* attn, const void* V, float* out, int64_t B, 
     h.engine = plan->engine;
     h.nsplit = plan->nsplit;
     h.v_align = plan->vec_bytes;
+    h.combine = plan->combine;
     gqa_av_plan check;
     const int mode = plan->mode;
     // Re-plan with the split count fixed: rows_per_split then follows from C.
@@ -401,7 +457,11 @@ int gqa_av_decode_plan(const float* attn, const void* V, float* out, int64_t B, 
     check.nsplit = plan->nsplit;
     check.grid = plan->grid;
     check.workspace_bytes = plan->workspace_bytes;
+    check.combine = plan->combine;
     if (!same_plan(check, *plan)) return fail(GQA_AV_ERR_INVALID_ARG, "plan does not belong to this problem");
+    if (plan->nsplit > 1 ? (plan->combine != GQA_AV_COMBINE_KERNEL && plan->combine != GQA_AV_COMBINE_LAST)
+                         : plan->combine != GQA_AV_COMBINE_AUTO)
+        return fail(GQA_AV_ERR_INVALID_ARG, "plan combine %d does not fit nsplit %d", plan->combine, plan->nsplit);
     // The split fields must still tile [0, C) exactly.
     if (C > 0) {
         if (plan->nsplit < 1 || plan->rows_per_split < 1 ||
@@ -414,7 +474,11 @@ int gqa_av_decode_plan(const float* attn, const void* V, float* out, int64_t B, 
     const int64_t heads_major = plan->mode == GQA_AV_REUSE ? plan->subgroups : Hq / Hkv;
     if (plan->grid % plan->nsplit != 0 || tiles_per_split != B * Hkv * heads_major * plan->d_tiles)
         return fail(GQA_AV_ERR_INVALID_ARG, "plan grid does not match the problem");
-    if (plan->workspace_bytes != workspace_bytes(B, Hq, D, plan->nsplit))
+    const int64_t tile_outputs = plan->engine == GQA_AV_ENGINE_MFMA
+        ? static_cast<int64_t>(plan->heads_per_tile) * D
+        : static_cast<int64_t>(plan->heads_per_tile) * (plan->vec_bytes / elem_bytes(v_dtype)) * plan->lanes_per_row;
+    if (plan->workspace_bytes !=
+        workspace_bytes(B, Hq, D, tiles_per_split, plan->nsplit, tile_outputs, plan->combine))
         return fail(GQA_AV_ERR_INVALID_ARG, "plan workspace does not match the problem");
 
     if (B == 0) return GQA_AV_OK;
@@ -432,8 +496,12 @@ int gqa_av_decode_plan(const float* attn, const void* V, float* out, int64_t B, 
     if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
 
     float* part = nullptr;
+    uint32_t* counters = nullptr;
+    const bool last = plan->nsplit > 1 && plan->combine == GQA_AV_COMBINE_LAST;
     if (plan->nsplit > 1) {
-        rc = get_workspace(dev, s, static_cast<size_t>(plan->workspace_bytes), &part);
+        const int64_t cbytes = last ? counter_bytes(tiles_per_split) : 0;
+        rc = get_workspace(dev, s, static_cast<size_t>(cbytes), static_cast<size_t>(plan->workspace_bytes - cbytes),
+                           &counters, &part);
         if (rc != GQA_AV_OK) return rc;
     }
 
@@ -442,6 +510,8 @@ int gqa_av_decode_plan(const float* attn, const void* V, float* out, int64_t B, 
     a.V = static_cast<const uint8_t*>(V);
     a.out = out;
     a.part = part;
+    a.counters = counters;
+    a.combine = last ? 1 : 0;
     a.C = C;
     a.rows_per_split = plan->rows_per_split;
     a.B = static_cast<int32_t>(B);
@@ -458,9 +528,11 @@ int gqa_av_decode_plan(const float* attn, const void* V, float* out, int64_t B, 
     a.rps = plan->row_slots;
     a.nblocks = static_cast<uint32_t>(plan->grid);
 
-    e = launch_pass1(v_dtype, *plan, D, a, s);
-    if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "pass-1 launch: %s", hipGetErrorString(e));
-    if (plan->nsplit > 1) {
+    if (which & kRunPass1) {
+        e = launch_pass1(v_dtype, *plan, D, a, s);
+        if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "pass-1 launch: %s", hipGetErrorString(e));
+    }
+    if ((which & kRunCombine) && plan->nsplit > 1 && !last) {
         const int64_t plane = B * Hq * D;
         const int64_t per_block = 4 * gqa_av::kQuadsPerBlock;
         const int64_t blocks = ceil_div(plane, per_block);
@@ -471,6 +543,25 @@ int gqa_av_decode_plan(const float* attn, const void* V, float* out, int64_t B, 
         if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "pass-2 launch: %s", hipGetErrorString(e));
     }
     return GQA_AV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_av_decode_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C, int64_t Hq,
+                       int64_t Hkv, int64_t D, int v_dtype, const gqa_av_plan* plan, void* stream) {
+    return run_plan(attn, V, out, B, C, Hq, Hkv, D, v_dtype, plan, stream, kRunPass1 | kRunCombine);
+}
+
+int gqa_av_decode_pass1(const float* attn, const void* V, float* out, int64_t B, int64_t C, int64_t Hq,
+                        int64_t Hkv, int64_t D, int v_dtype, const gqa_av_plan* plan, void* stream) {
+    return run_plan(attn, V, out, B, C, Hq, Hkv, D, v_dtype, plan, stream, kRunPass1);
+}
+
+int gqa_av_decode_combine(const float* attn, const void* V, float* out, int64_t B, int64_t C, int64_t Hq,
+                          int64_t Hkv, int64_t D, int v_dtype, const gqa_av_plan* plan, void* stream) {
+    return run_plan(attn, V, out, B, C, Hq, Hkv, D, v_dtype, plan, stream, kRunCombine);
 }
 
 int gqa_av_decode(const float* attn, const void* V, float* out, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
@@ -517,10 +608,11 @@ int gqa_av_release(void) {
     int status = GQA_AV_OK;
     for (auto& kv : g_ws) {
         Workspace& ws = kv.second;
-        if (!ws.part) continue;
+        if (!ws.counters && !ws.part) continue;
         hipError_t e = hipSetDevice(kv.first.first);
         if (e == hipSuccess) e = hipDeviceSynchronize();
-        if (e == hipSuccess) e = hipFree(ws.part);
+        if (e == hipSuccess && ws.counters) e = hipFree(ws.counters);
+        if (e == hipSuccess && ws.part) e = hipFree(ws.part);
         if (e != hipSuccess) status = fail(GQA_AV_ERR_HIP, "release: %s", hipGetErrorString(e));
         ws = Workspace();
     }

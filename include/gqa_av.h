@@ -43,14 +43,14 @@
  * error `out` is left untouched. gqa_av_last_error() gives a one-line detail
  * for the calling thread's last failing call.
  *
- * Workspace: when a plan splits the context (nsplit > 1) the library needs one
- * block of partial sums per (tile, split) and one uint32 counter per tile
- * (plan->workspace_bytes in total). It allocates them itself (hipMalloc) per
- * (device, stream) in two buffers, keeps them for reuse, grows them on demand
- * (synchronising that stream first) and frees them in gqa_av_release(). The
- * counters are zeroed when allocated and every call leaves them at zero.
- * Calls on different streams never share a workspace; calls on one stream are
- * ordered by the stream.
+ * Workspace: when a plan splits the context (nsplit > 1) the library needs
+ * nsplit blocks of partial sums and, for GQA_AV_COMBINE_LAST, one uint32
+ * counter per tile (plan->workspace_bytes in total). It allocates them itself
+ * (hipMalloc) per (device, stream) in two buffers, keeps them for reuse, grows
+ * them on demand (synchronising that stream first) and frees them in
+ * gqa_av_release(). The counters are zeroed when allocated and every call
+ * leaves them at zero. Calls on different streams never share a workspace;
+ * calls on one stream are ordered by the stream.
  *
  * Thread safety: all entry points may be called from several host threads.
  */
@@ -87,25 +87,34 @@ typedef enum gqa_av_status {
 
 /* Inner-product engine of the reuse kernel. */
 typedef enum gqa_av_engine {
-    GQA_AV_ENGINE_AUTO = -1,
-    GQA_AV_ENGINE_VALU = 0,      /* per-lane fp32 FMAs, any G, any D */
-    GQA_AV_ENGINE_MFMA = 1       /* fp32 matrix-core tiles over 16 query heads */
+    GQA_AV_ENGINE_AUTO = 0,
+    GQA_AV_ENGINE_VALU = 1,      /* per-lane fp32 FMAs, any G, any D */
+    GQA_AV_ENGINE_MFMA = 2       /* fp32 matrix-core tiles over 16 query heads */
 } gqa_av_engine;
 
+/* How the partial sums of a split context are added (both in increasing
+ * split order, so results are reproducible bit for bit). */
+typedef enum gqa_av_combine {
+    GQA_AV_COMBINE_AUTO = 0,
+    GQA_AV_COMBINE_KERNEL = 1,   /* a second kernel over per-split planes */
+    GQA_AV_COMBINE_LAST = 2      /* in pass 1: the last workgroup of each tile adds them */
+} gqa_av_combine;
+
 /* Optional planning hints. Zero-initialise, then set what you want to force:
- * a value <= 0 (or -1 for enums) means "choose automatically". */
+ * every field at 0 (or below) means "choose automatically". */
 typedef struct gqa_av_hint {
-    int32_t engine;     /* gqa_av_engine; -1 = auto */
-    int32_t nsplit;     /* number of context splits; <= 0 = auto */
-    int32_t cu_count;   /* compute units to plan for; <= 0 = the device's (decode) or 256 (make_plan) */
-    int32_t v_align;    /* byte alignment of V's base address; <= 0 = assume 16 */
-    int32_t reserved[4];
+    int32_t engine;     /* gqa_av_engine */
+    int32_t nsplit;     /* number of context splits */
+    int32_t cu_count;   /* compute units to plan for; auto = the device's (decode) or 256 (make_plan) */
+    int32_t v_align;    /* byte alignment of V's base address; auto = 16 */
+    int32_t combine;    /* gqa_av_combine for context splits */
+    int32_t reserved[3];
 } gqa_av_hint;
 
 /* A launch plan: what gqa_av_decode_plan will run. Produced by gqa_av_make_plan. */
 typedef struct gqa_av_plan {
     int32_t mode;            /* resolved: GQA_AV_PER_HEAD or GQA_AV_REUSE */
-    int32_t engine;          /* resolved gqa_av_engine */
+    int32_t engine;          /* resolved gqa_av_engine (VALU or MFMA) */
     int32_t heads_per_tile;  /* query heads one workgroup computes (reuse: VALU 1-4, 8 or 16; MFMA 16 or 32; per-head: 1) */
     int32_t subgroups;       /* workgroups that share one KV head's rows (ceil(G / heads_per_tile)) */
     int32_t vec_bytes;       /* bytes of V each lane loads per row (VALU: 16, 8, 4, 2; MFMA: D/16 elements) */
@@ -118,7 +127,8 @@ typedef struct gqa_av_plan {
     int64_t grid;            /* workgroups launched by the first kernel */
     int64_t workspace_bytes; /* device workspace the plan needs (0 if nsplit == 1) */
     int64_t v_bytes_read;    /* V bytes the plan reads from memory (G x more for per-head) */
-    int32_t reserved[4];
+    int32_t combine;         /* resolved gqa_av_combine: KERNEL or LAST when nsplit > 1, else AUTO */
+    int32_t reserved[3];
 } gqa_av_plan;
 
 /* Resolve `mode` for a head shape. Host-only: needs no GPU.
@@ -148,6 +158,21 @@ int gqa_av_decode(const float *attn, const void *V, float *out,
 int gqa_av_decode_plan(const float *attn, const void *V, float *out,
                        int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D,
                        int v_dtype, const gqa_av_plan *plan, void *stream);
+
+/* The two launches of gqa_av_decode_plan, for callers that schedule or time
+ * them separately (same arguments and checks). gqa_av_decode_pass1 streams V
+ * and writes `out` directly when plan->nsplit == 1 or the combine is
+ * GQA_AV_COMBINE_LAST; otherwise it leaves the split partials in the
+ * workspace of (current device, stream), and gqa_av_decode_combine, enqueued
+ * next on the same stream, adds them into `out` (a no-op for the other
+ * cases). Calling both in this order on one stream is exactly
+ * gqa_av_decode_plan; `out` is complete only after the combine. */
+int gqa_av_decode_pass1(const float *attn, const void *V, float *out,
+                        int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D,
+                        int v_dtype, const gqa_av_plan *plan, void *stream);
+int gqa_av_decode_combine(const float *attn, const void *V, float *out,
+                          int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D,
+                          int v_dtype, const gqa_av_plan *plan, void *stream);
 
 /* Static description of a status code. */
 const char *gqa_av_status_string(int status);

@@ -79,7 +79,8 @@ def _sweep_cases():
 
 
 def _plans(B, C, Hq, Hkv, D, dt, ns):
-    """The automatic plan, per-head, and each reuse engine that can take the shape."""
+    """The automatic plan, per-head, each reuse engine that can take the shape,
+    and both ways of adding split partials."""
     plans = [("auto", ga.make_plan(B, C, Hq, Hkv, D, dt, "auto", nsplit=ns))]
     if Hq // Hkv >= 2:
         plans.append(("per_head", ga.make_plan(B, C, Hq, Hkv, D, dt, "per_head", nsplit=ns)))
@@ -88,6 +89,13 @@ def _plans(B, C, Hq, Hkv, D, dt, ns):
                 plans.append((eng, ga.make_plan(B, C, Hq, Hkv, D, dt, "reuse", engine=eng, nsplit=ns)))
             except ga.GqaAvError as e:
                 assert e.name == "UNSUPPORTED"
+    for name, p in list(plans):
+        if p.nsplit > 1:
+            other = "last" if p.combine == 1 else "kernel"
+            mode = "per_head" if p.mode == 0 else ("reuse" if name != "auto" else "auto")
+            eng = {1: "valu", 2: "mfma"}[p.engine]
+            plans.append((f"{name}/{other}", ga.make_plan(B, C, Hq, Hkv, D, dt, mode, engine=eng, nsplit=ns,
+                                                          combine=other)))
     return plans
 
 
@@ -104,6 +112,23 @@ def test_sweep_small(B, C, Hq, Hkv, D, dt, ns, oracle_lib):
         # signed weights cancel; hold the elementwise error to fp32 accumulation
         assert np.abs(out - ref).max() <= 4 * C * 2.0 ** -24 * scale + 1e-30, \
             f"{(B, C, Hq, Hkv, D, dt, name)} plan={plan.as_dict()}"
+
+
+@pytest.mark.parametrize("wname", list(WORKLOADS))
+def test_workload_other_combine(wname, oracle_lib):
+    """Full-size workloads with split partials added the other way than the automatic plan."""
+    w = WORKLOADS[wname]
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    auto = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, cu_count=cu)
+    if auto.nsplit == 1:
+        pytest.skip("automatic plan does not split the context")
+    other = "last" if auto.combine == 1 else "kernel"
+    _say(f"[parity] {wname} combine={other}")
+    attn, V = make_inputs(w, seed=0)
+    ref = oracle_lib.full(attn, V, w.v_dtype)
+    plan = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, cu_count=cu, combine=other)
+    out = _run(attn, V, plan=plan)
+    assert_parity(out, ref, w.v_dtype, w.C, f"{wname}/{other} plan={plan.as_dict()}")
 
 
 @pytest.mark.parametrize("wname,engine", [
@@ -138,21 +163,29 @@ def test_one_hot_is_exact(dt):
             attn[b, c, q] = 1.0
             sel[b, q] = c
     Vd = V.to(torch.float32).numpy()
-    for mode, ns, eng in (("auto", 0, "auto"), ("auto", 5, "auto"), ("per_head", 3, "auto"), ("auto", 1, "auto"),
-                          ("reuse", 0, "mfma"), ("reuse", 4, "mfma"), ("reuse", 1, "mfma")):
-        plan = ga.make_plan(B, C, Hq, Hkv, D, dt, mode, nsplit=ns, engine=eng)
+    for mode, ns, eng, comb in (("auto", 0, "auto", "auto"), ("auto", 5, "auto", "kernel"),
+                                ("auto", 5, "auto", "last"), ("per_head", 3, "auto", "last"),
+                                ("auto", 1, "auto", "auto"), ("reuse", 0, "mfma", "kernel"),
+                                ("reuse", 4, "mfma", "last"), ("reuse", 1, "mfma", "auto")):
+        plan = ga.make_plan(B, C, Hq, Hkv, D, dt, mode, nsplit=ns, engine=eng, combine=comb)
         out = _run(attn, V, plan=plan).astype(np.float32)
         for (b, q), c in sel.items():
             assert np.array_equal(out[b, q], Vd[b, c, q // G]), (mode, ns, b, q)
 
 
-def test_deterministic_run_to_run():
+@pytest.mark.parametrize("combine", ["kernel", "last"])
+def test_deterministic_run_to_run(combine):
     w = WORKLOADS["mqa16-b4-c32768-hq16-hkv1-d128-bf16"]
     attn, V = make_inputs(w, seed=1)
     a, v = attn.to(DEV), V.to(DEV)
-    outs = [ga.gqa_av_decode(a, v).cpu() for _ in range(3)]
+    plan = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, combine=combine, nsplit=64)
+    outs = [ga.gqa_av_decode(a, v, plan=plan).cpu() for _ in range(3)]
     torch.cuda.synchronize()
     assert all(torch.equal(outs[0], o) for o in outs[1:])
+    # both ways of adding the splits use the same order: identical bits
+    other = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, combine="last" if combine == "kernel" else "kernel",
+                         nsplit=64)
+    assert torch.equal(outs[0], ga.gqa_av_decode(a, v, plan=other).cpu())
 
 
 def test_zero_context_writes_zeros():
@@ -248,9 +281,10 @@ def test_workspace_reuse_across_plans(oracle_lib):
     for k, (B, C, Hq, Hkv, D, dt, mode) in enumerate(shapes):
         attn, V = make_random(B, C, Hq, Hkv, D, dt, seed=300 + k)
         cases.append((attn, V, dt, C, mode, oracle_lib.full(attn, V, dt)))
-    for rnd in range(2):
+    for rnd in range(4):
         for attn, V, dt, C, mode, ref in cases:
-            plan = ga.make_plan(*attn.shape[:2], attn.shape[2], V.shape[2], V.shape[3], dt, mode, nsplit=9)
+            plan = ga.make_plan(*attn.shape[:2], attn.shape[2], V.shape[2], V.shape[3], dt, mode, nsplit=9,
+                                combine="last" if rnd % 2 == 0 else "kernel")
             out = _run(attn, V, plan=plan)
             assert_parity(out, ref, dt, C, f"round {rnd} {tuple(V.shape)} {mode} plan={plan.as_dict()}")
 
@@ -266,3 +300,33 @@ def test_bound_call_matches_decode(oracle_lib):
     torch.cuda.synchronize()
     assert_parity(out.cpu().numpy().astype(np.float64), ref, w.v_dtype, w.C, "bound call")
     assert torch.equal(out, ga.gqa_av_decode(a, v))
+
+
+@pytest.mark.parametrize("G", [5, 6, 7])
+@pytest.mark.parametrize("combine", ["kernel", "last"])
+def test_valu_groups_of_5_to_7(G, combine, oracle_lib):
+    """VALU tiles of 5-7 heads with 8 elements per lane: 40-56 accumulators, a
+    number that is not a multiple of the 32-slot reduction chunk."""
+    B, C, Hkv, D = 2, 700, 2, 256
+    attn, V = make_random(B, C, G * Hkv, Hkv, D, "bf16", seed=G)
+    ref = oracle_lib.full(attn, V, "bf16")
+    plan = ga.make_plan(B, C, G * Hkv, Hkv, D, "bf16", "reuse", engine="valu", nsplit=6, combine=combine)
+    assert plan.heads_per_tile == G
+    out = _run(attn, V, plan=plan)
+    assert_parity(out, ref, "bf16", C, f"G={G} {combine}")
+
+
+@pytest.mark.parametrize("wname", ["g2-b4-c32768-hq16-hkv8-d128-bf16", "mqa16-b4-c32768-hq16-hkv1-d128-bf16",
+                                   "tiny-f32-b1-c256-hq8-hkv2-d64"])
+def test_split_entry_points_equal_decode(wname):
+    """gqa_av_decode_pass1 then gqa_av_decode_combine is exactly gqa_av_decode_plan."""
+    w = WORKLOADS[wname]
+    attn, V = make_inputs(w, seed=6)
+    a, v = attn.to(DEV), V.to(DEV)
+    call = ga.bind(a, v)
+    whole = call().clone()
+    call.out.fill_(float("nan"))
+    call.pass1()
+    out = call.combine()
+    torch.cuda.synchronize()
+    assert torch.equal(out, whole)

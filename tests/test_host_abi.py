@@ -76,23 +76,25 @@ def _check_plan(p, B, C, Hq, Hkv, D, v_dtype, mode):
     es = 4 if v_dtype == "f32" else 2
     G = Hq // Hkv
     assert p.threads == 256
-    if p.engine == 1:                                   # MFMA: 16 lanes x D/16 elements per row
+    if p.engine == 2:                                   # MFMA: 16 lanes x D/16 elements per row
         assert p.mode == 1 and D % 16 == 0
         assert p.vec_bytes == D // 16 * es and p.lanes_per_row == 16 and p.row_slots == 16 and p.d_tiles == 1
         assert p.heads_per_tile in (16, 32)
+        tile_out = p.heads_per_tile * D
     else:
         assert p.vec_bytes in (16, 8, 4, 2) and (D * es) % p.vec_bytes == 0 and p.vec_bytes >= es
         L = D * es // p.vec_bytes
         assert p.lanes_per_row == min(L, 256)
         assert p.d_tiles == -(-L // p.lanes_per_row)
         assert p.row_slots == min(256 // p.lanes_per_row, 64)
+        tile_out = p.heads_per_tile * (p.vec_bytes // es) * p.lanes_per_row
     if C == 0:
         assert p.nsplit == 1
     else:
         assert p.nsplit >= 1 and p.rows_per_split >= 1
         assert -(-C // p.rows_per_split) == p.nsplit       # splits tile [0, C) exactly
     if p.mode == 1:
-        assert p.heads_per_tile >= min(G, 8) and (p.engine == 1 or p.heads_per_tile <= Hq)
+        assert p.heads_per_tile >= min(G, 8) and (p.engine == 2 or p.heads_per_tile <= Hq)
         assert p.subgroups == -(-G // p.heads_per_tile)
         tiles = B * Hkv * p.subgroups * p.d_tiles
         assert p.v_bytes_read == B * C * Hkv * D * es * p.subgroups
@@ -101,7 +103,12 @@ def _check_plan(p, B, C, Hq, Hkv, D, v_dtype, mode):
         tiles = B * Hq * p.d_tiles
         assert p.v_bytes_read == B * C * Hkv * D * es * G
     assert p.grid == tiles * p.nsplit
-    assert p.workspace_bytes == (p.nsplit * B * Hq * D * 4 if p.nsplit > 1 else 0)
+    if p.nsplit == 1:
+        assert p.combine == 0 and p.workspace_bytes == 0
+    elif p.combine == 2:                                # last workgroup adds: counters + tile blocks
+        assert p.workspace_bytes == -(-tiles * 4 // 256) * 256 + tiles * p.nsplit * (-(-tile_out // 4) * 4) * 4
+    else:
+        assert p.combine == 1 and p.workspace_bytes == p.nsplit * B * Hq * D * 4
 
 
 @pytest.mark.parametrize("wname", list(WORKLOADS))
@@ -154,7 +161,7 @@ def test_large_groups_use_subgroups():
     p = ga.make_plan(1, 4096, 40, 1, 128, "bf16", engine="valu")
     assert p.mode == 1 and p.heads_per_tile == 16 and p.subgroups == 3
     p = ga.make_plan(1, 4096, 40, 1, 128, "bf16")
-    assert p.mode == 1 and p.engine == 1 and p.heads_per_tile == 32 and p.subgroups == 2
+    assert p.mode == 1 and p.engine == 2 and p.heads_per_tile == 32 and p.subgroups == 2
 
 
 @pytest.mark.parametrize("args,status", [
@@ -221,31 +228,50 @@ def test_product_path_does_not_touch_the_oracle():
 
 
 @pytest.mark.parametrize("wname,engine", [
-    ("tiny-f32-b1-c256-hq8-hkv2-d64", 0), ("llama3-8b-b1-c4096-hq32-hkv8-d128-bf16", 0),
-    ("g3-b8-c16384-hq24-hkv8-d96-f16", 0), ("g2-b4-c32768-hq16-hkv8-d128-bf16", 0),
-    ("mqa16-b4-c32768-hq16-hkv1-d128-bf16", 1), ("batch64-b64-c8192-hq64-hkv8-d128-bf16", 1),
+    ("tiny-f32-b1-c256-hq8-hkv2-d64", 1), ("llama3-8b-b1-c4096-hq32-hkv8-d128-bf16", 1),
+    ("g3-b8-c16384-hq24-hkv8-d96-f16", 1), ("g2-b4-c32768-hq16-hkv8-d128-bf16", 1),
+    ("mqa16-b4-c32768-hq16-hkv1-d128-bf16", 2), ("batch64-b64-c8192-hq64-hkv8-d128-bf16", 2),
 ])
 def test_auto_engine(wname, engine):
     """Groups of 5 or more heads take the matrix-core engine, smaller ones the VALU engine."""
     w = WORKLOADS[wname]
     assert ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype).engine == engine
-    assert ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, "per_head").engine == 0
+    assert ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, "per_head").engine == 1
 
 
 def test_forced_engines():
     p = ga.make_plan(1, 300, 4, 2, 128, "bf16", engine="mfma")          # G = 2 on MFMA: allowed
-    assert p.engine == 1 and p.heads_per_tile == 16 and p.subgroups == 1
+    assert p.engine == 2 and p.heads_per_tile == 16 and p.subgroups == 1
     _check_plan(p, 1, 300, 4, 2, 128, "bf16", "auto")
     p = ga.make_plan(1, 300, 64, 1, 128, "bf16")                        # G = 64: 32-head sets
-    assert p.engine == 1 and p.heads_per_tile == 32 and p.subgroups == 2
+    assert p.engine == 2 and p.heads_per_tile == 32 and p.subgroups == 2
     p = ga.make_plan(1, 300, 64, 1, 256, "bf16")                        # D = 256: 16-head sets
-    assert p.engine == 1 and p.heads_per_tile == 16 and p.subgroups == 4
-    assert ga.make_plan(1, 300, 16, 1, 128, "bf16", engine="valu").engine == 0
+    assert p.engine == 2 and p.heads_per_tile == 16 and p.subgroups == 4
+    assert ga.make_plan(1, 300, 16, 1, 128, "bf16", engine="valu").engine == 1
     for args, kw in [((1, 300, 16, 1, 127, "bf16"), {}), ((1, 300, 16, 1, 128, "bf16", "per_head"), {}),
                      ((1, 300, 16, 1, 96, "f32"), {}), ((1, 300, 16, 1, 128, "bf16"), {"v_align": 8})]:
         with pytest.raises(ga.GqaAvError) as ei:
             ga.make_plan(*args, engine="mfma", **kw)
         assert ei.value.name == "UNSUPPORTED"
     # without the engine forced, shapes the MFMA engine cannot take fall back to VALU
-    assert ga.make_plan(1, 300, 16, 1, 127, "bf16").engine == 0
-    assert ga.make_plan(1, 300, 16, 1, 128, "bf16", v_align=8).engine == 0
+    assert ga.make_plan(1, 300, 16, 1, 127, "bf16").engine == 1
+    assert ga.make_plan(1, 300, 16, 1, 128, "bf16", v_align=8).engine == 1
+
+
+@pytest.mark.parametrize("combine,code", [("kernel", 1), ("last", 2)])
+def test_forced_combine(combine, code):
+    p = ga.make_plan(2, 5000, 16, 8, 128, "bf16", combine=combine, nsplit=9)
+    assert p.nsplit == 9 and p.combine == code
+    _check_plan(p, 2, 5000, 16, 8, 128, "bf16", "auto")
+    p1 = ga.make_plan(2, 5000, 16, 8, 128, "bf16", combine=combine, nsplit=1)
+    assert p1.nsplit == 1 and p1.combine == 0 and p1.workspace_bytes == 0
+
+
+def test_zeroed_hint_means_automatic():
+    lib = ga.load()
+    h, p, q = ga.Hint(), ga.Plan(), ga.Plan()
+    assert lib.gqa_av_make_plan(4, 32768, 16, 1, 128, 2, -1, ctypes.byref(h), ctypes.byref(p)) == 0
+    assert lib.gqa_av_make_plan(4, 32768, 16, 1, 128, 2, -1, None, ctypes.byref(q)) == 0
+    assert p.as_dict() == q.as_dict() and p.engine == 2
+    h.combine = 3
+    assert lib.gqa_av_make_plan(4, 32768, 16, 1, 128, 2, -1, ctypes.byref(h), ctypes.byref(p)) == 1

@@ -56,13 +56,16 @@ def parse():
     p = argparse.ArgumentParser(description=__doc__.splitlines()[1])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=-1,
+                   help="untimed warmup steps; -1 (default): at least 20 and about 0.25 s of GPU work, "
+                        "which MI355X needs to reach steady clocks")
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--mode", default="auto", choices=["auto", "per_head", "reuse"])
     p.add_argument("--nsplit", type=int, default=0, help="force the number of context splits (0 = plan)")
     p.add_argument("--engine", default="auto", choices=["auto", "valu", "mfma"])
     p.add_argument("--combine", default="auto", choices=["auto", "kernel", "last"],
                    help="how split partials are added (plan default: auto)")
+    p.add_argument("--kv-tile", type=int, default=0, help="adjacent KV heads per VALU workgroup (0 = plan)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle time budget")
     p.add_argument("--rotate-mb", type=float, default=ROTATE_BYTES / 2 ** 20)
@@ -221,7 +224,8 @@ def main():
 
     attn_h, V_h = make_inputs(w, seed=0)
     plan = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, args.mode, nsplit=args.nsplit,
-                        engine=args.engine, combine=args.combine, cu_count=props.multi_processor_count)
+                        engine=args.engine, combine=args.combine, kv_tile=args.kv_tile,
+                        cu_count=props.multi_processor_count)
     per_set = w.v_bytes() + w.attn_bytes() + w.out_bytes()
     nrot = max(1, math.ceil(args.rotate_mb * 2 ** 20 / per_set))
     sets = []
@@ -234,9 +238,21 @@ def main():
     calls = [ga.bind(a, v, o, plan=plan) for a, v, o in sets]
     stream = torch.cuda.current_stream(dev)
 
-    for i in range(args.warmup):
-        calls[i % nrot]()
+    warmup = args.warmup
+    if warmup < 0:
+        t0 = time.perf_counter()
+        for i in range(20):
+            calls[i % nrot]()
+        torch.cuda.synchronize()
+        per_call = (time.perf_counter() - t0) / 20
+        warmup = 20 + int(0.25 / max(per_call, 1e-6))
+        for i in range(20, warmup):
+            calls[i % nrot]()
+    else:
+        for i in range(warmup):
+            calls[i % nrot]()
     torch.cuda.synchronize()
+    args.warmup = warmup
 
     # Whole calls: the metric.
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -270,7 +286,7 @@ def main():
 
     split_kernel = plan.nsplit > 1 and plan.combine == 1
     traffic = recorded_traffic(w.name, args.mode) if (args.nsplit == 0 and args.engine == "auto"
-                                                      and args.combine == "auto") else None
+                                                      and args.combine == "auto" and args.kv_tile == 0) else None
     line = {
         "metric": METRIC,
         "value": round(gbs, 2),

@@ -37,7 +37,8 @@ class GqaAvError(RuntimeError):
 
 class Hint(ctypes.Structure):
     _fields_ = [("engine", ctypes.c_int32), ("nsplit", ctypes.c_int32), ("cu_count", ctypes.c_int32),
-                ("v_align", ctypes.c_int32), ("combine", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
+                ("v_align", ctypes.c_int32), ("combine", ctypes.c_int32), ("kv_tile", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 2)]
 
 
 class Plan(ctypes.Structure):
@@ -46,7 +47,7 @@ class Plan(ctypes.Structure):
                 ("row_slots", ctypes.c_int32), ("d_tiles", ctypes.c_int32), ("nsplit", ctypes.c_int32),
                 ("threads", ctypes.c_int32), ("rows_per_split", ctypes.c_int64), ("grid", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_int64), ("v_bytes_read", ctypes.c_int64),
-                ("combine", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
+                ("combine", ctypes.c_int32), ("kv_heads_per_tile", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
@@ -115,15 +116,16 @@ def resolve_mode(Hq: int, Hkv: int, mode: Union[str, int] = "auto") -> str:
 
 def make_plan(B: int, C: int, Hq: int, Hkv: int, D: int, v_dtype: str, mode: Union[str, int] = "auto",
               engine: Union[str, int] = "auto", nsplit: int = 0, cu_count: int = 0, v_align: int = 0,
-              combine: Union[str, int] = "auto") -> Plan:
-    """Host-only planning (no GPU needed). nsplit/cu_count/v_align <= 0 mean automatic.
+              combine: Union[str, int] = "auto", kv_tile: int = 0) -> Plan:
+    """Host-only planning (no GPU needed). nsplit/cu_count/v_align/kv_tile <= 0 mean automatic.
 
-    engine: "auto" | "valu" | "mfma"; combine: "auto" | "kernel" | "last".
+    engine: "auto" | "valu" | "mfma"; combine: "auto" | "kernel" | "last";
+    kv_tile: adjacent KV heads per VALU workgroup.
     """
     h = Hint()
     h.engine = ENGINES[engine] if isinstance(engine, str) else int(engine)
     h.combine = COMBINES[combine] if isinstance(combine, str) else int(combine)
-    h.nsplit, h.cu_count, h.v_align = int(nsplit), int(cu_count), int(v_align)
+    h.nsplit, h.cu_count, h.v_align, h.kv_tile = int(nsplit), int(cu_count), int(v_align), int(kv_tile)
     p = Plan()
     rc = load().gqa_av_make_plan(B, C, Hq, Hkv, D, DTYPES[v_dtype], _mode(mode), ctypes.byref(h), ctypes.byref(p))
     if rc != 0:

@@ -51,7 +51,8 @@ constexpr int kMaxRowSlots = 64;  // rows a VALU workgroup loads side by side, a
 
 // Tuning constants (compile-time; -D overrides build variants for sweeps).
 #ifndef GQA_AV_VALU_UNROLL
-#define GQA_AV_VALU_UNROLL 8      // rows per lane per stage, groups of up to 4 heads
+#define GQA_AV_VALU_UNROLL 4      // rows per lane per iteration, groups of up to 4 heads (4 measured
+                                  // best on MI355X: 3-4 % over 8, much better than 16 for D = 96)
 #endif
 #ifndef GQA_AV_VALU_PIPELINE
 #define GQA_AV_VALU_PIPELINE 0    // staged weights only: next stage's loads in flight during the current one
@@ -97,8 +98,9 @@ struct Pass1Args {
     int32_t nsg;            // head sub-groups per KV head (reuse)
     int32_t ndt;            // D-tiles (VALU)
     int32_t nsplit;
-    int32_t L;              // VALU: lanes per full D-row
-    int32_t Lc;             // VALU: lanes per D-row inside a workgroup (<= 256)
+    int32_t L;              // VALU: lanes per full D-row of one KV head
+    int32_t ht;             // VALU: adjacent KV heads per tile (their D-rows are contiguous)
+    int32_t Lc;             // VALU: lanes per tile row inside a workgroup (<= 256; ht * L when ht > 1)
     int32_t rps;            // VALU: row slots = min(256 / Lc, kMaxRowSlots)
     uint32_t nblocks;
 };
@@ -193,12 +195,14 @@ __device__ inline Tile decode_tile(const Pass1Args& a, int GT) {
     uint32_t t = xcd_remap(blockIdx.x, a.nblocks);
     Tile T;
     const uint32_t nminor = a.per_head ? a.ndt : a.nsg * a.ndt;
+    const uint32_t nkvt = a.Hkv / a.ht;              // tiles along the KV heads
     const uint32_t minor = t % nminor; t /= nminor;
-    T.kv = t % a.Hkv; t /= a.Hkv;
+    const uint32_t kvt = t % nkvt; t /= nkvt;
+    T.kv = kvt * a.ht;                               // first KV head of the tile
     T.s = t % a.nsplit; t /= a.nsplit;
     T.b = t % a.B; t /= a.B;
     const uint32_t major = t;
-    T.id = ((major * a.B + T.b) * a.Hkv + T.kv) * nminor + minor;
+    T.id = ((major * a.B + T.b) * nkvt + kvt) * nminor + minor;
     if (a.per_head) {
         T.dt = minor;
         T.q_first = T.kv * a.G + major;
@@ -317,7 +321,8 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
     const int Lc = a.Lc, rps = a.rps;
     const int r = tid / Lc;
     const int j = tid - r * Lc;
-    const int lane_d = T.dt * Lc + j;                // which VB-chunk of the D-row
+    const int kvl = j / a.L;                         // which KV head of the tile (0 when ht == 1)
+    const int lane_d = T.dt * Lc + (j - kvl * a.L);  // which VB-chunk of that head's D-row
     const bool active = (r < rps) && (lane_d < a.L);
 
     const int64_t cb = static_cast<int64_t>(T.s) * a.rows_per_split;
@@ -325,7 +330,7 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
     const int R = rps * U;                           // rows per stage
 
     const size_t vrow = static_cast<size_t>(a.Hkv) * a.D * ES;   // bytes from row c to c+1
-    const uint8_t* vbase = a.V + (static_cast<size_t>(T.b) * a.C * a.Hkv + T.kv) * a.D * ES
+    const uint8_t* vbase = a.V + (static_cast<size_t>(T.b) * a.C * a.Hkv + T.kv + kvl) * a.D * ES
                                + static_cast<size_t>(lane_d) * VB;
 
     float acc[GT][E];
@@ -335,8 +340,8 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
         for (int e = 0; e < E; ++e) acc[g][e] = 0.0f;
 
 #if GQA_AV_VALU_STAGE_WEIGHTS
-    const int q_lo = T.q_first;                      // accumulator g is head q_lo + g
-    const int g_off = 0;
+    const int q_lo = T.q_first;                      // accumulator g is head q_lo + g (tiles of one KV head)
+    auto lane_q_lo = [&](int) { return q_lo; };
     const float* abase = a.attn + static_cast<size_t>(T.b) * a.C * a.Hq + T.q_first;
     const int64_t nstage = ce > cb ? (ce - cb + R - 1) / R : 0;
 
@@ -448,8 +453,9 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
     // loads GT words at constant offsets and the window never leaves the attn
     // row (the planner keeps GT <= Hq). Accumulators outside the tile's own
     // heads are computed and dropped.
-    const int q_lo = min(T.q_first, a.Hq - GT);
-    const int g_off = T.q_first - q_lo;
+    // With ht > 1 every lane uses the window of its own KV head kv + kvl.
+    auto lane_q_lo = [&](int kl) { return min(T.q_first + kl * a.G, a.Hq - GT); };
+    const int q_lo = lane_q_lo(kvl);
     const float* wbase = a.attn + static_cast<size_t>(T.b) * a.C * a.Hq + q_lo;
     if (active) {
         int64_t c0 = cb;
@@ -499,9 +505,12 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
     float* const plane = (a.nsplit > 1 && !a.combine) ? a.part + static_cast<size_t>(T.s) * a.B * a.Hq * a.D : a.out;
     auto out_index = [&](int k, int jj, size_t* o) -> bool {
         const int g = k / E, e = k - (k / E) * E;
-        const int ld = T.dt * Lc + jj;
-        *o = (static_cast<size_t>(T.b) * a.Hq + q_lo + g) * a.D + static_cast<size_t>(ld) * E + e;
-        return g >= g_off && g < g_off + T.nq && ld < a.L;
+        const int kl = jj / a.L;
+        const int ld = T.dt * Lc + (jj - kl * a.L);
+        const int ql = lane_q_lo(kl);
+        const int go = T.q_first + kl * a.G - ql;    // accumulator of the tile's first head
+        *o = (static_cast<size_t>(T.b) * a.Hq + ql + g) * a.D + static_cast<size_t>(ld) * E + e;
+        return g >= go && g < go + T.nq && ld < a.L;
     };
 #pragma unroll
     for (int k0 = 0; k0 < NACC; k0 += CH) {

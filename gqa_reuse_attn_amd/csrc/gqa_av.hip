@@ -11,6 +11,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -52,8 +53,14 @@ int head_capacity(int64_t G) {
 
 
 constexpr int kDefaultCUs = 256;
-constexpr int64_t kMinRowsPerSplit = 256;     // below this a split's epilogue dominates
-constexpr int64_t kTargetWgPerCU = 8;
+// Context-split sizing, measured on MI355X. The VALU engine streams best with
+// few long-running workgroups (about 2 per CU): a plain streaming read shows
+// the same (7.0 TB/s with 512-1024 blocks, 6.8 with 4096). The MFMA engine
+// hides less latency per workgroup and wants more of them.
+constexpr int64_t kMinRowsPerSplit = 128;     // VALU: below this a split's epilogue dominates
+constexpr int64_t kMinRowsPerSplitMfma = 256;
+constexpr int64_t kTargetWgPerCuValu = 2;
+constexpr int64_t kTargetWgPerCuMfma = 8;
 
 // Split-C workspace of one (device, stream). The per-tile counters live in a
 // buffer of their own: they must be zero before a call, every call leaves the
@@ -296,6 +303,28 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
         return fail(GQA_AV_ERR_UNSUPPORTED,
                     "MFMA engine needs reuse mode, D %% 16 == 0 with a 4/8/12/16/32-byte lane chunk and matching V alignment");
 
+    // KV heads per tile: only the VALU engine in reuse mode streams several.
+    // Automatic: two adjacent heads (a 2 x D contiguous slice of each row)
+    // when the split grid still reaches its workgroup target with splits of
+    // at least kMinRowsPerSplit rows; measured 4-12 % faster than one head.
+    int ht = h.kv_tile > 0 ? h.kv_tile : 1;
+    if (h.kv_tile <= 0 && engine == GQA_AV_ENGINE_VALU && resolved == GQA_AV_REUSE && Hkv % 2 == 0 &&
+        !GQA_AV_VALU_STAGE_WEIGHTS) {
+        const int64_t lanes = (D * es) / 16 > 0 && (D * es) % 16 == 0 ? (D * es) / 16 : 0;
+        const int64_t nsg2 = ceil_div(G, head_capacity(G));
+        const int64_t tiles2 = B * (Hkv / 2) * nsg2;
+        const int64_t target = kTargetWgPerCuValu * cus;
+        if (lanes > 0 && 2 * lanes <= gqa_av::kThreads && v_align % 16 == 0 && tiles2 > 0 &&
+            tiles2 * std::min<int64_t>(ceil_div(target, tiles2), std::max<int64_t>(1, C / kMinRowsPerSplit)) >= target)
+            ht = 2;
+    }
+    if (ht > 1) {
+        if (engine != GQA_AV_ENGINE_VALU || resolved != GQA_AV_REUSE || GQA_AV_VALU_STAGE_WEIGHTS)
+            return fail(GQA_AV_ERR_UNSUPPORTED, "kv_tile > 1 needs the VALU engine in reuse mode");
+        if (Hkv % ht != 0)
+            return fail(GQA_AV_ERR_INVALID_ARG, "kv_tile %d does not divide Hkv=%lld", ht, (long long)Hkv);
+    }
+
     int VB, GT, nsg;
     int64_t Lc, rps, ndt, rows_per_step, tile_outputs;
     int64_t heads_major;  // tiles along the head axis per KV head
@@ -320,8 +349,18 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
             return fail(GQA_AV_ERR_UNSUPPORTED, "V must be aligned to its element size (%d bytes)", es);
         const int64_t E = VB / es;
         const int64_t L = D / E;
-        Lc = L < gqa_av::kThreads ? L : gqa_av::kThreads;
-        ndt = ceil_div(L, Lc);
+        if (ht > 1) {
+            // Several adjacent KV heads per workgroup: their D-rows form one
+            // contiguous tile row, which must fit the workgroup's lanes.
+            if (L * ht > gqa_av::kThreads)
+                return fail(GQA_AV_ERR_UNSUPPORTED, "kv_tile %d: %lld lanes per tile row exceed %d", ht,
+                            (long long)(L * ht), gqa_av::kThreads);
+            Lc = L * ht;
+            ndt = 1;
+        } else {
+            Lc = L < gqa_av::kThreads ? L : gqa_av::kThreads;
+            ndt = ceil_div(L, Lc);
+        }
         rps = gqa_av::kThreads / Lc;
         if (rps > gqa_av::kMaxRowSlots) rps = gqa_av::kMaxRowSlots;
         if (resolved == GQA_AV_REUSE) {
@@ -336,7 +375,7 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
         rows_per_step = rps * gqa_av::valu_unroll(GT);
         tile_outputs = static_cast<int64_t>(GT) * E * Lc;
     }
-    const int64_t tiles = B * Hkv * heads_major * ndt;
+    const int64_t tiles = B * (Hkv / ht) * heads_major * ndt;
 
     int64_t nsplit = 1, rows_per_split = C;
     if (C > 0) {
@@ -344,9 +383,9 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
             nsplit = h.nsplit < C ? h.nsplit : C;
             rows_per_split = ceil_div(C, nsplit);
         } else {
-            const int64_t target = kTargetWgPerCU * cus;
+            const int64_t target = (engine == GQA_AV_ENGINE_MFMA ? kTargetWgPerCuMfma : kTargetWgPerCuValu) * cus;
             nsplit = tiles > 0 ? ceil_div(target, tiles) : 1;
-            const int64_t cap = ceil_div(C, kMinRowsPerSplit);
+            const int64_t cap = ceil_div(C, engine == GQA_AV_ENGINE_MFMA ? kMinRowsPerSplitMfma : kMinRowsPerSplit);
             if (nsplit > cap) nsplit = cap;
             if (nsplit < 1) nsplit = 1;
             rows_per_split = ceil_div(ceil_div(C, nsplit), rows_per_step) * rows_per_step;
@@ -382,6 +421,7 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
             return fail(GQA_AV_ERR_UNSUPPORTED, "a tile's split partials exceed 2 GB; use the kernel combine");
     }
     plan->combine = combine;
+    plan->kv_heads_per_tile = ht;
     plan->workspace_bytes = workspace_bytes(B, Hq, D, tiles, nsplit, tile_outputs, combine);
     plan->v_bytes_read = B * C * Hkv * D * es * heads_major;
     return GQA_AV_OK;
@@ -392,7 +432,7 @@ bool same_plan(const gqa_av_plan& a, const gqa_av_plan& b) {
            a.subgroups == b.subgroups && a.vec_bytes == b.vec_bytes && a.lanes_per_row == b.lanes_per_row &&
            a.row_slots == b.row_slots && a.d_tiles == b.d_tiles && a.nsplit == b.nsplit &&
            a.threads == b.threads && a.rows_per_split == b.rows_per_split && a.grid == b.grid &&
-           a.workspace_bytes == b.workspace_bytes;
+           a.workspace_bytes == b.workspace_bytes && a.kv_heads_per_tile == b.kv_heads_per_tile;
 }
 
 }  // namespace
@@ -448,6 +488,7 @@ int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C,
     h.nsplit = plan->nsplit;
     h.v_align = plan->vec_bytes;
     h.combine = plan->combine;
+    h.kv_tile = plan->kv_heads_per_tile;
     gqa_av_plan check;
     const int mode = plan->mode;
     // Re-plan with the split count fixed: rows_per_split then follows from C.
@@ -472,7 +513,10 @@ int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C,
     }
     const int64_t tiles_per_split = plan->grid / plan->nsplit;
     const int64_t heads_major = plan->mode == GQA_AV_REUSE ? plan->subgroups : Hq / Hkv;
-    if (plan->grid % plan->nsplit != 0 || tiles_per_split != B * Hkv * heads_major * plan->d_tiles)
+    if (plan->kv_heads_per_tile < 1 || Hkv % plan->kv_heads_per_tile != 0)
+        return fail(GQA_AV_ERR_INVALID_ARG, "plan kv_heads_per_tile does not divide Hkv");
+    if (plan->grid % plan->nsplit != 0 ||
+        tiles_per_split != B * (Hkv / plan->kv_heads_per_tile) * heads_major * plan->d_tiles)
         return fail(GQA_AV_ERR_INVALID_ARG, "plan grid does not match the problem");
     const int64_t tile_outputs = plan->engine == GQA_AV_ENGINE_MFMA
         ? static_cast<int64_t>(plan->heads_per_tile) * D
@@ -524,6 +568,7 @@ int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C,
     a.ndt = plan->d_tiles;
     a.nsplit = plan->nsplit;
     a.L = static_cast<int32_t>(D * elem_bytes(v_dtype) / plan->vec_bytes);
+    a.ht = plan->kv_heads_per_tile;
     a.Lc = plan->lanes_per_row;
     a.rps = plan->row_slots;
     a.nblocks = static_cast<uint32_t>(plan->grid);

@@ -108,7 +108,8 @@ typedef struct gqa_av_hint {
     int32_t cu_count;   /* compute units to plan for; auto = the device's (decode) or 256 (make_plan) */
     int32_t v_align;    /* byte alignment of V's base address; auto = 16 */
     int32_t combine;    /* gqa_av_combine for context splits */
-    int32_t reserved[3];
+    int32_t kv_tile;    /* adjacent KV heads per VALU workgroup (their D-rows are contiguous) */
+    int32_t reserved[2];
 } gqa_av_hint;
 
 /* A launch plan: what gqa_av_decode_plan will run. Produced by gqa_av_make_plan. */
@@ -118,7 +119,7 @@ typedef struct gqa_av_plan {
     int32_t heads_per_tile;  /* query heads one workgroup computes (reuse: VALU 1-4, 8 or 16; MFMA 16 or 32; per-head: 1) */
     int32_t subgroups;       /* workgroups that share one KV head's rows (ceil(G / heads_per_tile)) */
     int32_t vec_bytes;       /* bytes of V each lane loads per row (VALU: 16, 8, 4, 2; MFMA: D/16 elements) */
-    int32_t lanes_per_row;   /* lanes covering one D-row of V inside a workgroup */
+    int32_t lanes_per_row;   /* lanes covering one row of the tile (kv_heads_per_tile D-rows) */
     int32_t row_slots;       /* rows a workgroup loads side by side */
     int32_t d_tiles;         /* workgroups along D */
     int32_t nsplit;          /* context splits (1 = no partial sums) */
@@ -128,7 +129,8 @@ typedef struct gqa_av_plan {
     int64_t workspace_bytes; /* device workspace the plan needs (0 if nsplit == 1) */
     int64_t v_bytes_read;    /* V bytes the plan reads from memory (G x more for per-head) */
     int32_t combine;         /* resolved gqa_av_combine: KERNEL or LAST when nsplit > 1, else AUTO */
-    int32_t reserved[3];
+    int32_t kv_heads_per_tile; /* adjacent KV heads one workgroup streams (VALU reuse; else 1) */
+    int32_t reserved[2];
 } gqa_av_plan;
 
 /* Resolve `mode` for a head shape. Host-only: needs no GPU.

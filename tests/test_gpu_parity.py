@@ -89,13 +89,23 @@ def _plans(B, C, Hq, Hkv, D, dt, ns):
                 plans.append((eng, ga.make_plan(B, C, Hq, Hkv, D, dt, "reuse", engine=eng, nsplit=ns)))
             except ga.GqaAvError as e:
                 assert e.name == "UNSUPPORTED"
+    if Hq // Hkv >= 2 and Hkv > 1:
+        for ht in (2, Hkv):
+            if Hkv % ht == 0:
+                try:
+                    plans.append((f"kv_tile={ht}", ga.make_plan(B, C, Hq, Hkv, D, dt, "reuse", engine="valu",
+                                                                 nsplit=ns, kv_tile=ht)))
+                except ga.GqaAvError as e:
+                    assert e.name == "UNSUPPORTED"
     for name, p in list(plans):
         if p.nsplit > 1:
             other = "last" if p.combine == 1 else "kernel"
             mode = "per_head" if p.mode == 0 else ("reuse" if name != "auto" else "auto")
             eng = {1: "valu", 2: "mfma"}[p.engine]
+            if name.startswith("kv_tile"):
+                mode = "reuse"
             plans.append((f"{name}/{other}", ga.make_plan(B, C, Hq, Hkv, D, dt, mode, engine=eng, nsplit=ns,
-                                                          combine=other)))
+                                                          combine=other, kv_tile=p.kv_heads_per_tile)))
     return plans
 
 
@@ -330,3 +340,18 @@ def test_split_entry_points_equal_decode(wname):
     out = call.combine()
     torch.cuda.synchronize()
     assert torch.equal(out, whole)
+
+
+
+@pytest.mark.parametrize("wname,ht", [("g2-b4-c32768-hq16-hkv8-d128-bf16", 8), ("g2-b4-c32768-hq16-hkv8-d128-bf16", 2),
+                                      ("g3-b8-c16384-hq24-hkv8-d96-f16", 4),
+                                      ("llama3-8b-b1-c4096-hq32-hkv8-d128-bf16", 8)])
+def test_workload_kv_tiles(wname, ht, oracle_lib):
+    """Full-size workloads with several adjacent KV heads per workgroup."""
+    w = WORKLOADS[wname]
+    attn, V = make_inputs(w, seed=0)
+    ref = oracle_lib.full(attn, V, w.v_dtype)
+    plan = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, "reuse", engine="valu", kv_tile=ht,
+                        cu_count=torch.cuda.get_device_properties(0).multi_processor_count)
+    out = _run(attn, V, plan=plan)
+    assert_parity(out, ref, w.v_dtype, w.C, f"{wname} kv_tile={ht} plan={plan.as_dict()}")

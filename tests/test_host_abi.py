@@ -84,8 +84,12 @@ def _check_plan(p, B, C, Hq, Hkv, D, v_dtype, mode):
     else:
         assert p.vec_bytes in (16, 8, 4, 2) and (D * es) % p.vec_bytes == 0 and p.vec_bytes >= es
         L = D * es // p.vec_bytes
-        assert p.lanes_per_row == min(L, 256)
-        assert p.d_tiles == -(-L // p.lanes_per_row)
+        ht = p.kv_heads_per_tile
+        if ht > 1:
+            assert p.lanes_per_row == ht * L <= 256 and p.d_tiles == 1 and Hkv % ht == 0
+        else:
+            assert p.lanes_per_row == min(L, 256)
+            assert p.d_tiles == -(-L // p.lanes_per_row)
         assert p.row_slots == min(256 // p.lanes_per_row, 64)
         tile_out = p.heads_per_tile * (p.vec_bytes // es) * p.lanes_per_row
     if C == 0:
@@ -96,7 +100,7 @@ def _check_plan(p, B, C, Hq, Hkv, D, v_dtype, mode):
     if p.mode == 1:
         assert p.heads_per_tile >= min(G, 8) and (p.engine == 2 or p.heads_per_tile <= Hq)
         assert p.subgroups == -(-G // p.heads_per_tile)
-        tiles = B * Hkv * p.subgroups * p.d_tiles
+        tiles = B * (Hkv // p.kv_heads_per_tile) * p.subgroups * p.d_tiles
         assert p.v_bytes_read == B * C * Hkv * D * es * p.subgroups
     else:
         assert p.heads_per_tile == 1
@@ -275,3 +279,22 @@ def test_zeroed_hint_means_automatic():
     assert p.as_dict() == q.as_dict() and p.engine == 2
     h.combine = 3
     assert lib.gqa_av_make_plan(4, 32768, 16, 1, 128, 2, -1, ctypes.byref(h), ctypes.byref(p)) == 1
+
+
+def test_kv_tile():
+    p = ga.make_plan(4, 32768, 16, 8, 128, "bf16", kv_tile=8)
+    assert p.kv_heads_per_tile == 8 and p.lanes_per_row == 128 and p.row_slots == 2
+    _check_plan(p, 4, 32768, 16, 8, 128, "bf16", "auto")
+    p = ga.make_plan(8, 16384, 24, 8, 96, "f16", kv_tile=4)
+    assert p.kv_heads_per_tile == 4 and p.lanes_per_row == 48 and p.row_slots == 5
+    _check_plan(p, 8, 16384, 24, 8, 96, "f16", "auto")
+    assert ga.make_plan(4, 100, 16, 8, 128, "bf16").kv_heads_per_tile >= 1
+    for kw, status in [(dict(kv_tile=3), "INVALID_ARG"),                      # does not divide Hkv
+                       (dict(kv_tile=2, mode="per_head"), "UNSUPPORTED"),
+                       (dict(kv_tile=2, engine="mfma"), "UNSUPPORTED")]:
+        with pytest.raises(ga.GqaAvError) as ei:
+            ga.make_plan(4, 100, 16, 8, 128, "bf16", **kw)
+        assert ei.value.name == status
+    with pytest.raises(ga.GqaAvError) as ei:                                 # 32 x 16 lanes > 256
+        ga.make_plan(1, 100, 64, 32, 128, "bf16", kv_tile=32, engine="valu")
+    assert ei.value.name == "UNSUPPORTED"

@@ -63,6 +63,9 @@ constexpr int kMaxRowSlots = 64;  // rows a VALU workgroup loads side by side, a
 #ifndef GQA_AV_MFMA_UNROLL
 #define GQA_AV_MFMA_UNROLL 4      // row groups of four per wave and step (16-byte lanes)
 #endif
+#ifndef GQA_AV_MFMA_PIPELINE
+#define GQA_AV_MFMA_PIPELINE 1    // 1: the next step's loads in flight during the current step's MFMAs
+#endif
 constexpr int valu_unroll(int GT) {
     return GT <= 4 ? GQA_AV_VALU_UNROLL : (GT <= 8 ? (GQA_AV_VALU_UNROLL + 1) / 2 : (GQA_AV_VALU_UNROLL + 3) / 4);
 }
@@ -571,10 +574,16 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma(Pass1Args a) {
     const size_t vrow = static_cast<size_t>(a.Hkv) * a.D * ES;
     const uint8_t* vbase = a.V + (static_cast<size_t>(T.b) * a.C * a.Hkv + T.kv) * a.D * ES
                                + static_cast<size_t>(n) * NB;
-    const float* abase = a.attn + static_cast<size_t>(T.b) * a.C * a.Hq + T.q_first + n;
-    bool hv[NSET];
+    // Lane n of set s reads head q_first + 16 s + n. Heads past the tile's nq
+    // read the tile's last head instead (a valid address): their A-operand row
+    // only feeds output rows past nq, which are never written. Every load is
+    // unconditional and no loaded value is touched before the MFMA, so the
+    // compiler's wait counts stay exact and the next step's loads overlap the
+    // current step's MFMAs.
+    const float* abase = a.attn + static_cast<size_t>(T.b) * a.C * a.Hq + T.q_first;
+    int woff[NSET];
 #pragma unroll
-    for (int s = 0; s < NSET; ++s) hv[s] = n + 16 * s < T.nq;
+    for (int s = 0; s < NSET; ++s) woff[s] = min(n + 16 * s, T.nq - 1);
 
     f32x4 acc[NSET][DE];
 #pragma unroll
@@ -594,16 +603,23 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma(Pass1Args a) {
                 const int64_t c = row_of(c0, u);
                 rv[u] = load_raw<NB>(vbase + static_cast<size_t>(c) * vrow);
 #pragma unroll
-                for (int s = 0; s < NSET; ++s) rw[u][s] = hv[s] ? abase[c * a.Hq + 16 * s] : 0.0f;
+                for (int s = 0; s < NSET; ++s) rw[u][s] = abase[c * a.Hq + woff[s]];
             }
         } else {
+            // Last, partial step: rows past ce read row ce - 1 and are zeroed.
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int64_t c = row_of(c0, u);
                 const bool in = c < ce;
-                rv[u] = in ? load_raw<NB>(vbase + static_cast<size_t>(c) * vrow) : zero_raw<NB>();
+                const int64_t cc = in ? c : ce - 1;
+                const Raw<NB> raw = load_raw<NB>(vbase + static_cast<size_t>(cc) * vrow);
 #pragma unroll
-                for (int s = 0; s < NSET; ++s) rw[u][s] = (in && hv[s]) ? abase[c * a.Hq + 16 * s] : 0.0f;
+                for (int i = 0; i < (NB >= 4 ? NB / 4 : 1); ++i) rv[u].w[i] = in ? raw.w[i] : 0u;
+#pragma unroll
+                for (int s = 0; s < NSET; ++s) {
+                    const float w = abase[cc * a.Hq + woff[s]];
+                    rw[u][s] = in ? w : 0.0f;
+                }
             }
         }
     };
@@ -620,6 +636,7 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma(Pass1Args a) {
         }
     };
 
+#if GQA_AV_MFMA_PIPELINE
     Raw<NB> vA[U], vB[U];
     float wA[U][NSET], wB[U][NSET];
     int64_t st = 0;
@@ -632,6 +649,14 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma(Pass1Args a) {
         compute(vB, wB);
     }
     if (st < nsteps) compute(vA, wA);
+#else
+    for (int64_t st = 0; st < nsteps; ++st) {
+        Raw<NB> v[U];
+        float w[U][NSET];
+        load(v, w, cb + st * RSTEP);
+        compute(v, w);
+    }
+#endif
 
     // Add the four waves' 16 x D tiles. Register i of acc[s][e] in lane l is
     // head 16 s + 4 (l / 16) + i, element d = (l % 16) * DE + e; as a tile

@@ -53,14 +53,13 @@ int head_capacity(int64_t G) {
 
 
 constexpr int kDefaultCUs = 256;
-// Context-split sizing, measured on MI355X. The VALU engine streams best with
-// few long-running workgroups (about 2 per CU): a plain streaming read shows
-// the same (7.0 TB/s with 512-1024 blocks, 6.8 with 4096). The MFMA engine
-// hides less latency per workgroup and wants more of them.
+// Context-split sizing, measured on MI355X. Both engines stream best with few
+// long-running workgroups (VALU about 2 per CU, MFMA about 1): a plain
+// streaming read shows the same (7.0 TB/s with 512-1024 blocks, 6.8 with 4096).
 constexpr int64_t kMinRowsPerSplit = 128;     // VALU: below this a split's epilogue dominates
 constexpr int64_t kMinRowsPerSplitMfma = 256;
 constexpr int64_t kTargetWgPerCuValu = 2;
-constexpr int64_t kTargetWgPerCuMfma = 8;
+constexpr int64_t kTargetWgPerCuMfma = 1;
 
 // Split-C workspace of one (device, stream). The per-tile counters live in a
 // buffer of their own: they must be zero before a call, every call leaves the

@@ -62,7 +62,7 @@ def parse():
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--mode", default="auto", choices=["auto", "per_head", "reuse"])
     p.add_argument("--nsplit", type=int, default=0, help="force the number of context splits (0 = plan)")
-    p.add_argument("--engine", default="auto", choices=["auto", "valu", "mfma"])
+    p.add_argument("--engine", default="auto", choices=["auto", "valu", "mfma", "mfma_bf16"])
     p.add_argument("--combine", default="auto", choices=["auto", "kernel", "last"],
                    help="how split partials are added (plan default: auto)")
     p.add_argument("--kv-tile", type=int, default=0, help="adjacent KV heads per VALU workgroup (0 = plan)")

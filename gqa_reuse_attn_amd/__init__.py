@@ -22,7 +22,7 @@ __all__ = [
 LIB_PATH = os.environ.get("GQA_AV_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_av.so")
 
 MODES = {"auto": -1, "per_head": 0, "reuse": 1}
-ENGINES = {"auto": 0, "valu": 1, "mfma": 2}
+ENGINES = {"auto": 0, "valu": 1, "mfma": 2, "mfma_bf16": 3}
 COMBINES = {"auto": 0, "kernel": 1, "last": 2}
 DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "INELIGIBLE", 3: "UNSUPPORTED", 4: "HIP"}

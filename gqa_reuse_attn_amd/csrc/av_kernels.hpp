@@ -66,6 +66,9 @@ constexpr int kMaxRowSlots = 64;  // rows a VALU workgroup loads side by side, a
 #ifndef GQA_AV_MFMA_PIPELINE
 #define GQA_AV_MFMA_PIPELINE 1    // 1: the next step's loads in flight during the current step's MFMAs
 #endif
+#ifndef GQA_AV_MFMA_BF16_CHUNKS
+#define GQA_AV_MFMA_BF16_CHUNKS 1 // bf16 matrix engine: 32-row chunks per wave and buffer (two buffers)
+#endif
 constexpr int valu_unroll(int GT) {
     return GT <= 4 ? GQA_AV_VALU_UNROLL : (GT <= 8 ? (GQA_AV_VALU_UNROLL + 1) / 2 : (GQA_AV_VALU_UNROLL + 3) / 4);
 }
@@ -114,6 +117,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short short4v __attribute__((ext_vector_type(4)));
 
 template <int NB>
 struct Raw {
@@ -184,6 +189,13 @@ __device__ inline void widen(const Raw<NB>& r, float* f) {
     }
 }
 
+// A value that is the same in every lane, moved to scalar registers.
+__device__ inline int64_t uniform64(int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(x) >> 32));
+    return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // ---- tile decode ------------------------------------------------------------
 
 struct Tile {
@@ -242,6 +254,7 @@ constexpr int kQuadsPerBlock = kThreads / kSplitGroups;
 // Buffer-resource word 3 for raw (untyped) buffer access on gfx9-family parts.
 constexpr int kRawBufferFlags = 0x00020000;
 constexpr int kCachePolicySc1 = 16;   // device-scope coherence (same policy as agent-scope atomics)
+constexpr int kCachePolicyNt = 2;     // non-temporal (streamed once)
 
 // Called by all threads of a workgroup after each stored its share of the
 // split's TO partial sums with store_coherent() into blk = the tile's block
@@ -679,6 +692,235 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma(Pass1Args a) {
         const int g = 16 * s + 4 * (l >> 4) + i;
         *o = (static_cast<size_t>(T.b) * a.Hq + T.q_first + g) * a.D + (l & 15) * DE + e;
         return g < T.nq;
+    };
+    for (int idx = threadIdx.x; idx < TO; idx += kThreads) {
+        float sum = red[idx];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) sum += red[w * TO + idx];
+        if (in_kernel) {
+            store_coherent(blk + static_cast<size_t>(T.s) * TO + idx, sum);
+        } else {
+            size_t o;
+            if (out_index(idx, &o)) plane[o] = sum;
+        }
+    }
+    if (in_kernel) {
+        combine_last(a, T, blk, TO, [&](int idx, float v) {
+            size_t o;
+            if (out_index(idx, &o)) a.out[o] = v;
+        });
+    }
+}
+
+// ---- pass 1: bf16 matrix-core engine ----------------------------------------
+
+// For bf16 V the fp32 matrix instruction above is the bottleneck at large G:
+// a 16-head set costs 2 * 16 * D flops per V row at the fp32 matrix rate,
+// which at 8 TB/s of V keeps every SIMD about 80 % busy. This engine uses
+// v_mfma_f32_16x16x32_bf16 instead (eight times the fp32 matrix rate per
+// instruction slot) and keeps the products exact:
+//  * each fp32 weight w is split into three bf16 terms by truncation,
+//    hi = trunc(w), mid = trunc(w - hi), lo = w - hi - mid. Both subtractions
+//    are exact (Sterbenz) and lo has at most 8 significant bits, so
+//    w = hi + mid + lo exactly for every normal w down to 2^-103; each
+//    product V * term is exact in fp32 (8-bit by 8-bit significands);
+//  * one 16 x 16 output tile takes three instructions per 32 context rows,
+//    so the matrix core is about 15 % busy at 8 TB/s.
+// Operand layout (K = 32 context rows): lane 16 g + m holds, in its eight
+// 16-bit slots j = 0..7, A[head m][row 8 g + j] and B[row 8 g + j][column m].
+// B needs eight rows of one column per lane while a V row is contiguous along
+// D, so each wave writes its 32 rows to a private LDS region as loaded
+// (16-byte lane stores) and reads the columns back as 16-bit loads. 16-byte
+// pieces of a row are XOR-swizzled by its row group (row / 8) so the four
+// lane groups of a column read hit different banks.
+//
+// PR = D / 8 16-byte pieces per row (8, 16 or 32); NSET sets of 16 heads; U
+// chunks of 32 rows per wave and buffer, two buffers in flight.
+template <int PR, int NSET, int U>
+__global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
+    static_assert(PR == 8 || PR == 16 || PR == 32, "D must be 64, 128 or 256");
+    constexpr int D = PR * 8;
+    constexpr int RB = PR * 16;                      // bytes of one D-row
+    constexpr int NT = D / 16;                       // 16-column output tiles
+    constexpr int LPI = PR / 2;                      // 16-byte loads per lane and chunk
+    constexpr int RPI = 64 / PR;                     // rows one 64-lane load covers
+    constexpr int TO = 16 * NSET * D;                // outputs of the tile
+    constexpr int STAGE = kWaves * 32 * RB;          // bytes: one 32-row region per wave
+    constexpr int RED = kWaves * TO * 4;             // bytes: the final cross-wave sum
+    __shared__ __align__(16) uint8_t smem[STAGE > RED ? STAGE : RED];
+
+    const Tile T = decode_tile(a, 16 * NSET);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4;                         // K group: rows 8 g .. 8 g + 7 of a chunk
+    const int m = lane & 15;                         // head (A) / column (B) inside a tile
+
+    // The split bounds are workgroup-uniform; keep them in scalar registers.
+    const int64_t cb = uniform64(static_cast<int64_t>(T.s) * a.rows_per_split);
+    const int64_t ce = uniform64(min(a.C, cb + a.rows_per_split));
+    const int nrows = static_cast<int>(ce - cb);     // > 0: splits never start past C
+    const int vrow = a.Hkv * D * 2;                  // bytes between consecutive rows of V
+
+    // Both operands are read through buffer resources that end with the
+    // split's last row: a row at or past ce reads as zero, so a partial last
+    // step needs no clamping or masking, and a step wholly past ce (the
+    // pipeline's unconditional reload) touches no memory. The plan keeps a
+    // split's V span under 2 GB so 32-bit offsets suffice.
+    const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.V) + ((static_cast<size_t>(T.b) * a.C + cb) * a.Hkv + T.kv) * D * 2, 0,
+        (nrows - 1) * vrow + D * 2, kRawBufferFlags);
+    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(a.attn) + (static_cast<size_t>(T.b) * a.C + cb) * a.Hq + T.q_first, 0,
+        ((nrows - 1) * a.Hq + T.nq) * 4, kRawBufferFlags);
+    // This lane's pieces of a chunk: load i covers rows RPI i .. RPI i + RPI - 1.
+    const int prow = lane / PR, ppiece = lane % PR;
+    const int vlane = prow * vrow + ppiece * 16;
+    // Heads past the tile's nq read the tile's last head (in range); their A
+    // rows only feed output rows that are never written.
+    int wlane[NSET];
+#pragma unroll
+    for (int s = 0; s < NSET; ++s) wlane[s] = (8 * g * a.Hq + min(m + 16 * s, T.nq - 1)) * 4;
+
+    // LDS region of this wave: 32 rows of RB bytes, each row cut into 32-byte
+    // column pairs (16 columns) whose order is XORed with swz(row) so that
+    // both the row stores and the transposing reads spread over the banks.
+    typedef __attribute__((address_space(3))) uint8_t lds_u8;
+    typedef __attribute__((address_space(3))) short4v lds_s4;
+    lds_u8* const region = (lds_u8*)(smem) + wave * 32 * RB;
+    auto swz = [](int row) {
+        return PR == 8 ? (((row & 3) ^ (row >> 3)) & 3) : (((row & 3) | ((row >> 3) << 2)) & (PR / 2 - 1));
+    };
+    // Load i's 16-byte piece of row RPI i + prow ...
+    auto st_off = [&](int i) {
+        const int row = RPI * i + prow;
+        return row * RB + 32 * ((ppiece >> 1) ^ swz(row)) + 16 * (ppiece & 1);
+    };
+    // ... and the transposing read of rows 8 g + 4 h .. 8 g + 4 h + 3 for
+    // column tile t: source lane 4 k + q of a 16-lane group points at row
+    // 8 g + 4 h + k, columns 16 t + 4 q .. 16 t + 4 q + 3; ds_read_b64_tr_b16
+    // then hands lane m of the group the column 16 t + m of those four rows.
+    auto tr_off = [&](int t, int h) {
+        const int row = 8 * g + 4 * h + ((lane & 15) >> 2);
+        return row * RB + 32 * (t ^ swz(row)) + 8 * (lane & 3);
+    };
+
+    f32x4 acc[NSET][NT];
+#pragma unroll
+    for (int s = 0; s < NSET; ++s)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[s][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    constexpr int RSTEP = 32 * kWaves * U;           // rows per workgroup step
+    const int nsteps = (nrows + RSTEP - 1) / RSTEP;
+
+    struct Buf {
+        u32x4 v[U][LPI];
+        float w[U][NSET][8];
+    };
+    // Chunk u of step st starts at split row 32 (st kWaves U + u kWaves + wave).
+    auto load = [&](Buf& bf, int st) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int r0 = 32 * (st * kWaves * U + u * kWaves + wave);
+#pragma unroll
+            for (int i = 0; i < LPI; ++i)
+                bf.v[u][i] = __builtin_amdgcn_raw_buffer_load_b128(vres, vlane, (r0 + RPI * i) * vrow, kCachePolicyNt);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int s = 0; s < NSET; ++s)
+                    bf.w[u][s][j] = __uint_as_float(
+                        __builtin_amdgcn_raw_buffer_load_b32(wres, wlane[s], (r0 + j) * a.Hq * 4, 0));
+        }
+    };
+    auto consume = [&](const Buf& bf) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            // The region's previous contents have been read (in program
+            // order; LDS executes one wave's operations in order).
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int i = 0; i < LPI; ++i)
+                *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(region + st_off(i)) = bf.v[u][i];
+            asm volatile("" ::: "memory");
+            // Split the weights: three bf16x8 A operands per head set.
+            u32x4 aw[3][NSET];
+#pragma unroll
+            for (int s = 0; s < NSET; ++s) {
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    uint32_t th[2], tm[2], tl[2];
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const float w = bf.w[u][s][2 * p + e];
+                        th[e] = __float_as_uint(w) & 0xffff0000u;
+                        const float r1 = w - __uint_as_float(th[e]);
+                        tm[e] = __float_as_uint(r1) & 0xffff0000u;
+                        tl[e] = __float_as_uint(r1 - __uint_as_float(tm[e]));
+                    }
+                    aw[0][s][p] = (th[0] >> 16) | th[1];
+                    aw[1][s][p] = (tm[0] >> 16) | tm[1];
+                    aw[2][s][p] = (tl[0] >> 16) | (tl[1] & 0xffff0000u);
+                }
+            }
+            // B operands of all column tiles, then the MFMAs with the tiles
+            // innermost so consecutive instructions never share an accumulator.
+            u32x4 bv[NT];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s4*>(region + tr_off(t, 0)));
+                const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s4*>(region + tr_off(t, 1)));
+                const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+                bv[t] = u32x4{l2.x, l2.y, h2.x, h2.y};
+            }
+#pragma unroll
+            for (int k = 0; k < 3; ++k)
+#pragma unroll
+                for (int s = 0; s < NSET; ++s)
+#pragma unroll
+                    for (int t = 0; t < NT; ++t)
+                        acc[s][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, aw[k][s]), __builtin_bit_cast(bf16x8, bv[t]), acc[s][t], 0, 0, 0);
+        }
+    };
+
+    // Two buffers in flight; the reload of bA is unconditional (past ce it
+    // reads zeros): a conditional load would leave the compiler unsure whether
+    // it is outstanding, and it would then wait for every load before
+    // consuming bB.
+    Buf bA, bB;
+    int st = 0;
+    if (nsteps > 0) load(bA, 0);
+    for (; st + 1 < nsteps; st += 2) {
+        load(bB, st + 1);
+        consume(bA);
+        load(bA, st + 2);
+        consume(bB);
+    }
+    if (st < nsteps) consume(bA);
+
+    // Add the four waves' tiles. Register i of acc[s][t] in lane l is head
+    // 16 s + 4 (l / 16) + i, column 16 t + l % 16; as a tile output index:
+    // ((s * NT + t) * 4 + i) * 64 + l.
+    __syncthreads();                                 // every wave is done with its region
+    float* const red = reinterpret_cast<float*>(smem);
+#pragma unroll
+    for (int s = 0; s < NSET; ++s)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[wave * TO + ((s * NT + t) * 4 + i) * 64 + lane] = acc[s][t][i];
+    __syncthreads();
+    const bool in_kernel = a.nsplit > 1 && a.combine;
+    float* const blk = in_kernel ? a.part + static_cast<size_t>(T.id) * a.nsplit * TO : nullptr;
+    float* const plane = (a.nsplit > 1 && !a.combine) ? a.part + static_cast<size_t>(T.s) * a.B * a.Hq * D : a.out;
+    auto out_index = [&](int idx, size_t* o) -> bool {
+        const int l = idx & 63, reg = idx >> 6;
+        const int i = reg & 3, st2 = reg >> 2;
+        const int t = st2 % NT, s = st2 / NT;
+        const int h = 16 * s + 4 * (l >> 4) + i;
+        *o = (static_cast<size_t>(T.b) * a.Hq + T.q_first + h) * D + 16 * t + (l & 15);
+        return h < T.nq;
     };
     for (int idx = threadIdx.x; idx < TO; idx += kThreads) {
         float sum = red[idx];

@@ -202,6 +202,22 @@ hipError_t launch_mfma_set(int nset, const Pass1Args& a, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
+template <int PR, int NSET>
+hipError_t launch_mfma_bf16(const Pass1Args& a, hipStream_t s) {
+    hipLaunchKernelGGL((gqa_av::av_pass1_mfma_bf16<PR, NSET, GQA_AV_MFMA_BF16_CHUNKS>), dim3(a.nblocks),
+                       dim3(gqa_av::kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_mfma_bf16_pr(int64_t D, int nset, const Pass1Args& a, hipStream_t s) {
+    switch (D) {
+    case 64: return nset == 1 ? launch_mfma_bf16<8, 1>(a, s) : launch_mfma_bf16<8, 2>(a, s);
+    case 128: return nset == 1 ? launch_mfma_bf16<16, 1>(a, s) : launch_mfma_bf16<16, 2>(a, s);
+    case 256: return nset == 1 ? launch_mfma_bf16<32, 1>(a, s) : hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+    }
+}
+
 template <int DT>
 hipError_t launch_mfma_de(int DE, int nset, const Pass1Args& a, hipStream_t s) {
     switch (DE) {
@@ -219,6 +235,10 @@ hipError_t launch_mfma_de(int DE, int nset, const Pass1Args& a, hipStream_t s) {
 }
 
 hipError_t launch_pass1(int v_dtype, const gqa_av_plan& p, int64_t D, const Pass1Args& a, hipStream_t s) {
+    if (p.engine == GQA_AV_ENGINE_MFMA_BF16) {
+        if (v_dtype != GQA_AV_BF16) return hipErrorInvalidValue;
+        return launch_mfma_bf16_pr(D, p.heads_per_tile / 16, a, s);
+    }
     if (p.engine == GQA_AV_ENGINE_MFMA) {
         const int DE = static_cast<int>(D / 16), nset = p.heads_per_tile / 16;
         switch (v_dtype) {
@@ -254,6 +274,17 @@ bool mfma_fits(int64_t D, int es, int v_align, int nset) {
     return nset * DE <= 16 && (nset == 1 || DE <= 8);
 }
 
+// Can the bf16 matrix-core engine take this problem? bf16 V, D of 64, 128 or
+// 256 (whole 16-byte pieces per row, a power of two of them for the LDS
+// swizzle), 16-byte aligned V, rows of V and attn of at most 1 MB, and the
+// same 64 KB bound on the four waves' tiles as the fp32 engine.
+bool mfma_bf16_fits(int v_dtype, int64_t Hq, int64_t Hkv, int64_t D, int v_align, int nset) {
+    if (v_dtype != GQA_AV_BF16 || !(D == 64 || D == 128 || D == 256)) return false;
+    if (Hkv * D * 2 > (int64_t{1} << 20) || Hq * 4 > (int64_t{1} << 20)) return false;  // row bytes for 32-bit offsets
+    if (v_align % 16 != 0) return false;
+    return nset * D <= 256;
+}
+
 constexpr int64_t kMfmaMinGroup = 5;     // below this the VALU engine does less work
 
 constexpr int64_t kCounterBytes = 256;          // the counter block is padded to this
@@ -281,7 +312,7 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
     gqa_av_hint h;
     std::memset(&h, 0, sizeof h);
     if (hint) h = *hint;
-    if (h.engine < GQA_AV_ENGINE_AUTO || h.engine > GQA_AV_ENGINE_MFMA)
+    if (h.engine < GQA_AV_ENGINE_AUTO || h.engine > GQA_AV_ENGINE_MFMA_BF16)
         return fail(GQA_AV_ERR_INVALID_ARG, "unknown engine %d", h.engine);
     if (h.combine < GQA_AV_COMBINE_AUTO || h.combine > GQA_AV_COMBINE_LAST)
         return fail(GQA_AV_ERR_INVALID_ARG, "unknown combine %d", h.combine);
@@ -291,16 +322,28 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
     const int es = elem_bytes(v_dtype);
     const int64_t G = Hq / Hkv;
 
-    // Engine. The matrix-core engine always computes 16 (or 32) heads per
-    // tile, so it only pays off for larger groups; the per-head baseline is
-    // always the VALU engine with one head per tile.
+    // Engine. The matrix-core engines always compute 16 (or 32) heads per
+    // tile, so they only pay off for larger groups; the per-head baseline is
+    // always the VALU engine with one head per tile. For bf16 V the bf16
+    // matrix engine is preferred: the fp32 one keeps the SIMDs about 80 %
+    // busy at full bandwidth with 16 heads per tile.
     const int nset = (G > 16 && mfma_fits(D, es, v_align, 2)) ? 2 : 1;
     const bool mfma_ok = resolved == GQA_AV_REUSE && mfma_fits(D, es, v_align, nset);
+    const int nset16 = (G > 16 && mfma_bf16_fits(v_dtype, Hq, Hkv, D, v_align, 2)) ? 2 : 1;
+    const bool mfma16_ok = resolved == GQA_AV_REUSE && mfma_bf16_fits(v_dtype, Hq, Hkv, D, v_align, nset16);
     int engine = h.engine;
-    if (engine == GQA_AV_ENGINE_AUTO) engine = (mfma_ok && G >= kMfmaMinGroup) ? GQA_AV_ENGINE_MFMA : GQA_AV_ENGINE_VALU;
+    if (engine == GQA_AV_ENGINE_AUTO) {
+        engine = GQA_AV_ENGINE_VALU;
+        if (G >= kMfmaMinGroup && mfma16_ok) engine = GQA_AV_ENGINE_MFMA_BF16;
+        else if (G >= kMfmaMinGroup && mfma_ok) engine = GQA_AV_ENGINE_MFMA;
+    }
     if (engine == GQA_AV_ENGINE_MFMA && !mfma_ok)
         return fail(GQA_AV_ERR_UNSUPPORTED,
                     "MFMA engine needs reuse mode, D %% 16 == 0 with a 4/8/12/16/32-byte lane chunk and matching V alignment");
+    if (engine == GQA_AV_ENGINE_MFMA_BF16 && !mfma16_ok)
+        return fail(GQA_AV_ERR_UNSUPPORTED,
+                    "bf16 MFMA engine needs reuse mode, bf16 V, D of 64, 128 or 256 and 16-byte aligned V");
+    const bool matrix = engine == GQA_AV_ENGINE_MFMA || engine == GQA_AV_ENGINE_MFMA_BF16;
 
     // KV heads per tile: only the VALU engine in reuse mode streams several.
     // Automatic: two adjacent heads (a 2 x D contiguous slice of each row)
@@ -327,7 +370,17 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
     int VB, GT, nsg;
     int64_t Lc, rps, ndt, rows_per_step, tile_outputs;
     int64_t heads_major;  // tiles along the head axis per KV head
-    if (engine == GQA_AV_ENGINE_MFMA) {
+    if (engine == GQA_AV_ENGINE_MFMA_BF16) {
+        VB = 16;
+        GT = 16 * nset16;
+        nsg = static_cast<int>(ceil_div(G, GT));
+        heads_major = nsg;
+        Lc = D / 8;                     // 16-byte pieces of a row
+        rps = 32 * gqa_av::kWaves;      // one 32-row chunk per wave
+        ndt = 1;
+        rows_per_step = rps * GQA_AV_MFMA_BF16_CHUNKS;
+        tile_outputs = static_cast<int64_t>(GT) * D;
+    } else if (engine == GQA_AV_ENGINE_MFMA) {
         const int64_t DE = D / 16;
         VB = static_cast<int>(DE * es);
         GT = 16 * nset;
@@ -382,14 +435,25 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
             nsplit = h.nsplit < C ? h.nsplit : C;
             rows_per_split = ceil_div(C, nsplit);
         } else {
-            const int64_t target = (engine == GQA_AV_ENGINE_MFMA ? kTargetWgPerCuMfma : kTargetWgPerCuValu) * cus;
+            const int64_t target = (matrix ? kTargetWgPerCuMfma : kTargetWgPerCuValu) * cus;
             nsplit = tiles > 0 ? ceil_div(target, tiles) : 1;
-            const int64_t cap = ceil_div(C, engine == GQA_AV_ENGINE_MFMA ? kMinRowsPerSplitMfma : kMinRowsPerSplit);
+            const int64_t cap = ceil_div(C, matrix ? kMinRowsPerSplitMfma : kMinRowsPerSplit);
             if (nsplit > cap) nsplit = cap;
             if (nsplit < 1) nsplit = 1;
             rows_per_split = ceil_div(ceil_div(C, nsplit), rows_per_step) * rows_per_step;
         }
         nsplit = ceil_div(C, rows_per_split);
+        if (engine == GQA_AV_ENGINE_MFMA_BF16) {
+            // The bf16 matrix engine addresses one split of V and attn through
+            // buffer resources with 32-bit offsets (the last step's reads run up
+            // to two steps of 128 rows past the split): keep a split under 1 GB.
+            const int64_t row_bytes = std::max<int64_t>(Hkv * D * 2, Hq * 4);
+            const int64_t max_rows = (int64_t{1} << 30) / row_bytes - 512;
+            if (rows_per_split > max_rows) {
+                rows_per_split = max_rows;
+                nsplit = ceil_div(C, rows_per_split);
+            }
+        }
     }
     if (nsplit > INT32_MAX) return fail(GQA_AV_ERR_UNSUPPORTED, "too many context splits");
     const int64_t grid = tiles * nsplit;
@@ -517,7 +581,7 @@ int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C,
     if (plan->grid % plan->nsplit != 0 ||
         tiles_per_split != B * (Hkv / plan->kv_heads_per_tile) * heads_major * plan->d_tiles)
         return fail(GQA_AV_ERR_INVALID_ARG, "plan grid does not match the problem");
-    const int64_t tile_outputs = plan->engine == GQA_AV_ENGINE_MFMA
+    const int64_t tile_outputs = (plan->engine == GQA_AV_ENGINE_MFMA || plan->engine == GQA_AV_ENGINE_MFMA_BF16)
         ? static_cast<int64_t>(plan->heads_per_tile) * D
         : static_cast<int64_t>(plan->heads_per_tile) * (plan->vec_bytes / elem_bytes(v_dtype)) * plan->lanes_per_row;
     if (plan->workspace_bytes !=

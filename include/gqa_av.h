@@ -89,7 +89,11 @@ typedef enum gqa_av_status {
 typedef enum gqa_av_engine {
     GQA_AV_ENGINE_AUTO = 0,
     GQA_AV_ENGINE_VALU = 1,      /* per-lane fp32 FMAs, any G, any D */
-    GQA_AV_ENGINE_MFMA = 2       /* fp32 matrix-core tiles over 16 query heads */
+    GQA_AV_ENGINE_MFMA = 2,      /* fp32 matrix-core tiles over 16 query heads */
+    GQA_AV_ENGINE_MFMA_BF16 = 3  /* bf16 V only (D = 64, 128 or 256, V 16-byte aligned): bf16
+                                    matrix-core tiles over 16 query heads and 32 rows; each fp32
+                                    weight is split exactly into three bf16 terms, so every
+                                    product is exact and the sums are fp32 as in the others */
 } gqa_av_engine;
 
 /* How the partial sums of a split context are added (both in increasing
@@ -116,11 +120,11 @@ typedef struct gqa_av_hint {
 typedef struct gqa_av_plan {
     int32_t mode;            /* resolved: GQA_AV_PER_HEAD or GQA_AV_REUSE */
     int32_t engine;          /* resolved gqa_av_engine (VALU or MFMA) */
-    int32_t heads_per_tile;  /* query heads one workgroup computes (reuse: VALU 1-4, 8 or 16; MFMA 16 or 32; per-head: 1) */
+    int32_t heads_per_tile;  /* query heads one workgroup computes (reuse: VALU 1-8 or 16; MFMA engines 16 or 32; per-head: 1) */
     int32_t subgroups;       /* workgroups that share one KV head's rows (ceil(G / heads_per_tile)) */
-    int32_t vec_bytes;       /* bytes of V each lane loads per row (VALU: 16, 8, 4, 2; MFMA: D/16 elements) */
+    int32_t vec_bytes;       /* bytes of V each lane loads per row (VALU: 16, 8, 4, 2; MFMA: D/16 elements; MFMA_BF16: 16) */
     int32_t lanes_per_row;   /* lanes covering one row of the tile (kv_heads_per_tile D-rows) */
-    int32_t row_slots;       /* rows a workgroup loads side by side */
+    int32_t row_slots;       /* rows a workgroup loads side by side (MFMA_BF16: four waves x 32) */
     int32_t d_tiles;         /* workgroups along D */
     int32_t nsplit;          /* context splits (1 = no partial sums) */
     int32_t threads;         /* threads per workgroup */

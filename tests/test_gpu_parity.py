@@ -84,7 +84,7 @@ def _plans(B, C, Hq, Hkv, D, dt, ns):
     plans = [("auto", ga.make_plan(B, C, Hq, Hkv, D, dt, "auto", nsplit=ns))]
     if Hq // Hkv >= 2:
         plans.append(("per_head", ga.make_plan(B, C, Hq, Hkv, D, dt, "per_head", nsplit=ns)))
-        for eng in ("valu", "mfma"):
+        for eng in ("valu", "mfma", "mfma_bf16"):
             try:
                 plans.append((eng, ga.make_plan(B, C, Hq, Hkv, D, dt, "reuse", engine=eng, nsplit=ns)))
             except ga.GqaAvError as e:
@@ -101,7 +101,7 @@ def _plans(B, C, Hq, Hkv, D, dt, ns):
         if p.nsplit > 1:
             other = "last" if p.combine == 1 else "kernel"
             mode = "per_head" if p.mode == 0 else ("reuse" if name != "auto" else "auto")
-            eng = {1: "valu", 2: "mfma"}[p.engine]
+            eng = {1: "valu", 2: "mfma", 3: "mfma_bf16"}[p.engine]
             if name.startswith("kv_tile"):
                 mode = "reuse"
             plans.append((f"{name}/{other}", ga.make_plan(B, C, Hq, Hkv, D, dt, mode, engine=eng, nsplit=ns,
@@ -143,9 +143,13 @@ def test_workload_other_combine(wname, oracle_lib):
 
 @pytest.mark.parametrize("wname,engine", [
     ("llama3-8b-b1-c4096-hq32-hkv8-d128-bf16", "mfma"),
+    ("llama3-8b-b1-c4096-hq32-hkv8-d128-bf16", "mfma_bf16"),
     ("g2-b4-c32768-hq16-hkv8-d128-bf16", "mfma"),
+    ("g2-b4-c32768-hq16-hkv8-d128-bf16", "mfma_bf16"),
     ("mqa16-b4-c32768-hq16-hkv1-d128-bf16", "valu"),
+    ("mqa16-b4-c32768-hq16-hkv1-d128-bf16", "mfma"),
     ("batch64-b64-c8192-hq64-hkv8-d128-bf16", "valu"),
+    ("batch64-b64-c8192-hq64-hkv8-d128-bf16", "mfma"),
 ])
 def test_workload_other_engine(wname, engine, oracle_lib):
     """Full-size workloads on the engine the automatic plan does not pick."""
@@ -181,6 +185,43 @@ def test_one_hot_is_exact(dt):
         out = _run(attn, V, plan=plan).astype(np.float32)
         for (b, q), c in sel.items():
             assert np.array_equal(out[b, q], Vd[b, c, q // G]), (mode, ns, b, q)
+    if dt == "bf16":
+        for ns, comb in ((0, "kernel"), (4, "last"), (1, "auto")):
+            plan = ga.make_plan(B, C, Hq, Hkv, D, dt, "reuse", nsplit=ns, engine="mfma_bf16", combine=comb)
+            out = _run(attn, V, plan=plan).astype(np.float32)
+            for (b, q), c in sel.items():
+                assert np.array_equal(out[b, q], Vd[b, c, q // G]), ("mfma_bf16", ns, b, q)
+
+
+def test_bf16_engine_splits_weights_exactly():
+    """The bf16 matrix engine splits each fp32 weight into three bf16 terms.
+    With a single nonzero weight per head and V a power of two, the output is
+    weight * V exactly: any lost weight bit shows up."""
+    B, C, Hq, Hkv, D = 2, 301, 32, 2, 128
+    G = Hq // Hkv
+    gen = torch.Generator().manual_seed(11)
+    mant = torch.rand(B, Hq, generator=gen) + 1.0                 # full 24-bit significands
+    # products of every split term stay normal fp32: |w| >= 2^-60, |V| >= 2^-20
+    expo = torch.randint(-60, 3, (B, Hq), generator=gen).float()
+    w = (mant * torch.pow(2.0, expo)).to(torch.float32)
+    w[0, :4] = torch.tensor([1.0 - 2.0 ** -24, 2.0 ** -50 * (1.0 + 2.0 ** -23), -3.75, 65504.0 + 1.0 / 3.0])
+    attn = torch.zeros(B, C, Hq)
+    sel = {}
+    for b in range(B):
+        for q in range(Hq):
+            c = (53 * b + 17 * q + 5) % C
+            attn[b, c, q] = w[b, q]
+            sel[b, q] = c
+    V = torch.zeros(B, C, Hkv, D, dtype=torch.bfloat16)
+    pw = torch.pow(2.0, torch.randint(-20, 20, (B, C, Hkv, D), generator=gen).float())
+    V.copy_(pw.to(torch.bfloat16))
+    Vd = V.to(torch.float64).numpy()
+    for ns, comb in ((1, "auto"), (3, "kernel"), (5, "last")):
+        plan = ga.make_plan(B, C, Hq, Hkv, D, "bf16", "reuse", nsplit=ns, engine="mfma_bf16", combine=comb)
+        out = _run(attn, V, plan=plan)
+        for (b, q), c in sel.items():
+            want = (w[b, q].double().item() * Vd[b, c, q // G]).astype(np.float32)
+            assert np.array_equal(out[b, q].astype(np.float32), want), (ns, b, q, w[b, q].item())
 
 
 @pytest.mark.parametrize("combine", ["kernel", "last"])

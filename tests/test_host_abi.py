@@ -81,6 +81,11 @@ def _check_plan(p, B, C, Hq, Hkv, D, v_dtype, mode):
         assert p.vec_bytes == D // 16 * es and p.lanes_per_row == 16 and p.row_slots == 16 and p.d_tiles == 1
         assert p.heads_per_tile in (16, 32)
         tile_out = p.heads_per_tile * D
+    elif p.engine == 3:                                 # bf16 MFMA: 16-byte pieces, 32-row chunk per wave
+        assert p.mode == 1 and v_dtype == "bf16" and D in (64, 128, 256)
+        assert p.vec_bytes == 16 and p.lanes_per_row == D // 8 and p.row_slots == 128 and p.d_tiles == 1
+        assert p.heads_per_tile in (16, 32) and p.heads_per_tile * D <= 4096
+        tile_out = p.heads_per_tile * D
     else:
         assert p.vec_bytes in (16, 8, 4, 2) and (D * es) % p.vec_bytes == 0 and p.vec_bytes >= es
         L = D * es // p.vec_bytes
@@ -98,7 +103,7 @@ def _check_plan(p, B, C, Hq, Hkv, D, v_dtype, mode):
         assert p.nsplit >= 1 and p.rows_per_split >= 1
         assert -(-C // p.rows_per_split) == p.nsplit       # splits tile [0, C) exactly
     if p.mode == 1:
-        assert p.heads_per_tile >= min(G, 8) and (p.engine == 2 or p.heads_per_tile <= Hq)
+        assert p.heads_per_tile >= min(G, 8) and (p.engine in (2, 3) or p.heads_per_tile <= Hq)
         assert p.subgroups == -(-G // p.heads_per_tile)
         tiles = B * (Hkv // p.kv_heads_per_tile) * p.subgroups * p.d_tiles
         assert p.v_bytes_read == B * C * Hkv * D * es * p.subgroups
@@ -165,6 +170,8 @@ def test_large_groups_use_subgroups():
     p = ga.make_plan(1, 4096, 40, 1, 128, "bf16", engine="valu")
     assert p.mode == 1 and p.heads_per_tile == 16 and p.subgroups == 3
     p = ga.make_plan(1, 4096, 40, 1, 128, "bf16")
+    assert p.mode == 1 and p.engine == 3 and p.heads_per_tile == 32 and p.subgroups == 2
+    p = ga.make_plan(1, 4096, 40, 1, 128, "f16")
     assert p.mode == 1 and p.engine == 2 and p.heads_per_tile == 32 and p.subgroups == 2
 
 
@@ -234,10 +241,11 @@ def test_product_path_does_not_touch_the_oracle():
 @pytest.mark.parametrize("wname,engine", [
     ("tiny-f32-b1-c256-hq8-hkv2-d64", 1), ("llama3-8b-b1-c4096-hq32-hkv8-d128-bf16", 1),
     ("g3-b8-c16384-hq24-hkv8-d96-f16", 1), ("g2-b4-c32768-hq16-hkv8-d128-bf16", 1),
-    ("mqa16-b4-c32768-hq16-hkv1-d128-bf16", 2), ("batch64-b64-c8192-hq64-hkv8-d128-bf16", 2),
+    ("mqa16-b4-c32768-hq16-hkv1-d128-bf16", 3), ("batch64-b64-c8192-hq64-hkv8-d128-bf16", 3),
 ])
 def test_auto_engine(wname, engine):
-    """Groups of 5 or more heads take the matrix-core engine, smaller ones the VALU engine."""
+    """Groups of 5 or more heads take a matrix-core engine (bf16 V: the bf16 one),
+    smaller ones the VALU engine."""
     w = WORKLOADS[wname]
     assert ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype).engine == engine
     assert ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, "per_head").engine == 1
@@ -248,9 +256,24 @@ def test_forced_engines():
     assert p.engine == 2 and p.heads_per_tile == 16 and p.subgroups == 1
     _check_plan(p, 1, 300, 4, 2, 128, "bf16", "auto")
     p = ga.make_plan(1, 300, 64, 1, 128, "bf16")                        # G = 64: 32-head sets
-    assert p.engine == 2 and p.heads_per_tile == 32 and p.subgroups == 2
+    assert p.engine == 3 and p.heads_per_tile == 32 and p.subgroups == 2
     p = ga.make_plan(1, 300, 64, 1, 256, "bf16")                        # D = 256: 16-head sets
+    assert p.engine == 3 and p.heads_per_tile == 16 and p.subgroups == 4
+    p = ga.make_plan(1, 300, 64, 1, 128, "f16")                         # fp16 V: the fp32 matrix engine
+    assert p.engine == 2 and p.heads_per_tile == 32 and p.subgroups == 2
+    p = ga.make_plan(1, 300, 64, 1, 256, "bf16", engine="mfma")
     assert p.engine == 2 and p.heads_per_tile == 16 and p.subgroups == 4
+    p = ga.make_plan(1, 300, 4, 2, 64, "bf16", engine="mfma_bf16")      # G = 2 on the bf16 engine: allowed
+    assert p.engine == 3 and p.heads_per_tile == 16 and p.subgroups == 1
+    _check_plan(p, 1, 300, 4, 2, 64, "bf16", "auto")
+    for args, kw in [((1, 300, 16, 1, 96, "bf16"), {}), ((1, 300, 16, 1, 128, "f16"), {}),
+                     ((1, 300, 16, 1, 128, "bf16", "per_head"), {}), ((1, 300, 16, 1, 128, "bf16"), {"v_align": 8}),
+                     ((1, 300, 16, 1, 512, "bf16"), {})]:
+        with pytest.raises(ga.GqaAvError) as ei:
+            ga.make_plan(*args, engine="mfma_bf16", **kw)
+        assert ei.value.name == "UNSUPPORTED"
+    # shapes the bf16 engine cannot take go to the fp32 matrix engine
+    assert ga.make_plan(1, 300, 16, 1, 96, "bf16").engine == 2
     assert ga.make_plan(1, 300, 16, 1, 128, "bf16", engine="valu").engine == 1
     for args, kw in [((1, 300, 16, 1, 127, "bf16"), {}), ((1, 300, 16, 1, 128, "bf16", "per_head"), {}),
                      ((1, 300, 16, 1, 96, "f32"), {}), ((1, 300, 16, 1, 128, "bf16"), {"v_align": 8})]:
@@ -276,7 +299,7 @@ def test_zeroed_hint_means_automatic():
     h, p, q = ga.Hint(), ga.Plan(), ga.Plan()
     assert lib.gqa_av_make_plan(4, 32768, 16, 1, 128, 2, -1, ctypes.byref(h), ctypes.byref(p)) == 0
     assert lib.gqa_av_make_plan(4, 32768, 16, 1, 128, 2, -1, None, ctypes.byref(q)) == 0
-    assert p.as_dict() == q.as_dict() and p.engine == 2
+    assert p.as_dict() == q.as_dict() and p.engine == 3
     h.combine = 3
     assert lib.gqa_av_make_plan(4, 32768, 16, 1, 128, 2, -1, ctypes.byref(h), ctypes.byref(p)) == 1
 
@@ -291,10 +314,21 @@ def test_kv_tile():
     assert ga.make_plan(4, 100, 16, 8, 128, "bf16").kv_heads_per_tile >= 1
     for kw, status in [(dict(kv_tile=3), "INVALID_ARG"),                      # does not divide Hkv
                        (dict(kv_tile=2, mode="per_head"), "UNSUPPORTED"),
-                       (dict(kv_tile=2, engine="mfma"), "UNSUPPORTED")]:
+                       (dict(kv_tile=2, engine="mfma"), "UNSUPPORTED"),
+                       (dict(kv_tile=2, engine="mfma_bf16"), "UNSUPPORTED")]:
         with pytest.raises(ga.GqaAvError) as ei:
             ga.make_plan(4, 100, 16, 8, 128, "bf16", **kw)
         assert ei.value.name == status
     with pytest.raises(ga.GqaAvError) as ei:                                 # 32 x 16 lanes > 256
         ga.make_plan(1, 100, 64, 32, 128, "bf16", kv_tile=32, engine="valu")
     assert ei.value.name == "UNSUPPORTED"
+
+
+def test_bf16_engine_keeps_split_spans_small():
+    """The bf16 matrix engine reads a split through 32-bit buffer offsets: a split's
+    rows of V stay under 1 GB, with more splits than asked for if need be."""
+    p = ga.make_plan(1, 10_000_000, 16, 1, 128, "bf16", engine="mfma_bf16", nsplit=1)
+    assert p.engine == 3 and p.nsplit == 3 and p.rows_per_split * 256 <= 2 ** 30
+    _check_plan(p, 1, 10_000_000, 16, 1, 128, "bf16", "auto")
+    # rows of V beyond 1 MB are not taken by this engine
+    assert ga.make_plan(1, 100, 16 * 8192, 8192, 128, "bf16").engine != 3

@@ -735,16 +735,21 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma(Pass1Args a) {
 // lane groups of a column read hit different banks.
 //
 // PR = D / 8 16-byte pieces per row (8, 16 or 32); NSET sets of 16 heads; U
-// chunks of 32 rows per wave and buffer, two buffers in flight.
-template <int PR, int NSET, int U>
+// chunks of 32 rows per wave and buffer, two buffers in flight; HT adjacent
+// KV heads per workgroup (1, 2 or 4), each streamed by kWaves / HT waves, so
+// the workgroup reads HT * 2 D contiguous bytes of every row.
+template <int PR, int NSET, int U, int HT>
 __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
     static_assert(PR == 8 || PR == 16 || PR == 32, "D must be 64, 128 or 256");
+    static_assert(HT == 1 || HT == 2 || HT == 4, "KV heads per tile must divide the waves");
     constexpr int D = PR * 8;
     constexpr int RB = PR * 16;                      // bytes of one D-row
     constexpr int NT = D / 16;                       // 16-column output tiles
     constexpr int LPI = PR / 2;                      // 16-byte loads per lane and chunk
     constexpr int RPI = 64 / PR;                     // rows one 64-lane load covers
-    constexpr int TO = 16 * NSET * D;                // outputs of the tile
+    constexpr int WPH = kWaves / HT;                 // waves per KV head
+    constexpr int TO = 16 * NSET * D;                // outputs of one KV head's tile
+    constexpr int TOW = HT * TO;                     // outputs of the workgroup
     constexpr int STAGE = kWaves * 32 * RB;          // bytes: one 32-row region per wave
     constexpr int RED = kWaves * TO * 4;             // bytes: the final cross-wave sum
     __shared__ __align__(16) uint8_t smem[STAGE > RED ? STAGE : RED];
@@ -754,6 +759,8 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4;                         // K group: rows 8 g .. 8 g + 7 of a chunk
     const int m = lane & 15;                         // head (A) / column (B) inside a tile
+    const int kvl = wave / WPH;                      // which KV head of the tile
+    const int wh = wave % WPH;                       // which of that head's waves
 
     // The split bounds are workgroup-uniform; keep them in scalar registers.
     const int64_t cb = uniform64(static_cast<int64_t>(T.s) * a.rows_per_split);
@@ -768,18 +775,18 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
     // split's V span under 2 GB so 32-bit offsets suffice.
     const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(a.V) + ((static_cast<size_t>(T.b) * a.C + cb) * a.Hkv + T.kv) * D * 2, 0,
-        (nrows - 1) * vrow + D * 2, kRawBufferFlags);
+        (nrows - 1) * vrow + HT * D * 2, kRawBufferFlags);
     const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(a.attn) + (static_cast<size_t>(T.b) * a.C + cb) * a.Hq + T.q_first, 0,
-        ((nrows - 1) * a.Hq + T.nq) * 4, kRawBufferFlags);
+        ((nrows - 1) * a.Hq + (HT - 1) * a.G + T.nq) * 4, kRawBufferFlags);
     // This lane's pieces of a chunk: load i covers rows RPI i .. RPI i + RPI - 1.
     const int prow = lane / PR, ppiece = lane % PR;
-    const int vlane = prow * vrow + ppiece * 16;
+    const int vlane = prow * vrow + kvl * D * 2 + ppiece * 16;
     // Heads past the tile's nq read the tile's last head (in range); their A
     // rows only feed output rows that are never written.
     int wlane[NSET];
 #pragma unroll
-    for (int s = 0; s < NSET; ++s) wlane[s] = (8 * g * a.Hq + min(m + 16 * s, T.nq - 1)) * 4;
+    for (int s = 0; s < NSET; ++s) wlane[s] = (8 * g * a.Hq + kvl * a.G + min(m + 16 * s, T.nq - 1)) * 4;
 
     // LDS region of this wave: 32 rows of RB bytes, each row cut into 32-byte
     // column pairs (16 columns) whose order is XORed with swz(row) so that
@@ -810,18 +817,18 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[s][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    constexpr int RSTEP = 32 * kWaves * U;           // rows per workgroup step
+    constexpr int RSTEP = 32 * WPH * U;             // rows per workgroup step
     const int nsteps = (nrows + RSTEP - 1) / RSTEP;
 
     struct Buf {
         u32x4 v[U][LPI];
         float w[U][NSET][8];
     };
-    // Chunk u of step st starts at split row 32 (st kWaves U + u kWaves + wave).
+    // Chunk u of step st starts at split row 32 (st WPH U + u WPH + wh).
     auto load = [&](Buf& bf, int st) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int r0 = 32 * (st * kWaves * U + u * kWaves + wave);
+            const int r0 = 32 * (st * WPH * U + u * WPH + wh);
 #pragma unroll
             for (int i = 0; i < LPI; ++i)
                 bf.v[u][i] = __builtin_amdgcn_raw_buffer_load_b128(vres, vlane, (r0 + RPI * i) * vrow, kCachePolicyNt);
@@ -899,9 +906,10 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
     }
     if (st < nsteps) consume(bA);
 
-    // Add the four waves' tiles. Register i of acc[s][t] in lane l is head
-    // 16 s + 4 (l / 16) + i, column 16 t + l % 16; as a tile output index:
-    // ((s * NT + t) * 4 + i) * 64 + l.
+    // Add the tiles of each KV head's waves. Register i of acc[s][t] in lane
+    // l is head 16 s + 4 (l / 16) + i, column 16 t + l % 16; as an output
+    // index of the KV head's tile: ((s * NT + t) * 4 + i) * 64 + l. The
+    // workgroup's outputs are the HT heads' tiles one after another.
     __syncthreads();                                 // every wave is done with its region
     float* const red = reinterpret_cast<float*>(smem);
 #pragma unroll
@@ -912,29 +920,31 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
             for (int i = 0; i < 4; ++i) red[wave * TO + ((s * NT + t) * 4 + i) * 64 + lane] = acc[s][t][i];
     __syncthreads();
     const bool in_kernel = a.nsplit > 1 && a.combine;
-    float* const blk = in_kernel ? a.part + static_cast<size_t>(T.id) * a.nsplit * TO : nullptr;
+    float* const blk = in_kernel ? a.part + static_cast<size_t>(T.id) * a.nsplit * TOW : nullptr;
     float* const plane = (a.nsplit > 1 && !a.combine) ? a.part + static_cast<size_t>(T.s) * a.B * a.Hq * D : a.out;
     auto out_index = [&](int idx, size_t* o) -> bool {
-        const int l = idx & 63, reg = idx >> 6;
+        const int k = idx / TO, e = idx - k * TO;
+        const int l = e & 63, reg = e >> 6;
         const int i = reg & 3, st2 = reg >> 2;
         const int t = st2 % NT, s = st2 / NT;
         const int h = 16 * s + 4 * (l >> 4) + i;
-        *o = (static_cast<size_t>(T.b) * a.Hq + T.q_first + h) * D + 16 * t + (l & 15);
+        *o = (static_cast<size_t>(T.b) * a.Hq + T.q_first + k * a.G + h) * D + 16 * t + (l & 15);
         return h < T.nq;
     };
-    for (int idx = threadIdx.x; idx < TO; idx += kThreads) {
-        float sum = red[idx];
+    for (int idx = threadIdx.x; idx < TOW; idx += kThreads) {
+        const int k = idx / TO, e = idx - k * TO;
+        float sum = red[k * WPH * TO + e];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) sum += red[w * TO + idx];
+        for (int w = 1; w < WPH; ++w) sum += red[(k * WPH + w) * TO + e];
         if (in_kernel) {
-            store_coherent(blk + static_cast<size_t>(T.s) * TO + idx, sum);
+            store_coherent(blk + static_cast<size_t>(T.s) * TOW + idx, sum);
         } else {
             size_t o;
             if (out_index(idx, &o)) plane[o] = sum;
         }
     }
     if (in_kernel) {
-        combine_last(a, T, blk, TO, [&](int idx, float v) {
+        combine_last(a, T, blk, TOW, [&](int idx, float v) {
             size_t o;
             if (out_index(idx, &o)) a.out[o] = v;
         });

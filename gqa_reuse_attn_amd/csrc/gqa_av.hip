@@ -53,13 +53,16 @@ int head_capacity(int64_t G) {
 
 
 constexpr int kDefaultCUs = 256;
-// Context-split sizing, measured on MI355X. Both engines stream best with few
-// long-running workgroups (VALU about 2 per CU, MFMA about 1): a plain
-// streaming read shows the same (7.0 TB/s with 512-1024 blocks, 6.8 with 4096).
+// Context-split sizing, measured on MI355X. The engines stream best with few
+// long-running workgroups (VALU about 2 per CU, the matrix engines about 1):
+// a plain streaming read shows the same (7.0 TB/s with 512-1024 blocks, 6.8
+// with 4096).
 constexpr int64_t kMinRowsPerSplit = 128;     // VALU: below this a split's epilogue dominates
 constexpr int64_t kMinRowsPerSplitMfma = 256;
 constexpr int64_t kTargetWgPerCuValu = 2;
 constexpr int64_t kTargetWgPerCuMfma = 1;
+constexpr int64_t kMinRowsPerSplitBf16 = 512;  // bf16 matrix engine: measured best for MQA at B = 4, C = 32768
+constexpr int64_t kTargetWgPerCuBf16 = 1;
 
 // Split-C workspace of one (device, stream). The per-tile counters live in a
 // buffer of their own: they must be zero before a call, every call leaves the
@@ -202,18 +205,28 @@ hipError_t launch_mfma_set(int nset, const Pass1Args& a, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
-template <int PR, int NSET>
+template <int PR, int NSET, int HT>
 hipError_t launch_mfma_bf16(const Pass1Args& a, hipStream_t s) {
-    hipLaunchKernelGGL((gqa_av::av_pass1_mfma_bf16<PR, NSET, GQA_AV_MFMA_BF16_CHUNKS>), dim3(a.nblocks),
+    hipLaunchKernelGGL((gqa_av::av_pass1_mfma_bf16<PR, NSET, GQA_AV_MFMA_BF16_CHUNKS, HT>), dim3(a.nblocks),
                        dim3(gqa_av::kThreads), 0, s, a);
     return hipGetLastError();
 }
 
-hipError_t launch_mfma_bf16_pr(int64_t D, int nset, const Pass1Args& a, hipStream_t s) {
+template <int PR, int NSET>
+hipError_t launch_mfma_bf16_ht(int ht, const Pass1Args& a, hipStream_t s) {
+    switch (ht) {
+    case 1: return launch_mfma_bf16<PR, NSET, 1>(a, s);
+    case 2: return launch_mfma_bf16<PR, NSET, 2>(a, s);
+    case 4: return launch_mfma_bf16<PR, NSET, 4>(a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_mfma_bf16_pr(int64_t D, int nset, int ht, const Pass1Args& a, hipStream_t s) {
     switch (D) {
-    case 64: return nset == 1 ? launch_mfma_bf16<8, 1>(a, s) : launch_mfma_bf16<8, 2>(a, s);
-    case 128: return nset == 1 ? launch_mfma_bf16<16, 1>(a, s) : launch_mfma_bf16<16, 2>(a, s);
-    case 256: return nset == 1 ? launch_mfma_bf16<32, 1>(a, s) : hipErrorInvalidValue;
+    case 64: return nset == 1 ? launch_mfma_bf16_ht<8, 1>(ht, a, s) : launch_mfma_bf16_ht<8, 2>(ht, a, s);
+    case 128: return nset == 1 ? launch_mfma_bf16_ht<16, 1>(ht, a, s) : launch_mfma_bf16_ht<16, 2>(ht, a, s);
+    case 256: return nset == 1 ? launch_mfma_bf16_ht<32, 1>(ht, a, s) : hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
     }
 }
@@ -237,7 +250,7 @@ hipError_t launch_mfma_de(int DE, int nset, const Pass1Args& a, hipStream_t s) {
 hipError_t launch_pass1(int v_dtype, const gqa_av_plan& p, int64_t D, const Pass1Args& a, hipStream_t s) {
     if (p.engine == GQA_AV_ENGINE_MFMA_BF16) {
         if (v_dtype != GQA_AV_BF16) return hipErrorInvalidValue;
-        return launch_mfma_bf16_pr(D, p.heads_per_tile / 16, a, s);
+        return launch_mfma_bf16_pr(D, p.heads_per_tile / 16, p.kv_heads_per_tile, a, s);
     }
     if (p.engine == GQA_AV_ENGINE_MFMA) {
         const int DE = static_cast<int>(D / 16), nset = p.heads_per_tile / 16;
@@ -345,26 +358,41 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
                     "bf16 MFMA engine needs reuse mode, bf16 V, D of 64, 128 or 256 and 16-byte aligned V");
     const bool matrix = engine == GQA_AV_ENGINE_MFMA || engine == GQA_AV_ENGINE_MFMA_BF16;
 
-    // KV heads per tile: only the VALU engine in reuse mode streams several.
-    // Automatic: two adjacent heads (a 2 x D contiguous slice of each row)
-    // when the split grid still reaches its workgroup target with splits of
-    // at least kMinRowsPerSplit rows; measured 4-12 % faster than one head.
+    // KV heads per tile: the VALU and bf16 matrix engines in reuse mode can
+    // stream several adjacent KV heads, i.e. a contiguous ht x D slice of each
+    // row. Automatic: the widest tile (VALU: 2 heads; bf16 matrix: 4, else 2)
+    // whose split grid still reaches the engine's workgroup target with
+    // splits of its minimum length. Measured on MI355X: two heads run 4-12 %
+    // faster than one for VALU; a plain streaming read of 2 KB rows in
+    // 512-byte slices runs at 7.1 TB/s against 6.8 TB/s in 256-byte slices;
+    // the bf16 matrix engine on B = 64, C = 8192, Hkv = 8, G = 8 takes 193 us
+    // with one head per tile, 181 with two and 177 with four.
     int ht = h.kv_tile > 0 ? h.kv_tile : 1;
-    if (h.kv_tile <= 0 && engine == GQA_AV_ENGINE_VALU && resolved == GQA_AV_REUSE && Hkv % 2 == 0 &&
-        !GQA_AV_VALU_STAGE_WEIGHTS) {
+    const bool bf16_engine = engine == GQA_AV_ENGINE_MFMA_BF16;
+    if (h.kv_tile <= 0 && resolved == GQA_AV_REUSE &&
+        ((engine == GQA_AV_ENGINE_VALU && !GQA_AV_VALU_STAGE_WEIGHTS) || bf16_engine)) {
         const int64_t lanes = (D * es) / 16 > 0 && (D * es) % 16 == 0 ? (D * es) / 16 : 0;
-        const int64_t nsg2 = ceil_div(G, head_capacity(G));
-        const int64_t tiles2 = B * (Hkv / 2) * nsg2;
-        const int64_t target = kTargetWgPerCuValu * cus;
-        if (lanes > 0 && 2 * lanes <= gqa_av::kThreads && v_align % 16 == 0 && tiles2 > 0 &&
-            tiles2 * std::min<int64_t>(ceil_div(target, tiles2), std::max<int64_t>(1, C / kMinRowsPerSplit)) >= target)
-            ht = 2;
+        const int64_t nsgw = ceil_div(G, bf16_engine ? 16 * nset16 : head_capacity(G));
+        const int64_t target = (bf16_engine ? kTargetWgPerCuBf16 : kTargetWgPerCuValu) * cus;
+        const int64_t min_rows = bf16_engine ? kMinRowsPerSplitBf16 : kMinRowsPerSplit;
+        for (int cand : {4, 2}) {
+            if ((cand == 4 && !bf16_engine) || Hkv % cand != 0) continue;
+            const int64_t tiles_w = B * (Hkv / cand) * nsgw;
+            if (lanes > 0 && (bf16_engine || cand * lanes <= gqa_av::kThreads) && v_align % 16 == 0 &&
+                tiles_w > 0 &&
+                tiles_w * std::min<int64_t>(ceil_div(target, tiles_w), std::max<int64_t>(1, C / min_rows)) >= target) {
+                ht = cand;
+                break;
+            }
+        }
     }
     if (ht > 1) {
-        if (engine != GQA_AV_ENGINE_VALU || resolved != GQA_AV_REUSE || GQA_AV_VALU_STAGE_WEIGHTS)
-            return fail(GQA_AV_ERR_UNSUPPORTED, "kv_tile > 1 needs the VALU engine in reuse mode");
+        if (resolved != GQA_AV_REUSE || !((engine == GQA_AV_ENGINE_VALU && !GQA_AV_VALU_STAGE_WEIGHTS) || bf16_engine))
+            return fail(GQA_AV_ERR_UNSUPPORTED, "kv_tile > 1 needs the VALU or bf16 matrix engine in reuse mode");
         if (Hkv % ht != 0)
             return fail(GQA_AV_ERR_INVALID_ARG, "kv_tile %d does not divide Hkv=%lld", ht, (long long)Hkv);
+        if (bf16_engine && ht != 2 && ht != 4)
+            return fail(GQA_AV_ERR_UNSUPPORTED, "the bf16 matrix engine takes 1, 2 or 4 KV heads per tile");
     }
 
     int VB, GT, nsg;
@@ -375,11 +403,11 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
         GT = 16 * nset16;
         nsg = static_cast<int>(ceil_div(G, GT));
         heads_major = nsg;
-        Lc = D / 8;                     // 16-byte pieces of a row
-        rps = 32 * gqa_av::kWaves;      // one 32-row chunk per wave
+        Lc = ht * D / 8;                // 16-byte pieces of a tile row
+        rps = 32 * gqa_av::kWaves / ht; // one 32-row chunk per wave, kWaves / ht waves per KV head
         ndt = 1;
         rows_per_step = rps * GQA_AV_MFMA_BF16_CHUNKS;
-        tile_outputs = static_cast<int64_t>(GT) * D;
+        tile_outputs = static_cast<int64_t>(ht) * GT * D;
     } else if (engine == GQA_AV_ENGINE_MFMA) {
         const int64_t DE = D / 16;
         VB = static_cast<int>(DE * es);
@@ -435,9 +463,11 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
             nsplit = h.nsplit < C ? h.nsplit : C;
             rows_per_split = ceil_div(C, nsplit);
         } else {
-            const int64_t target = (matrix ? kTargetWgPerCuMfma : kTargetWgPerCuValu) * cus;
+            const int64_t target =
+                (bf16_engine ? kTargetWgPerCuBf16 : matrix ? kTargetWgPerCuMfma : kTargetWgPerCuValu) * cus;
             nsplit = tiles > 0 ? ceil_div(target, tiles) : 1;
-            const int64_t cap = ceil_div(C, matrix ? kMinRowsPerSplitMfma : kMinRowsPerSplit);
+            const int64_t cap =
+                ceil_div(C, bf16_engine ? kMinRowsPerSplitBf16 : matrix ? kMinRowsPerSplitMfma : kMinRowsPerSplit);
             if (nsplit > cap) nsplit = cap;
             if (nsplit < 1) nsplit = 1;
             rows_per_split = ceil_div(ceil_div(C, nsplit), rows_per_step) * rows_per_step;
@@ -582,7 +612,7 @@ int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C,
         tiles_per_split != B * (Hkv / plan->kv_heads_per_tile) * heads_major * plan->d_tiles)
         return fail(GQA_AV_ERR_INVALID_ARG, "plan grid does not match the problem");
     const int64_t tile_outputs = (plan->engine == GQA_AV_ENGINE_MFMA || plan->engine == GQA_AV_ENGINE_MFMA_BF16)
-        ? static_cast<int64_t>(plan->heads_per_tile) * D
+        ? static_cast<int64_t>(plan->heads_per_tile) * D * plan->kv_heads_per_tile
         : static_cast<int64_t>(plan->heads_per_tile) * (plan->vec_bytes / elem_bytes(v_dtype)) * plan->lanes_per_row;
     if (plan->workspace_bytes !=
         workspace_bytes(B, Hq, D, tiles_per_split, plan->nsplit, tile_outputs, plan->combine))

@@ -90,13 +90,14 @@ def _plans(B, C, Hq, Hkv, D, dt, ns):
             except ga.GqaAvError as e:
                 assert e.name == "UNSUPPORTED"
     if Hq // Hkv >= 2 and Hkv > 1:
-        for ht in (2, Hkv):
-            if Hkv % ht == 0:
-                try:
-                    plans.append((f"kv_tile={ht}", ga.make_plan(B, C, Hq, Hkv, D, dt, "reuse", engine="valu",
-                                                                 nsplit=ns, kv_tile=ht)))
-                except ga.GqaAvError as e:
-                    assert e.name == "UNSUPPORTED"
+        for eng in ("valu", "mfma_bf16"):
+            for ht in sorted({2, Hkv}):
+                if Hkv % ht == 0:
+                    try:
+                        plans.append((f"kv_tile={ht}/{eng}", ga.make_plan(B, C, Hq, Hkv, D, dt, "reuse", engine=eng,
+                                                                          nsplit=ns, kv_tile=ht)))
+                    except ga.GqaAvError as e:
+                        assert e.name == "UNSUPPORTED"
     for name, p in list(plans):
         if p.nsplit > 1:
             other = "last" if p.combine == 1 else "kernel"
@@ -216,8 +217,9 @@ def test_bf16_engine_splits_weights_exactly():
     pw = torch.pow(2.0, torch.randint(-20, 20, (B, C, Hkv, D), generator=gen).float())
     V.copy_(pw.to(torch.bfloat16))
     Vd = V.to(torch.float64).numpy()
-    for ns, comb in ((1, "auto"), (3, "kernel"), (5, "last")):
-        plan = ga.make_plan(B, C, Hq, Hkv, D, "bf16", "reuse", nsplit=ns, engine="mfma_bf16", combine=comb)
+    for ns, comb, ht in ((1, "auto", 1), (3, "kernel", 1), (5, "last", 1), (1, "auto", 2), (4, "last", 2)):
+        plan = ga.make_plan(B, C, Hq, Hkv, D, "bf16", "reuse", nsplit=ns, engine="mfma_bf16", combine=comb,
+                            kv_tile=ht)
         out = _run(attn, V, plan=plan)
         for (b, q), c in sel.items():
             want = (w[b, q].double().item() * Vd[b, c, q // G]).astype(np.float32)
@@ -384,15 +386,35 @@ def test_split_entry_points_equal_decode(wname):
 
 
 
-@pytest.mark.parametrize("wname,ht", [("g2-b4-c32768-hq16-hkv8-d128-bf16", 8), ("g2-b4-c32768-hq16-hkv8-d128-bf16", 2),
-                                      ("g3-b8-c16384-hq24-hkv8-d96-f16", 4),
-                                      ("llama3-8b-b1-c4096-hq32-hkv8-d128-bf16", 8)])
-def test_workload_kv_tiles(wname, ht, oracle_lib):
+@pytest.mark.parametrize("wname,ht,engine", [
+    ("g2-b4-c32768-hq16-hkv8-d128-bf16", 8, "valu"), ("g2-b4-c32768-hq16-hkv8-d128-bf16", 2, "valu"),
+    ("g3-b8-c16384-hq24-hkv8-d96-f16", 4, "valu"), ("llama3-8b-b1-c4096-hq32-hkv8-d128-bf16", 8, "valu"),
+    ("g2-b4-c32768-hq16-hkv8-d128-bf16", 4, "mfma_bf16"), ("llama3-8b-b1-c4096-hq32-hkv8-d128-bf16", 2, "mfma_bf16"),
+    ("batch64-b64-c8192-hq64-hkv8-d128-bf16", 2, "mfma_bf16"),
+])
+def test_workload_kv_tiles(wname, ht, engine, oracle_lib):
     """Full-size workloads with several adjacent KV heads per workgroup."""
     w = WORKLOADS[wname]
     attn, V = make_inputs(w, seed=0)
     ref = oracle_lib.full(attn, V, w.v_dtype)
-    plan = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, "reuse", engine="valu", kv_tile=ht,
+    plan = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, "reuse", engine=engine, kv_tile=ht,
                         cu_count=torch.cuda.get_device_properties(0).multi_processor_count)
     out = _run(attn, V, plan=plan)
     assert_parity(out, ref, w.v_dtype, w.C, f"{wname} kv_tile={ht} plan={plan.as_dict()}")
+
+
+@pytest.mark.parametrize("B,C,G,Hkv,D", [(2, 1000, 8, 4, 128), (1, 777, 16, 8, 64), (3, 301, 5, 4, 256),
+                                         (2, 515, 32, 4, 128), (1, 64, 12, 8, 128)])
+def test_bf16_engine_kv_tiles_small(B, C, G, Hkv, D, oracle_lib):
+    """bf16 matrix engine with 1, 2 and 4 KV heads per workgroup, ragged splits,
+    both combines; 32-head sets at G = 32."""
+    Hq = G * Hkv
+    attn, V = make_random(B, C, Hq, Hkv, D, "bf16", seed=C + G, attn_kind="softmax")
+    ref = oracle_lib.full(attn, V, "bf16")
+    for ht in (1, 2, 4):
+        for ns, comb in ((1, "auto"), (3, "kernel"), (7, "last")):
+            plan = ga.make_plan(B, C, Hq, Hkv, D, "bf16", "reuse", engine="mfma_bf16", kv_tile=ht, nsplit=ns,
+                                combine=comb)
+            assert plan.kv_heads_per_tile == ht
+            out = _run(attn, V, plan=plan)
+            assert_parity(out, ref, "bf16", C, f"{(B, C, G, Hkv, D)} kv_tile={ht} ns={ns} {comb}")

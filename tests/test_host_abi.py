@@ -82,10 +82,11 @@ def _check_plan(p, B, C, Hq, Hkv, D, v_dtype, mode):
         assert p.heads_per_tile in (16, 32)
         tile_out = p.heads_per_tile * D
     elif p.engine == 3:                                 # bf16 MFMA: 16-byte pieces, 32-row chunk per wave
-        assert p.mode == 1 and v_dtype == "bf16" and D in (64, 128, 256)
-        assert p.vec_bytes == 16 and p.lanes_per_row == D // 8 and p.row_slots == 128 and p.d_tiles == 1
+        ht = p.kv_heads_per_tile
+        assert p.mode == 1 and v_dtype == "bf16" and D in (64, 128, 256) and ht in (1, 2, 4) and Hkv % ht == 0
+        assert p.vec_bytes == 16 and p.lanes_per_row == ht * D // 8 and p.row_slots == 128 // ht and p.d_tiles == 1
         assert p.heads_per_tile in (16, 32) and p.heads_per_tile * D <= 4096
-        tile_out = p.heads_per_tile * D
+        tile_out = ht * p.heads_per_tile * D
     else:
         assert p.vec_bytes in (16, 8, 4, 2) and (D * es) % p.vec_bytes == 0 and p.vec_bytes >= es
         L = D * es // p.vec_bytes
@@ -315,7 +316,7 @@ def test_kv_tile():
     for kw, status in [(dict(kv_tile=3), "INVALID_ARG"),                      # does not divide Hkv
                        (dict(kv_tile=2, mode="per_head"), "UNSUPPORTED"),
                        (dict(kv_tile=2, engine="mfma"), "UNSUPPORTED"),
-                       (dict(kv_tile=2, engine="mfma_bf16"), "UNSUPPORTED")]:
+                       (dict(kv_tile=8, engine="mfma_bf16"), "UNSUPPORTED")]:
         with pytest.raises(ga.GqaAvError) as ei:
             ga.make_plan(4, 100, 16, 8, 128, "bf16", **kw)
         assert ei.value.name == status

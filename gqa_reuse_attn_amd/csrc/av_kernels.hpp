@@ -260,12 +260,13 @@ constexpr int kCachePolicyNt = 2;     // non-temporal (streamed once)
 // split's TO partial sums with store_coherent() into blk = the tile's block
 // [nsplit][padded_outputs(TO)]. In the one workgroup that arrives last, every
 // tile output k is summed over the splits in the fixed association of
-// av_pass2_combine (kSplitGroups contiguous split ranges, each in increasing
-// split order, then the range sums in range order) and handed to emit(k, sum).
+// av_pass2_combine (kSplitGroups contiguous split ranges, each summed from
+// +0 in increasing split order, then the range sums in range order) and
+// handed to emit(k, sum). Each thread owns whole float4s of outputs and
+// issues their split loads in batches, with no barrier between batches.
 template <typename Emit>
 __device__ inline void combine_last(const Pass1Args& a, const Tile& T, const float* blk, int TO, Emit emit) {
     __shared__ uint32_t s_last;
-    __shared__ f32x4 red[kSplitGroups][kQuadsPerBlock];
     // The partials must have reached device scope before this workgroup counts
     // itself in: wait for every outstanding store of this wave, then barrier.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -283,28 +284,35 @@ __device__ inline void combine_last(const Pass1Args& a, const Tile& T, const flo
     // every access to the block.
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(blk), 0, ns * TOP * 4, kRawBufferFlags);
-    const int q = threadIdx.x % kQuadsPerBlock, g = threadIdx.x / kQuadsPerBlock;
-    const int s0 = static_cast<int>((static_cast<int64_t>(ns) * g) / kSplitGroups);
-    const int s1 = static_cast<int>((static_cast<int64_t>(ns) * (g + 1)) / kSplitGroups);
-    for (int q0 = 0; q0 < nquads; q0 += kQuadsPerBlock) {
-        const int quad = q0 + q;
-        f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (quad < nquads) {
-#pragma unroll 8
-            for (int s = s0; s < s1; ++s)
-                sum += __builtin_amdgcn_raw_buffer_load_b128(rsrc, (s * TOP + quad * 4) * 4, 0, kCachePolicySc1);
-        }
-        red[g][q] = sum;
-        __syncthreads();
-        if (g == 0 && quad < nquads) {
-            f32x4 t = red[0][q];
+    constexpr int kBatch = 16;
+    for (int quad = threadIdx.x; quad < nquads; quad += kThreads) {
+        f32x4 total = {0.0f, 0.0f, 0.0f, 0.0f}, part = {0.0f, 0.0f, 0.0f, 0.0f};
+        int g = 0;
+        int gend = ns / kSplitGroups;                // first split past group 0
+        auto close_group = [&]() {
+            total = g == 0 ? part : total + part;
+            part = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            ++g;
+            gend = static_cast<int>((static_cast<int64_t>(ns) * (g + 1)) / kSplitGroups);
+        };
+        for (int s0 = 0; s0 < ns; s0 += kBatch) {
+            f32x4 v[kBatch];
 #pragma unroll
-            for (int k = 1; k < kSplitGroups; ++k) t += red[k][q];
+            for (int k = 0; k < kBatch; ++k)
+                if (s0 + k < ns)
+                    v[k] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, ((s0 + k) * TOP + quad * 4) * 4, 0,
+                                                                 kCachePolicySc1);
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                if (quad * 4 + c < TO) emit(quad * 4 + c, t[c]);
+            for (int k = 0; k < kBatch; ++k) {
+                if (s0 + k >= ns) break;
+                while (s0 + k >= gend) close_group();
+                part += v[k];
+            }
         }
-        __syncthreads();
+        while (g < kSplitGroups) close_group();
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if (quad * 4 + c < TO) emit(quad * 4 + c, total[c]);
     }
     if (threadIdx.x == 0) __hip_atomic_store(a.counters + T.id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -1,0 +1,142 @@
+"""CPU checks of the bf16 matrix engine's index arithmetic (no GPU needed).
+
+The kernel's LDS layout and its buffer-resource bounds are restated here in
+plain Python from the kernel's own formulas and checked exhaustively on small
+plans produced by the library's planner:
+
+* the row stores and the transposing reads (ds_read_b64_tr_b16, whose lane
+  layout was probed on MI355X: in each 16-lane group, output lane i element k
+  comes from source lane 4k + i/4, element i mod 4) hand lane (g, m) of a wave
+  the B operand V[8g + j][16t + m], j = 0..7;
+* a lane's V and attn accesses are inside the buffer resource exactly when the
+  row is inside the split (rows past it read as zero), the resources lie inside
+  the tensors, every row of a split is consumed once per KV head, and every
+  output is written once.
+"""
+import numpy as np
+import pytest
+
+import gqa_reuse_attn_amd as ga
+
+ENGINE_BF16 = 3
+
+
+def _swz(PR, row):
+    return ((row & 3) ^ (row >> 3)) & 3 if PR == 8 else ((row & 3) | ((row >> 3) << 2)) & (PR // 2 - 1)
+
+
+@pytest.mark.parametrize("PR", [8, 16, 32])
+def test_lds_transpose_layout(PR):
+    RB, RPI, LPI, D = PR * 16, 64 // PR, PR // 2, PR * 8
+    mem = {}
+    for i in range(LPI):                       # row stores: load i, lane -> (row, 16-byte piece)
+        for lane in range(64):
+            prow, pp = lane // PR, lane % PR
+            row = RPI * i + prow
+            off = row * RB + 32 * ((pp >> 1) ^ _swz(PR, row)) + 16 * (pp & 1)
+            assert 0 <= off and off + 16 <= 32 * RB
+            for e in range(8):
+                assert off + 2 * e not in mem
+                mem[off + 2 * e] = (row, 8 * pp + e)
+    assert len(mem) == 32 * D
+    for t in range(D // 16):
+        for h in range(2):
+            addr = []
+            for lane in range(64):                 # transposing reads: source addresses
+                g = lane >> 4
+                row = 8 * g + 4 * h + ((lane & 15) >> 2)
+                addr.append(row * RB + 32 * (t ^ _swz(PR, row)) + 8 * (lane & 3))
+            for lane in range(64):
+                g, i = lane >> 4, lane & 15
+                for k in range(4):
+                    got = mem[addr[16 * g + 4 * k + i // 4] + 2 * (i % 4)]
+                    assert got == (8 * g + 4 * h + k, 16 * t + i)
+            # 512 bytes per read: at best two passes over 64 banks of 4 bytes
+            banks = {}
+            for a in addr:
+                for w in (a // 4, a // 4 + 1):
+                    banks.setdefault(w % 64, set()).add(w)
+            assert max(len(v) for v in banks.values()) <= 2
+
+
+def _remap(i, n):
+    per, rem = n // 8, n % 8
+    x, k = i % 8, i // 8
+    return x * (per + 1) + k if x < rem else rem * (per + 1) + (x - rem) * per + k
+
+
+def _check_plan(p, B, C, Hq, Hkv, D):
+    assert p.engine == ENGINE_BF16
+    PR, HT = D // 8, p.kv_heads_per_tile
+    RPI, LPI, WPH = 64 // PR, PR // 2, 4 // HT
+    NSET = p.heads_per_tile // 16
+    RSTEP, vrow, G = 32 * WPH, Hkv * D * 2, Hq // Hkv
+    GT, nsg, ns = 16 * NSET, p.subgroups, p.nsplit
+    TO = GT * D
+    assert p.lanes_per_row == HT * D // 8 and p.row_slots == 32 * WPH
+    lanes = np.arange(64)
+    cnt = np.zeros((B, Hq, D), np.int64)
+    nkvt = Hkv // HT
+    for blk in range(p.grid):
+        t = _remap(blk, p.grid)
+        sg = t % nsg; t //= nsg
+        kv = (t % nkvt) * HT; t //= nkvt
+        s = t % ns; t //= ns
+        b = t % B
+        qf, nq = kv * G + sg * GT, min(GT, G - sg * GT)
+        cb = s * p.rows_per_split
+        ce = min(C, cb + p.rows_per_split)
+        nrows = ce - cb
+        assert nrows > 0
+        vrec = (nrows - 1) * vrow + HT * D * 2
+        assert ((b * C + cb) * Hkv + kv) * D * 2 + vrec <= B * C * Hkv * D * 2 and vrec < 2 ** 31
+        wrec = ((nrows - 1) * Hq + (HT - 1) * G + nq) * 4
+        assert ((b * C + cb) * Hq + qf) * 4 + wrec <= B * C * Hq * 4 and wrec < 2 ** 31
+        nsteps = -(-nrows // RSTEP)
+        loaded, st = ([0] if nsteps else []), 0
+        while st + 1 < nsteps:                  # the pipeline's loads, including its unconditional reload
+            loaded += [st + 1, st + 2]
+            st += 2
+        seen = {k: [] for k in range(HT)}
+        for step in loaded:
+            for wave in range(4):
+                kvl, wh = wave // WPH, wave % WPH
+                r0 = 32 * (step * WPH + wh)
+                rows = r0 + RPI * np.arange(LPI)[:, None] + lanes[None, :] // PR
+                off = ((lanes // PR) * vrow + kvl * D * 2 + (lanes % PR) * 16
+                       + (r0 + RPI * np.arange(LPI)[:, None]) * vrow)
+                assert np.array_equal(off + 16 <= vrec, rows < nrows)
+                wrows = r0 + 8 * (lanes >> 4)[None, :] + np.arange(8)[:, None]
+                for sset in range(NSET):
+                    woff = np.minimum((lanes & 15) + 16 * sset, nq - 1)
+                    wo = ((8 * (lanes >> 4)[None, :] * Hq + kvl * G + woff[None, :]) * 4
+                          + (r0 + np.arange(8)[:, None]) * Hq * 4)
+                    assert np.array_equal(wo + 4 <= wrec, wrows < nrows)
+                if step < nsteps:
+                    seen[kvl] += [r for r in range(r0, r0 + 32) if r < nrows]
+        for k in range(HT):
+            assert sorted(seen[k]) == list(range(nrows))
+        if s == 0:
+            idx = np.arange(HT * TO)
+            k, e = idx // TO, idx % TO
+            l, reg = e & 63, e >> 6
+            i, st2 = reg & 3, reg >> 2
+            tt, ss = st2 % (D // 16), st2 // (D // 16)
+            h = 16 * ss + 4 * (l >> 4) + i
+            ok = h < nq
+            np.add.at(cnt, (b, qf + k[ok] * G + h[ok], 16 * tt[ok] + (l[ok] & 15)), 1)
+    assert (cnt == 1).all()
+
+
+@pytest.mark.parametrize("B,C,Hq,Hkv,D", [(1, 300, 16, 1, 128), (2, 1000, 16, 2, 64), (2, 130, 40, 2, 64),
+                                         (1, 257, 24, 1, 256), (2, 31, 16, 1, 128), (1, 1, 16, 1, 64),
+                                         (2, 700, 32, 4, 128), (1, 300, 48, 4, 256), (3, 1500, 16, 2, 64)])
+def test_bf16_engine_plan_bounds(B, C, Hq, Hkv, D):
+    for ns in (0, 1, 3, 7):
+        for comb in ("kernel", "last"):
+            for ht in (0, 1, 2, 4):
+                if ht > 1 and Hkv % ht:
+                    continue
+                p = ga.make_plan(B, C, Hq, Hkv, D, "bf16", "reuse", engine="mfma_bf16", nsplit=ns,
+                                 combine=comb, kv_tile=ht)
+                _check_plan(p, B, C, Hq, Hkv, D)

@@ -6,8 +6,10 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 
 ``gqa_av_oracle.c`` holds the definition (ExecuTorch PR #21063, "...GEMV",
 introduction, with a batch index added): fp64 sums over context positions c of
-exact fp32 x V products, kv_h = floor(q_h / G). ``brute.py`` holds a
-pure-Python correctly rounded version for tiny shapes. Every function here is
+exact fp32 x V products, kv_h = floor(q_h / G). It also holds the decode score
+step that precedes it (not on the page: scale * sum over d of q * K with the
+same head grouping, output in the attn layout). ``brute.py`` holds
+pure-Python correctly rounded versions of both for tiny shapes. Every function here is
 pinned by ``tests/test_oracle_pins.py``; none is "parity unpinned".
 """
 from __future__ import annotations
@@ -53,6 +55,8 @@ class Oracle:
         lib.gqa_av_oracle_points.restype = ip
         lib.gqa_av_oracle_decode.argtypes = [vp, ip, i64, vp]
         lib.gqa_av_oracle_decode.restype = ip
+        lib.gqa_qk_oracle.argtypes = [vp, vp, ip, i64, i64, i64, i64, i64, ctypes.c_double, vp, ip]
+        lib.gqa_qk_oracle.restype = ip
         self.lib = lib
 
     @staticmethod
@@ -73,6 +77,19 @@ class Oracle:
         out = np.empty((B, Hq, D), dtype=np.float64)
         rc = self.lib.gqa_av_oracle(a.ctypes.data, v.ctypes.data, DTYPE_CODE[v_dtype],
                                     B, C, Hq, Hkv, D, out.ctypes.data, nthreads)
+        if rc != 0:
+            raise ValueError(f"oracle rejected the arguments (status {rc})")
+        return out
+
+    def qk(self, q, K, k_dtype: str, scale: float = 1.0, nthreads: int = 0) -> np.ndarray:
+        """scores[B, C, Hq] (float64) for q [B,Hq,D] fp32 and K [B,C,Hkv,D]."""
+        qa, k = self._np_inputs(q, K, k_dtype)
+        B, Hq, D = qa.shape
+        B2, C, Hkv, D2 = k.shape
+        assert B2 == B and D2 == D
+        out = np.empty((B, C, Hq), dtype=np.float64)
+        rc = self.lib.gqa_qk_oracle(qa.ctypes.data, k.ctypes.data, DTYPE_CODE[k_dtype],
+                                    B, C, Hq, Hkv, D, float(scale), out.ctypes.data, nthreads)
         if rc != 0:
             raise ValueError(f"oracle rejected the arguments (status {rc})")
         return out

@@ -42,3 +42,28 @@ def abs_sum(attn: torch.Tensor, V: torch.Tensor) -> np.ndarray:
     G = a.shape[2] // v.shape[2]
     vq = np.repeat(v, G, axis=2)                       # [B, C, Hq, D]
     return np.einsum("bch,bchd->bhd", np.abs(a), np.abs(vq))
+
+
+def brute_force_qk(q: torch.Tensor, K: torch.Tensor, scale: float) -> np.ndarray:
+    """scores[B, C, Hq] as float64: the exact sum over d rounded once, times scale."""
+    qa = q.detach().cpu().to(torch.float64).tolist()     # [B][Hq][D]
+    k = K.detach().cpu().to(torch.float64).tolist()      # [B][C][Hkv][D]
+    B, Hq, D = q.shape
+    C, Hkv = K.shape[1], K.shape[2]
+    G = Hq // Hkv
+    out = np.zeros((B, C, Hq), dtype=np.float64)
+    for b in range(B):
+        for c in range(C):
+            for h in range(Hq):
+                kv = h // G
+                out[b, c, h] = math.fsum(qa[b][h][d] * k[b][c][kv][d] for d in range(D)) * scale
+    return out
+
+
+def abs_sum_qk(q: torch.Tensor, K: torch.Tensor) -> np.ndarray:
+    """sum_d |q * K| per score (scale for the oracle's error bound)."""
+    qa = q.detach().cpu().to(torch.float64).numpy()
+    k = K.detach().cpu().to(torch.float64).numpy()
+    G = qa.shape[1] // k.shape[2]
+    kq = np.repeat(k, G, axis=2)                       # [B, C, Hq, D]
+    return np.einsum("bhd,bchd->bch", np.abs(qa), np.abs(kq))

@@ -28,6 +28,17 @@
  *
  * Layouts are dense row-major: attn [B][C][Hq] float32, V [B][C][Hkv][D] of
  * the given dtype, out [B][Hq][D] double.
+ *
+ * The score step that precedes it in decode attention is not on the page; it
+ * is the standard first half of decode attention with the same head grouping
+ * (each K row shared by the G query heads of its group), and its output has
+ * the layout of attn above:
+ *
+ *   scores[b, c, q_h] = scale * sum_{d=0}^{D-1} q[b, q_h, d] * K[b, c, kv_h(q_h), d]
+ *
+ * with q [B][Hq][D] float32, K [B][C][Hkv][D] of the given dtype and scores
+ * [B][C][Hq] double. Each product is exact in double, the sum runs in double
+ * in increasing d, and the scale multiplies the sum.
  */
 #include <math.h>
 #include <pthread.h>
@@ -172,6 +183,40 @@ int gqa_av_oracle_points(const float *attn, const void *V, int dtype,
                    orc_load(V, dtype, ((b * C + c) * Hkv + kv) * D + d);
         out[k] = acc;
     }
+    (void)nthreads;
+    return ORC_OK;
+}
+
+/* Scores of one context row: scores[b, c, 0:Hq], the definition above. */
+static void orc_qk_row(const float *q, const void *K, int dtype,
+                       int64_t C, int64_t Hq, int64_t Hkv, int64_t D,
+                       int64_t b, int64_t c, double scale, double *out)
+{
+    const int64_t G = Hq / Hkv;
+    for (int64_t h = 0; h < Hq; ++h) {
+        const int64_t kvh = h / G;
+        const float *qrow = q + (b * Hq + h) * D;
+        const int64_t krow = ((b * C + c) * Hkv + kvh) * D;
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; ++d) dot += (double)qrow[d] * orc_load(K, dtype, krow + d);
+        out[h] = dot * scale;
+    }
+}
+
+/* Full scores: out[B][C][Hq] in double. nthreads <= 0 uses the OpenMP default. */
+int gqa_qk_oracle(const float *q, const void *K, int dtype,
+                  int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D,
+                  double scale, double *out, int nthreads)
+{
+    int rc = orc_check(dtype, B, C, Hq, Hkv, D);
+    if (rc != ORC_OK) return rc;
+    const int64_t rows = B * C;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 64) num_threads(nthreads)
+#endif
+    for (int64_t i = 0; i < rows; ++i)
+        orc_qk_row(q, K, dtype, C, Hq, Hkv, D, i / C, i % C, scale, out + i * Hq);
     (void)nthreads;
     return ORC_OK;
 }

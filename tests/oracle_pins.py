@@ -22,6 +22,19 @@ What pins what:
   * points            the sampled entry point equals brute force.
   * edges             C = 0 gives zeros; B = 0 gives an empty result;
                       Hq % Hkv != 0 is rejected.
+
+The score step (scores = scale * q . K over d, in the attn layout):
+  * qk_brute_force    tiny shapes, all dtypes, against the correctly rounded
+                      exact dot products (oracle/brute.py).
+  * qk_mha_einsum     G = 1 equals numpy's einsum 'bhd,bchd->bch' in fp64.
+  * qk_repeat_mha     GQA equals MHA over K repeated G times (bitwise).
+  * qk_one_hot        q = e_j returns scale * K[..., j] exactly.
+  * qk_scale_linear   scale by a power of two is exact; linearity in q.
+  * qk_composition    softmax over c of the scores, then the AV oracle, equals
+                      decode attention written as one numpy fp64 expression:
+                      pins that the scores come out in the attn layout.
+  * qk_edges          C = 0 and B = 0 give empty results; Hq % Hkv != 0 is
+                      rejected; D = 1.
 """
 from __future__ import annotations
 
@@ -30,8 +43,8 @@ import math
 import numpy as np
 import torch
 
-from oracle.brute import abs_sum, brute_force
-from workloads import make_random
+from oracle.brute import abs_sum, abs_sum_qk, brute_force, brute_force_qk
+from workloads import make_qk_random, make_random
 
 U64 = 2.0 ** -53
 
@@ -215,6 +228,123 @@ def pin_edges(orc):
         raise AssertionError("Hq % Hkv != 0 must be rejected")
 
 
+def _qk_cases():
+    return [
+        # B, C, Hq, Hkv, D, dtype
+        (1, 1, 1, 1, 1, "f32"),
+        (2, 7, 6, 2, 13, "f32"),
+        (2, 5, 4, 1, 16, "bf16"),
+        (1, 6, 6, 3, 9, "f16"),
+        (2, 4, 8, 8, 5, "bf16"),
+    ]
+
+
+def pin_qk_brute_force(orc):
+    for i, (B, C, Hq, Hkv, D, dt) in enumerate(_qk_cases()):
+        q, K = make_qk_random(B, C, Hq, Hkv, D, dt, seed=500 + i)
+        for scale in (1.0, 0.125, 0.3):
+            exact = brute_force_qk(q, K, scale)
+            o = orc.qk(q, K, dt, scale)
+            # a-priori bound: gamma_{D-1} on the sum, one rounding for the scale
+            bound = (gamma(max(D - 1, 0)) * abs_sum_qk(q, K) * abs(scale) + 2 * U64 * np.abs(exact)) + 1e-300
+            err = np.abs(o - exact)
+            assert (err <= bound).all(), f"qk brute {B, C, Hq, Hkv, D, dt} scale {scale}: worst {float((err - bound).max()):.3e}"
+
+
+def pin_qk_mha_einsum(orc):
+    for dt in ("f32", "bf16", "f16"):
+        q, K = make_qk_random(2, 9, 3, 3, 24, dt, seed=41)
+        ref = np.einsum("bhd,bchd->bch", q.double().numpy(), K.double().numpy()) * 0.25
+        o = orc.qk(q, K, dt, 0.25)
+        bound = gamma(2 * 24) * abs_sum_qk(q, K) * 0.25 + 1e-300
+        assert (np.abs(o - ref) <= bound).all(), f"qk einsum {dt}"
+
+
+def pin_qk_repeat_mha(orc):
+    for dt, (Hq, Hkv) in (("bf16", (8, 2)), ("f16", (6, 3)), ("f32", (5, 1))):
+        q, K = make_qk_random(2, 11, Hq, Hkv, 10, dt, seed=43)
+        G = Hq // Hkv
+        Krep = K.repeat_interleave(G, dim=2).contiguous()
+        a = orc.qk(q, K, dt, 0.5)
+        b = orc.qk(q, Krep, dt, 0.5)
+        assert np.array_equal(a, b), f"qk: GQA != MHA over repeated K ({dt}, G={G})"
+        ref = np.einsum("bhd,bchd->bch", q.double().numpy(), Krep.double().numpy()) * 0.5
+        bound = gamma(2 * 10) * abs_sum_qk(q, K) * 0.5 + 1e-300
+        assert (np.abs(a - ref) <= bound).all(), f"qk repeat-einsum {dt}"
+
+
+def pin_qk_one_hot(orc):
+    for dt in ("f32", "bf16", "f16"):
+        B, C, Hq, Hkv, D = 2, 13, 6, 2, 11
+        _, K = make_qk_random(B, C, Hq, Hkv, D, dt, seed=47)
+        G = Hq // Hkv
+        q = torch.zeros(B, Hq, D)
+        pick = {}
+        for b in range(B):
+            for h in range(Hq):
+                j = (5 * b + 3 * h + 1) % D
+                q[b, h, j] = 1.0
+                pick[b, h] = j
+        o = orc.qk(q, K, dt, 0.5)
+        Kd = K.double().numpy()
+        for (b, h), j in pick.items():
+            assert np.array_equal(o[b, :, h], 0.5 * Kd[b, :, h // G, j]), f"qk one-hot {dt} b={b} h={h}"
+
+
+def pin_qk_scale_linear(orc):
+    q1, K = make_qk_random(2, 8, 4, 2, 12, "bf16", seed=53)
+    q2, _ = make_qk_random(2, 8, 4, 2, 12, "bf16", seed=54)
+    base = orc.qk(q1, K, "bf16", 1.0)
+    assert np.array_equal(orc.qk(q1, K, "bf16", 0.25), 0.25 * base), "qk: a power-of-two scale must be exact"
+    assert np.array_equal(orc.qk(q1, K, "bf16", -1.0), -base), "qk: scale -1 must negate"
+    # dyadic q with few significant bits, so 3 q1 - 0.5 q2 is exact in fp32
+    q1 = torch.round(q1 * 64) / 64
+    q2 = torch.round(q2 * 64) / 64
+    base = orc.qk(q1, K, "bf16", 1.0)
+    mix = orc.qk(3.0 * q1 - 0.5 * q2, K, "bf16", 1.0)
+    ref = 3.0 * base - 0.5 * orc.qk(q2, K, "bf16", 1.0)
+    scale = abs_sum_qk(3.0 * q1, K) + abs_sum_qk(0.5 * q2, K)
+    assert (np.abs(mix - ref) <= 64 * U64 * scale + 1e-300).all(), "qk linearity in q"
+
+
+def pin_qk_composition(orc):
+    B, C, Hq, Hkv, D = 2, 40, 8, 2, 16
+    for dt in ("bf16", "f32"):
+        q, K = make_qk_random(B, C, Hq, Hkv, D, dt, seed=59)
+        _, V = make_qk_random(B, C, Hq, Hkv, D, dt, seed=61)
+        s = orc.qk(q, K, dt, D ** -0.5)                       # [B, C, Hq]
+        e = np.exp(s - s.max(axis=1, keepdims=True))
+        attn = (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
+        out = orc.full(torch.from_numpy(attn), V, dt)          # [B, Hq, D]
+        G = Hq // Hkv
+        Kr = np.repeat(K.double().numpy(), G, axis=2)          # [B, C, Hq, D]
+        Vr = np.repeat(V.double().numpy(), G, axis=2)
+        logits = np.einsum("bhd,bchd->bhc", q.double().numpy(), Kr) * D ** -0.5
+        p = np.exp(logits - logits.max(axis=2, keepdims=True))
+        p /= p.sum(axis=2, keepdims=True)
+        ref = np.einsum("bhc,bchd->bhd", p, Vr)
+        rel = np.abs(out - ref).max() / np.abs(ref).max()
+        assert rel < 1e-6, f"qk composition {dt}: {rel:.2e}"      # attn is rounded to fp32 in between
+
+
+def pin_qk_edges(orc):
+    q = torch.zeros(2, 4, 3)
+    o = orc.qk(q, torch.zeros(2, 0, 2, 3, dtype=torch.bfloat16), "bf16")
+    assert o.shape == (2, 0, 4)
+    o = orc.qk(torch.zeros(0, 4, 3), torch.zeros(0, 5, 2, 3), "f32")
+    assert o.shape == (0, 5, 4)
+    try:
+        orc.qk(torch.zeros(1, 5, 3), torch.zeros(1, 2, 2, 3), "f32")
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("qk: Hq % Hkv != 0 must be rejected")
+    q, K = make_qk_random(1, 3, 2, 1, 1, "f16", seed=67)
+    o = orc.qk(q, K, "f16", 2.0)
+    assert np.array_equal(o[0, :, 1], 2.0 * q[0, 1, 0].item() * K[0, :, 0, 0].double().numpy()), "qk D = 1"
+
+
 ALL_PINS = [pin_decode_table, pin_brute_force, pin_mha_einsum, pin_repeat_mha, pin_constant_v,
             pin_one_hot, pin_linearity, pin_permutation, pin_batch_independence, pin_points,
-            pin_edges]
+            pin_edges, pin_qk_brute_force, pin_qk_mha_einsum, pin_qk_repeat_mha, pin_qk_one_hot,
+            pin_qk_scale_linear, pin_qk_composition, pin_qk_edges]

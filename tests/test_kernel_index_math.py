@@ -1,8 +1,8 @@
-"""CPU checks of the bf16 matrix engine's index arithmetic (no GPU needed).
+"""CPU checks of the pass-1 kernels' index arithmetic (no GPU needed).
 
-The kernel's LDS layout and its buffer-resource bounds are restated here in
-plain Python from the kernel's own formulas and checked exhaustively on small
-plans produced by the library's planner:
+The kernels' LDS layout and buffer-resource bounds are restated here in plain
+Python from the kernels' own formulas and checked exhaustively on small plans
+produced by the library's planner. bf16 matrix engine:
 
 * the row stores and the transposing reads (ds_read_b64_tr_b16, whose lane
   layout was probed on MI355X: in each 16-lane group, output lane i element k
@@ -12,6 +12,10 @@ plans produced by the library's planner:
   row is inside the split (rows past it read as zero), the resources lie inside
   the tensors, every row of a split is consumed once per KV head, and every
   output is written once.
+
+VALU engine: the same bounds, rows and outputs for its lane layout (row slots,
+lane chunks, KV heads per tile, D-tiles, weight windows), in reuse and
+per-head mode, for every V dtype.
 """
 import numpy as np
 import pytest
@@ -140,3 +144,102 @@ def test_bf16_engine_plan_bounds(B, C, Hq, Hkv, D):
                 p = ga.make_plan(B, C, Hq, Hkv, D, "bf16", "reuse", engine="mfma_bf16", nsplit=ns,
                                  combine=comb, kv_tile=ht)
                 _check_plan(p, B, C, Hq, Hkv, D)
+
+
+ENGINE_VALU = 1
+
+
+def _esize(dt):
+    return 4 if dt == "f32" else 2
+
+
+def _check_valu_plan(p, B, C, Hq, Hkv, D, dt):
+    assert p.engine == ENGINE_VALU
+    es, G = _esize(dt), Hq // Hkv
+    VB, Lc, rps, ndt, HT = p.vec_bytes, p.lanes_per_row, p.row_slots, p.d_tiles, p.kv_heads_per_tile
+    E, L = VB // es, D * es // VB
+    per_head = p.mode == 0
+    GT = 1 if per_head else p.heads_per_tile
+    U = 4 if GT <= 4 else (2 if GT <= 8 else 1)
+    R, vrow, ns = rps * U, Hkv * D * es, p.nsplit
+    assert rps * Lc <= 256 and GT <= Hq
+    nminor = ndt if per_head else p.subgroups * ndt
+    nkvt = Hkv // HT
+    tid = np.arange(256)
+    r, j = tid // Lc, tid % Lc
+    kvl = j // L
+    cnt = np.zeros((B, Hq, D), np.int64)
+    for blk in range(p.grid):
+        t = _remap(blk, p.grid)
+        minor = t % nminor; t //= nminor
+        kvt = t % nkvt; t //= nkvt
+        kv = kvt * HT
+        s = t % ns; t //= ns
+        b = t % B; major = t // B
+        if per_head:
+            dtile, qf, nq = minor, kv * G + major, 1
+        else:
+            sg, dtile = minor // ndt, minor % ndt
+            qf, nq = kv * G + sg * GT, min(GT, G - sg * GT)
+        lane_d = dtile * Lc + (j - kvl * L)
+        active = (r < rps) & (lane_d < L)
+        cb = s * p.rows_per_split
+        ce = min(C, cb + p.rows_per_split)
+        nrows = ce - cb
+        assert nrows > 0
+        vrec = (nrows - 1) * vrow + HT * D * es
+        assert ((b * C + cb) * Hkv + kv) * D * es + vrec <= B * C * Hkv * D * es and vrec < 2 ** 31
+        wrec = nrows * Hq * 4
+        assert (b * C + cb) * Hq * 4 + wrec <= B * C * Hq * 4
+        q_lo = np.minimum(qf + kvl * G, Hq - GT)
+        voff = r * vrow + kvl * D * es + lane_d * VB
+        woff = (r * Hq + q_lo) * 4
+        nsteps = -(-nrows // R)
+        loaded, st = ([0] if nsteps else []), 0
+        while st + 1 < nsteps:
+            loaded += [st + 1, st + 2]
+            st += 2
+        for step in loaded:
+            for u in range(U):
+                row = step * R + u * rps
+                assert (row + 2 * R) * vrow < 2 ** 31 and (row + 2 * R) * Hq * 4 < 2 ** 31
+                inrow = (row + r) < nrows
+                off = voff + row * vrow
+                assert np.array_equal((off + VB <= vrec)[active], inrow[active])
+                assert (off[active] >= 0).all()
+                wo = woff + row * Hq * 4
+                for k0 in range(0, GT, 4):
+                    n = min(4, GT - k0)
+                    assert np.array_equal((wo + 4 * k0 + 4 * n <= wrec)[active], inrow[active])
+        if s == 0:
+            for jj in range(Lc):
+                kl = jj // L
+                ld = dtile * Lc + (jj - kl * L)
+                if ld >= L:
+                    continue
+                ql = min(qf + kl * G, Hq - GT)
+                go = qf + kl * G - ql
+                for g in range(go, go + nq):
+                    cnt[b, ql + g, ld * E:(ld + 1) * E] += 1
+    assert (cnt == 1).all()
+
+
+@pytest.mark.parametrize("B,C,Hq,Hkv,D,dt", [
+    (2, 1000, 8, 4, 128, "bf16"), (1, 300, 4, 2, 127, "bf16"), (2, 129, 6, 3, 1, "f16"), (1, 200, 1, 1, 64, "f32"),
+    (2, 150, 64, 1, 64, "bf16"), (1, 90, 4, 2, 2048, "f32"), (3, 257, 10, 5, 80, "f16"), (2, 333, 24, 8, 96, "f16"),
+    (1, 64, 32, 8, 128, "bf16"), (2, 500, 14, 2, 256, "bf16"), (1, 777, 12, 3, 128, "f32")])
+def test_valu_engine_plan_bounds(B, C, Hq, Hkv, D, dt):
+    modes = ("reuse", "per_head") if Hq // Hkv >= 2 else ("per_head",)
+    for mode in modes:
+        for ns in (0, 1, 3, 7):
+            for ht in (0, 1, 2, 4):
+                if ht > 1 and (Hkv % ht or mode == "per_head"):
+                    continue
+                for align in (0, 2):
+                    try:
+                        p = ga.make_plan(B, C, Hq, Hkv, D, dt, mode, engine="valu", nsplit=ns, kv_tile=ht,
+                                         v_align=align)
+                    except ga.GqaAvError as e:
+                        assert e.name == "UNSUPPORTED"
+                        continue
+                    _check_valu_plan(p, B, C, Hq, Hkv, D, dt)

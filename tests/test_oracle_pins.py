@@ -41,6 +41,14 @@ PLANTS = [
      "for (int64_t d = 0; d < D; ++d) acc[d] += (float)(a * orc_f32(r + d));"),
     ("points_wrong_head", "const int64_t kv = q / G;\n        double acc = 0.0;",
      "const int64_t kv = q / G + (q % G == 1);\n        double acc = 0.0;"),
+    ("qk_kv_mod_mapping", "const int64_t kvh = h / G;", "const int64_t kvh = h % Hkv;"),
+    ("qk_drop_last_d", "for (int64_t d = 0; d < D; ++d) dot +=", "for (int64_t d = 0; d < D - 1; ++d) dot +="),
+    ("qk_no_scale", "out[h] = dot * scale;", "out[h] = dot;"),
+    ("qk_q_of_head_zero", "const float *qrow = q + (b * Hq + h) * D;", "const float *qrow = q + (b * Hq + 0) * D;"),
+    ("qk_out_transposed", "orc_qk_row(q, K, dtype, C, Hq, Hkv, D, i / C, i % C, scale, out + i * Hq);",
+     "orc_qk_row(q, K, dtype, C, Hq, Hkv, D, i % B, i / B, scale, out + i * Hq);"),
+    ("qk_k_ignores_batch", "const int64_t krow = ((b * C + c) * Hkv + kvh) * D;",
+     "const int64_t krow = ((0 * C + c) * Hkv + kvh) * D;"),
 ]
 
 

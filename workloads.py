@@ -154,3 +154,15 @@ def make_random(B: int, C: int, Hq: int, Hkv: int, D: int, v_dtype: str,
         g = torch.Generator(device="cpu").manual_seed(seed + 7919)
         attn = torch.randn(B, C, Hq, generator=g, dtype=torch.float32)
     return attn, V
+
+
+def make_qk_random(B: int, C: int, Hq: int, Hkv: int, D: int, k_dtype: str,
+                   seed: int = 0, q_std: float = 1.0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Inputs of the decode score step: q [B, Hq, D] fp32 ~ N(0, q_std^2) and the
+    K cache [B, C, Hkv, D] ~ N(0, 1) rounded to k_dtype. Drawn in this order on
+    one CPU generator; no arithmetic of the method."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    K = torch.randn(B, C, Hkv, D, generator=g, dtype=torch.float32)
+    q = torch.randn(B, Hq, D, generator=g, dtype=torch.float32) * q_std
+    dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[k_dtype]
+    return q.contiguous(), K.to(dt).contiguous()

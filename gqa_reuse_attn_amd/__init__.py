@@ -2,8 +2,13 @@
 
     out[b, q_h, d] = sum_c attn[b, c, q_h] * V[b, c, q_h // G, d],   G = Hq // Hkv
 
-(ExecuTorch PR #21063, "...GEMV", introduction; batch index added.) Every
-step runs in the HIP library; this module only checks tensors and marshals
+(ExecuTorch PR #21063, "...GEMV", introduction; batch index added.) The same
+library holds the decode score step before it (not on that page; the same
+head grouping, output in the attn layout):
+
+    scores[b, c, q_h] = scale * sum_d q[b, q_h, d] * K[b, c, q_h // G, d]
+
+Every step runs in the HIP library; this module only checks tensors and marshals
 pointers, sizes and the stream through ctypes. PyTorch provides device memory
 and streams. There is no CPU fallback: if the library is missing, calls raise.
 """
@@ -16,6 +21,7 @@ from typing import Optional, Union
 __all__ = [
     "LIB_PATH", "GqaAvError", "Hint", "Plan", "load", "resolve_mode", "make_plan",
     "gqa_av_decode", "gqa_av_decode_plan", "bind", "BoundCall", "release", "status_string", "MODES", "DTYPES",
+    "QkPlan", "qk_make_plan", "gqa_qk_decode", "bind_qk",
 ]
 
 # GQA_AV_LIBRARY may name another build of the same library (tuning variants).
@@ -56,6 +62,18 @@ class Plan(ctypes.Structure):
         return f"Plan({self.as_dict()})"
 
 
+class QkPlan(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("engine", ctypes.c_int32), ("heads_per_tile", ctypes.c_int32),
+                ("subgroups", ctypes.c_int32), ("rows_per_block", ctypes.c_int64), ("grid", ctypes.c_int64),
+                ("k_bytes_read", ctypes.c_int64), ("reserved", ctypes.c_int32 * 4)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+
+    def __repr__(self) -> str:
+        return f"QkPlan({self.as_dict()})"
+
+
 _lib = None
 
 
@@ -84,6 +102,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gqa_av_last_error.restype = ctypes.c_char_p
     lib.gqa_av_release.argtypes = []
     lib.gqa_av_release.restype = ip
+    lib.gqa_qk_make_plan.argtypes = [i64, i64, i64, i64, i64, ip, ip, i64, ip, ctypes.POINTER(QkPlan)]
+    lib.gqa_qk_make_plan.restype = ip
+    lib.gqa_qk_decode.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ip, ctypes.c_float, ip, vp]
+    lib.gqa_qk_decode.restype = ip
+    lib.gqa_qk_decode_plan.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ip, ctypes.c_float,
+                                       ctypes.POINTER(QkPlan), vp]
+    lib.gqa_qk_decode_plan.restype = ip
     del i32
     _lib = lib
     return lib
@@ -255,3 +280,98 @@ def release() -> None:
     rc = load().gqa_av_release()
     if rc != 0:
         _raise(rc)
+
+
+# ---- decode score step ----------------------------------------------------------
+
+def qk_make_plan(B: int, C: int, Hq: int, Hkv: int, D: int, k_dtype: str, mode: Union[str, int] = "auto",
+                 rows_per_block: int = 0, cu_count: int = 0) -> QkPlan:
+    """Host-only planning of the score step (no GPU needed); 0 means automatic."""
+    p = QkPlan()
+    rc = load().gqa_qk_make_plan(B, C, Hq, Hkv, D, DTYPES[k_dtype], _mode(mode), int(rows_per_block),
+                                 int(cu_count), ctypes.byref(p))
+    if rc != 0:
+        _raise(rc)
+    return p
+
+
+def _check_qk(q, K, scores):
+    torch = _torch()
+    kmap = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
+    if q.dim() != 3 or K.dim() != 4:
+        raise ValueError(f"q must be [B,Hq,D] and K [B,C,Hkv,D]; got {tuple(q.shape)} and {tuple(K.shape)}")
+    B, Hq, D = q.shape
+    if K.shape[0] != B or K.shape[3] != D:
+        raise ValueError(f"K {tuple(K.shape)} does not match q {tuple(q.shape)} in B or D")
+    C, Hkv = K.shape[1], K.shape[2]
+    if q.dtype != torch.float32:
+        raise TypeError(f"q must be float32, got {q.dtype}")
+    if K.dtype not in kmap:
+        raise TypeError(f"K must be float32, float16 or bfloat16, got {K.dtype}")
+    if not (q.is_cuda and K.is_cuda) or q.device != K.device:
+        raise ValueError("q and K must be GPU tensors on one device")
+    if not (q.is_contiguous() and K.is_contiguous()):
+        raise ValueError("q and K must be contiguous")
+    if scores is not None:
+        if scores.dtype != torch.float32 or tuple(scores.shape) != (B, C, Hq) or not scores.is_contiguous() \
+                or scores.device != q.device:
+            raise ValueError(f"scores must be a contiguous float32 [{B},{C},{Hq}] tensor on {q.device}")
+    return B, C, Hq, Hkv, D, kmap[K.dtype]
+
+
+def gqa_qk_decode(q, K, scores=None, scale: float = 1.0, mode: Union[str, int] = "auto", stream=None,
+                  plan: Optional[QkPlan] = None):
+    """scores[b,c,q_h] = scale * sum_d q[b,q_h,d] * K[b,c,q_h//G,d] on the GPU; returns scores.
+
+    q: float32 [B,Hq,D]; K: float32/float16/bfloat16 [B,C,Hkv,D]; both
+    contiguous on one GPU. The result has the attn layout [B,C,Hq] of
+    gqa_av_decode.
+    """
+    torch = _torch()
+    B, C, Hq, Hkv, D, kdt = _check_qk(q, K, scores)
+    if scores is None:
+        scores = torch.empty((B, C, Hq), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    lib = load()
+    with torch.cuda.device(q.device):
+        if plan is None:
+            rc = lib.gqa_qk_decode(q.data_ptr(), K.data_ptr(), scores.data_ptr(), B, C, Hq, Hkv, D, DTYPES[kdt],
+                                   float(scale), _mode(mode), stream.cuda_stream)
+        else:
+            rc = lib.gqa_qk_decode_plan(q.data_ptr(), K.data_ptr(), scores.data_ptr(), B, C, Hq, Hkv, D,
+                                        DTYPES[kdt], float(scale), ctypes.byref(plan), stream.cuda_stream)
+    if rc != 0:
+        _raise(rc)
+    return scores
+
+
+class BoundQk:
+    """Pre-checked score-step call for loops (see BoundCall)."""
+
+    def __init__(self, q, K, scores=None, scale: float = 1.0, plan: Optional[QkPlan] = None,
+                 mode: Union[str, int] = "auto", stream=None):
+        torch = _torch()
+        B, C, Hq, Hkv, D, kdt = _check_qk(q, K, scores)
+        if scores is None:
+            scores = torch.empty((B, C, Hq), dtype=torch.float32, device=q.device)
+        if plan is None:
+            cu = torch.cuda.get_device_properties(q.device).multi_processor_count
+            plan = qk_make_plan(B, C, Hq, Hkv, D, kdt, mode, cu_count=cu)
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        self.q, self.K, self.scores, self.plan = q, K, scores, plan
+        self._fn = load().gqa_qk_decode_plan
+        self._args = (q.data_ptr(), K.data_ptr(), scores.data_ptr(), B, C, Hq, Hkv, D, DTYPES[kdt],
+                      ctypes.c_float(scale), ctypes.byref(plan), stream.cuda_stream)
+
+    def __call__(self):
+        rc = self._fn(*self._args)
+        if rc != 0:
+            _raise(rc)
+        return self.scores
+
+
+def bind_qk(q, K, scores=None, scale: float = 1.0, plan: Optional[QkPlan] = None, mode: Union[str, int] = "auto",
+            stream=None) -> BoundQk:
+    return BoundQk(q, K, scores=scores, scale=scale, plan=plan, mode=mode, stream=stream)

@@ -117,6 +117,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer-resource word 3 for raw (untyped) buffer access on gfx9-family parts.
+constexpr int kRawBufferFlags = 0x00020000;
+constexpr int kCachePolicySc1 = 16;   // device-scope coherence (same policy as agent-scope atomics)
+constexpr int kCachePolicyNt = 2;     // non-temporal (streamed once)
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 
@@ -154,12 +159,66 @@ __device__ inline Raw<NB> load_raw(const uint8_t* p) {
     return r;
 }
 
+// Buffer-resource forms: NB bytes (2, 4, 8 or 16) at voffset + soffset of
+// the resource, non-temporal; zero when the range check of the resource fails.
+template <int NB>
+__device__ inline Raw<NB> load_raw_buf(__amdgpu_buffer_rsrc_t rs, int voffset, int soffset) {
+    Raw<NB> r;
+    if constexpr (NB == 16) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, voffset, soffset, kCachePolicyNt);
+        r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+    } else if constexpr (NB == 8) {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, voffset, soffset, kCachePolicyNt);
+        r.w[0] = v.x; r.w[1] = v.y;
+    } else if constexpr (NB == 4) {
+        r.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, voffset, soffset, kCachePolicyNt);
+    } else {
+        static_assert(NB == 2, "lane loads are 2, 4, 8 or 16 bytes");
+        r.w[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, voffset, soffset, kCachePolicyNt);
+    }
+    return r;
+}
+
+// N consecutive floats at voffset + soffset of the resource (4-byte aligned),
+// in loads of up to 16 bytes.
+template <int N>
+__device__ inline void load_floats(__amdgpu_buffer_rsrc_t rs, int voffset, int soffset, float* out) {
+    int k = 0;
+#pragma unroll
+    for (; k + 4 <= N; k += 4) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, voffset + 4 * k, soffset, 0);
+        out[k] = __uint_as_float(v.x); out[k + 1] = __uint_as_float(v.y);
+        out[k + 2] = __uint_as_float(v.z); out[k + 3] = __uint_as_float(v.w);
+    }
+    if constexpr (N % 4 == 3) {
+        const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(rs, voffset + 4 * k, soffset, 0);
+        out[k] = __uint_as_float(v.x); out[k + 1] = __uint_as_float(v.y); out[k + 2] = __uint_as_float(v.z);
+    } else if constexpr (N % 4 == 2) {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, voffset + 4 * k, soffset, 0);
+        out[k] = __uint_as_float(v.x); out[k + 1] = __uint_as_float(v.y);
+    } else if constexpr (N % 4 == 1) {
+        out[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, voffset + 4 * k, soffset, 0));
+    }
+}
+
 template <int NB>
 __device__ inline Raw<NB> zero_raw() {
     Raw<NB> r;
 #pragma unroll
     for (int i = 0; i < (NB >= 4 ? NB / 4 : 1); ++i) r.w[i] = 0u;
     return r;
+}
+
+// Exact split of an fp32 value w into three bfloat16 terms by truncation:
+// th = trunc(w), tm = trunc(w - th), tl = w - th - tm. Both subtractions are
+// exact (Sterbenz) and tl has at most 8 significant bits, so th + tm + tl = w
+// for every normal w down to 2^-103. Returned as fp32 bit patterns whose low
+// 16 bits are zero (the upper halves are the bfloat16 encodings).
+__device__ inline void split_bf16x3(float w, uint32_t& th, uint32_t& tm, uint32_t& tl) {
+    th = __float_as_uint(w) & 0xffff0000u;
+    const float r1 = w - __uint_as_float(th);
+    tm = __float_as_uint(r1) & 0xffff0000u;
+    tl = __float_as_uint(r1 - __uint_as_float(tm)) & 0xffff0000u;
 }
 
 __device__ inline float f16_bits_to_f32(uint32_t h) {
@@ -251,10 +310,6 @@ __device__ inline float load_coherent(const float* p) {
 __device__ __host__ constexpr int padded_outputs(int TO) { return (TO + 3) / 4 * 4; }
 
 constexpr int kQuadsPerBlock = kThreads / kSplitGroups;
-// Buffer-resource word 3 for raw (untyped) buffer access on gfx9-family parts.
-constexpr int kRawBufferFlags = 0x00020000;
-constexpr int kCachePolicySc1 = 16;   // device-scope coherence (same policy as agent-scope atomics)
-constexpr int kCachePolicyNt = 2;     // non-temporal (streamed once)
 
 // Called by all threads of a workgroup after each stored its share of the
 // split's TO partial sums with store_coherent() into blk = the tile's block
@@ -354,8 +409,6 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
     const int R = rps * U;                           // rows per stage
 
     const size_t vrow = static_cast<size_t>(a.Hkv) * a.D * ES;   // bytes from row c to c+1
-    const uint8_t* vbase = a.V + (static_cast<size_t>(T.b) * a.C * a.Hkv + T.kv + kvl) * a.D * ES
-                               + static_cast<size_t>(lane_d) * VB;
 
     float acc[GT][E];
 #pragma unroll
@@ -364,6 +417,8 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
         for (int e = 0; e < E; ++e) acc[g][e] = 0.0f;
 
 #if GQA_AV_VALU_STAGE_WEIGHTS
+    const uint8_t* vbase = a.V + (static_cast<size_t>(T.b) * a.C * a.Hkv + T.kv + kvl) * a.D * ES
+                               + static_cast<size_t>(lane_d) * VB;
     const int q_lo = T.q_first;                      // accumulator g is head q_lo + g (tiles of one KV head)
     auto lane_q_lo = [&](int) { return q_lo; };
     const float* abase = a.attn + static_cast<size_t>(T.b) * a.C * a.Hq + T.q_first;
@@ -480,42 +535,58 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
     // With ht > 1 every lane uses the window of its own KV head kv + kvl.
     auto lane_q_lo = [&](int kl) { return min(T.q_first + kl * a.G, a.Hq - GT); };
     const int q_lo = lane_q_lo(kvl);
-    const float* wbase = a.attn + static_cast<size_t>(T.b) * a.C * a.Hq + q_lo;
-    if (active) {
-        int64_t c0 = cb;
-        for (; c0 + R <= ce; c0 += R) {
-            Raw<VB> raw[U];
-            float w[U][GT];
+    // V and attn are read through buffer resources that end with the split's
+    // last row: rows at or past ce read as zero (and add nothing), so every
+    // step is a full one, and a row's address is a per-lane constant plus a
+    // workgroup-uniform offset held in a scalar register. The plan keeps a
+    // split's span under 1 GB so 32-bit offsets suffice.
+    const int nrows = static_cast<int>(uniform64(ce - cb));
+    const int vrow32 = static_cast<int>(vrow);
+    const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.V) + ((static_cast<size_t>(T.b) * a.C + cb) * a.Hkv + T.kv) * a.D * ES, 0,
+        nrows > 0 ? (nrows - 1) * vrow32 + a.ht * a.D * ES : 0, kRawBufferFlags);
+    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(a.attn) + (static_cast<size_t>(T.b) * a.C + cb) * a.Hq, 0, nrows * a.Hq * 4,
+        kRawBufferFlags);
+    const int voff = r * vrow32 + (kvl * a.D * ES + lane_d * VB);
+    const int woff = (r * a.Hq + q_lo) * 4;
+    const int nsteps = (nrows + R - 1) / R;
+    struct Buf {
+        Raw<VB> v[U];
+        float w[U][GT];
+    };
+    auto load = [&](Buf& bf, int st) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int64_t c = c0 + r + u * rps;
-                raw[u] = load_raw<VB>(vbase + static_cast<size_t>(c) * vrow);
-                const float* wr = wbase + c * a.Hq;
-#pragma unroll
-                for (int g = 0; g < GT; ++g) w[u][g] = wr[g];
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float f[E];
-                widen<DT, VB>(raw[u], f);
-#pragma unroll
-                for (int g = 0; g < GT; ++g)
-#pragma unroll
-                    for (int e = 0; e < E; ++e) acc[g][e] = __builtin_fmaf(w[u][g], f[e], acc[g][e]);
-            }
+        for (int u = 0; u < U; ++u) {
+            const int row = st * R + u * rps;        // of this step's slot 0; the lane adds r
+            bf.v[u] = load_raw_buf<VB>(vres, voff, row * vrow32);
+            load_floats<GT>(wres, woff, row * a.Hq * 4, bf.w[u]);
         }
-        for (int64_t c = c0 + r; c < ce; c += rps) {
-            const Raw<VB> raw = load_raw<VB>(vbase + static_cast<size_t>(c) * vrow);
-            const float* wr = wbase + c * a.Hq;
+    };
+    auto compute = [&](const Buf& bf) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
             float f[E];
-            widen<DT, VB>(raw, f);
+            widen<DT, VB>(bf.v[u], f);
 #pragma unroll
-            for (int g = 0; g < GT; ++g) {
-                const float wg = wr[g];
+            for (int g = 0; g < GT; ++g)
 #pragma unroll
-                for (int e = 0; e < E; ++e) acc[g][e] = __builtin_fmaf(wg, f[e], acc[g][e]);
-            }
+                for (int e = 0; e < E; ++e) acc[g][e] = __builtin_fmaf(bf.w[u][g], f[e], acc[g][e]);
         }
+    };
+    if (active) {
+        // Two buffers in flight; the reload of bA is unconditional (a step
+        // past ce reads zeros and is never computed).
+        Buf bA, bB;
+        int st = 0;
+        if (nsteps > 0) load(bA, 0);
+        for (; st + 1 < nsteps; st += 2) {
+            load(bB, st + 1);
+            compute(bA);
+            load(bA, st + 2);
+            compute(bB);
+        }
+        if (st < nsteps) compute(bA);
     }
 #endif
     __syncthreads();                                  // LDS is reused below
@@ -866,16 +937,10 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
                 for (int p = 0; p < 4; ++p) {
                     uint32_t th[2], tm[2], tl[2];
 #pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const float w = bf.w[u][s][2 * p + e];
-                        th[e] = __float_as_uint(w) & 0xffff0000u;
-                        const float r1 = w - __uint_as_float(th[e]);
-                        tm[e] = __float_as_uint(r1) & 0xffff0000u;
-                        tl[e] = __float_as_uint(r1 - __uint_as_float(tm[e]));
-                    }
+                    for (int e = 0; e < 2; ++e) split_bf16x3(bf.w[u][s][2 * p + e], th[e], tm[e], tl[e]);
                     aw[0][s][p] = (th[0] >> 16) | th[1];
                     aw[1][s][p] = (tm[0] >> 16) | tm[1];
-                    aw[2][s][p] = (tl[0] >> 16) | (tl[1] & 0xffff0000u);
+                    aw[2][s][p] = (tl[0] >> 16) | tl[1];
                 }
             }
             // B operands of all column tiles, then the MFMAs with the tiles

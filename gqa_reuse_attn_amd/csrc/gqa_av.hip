@@ -473,12 +473,13 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
             rows_per_split = ceil_div(ceil_div(C, nsplit), rows_per_step) * rows_per_step;
         }
         nsplit = ceil_div(C, rows_per_split);
-        if (engine == GQA_AV_ENGINE_MFMA_BF16) {
-            // The bf16 matrix engine addresses one split of V and attn through
-            // buffer resources with 32-bit offsets (the last step's reads run up
-            // to two steps of 128 rows past the split): keep a split under 1 GB.
-            const int64_t row_bytes = std::max<int64_t>(Hkv * D * 2, Hq * 4);
-            const int64_t max_rows = (int64_t{1} << 30) / row_bytes - 512;
+        if (engine != GQA_AV_ENGINE_MFMA) {
+            // The VALU and bf16 matrix engines address one split of V and attn
+            // through buffer resources with 32-bit offsets (the pipeline's last
+            // reads run up to two steps past the split): keep a split under 1 GB.
+            const int64_t row_bytes = std::max<int64_t>(Hkv * D * es, Hq * 4);
+            const int64_t max_rows = (int64_t{1} << 30) / row_bytes - 2 * rows_per_step;
+            if (max_rows < 1) return fail(GQA_AV_ERR_UNSUPPORTED, "one context row of V or attn exceeds 1 GB");
             if (rows_per_split > max_rows) {
                 rows_per_split = max_rows;
                 nsplit = ceil_div(C, rows_per_split);
@@ -760,3 +761,6 @@ int gqa_av_release(void) {
 }
 
 }  // extern "C"
+
+// The decode score step shares this library's error, size and device helpers.
+#include "qk_host.hpp"

@@ -1,0 +1,171 @@
+// Host side of the decode score step (include/gqa_qk.h): planning, checks and
+// launches. Included at the end of gqa_av.hip, whose error, size and device
+// helpers it shares.
+#pragma once
+
+#include "gqa_qk.h"
+#include "qk_kernels.hpp"
+
+namespace {
+
+using gqa_av::QkArgs;
+
+constexpr int64_t kQkRowsQuantum = 64;        // 4 waves x 16 rows
+constexpr int64_t kQkTargetWgPerCu = 2;
+
+int qk_plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int k_dtype, int mode,
+                 int64_t rows_hint, int cus, gqa_qk_plan* plan) {
+    int rc = check_sizes(B, C, Hq, Hkv, D, k_dtype);
+    if (rc != GQA_AV_OK) return rc;
+    const int resolved = gqa_av_resolve_mode(Hq, Hkv, mode);
+    if (resolved < 0) return -resolved;
+    if (!plan) return fail(GQA_AV_ERR_INVALID_ARG, "plan is NULL");
+    if (D % 32 != 0 || D > 256)
+        return fail(GQA_AV_ERR_UNSUPPORTED, "score step: D=%lld must be a multiple of 32 and at most 256", (long long)D);
+    const int es = elem_bytes(k_dtype);
+    const int64_t G = Hq / Hkv;
+    const int64_t krow = Hkv * D * es;
+    if (krow > (int64_t{1} << 20)) return fail(GQA_AV_ERR_UNSUPPORTED, "score step: a row of K exceeds 1 MB");
+
+    int hpt, nsg;
+    if (resolved == GQA_AV_PER_HEAD) {
+        hpt = 1;
+        nsg = 1;
+    } else {
+        // 32-head tiles for larger groups while the q operand stays small.
+        hpt = (G > 16 && D <= 128) ? 32 : 16;
+        nsg = static_cast<int>(ceil_div(G, hpt));
+    }
+    const int64_t minor = resolved == GQA_AV_PER_HEAD ? G : nsg;
+    const int64_t tiles = B * Hkv * minor;
+
+    // Context rows per workgroup: enough workgroups for about two per CU, in
+    // whole 64-row steps; 32-bit K offsets for the chunk and its overrun.
+    int64_t rows = rows_hint;
+    if (rows <= 0) {
+        const int64_t target = kQkTargetWgPerCu * (cus > 0 ? cus : kDefaultCUs);
+        const int64_t nchunk = tiles > 0 ? std::max<int64_t>(1, ceil_div(target, tiles)) : 1;
+        rows = std::max<int64_t>(1, ceil_div(C, nchunk));
+    }
+    rows = ceil_div(rows, kQkRowsQuantum) * kQkRowsQuantum;
+    const int64_t max_rows = ((int64_t{1} << 30) / krow - 2 * kQkRowsQuantum) / kQkRowsQuantum * kQkRowsQuantum;
+    if (max_rows < kQkRowsQuantum) return fail(GQA_AV_ERR_UNSUPPORTED, "score step: rows of K too large");
+    if (rows > max_rows) rows = max_rows;
+    if (rows > INT32_MAX) rows = max_rows;
+    const int64_t nchunk = C > 0 ? ceil_div(C, rows) : 0;
+    const int64_t grid = tiles * nchunk;
+    if (grid > INT32_MAX || nchunk > INT32_MAX) return fail(GQA_AV_ERR_UNSUPPORTED, "score step: grid too large");
+
+    std::memset(plan, 0, sizeof *plan);
+    plan->mode = resolved;
+    plan->engine = k_dtype == GQA_AV_BF16 ? GQA_AV_ENGINE_MFMA_BF16 : GQA_AV_ENGINE_MFMA;
+    plan->heads_per_tile = hpt;
+    plan->subgroups = nsg;
+    plan->rows_per_block = rows;
+    plan->grid = grid;
+    plan->k_bytes_read = B * C * Hkv * D * es * (resolved == GQA_AV_PER_HEAD ? G : nsg);
+    return GQA_AV_OK;
+}
+
+template <int KDT, int NBLK>
+hipError_t launch_qk_nset(int nset, const QkArgs& a, hipStream_t s) {
+    if (nset == 1) {
+        hipLaunchKernelGGL((gqa_av::qk_scores<KDT, NBLK, 1>), dim3(a.nblocks), dim3(gqa_av::kThreads), 0, s, a);
+    } else if constexpr (NBLK <= 4) {
+        hipLaunchKernelGGL((gqa_av::qk_scores<KDT, NBLK, 2>), dim3(a.nblocks), dim3(gqa_av::kThreads), 0, s, a);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int KDT>
+hipError_t launch_qk_nblk(int64_t D, int nset, const QkArgs& a, hipStream_t s) {
+    switch (D / 32) {
+    case 1: return launch_qk_nset<KDT, 1>(nset, a, s);
+    case 2: return launch_qk_nset<KDT, 2>(nset, a, s);
+    case 3: return launch_qk_nset<KDT, 3>(nset, a, s);
+    case 4: return launch_qk_nset<KDT, 4>(nset, a, s);
+    case 5: return launch_qk_nset<KDT, 5>(nset, a, s);
+    case 6: return launch_qk_nset<KDT, 6>(nset, a, s);
+    case 7: return launch_qk_nset<KDT, 7>(nset, a, s);
+    case 8: return launch_qk_nset<KDT, 8>(nset, a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+int qk_run(const float* q, const void* K, float* scores, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
+           int64_t D, int k_dtype, float scale, const gqa_qk_plan* plan, void* stream) {
+    if (!plan) return fail(GQA_AV_ERR_INVALID_ARG, "plan is NULL");
+    gqa_qk_plan check;
+    int rc = qk_plan_impl(B, C, Hq, Hkv, D, k_dtype, plan->mode, plan->rows_per_block, kDefaultCUs, &check);
+    if (rc != GQA_AV_OK) return rc;
+    if (check.mode != plan->mode || check.engine != plan->engine || check.heads_per_tile != plan->heads_per_tile ||
+        check.subgroups != plan->subgroups || check.rows_per_block != plan->rows_per_block ||
+        check.grid != plan->grid || check.k_bytes_read != plan->k_bytes_read)
+        return fail(GQA_AV_ERR_INVALID_ARG, "score plan does not belong to this problem");
+    if (B == 0 || C == 0) return GQA_AV_OK;
+    if (!q || !K || !scores) return fail(GQA_AV_ERR_INVALID_ARG, "q, K and scores must not be NULL");
+    if ((reinterpret_cast<uintptr_t>(q) & 3u) || (reinterpret_cast<uintptr_t>(scores) & 3u))
+        return fail(GQA_AV_ERR_INVALID_ARG, "q and scores must be 4-byte aligned");
+    if (reinterpret_cast<uintptr_t>(K) & 15u) return fail(GQA_AV_ERR_UNSUPPORTED, "K must be 16-byte aligned");
+
+    QkArgs a;
+    a.q = q;
+    a.K = static_cast<const uint8_t*>(K);
+    a.scores = scores;
+    a.scale = scale;
+    a.C = C;
+    a.rows_per_block = static_cast<int32_t>(plan->rows_per_block);
+    a.nchunk = static_cast<int32_t>(ceil_div(C, plan->rows_per_block));
+    a.B = static_cast<int32_t>(B);
+    a.Hq = static_cast<int32_t>(Hq);
+    a.Hkv = static_cast<int32_t>(Hkv);
+    a.G = static_cast<int32_t>(Hq / Hkv);
+    a.per_head = plan->mode == GQA_AV_PER_HEAD;
+    a.nsg = plan->subgroups;
+    a.nblocks = static_cast<uint32_t>(plan->grid);
+    const int nset = plan->mode == GQA_AV_PER_HEAD ? 1 : plan->heads_per_tile / 16;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    switch (k_dtype) {
+    case GQA_AV_F32: e = launch_qk_nblk<gqa_av::kF32>(D, nset, a, s); break;
+    case GQA_AV_F16: e = launch_qk_nblk<gqa_av::kF16>(D, nset, a, s); break;
+    default: e = launch_qk_nblk<gqa_av::kBF16>(D, nset, a, s); break;
+    }
+    if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "score launch: %s", hipGetErrorString(e));
+    return GQA_AV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_qk_make_plan(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int k_dtype, int mode,
+                     int64_t rows_per_block, int cu_count, gqa_qk_plan* plan) {
+    return qk_plan_impl(B, C, Hq, Hkv, D, k_dtype, mode, rows_per_block, cu_count > 0 ? cu_count : kDefaultCUs,
+                        plan);
+}
+
+int gqa_qk_decode_plan(const float* q, const void* K, float* scores, int64_t B, int64_t C, int64_t Hq,
+                       int64_t Hkv, int64_t D, int k_dtype, float scale, const gqa_qk_plan* plan, void* stream) {
+    return qk_run(q, K, scores, B, C, Hq, Hkv, D, k_dtype, scale, plan, stream);
+}
+
+int gqa_qk_decode(const float* q, const void* K, float* scores, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
+                  int64_t D, int k_dtype, float scale, int mode, void* stream) {
+    int rc = check_sizes(B, C, Hq, Hkv, D, k_dtype);
+    if (rc != GQA_AV_OK) return rc;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    int cus = kDefaultCUs;
+    rc = device_cus(dev, &cus);
+    if (rc != GQA_AV_OK) return rc;
+    gqa_qk_plan plan;
+    rc = qk_plan_impl(B, C, Hq, Hkv, D, k_dtype, mode, 0, cus, &plan);
+    if (rc != GQA_AV_OK) return rc;
+    return qk_run(q, K, scores, B, C, Hq, Hkv, D, k_dtype, scale, &plan, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,196 @@
+// Device code of the GQA decode score step on gfx950 (MI355X).
+//
+//   scores[b, c, q_h] = scale * sum_d q[b, q_h, d] * K[b, c, kv_h, d],  kv_h = q_h / G
+//
+// It is the step before the attention-times-V product of ExecuTorch PR #21063,
+// "...GEMV" (that page covers the product only): its output, after a softmax
+// over c, is that product's attn input and has the same [B][C][Hq] layout. The
+// page's idea carries over unchanged -- the G query heads of a group share one
+// K row, so a workgroup per KV head reads each K row once for all G of them.
+//
+// Every score depends on a single K row, so the context needs no split and no
+// combine: a workgroup owns a tile (b, kv_h, head set) and a block of context
+// rows. The contraction over d is a skinny matrix product, done on the matrix
+// cores with the K rows as the A operand (16 rows x 32 d), which is K's own
+// row-major layout, and the query heads as the B operand (32 d x 16 heads):
+//  * bf16 K: v_mfma_f32_16x16x32_bf16, with each fp32 q value split once per
+//    workgroup into three bf16 terms (split_bf16x3, exact), so every product is
+//    exact and only the fp32 sums round;
+//  * fp16 / fp32 K: K widened exactly to fp32 and v_mfma_f32_16x16x4_f32.
+// Lane 16 g + m of a wave loads row m's d-range [32 blk + 8 g, 32 blk + 8 g + 8)
+// for each 32-wide block blk of D (one 16-byte load per block, two for fp32),
+// and holds head m's q values for the same d-range. The result of a 16-row
+// block comes back as lane 16 g + n holding rows 4 g + i, head n.
+#pragma once
+
+#include "av_kernels.hpp"
+
+namespace gqa_av {
+
+struct QkArgs {
+    const float* q;          // [B][Hq][D]
+    const uint8_t* K;        // [B][C][Hkv][D] of KDT
+    float* scores;           // [B][C][Hq]
+    float scale;
+    int64_t C;
+    int32_t rows_per_block;  // context rows per workgroup, a multiple of 64
+    int32_t nchunk;          // ceil(C / rows_per_block)
+    int32_t B, Hq, Hkv, G;
+    int32_t per_head;        // 0: tiles of up to 16 * NSET heads of one group; 1: one head per tile
+    int32_t nsg;             // head sub-groups per KV head (reuse)
+    uint32_t nblocks;
+};
+
+// KDT: element type of K; NBLK = D / 32; NSET sets of 16 heads per tile.
+template <int KDT, int NBLK, int NSET>
+__global__ __launch_bounds__(kThreads) void qk_scores(QkArgs a) {
+    constexpr int ES = esize<KDT>();
+    constexpr int D = 32 * NBLK;
+    constexpr int PIECES = KDT == kF32 ? 2 : 1;      // 16-byte loads per lane and block of 32 d
+    constexpr bool BF16 = KDT == kBF16;
+
+    // Logical tile order, fastest first: head sub-group (or the head's place in
+    // its group for the per-head baseline), KV head, context chunk, batch. The
+    // KV heads of one (b, chunk) then run on one XCD: they share the lines of
+    // each score row they write.
+    uint32_t t = xcd_remap(blockIdx.x, a.nblocks);
+    const int nminor = a.per_head ? a.G : a.nsg;
+    const int minor = t % nminor; t /= nminor;
+    const int kv = t % a.Hkv; t /= a.Hkv;
+    const int chunk = t % a.nchunk; t /= a.nchunk;
+    const int b = static_cast<int>(t);
+    const int q_first = a.per_head ? kv * a.G + minor : kv * a.G + minor * 16 * NSET;
+    const int nq = a.per_head ? 1 : min(16 * NSET, a.G - minor * 16 * NSET);
+    const int64_t r0 = uniform64(static_cast<int64_t>(chunk) * a.rows_per_block);
+    const int nrows = static_cast<int>(uniform64(min(static_cast<int64_t>(a.rows_per_block), a.C - r0)));
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int m = lane & 15;                         // row (A) / head (B, result) inside a tile
+    const int g = lane >> 4;                         // d-group of 8 inside a block of 32
+
+    // K through a buffer resource ending at the chunk's last row: rows past it
+    // read as zero (their scores are never stored).
+    const int krow = a.Hkv * D * ES;
+    const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.K) + ((static_cast<size_t>(b) * a.C + r0) * a.Hkv + kv) * D * ES, 0,
+        (nrows - 1) * krow + D * ES, kRawBufferFlags);
+    const int klane = m * krow + 8 * g * ES;
+
+    // q operand, once per workgroup. Heads past nq read the tile's last head (a
+    // valid address); their result columns are never stored.
+    constexpr int QW = BF16 ? 3 : 1;                 // bf16: three exact terms
+    u32x4 qb[BF16 ? 3 : 1][NSET][NBLK];
+    float qf[BF16 ? 1 : NSET][BF16 ? 1 : NBLK][8];
+#pragma unroll
+    for (int s = 0; s < NSET; ++s) {
+        const float* qrow = a.q + (static_cast<size_t>(b) * a.Hq + q_first + min(m + 16 * s, nq - 1)) * D + 8 * g;
+#pragma unroll
+        for (int blk = 0; blk < NBLK; ++blk) {
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = qrow[32 * blk + j];
+            if constexpr (BF16) {
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    uint32_t th[2], tm[2], tl[2];
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) split_bf16x3(v[2 * p + e], th[e], tm[e], tl[e]);
+                    qb[0][s][blk][p] = (th[0] >> 16) | th[1];
+                    qb[1][s][blk][p] = (tm[0] >> 16) | tm[1];
+                    qb[2][s][blk][p] = (tl[0] >> 16) | tl[1];
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) qf[s][blk][j] = v[j];
+            }
+        }
+    }
+    (void)QW;
+
+    struct Buf {
+        u32x4 raw[NBLK][PIECES];
+    };
+    // Row block j (16 rows) of the chunk: wave w takes j = w, w + kWaves, ...
+    auto load = [&](Buf& bf, int j) {
+#pragma unroll
+        for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+            for (int p = 0; p < PIECES; ++p)
+                bf.raw[blk][p] = __builtin_amdgcn_raw_buffer_load_b128(
+                    kres, klane + (32 * blk * ES + 16 * p), 16 * j * krow, kCachePolicyNt);
+    };
+    auto compute_store = [&](const Buf& bf, int j) {
+        // Independent accumulators keep consecutive MFMAs off one dependency chain.
+        constexpr int NACC = BF16 ? 3 : 4;
+        f32x4 acc[NACC][NSET];
+#pragma unroll
+        for (int k = 0; k < NACC; ++k)
+#pragma unroll
+            for (int s = 0; s < NSET; ++s) acc[k][s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int blk = 0; blk < NBLK; ++blk) {
+            if constexpr (BF16) {
+                const bf16x8 ka = __builtin_bit_cast(bf16x8, bf.raw[blk][0]);
+#pragma unroll
+                for (int k = 0; k < 3; ++k)
+#pragma unroll
+                    for (int s = 0; s < NSET; ++s)
+                        acc[k][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            ka, __builtin_bit_cast(bf16x8, qb[k][s][blk]), acc[k][s], 0, 0, 0);
+            } else {
+                float kf[8];
+                if constexpr (KDT == kF32) {
+#pragma unroll
+                    for (int p = 0; p < 2; ++p)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) kf[4 * p + e] = __uint_as_float(bf.raw[blk][p][e]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        kf[2 * e] = f16_bits_to_f32(bf.raw[blk][0][e] & 0xffffu);
+                        kf[2 * e + 1] = f16_bits_to_f32(bf.raw[blk][0][e] >> 16);
+                    }
+                }
+#pragma unroll
+                for (int st = 0; st < 8; ++st)
+#pragma unroll
+                    for (int s = 0; s < NSET; ++s)
+                        acc[st & 3][s] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[st], qf[s][blk][st], acc[st & 3][s],
+                                                                            0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < NSET; ++s) {
+            f32x4 sum = acc[0][s];
+#pragma unroll
+            for (int k = 1; k < NACC; ++k) sum += acc[k][s];
+            const int h = m + 16 * s;
+            if (h < nq) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * j + 4 * g + i;
+                    if (row < nrows)
+                        a.scores[(static_cast<size_t>(b) * a.C + r0 + row) * a.Hq + q_first + h] = sum[i] * a.scale;
+                }
+            }
+        }
+    };
+
+    // Two buffers in flight; the reload is unconditional (blocks past the
+    // chunk read zeros and store nothing).
+    const int nrb = (nrows + 15) / 16;
+    const int nsteps = (nrb + kWaves - 1) / kWaves;
+    Buf bA, bB;
+    int st = 0;
+    if (nsteps > 0) load(bA, wave);
+    for (; st + 1 < nsteps; st += 2) {
+        load(bB, (st + 1) * kWaves + wave);
+        compute_store(bA, st * kWaves + wave);
+        load(bA, (st + 2) * kWaves + wave);
+        compute_store(bB, (st + 1) * kWaves + wave);
+    }
+    if (st < nsteps) compute_store(bA, st * kWaves + wave);
+}
+
+}  // namespace gqa_av

@@ -1,0 +1,82 @@
+/*
+ * gqa_qk.h -- C ABI of the decode score step in libgqa_av.so (MI355X, gfx950).
+ *
+ * The operation: in grouped-query attention the Hq = G * Hkv query heads come
+ * in groups of G that share one KV head (ExecuTorch PR #21063, "...GEMV",
+ * introduction), and the decode step's scores are
+ *
+ *     scores[b, c, q_h] = scale * sum_{d < D} q[b, q_h, d] * K[b, c, kv_h, d]
+ *     kv_h              = q_h / G            (integer division)
+ *
+ * for every sequence b < B, context position c < C and query head q_h < Hq.
+ * That page covers the attention-times-V product that follows (gqa_av.h); this
+ * step is not on it. It is the standard first half of decode attention with the
+ * same head grouping: after a softmax over c, `scores` is the `attn` input of
+ * gqa_av_decode, in the same layout. The page's reuse idea carries over: in
+ * GQA_AV_REUSE mode each K row is read once for all G query heads of its
+ * group; GQA_AV_PER_HEAD reads it once per query head (the measured baseline).
+ * Mode values and their resolution are those of gqa_av_resolve_mode.
+ *
+ * Memory layout: dense, row-major, no padding or strides.
+ *   q       [B][Hq][D]      float32
+ *   K       [B][C][Hkv][D]  float32, float16 or bfloat16 (k_dtype, a gqa_av_dtype)
+ *   scores  [B][C][Hq]      float32, fully overwritten
+ * All three are DEVICE pointers on the current HIP device, owned by the caller.
+ * Accumulation is in float32: with bf16 K every product q * K is exact (q is
+ * split exactly into three bf16 terms) and only the sums round; with fp16 and
+ * fp32 K the products are fp32 fused multiply-adds. The scale multiplies the
+ * sum once at the end.
+ *
+ * Requirements of this build: D a multiple of 32 and at most 256, K 16-byte
+ * aligned, q and scores 4-byte aligned; otherwise GQA_AV_ERR_UNSUPPORTED (or
+ * GQA_AV_ERR_INVALID_ARG for bad sizes, as in gqa_av.h). No workspace: the
+ * context is never split.
+ *
+ * Asynchrony, errors and threading are as in gqa_av.h: calls enqueue on
+ * `stream` and return a gqa_av_status; gqa_av_last_error() gives the detail.
+ */
+#ifndef GQA_QK_H
+#define GQA_QK_H
+
+#include <stdint.h>
+
+#include "gqa_av.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Launch plan of the score step. */
+typedef struct gqa_qk_plan {
+    int32_t mode;            /* resolved: GQA_AV_PER_HEAD or GQA_AV_REUSE */
+    int32_t engine;          /* GQA_AV_ENGINE_MFMA_BF16 (bf16 K) or GQA_AV_ENGINE_MFMA (fp16 / fp32 K) */
+    int32_t heads_per_tile;  /* query heads one workgroup computes: 16 or 32 (reuse), 1 (per-head) */
+    int32_t subgroups;       /* workgroups along the heads of one KV head (reuse: ceil(G / heads_per_tile)) */
+    int64_t rows_per_block;  /* context rows per workgroup (a multiple of 64) */
+    int64_t grid;            /* workgroups launched */
+    int64_t k_bytes_read;    /* K bytes the plan reads from memory (G x more for per-head) */
+    int32_t reserved[4];
+} gqa_qk_plan;
+
+/* Build the plan. Host-only: needs no GPU. rows_per_block <= 0 and
+ * cu_count <= 0 mean automatic (cu_count: 256). Returns a gqa_av_status. */
+int gqa_qk_make_plan(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int k_dtype, int mode,
+                     int64_t rows_per_block, int cu_count, gqa_qk_plan *plan);
+
+/* scores = scale * q . K as defined above, with an automatic plan for the
+ * current device. B == 0 or C == 0 does nothing (scores is empty). */
+int gqa_qk_decode(const float *q, const void *K, float *scores,
+                  int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D,
+                  int k_dtype, float scale, int mode, void *stream);
+
+/* Same, with an explicit plan from gqa_qk_make_plan for the same problem;
+ * GQA_AV_ERR_INVALID_ARG if the plan does not match it. */
+int gqa_qk_decode_plan(const float *q, const void *K, float *scores,
+                       int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D,
+                       int k_dtype, float scale, const gqa_qk_plan *plan, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_QK_H */

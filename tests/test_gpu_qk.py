@@ -1,0 +1,163 @@
+"""GPU parity of the decode score step (scores = scale * q . K, K shared by each
+head group) through the C ABI, against the fp64 CPU oracle.
+
+Gate: the acceptance gate of tests/parity.py (max-abs for fp32 K, relative L2
+for bf16/fp16 K) with the fp32-accumulation bound over the D terms of each dot
+product, plus an elementwise bound on small shapes: |err| <= 2 D 2^-24 scale
+sum_d |q K|. All tests need an MI355X and are marked ``gpu``.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import gqa_reuse_attn_amd as ga
+from oracle.brute import abs_sum_qk
+from tests.parity import assert_parity
+from workloads import WORKLOADS, make_qk_random
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+U32 = 2.0 ** -24
+
+
+def _say(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ga.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _run(q, K, scale, mode="auto", plan=None):
+    s = ga.gqa_qk_decode(q.to(DEV), K.to(DEV), scale=scale, mode=mode, plan=plan)
+    torch.cuda.synchronize()
+    return s.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("wname", list(WORKLOADS))
+@pytest.mark.parametrize("mode", ["auto", "per_head"])
+def test_qk_workload_shapes(wname, mode, oracle_lib):
+    """The six decode shapes (K of the workload's V dtype), scale 1/sqrt(D)."""
+    w = WORKLOADS[wname]
+    if w.B * w.C * w.Hkv * w.D > 2 ** 28:
+        w = w.replace(B=8)                     # the large batch: 8 sequences keep the oracle in seconds
+    _say(f"[qk] {w.name} B={w.B} mode={mode}")
+    q, K = make_qk_random(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, seed=3)
+    scale = w.D ** -0.5
+    ref = oracle_lib.qk(q, K, w.v_dtype, scale)
+    out = _run(q, K, scale, mode)
+    assert_parity(out, ref, w.v_dtype, w.D, f"qk {w.name} {mode}")
+
+
+def _qk_cases():
+    cases = []
+    k = 0
+    for G in (1, 2, 3, 4, 5, 8, 16, 17, 32):
+        for D in (32, 64, 96, 128, 160, 256):
+            for C in (1, 63, 65, 300):
+                if (G + D + C) % 3:
+                    continue                    # a spread subset of the grid
+                dt = ("bf16", "f16", "f32")[k % 3]
+                Hkv = 1 + k % 3
+                rows = (0, 64, 128)[k % 3]
+                cases.append((1 + k % 2, C, G * Hkv, Hkv, D, dt, rows))
+                k += 1
+    return cases
+
+
+@pytest.mark.parametrize("B,C,Hq,Hkv,D,dt,rows", _qk_cases())
+def test_qk_sweep(B, C, Hq, Hkv, D, dt, rows, oracle_lib):
+    """Small shapes: G 1..32, D 32..256, ragged C, all dtypes, forced row blocks."""
+    q, K = make_qk_random(B, C, Hq, Hkv, D, dt, seed=B * 1000 + C + D)
+    scale = 0.375
+    ref = oracle_lib.qk(q, K, dt, scale)
+    bound = 2 * D * U32 * scale * abs_sum_qk(q, K) + 1e-30
+    modes = ("auto", "per_head") if Hq // Hkv >= 2 else ("auto",)
+    for mode in modes:
+        plan = ga.qk_make_plan(B, C, Hq, Hkv, D, dt, mode, rows_per_block=rows)
+        out = _run(q, K, scale, plan=plan)
+        assert_parity(out, ref, dt, D, f"qk {(B, C, Hq, Hkv, D, dt, mode)} plan={plan.as_dict()}")
+        assert (np.abs(out - ref) <= bound).all(), f"qk elementwise bound {(B, C, Hq, Hkv, D, dt, mode)}"
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+def test_qk_single_term_is_exact(dt):
+    """One nonzero q element per head and K a power of two: each score is
+    scale * q * K exactly (bf16 K: the three-term split of q loses no bit)."""
+    B, C, Hq, Hkv, D = 2, 200, 32, 2, 128
+    G = Hq // Hkv
+    gen = torch.Generator().manual_seed(5)
+    q = torch.zeros(B, Hq, D)
+    pick = {}
+    for b in range(B):
+        for h in range(Hq):
+            j = (7 * b + 11 * h + 3) % D
+            val = (torch.rand(1, generator=gen).item() + 1.0) * 2.0 ** int(torch.randint(-30, 10, (1,), generator=gen))
+            q[b, h, j] = val
+            pick[b, h] = j
+    kt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dt]
+    K = torch.pow(2.0, torch.randint(-10, 10, (B, C, Hkv, D), generator=gen).float()).to(kt)
+    out = _run(q, K, 0.5)
+    Kd = K.double().numpy()
+    for (b, h), j in pick.items():
+        want = (0.5 * q[b, h, j].double().item() * Kd[b, :, h // G, j]).astype(np.float32)
+        assert np.array_equal(out[b, :, h].astype(np.float32), want), (dt, b, h)
+
+
+def test_qk_deterministic():
+    q, K = make_qk_random(4, 5000, 16, 8, 128, "bf16", seed=9)
+    a = [ga.gqa_qk_decode(q.to(DEV), K.to(DEV), scale=0.1).cpu() for _ in range(3)]
+    torch.cuda.synchronize()
+    assert all(torch.equal(a[0], x) for x in a[1:])
+
+
+def test_qk_edges(oracle_lib):
+    # C = 0 and B = 0: nothing to do
+    s = ga.gqa_qk_decode(torch.zeros(2, 4, 64, device=DEV), torch.zeros(2, 0, 2, 64, dtype=torch.bfloat16, device=DEV))
+    assert s.shape == (2, 0, 4)
+    s = ga.gqa_qk_decode(torch.zeros(0, 4, 64, device=DEV), torch.zeros(0, 9, 2, 64, dtype=torch.bfloat16, device=DEV))
+    assert s.shape == (0, 9, 4)
+    # D not a multiple of 32 is refused, not run
+    with pytest.raises(ga.GqaAvError) as ei:
+        ga.gqa_qk_decode(torch.zeros(1, 4, 48, device=DEV), torch.zeros(1, 8, 2, 48, dtype=torch.bfloat16, device=DEV))
+    assert ei.value.name == "UNSUPPORTED"
+    # K not 16-byte aligned is refused
+    buf = torch.zeros(1 * 8 * 2 * 64 + 8, dtype=torch.bfloat16, device=DEV)
+    k_off = buf[1:1 + 8 * 2 * 64].view(1, 8, 2, 64)
+    with pytest.raises(ga.GqaAvError) as ei:
+        ga.gqa_qk_decode(torch.zeros(1, 4, 64, device=DEV), k_off)
+    assert ei.value.name == "UNSUPPORTED"
+    # forced reuse with G = 1 is ineligible
+    with pytest.raises(ga.GqaAvError) as ei:
+        ga.gqa_qk_decode(torch.zeros(1, 2, 64, device=DEV), torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16, device=DEV),
+                         mode="reuse")
+    assert ei.value.name == "INELIGIBLE"
+
+
+def test_qk_then_av_matches_attention(oracle_lib):
+    """Scores -> softmax over c -> attention-times-V on the GPU equals the
+    oracles composed the same way (the two steps agree on the attn layout)."""
+    B, C, Hq, Hkv, D = 2, 3000, 16, 4, 128
+    q, K = make_qk_random(B, C, Hq, Hkv, D, "bf16", seed=21)
+    _, V = make_qk_random(B, C, Hq, Hkv, D, "bf16", seed=22)
+    scale = D ** -0.5
+    s = ga.gqa_qk_decode(q.to(DEV), K.to(DEV), scale=scale)
+    attn = torch.softmax(s.double(), dim=1).float().contiguous()
+    out = ga.gqa_av_decode(attn, V.to(DEV))
+    torch.cuda.synchronize()
+    ref_s = oracle_lib.qk(q, K, "bf16", scale)
+    e = np.exp(ref_s - ref_s.max(axis=1, keepdims=True))
+    ref_attn = (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
+    ref = oracle_lib.full(torch.from_numpy(ref_attn), V, "bf16")
+    assert_parity(out.cpu().numpy().astype(np.float64), ref, "bf16", C, "qk -> softmax -> av")

@@ -5,6 +5,7 @@ No kernel is launched here.
 from __future__ import annotations
 
 import ctypes
+import glob
 import os
 import re
 
@@ -18,23 +19,27 @@ HEADER = os.path.join(ROOT, "include", "gqa_av.h")
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gqa_av_\w+)\s*\(", text)))
+    """Every function declared in include/*.h (comments stripped)."""
+    names = set()
+    for h in sorted(glob.glob(os.path.join(os.path.dirname(HEADER), "*.h"))):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(gqa_(?:av|qk)_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
     lib = ga.load()
     names = declared_functions()
-    assert len(names) >= 7, names
+    assert len(names) >= 10, names
+    assert {"gqa_qk_decode", "gqa_qk_decode_plan", "gqa_qk_make_plan"} <= set(names)
     for n in names:
-        assert hasattr(lib, n), f"{n} declared in gqa_av.h but not exported"
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
 
 
 def test_exports_are_c_symbols():
     # extern "C": no mangled gqa_av names in the dynamic symbol table
     out = os.popen(f"nm -D --defined-only {ga.LIB_PATH}").read()
-    exported = set(re.findall(r"\s(gqa_av_\w+)$", out, flags=re.M))
+    exported = set(re.findall(r"\s(gqa_(?:av|qk)_\w+)$", out, flags=re.M))
     assert set(declared_functions()) <= exported
 
 
@@ -333,3 +338,43 @@ def test_bf16_engine_keeps_split_spans_small():
     _check_plan(p, 1, 10_000_000, 16, 1, 128, "bf16", "auto")
     # rows of V beyond 1 MB are not taken by this engine
     assert ga.make_plan(1, 100, 16 * 8192, 8192, 128, "bf16").engine != 3
+
+
+def test_qk_plans():
+    """Score-step planning: engine by K dtype, tiles per head group, row blocks."""
+    p = ga.qk_make_plan(4, 32768, 16, 8, 128, "bf16")
+    assert p.mode == 1 and p.engine == 3 and p.heads_per_tile == 16 and p.subgroups == 1
+    assert p.rows_per_block % 64 == 0 and p.grid == 4 * 8 * -(-32768 // p.rows_per_block)
+    assert p.k_bytes_read == 4 * 32768 * 8 * 128 * 2
+    p = ga.qk_make_plan(4, 32768, 16, 8, 128, "bf16", "per_head")
+    assert p.mode == 0 and p.heads_per_tile == 1 and p.k_bytes_read == 2 * 4 * 32768 * 8 * 128 * 2
+    assert ga.qk_make_plan(8, 16384, 24, 8, 96, "f16").engine == 2
+    assert ga.qk_make_plan(1, 256, 8, 2, 64, "f32").engine == 2
+    p = ga.qk_make_plan(1, 300, 40, 1, 128, "bf16")                 # G = 40: 32-head sets
+    assert p.heads_per_tile == 32 and p.subgroups == 2
+    p = ga.qk_make_plan(1, 300, 40, 1, 256, "bf16")                 # D = 256: 16-head sets
+    assert p.heads_per_tile == 16 and p.subgroups == 3
+    assert ga.qk_make_plan(2, 1000, 8, 2, 64, "bf16", rows_per_block=100).rows_per_block == 128
+    for args in [(1, 10, 8, 2, 48, "bf16"), (1, 10, 8, 2, 288, "bf16")]:
+        with pytest.raises(ga.GqaAvError) as ei:
+            ga.qk_make_plan(*args)
+        assert ei.value.name == "UNSUPPORTED"
+    with pytest.raises(ga.GqaAvError) as ei:
+        ga.qk_make_plan(1, 10, 9, 2, 64, "bf16")
+    assert ei.value.name == "INVALID_ARG"
+    with pytest.raises(ga.GqaAvError) as ei:
+        ga.qk_make_plan(1, 10, 4, 4, 64, "bf16", "reuse")
+    assert ei.value.name == "INELIGIBLE"
+
+
+def test_qk_decode_plan_rejects_before_launch():
+    lib = ga.load()
+    p = ga.qk_make_plan(2, 100, 8, 2, 64, "bf16")
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.gqa_qk_decode_plan(fake, fake, fake, 2, 5000, 8, 2, 64, 2, ctypes.c_float(1.0), ctypes.byref(p), None) == 1
+    assert lib.gqa_qk_decode_plan(None, fake, fake, 2, 100, 8, 2, 64, 2, ctypes.c_float(1.0), ctypes.byref(p), None) == 1
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    assert lib.gqa_qk_decode_plan(fake, odd, fake, 2, 100, 8, 2, 64, 2, ctypes.c_float(1.0), ctypes.byref(p), None) == 3
+    assert lib.gqa_qk_decode_plan(odd, fake, fake, 2, 100, 8, 2, 64, 2, ctypes.c_float(1.0), ctypes.byref(p), None) == 1
+    p0 = ga.qk_make_plan(0, 100, 8, 2, 64, "bf16")
+    assert lib.gqa_qk_decode_plan(None, None, None, 0, 100, 8, 2, 64, 2, ctypes.c_float(1.0), ctypes.byref(p0), None) == 0

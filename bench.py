@@ -40,13 +40,19 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 ROTATE_BYTES = 512 * 2 ** 20   # 2 x the 256 MB Infinity Cache
 DEFAULT_WORKLOAD = "g2-b4-c32768-hq16-hkv8-d128-bf16"
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = [os.path.join(ROOT, "gqa_reuse_attn_amd", "csrc", f) for f in ("av_kernels.hpp", "gqa_av.hip")]
+KERNEL_SOURCES = {
+    "av": [os.path.join(ROOT, "gqa_reuse_attn_amd", "csrc", f) for f in ("av_kernels.hpp", "gqa_av.hip")],
+    "qk": [os.path.join(ROOT, "gqa_reuse_attn_amd", "csrc", f) for f in ("av_kernels.hpp", "qk_kernels.hpp",
+                                                                       "qk_host.hpp")],
+}
+# Profile file prefix and the dominant kernel's name fragment, per operation.
+OPS = {"av": ("pass1", "pass1"), "qk": ("qk", "qk_scores")}
 
 
-def source_hash() -> str:
+def source_hash(op: str = "av") -> str:
     """SHA-256 over the kernel sources: identifies the kernels a profile was taken on."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[op]:
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -55,6 +61,8 @@ def source_hash() -> str:
 def parse():
     p = argparse.ArgumentParser(description=__doc__.splitlines()[1])
     p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--op", default="av", choices=["av", "qk"],
+                   help="av: attention-times-V (the headline); qk: the decode score step before it")
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=-1,
                    help="untimed warmup steps; -1 (default): at least 20 and about 0.25 s of GPU work, "
@@ -88,9 +96,9 @@ def _rows(d: str, suffix: str):
         return list(csv.DictReader(fh))
 
 
-def summarize_trace(d: str, out: str, command: str):
+def summarize_trace(d: str, out: str, command: str, op: str = "av"):
     rows = _rows(d, "kernel_stats.csv")
-    lines = ["# rocprofv3 kernel trace summary", f"command: {command}", f"kernel_sources_sha256: {source_hash()}", "",
+    lines = ["# rocprofv3 kernel trace summary", f"command: {command}", f"kernel_sources_sha256: {source_hash(op)}", "",
              "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
     for r in rows:
         lines.append(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
@@ -107,7 +115,7 @@ def _counter_medians(d: str):
     return {k: statistics.median(v) for k, v in vals.items()}
 
 
-def summarize_pmc(dirs, copy_mib: float, out: str, command: str):
+def summarize_pmc(dirs, copy_mib: float, out: str, command: str, op: str = "av"):
     fetch, write, cfetch, cwrite = (_counter_medians(d) for d in dirs)
     copy_bytes = copy_mib * 2 ** 20
 
@@ -116,7 +124,7 @@ def summarize_pmc(dirs, copy_mib: float, out: str, command: str):
         return copy_bytes / (max(vals) * 1024.0)
     ff, wf = copy_factor(cfetch, "FETCH_SIZE"), copy_factor(cwrite, "WRITE_SIZE")
     lines = ["# rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE summary", f"command: {command}",
-             f"kernel_sources_sha256: {source_hash()}",
+             f"kernel_sources_sha256: {source_hash(op)}",
              f"copy_calibration: {copy_mib:.0f} MiB device-to-device copy (__amd_rocclr_copyBuffer)",
              f"fetch_scale: {ff:.4f}", f"write_scale: {wf:.4f}", "",
              "| kernel | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | scaled HBM bytes/dispatch |",
@@ -128,18 +136,20 @@ def summarize_pmc(dirs, copy_mib: float, out: str, command: str):
         w = write.get((k, "WRITE_SIZE"), 0.0)
         traffic = v * 1024 * ff + w * 1024 * wf
         lines.append(f"| {k[:90]} | {v:.1f} | {w:.1f} | {traffic:.0f} |")
-        if "pass1" in k:
-            extra.append(f"pass1_traffic_bytes: {traffic:.0f}")
+        prefix, fragment = OPS[op]
+        if fragment in k:
+            extra.append(f"{prefix}_traffic_bytes: {traffic:.0f}")
     lines += [""] + extra
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
-def recorded_traffic(workload: str, mode: str):
-    """Pass-1 HBM bytes per launch from the committed PMC summary, if it was
-    taken on the current kernel sources (else None)."""
-    f = os.path.join(PROFILES, f"pass1_{workload}_{mode}_traffic.md")
+def recorded_traffic(workload: str, mode: str, op: str = "av"):
+    """The dominant kernel's HBM bytes per launch from the committed PMC summary,
+    if it was taken on the current kernel sources (else None)."""
+    prefix = OPS[op][0]
+    f = os.path.join(PROFILES, f"{prefix}_{workload}_{mode}_traffic.md")
     if not os.path.exists(f):
         return None
     kv = {}
@@ -147,9 +157,10 @@ def recorded_traffic(workload: str, mode: str):
         if ":" in line and not line.startswith("|"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_sources_sha256") != source_hash() or "pass1_traffic_bytes" not in kv:
+    key = f"{prefix}_traffic_bytes"
+    if kv.get("kernel_sources_sha256") != source_hash(op) or key not in kv:
         return None
-    return float(kv["pass1_traffic_bytes"])
+    return float(kv[key])
 
 
 def copy_calibration(mib: float):
@@ -191,13 +202,105 @@ def cpu_baseline(w, attn, V, budget_s: float):
 
 # ---- benchmark --------------------------------------------------------------------
 
+def _warm(args, calls, nrot):
+    """Untimed warmup: W calls, or (W < 0) at least 20 and about 0.25 s of GPU work."""
+    import torch
+    warmup = args.warmup
+    if warmup < 0:
+        t0 = time.perf_counter()
+        for i in range(20):
+            calls[i % nrot]()
+        torch.cuda.synchronize()
+        per_call = (time.perf_counter() - t0) / 20
+        warmup = 20 + int(0.25 / max(per_call, 1e-6))
+        for i in range(20, warmup):
+            calls[i % nrot]()
+    else:
+        for i in range(warmup):
+            calls[i % nrot]()
+    torch.cuda.synchronize()
+    args.warmup = warmup
+
+
+def _timed(calls, nrot, steps, stream):
+    """ms per call over `steps` back-to-back calls, HIP events on the launch stream."""
+    import torch
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        calls[i % nrot]()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+QK_METRIC = "GQA decode QK scores: µs/call and achieved HBM GB/s (% of MI355X peak)"
+
+
+def bench_qk(args, w, dev, props):
+    """The decode score step on the workload's shape: K (the workload's V dtype)
+    once + q once + scores once per call. One kernel per call, so it is also
+    the roofline kernel."""
+    import torch
+
+    import gqa_reuse_attn_amd as ga
+    from workloads import make_qk_random
+
+    q_h, K_h = make_qk_random(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, seed=0)
+    es = 4 if w.v_dtype == "f32" else 2
+    alg = w.B * w.C * w.Hkv * w.D * es + 4 * w.B * w.Hq * w.D + 4 * w.B * w.C * w.Hq
+    plan = ga.qk_make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, args.mode, cu_count=props.multi_processor_count)
+    nrot = max(1, math.ceil(args.rotate_mb * 2 ** 20 / alg))
+    q0, k0 = q_h.to(dev), K_h.to(dev)
+    calls = []
+    for i in range(nrot):
+        calls.append(ga.bind_qk(q0 if i == 0 else q0.clone(), k0 if i == 0 else k0.clone(), scale=w.D ** -0.5,
+                                plan=plan))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    _warm(args, calls, nrot)
+    ms = _timed(calls, nrot, args.steps, stream)
+    gbs = alg / (ms / 1e3) / 1e9
+    print(f"[bench] qk {ms * 1e3:.2f} us/call, {gbs:.1f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of peak); "
+          f"{nrot} rotation sets, plan {plan.as_dict()}", file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        orc = oracle.get()
+        threads = int(os.environ.get("OMP_NUM_THREADS") or 0) or len(os.sched_getaffinity(0))
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            orc.qk(q_h, K_h, w.v_dtype, w.D ** -0.5, nthreads=threads)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds or reps >= 1000:
+                break
+        cpu = {"value": round(alg / (el / reps) / 1e9, 3), "unit": "GB/s", "us_per_call": round(el / reps * 1e6, 1),
+               "cores": threads, "kind": "oracle",
+               "sample": f"full score step of {w.name}, {reps} calls in {el:.1f} s (fp64 C oracle, OpenMP)"}
+    line = {
+        "metric": QK_METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "us_per_call": round(ms * 1e3, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"qk:{w.name}", "B": w.B, "C": w.C, "Hq": w.Hq, "Hkv": w.Hkv, "G": w.G, "D": w.D,
+                   "k_dtype": w.v_dtype, "mode": args.mode, "algorithmic_bytes": alg, "rotation_sets": nrot,
+                   "kernels_per_call": 1, "plan": plan.as_dict()},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(w.name, args.mode, "qk"),
+                     "kernel": "qk_scores", "us_per_launch": round(ms * 1e3, 3),
+                     "timing": "HIP events around K back-to-back launches on the launch stream"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace, args.out, args.command)
+        summarize_trace(args.summarize_trace, args.out, args.command, args.op)
         return
     if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc, args.copy_bytes, args.out, args.command)
+        summarize_pmc(args.summarize_pmc, args.copy_bytes, args.out, args.command, args.op)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this path has no "
@@ -219,8 +322,11 @@ def main():
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(dev)
-    print(f"[bench] {w.name} mode={args.mode} on {props.name} ({props.multi_processor_count} CUs)",
+    print(f"[bench] {args.op} {w.name} mode={args.mode} on {props.name} ({props.multi_processor_count} CUs)",
           file=sys.stderr, flush=True)
+    if args.op == "qk":
+        bench_qk(args, w, dev, props)
+        return
 
     attn_h, V_h = make_inputs(w, seed=0)
     plan = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, args.mode, nsplit=args.nsplit,
@@ -238,30 +344,10 @@ def main():
     calls = [ga.bind(a, v, o, plan=plan) for a, v, o in sets]
     stream = torch.cuda.current_stream(dev)
 
-    warmup = args.warmup
-    if warmup < 0:
-        t0 = time.perf_counter()
-        for i in range(20):
-            calls[i % nrot]()
-        torch.cuda.synchronize()
-        per_call = (time.perf_counter() - t0) / 20
-        warmup = 20 + int(0.25 / max(per_call, 1e-6))
-        for i in range(20, warmup):
-            calls[i % nrot]()
-    else:
-        for i in range(warmup):
-            calls[i % nrot]()
-    torch.cuda.synchronize()
-    args.warmup = warmup
+    _warm(args, calls, nrot)
 
     # Whole calls: the metric.
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(args.steps):
-        calls[i % nrot]()
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    ms = _timed(calls, nrot, args.steps, stream)
     gbs = w.algorithmic_bytes() / (ms / 1e3) / 1e9
 
     # The dominant kernel alone: K back-to-back pass-1 launches over the same
@@ -285,7 +371,7 @@ def main():
         cpu = cpu_baseline(w, attn_h, V_h, args.cpu_seconds)
 
     split_kernel = plan.nsplit > 1 and plan.combine == 1
-    traffic = recorded_traffic(w.name, args.mode) if (args.nsplit == 0 and args.engine == "auto"
+    traffic = recorded_traffic(w.name, args.mode, "av") if (args.nsplit == 0 and args.engine == "auto"
                                                       and args.combine == "auto" and args.kv_tile == 0) else None
     line = {
         "metric": METRIC,

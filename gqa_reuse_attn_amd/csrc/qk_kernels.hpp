@@ -17,10 +17,16 @@
 //    workgroup into three bf16 terms (split_bf16x3, exact), so every product is
 //    exact and only the fp32 sums round;
 //  * fp16 / fp32 K: K widened exactly to fp32 and v_mfma_f32_16x16x4_f32.
-// Lane 16 g + m of a wave loads row m's d-range [32 blk + 8 g, 32 blk + 8 g + 8)
-// for each 32-wide block blk of D (one 16-byte load per block, two for fp32),
-// and holds head m's q values for the same d-range. The result of a 16-row
-// block comes back as lane 16 g + n holding rows 4 g + i, head n.
+// The A operand wants lane 16 g + m to hold row m's d-range
+// [32 blk + 8 g, 32 blk + 8 g + 8). Loaded that way, one 64-lane load would
+// touch 16 rows at 64 bytes each, a pattern that streams 25 % slower on
+// MI355X than whole rows. So each wave loads its 16-row block as consecutive
+// 16-byte pieces (whole rows, several per load), stores them to a private LDS
+// region with rows padded by 16 bytes (so the 16 rows of an operand read fall
+// in different banks), and reads each lane's operand back with one 16-byte
+// LDS load per block of 32 d (two for fp32). Lane 16 g + n holds head n's q
+// values for the same d-range. The result of a 16-row block comes back as lane
+// 16 g + n holding rows 4 g + i, head n.
 #pragma once
 
 #include "av_kernels.hpp"
@@ -46,8 +52,12 @@ template <int KDT, int NBLK, int NSET>
 __global__ __launch_bounds__(kThreads) void qk_scores(QkArgs a) {
     constexpr int ES = esize<KDT>();
     constexpr int D = 32 * NBLK;
-    constexpr int PIECES = KDT == kF32 ? 2 : 1;      // 16-byte loads per lane and block of 32 d
+    constexpr int PIECES = KDT == kF32 ? 2 : 1;      // 16-byte operand pieces per lane and block of 32 d
     constexpr bool BF16 = KDT == kBF16;
+    constexpr int NP = D * ES / 16;                  // 16-byte pieces per row (a multiple of 4)
+    constexpr int NLD = NP / 4;                      // 64-lane loads per 16-row block
+    constexpr int RBP = D * ES + 16;                 // padded LDS row
+    __shared__ __align__(16) uint8_t stage[kWaves * 16 * RBP];
 
     // Logical tile order, fastest first: head sub-group (or the head's place in
     // its group for the per-head baseline), KV head, context chunk, batch. The
@@ -75,7 +85,17 @@ __global__ __launch_bounds__(kThreads) void qk_scores(QkArgs a) {
     const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(a.K) + ((static_cast<size_t>(b) * a.C + r0) * a.Hkv + kv) * D * ES, 0,
         (nrows - 1) * krow + D * ES, kRawBufferFlags);
-    const int klane = m * krow + 8 * g * ES;
+    // Load i of a block: lane l takes piece f = 64 i + l, i.e. row f / NP,
+    // piece f % NP (whole rows, consecutive in memory within each row).
+    int koff[NLD], soff[NLD];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+        const int f = 64 * i + lane;
+        koff[i] = (f / NP) * krow + (f % NP) * 16;
+        soff[i] = (f / NP) * RBP + (f % NP) * 16;
+    }
+    typedef __attribute__((address_space(3))) uint8_t lds_u8;
+    lds_u8* const region = (lds_u8*)stage + wave * 16 * RBP;
 
     // q operand, once per workgroup. Heads past nq read the tile's last head (a
     // valid address); their result columns are never stored.
@@ -109,18 +129,32 @@ __global__ __launch_bounds__(kThreads) void qk_scores(QkArgs a) {
     (void)QW;
 
     struct Buf {
-        u32x4 raw[NBLK][PIECES];
+        u32x4 raw[NLD];
     };
     // Row block j (16 rows) of the chunk: wave w takes j = w, w + kWaves, ...
     auto load = [&](Buf& bf, int j) {
 #pragma unroll
+        for (int i = 0; i < NLD; ++i)
+            bf.raw[i] = __builtin_amdgcn_raw_buffer_load_b128(kres, koff[i], 16 * j * krow, kCachePolicyNt);
+    };
+    auto compute_store = [&](const Buf& bfin, int j) {
+        // Re-layout through the wave's LDS region (in program order: one
+        // wave's LDS operations execute in order).
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < NLD; ++i)
+            *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(region + soff[i]) = bfin.raw[i];
+        asm volatile("" ::: "memory");
+        struct {
+            u32x4 raw[NBLK][PIECES];
+        } bf;
+#pragma unroll
         for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
             for (int p = 0; p < PIECES; ++p)
-                bf.raw[blk][p] = __builtin_amdgcn_raw_buffer_load_b128(
-                    kres, klane + (32 * blk * ES + 16 * p), 16 * j * krow, kCachePolicyNt);
-    };
-    auto compute_store = [&](const Buf& bf, int j) {
+                bf.raw[blk][p] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+                    region + m * RBP + (32 * blk + 8 * g) * ES + 16 * p);
+        asm volatile("" ::: "memory");
         // Independent accumulators keep consecutive MFMAs off one dependency chain.
         constexpr int NACC = BF16 ? 3 : 4;
         f32x4 acc[NACC][NSET];

@@ -291,10 +291,11 @@ def _check_qk_plan(p, B, C, Hq, Hkv, D, dt):
             for wave in range(4):
                 j = step * 4 + wave
                 assert 16 * (j + 1) * krow < 2 ** 31
-                for blk in range(NBLK):
-                    for pc in range(PIECES):
-                        off = m * krow + 8 * g * es + 32 * blk * es + 16 * pc + 16 * j * krow
-                        assert np.array_equal(off + 16 <= krec, (16 * j + m) < nrows)
+                NP = D * es // 16
+                for i in range(NP // 4):               # whole-row loads: piece f = 64 i + lane
+                    f = 64 * i + lanes
+                    off = (f // NP) * krow + (f % NP) * 16 + 16 * j * krow
+                    assert np.array_equal(off + 16 <= krec, (16 * j + f // NP) < nrows)
                 if step < nsteps:
                     for s in range(NSET):
                         h = m + 16 * s
@@ -314,3 +315,34 @@ def test_qk_plan_bounds(B, C, Hq, Hkv, D, dt):
         for rows in (0, 64, 128, 192):
             p = ga.qk_make_plan(B, C, Hq, Hkv, D, dt, mode, rows_per_block=rows)
             _check_qk_plan(p, B, C, Hq, Hkv, D, dt)
+
+
+@pytest.mark.parametrize("D,dt", [(32, "bf16"), (96, "f16"), (128, "bf16"), (160, "f32"), (256, "f32"), (224, "f16")])
+def test_qk_lds_relayout(D, dt):
+    """The score kernel's LDS re-layout: every 16-byte piece of the 16-row block
+    is stored once inside the wave's region, and lane (m, g) reads back row m's
+    d-range [32 blk + 8 g, +8) for each block of 32 d (16-row reads in
+    distinct 16-byte bank groups)."""
+    es = _esize(dt)
+    NP, RBP = D * es // 16, D * es + 16
+    where = {}
+    for i in range(NP // 4):
+        for lane in range(64):
+            f = 64 * i + lane
+            row, piece = f // NP, f % NP
+            off = row * RBP + piece * 16
+            assert 0 <= off and off + 16 <= 16 * RBP and off not in where.values()
+            where[(row, piece)] = off
+    assert len(where) == 16 * NP
+    pieces_per_op = 2 if dt == "f32" else 1
+    for blk in range(D // 32):
+        for pc in range(pieces_per_op):
+            groups = set()
+            for lane in range(64):
+                m, g = lane & 15, lane >> 4
+                off = m * RBP + (32 * blk + 8 * g) * es + 16 * pc
+                byte = (32 * blk + 8 * g) * es + 16 * pc
+                assert where[(m, byte // 16)] == off       # the piece holding d = 32 blk + 8 g (+ 4 pc for fp32)
+                if g == 0:
+                    groups.add((off // 16) % 16)
+            assert len(groups) == 16                      # the 16 rows of one lane group: distinct bank groups

@@ -21,7 +21,7 @@ from typing import Optional, Union
 __all__ = [
     "LIB_PATH", "GqaAvError", "Hint", "Plan", "load", "resolve_mode", "make_plan",
     "gqa_av_decode", "gqa_av_decode_plan", "bind", "BoundCall", "release", "status_string", "MODES", "DTYPES",
-    "QkPlan", "qk_make_plan", "gqa_qk_decode", "bind_qk",
+    "QkHint", "QkPlan", "qk_make_plan", "gqa_qk_decode", "bind_qk",
 ]
 
 # GQA_AV_LIBRARY may name another build of the same library (tuning variants).
@@ -62,10 +62,16 @@ class Plan(ctypes.Structure):
         return f"Plan({self.as_dict()})"
 
 
+class QkHint(ctypes.Structure):
+    _fields_ = [("rows_per_block", ctypes.c_int64), ("cu_count", ctypes.c_int32), ("kv_tile", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 4)]
+
+
 class QkPlan(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("engine", ctypes.c_int32), ("heads_per_tile", ctypes.c_int32),
                 ("subgroups", ctypes.c_int32), ("rows_per_block", ctypes.c_int64), ("grid", ctypes.c_int64),
-                ("k_bytes_read", ctypes.c_int64), ("reserved", ctypes.c_int32 * 4)]
+                ("k_bytes_read", ctypes.c_int64), ("kv_heads_per_tile", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 3)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
@@ -102,7 +108,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gqa_av_last_error.restype = ctypes.c_char_p
     lib.gqa_av_release.argtypes = []
     lib.gqa_av_release.restype = ip
-    lib.gqa_qk_make_plan.argtypes = [i64, i64, i64, i64, i64, ip, ip, i64, ip, ctypes.POINTER(QkPlan)]
+    lib.gqa_qk_make_plan.argtypes = [i64, i64, i64, i64, i64, ip, ip, ctypes.POINTER(QkHint), ctypes.POINTER(QkPlan)]
     lib.gqa_qk_make_plan.restype = ip
     lib.gqa_qk_decode.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ip, ctypes.c_float, ip, vp]
     lib.gqa_qk_decode.restype = ip
@@ -285,11 +291,12 @@ def release() -> None:
 # ---- decode score step ----------------------------------------------------------
 
 def qk_make_plan(B: int, C: int, Hq: int, Hkv: int, D: int, k_dtype: str, mode: Union[str, int] = "auto",
-                 rows_per_block: int = 0, cu_count: int = 0) -> QkPlan:
+                 rows_per_block: int = 0, cu_count: int = 0, kv_tile: int = 0) -> QkPlan:
     """Host-only planning of the score step (no GPU needed); 0 means automatic."""
+    h = QkHint()
+    h.rows_per_block, h.cu_count, h.kv_tile = int(rows_per_block), int(cu_count), int(kv_tile)
     p = QkPlan()
-    rc = load().gqa_qk_make_plan(B, C, Hq, Hkv, D, DTYPES[k_dtype], _mode(mode), int(rows_per_block),
-                                 int(cu_count), ctypes.byref(p))
+    rc = load().gqa_qk_make_plan(B, C, Hq, Hkv, D, DTYPES[k_dtype], _mode(mode), ctypes.byref(h), ctypes.byref(p))
     if rc != 0:
         _raise(rc)
     return p

@@ -123,6 +123,7 @@ constexpr int kRawBufferFlags = 0x00020000;
 constexpr int kCachePolicySc1 = 16;   // device-scope coherence (same policy as agent-scope atomics)
 constexpr int kCachePolicyNt = 2;     // non-temporal (streamed once)
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 
 template <int NB>

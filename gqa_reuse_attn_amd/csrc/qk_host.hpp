@@ -12,9 +12,10 @@ using gqa_av::QkArgs;
 
 constexpr int64_t kQkRowsQuantum = 64;        // 4 waves x 16 rows
 constexpr int64_t kQkTargetWgPerCu = 2;
+constexpr int64_t kQkMinRowsWide = 256;       // shortest chunk worth a wider KV tile
 
 int qk_plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int k_dtype, int mode,
-                 int64_t rows_hint, int cus, gqa_qk_plan* plan) {
+                 int64_t rows_hint, int cus, int kv_tile, gqa_qk_plan* plan) {
     int rc = check_sizes(B, C, Hq, Hkv, D, k_dtype);
     if (rc != GQA_AV_OK) return rc;
     const int resolved = gqa_av_resolve_mode(Hq, Hkv, mode);
@@ -37,13 +38,33 @@ int qk_plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int k
         nsg = static_cast<int>(ceil_div(G, hpt));
     }
     const int64_t minor = resolved == GQA_AV_PER_HEAD ? G : nsg;
-    const int64_t tiles = B * Hkv * minor;
+    if (cus <= 0) cus = kDefaultCUs;
+    const int64_t target = kQkTargetWgPerCu * cus;
+    // KV heads per tile: forced, or the widest of 4 and 2 whose grid still
+    // reaches the target with chunks of at least kQkMinRowsWide rows (a plain
+    // read of 2 KB rows streams faster in wider slices).
+    int ht = kv_tile > 0 ? kv_tile : 1;
+    if (kv_tile <= 0 && resolved == GQA_AV_REUSE) {
+        for (int cand : {4, 2}) {
+            if (Hkv % cand != 0) continue;
+            const int64_t tw = B * (Hkv / cand) * minor;
+            if (tw > 0 && tw * std::min<int64_t>(ceil_div(target, tw), std::max<int64_t>(1, C / kQkMinRowsWide)) >= target) {
+                ht = cand;
+                break;
+            }
+        }
+    }
+    if (ht != 1 && ht != 2 && ht != 4)
+        return fail(GQA_AV_ERR_UNSUPPORTED, "score step: kv_tile %d (1, 2 or 4)", ht);
+    if (Hkv % ht != 0) return fail(GQA_AV_ERR_INVALID_ARG, "score step: kv_tile %d does not divide Hkv", ht);
+    if (ht > 1 && resolved != GQA_AV_REUSE)
+        return fail(GQA_AV_ERR_UNSUPPORTED, "score step: kv_tile > 1 needs reuse mode");
+    const int64_t tiles = B * (Hkv / ht) * minor;
 
     // Context rows per workgroup: enough workgroups for about two per CU, in
     // whole 64-row steps; 32-bit K offsets for the chunk and its overrun.
     int64_t rows = rows_hint;
     if (rows <= 0) {
-        const int64_t target = kQkTargetWgPerCu * (cus > 0 ? cus : kDefaultCUs);
         const int64_t nchunk = tiles > 0 ? std::max<int64_t>(1, ceil_div(target, tiles)) : 1;
         rows = std::max<int64_t>(1, ceil_div(C, nchunk));
     }
@@ -58,25 +79,35 @@ int qk_plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int k
 
     std::memset(plan, 0, sizeof *plan);
     plan->mode = resolved;
-    plan->engine = k_dtype == GQA_AV_BF16 ? GQA_AV_ENGINE_MFMA_BF16 : GQA_AV_ENGINE_MFMA;
+    // The 16-bit matrix path for bf16 and fp16 K, the fp32 one for fp32 K.
+    plan->engine = k_dtype == GQA_AV_F32 ? GQA_AV_ENGINE_MFMA : GQA_AV_ENGINE_MFMA_BF16;
     plan->heads_per_tile = hpt;
     plan->subgroups = nsg;
     plan->rows_per_block = rows;
     plan->grid = grid;
     plan->k_bytes_read = B * C * Hkv * D * es * (resolved == GQA_AV_PER_HEAD ? G : nsg);
+    plan->kv_heads_per_tile = ht;
     return GQA_AV_OK;
+}
+
+template <int KDT, int NBLK, int NSET>
+hipError_t launch_qk_ht(const QkArgs& a, hipStream_t s) {
+    switch (a.ht) {
+    case 1: hipLaunchKernelGGL((gqa_av::qk_scores<KDT, NBLK, NSET, 1>), dim3(a.nblocks), dim3(gqa_av::kThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((gqa_av::qk_scores<KDT, NBLK, NSET, 2>), dim3(a.nblocks), dim3(gqa_av::kThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((gqa_av::qk_scores<KDT, NBLK, NSET, 4>), dim3(a.nblocks), dim3(gqa_av::kThreads), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 template <int KDT, int NBLK>
 hipError_t launch_qk_nset(int nset, const QkArgs& a, hipStream_t s) {
-    if (nset == 1) {
-        hipLaunchKernelGGL((gqa_av::qk_scores<KDT, NBLK, 1>), dim3(a.nblocks), dim3(gqa_av::kThreads), 0, s, a);
-    } else if constexpr (NBLK <= 4) {
-        hipLaunchKernelGGL((gqa_av::qk_scores<KDT, NBLK, 2>), dim3(a.nblocks), dim3(gqa_av::kThreads), 0, s, a);
-    } else {
-        return hipErrorInvalidValue;
+    if (nset == 1) return launch_qk_ht<KDT, NBLK, 1>(a, s);
+    if constexpr (NBLK <= 4) {
+        if (nset == 2) return launch_qk_ht<KDT, NBLK, 2>(a, s);
     }
-    return hipGetLastError();
+    return hipErrorInvalidValue;
 }
 
 template <int KDT>
@@ -98,11 +129,13 @@ int qk_run(const float* q, const void* K, float* scores, int64_t B, int64_t C, i
            int64_t D, int k_dtype, float scale, const gqa_qk_plan* plan, void* stream) {
     if (!plan) return fail(GQA_AV_ERR_INVALID_ARG, "plan is NULL");
     gqa_qk_plan check;
-    int rc = qk_plan_impl(B, C, Hq, Hkv, D, k_dtype, plan->mode, plan->rows_per_block, kDefaultCUs, &check);
+    int rc = qk_plan_impl(B, C, Hq, Hkv, D, k_dtype, plan->mode, plan->rows_per_block, kDefaultCUs,
+                          plan->kv_heads_per_tile, &check);
     if (rc != GQA_AV_OK) return rc;
     if (check.mode != plan->mode || check.engine != plan->engine || check.heads_per_tile != plan->heads_per_tile ||
         check.subgroups != plan->subgroups || check.rows_per_block != plan->rows_per_block ||
-        check.grid != plan->grid || check.k_bytes_read != plan->k_bytes_read)
+        check.grid != plan->grid || check.k_bytes_read != plan->k_bytes_read ||
+        check.kv_heads_per_tile != plan->kv_heads_per_tile)
         return fail(GQA_AV_ERR_INVALID_ARG, "score plan does not belong to this problem");
     if (B == 0 || C == 0) return GQA_AV_OK;
     if (!q || !K || !scores) return fail(GQA_AV_ERR_INVALID_ARG, "q, K and scores must not be NULL");
@@ -124,6 +157,7 @@ int qk_run(const float* q, const void* K, float* scores, int64_t B, int64_t C, i
     a.G = static_cast<int32_t>(Hq / Hkv);
     a.per_head = plan->mode == GQA_AV_PER_HEAD;
     a.nsg = plan->subgroups;
+    a.ht = plan->kv_heads_per_tile;
     a.nblocks = static_cast<uint32_t>(plan->grid);
     const int nset = plan->mode == GQA_AV_PER_HEAD ? 1 : plan->heads_per_tile / 16;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -142,9 +176,12 @@ int qk_run(const float* q, const void* K, float* scores, int64_t B, int64_t C, i
 extern "C" {
 
 int gqa_qk_make_plan(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int k_dtype, int mode,
-                     int64_t rows_per_block, int cu_count, gqa_qk_plan* plan) {
-    return qk_plan_impl(B, C, Hq, Hkv, D, k_dtype, mode, rows_per_block, cu_count > 0 ? cu_count : kDefaultCUs,
-                        plan);
+                     const gqa_qk_hint* hint, gqa_qk_plan* plan) {
+    gqa_qk_hint h;
+    std::memset(&h, 0, sizeof h);
+    if (hint) h = *hint;
+    return qk_plan_impl(B, C, Hq, Hkv, D, k_dtype, mode, h.rows_per_block, h.cu_count > 0 ? h.cu_count : kDefaultCUs,
+                        h.kv_tile, plan);
 }
 
 int gqa_qk_decode_plan(const float* q, const void* K, float* scores, int64_t B, int64_t C, int64_t Hq,
@@ -163,7 +200,7 @@ int gqa_qk_decode(const float* q, const void* K, float* scores, int64_t B, int64
     rc = device_cus(dev, &cus);
     if (rc != GQA_AV_OK) return rc;
     gqa_qk_plan plan;
-    rc = qk_plan_impl(B, C, Hq, Hkv, D, k_dtype, mode, 0, cus, &plan);
+    rc = qk_plan_impl(B, C, Hq, Hkv, D, k_dtype, mode, 0, cus, 0, &plan);
     if (rc != GQA_AV_OK) return rc;
     return qk_run(q, K, scores, B, C, Hq, Hkv, D, k_dtype, scale, &plan, stream);
 }

@@ -9,14 +9,22 @@
 // K row, so a workgroup per KV head reads each K row once for all G of them.
 //
 // Every score depends on a single K row, so the context needs no split and no
-// combine: a workgroup owns a tile (b, kv_h, head set) and a block of context
-// rows. The contraction over d is a skinny matrix product, done on the matrix
+// combine: a workgroup owns a tile (b, HT adjacent KV heads, head set) and a
+// block of context rows; 4 / HT of its waves stream each KV head, so the
+// workgroup reads an HT * D-wide contiguous slice of every row. The contraction over d is a skinny matrix product, done on the matrix
 // cores with the K rows as the A operand (16 rows x 32 d), which is K's own
 // row-major layout, and the query heads as the B operand (32 d x 16 heads):
 //  * bf16 K: v_mfma_f32_16x16x32_bf16, with each fp32 q value split once per
 //    workgroup into three bf16 terms (split_bf16x3, exact), so every product is
 //    exact and only the fp32 sums round;
-//  * fp16 / fp32 K: K widened exactly to fp32 and v_mfma_f32_16x16x4_f32.
+//  * fp16 K: v_mfma_f32_16x16x32_f16 with K as it is. Each query head's q
+//    values are scaled by a power of two 2^e that brings their largest
+//    magnitude into [2^14, 2^15) and split into three fp16 terms by rounding
+//    (each remainder is exact); every product of fp16 values is exact in fp32,
+//    and what the split drops is below 2^-33 of that head's largest q value
+//    (2^-38 of it near fp16's subnormal range), far under the fp32 rounding of
+//    the sums. The head's result column is multiplied by scale * 2^-e;
+//  * fp32 K: K as fp32 and v_mfma_f32_16x16x4_f32.
 // The A operand wants lane 16 g + m to hold row m's d-range
 // [32 blk + 8 g, 32 blk + 8 g + 8). Loaded that way, one 64-lane load would
 // touch 16 rows at 64 bytes each, a pattern that streams 25 % slower on
@@ -31,6 +39,10 @@
 
 #include "av_kernels.hpp"
 
+#ifndef GQA_QK_BLOCKS
+#define GQA_QK_BLOCKS 1   // 16-row blocks per wave and buffer (two buffers in flight); 2 and 4 measured slower
+#endif
+
 namespace gqa_av {
 
 struct QkArgs {
@@ -44,16 +56,22 @@ struct QkArgs {
     int32_t B, Hq, Hkv, G;
     int32_t per_head;        // 0: tiles of up to 16 * NSET heads of one group; 1: one head per tile
     int32_t nsg;             // head sub-groups per KV head (reuse)
+    int32_t ht;              // adjacent KV heads per tile (reuse; 1 for per-head)
     uint32_t nblocks;
 };
 
-// KDT: element type of K; NBLK = D / 32; NSET sets of 16 heads per tile.
-template <int KDT, int NBLK, int NSET>
+// KDT: element type of K; NBLK = D / 32; NSET sets of 16 heads per tile; HT
+// adjacent KV heads per tile (1, 2 or 4).
+template <int KDT, int NBLK, int NSET, int HT>
 __global__ __launch_bounds__(kThreads) void qk_scores(QkArgs a) {
+    static_assert(HT == 1 || HT == 2 || HT == 4, "KV heads per tile must divide the waves");
+    constexpr int WPH = kWaves / HT;                 // waves per KV head
     constexpr int ES = esize<KDT>();
     constexpr int D = 32 * NBLK;
     constexpr int PIECES = KDT == kF32 ? 2 : 1;      // 16-byte operand pieces per lane and block of 32 d
     constexpr bool BF16 = KDT == kBF16;
+    constexpr bool F16 = KDT == kF16;
+    constexpr bool SPLIT = BF16 || F16;              // three 16-bit q terms on the 16x16x32 instruction
     constexpr int NP = D * ES / 16;                  // 16-byte pieces per row (a multiple of 4)
     constexpr int NLD = NP / 4;                      // 64-lane loads per 16-row block
     constexpr int RBP = D * ES + 16;                 // padded LDS row
@@ -66,11 +84,10 @@ __global__ __launch_bounds__(kThreads) void qk_scores(QkArgs a) {
     uint32_t t = xcd_remap(blockIdx.x, a.nblocks);
     const int nminor = a.per_head ? a.G : a.nsg;
     const int minor = t % nminor; t /= nminor;
-    const int kv = t % a.Hkv; t /= a.Hkv;
+    const int nkvt = a.Hkv / HT;
+    const int kv0 = static_cast<int>(t % nkvt) * HT; t /= nkvt;   // first KV head of the tile
     const int chunk = t % a.nchunk; t /= a.nchunk;
     const int b = static_cast<int>(t);
-    const int q_first = a.per_head ? kv * a.G + minor : kv * a.G + minor * 16 * NSET;
-    const int nq = a.per_head ? 1 : min(16 * NSET, a.G - minor * 16 * NSET);
     const int64_t r0 = uniform64(static_cast<int64_t>(chunk) * a.rows_per_block);
     const int nrows = static_cast<int>(uniform64(min(static_cast<int64_t>(a.rows_per_block), a.C - r0)));
 
@@ -78,39 +95,93 @@ __global__ __launch_bounds__(kThreads) void qk_scores(QkArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int m = lane & 15;                         // row (A) / head (B, result) inside a tile
     const int g = lane >> 4;                         // d-group of 8 inside a block of 32
+    const int kvl = wave / WPH;                      // this wave's KV head inside the tile
+    const int wh = wave % WPH;                       // and its place among that head's waves
+    const int kv = kv0 + kvl;
+    const int q_first = a.per_head ? kv * a.G + minor : kv * a.G + minor * 16 * NSET;
+    const int nq = a.per_head ? 1 : min(16 * NSET, a.G - minor * 16 * NSET);
 
     // K through a buffer resource ending at the chunk's last row: rows past it
     // read as zero (their scores are never stored).
     const int krow = a.Hkv * D * ES;
     const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(a.K) + ((static_cast<size_t>(b) * a.C + r0) * a.Hkv + kv) * D * ES, 0,
-        (nrows - 1) * krow + D * ES, kRawBufferFlags);
+        const_cast<uint8_t*>(a.K) + ((static_cast<size_t>(b) * a.C + r0) * a.Hkv + kv0) * D * ES, 0,
+        (nrows - 1) * krow + HT * D * ES, kRawBufferFlags);
     // Load i of a block: lane l takes piece f = 64 i + l, i.e. row f / NP,
     // piece f % NP (whole rows, consecutive in memory within each row).
     int koff[NLD], soff[NLD];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
         const int f = 64 * i + lane;
-        koff[i] = (f / NP) * krow + (f % NP) * 16;
+        koff[i] = (f / NP) * krow + kvl * D * ES + (f % NP) * 16;
         soff[i] = (f / NP) * RBP + (f % NP) * 16;
     }
     typedef __attribute__((address_space(3))) uint8_t lds_u8;
     lds_u8* const region = (lds_u8*)stage + wave * 16 * RBP;
 
-    // q operand, once per workgroup. Heads past nq read the tile's last head (a
+    // q operand, once per wave. Heads past nq read the tile's last head (a
     // valid address); their result columns are never stored.
-    constexpr int QW = BF16 ? 3 : 1;                 // bf16: three exact terms
-    u32x4 qb[BF16 ? 3 : 1][NSET][NBLK];
-    float qf[BF16 ? 1 : NSET][BF16 ? 1 : NBLK][8];
+    u32x4 qb[SPLIT ? 3 : 1][NSET][NBLK];
+    float qf[SPLIT ? 1 : NSET][SPLIT ? 1 : NBLK][8];
+    float qv[NSET][NBLK][8];
 #pragma unroll
     for (int s = 0; s < NSET; ++s) {
         const float* qrow = a.q + (static_cast<size_t>(b) * a.Hq + q_first + min(m + 16 * s, nq - 1)) * D + 8 * g;
 #pragma unroll
-        for (int blk = 0; blk < NBLK; ++blk) {
-            float v[8];
+        for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = qrow[32 * blk + j];
-            if constexpr (BF16) {
+            for (int j = 0; j < 8; ++j) qv[s][blk][j] = qrow[32 * blk + j];
+    }
+    // fp16 K: each head's power-of-two scale (see above). Head m + 16 s's q
+    // values sit in lanes m, m + 16, m + 32 and m + 48; its result column in
+    // the same lanes.
+    float out_scale[NSET];
+#pragma unroll
+    for (int s = 0; s < NSET; ++s) out_scale[s] = a.scale;
+    if constexpr (F16) {
+#pragma unroll
+        for (int s = 0; s < NSET; ++s) {
+            float mx = 0.0f;
+#pragma unroll
+            for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(qv[s][blk][j]));
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            int ex = 0;
+            (void)frexpf(mx, &ex);                   // mx in [2^(ex-1), 2^ex)
+            const int e = mx > 0.0f ? 15 - ex : 0;
+#pragma unroll
+            for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) qv[s][blk][j] = ldexpf(qv[s][blk][j], e);
+            out_scale[s] = ldexpf(a.scale, -e);
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < NSET; ++s) {
+#pragma unroll
+        for (int blk = 0; blk < NBLK; ++blk) {
+            const float* v = qv[s][blk];
+            if constexpr (F16) {
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    uint32_t t[3][2];
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const _Float16 h1 = static_cast<_Float16>(v[2 * p + e]);
+                        const float r1 = v[2 * p + e] - static_cast<float>(h1);
+                        const _Float16 h2 = static_cast<_Float16>(r1);
+                        const float r2 = r1 - static_cast<float>(h2);
+                        const _Float16 h3 = static_cast<_Float16>(r2);
+                        t[0][e] = __builtin_bit_cast(uint16_t, h1);
+                        t[1][e] = __builtin_bit_cast(uint16_t, h2);
+                        t[2][e] = __builtin_bit_cast(uint16_t, h3);
+                    }
+#pragma unroll
+                    for (int k = 0; k < 3; ++k) qb[k][s][blk][p] = t[k][0] | (t[k][1] << 16);
+                }
+            } else if constexpr (BF16) {
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
                     uint32_t th[2], tm[2], tl[2];
@@ -126,24 +197,29 @@ __global__ __launch_bounds__(kThreads) void qk_scores(QkArgs a) {
             }
         }
     }
-    (void)QW;
 
+    constexpr int UB = GQA_QK_BLOCKS;                // 16-row blocks per wave and buffer
     struct Buf {
-        u32x4 raw[NLD];
+        u32x4 raw[UB][NLD];
     };
-    // Row block j (16 rows) of the chunk: wave w takes j = w, w + kWaves, ...
-    auto load = [&](Buf& bf, int j) {
+    // Step st of the head's wave wh covers row blocks j = (st UB + u) WPH + wh,
+    // u < UB, each of 16 rows.
+    auto block_of = [&](int st, int u) { return (st * UB + u) * WPH + wh; };
+    auto load = [&](Buf& bf, int st) {
 #pragma unroll
-        for (int i = 0; i < NLD; ++i)
-            bf.raw[i] = __builtin_amdgcn_raw_buffer_load_b128(kres, koff[i], 16 * j * krow, kCachePolicyNt);
+        for (int u = 0; u < UB; ++u)
+#pragma unroll
+            for (int i = 0; i < NLD; ++i)
+                bf.raw[u][i] = __builtin_amdgcn_raw_buffer_load_b128(kres, koff[i], 16 * block_of(st, u) * krow,
+                                                                     kCachePolicyNt);
     };
-    auto compute_store = [&](const Buf& bfin, int j) {
+    auto compute_store = [&](const u32x4 (&bfin)[NLD], int j) {
         // Re-layout through the wave's LDS region (in program order: one
         // wave's LDS operations execute in order).
         asm volatile("" ::: "memory");
 #pragma unroll
         for (int i = 0; i < NLD; ++i)
-            *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(region + soff[i]) = bfin.raw[i];
+            *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(region + soff[i]) = bfin[i];
         asm volatile("" ::: "memory");
         struct {
             u32x4 raw[NBLK][PIECES];
@@ -156,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void qk_scores(QkArgs a) {
                     region + m * RBP + (32 * blk + 8 * g) * ES + 16 * p);
         asm volatile("" ::: "memory");
         // Independent accumulators keep consecutive MFMAs off one dependency chain.
-        constexpr int NACC = BF16 ? 3 : 4;
+        constexpr int NACC = SPLIT ? 3 : 4;
         f32x4 acc[NACC][NSET];
 #pragma unroll
         for (int k = 0; k < NACC; ++k)
@@ -172,20 +248,20 @@ __global__ __launch_bounds__(kThreads) void qk_scores(QkArgs a) {
                     for (int s = 0; s < NSET; ++s)
                         acc[k][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                             ka, __builtin_bit_cast(bf16x8, qb[k][s][blk]), acc[k][s], 0, 0, 0);
+            } else if constexpr (F16) {
+                const half8 ka = __builtin_bit_cast(half8, bf.raw[blk][0]);
+#pragma unroll
+                for (int k = 0; k < 3; ++k)
+#pragma unroll
+                    for (int s = 0; s < NSET; ++s)
+                        acc[k][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            ka, __builtin_bit_cast(half8, qb[k][s][blk]), acc[k][s], 0, 0, 0);
             } else {
                 float kf[8];
-                if constexpr (KDT == kF32) {
 #pragma unroll
-                    for (int p = 0; p < 2; ++p)
+                for (int p = 0; p < 2; ++p)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) kf[4 * p + e] = __uint_as_float(bf.raw[blk][p][e]);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        kf[2 * e] = f16_bits_to_f32(bf.raw[blk][0][e] & 0xffffu);
-                        kf[2 * e + 1] = f16_bits_to_f32(bf.raw[blk][0][e] >> 16);
-                    }
-                }
+                    for (int e = 0; e < 4; ++e) kf[4 * p + e] = __uint_as_float(bf.raw[blk][p][e]);
 #pragma unroll
                 for (int st = 0; st < 8; ++st)
 #pragma unroll
@@ -205,7 +281,7 @@ __global__ __launch_bounds__(kThreads) void qk_scores(QkArgs a) {
                 for (int i = 0; i < 4; ++i) {
                     const int row = 16 * j + 4 * g + i;
                     if (row < nrows)
-                        a.scores[(static_cast<size_t>(b) * a.C + r0 + row) * a.Hq + q_first + h] = sum[i] * a.scale;
+                        a.scores[(static_cast<size_t>(b) * a.C + r0 + row) * a.Hq + q_first + h] = sum[i] * out_scale[s];
                 }
             }
         }
@@ -214,17 +290,21 @@ __global__ __launch_bounds__(kThreads) void qk_scores(QkArgs a) {
     // Two buffers in flight; the reload is unconditional (blocks past the
     // chunk read zeros and store nothing).
     const int nrb = (nrows + 15) / 16;
-    const int nsteps = (nrb + kWaves - 1) / kWaves;
+    const int nsteps = (nrb + WPH * UB - 1) / (WPH * UB);
+    auto consume = [&](const Buf& bf, int st) {
+#pragma unroll
+        for (int u = 0; u < UB; ++u) compute_store(bf.raw[u], block_of(st, u));
+    };
     Buf bA, bB;
     int st = 0;
-    if (nsteps > 0) load(bA, wave);
+    if (nsteps > 0) load(bA, 0);
     for (; st + 1 < nsteps; st += 2) {
-        load(bB, (st + 1) * kWaves + wave);
-        compute_store(bA, st * kWaves + wave);
-        load(bA, (st + 2) * kWaves + wave);
-        compute_store(bB, (st + 1) * kWaves + wave);
+        load(bB, st + 1);
+        consume(bA, st);
+        load(bA, st + 2);
+        consume(bB, st + 1);
     }
-    if (st < nsteps) compute_store(bA, st * kWaves + wave);
+    if (st < nsteps) consume(bA, st);
 }
 
 }  // namespace gqa_av

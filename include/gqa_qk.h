@@ -23,7 +23,9 @@
  *   scores  [B][C][Hq]      float32, fully overwritten
  * All three are DEVICE pointers on the current HIP device, owned by the caller.
  * Accumulation is in float32: with bf16 K every product q * K is exact (q is
- * split exactly into three bf16 terms) and only the sums round; with fp16 and
+ * split exactly into three bf16 terms) and only the sums round; with fp16 K,
+ * q is scaled by a power of two and split into three fp16 terms, the products
+ * are exact and the split drops less than 2^-33 of the largest q value; with
  * fp32 K the products are fp32 fused multiply-adds. The scale multiplies the
  * sum once at the end.
  *
@@ -46,22 +48,30 @@
 extern "C" {
 #endif
 
+/* Optional planning hints. Zero-initialise; every field at 0 means automatic. */
+typedef struct gqa_qk_hint {
+    int64_t rows_per_block;  /* context rows per workgroup (rounded up to a multiple of 64) */
+    int32_t cu_count;        /* compute units to plan for (make_plan: 256; decode: the device's) */
+    int32_t kv_tile;         /* adjacent KV heads per workgroup in reuse mode: 1, 2 or 4 */
+    int32_t reserved[4];
+} gqa_qk_hint;
+
 /* Launch plan of the score step. */
 typedef struct gqa_qk_plan {
     int32_t mode;            /* resolved: GQA_AV_PER_HEAD or GQA_AV_REUSE */
-    int32_t engine;          /* GQA_AV_ENGINE_MFMA_BF16 (bf16 K) or GQA_AV_ENGINE_MFMA (fp16 / fp32 K) */
-    int32_t heads_per_tile;  /* query heads one workgroup computes: 16 or 32 (reuse), 1 (per-head) */
+    int32_t engine;          /* GQA_AV_ENGINE_MFMA_BF16 (16-bit matrix path: bf16 and fp16 K) or GQA_AV_ENGINE_MFMA (fp32 K) */
+    int32_t heads_per_tile;  /* query heads per KV head in one workgroup: 16 or 32 (reuse), 1 (per-head) */
     int32_t subgroups;       /* workgroups along the heads of one KV head (reuse: ceil(G / heads_per_tile)) */
     int64_t rows_per_block;  /* context rows per workgroup (a multiple of 64) */
     int64_t grid;            /* workgroups launched */
     int64_t k_bytes_read;    /* K bytes the plan reads from memory (G x more for per-head) */
-    int32_t reserved[4];
+    int32_t kv_heads_per_tile; /* adjacent KV heads one workgroup streams (reuse: 1, 2 or 4; per-head: 1) */
+    int32_t reserved[3];
 } gqa_qk_plan;
 
-/* Build the plan. Host-only: needs no GPU. rows_per_block <= 0 and
- * cu_count <= 0 mean automatic (cu_count: 256). Returns a gqa_av_status. */
+/* Build the plan. Host-only: needs no GPU. hint may be NULL. Returns a gqa_av_status. */
 int gqa_qk_make_plan(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int k_dtype, int mode,
-                     int64_t rows_per_block, int cu_count, gqa_qk_plan *plan);
+                     const gqa_qk_hint *hint, gqa_qk_plan *plan);
 
 /* scores = scale * q . K as defined above, with an automatic plan for the
  * current device. B == 0 or C == 0 does nothing (scores is empty). */

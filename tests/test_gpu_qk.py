@@ -69,7 +69,7 @@ def _qk_cases():
                 if (G + D + C) % 3:
                     continue                    # a spread subset of the grid
                 dt = ("bf16", "f16", "f32")[k % 3]
-                Hkv = 1 + k % 3
+                Hkv = (1, 2, 4)[k % 3]
                 rows = (0, 64, 128)[k % 3]
                 cases.append((1 + k % 2, C, G * Hkv, Hkv, D, dt, rows))
                 k += 1
@@ -84,11 +84,13 @@ def test_qk_sweep(B, C, Hq, Hkv, D, dt, rows, oracle_lib):
     ref = oracle_lib.qk(q, K, dt, scale)
     bound = 2 * D * U32 * scale * abs_sum_qk(q, K) + 1e-30
     modes = ("auto", "per_head") if Hq // Hkv >= 2 else ("auto",)
-    for mode in modes:
-        plan = ga.qk_make_plan(B, C, Hq, Hkv, D, dt, mode, rows_per_block=rows)
+    plans = [ga.qk_make_plan(B, C, Hq, Hkv, D, dt, mode, rows_per_block=rows) for mode in modes]
+    plans += [ga.qk_make_plan(B, C, Hq, Hkv, D, dt, "reuse", rows_per_block=rows, kv_tile=ht)
+              for ht in (2, 4) if Hq // Hkv >= 2 and Hkv % ht == 0]
+    for plan in plans:
         out = _run(q, K, scale, plan=plan)
-        assert_parity(out, ref, dt, D, f"qk {(B, C, Hq, Hkv, D, dt, mode)} plan={plan.as_dict()}")
-        assert (np.abs(out - ref) <= bound).all(), f"qk elementwise bound {(B, C, Hq, Hkv, D, dt, mode)}"
+        assert_parity(out, ref, dt, D, f"qk {(B, C, Hq, Hkv, D, dt)} plan={plan.as_dict()}")
+        assert (np.abs(out - ref) <= bound).all(), f"qk elementwise bound {(B, C, Hq, Hkv, D, dt)} {plan.as_dict()}"
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])

@@ -344,11 +344,18 @@ def test_qk_plans():
     """Score-step planning: engine by K dtype, tiles per head group, row blocks."""
     p = ga.qk_make_plan(4, 32768, 16, 8, 128, "bf16")
     assert p.mode == 1 and p.engine == 3 and p.heads_per_tile == 16 and p.subgroups == 1
-    assert p.rows_per_block % 64 == 0 and p.grid == 4 * 8 * -(-32768 // p.rows_per_block)
+    assert p.kv_heads_per_tile == 4                                   # widest tile that still fills the GPU
+    assert p.rows_per_block % 64 == 0 and p.grid == 4 * 2 * -(-32768 // p.rows_per_block)
+    assert ga.qk_make_plan(4, 32768, 16, 1, 128, "bf16").kv_heads_per_tile == 1
+    assert ga.qk_make_plan(4, 32768, 16, 8, 128, "bf16", kv_tile=2).kv_heads_per_tile == 2
+    for kw in (dict(kv_tile=3), dict(kv_tile=8), dict(kv_tile=2, mode="per_head")):
+        with pytest.raises(ga.GqaAvError):
+            ga.qk_make_plan(4, 32768, 16, 8, 128, "bf16", **kw)
     assert p.k_bytes_read == 4 * 32768 * 8 * 128 * 2
     p = ga.qk_make_plan(4, 32768, 16, 8, 128, "bf16", "per_head")
     assert p.mode == 0 and p.heads_per_tile == 1 and p.k_bytes_read == 2 * 4 * 32768 * 8 * 128 * 2
-    assert ga.qk_make_plan(8, 16384, 24, 8, 96, "f16").engine == 2
+    assert p.kv_heads_per_tile == 1
+    assert ga.qk_make_plan(8, 16384, 24, 8, 96, "f16").engine == 3                # 16-bit matrix path
     assert ga.qk_make_plan(1, 256, 8, 2, 64, "f32").engine == 2
     p = ga.qk_make_plan(1, 300, 40, 1, 128, "bf16")                 # G = 40: 32-head sets
     assert p.heads_per_tile == 32 and p.subgroups == 2

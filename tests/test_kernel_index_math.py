@@ -247,54 +247,63 @@ def test_valu_engine_plan_bounds(B, C, Hq, Hkv, D, dt):
 
 # ---- decode score step -------------------------------------------------------
 
-def _check_qk_plan(p, B, C, Hq, Hkv, D, dt):
+QK_BLOCKS = 1   # 16-row blocks per wave and buffer in the score kernel
+
+
+def _check_qk_plan(p, B, C, Hq, Hkv, D, dt, UB=QK_BLOCKS):
     es, G = _esize(dt), Hq // Hkv
     per_head = p.mode == 0
-    NBLK, PIECES = D // 32, (2 if dt == "f32" else 1)
+    NBLK = D // 32
     NSET = 1 if per_head else p.heads_per_tile // 16
+    HT = p.kv_heads_per_tile
+    WPH = 4 // HT
+    assert HT in (1, 2, 4) and Hkv % HT == 0 and (HT == 1 or not per_head)
     rows = p.rows_per_block
     assert rows % 64 == 0 and D % 32 == 0
     nchunk = -(-C // rows)
     nminor = G if per_head else p.subgroups
-    assert p.grid == B * Hkv * nminor * nchunk
+    nkvt = Hkv // HT
+    assert p.grid == B * nkvt * nminor * nchunk
     krow = Hkv * D * es
+    NP = D * es // 16
     lanes = np.arange(64)
     m, g = lanes & 15, lanes >> 4
     written = np.zeros((B, C, Hq), np.int64)
     for blk_id in range(p.grid):
         t = _remap(blk_id, p.grid)
         minor = t % nminor; t //= nminor
-        kv = t % Hkv; t //= Hkv
+        kv0 = (t % nkvt) * HT; t //= nkvt
         chunk = t % nchunk; t //= nchunk
         b = t
         assert b < B
-        q_first = kv * G + minor if per_head else kv * G + minor * 16 * NSET
-        nq = 1 if per_head else min(16 * NSET, G - minor * 16 * NSET)
-        assert nq >= 1 and q_first + nq <= Hq
         r0 = chunk * rows
         nrows = min(rows, C - r0)
         assert nrows > 0
-        kbase = ((b * C + r0) * Hkv + kv) * D * es
-        krec = (nrows - 1) * krow + D * es
+        kbase = ((b * C + r0) * Hkv + kv0) * D * es
+        krec = (nrows - 1) * krow + HT * D * es
         assert kbase + krec <= B * C * Hkv * D * es
-        for s in range(NSET):                          # q operand reads
-            head = q_first + np.minimum(m + 16 * s, nq - 1)
-            qidx = (b * Hq + head) * D + 8 * g
-            assert qidx.min() >= 0 and (qidx + 32 * (NBLK - 1) + 7).max() < B * Hq * D
         nrb = -(-nrows // 16)
-        nsteps = -(-nrb // 4)
+        nsteps = -(-nrb // (WPH * UB))
         loaded, st = ([0] if nsteps else []), 0
         while st + 1 < nsteps:
             loaded += [st + 1, st + 2]
             st += 2
-        for step in loaded:
-            for wave in range(4):
-                j = step * 4 + wave
+        for wave in range(4):
+            kvl, wh = wave // WPH, wave % WPH
+            kv = kv0 + kvl
+            q_first = kv * G + minor if per_head else kv * G + minor * 16 * NSET
+            nq = 1 if per_head else min(16 * NSET, G - minor * 16 * NSET)
+            assert nq >= 1 and q_first + nq <= Hq
+            for s in range(NSET):                      # q operand reads
+                head = q_first + np.minimum(m + 16 * s, nq - 1)
+                qidx = (b * Hq + head) * D + 8 * g
+                assert qidx.min() >= 0 and (qidx + 32 * (NBLK - 1) + 7).max() < B * Hq * D
+            for step, u in ((st_, u_) for st_ in loaded for u_ in range(UB)):
+                j = (step * UB + u) * WPH + wh
                 assert 16 * (j + 1) * krow < 2 ** 31
-                NP = D * es // 16
                 for i in range(NP // 4):               # whole-row loads: piece f = 64 i + lane
                     f = 64 * i + lanes
-                    off = (f // NP) * krow + (f % NP) * 16 + 16 * j * krow
+                    off = (f // NP) * krow + kvl * D * es + (f % NP) * 16 + 16 * j * krow
                     assert np.array_equal(off + 16 <= krec, (16 * j + f // NP) < nrows)
                 if step < nsteps:
                     for s in range(NSET):
@@ -308,13 +317,17 @@ def _check_qk_plan(p, B, C, Hq, Hkv, D, dt):
 
 @pytest.mark.parametrize("B,C,Hq,Hkv,D,dt", [
     (2, 300, 8, 2, 64, "bf16"), (1, 65, 16, 1, 128, "f16"), (2, 129, 6, 3, 32, "f32"), (1, 1, 4, 4, 96, "bf16"),
-    (2, 500, 64, 2, 256, "bf16"), (1, 1000, 40, 1, 128, "f16"), (3, 77, 24, 8, 96, "f32"), (1, 257, 68, 2, 160, "bf16")])
+    (2, 500, 64, 2, 256, "bf16"), (1, 1000, 40, 1, 128, "f16"), (3, 77, 24, 8, 96, "f32"), (1, 257, 68, 2, 160, "bf16"),
+    (2, 700, 32, 4, 128, "bf16"), (1, 333, 24, 8, 96, "f16")])
 def test_qk_plan_bounds(B, C, Hq, Hkv, D, dt):
     modes = ("auto", "per_head") if Hq // Hkv >= 2 else ("auto",)
     for mode in modes:
         for rows in (0, 64, 128, 192):
-            p = ga.qk_make_plan(B, C, Hq, Hkv, D, dt, mode, rows_per_block=rows)
-            _check_qk_plan(p, B, C, Hq, Hkv, D, dt)
+            for ht in (0, 1, 2, 4):
+                if ht > 1 and (Hkv % ht or mode == "per_head" or Hq // Hkv < 2):
+                    continue
+                p = ga.qk_make_plan(B, C, Hq, Hkv, D, dt, mode, rows_per_block=rows, kv_tile=ht)
+                _check_qk_plan(p, B, C, Hq, Hkv, D, dt)
 
 
 @pytest.mark.parametrize("D,dt", [(32, "bf16"), (96, "f16"), (128, "bf16"), (160, "f32"), (256, "f32"), (224, "f16")])

@@ -122,6 +122,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kRawBufferFlags = 0x00020000;
 constexpr int kCachePolicySc1 = 16;   // device-scope coherence (same policy as agent-scope atomics)
 constexpr int kCachePolicyNt = 2;     // non-temporal (streamed once)
+// A buffer offset past every resource the kernels build (their ranges stay
+// below 2^30 bytes and their scalar offsets add less than 2^30): an access
+// there fails the range check, so a load reads zero and a store is dropped.
+constexpr int kOutOfRange = 0x40000000;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef short short4v __attribute__((ext_vector_type(4)));

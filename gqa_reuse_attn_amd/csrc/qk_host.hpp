@@ -69,7 +69,10 @@ int qk_plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int k
         rows = std::max<int64_t>(1, ceil_div(C, nchunk));
     }
     rows = ceil_div(rows, kQkRowsQuantum) * kQkRowsQuantum;
-    const int64_t max_rows = ((int64_t{1} << 30) / krow - 2 * kQkRowsQuantum) / kQkRowsQuantum * kQkRowsQuantum;
+    // K and score offsets inside a chunk stay below 2^30 bytes, with room for
+    // the reads and the scalar row offsets past its end.
+    const int64_t max_rows =
+        ((int64_t{1} << 30) / std::max(krow, 4 * Hq) - 2 * kQkRowsQuantum) / kQkRowsQuantum * kQkRowsQuantum;
     if (max_rows < kQkRowsQuantum) return fail(GQA_AV_ERR_UNSUPPORTED, "score step: rows of K too large");
     if (rows > max_rows) rows = max_rows;
     if (rows > INT32_MAX) rows = max_rows;
@@ -159,6 +162,11 @@ int qk_run(const float* q, const void* K, float* scores, int64_t B, int64_t C, i
     a.nsg = plan->subgroups;
     a.ht = plan->kv_heads_per_tile;
     a.nblocks = static_cast<uint32_t>(plan->grid);
+    // 16-byte score stores: each tile's heads are one run (one head subgroup)
+    // starting at a multiple of 4 heads (kv_heads_per_tile * G a multiple of
+    // 4), rows are whole 16-byte groups, and scores is 16-byte aligned.
+    a.vec4 = plan->mode == GQA_AV_REUSE && plan->subgroups == 1 && (plan->kv_heads_per_tile * a.G) % 4 == 0 &&
+             Hq % 4 == 0 && (reinterpret_cast<uintptr_t>(scores) & 15u) == 0;
     const int nset = plan->mode == GQA_AV_PER_HEAD ? 1 : plan->heads_per_tile / 16;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;

@@ -57,6 +57,7 @@ struct QkArgs {
     int32_t per_head;        // 0: tiles of up to 16 * NSET heads of one group; 1: one head per tile
     int32_t nsg;             // head sub-groups per KV head (reuse)
     int32_t ht;              // adjacent KV heads per tile (reuse; 1 for per-head)
+    int32_t vec4;            // 1: every tile's score run is whole rows of 16-byte groups, 16-byte aligned
     uint32_t nblocks;
 };
 
@@ -118,6 +119,49 @@ __global__ __launch_bounds__(kThreads) void qk_scores(QkArgs a) {
     }
     typedef __attribute__((address_space(3))) uint8_t lds_u8;
     lds_u8* const region = (lds_u8*)stage + wave * 16 * RBP;
+
+    // Scores: each step's results of all waves are gathered in an LDS tile of
+    // R rows (the step's 16-row blocks) by W = HT nq columns (the tile's heads,
+    // KV head by KV head) and written out by the whole workgroup: row r of the
+    // tile goes to wave r % 4, whose lanes store consecutive heads of the row
+    // (one contiguous run per row when nsg = 1), VE of them per lane: 4 (16-byte
+    // stores) when every run is 16-byte aligned (a.vec4, set by the host),
+    // else 1. Masked MI355X stores are not free, so a step issues only the
+    // rounds that hold entries (one round per set of 16 heads for VE = 4).
+    // Rows past the chunk fall outside the score resource, which ends after the
+    // chunk's last row of the tile's heads; lanes past the tile get an offset
+    // beyond it. Every offset, plus the step's row offset, stays below 2^30
+    // (the plan keeps a chunk's scores under it).
+    constexpr int R = 16 * WPH * GQA_QK_BLOCKS;      // rows per step
+    constexpr int WMAX = HT * 16 * NSET;             // tile columns at most
+    constexpr int OP = WMAX + 4;                     // LDS tile pitch in floats (4 spare columns)
+    constexpr int NSR = R / kWaves * WMAX / 64;      // 4-byte store rounds per wave and step at most
+    __shared__ __align__(16) float otile[2][R * OP];
+    const int q_tile = kv0 * a.G + (a.per_head ? minor : minor * 16 * NSET);   // first head of the tile
+    const int W = HT * nq;
+    const int VE = a.vec4 ? 4 : 1;
+    const int WQ = W / VE;                           // lanes per tile row
+    const int nsr = a.vec4 ? NSET : (R / kWaves * W + 63) / 64;   // store rounds per step
+    const int srow = a.Hq * 4;
+    const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
+        a.scores + (static_cast<size_t>(b) * a.C + r0) * a.Hq + q_tile, 0,
+        (nrows - 1) * srow + 4 * ((HT - 1) * a.G + nq), kRawBufferFlags);
+    int st_lds[NSR], st_off[NSR];
+#pragma unroll
+    for (int k = 0; k < NSR; ++k) {
+        const int e = 64 * k + lane;
+        const int rq = e / WQ, c = (e - rq * WQ) * VE;
+        const int r = kWaves * rq + wave;            // tile row
+        const int kc = c / nq;                       // KV head of column c inside the tile
+        const bool ok = r < R;
+        st_lds[k] = ok ? r * OP + c : 0;
+        st_off[k] = ok ? r * srow + 4 * (kc * a.G + c - kc * nq) : kOutOfRange;
+    }
+    // This lane's tile column for head m + 16 s (a spare column past the
+    // tile's heads when m + 16 s >= nq).
+    int o_col[NSET];
+#pragma unroll
+    for (int s = 0; s < NSET; ++s) o_col[s] = m + 16 * s < nq ? kvl * nq + m + 16 * s : WMAX + (m & 3);
 
     // q operand, once per wave. Heads past nq read the tile's last head (a
     // valid address); their result columns are never stored.
@@ -213,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void qk_scores(QkArgs a) {
                 bf.raw[u][i] = __builtin_amdgcn_raw_buffer_load_b128(kres, koff[i], 16 * block_of(st, u) * krow,
                                                                      kCachePolicyNt);
     };
-    auto compute_store = [&](const u32x4 (&bfin)[NLD], int j) {
+    auto compute_store = [&](const u32x4 (&bfin)[NLD], int j, int st, int tb) {
         // Re-layout through the wave's LDS region (in program order: one
         // wave's LDS operations execute in order).
         asm volatile("" ::: "memory");
@@ -270,20 +314,15 @@ __global__ __launch_bounds__(kThreads) void qk_scores(QkArgs a) {
                                                                             0, 0, 0);
             }
         }
+        // Into the step's LDS tile: row 16 (j - first block of the step) + 4 g + i.
+        float* const tile = otile[tb] + (16 * (j - st * GQA_QK_BLOCKS * WPH) + 4 * g) * OP;
 #pragma unroll
         for (int s = 0; s < NSET; ++s) {
             f32x4 sum = acc[0][s];
 #pragma unroll
             for (int k = 1; k < NACC; ++k) sum += acc[k][s];
-            const int h = m + 16 * s;
-            if (h < nq) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 16 * j + 4 * g + i;
-                    if (row < nrows)
-                        a.scores[(static_cast<size_t>(b) * a.C + r0 + row) * a.Hq + q_first + h] = sum[i] * out_scale[s];
-                }
-            }
+            for (int i = 0; i < 4; ++i) tile[i * OP + o_col[s]] = sum[i] * out_scale[s];
         }
     };
 
@@ -291,20 +330,36 @@ __global__ __launch_bounds__(kThreads) void qk_scores(QkArgs a) {
     // chunk read zeros and store nothing).
     const int nrb = (nrows + 15) / 16;
     const int nsteps = (nrb + WPH * UB - 1) / (WPH * UB);
-    auto consume = [&](const Buf& bf, int st) {
+    // Step st fills tile tb = st & 1; the barrier of step st + 1 comes after
+    // every wave's reads of tile tb, so step st + 2 may overwrite it.
+    auto consume = [&](const Buf& bf, int st, int tb) {
 #pragma unroll
-        for (int u = 0; u < UB; ++u) compute_store(bf.raw[u], block_of(st, u));
+        for (int u = 0; u < UB; ++u) compute_store(bf.raw[u], block_of(st, u), st, tb);
+        __syncthreads();
+        if (a.vec4) {
+#pragma unroll
+            for (int k = 0; k < NSET; ++k)
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(u32x4, *reinterpret_cast<const f32x4*>(&otile[tb][st_lds[k]])), sres,
+                    st_off[k], st * R * srow, 0);
+        } else {
+#pragma unroll
+            for (int k = 0; k < NSR; ++k)
+                if (k < nsr)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(otile[tb][st_lds[k]]), sres, st_off[k],
+                                                          st * R * srow, 0);
+        }
     };
     Buf bA, bB;
     int st = 0;
     if (nsteps > 0) load(bA, 0);
     for (; st + 1 < nsteps; st += 2) {
         load(bB, st + 1);
-        consume(bA, st);
+        consume(bA, st, 0);
         load(bA, st + 2);
-        consume(bB, st + 1);
+        consume(bB, st + 1, 1);
     }
-    if (st < nsteps) consume(bA, st);
+    if (st < nsteps) consume(bA, st, 0);
 }
 
 }  // namespace gqa_av

@@ -147,6 +147,25 @@ def test_qk_edges(oracle_lib):
     assert ei.value.name == "INELIGIBLE"
 
 
+@pytest.mark.parametrize("B,C,Hq,Hkv,D,dt,ht", [(2, 700, 16, 8, 128, "bf16", 4), (1, 333, 24, 8, 96, "f16", 4),
+                                               (2, 129, 16, 1, 64, "bf16", 1), (1, 200, 32, 8, 128, "f32", 2)])
+def test_qk_unaligned_scores(B, C, Hq, Hkv, D, dt, ht, oracle_lib):
+    """scores 4-byte but not 16-byte aligned (the 4-byte store path on shapes
+    that otherwise take 16-byte stores); the floats around it stay untouched."""
+    q, K = make_qk_random(B, C, Hq, Hkv, D, dt, seed=C + D)
+    ref = oracle_lib.qk(q, K, dt, 0.25)
+    n = B * C * Hq
+    buf = torch.full((n + 8,), 7.5, dtype=torch.float32, device=DEV)
+    sc = buf[1:1 + n].view(B, C, Hq)
+    assert sc.data_ptr() % 16 == 4
+    plan = ga.qk_make_plan(B, C, Hq, Hkv, D, dt, "auto", kv_tile=ht)
+    ga.gqa_qk_decode(q.to(DEV), K.to(DEV), scores=sc, scale=0.25, plan=plan)
+    torch.cuda.synchronize()
+    host = buf.cpu().numpy()
+    assert host[0] == 7.5 and (host[1 + n:] == 7.5).all()
+    assert_parity(host[1:1 + n].reshape(B, C, Hq).astype(np.float64), ref, dt, D, f"qk unaligned {(B, C, Hq, Hkv, D)}")
+
+
 def test_qk_then_av_matches_attention(oracle_lib):
     """Scores -> softmax over c -> attention-times-V on the GPU equals the
     oracles composed the same way (the two steps agree on the attn layout)."""

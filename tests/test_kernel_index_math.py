@@ -248,9 +248,10 @@ def test_valu_engine_plan_bounds(B, C, Hq, Hkv, D, dt):
 # ---- decode score step -------------------------------------------------------
 
 QK_BLOCKS = 1   # 16-row blocks per wave and buffer in the score kernel
+OUT_OF_RANGE = 0x40000000   # kOutOfRange: a buffer offset past every resource
 
 
-def _check_qk_plan(p, B, C, Hq, Hkv, D, dt, UB=QK_BLOCKS):
+def _check_qk_plan(p, B, C, Hq, Hkv, D, dt, UB=QK_BLOCKS, vec4=False):
     es, G = _esize(dt), Hq // Hkv
     per_head = p.mode == 0
     NBLK = D // 32
@@ -305,13 +306,56 @@ def _check_qk_plan(p, B, C, Hq, Hkv, D, dt, UB=QK_BLOCKS):
                     f = 64 * i + lanes
                     off = (f // NP) * krow + kvl * D * es + (f % NP) * 16 + 16 * j * krow
                     assert np.array_equal(off + 16 <= krec, (16 * j + f // NP) < nrows)
-                if step < nsteps:
+        # Scores: each step's LDS tile (R rows x W columns), filled by the
+        # waves, then stored with unconditional stores that the score
+        # resource masks: row r by wave r % 4, VE heads per lane.
+        R, WMAX = 16 * WPH * UB, HT * 16 * (1 if per_head else NSET)
+        OP, NSR = WMAX + 4, R // 4 * WMAX // 64
+        nq = 1 if per_head else min(16 * NSET, G - minor * 16 * NSET)
+        q_tile = kv0 * G + (minor if per_head else minor * 16 * NSET)
+        W, srow = HT * nq, 4 * Hq
+        sbase = ((b * C + r0) * Hq + q_tile) * 4
+        srec = (nrows - 1) * srow + 4 * ((HT - 1) * G + nq)
+        assert sbase + srec <= 4 * B * C * Hq and srec <= 2 ** 30
+        VE = 4 if vec4 else 1
+        nsr = (1 if per_head else NSET) if vec4 else -(-(R // 4 * W) // 64)
+        assert nsr <= NSR
+        for step in range(nsteps):
+            tile = {}
+            for wave in range(4):
+                kvl, wh = wave // WPH, wave % WPH
+                for u in range(UB):
+                    j = (step * UB + u) * WPH + wh
                     for s in range(NSET):
                         h = m + 16 * s
+                        col = np.where(h < nq, kvl * nq + h, WMAX + (m & 3))
                         for i in range(4):
-                            row = 16 * j + 4 * g + i
-                            ok = (h < nq) & (row < nrows)
-                            np.add.at(written, (b, r0 + row[ok], q_first + h[ok]), 1)
+                            r = 16 * (j - step * UB * WPH) + 4 * g + i
+                            assert r.max() < R and col.max() < OP
+                            for rr, cc, hh in zip(r, col, h):
+                                if hh < nq:
+                                    assert (rr, cc) not in tile
+                                    tile[(rr, cc)] = (16 * j + rr - 16 * (j - step * UB * WPH),
+                                                      (kv0 + kvl) * G + (minor if per_head else minor * 16 * NSET) + hh)
+            for wave in range(4):
+                for k in range(nsr):
+                    e = 64 * k + lanes
+                    rq, c = e // (W // VE), (e % (W // VE)) * VE
+                    r = 4 * rq + wave
+                    kc = c // nq
+                    ok = r < R
+                    lds = np.where(ok, r * OP + c, 0)
+                    assert (lds + VE <= R * OP).all() and (lds % VE == 0).all()
+                    off = np.where(ok, r * srow + 4 * (kc * G + c - kc * nq), OUT_OF_RANGE) + step * R * srow
+                    assert off.max() < 2 ** 31
+                    inr = off + 4 * VE <= srec
+                    assert np.array_equal(inr, ok & (step * R + r < nrows))
+                    for rr, cc, oo in zip(r[inr], c[inr], off[inr]):
+                        assert (sbase + oo) % (4 * VE) == 0
+                        for v in range(VE):
+                            row, head = tile[(rr, cc + v)]
+                            assert (sbase + oo) // 4 + v == (b * C + r0 + row) * Hq + head
+                            written[b, r0 + row, head] += 1
     assert (written == 1).all()
 
 
@@ -327,7 +371,11 @@ def test_qk_plan_bounds(B, C, Hq, Hkv, D, dt):
                 if ht > 1 and (Hkv % ht or mode == "per_head" or Hq // Hkv < 2):
                     continue
                 p = ga.qk_make_plan(B, C, Hq, Hkv, D, dt, mode, rows_per_block=rows, kv_tile=ht)
-                _check_qk_plan(p, B, C, Hq, Hkv, D, dt)
+                # 16-byte score stores when the host would choose them (scores
+                # 16-byte aligned), 4-byte stores always possible
+                v4 = p.mode == 1 and p.subgroups == 1 and (p.kv_heads_per_tile * (Hq // Hkv)) % 4 == 0 and Hq % 4 == 0
+                for vec4 in ((False, True) if v4 else (False,)):
+                    _check_qk_plan(p, B, C, Hq, Hkv, D, dt, vec4=vec4)
 
 
 @pytest.mark.parametrize("D,dt", [(32, "bf16"), (96, "f16"), (128, "bf16"), (160, "f32"), (256, "f32"), (224, "f16")])

@@ -8,7 +8,9 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 introduction, with a batch index added): fp64 sums over context positions c of
 exact fp32 x V products, kv_h = floor(q_h / G). It also holds the decode score
 step that precedes it (not on the page: scale * sum over d of q * K with the
-same head grouping, output in the attn layout). ``brute.py`` holds
+same head grouping, output in the attn layout) and the fused product that
+takes the scores and applies the softmax over c itself (the page's attn is
+that softmax). ``brute.py`` holds
 pure-Python correctly rounded versions of both for tiny shapes. Every function here is
 pinned by ``tests/test_oracle_pins.py``; none is "parity unpinned".
 """
@@ -57,6 +59,8 @@ class Oracle:
         lib.gqa_av_oracle_decode.restype = ip
         lib.gqa_qk_oracle.argtypes = [vp, vp, ip, i64, i64, i64, i64, i64, ctypes.c_double, vp, ip]
         lib.gqa_qk_oracle.restype = ip
+        lib.gqa_softmax_av_oracle.argtypes = [vp, vp, ip, i64, i64, i64, i64, i64, vp, ip]
+        lib.gqa_softmax_av_oracle.restype = ip
         self.lib = lib
 
     @staticmethod
@@ -90,6 +94,19 @@ class Oracle:
         out = np.empty((B, C, Hq), dtype=np.float64)
         rc = self.lib.gqa_qk_oracle(qa.ctypes.data, k.ctypes.data, DTYPE_CODE[k_dtype],
                                     B, C, Hq, Hkv, D, float(scale), out.ctypes.data, nthreads)
+        if rc != 0:
+            raise ValueError(f"oracle rejected the arguments (status {rc})")
+        return out
+
+    def softmax_av(self, scores, V, v_dtype: str, nthreads: int = 0) -> np.ndarray:
+        """out[B, Hq, D] (float64): softmax over c of scores [B,C,Hq] fp32, times V."""
+        a, v = self._np_inputs(scores, V, v_dtype)
+        B, C, Hq = a.shape
+        _, C2, Hkv, D = v.shape
+        assert C2 == C and v.shape[0] == B
+        out = np.empty((B, Hq, D), dtype=np.float64)
+        rc = self.lib.gqa_softmax_av_oracle(a.ctypes.data, v.ctypes.data, DTYPE_CODE[v_dtype],
+                                            B, C, Hq, Hkv, D, out.ctypes.data, nthreads)
         if rc != 0:
             raise ValueError(f"oracle rejected the arguments (status {rc})")
         return out

@@ -39,6 +39,19 @@
  * with q [B][Hq][D] float32, K [B][C][Hkv][D] of the given dtype and scores
  * [B][C][Hq] double. Each product is exact in double, the sum runs in double
  * in increasing d, and the scale multiplies the sum.
+ *
+ * The fused variant takes the scores instead of the weights: the page's attn
+ * is a softmax over the context of the scores, and the fused product applies
+ * that softmax itself,
+ *
+ *   out[b, q_h, d] = sum_c p[b, c, q_h] * V[b, c, kv_h(q_h), d]
+ *   p[b, c, q_h]   = exp(s[b, c, q_h] - m) / sum_{c'} exp(s[b, c', q_h] - m)
+ *   m              = max_c s[b, c, q_h]
+ *
+ * with s [B][C][Hq] float32. Written out in double: the maximum, then
+ * e_c = exp(s_c - m) (libm), the sums of e_c * V and of e_c in increasing c,
+ * and one division at the end. C = 0 gives zeros (an empty sum, as above); a
+ * row whose scores are all -inf gives NaN, as the definition does.
  */
 #include <math.h>
 #include <pthread.h>
@@ -217,6 +230,49 @@ int gqa_qk_oracle(const float *q, const void *K, int dtype,
 #endif
     for (int64_t i = 0; i < rows; ++i)
         orc_qk_row(q, K, dtype, C, Hq, Hkv, D, i / C, i % C, scale, out + i * Hq);
+    (void)nthreads;
+    return ORC_OK;
+}
+
+/* One output row of the fused softmax and AV product (see the header). */
+static void orc_sav_row(const float *scores, const void *V, int dtype,
+                        int64_t C, int64_t Hq, int64_t Hkv, int64_t D,
+                        int64_t b, int64_t q, double *acc)
+{
+    const int64_t G = Hq / Hkv;
+    const int64_t kv = q / G;
+    for (int64_t d = 0; d < D; ++d) acc[d] = 0.0;
+    if (C == 0) return;
+    double m = -INFINITY;
+    for (int64_t c = 0; c < C; ++c) {
+        const double s = (double)scores[(b * C + c) * Hq + q];
+        if (s > m) m = s;
+    }
+    double l = 0.0;
+    for (int64_t c = 0; c < C; ++c) {
+        const double e = exp((double)scores[(b * C + c) * Hq + q] - m);
+        l += e;
+        const int64_t row = ((b * C + c) * Hkv + kv) * D;
+        for (int64_t d = 0; d < D; ++d) acc[d] += e * orc_load(V, dtype, row + d);
+    }
+    for (int64_t d = 0; d < D; ++d) acc[d] /= l;
+}
+
+/* Full fused output: out[B][Hq][D] in double. nthreads <= 0 uses the OpenMP default. */
+int gqa_softmax_av_oracle(const float *scores, const void *V, int dtype,
+                          int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D,
+                          double *out, int nthreads)
+{
+    int rc = orc_check(dtype, B, C, Hq, Hkv, D);
+    if (rc != ORC_OK) return rc;
+    pthread_once(&orc_f16_once, orc_f16_fill);
+    const int64_t rows = B * Hq;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int64_t i = 0; i < rows; ++i)
+        orc_sav_row(scores, V, dtype, C, Hq, Hkv, D, i / Hq, i % Hq, out + i * D);
     (void)nthreads;
     return ORC_OK;
 }

@@ -35,6 +35,22 @@ The score step (scores = scale * q . K over d, in the attn layout):
                       pins that the scores come out in the attn layout.
   * qk_edges          C = 0 and B = 0 give empty results; Hq % Hkv != 0 is
                       rejected; D = 1.
+
+The fused softmax product (out = softmax over c of the scores, times V):
+  * sav_library       scipy's softmax over c in fp64, then numpy's einsum with
+                      V repeated along the heads: an independent route.
+  * sav_shift         adding a constant to every score of a row changes
+                      nothing (dyadic scores, so the shifted scores are exact).
+  * sav_large         scores near 8192 (where exp without the max overflows)
+                      equal the same scores shifted down by 8192.
+  * sav_one_hot       one score 800 above the rest returns that V row exactly.
+  * sav_uniform       equal scores give the mean of the V rows over c.
+  * sav_two_rows      C = 2: the logistic closed form.
+  * sav_mask          -inf scores drop their rows: the result equals the
+                      oracle over the remaining rows, bit for bit.
+  * sav_repeat_mha    GQA equals MHA over V repeated G times (bitwise).
+  * sav_edges         C = 0 gives zeros; a row of all -inf gives NaN; B = 0
+                      gives an empty result.
 """
 from __future__ import annotations
 
@@ -44,7 +60,7 @@ import numpy as np
 import torch
 
 from oracle.brute import abs_sum, abs_sum_qk, brute_force, brute_force_qk
-from workloads import make_qk_random, make_random
+from workloads import make_qk_random, make_random, make_scores_random
 
 U64 = 2.0 ** -53
 
@@ -344,7 +360,125 @@ def pin_qk_edges(orc):
     assert np.array_equal(o[0, :, 1], 2.0 * q[0, 1, 0].item() * K[0, :, 0, 0].double().numpy()), "qk D = 1"
 
 
+def _repeat_ref(p: np.ndarray, V: torch.Tensor, Hq: int) -> np.ndarray:
+    """sum_c p[b, c, h] * V[b, c, h // G, :] in numpy fp64 (V repeated along heads)."""
+    Hkv = V.shape[2]
+    Vr = np.repeat(V.double().numpy(), Hq // Hkv, axis=2)      # [B, C, Hq, D]
+    return np.einsum("bch,bchd->bhd", p, Vr)
+
+
+def _dyadic(x: torch.Tensor, bits: int = 8) -> torch.Tensor:
+    return torch.round(x * 2 ** bits) / 2 ** bits
+
+
+def pin_sav_library(orc):
+    from scipy.special import softmax
+    for i, (B, C, Hq, Hkv, D, dt, std) in enumerate([(2, 37, 6, 2, 5, "f32", 1.0), (1, 64, 8, 1, 16, "bf16", 3.0),
+                                                     (2, 19, 9, 3, 7, "f16", 0.5), (1, 1, 2, 2, 3, "f32", 1.0)]):
+        s, V = make_scores_random(B, C, Hq, Hkv, D, dt, seed=700 + i, score_std=std)
+        p = softmax(s.double().numpy(), axis=1)
+        ref = _repeat_ref(p, V, Hq)
+        o = orc.softmax_av(s, V, dt)
+        scale = _repeat_ref(p, V.abs() if dt == "f32" else V.float().abs(), Hq)
+        assert (np.abs(o - ref) <= 64 * C * U64 * (scale + np.abs(ref)) + 1e-300).all(), f"sav library {B, C, Hq, Hkv, D, dt}"
+
+
+def pin_sav_shift(orc):
+    s, V = make_scores_random(2, 45, 4, 2, 6, "bf16", seed=711, score_std=2.0)
+    s = _dyadic(s)
+    a = orc.softmax_av(s, V, "bf16")
+    b = orc.softmax_av(s + 64.0, V, "bf16")
+    c = orc.softmax_av(s - 40.0, V, "bf16")
+    ref = np.abs(a).max()
+    assert np.abs(a - b).max() <= 1e-13 * ref and np.abs(a - c).max() <= 1e-13 * ref, "sav: not shift invariant"
+
+
+def pin_sav_large(orc):
+    s, V = make_scores_random(1, 50, 6, 3, 4, "f32", seed=713, score_std=3.0)
+    s = _dyadic(s)
+    a = orc.softmax_av(s, V, "f32")
+    b = orc.softmax_av(s + 8192.0, V, "f32")
+    assert np.isfinite(b).all(), "sav: large scores overflow"
+    assert np.abs(a - b).max() <= 1e-13 * np.abs(a).max(), "sav: large scores differ from shifted ones"
+
+
+def pin_sav_one_hot(orc):
+    for dt in ("f32", "bf16", "f16"):
+        B, C, Hq, Hkv, D = 2, 17, 6, 2, 5
+        s, V = make_scores_random(B, C, Hq, Hkv, D, dt, seed=717)
+        G = Hq // Hkv
+        pick = {}
+        for b in range(B):
+            for h in range(Hq):
+                c = (3 * b + 5 * h + 2) % C
+                s[b, c, h] = 800.0
+                pick[b, h] = c
+        o = orc.softmax_av(s, V, dt)
+        Vd = V.double().numpy()
+        for (b, h), c in pick.items():
+            assert np.array_equal(o[b, h], Vd[b, c, h // G]), f"sav one-hot {dt} b={b} h={h}"
+
+
+def pin_sav_uniform(orc):
+    for dt in ("f32", "f16"):
+        B, C, Hq, Hkv, D = 2, 23, 4, 2, 3
+        _, V = make_scores_random(B, C, Hq, Hkv, D, dt, seed=719)
+        s = torch.full((B, C, Hq), 1.5)
+        o = orc.softmax_av(s, V, dt)
+        Vd = V.double().numpy()
+        for b in range(B):
+            for h in range(Hq):
+                for d in range(D):
+                    mean = math.fsum(Vd[b, :, h // (Hq // Hkv), d]) / C
+                    assert abs(o[b, h, d] - mean) <= 1e-14 * max(1.0, abs(mean)), f"sav uniform {dt}"
+
+
+def pin_sav_two_rows(orc):
+    s, V = make_scores_random(3, 2, 4, 1, 5, "bf16", seed=723, score_std=2.0)
+    o = orc.softmax_av(s, V, "bf16")
+    Vd, sd = V.double().numpy(), s.double().numpy()
+    for b in range(3):
+        for h in range(4):
+            x = sd[b, 0, h] - sd[b, 1, h]
+            w0 = 1.0 / (1.0 + math.exp(-x))
+            w1 = 1.0 / (1.0 + math.exp(x))
+            ref = w0 * Vd[b, 0, 0] + w1 * Vd[b, 1, 0]
+            assert np.abs(o[b, h] - ref).max() <= 1e-14 * max(1.0, np.abs(ref).max()), "sav two rows"
+
+
+def pin_sav_mask(orc):
+    B, C, Hq, Hkv, D = 1, 30, 4, 2, 6
+    s, V = make_scores_random(B, C, Hq, Hkv, D, "f32", seed=727)
+    keep = [c for c in range(C) if c % 3 != 1]
+    for h in range(Hq):
+        sm = s.clone()
+        sm[:, [c for c in range(C) if c % 3 == 1], :] = float("-inf")
+        a = orc.softmax_av(sm, V, "f32")
+        b = orc.softmax_av(s[:, keep].contiguous(), V[:, keep].contiguous(), "f32")
+        assert np.array_equal(a, b), "sav: -inf scores must drop their rows"
+
+
+def pin_sav_repeat_mha(orc):
+    for dt, (Hq, Hkv) in (("bf16", (8, 2)), ("f16", (6, 3)), ("f32", (5, 1))):
+        s, V = make_scores_random(2, 13, Hq, Hkv, 7, dt, seed=729)
+        Vrep = V.repeat_interleave(Hq // Hkv, dim=2).contiguous()
+        assert np.array_equal(orc.softmax_av(s, V, dt), orc.softmax_av(s, Vrep, dt)), f"sav: GQA != MHA ({dt})"
+
+
+def pin_sav_edges(orc):
+    o = orc.softmax_av(torch.zeros(2, 0, 4), torch.zeros(2, 0, 2, 3, dtype=torch.bfloat16), "bf16")
+    assert o.shape == (2, 4, 3) and (o == 0).all(), "sav: C = 0 must give zeros"
+    o = orc.softmax_av(torch.zeros(0, 5, 4), torch.zeros(0, 5, 2, 3), "f32")
+    assert o.shape == (0, 4, 3)
+    s, V = make_scores_random(1, 6, 2, 1, 3, "f32", seed=731)
+    s[0, :, 1] = float("-inf")
+    o = orc.softmax_av(s, V, "f32")
+    assert np.isnan(o[0, 1]).all() and np.isfinite(o[0, 0]).all(), "sav: a row of all -inf gives NaN"
+
+
 ALL_PINS = [pin_decode_table, pin_brute_force, pin_mha_einsum, pin_repeat_mha, pin_constant_v,
             pin_one_hot, pin_linearity, pin_permutation, pin_batch_independence, pin_points,
             pin_edges, pin_qk_brute_force, pin_qk_mha_einsum, pin_qk_repeat_mha, pin_qk_one_hot,
-            pin_qk_scale_linear, pin_qk_composition, pin_qk_edges]
+            pin_qk_scale_linear, pin_qk_composition, pin_qk_edges, pin_sav_library, pin_sav_shift,
+            pin_sav_large, pin_sav_one_hot, pin_sav_uniform, pin_sav_two_rows, pin_sav_mask,
+            pin_sav_repeat_mha, pin_sav_edges]

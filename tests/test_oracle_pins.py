@@ -49,6 +49,18 @@ PLANTS = [
      "orc_qk_row(q, K, dtype, C, Hq, Hkv, D, i % B, i / B, scale, out + i * Hq);"),
     ("qk_k_ignores_batch", "const int64_t krow = ((b * C + c) * Hkv + kvh) * D;",
      "const int64_t krow = ((0 * C + c) * Hkv + kvh) * D;"),
+    ("sav_no_max", "const double e = exp((double)scores[(b * C + c) * Hq + q] - m);",
+     "const double e = exp((double)scores[(b * C + c) * Hq + q]);"),
+    ("sav_normalise_by_C", "for (int64_t d = 0; d < D; ++d) acc[d] /= l;",
+     "for (int64_t d = 0; d < D; ++d) acc[d] /= (double)C;"),
+    ("sav_scores_transposed", "const double e = exp((double)scores[(b * C + c) * Hq + q] - m);",
+     "const double e = exp((double)scores[(b * Hq + q) * C + c] - m);"),
+    ("sav_kv_mod", "const int64_t kv = q / G;\n    for (int64_t d = 0; d < D; ++d) acc[d] = 0.0;\n    if (C == 0) return;",
+     "const int64_t kv = q % Hkv;\n    for (int64_t d = 0; d < D; ++d) acc[d] = 0.0;\n    if (C == 0) return;"),
+    ("sav_drop_last_row", "for (int64_t c = 0; c < C; ++c) {\n        const double e",
+     "for (int64_t c = 0; c < C - 1; ++c) {\n        const double e"),
+    ("sav_weight_sum_squared", "l += e;", "l += e * e;"),
+    ("sav_max_is_first", "if (s > m) m = s;", "if (c == 0) m = s;"),
 ]
 
 

@@ -11,6 +11,8 @@ high-ratio MQA cases its dispatch bullet discusses.
 
 Layouts (dense, row-major):
   attn [B, C, Hq]      float32, softmax over c of Gaussian logits
+                       (make_scores hands over the logits themselves, the
+                       input of the fused softmax product)
   V    [B, C, Hkv, D]  float32 / float16 / bfloat16 (drawn in fp32, rounded RNE)
 
 Draw order on one CPU ``torch.Generator`` seeded with ``seed``: V values, then
@@ -120,8 +122,8 @@ def _softmax_over_c(logits: torch.Tensor) -> torch.Tensor:
     return (e / e.sum(dim=1, keepdim=True)).to(torch.float32)
 
 
-def make_inputs(w: Workload, seed: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Draw (attn, V) on the CPU for workload ``w`` with a fixed draw order."""
+def _draw(w: Workload, seed: int) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(logits [B, C, Hq] fp32, V) for workload ``w`` in the fixed draw order."""
     g = torch.Generator(device="cpu").manual_seed(seed)
     nv = w.B * w.C * w.Hkv * w.D
     if w.v_dist == "uniform":
@@ -140,8 +142,28 @@ def make_inputs(w: Workload, seed: int = 0) -> Tuple[torch.Tensor, torch.Tensor]
         rows = torch.randperm(nrows, generator=g)[:k]
         v.view(nrows, w.D)[rows] *= w.outlier_scale
     V = v.view(w.B, w.C, w.Hkv, w.D).to(w.v_torch_dtype)
+    return logits.contiguous(), V.contiguous()
+
+
+def make_inputs(w: Workload, seed: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Draw (attn, V) on the CPU for workload ``w`` with a fixed draw order."""
+    logits, V = _draw(w, seed)
     attn = _softmax_over_c(logits) if w.C > 0 else logits
-    return attn.contiguous(), V.contiguous()
+    return attn.contiguous(), V
+
+
+def make_scores(w: Workload, seed: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(scores, V) for the fused softmax product: the same draws as make_inputs,
+    with the logits handed over as they are (no softmax)."""
+    return _draw(w, seed)
+
+
+def make_scores_random(B: int, C: int, Hq: int, Hkv: int, D: int, v_dtype: str, seed: int = 0,
+                       score_std: float = 1.0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Small ad-hoc shapes for the fused product: V ~ N(0,1), scores ~ N(0, score_std^2)."""
+    w = Workload(f"adhoc-b{B}-c{C}-hq{Hq}-hkv{Hkv}-d{D}-{v_dtype}", B=B, C=C, Hq=Hq, Hkv=Hkv, D=D,
+                 v_dtype=v_dtype, v_dist="normal", logit_std=score_std)
+    return _draw(w, seed)
 
 
 def make_random(B: int, C: int, Hq: int, Hkv: int, D: int, v_dtype: str,

@@ -45,8 +45,10 @@ KERNEL_SOURCES = {
     "qk": [os.path.join(ROOT, "gqa_reuse_attn_amd", "csrc", f) for f in ("av_kernels.hpp", "qk_kernels.hpp",
                                                                        "qk_host.hpp")],
 }
+KERNEL_SOURCES["softmax"] = KERNEL_SOURCES["av"]
 # Profile file prefix and the dominant kernel's name fragment, per operation.
-OPS = {"av": ("pass1", "pass1"), "qk": ("qk", "qk_scores")}
+OPS = {"av": ("pass1", "pass1"), "qk": ("qk", "qk_scores"), "softmax": ("softmax_pass1", "pass1")}
+SOFTMAX_METRIC = "GQA decode fused softmax x V: µs/call and achieved HBM GB/s (% of MI355X peak)"
 
 
 def source_hash(op: str = "av") -> str:
@@ -61,8 +63,9 @@ def source_hash(op: str = "av") -> str:
 def parse():
     p = argparse.ArgumentParser(description=__doc__.splitlines()[1])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--op", default="av", choices=["av", "qk"],
-                   help="av: attention-times-V (the headline); qk: the decode score step before it")
+    p.add_argument("--op", default="av", choices=["av", "qk", "softmax"],
+                   help="av: attention-times-V (the headline); qk: the decode score step before it; "
+                        "softmax: the fused softmax x V product on the scores")
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=-1,
                    help="untimed warmup steps; -1 (default): at least 20 and about 0.25 s of GPU work, "
@@ -176,15 +179,16 @@ def copy_calibration(mib: float):
 
 # ---- CPU baseline ---------------------------------------------------------------
 
-def cpu_baseline(w, attn, V, budget_s: float):
+def cpu_baseline(w, attn, V, budget_s: float, softmax: bool = False):
     """The CPU oracle (fp64, OpenMP) on the same workload, repeated for ~budget_s."""
     import oracle
     orc = oracle.get()
     threads = int(os.environ.get("OMP_NUM_THREADS") or 0) or len(os.sched_getaffinity(0))
+    fn = orc.softmax_av if softmax else orc.full
     reps = 0
     t0 = time.perf_counter()
     while True:
-        orc.full(attn, V, w.v_dtype, nthreads=threads)
+        fn(attn, V, w.v_dtype, nthreads=threads)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or reps >= 1000:
@@ -196,7 +200,8 @@ def cpu_baseline(w, attn, V, budget_s: float):
         "us_per_call": round(per_call * 1e6, 1),
         "cores": threads,
         "kind": "oracle",
-        "sample": f"full workload {w.name}, {reps} calls in {el:.1f} s (fp64 C oracle, OpenMP)",
+        "sample": f"full workload {w.name}{' (fused softmax)' if softmax else ''}, {reps} calls in {el:.1f} s "
+                  "(fp64 C oracle, OpenMP)",
     }
 
 
@@ -328,10 +333,15 @@ def main():
         bench_qk(args, w, dev, props)
         return
 
-    attn_h, V_h = make_inputs(w, seed=0)
+    softmax = args.op == "softmax"
+    if softmax:
+        from workloads import make_scores
+        attn_h, V_h = make_scores(w, seed=0)        # the workload's logits, as scores
+    else:
+        attn_h, V_h = make_inputs(w, seed=0)
     plan = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, args.mode, nsplit=args.nsplit,
                         engine=args.engine, combine=args.combine, kv_tile=args.kv_tile,
-                        cu_count=props.multi_processor_count)
+                        cu_count=props.multi_processor_count, softmax=softmax)
     per_set = w.v_bytes() + w.attn_bytes() + w.out_bytes()
     nrot = max(1, math.ceil(args.rotate_mb * 2 ** 20 / per_set))
     sets = []
@@ -341,7 +351,7 @@ def main():
         v = v0 if i == 0 else v0.clone()
         sets.append((a, v, torch.empty(w.B, w.Hq, w.D, device=dev)))
     torch.cuda.synchronize()
-    calls = [ga.bind(a, v, o, plan=plan) for a, v, o in sets]
+    calls = [(ga.bind_softmax if softmax else ga.bind)(a, v, o, plan=plan) for a, v, o in sets]
     stream = torch.cuda.current_stream(dev)
 
     _warm(args, calls, nrot)
@@ -368,13 +378,13 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w, attn_h, V_h, args.cpu_seconds)
+        cpu = cpu_baseline(w, attn_h, V_h, args.cpu_seconds, softmax=softmax)
 
     split_kernel = plan.nsplit > 1 and plan.combine == 1
-    traffic = recorded_traffic(w.name, args.mode, "av") if (args.nsplit == 0 and args.engine == "auto"
-                                                      and args.combine == "auto" and args.kv_tile == 0) else None
+    traffic = recorded_traffic(w.name, args.mode, args.op) if (args.nsplit == 0 and args.engine == "auto"
+                                                             and args.combine == "auto" and args.kv_tile == 0) else None
     line = {
-        "metric": METRIC,
+        "metric": SOFTMAX_METRIC if softmax else METRIC,
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -388,7 +398,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": w.name, "B": w.B, "C": w.C, "Hq": w.Hq, "Hkv": w.Hkv, "G": w.G, "D": w.D,
+            "workload": ("softmax:" if softmax else "") + w.name, "B": w.B, "C": w.C, "Hq": w.Hq, "Hkv": w.Hkv,
+            "G": w.G, "D": w.D,
             "v_dtype": w.v_dtype, "mode": args.mode, "algorithmic_bytes": w.algorithmic_bytes(),
             "rotation_sets": nrot, "kernels_per_call": 2 if split_kernel else 1, "plan": plan.as_dict(),
         },

@@ -8,6 +8,11 @@ head grouping, output in the attn layout):
 
     scores[b, c, q_h] = scale * sum_d q[b, q_h, d] * K[b, c, q_h // G, d]
 
+and the fused product that takes those scores and applies the softmax over c
+itself (the page's attn is that softmax):
+
+    out[b, q_h, d] = sum_c softmax_c(scores[b, :, q_h])[c] * V[b, c, q_h // G, d]
+
 Every step runs in the HIP library; this module only checks tensors and marshals
 pointers, sizes and the stream through ctypes. PyTorch provides device memory
 and streams. There is no CPU fallback: if the library is missing, calls raise.
@@ -21,7 +26,7 @@ from typing import Optional, Union
 __all__ = [
     "LIB_PATH", "GqaAvError", "Hint", "Plan", "load", "resolve_mode", "make_plan",
     "gqa_av_decode", "gqa_av_decode_plan", "bind", "BoundCall", "release", "status_string", "MODES", "DTYPES",
-    "QkHint", "QkPlan", "qk_make_plan", "gqa_qk_decode", "bind_qk",
+    "QkHint", "QkPlan", "qk_make_plan", "gqa_qk_decode", "bind_qk", "gqa_softmax_av_decode", "bind_softmax",
 ]
 
 # GQA_AV_LIBRARY may name another build of the same library (tuning variants).
@@ -44,7 +49,7 @@ class GqaAvError(RuntimeError):
 class Hint(ctypes.Structure):
     _fields_ = [("engine", ctypes.c_int32), ("nsplit", ctypes.c_int32), ("cu_count", ctypes.c_int32),
                 ("v_align", ctypes.c_int32), ("combine", ctypes.c_int32), ("kv_tile", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 2)]
+                ("softmax", ctypes.c_int32), ("reserved", ctypes.c_int32 * 1)]
 
 
 class Plan(ctypes.Structure):
@@ -53,7 +58,8 @@ class Plan(ctypes.Structure):
                 ("row_slots", ctypes.c_int32), ("d_tiles", ctypes.c_int32), ("nsplit", ctypes.c_int32),
                 ("threads", ctypes.c_int32), ("rows_per_split", ctypes.c_int64), ("grid", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_int64), ("v_bytes_read", ctypes.c_int64),
-                ("combine", ctypes.c_int32), ("kv_heads_per_tile", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2)]
+                ("combine", ctypes.c_int32), ("kv_heads_per_tile", ctypes.c_int32), ("softmax", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 1)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
@@ -102,6 +108,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     for fn in ("gqa_av_decode_plan", "gqa_av_decode_pass1", "gqa_av_decode_combine"):
         getattr(lib, fn).argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ip, ctypes.POINTER(Plan), vp]
         getattr(lib, fn).restype = ip
+    lib.gqa_softmax_av_decode.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ip, ip, vp]
+    lib.gqa_softmax_av_decode.restype = ip
+    for fn in ("gqa_softmax_av_decode_plan", "gqa_softmax_av_decode_pass1", "gqa_softmax_av_decode_combine"):
+        getattr(lib, fn).argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ip, ctypes.POINTER(Plan), vp]
+        getattr(lib, fn).restype = ip
     lib.gqa_av_status_string.argtypes = [ip]
     lib.gqa_av_status_string.restype = ctypes.c_char_p
     lib.gqa_av_last_error.argtypes = []
@@ -147,16 +158,17 @@ def resolve_mode(Hq: int, Hkv: int, mode: Union[str, int] = "auto") -> str:
 
 def make_plan(B: int, C: int, Hq: int, Hkv: int, D: int, v_dtype: str, mode: Union[str, int] = "auto",
               engine: Union[str, int] = "auto", nsplit: int = 0, cu_count: int = 0, v_align: int = 0,
-              combine: Union[str, int] = "auto", kv_tile: int = 0) -> Plan:
+              combine: Union[str, int] = "auto", kv_tile: int = 0, softmax: bool = False) -> Plan:
     """Host-only planning (no GPU needed). nsplit/cu_count/v_align/kv_tile <= 0 mean automatic.
 
-    engine: "auto" | "valu" | "mfma"; combine: "auto" | "kernel" | "last";
-    kv_tile: adjacent KV heads per VALU workgroup.
+    engine: "auto" | "valu" | "mfma" | "mfma_bf16"; combine: "auto" | "kernel" | "last";
+    kv_tile: adjacent KV heads per workgroup; softmax: plan the fused softmax product.
     """
     h = Hint()
     h.engine = ENGINES[engine] if isinstance(engine, str) else int(engine)
     h.combine = COMBINES[combine] if isinstance(combine, str) else int(combine)
     h.nsplit, h.cu_count, h.v_align, h.kv_tile = int(nsplit), int(cu_count), int(v_align), int(kv_tile)
+    h.softmax = 1 if softmax else 0
     p = Plan()
     rc = load().gqa_av_make_plan(B, C, Hq, Hkv, D, DTYPES[v_dtype], _mode(mode), ctypes.byref(h), ctypes.byref(p))
     if rc != 0:
@@ -236,7 +248,7 @@ class BoundCall:
     """
 
     def __init__(self, attn, V, out=None, plan: Optional[Plan] = None, mode: Union[str, int] = "auto",
-                 stream=None):
+                 stream=None, softmax: bool = False):
         torch = _torch()
         B, C, Hq, Hkv, D, vdt = _check(attn, V, out)
         if out is None:
@@ -247,12 +259,14 @@ class BoundCall:
             props = torch.cuda.get_device_properties(attn.device)
             addr = V.data_ptr()
             align = 16 if addr % 16 == 0 else (addr & -addr)
-            plan = make_plan(B, C, Hq, Hkv, D, vdt, mode, cu_count=props.multi_processor_count, v_align=align)
+            plan = make_plan(B, C, Hq, Hkv, D, vdt, mode, cu_count=props.multi_processor_count, v_align=align,
+                             softmax=softmax)
         self.attn, self.V, self.out, self.plan, self.stream = attn, V, out, plan, stream
         lib = load()
-        self._fn = lib.gqa_av_decode_plan
-        self._pass1 = lib.gqa_av_decode_pass1
-        self._combine = lib.gqa_av_decode_combine
+        pre = "gqa_softmax_av_decode" if plan.softmax else "gqa_av_decode"
+        self._fn = getattr(lib, pre + "_plan")
+        self._pass1 = getattr(lib, pre + "_pass1")
+        self._combine = getattr(lib, pre + "_combine")
         self._args = (attn.data_ptr(), V.data_ptr(), out.data_ptr(), B, C, Hq, Hkv, D, DTYPES[vdt],
                       ctypes.byref(plan), stream.cuda_stream)
 
@@ -279,6 +293,38 @@ class BoundCall:
 def bind(attn, V, out=None, plan: Optional[Plan] = None, mode: Union[str, int] = "auto", stream=None) -> BoundCall:
     """A BoundCall for (attn, V, out): see BoundCall."""
     return BoundCall(attn, V, out=out, plan=plan, mode=mode, stream=stream)
+
+
+def gqa_softmax_av_decode(scores, V, out=None, mode: Union[str, int] = "auto", stream=None,
+                          plan: Optional[Plan] = None):
+    """out[b,q_h,d] = sum_c softmax_c(scores[b,:,q_h])[c] * V[b,c,q_h//G,d] on the GPU; returns out.
+
+    scores: float32 [B,C,Hq] (the attn layout); V and the rest as gqa_av_decode.
+    plan: a make_plan(..., softmax=True) plan for the same problem.
+    """
+    torch = _torch()
+    B, C, Hq, Hkv, D, vdt = _check(scores, V, out)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=scores.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(scores.device)
+    lib = load()
+    with torch.cuda.device(scores.device):
+        if plan is None:
+            rc = lib.gqa_softmax_av_decode(scores.data_ptr(), V.data_ptr(), out.data_ptr(), B, C, Hq, Hkv, D,
+                                           DTYPES[vdt], _mode(mode), stream.cuda_stream)
+        else:
+            rc = lib.gqa_softmax_av_decode_plan(scores.data_ptr(), V.data_ptr(), out.data_ptr(), B, C, Hq, Hkv, D,
+                                                DTYPES[vdt], ctypes.byref(plan), stream.cuda_stream)
+    if rc != 0:
+        _raise(rc)
+    return out
+
+
+def bind_softmax(scores, V, out=None, plan: Optional[Plan] = None, mode: Union[str, int] = "auto",
+                 stream=None) -> BoundCall:
+    """A BoundCall of the fused softmax product for (scores, V, out)."""
+    return BoundCall(scores, V, out=out, plan=plan, mode=mode, stream=stream, softmax=True)
 
 
 def release() -> None:

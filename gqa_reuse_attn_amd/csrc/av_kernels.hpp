@@ -76,6 +76,14 @@ constexpr int mfma_unroll(int NB) { return NB > 16 ? (GQA_AV_MFMA_UNROLL + 1) / 
 
 enum : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
+// Fused softmax: a weight is exp2((s - r) * log2(e)) for a running maximum r of
+// the scores. The difference is taken first (exact when s and r are within a
+// factor of two), so the weight's error grows with s - r, not with s. exp2 is
+// the hardware's v_exp_f32 (about 1 ulp), whose results below 2^-126 may be
+// flushed to zero: a weight that small beside the maximum's 1 changes no fp32
+// result.
+constexpr float kLog2e = 1.4426950408889634f;
+
 template <int DT>
 constexpr int esize() { return DT == kF32 ? 4 : 2; }
 
@@ -94,6 +102,8 @@ struct Pass1Args {
     const uint8_t* V;       // [B][C][Hkv][D] of DT
     float* out;             // [B][Hq][D]
     float* part;            // combine in kernel: [tiles][nsplit][tile outputs]; else [nsplit][B][Hq][D]
+    float* stats;           // fused softmax with nsplit > 1: [nsplit][B][Hq] pairs (maximum score, weight sum),
+                            // 16-byte aligned
     uint32_t* counters;     // combine in kernel: [tiles], zero between calls
     int32_t combine;        // 1: last workgroup of a tile adds the splits; 0: second kernel
     int64_t C;
@@ -383,7 +393,15 @@ __device__ inline void combine_last(const Pass1Args& a, const Tile& T, const flo
 template <int GT>
 constexpr int padded_heads() { return GT <= 2 ? GT : (GT + 3) / 4 * 4; }
 
-template <int DT, int VB, int GT, int U>
+// SM: fused softmax. attn then holds raw scores s; a lane's weight for a row is
+// exp2((s - mx) log2 e) with mx the running maximum of the scores the lane has
+// seen (per head). When a step raises mx, the lane's accumulators and weight
+// sum are multiplied by exp2((old - new) log2 e) (skipped when no lane of the
+// wave saw a new maximum). At the end of the split the row slots are brought
+// to the workgroup's maximum before they are summed; the split's result is the
+// weighted sum divided by the weight sum, or, with several splits, the
+// unnormalised sum with its (maximum, weight sum) for the combine.
+template <int DT, int VB, int GT, int U, bool SM = false>
 __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
     constexpr int ES = esize<DT>();
     constexpr int E = VB / ES;
@@ -411,6 +429,7 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
 
     const int64_t cb = static_cast<int64_t>(T.s) * a.rows_per_split;
     const int64_t ce = min(a.C, cb + a.rows_per_split);
+    const int64_t nrows_split = ce - cb;
     const int R = rps * U;                           // rows per stage
 
     const size_t vrow = static_cast<size_t>(a.Hkv) * a.D * ES;   // bytes from row c to c+1
@@ -420,8 +439,16 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
     for (int g = 0; g < GT; ++g)
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[g][e] = 0.0f;
+    float mx[GT], lsum[GT];                          // SM: running maximum score and weight sum
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+        mx[g] = -INFINITY;
+        lsum[g] = 0.0f;
+    }
+    __shared__ float s_stat[2][4 * GT];              // SM: the workgroup's maximum and weight sum per head
 
 #if GQA_AV_VALU_STAGE_WEIGHTS
+    static_assert(!SM, "the fused softmax needs the per-lane weight path");
     const uint8_t* vbase = a.V + (static_cast<size_t>(T.b) * a.C * a.Hkv + T.kv + kvl) * a.D * ES
                                + static_cast<size_t>(lane_d) * VB;
     const int q_lo = T.q_first;                      // accumulator g is head q_lo + g (tiles of one KV head)
@@ -568,15 +595,57 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
             load_floats<GT>(wres, woff, row * a.Hq * 4, bf.w[u]);
         }
     };
-    auto compute = [&](const Buf& bf) {
+    auto compute = [&](const Buf& bf, int st) {
+        if constexpr (SM) {
+            // Rows past the split read as zero; they must not count as scores.
+            float x[U][GT], nm[GT];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float f[E];
-            widen<DT, VB>(bf.v[u], f);
+            for (int u = 0; u < U; ++u) {
+                const bool ok = st * R + u * rps + r < nrows;
 #pragma unroll
-            for (int g = 0; g < GT; ++g)
+                for (int g = 0; g < GT; ++g) x[u][g] = ok ? bf.w[u][g] : -INFINITY;
+            }
+            bool up = false;
 #pragma unroll
-                for (int e = 0; e < E; ++e) acc[g][e] = __builtin_fmaf(bf.w[u][g], f[e], acc[g][e]);
+            for (int g = 0; g < GT; ++g) {
+                float t = mx[g];
+#pragma unroll
+                for (int u = 0; u < U; ++u) t = fmaxf(t, x[u][g]);
+                nm[g] = t;
+                up |= t > mx[g];
+            }
+            if (__any(up)) {
+#pragma unroll
+                for (int g = 0; g < GT; ++g) {
+                    const float al = nm[g] > mx[g] ? __builtin_amdgcn_exp2f((mx[g] - nm[g]) * kLog2e) : 1.0f;
+#pragma unroll
+                    for (int e = 0; e < E; ++e) acc[g][e] *= al;
+                    lsum[g] *= al;
+                    mx[g] = nm[g];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float f[E];
+                widen<DT, VB>(bf.v[u], f);
+#pragma unroll
+                for (int g = 0; g < GT; ++g) {
+                    const float w = __builtin_amdgcn_exp2f((x[u][g] - (mx[g] == -INFINITY ? 0.0f : mx[g])) * kLog2e);
+                    lsum[g] += w;
+#pragma unroll
+                    for (int e = 0; e < E; ++e) acc[g][e] = __builtin_fmaf(w, f[e], acc[g][e]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float f[E];
+                widen<DT, VB>(bf.v[u], f);
+#pragma unroll
+                for (int g = 0; g < GT; ++g)
+#pragma unroll
+                    for (int e = 0; e < E; ++e) acc[g][e] = __builtin_fmaf(bf.w[u][g], f[e], acc[g][e]);
+            }
         }
     };
     if (active) {
@@ -587,14 +656,51 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
         if (nsteps > 0) load(bA, 0);
         for (; st + 1 < nsteps; st += 2) {
             load(bB, st + 1);
-            compute(bA);
+            compute(bA, st);
             load(bA, st + 2);
-            compute(bB);
+            compute(bB, st + 1);
         }
-        if (st < nsteps) compute(bA);
+        if (st < nsteps) compute(bA, st);
     }
 #endif
     __syncthreads();                                  // LDS is reused below
+
+    // SM: bring every row slot to the workgroup's maximum per (KV head of the
+    // tile, head): the first lane of each slot and KV head holds the slot's
+    // values (the other lanes of the slot saw the same rows and weights).
+    const int nst = a.ht * GT;                        // <= 4 GT: the plan keeps ht <= 4 here
+    if constexpr (SM) {
+        const bool lead = active && j - kvl * a.L == 0;
+        if (lead)
+#pragma unroll
+            for (int g = 0; g < GT; ++g) smem[(r * a.ht + kvl) * GT + g] = mx[g];
+        __syncthreads();
+        if (tid < nst) {
+            float M = -INFINITY;
+            for (int rr = 0; rr < rps; ++rr) M = fmaxf(M, smem[rr * nst + tid]);
+            s_stat[0][tid] = M;
+        }
+        __syncthreads();
+        if (active) {
+#pragma unroll
+            for (int g = 0; g < GT; ++g) {
+                const float al = mx[g] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((mx[g] - s_stat[0][kvl * GT + g]) * kLog2e);
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[g][e] *= al;
+                lsum[g] *= al;
+            }
+        }
+        if (lead)
+#pragma unroll
+            for (int g = 0; g < GT; ++g) smem[(r * a.ht + kvl) * GT + g] = lsum[g];
+        __syncthreads();
+        if (tid < nst) {
+            float L = 0.0f;
+            for (int rr = 0; rr < rps; ++rr) L += smem[rr * nst + tid];
+            s_stat[1][tid] = L;
+        }
+        __syncthreads();
+    }
 
     // Sum the row slots: slot kk of thread tid lives at smem[kk * 256 + tid].
     // Output slot k = g * E + e of lane chunk jj is tile output k * Lc + jj.
@@ -628,6 +734,12 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
             float sum = 0.0f;
             for (int rr = 0; rr < rps; ++rr) sum += smem[kk * kThreads + rr * Lc + jj];
             const int k = k0 + kk;
+            if constexpr (SM) {
+                // One split: normalise here (C = 0 gives zeros); several: the
+                // combine does, from the statistics written below.
+                if (a.nsplit == 1)
+                    sum = nrows_split > 0 ? sum / s_stat[1][(jj / a.L) * GT + k / E] : 0.0f;
+            }
             if (in_kernel) {
                 store_coherent(blk + static_cast<size_t>(T.s) * TOP + k * Lc + jj, sum);
             } else {
@@ -636,6 +748,18 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
             }
         }
         __syncthreads();
+    }
+    if constexpr (SM) {
+        if (a.nsplit > 1 && T.dt == 0 && tid < nst) {
+            const int kl = tid / GT, g = tid - kl * GT;
+            const int ql = lane_q_lo(kl);
+            const int go = T.q_first + kl * a.G - ql;
+            if (g >= go && g < go + T.nq) {
+                float* const st = a.stats + ((static_cast<size_t>(T.s) * a.B + T.b) * a.Hq + ql + g) * 2;
+                st[0] = s_stat[0][tid];
+                st[1] = s_stat[1][tid];
+            }
+        }
     }
     if (in_kernel) {
         combine_last(a, T, blk, TO, [&](int idx, float v) {
@@ -822,7 +946,13 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma(Pass1Args a) {
 // chunks of 32 rows per wave and buffer, two buffers in flight; HT adjacent
 // KV heads per workgroup (1, 2 or 4), each streamed by kWaves / HT waves, so
 // the workgroup reads HT * 2 D contiguous bytes of every row.
-template <int PR, int NSET, int U, int HT>
+//
+// SM: fused softmax (see av_pass1_valu). A wave keeps one running maximum per
+// head for its rows: the four lane groups holding a head's weights of a chunk
+// agree on the chunk's maximum through two lane exchanges, so every product
+// summed into one accumulator uses the same maximum. The waves of a KV head
+// are brought to their common maximum before they are added.
+template <int PR, int NSET, int U, int HT, bool SM = false>
 __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
     static_assert(PR == 8 || PR == 16 || PR == 32, "D must be 64, 128 or 256");
     static_assert(HT == 1 || HT == 2 || HT == 4, "KV heads per tile must divide the waves");
@@ -900,6 +1030,12 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
     for (int s = 0; s < NSET; ++s)
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[s][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float mx[NSET], lsum[NSET];                      // SM: head m + 16 s, this lane's rows (maximum score, weight sum)
+#pragma unroll
+    for (int s = 0; s < NSET; ++s) {
+        mx[s] = -INFINITY;
+        lsum[s] = 0.0f;
+    }
 
     constexpr int RSTEP = 32 * WPH * U;             // rows per workgroup step
     const int nsteps = (nrows + RSTEP - 1) / RSTEP;
@@ -924,7 +1060,7 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
                         __builtin_amdgcn_raw_buffer_load_b32(wres, wlane[s], (r0 + j) * a.Hq * 4, 0));
         }
     };
-    auto consume = [&](const Buf& bf) {
+    auto consume = [&](const Buf& bf, int st) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             // The region's previous contents have been read (in program
@@ -934,6 +1070,57 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
             for (int i = 0; i < LPI; ++i)
                 *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(region + st_off(i)) = bf.v[u][i];
             asm volatile("" ::: "memory");
+            float wt[NSET][8];
+            if constexpr (SM) {
+                // Scores of rows 8 g .. 8 g + 7 of the chunk; rows past the
+                // split read as zero and must not count.
+                const int rb = 32 * (st * WPH * U + u * WPH + wh) + 8 * g;
+                float nm[NSET];
+                bool up = false;
+#pragma unroll
+                for (int s = 0; s < NSET; ++s) {
+                    float t = -INFINITY;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        wt[s][j] = rb + j < nrows ? bf.w[u][s][j] : -INFINITY;
+                        t = fmaxf(t, wt[s][j]);
+                    }
+                    t = fmaxf(t, __shfl_xor(t, 16));
+                    t = fmaxf(t, __shfl_xor(t, 32));
+                    nm[s] = fmaxf(mx[s], t);
+                    up |= nm[s] > mx[s];
+                }
+                if (__any(up)) {
+#pragma unroll
+                    for (int s = 0; s < NSET; ++s) {
+                        const float al = nm[s] > mx[s] ? __builtin_amdgcn_exp2f((mx[s] - nm[s]) * kLog2e) : 1.0f;
+                        lsum[s] *= al;
+                        mx[s] = nm[s];
+                        // Register i of acc[s][t] belongs to head 16 s + 4 (lane / 16) + i,
+                        // whose factor lane 4 (lane / 16) + i holds.
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float ai = __shfl(al, 4 * (lane >> 4) + i);
+#pragma unroll
+                            for (int t = 0; t < NT; ++t) acc[s][t][i] *= ai;
+                        }
+                    }
+                }
+#pragma unroll
+                for (int s = 0; s < NSET; ++s) {
+                    const float ref = mx[s] == -INFINITY ? 0.0f : mx[s];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        wt[s][j] = __builtin_amdgcn_exp2f((wt[s][j] - ref) * kLog2e);
+                        lsum[s] += wt[s][j];
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < NSET; ++s)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) wt[s][j] = bf.w[u][s][j];
+            }
             // Split the weights: three bf16x8 A operands per head set.
             u32x4 aw[3][NSET];
 #pragma unroll
@@ -942,7 +1129,7 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
                 for (int p = 0; p < 4; ++p) {
                     uint32_t th[2], tm[2], tl[2];
 #pragma unroll
-                    for (int e = 0; e < 2; ++e) split_bf16x3(bf.w[u][s][2 * p + e], th[e], tm[e], tl[e]);
+                    for (int e = 0; e < 2; ++e) split_bf16x3(wt[s][2 * p + e], th[e], tm[e], tl[e]);
                     aw[0][s][p] = (th[0] >> 16) | th[1];
                     aw[1][s][p] = (tm[0] >> 16) | tm[1];
                     aw[2][s][p] = (tl[0] >> 16) | tl[1];
@@ -978,17 +1165,63 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
     if (nsteps > 0) load(bA, 0);
     for (; st + 1 < nsteps; st += 2) {
         load(bB, st + 1);
-        consume(bA);
+        consume(bA, st);
         load(bA, st + 2);
-        consume(bB);
+        consume(bB, st + 1);
     }
-    if (st < nsteps) consume(bA);
+    if (st < nsteps) consume(bA, st);
+
+    // SM: each wave's maximum and weight sum per head (lane group 0 holds head
+    // m + 16 s after the sum over the four lane groups).
+    constexpr int GH = 16 * NSET;
+    __shared__ float s_wm[kWaves][GH], s_wl[kWaves][GH], s_tm[HT][GH], s_tl[HT][GH];
+    if constexpr (SM) {
+#pragma unroll
+        for (int s = 0; s < NSET; ++s) {
+            lsum[s] += __shfl_xor(lsum[s], 16);
+            lsum[s] += __shfl_xor(lsum[s], 32);
+            if (g == 0) {
+                s_wm[wave][m + 16 * s] = mx[s];
+                s_wl[wave][m + 16 * s] = lsum[s];
+            }
+        }
+    }
 
     // Add the tiles of each KV head's waves. Register i of acc[s][t] in lane
     // l is head 16 s + 4 (l / 16) + i, column 16 t + l % 16; as an output
     // index of the KV head's tile: ((s * NT + t) * 4 + i) * 64 + l. The
     // workgroup's outputs are the HT heads' tiles one after another.
     __syncthreads();                                 // every wave is done with its region
+    if constexpr (SM) {
+        // Bring this wave's tile to the maximum of its KV head's waves.
+#pragma unroll
+        for (int s = 0; s < NSET; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int hh = 16 * s + 4 * (lane >> 4) + i;
+                float M = -INFINITY;
+#pragma unroll
+                for (int w = 0; w < WPH; ++w) M = fmaxf(M, s_wm[kvl * WPH + w][hh]);
+                const float mw = s_wm[wave][hh];
+                const float al = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((mw - M) * kLog2e);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) acc[s][t][i] *= al;
+            }
+        // The tile's maximum and weight sum per (KV head, head).
+        if (threadIdx.x < HT * GH) {
+            const int k = threadIdx.x / GH, hh = threadIdx.x % GH;
+            float M = -INFINITY, L = 0.0f;
+#pragma unroll
+            for (int w = 0; w < WPH; ++w) M = fmaxf(M, s_wm[k * WPH + w][hh]);
+#pragma unroll
+            for (int w = 0; w < WPH; ++w) {
+                const float mw = s_wm[k * WPH + w][hh];
+                L += mw == -INFINITY ? 0.0f : s_wl[k * WPH + w][hh] * __builtin_amdgcn_exp2f((mw - M) * kLog2e);
+            }
+            s_tm[k][hh] = M;
+            s_tl[k][hh] = L;
+        }
+    }
     float* const red = reinterpret_cast<float*>(smem);
 #pragma unroll
     for (int s = 0; s < NSET; ++s)
@@ -1014,11 +1247,29 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
         float sum = red[k * WPH * TO + e];
 #pragma unroll
         for (int w = 1; w < WPH; ++w) sum += red[(k * WPH + w) * TO + e];
+        if constexpr (SM) {
+            // One split: normalise here; several: the combine does.
+            if (a.nsplit == 1) {
+                const int reg = (e >> 6), h = 16 * ((reg >> 2) / NT) + 4 * ((e & 63) >> 4) + (reg & 3);
+                sum = nrows > 0 ? sum / s_tl[k][h] : 0.0f;
+            }
+        }
         if (in_kernel) {
             store_coherent(blk + static_cast<size_t>(T.s) * TOW + idx, sum);
         } else {
             size_t o;
             if (out_index(idx, &o)) plane[o] = sum;
+        }
+    }
+    if constexpr (SM) {
+        if (a.nsplit > 1 && threadIdx.x < HT * GH) {
+            const int k = threadIdx.x / GH, hh = threadIdx.x % GH;
+            if (hh < T.nq) {
+                float* const stp =
+                    a.stats + ((static_cast<size_t>(T.s) * a.B + T.b) * a.Hq + T.q_first + k * a.G + hh) * 2;
+                stp[0] = s_tm[k][hh];
+                stp[1] = s_tl[k][hh];
+            }
         }
     }
     if (in_kernel) {
@@ -1070,6 +1321,162 @@ __global__ __launch_bounds__(kThreads) void av_pass2_combine(const float* __rest
             for (int c = 0; c < 4; ++c)
                 if (i0 + c < plane) out[i0 + c] = t[c];
         }
+    }
+}
+
+// Fused softmax, several splits: split s left the unnormalised sum
+// part[s][b][q][d] = sum_c exp(s_c - m_s) V[c][d] over its rows and stats[s][b][q] =
+// (m_s, l_s), its maximum score and weight sum. With M = max_s m_s and
+// f_s = exp(m_s - M) (computed as exp2((m_s - M) log2 e)),
+//   out[b][q][d] = sum_s f_s part[s][b][q][d] / sum_s f_s l_s.
+// A split with m_s = -inf (all of its scores -inf) adds nothing; a row whose
+// scores are all -inf gives 0 / 0. Two kernels, each summing in a fixed order:
+//  * few splits (nsplit <= kCombineBatch): one thread per 4 outputs of a row,
+//    every split loaded at once, summed in increasing s;
+//  * more: one workgroup per (b, q), 8 split groups x 32 quad lanes, each group
+//    summing its contiguous split range in increasing order, then the groups in
+//    order (the association of av_pass2_combine). A group's loads run in
+//    batches of kCombineBatch independent splits; the first batch is in flight
+//    while the workgroup finds M.
+constexpr int kCombineBatch = 8;
+
+// Outputs d .. d + 3 of a D-long row (zeros past D). The address is clamped
+// into the row and the value masked afterwards, so the load never sits behind
+// a branch (a branch around each load makes the compiler wait for every load
+// before the next). QUADS: D % 4 == 0 and the row 16-byte aligned.
+template <bool QUADS>
+__device__ inline f32x4 load_quad(const float* row, int d, int D) {
+    f32x4 v;
+    if constexpr (QUADS) {
+        v = *reinterpret_cast<const f32x4*>(row + min(d, D - 4));
+        if (d >= D) v = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = row[min(d + c, D - 1)];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if (d + c >= D) v[c] = 0.0f;
+    }
+    return v;
+}
+
+__device__ inline float combine_factor(float ms, float M) {
+    return ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((ms - M) * kLog2e);
+}
+
+// Splits sb .. sb + kCombineBatch - 1 (those below s1) of row bq at d, loaded
+// all at once: statistics as (m, l) pairs and partial quads. Splits at or past
+// s1 read split s1 - 1 and are masked to (-inf, 0) and zeros.
+template <bool QUADS>
+__device__ inline void load_batch(const float2* st2, const float* part, int64_t nbq, int64_t bq, int D, int sb,
+                                  int s1, int d, float2 (&ml)[kCombineBatch], f32x4 (&pv)[kCombineBatch]) {
+    const int64_t pstride = nbq * D;
+#pragma unroll
+    for (int k = 0; k < kCombineBatch; ++k) {
+        const int s = min(sb + k, s1 - 1);
+        ml[k] = st2[s * nbq + bq];
+        pv[k] = load_quad<QUADS>(part + s * pstride + bq * D, d, D);
+    }
+#pragma unroll
+    for (int k = 0; k < kCombineBatch; ++k)
+        if (sb + k >= s1) {
+            ml[k] = float2{-INFINITY, 0.0f};
+            pv[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+}
+
+template <bool QUADS>
+__global__ __launch_bounds__(kThreads) void av_pass2_softmax_combine_few(const float* __restrict__ part,
+                                                                         const float* __restrict__ stats,
+                                                                         float* __restrict__ out, int32_t D,
+                                                                         int64_t nbq, int32_t nsplit) {
+    const int qpr = (D + 3) / 4;                     // quads per row
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (gid >= nbq * qpr) return;
+    const int64_t bq = gid / qpr;
+    const int d = static_cast<int>(gid - bq * qpr) * 4;
+    float2 ml[kCombineBatch];
+    f32x4 pv[kCombineBatch];
+    load_batch<QUADS>(reinterpret_cast<const float2*>(stats), part, nbq, bq, D, 0, nsplit, d, ml, pv);
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kCombineBatch; ++k) M = fmaxf(M, ml[k].x);
+    f32x4 num = {0.0f, 0.0f, 0.0f, 0.0f};
+    float den = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kCombineBatch; ++k) {
+        const float f = combine_factor(ml[k].x, M);
+        den += f * ml[k].y;
+        num += f * pv[k];
+    }
+    float* const ob = out + bq * D;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        if (d + c < D) ob[d + c] = num[c] / den;
+}
+
+template <bool QUADS>
+__global__ __launch_bounds__(kThreads) void av_pass2_softmax_combine(const float* __restrict__ part,
+                                                                     const float* __restrict__ stats,
+                                                                     float* __restrict__ out, int32_t D,
+                                                                     int64_t nbq, int32_t nsplit) {
+    constexpr int kQL = kThreads / kSplitGroups;     // quad lanes per split group
+    constexpr int kB = kCombineBatch;
+    __shared__ float s_max[kWaves];
+    __shared__ float s_den[kSplitGroups];
+    __shared__ f32x4 s_num[kSplitGroups][kQL];
+    const int64_t bq = blockIdx.x;
+    const int tid = threadIdx.x;
+    const float2* const st2 = reinterpret_cast<const float2*>(stats);
+    const int sg = tid / kQL, ql = tid % kQL;
+    // nsplit > kCombineBatch >= ... so every group holds at least one split.
+    const int s0 = static_cast<int>((static_cast<int64_t>(nsplit) * sg) / kSplitGroups);
+    const int s1 = static_cast<int>((static_cast<int64_t>(nsplit) * (sg + 1)) / kSplitGroups);
+    // This group's first batch at d = 4 ql: in flight while M is found.
+    float2 ml[kB];
+    f32x4 pv[kB];
+    load_batch<QUADS>(st2, part, nbq, bq, D, s0, s1, 4 * ql, ml, pv);
+    float m = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kB; ++k) m = fmaxf(m, ml[k].x);
+    for (int s = s0 + kB; s < s1; ++s) m = fmaxf(m, st2[s * nbq + bq].x);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if ((tid & 63) == 0) s_max[tid >> 6] = m;
+    __syncthreads();
+    float M = s_max[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_max[w]);
+    float* const ob = out + bq * D;
+    for (int d0 = 0; d0 < D; d0 += 4 * kQL) {       // uniform trip count: barriers inside
+        const int d = d0 + 4 * ql;
+        f32x4 num = {0.0f, 0.0f, 0.0f, 0.0f};
+        float den = 0.0f;
+        for (int sb = s0; sb < s1; sb += kB) {
+            if (d0 > 0 || sb > s0) load_batch<QUADS>(st2, part, nbq, bq, D, sb, s1, d, ml, pv);
+#pragma unroll
+            for (int k = 0; k < kB; ++k) {
+                const float f = combine_factor(ml[k].x, M);
+                den += f * ml[k].y;
+                num += f * pv[k];
+            }
+        }
+        s_num[sg][ql] = num;
+        if (ql == 0) s_den[sg] = den;
+        __syncthreads();
+        if (sg == 0) {
+            f32x4 t = s_num[0][ql];
+            float dn = s_den[0];
+#pragma unroll
+            for (int k = 1; k < kSplitGroups; ++k) {
+                t += s_num[k][ql];
+                dn += s_den[k];
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (d + c < D) ob[d + c] = t[c] / dn;
+        }
+        __syncthreads();
     }
 }
 

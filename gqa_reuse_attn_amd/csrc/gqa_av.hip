@@ -8,6 +8,7 @@
 // also caps G at 8 and sends larger groups to the per-head kernel; that cap
 // is not kept: any G takes the reuse path (G > 16 in sub-groups of 16 heads).
 #include "gqa_av.h"
+#include "gqa_softmax_av.h"
 
 #include <hip/hip_runtime.h>
 
@@ -153,37 +154,42 @@ int check_sizes(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_
 
 // ---- kernel dispatch ----------------------------------------------------------
 
-template <int DT, int VB, int GT>
+template <int DT, int VB, int GT, bool SM>
 hipError_t launch_valu(const Pass1Args& a, hipStream_t s) {
     constexpr int U = gqa_av::valu_unroll(GT);
-    hipLaunchKernelGGL((gqa_av::av_pass1_valu<DT, VB, GT, U>), dim3(a.nblocks), dim3(gqa_av::kThreads), 0, s, a);
-    return hipGetLastError();
+    if constexpr (SM && GQA_AV_VALU_STAGE_WEIGHTS) {
+        return hipErrorInvalidValue;                 // the plan refuses this combination
+    } else {
+        hipLaunchKernelGGL((gqa_av::av_pass1_valu<DT, VB, GT, U, SM>), dim3(a.nblocks), dim3(gqa_av::kThreads), 0,
+                           s, a);
+        return hipGetLastError();
+    }
 }
 
-template <int DT, int VB>
+template <int DT, int VB, bool SM>
 hipError_t launch_valu_gt(int GT, const Pass1Args& a, hipStream_t s) {
     switch (GT) {
-    case 1: return launch_valu<DT, VB, 1>(a, s);
-    case 2: return launch_valu<DT, VB, 2>(a, s);
-    case 3: return launch_valu<DT, VB, 3>(a, s);
-    case 4: return launch_valu<DT, VB, 4>(a, s);
-    case 5: return launch_valu<DT, VB, 5>(a, s);
-    case 6: return launch_valu<DT, VB, 6>(a, s);
-    case 7: return launch_valu<DT, VB, 7>(a, s);
-    case 8: return launch_valu<DT, VB, 8>(a, s);
-    case 16: return launch_valu<DT, VB, 16>(a, s);
+    case 1: return launch_valu<DT, VB, 1, SM>(a, s);
+    case 2: return launch_valu<DT, VB, 2, SM>(a, s);
+    case 3: return launch_valu<DT, VB, 3, SM>(a, s);
+    case 4: return launch_valu<DT, VB, 4, SM>(a, s);
+    case 5: return launch_valu<DT, VB, 5, SM>(a, s);
+    case 6: return launch_valu<DT, VB, 6, SM>(a, s);
+    case 7: return launch_valu<DT, VB, 7, SM>(a, s);
+    case 8: return launch_valu<DT, VB, 8, SM>(a, s);
+    case 16: return launch_valu<DT, VB, 16, SM>(a, s);
     default: return hipErrorInvalidValue;
     }
 }
 
-template <int DT>
+template <int DT, bool SM>
 hipError_t launch_valu_vb(int VB, int GT, const Pass1Args& a, hipStream_t s) {
     switch (VB) {
-    case 16: return launch_valu_gt<DT, 16>(GT, a, s);
-    case 8: return launch_valu_gt<DT, 8>(GT, a, s);
-    case 4: return launch_valu_gt<DT, 4>(GT, a, s);
+    case 16: return launch_valu_gt<DT, 16, SM>(GT, a, s);
+    case 8: return launch_valu_gt<DT, 8, SM>(GT, a, s);
+    case 4: return launch_valu_gt<DT, 4, SM>(GT, a, s);
     case 2:
-        if constexpr (DT != gqa_av::kF32) return launch_valu_gt<DT, 2>(GT, a, s);
+        if constexpr (DT != gqa_av::kF32) return launch_valu_gt<DT, 2, SM>(GT, a, s);
         return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
     }
@@ -205,28 +211,29 @@ hipError_t launch_mfma_set(int nset, const Pass1Args& a, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
-template <int PR, int NSET, int HT>
+template <int PR, int NSET, int HT, bool SM>
 hipError_t launch_mfma_bf16(const Pass1Args& a, hipStream_t s) {
-    hipLaunchKernelGGL((gqa_av::av_pass1_mfma_bf16<PR, NSET, GQA_AV_MFMA_BF16_CHUNKS, HT>), dim3(a.nblocks),
+    hipLaunchKernelGGL((gqa_av::av_pass1_mfma_bf16<PR, NSET, GQA_AV_MFMA_BF16_CHUNKS, HT, SM>), dim3(a.nblocks),
                        dim3(gqa_av::kThreads), 0, s, a);
     return hipGetLastError();
 }
 
-template <int PR, int NSET>
+template <int PR, int NSET, bool SM>
 hipError_t launch_mfma_bf16_ht(int ht, const Pass1Args& a, hipStream_t s) {
     switch (ht) {
-    case 1: return launch_mfma_bf16<PR, NSET, 1>(a, s);
-    case 2: return launch_mfma_bf16<PR, NSET, 2>(a, s);
-    case 4: return launch_mfma_bf16<PR, NSET, 4>(a, s);
+    case 1: return launch_mfma_bf16<PR, NSET, 1, SM>(a, s);
+    case 2: return launch_mfma_bf16<PR, NSET, 2, SM>(a, s);
+    case 4: return launch_mfma_bf16<PR, NSET, 4, SM>(a, s);
     default: return hipErrorInvalidValue;
     }
 }
 
+template <bool SM>
 hipError_t launch_mfma_bf16_pr(int64_t D, int nset, int ht, const Pass1Args& a, hipStream_t s) {
     switch (D) {
-    case 64: return nset == 1 ? launch_mfma_bf16_ht<8, 1>(ht, a, s) : launch_mfma_bf16_ht<8, 2>(ht, a, s);
-    case 128: return nset == 1 ? launch_mfma_bf16_ht<16, 1>(ht, a, s) : launch_mfma_bf16_ht<16, 2>(ht, a, s);
-    case 256: return nset == 1 ? launch_mfma_bf16_ht<32, 1>(ht, a, s) : hipErrorInvalidValue;
+    case 64: return nset == 1 ? launch_mfma_bf16_ht<8, 1, SM>(ht, a, s) : launch_mfma_bf16_ht<8, 2, SM>(ht, a, s);
+    case 128: return nset == 1 ? launch_mfma_bf16_ht<16, 1, SM>(ht, a, s) : launch_mfma_bf16_ht<16, 2, SM>(ht, a, s);
+    case 256: return nset == 1 ? launch_mfma_bf16_ht<32, 1, SM>(ht, a, s) : hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
     }
 }
@@ -250,7 +257,17 @@ hipError_t launch_mfma_de(int DE, int nset, const Pass1Args& a, hipStream_t s) {
 hipError_t launch_pass1(int v_dtype, const gqa_av_plan& p, int64_t D, const Pass1Args& a, hipStream_t s) {
     if (p.engine == GQA_AV_ENGINE_MFMA_BF16) {
         if (v_dtype != GQA_AV_BF16) return hipErrorInvalidValue;
-        return launch_mfma_bf16_pr(D, p.heads_per_tile / 16, p.kv_heads_per_tile, a, s);
+        return p.softmax ? launch_mfma_bf16_pr<true>(D, p.heads_per_tile / 16, p.kv_heads_per_tile, a, s)
+                         : launch_mfma_bf16_pr<false>(D, p.heads_per_tile / 16, p.kv_heads_per_tile, a, s);
+    }
+    if (p.softmax) {
+        if (p.engine != GQA_AV_ENGINE_VALU) return hipErrorInvalidValue;
+        switch (v_dtype) {
+        case GQA_AV_F32: return launch_valu_vb<gqa_av::kF32, true>(p.vec_bytes, p.heads_per_tile, a, s);
+        case GQA_AV_F16: return launch_valu_vb<gqa_av::kF16, true>(p.vec_bytes, p.heads_per_tile, a, s);
+        case GQA_AV_BF16: return launch_valu_vb<gqa_av::kBF16, true>(p.vec_bytes, p.heads_per_tile, a, s);
+        default: return hipErrorInvalidValue;
+        }
     }
     if (p.engine == GQA_AV_ENGINE_MFMA) {
         const int DE = static_cast<int>(D / 16), nset = p.heads_per_tile / 16;
@@ -262,9 +279,9 @@ hipError_t launch_pass1(int v_dtype, const gqa_av_plan& p, int64_t D, const Pass
         }
     }
     switch (v_dtype) {
-    case GQA_AV_F32: return launch_valu_vb<gqa_av::kF32>(p.vec_bytes, p.heads_per_tile, a, s);
-    case GQA_AV_F16: return launch_valu_vb<gqa_av::kF16>(p.vec_bytes, p.heads_per_tile, a, s);
-    case GQA_AV_BF16: return launch_valu_vb<gqa_av::kBF16>(p.vec_bytes, p.heads_per_tile, a, s);
+    case GQA_AV_F32: return launch_valu_vb<gqa_av::kF32, false>(p.vec_bytes, p.heads_per_tile, a, s);
+    case GQA_AV_F16: return launch_valu_vb<gqa_av::kF16, false>(p.vec_bytes, p.heads_per_tile, a, s);
+    case GQA_AV_BF16: return launch_valu_vb<gqa_av::kBF16, false>(p.vec_bytes, p.heads_per_tile, a, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -304,13 +321,19 @@ constexpr int64_t kCounterBytes = 256;          // the counter block is padded t
 
 int64_t counter_bytes(int64_t tiles) { return ceil_div(tiles * 4, kCounterBytes) * kCounterBytes; }
 
-// KERNEL: one fp32 plane of `out` per split. LAST: [tiles][nsplit][tile outputs]
-// partials plus one counter per tile.
+// Floats from the start of the split planes to the fused softmax's statistics
+// (the planes rounded up to whole 16-byte groups).
+int64_t stats_offset(int64_t nsplit, int64_t B, int64_t Hq, int64_t D) { return (nsplit * B * Hq * D + 3) / 4 * 4; }
+
+// KERNEL: one fp32 plane of `out` per split, and for the fused softmax one
+// (maximum, weight sum) pair per split and (b, q_h) after the planes. LAST:
+// [tiles][nsplit][tile outputs] partials plus one counter per tile.
 int64_t workspace_bytes(int64_t B, int64_t Hq, int64_t D, int64_t tiles, int64_t nsplit, int64_t tile_outputs,
-                        int combine) {
+                        int combine, bool softmax) {
     if (nsplit <= 1) return 0;
     if (combine == GQA_AV_COMBINE_LAST)
         return counter_bytes(tiles) + tiles * nsplit * gqa_av::padded_outputs(static_cast<int>(tile_outputs)) * 4;
+    if (softmax) return stats_offset(nsplit, B, Hq, D) * 4 + nsplit * B * Hq * 2 * 4;
     return nsplit * B * Hq * D * 4;
 }
 
@@ -329,6 +352,8 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
         return fail(GQA_AV_ERR_INVALID_ARG, "unknown engine %d", h.engine);
     if (h.combine < GQA_AV_COMBINE_AUTO || h.combine > GQA_AV_COMBINE_LAST)
         return fail(GQA_AV_ERR_INVALID_ARG, "unknown combine %d", h.combine);
+    if (h.softmax != 0 && h.softmax != 1) return fail(GQA_AV_ERR_INVALID_ARG, "hint softmax must be 0 or 1");
+    const bool sm = h.softmax == 1;
     const int cus = h.cu_count > 0 ? h.cu_count : cu_default;
     const int v_align = h.v_align > 0 ? h.v_align : 16;
 
@@ -348,8 +373,12 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
     if (engine == GQA_AV_ENGINE_AUTO) {
         engine = GQA_AV_ENGINE_VALU;
         if (G >= kMfmaMinGroup && mfma16_ok) engine = GQA_AV_ENGINE_MFMA_BF16;
-        else if (G >= kMfmaMinGroup && mfma_ok) engine = GQA_AV_ENGINE_MFMA;
+        else if (G >= kMfmaMinGroup && mfma_ok && !sm) engine = GQA_AV_ENGINE_MFMA;
     }
+    if (sm && engine == GQA_AV_ENGINE_MFMA)
+        return fail(GQA_AV_ERR_UNSUPPORTED, "the fused softmax runs on the VALU or bf16 matrix engine");
+    if (sm && engine == GQA_AV_ENGINE_VALU && GQA_AV_VALU_STAGE_WEIGHTS)
+        return fail(GQA_AV_ERR_UNSUPPORTED, "the fused softmax needs the per-lane weight VALU build");
     if (engine == GQA_AV_ENGINE_MFMA && !mfma_ok)
         return fail(GQA_AV_ERR_UNSUPPORTED,
                     "MFMA engine needs reuse mode, D %% 16 == 0 with a 4/8/12/16/32-byte lane chunk and matching V alignment");
@@ -393,6 +422,7 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
             return fail(GQA_AV_ERR_INVALID_ARG, "kv_tile %d does not divide Hkv=%lld", ht, (long long)Hkv);
         if (bf16_engine && ht != 2 && ht != 4)
             return fail(GQA_AV_ERR_UNSUPPORTED, "the bf16 matrix engine takes 1, 2 or 4 KV heads per tile");
+        if (sm && ht > 4) return fail(GQA_AV_ERR_UNSUPPORTED, "the fused softmax takes at most 4 KV heads per tile");
     }
 
     int VB, GT, nsg;
@@ -510,14 +540,17 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
         // workload (the last-workgroup combine pays for device-coherent
         // stores and loads of the partials), so it is the automatic choice.
         if (combine == GQA_AV_COMBINE_AUTO) combine = GQA_AV_COMBINE_KERNEL;
+        if (sm && combine != GQA_AV_COMBINE_KERNEL)
+            return fail(GQA_AV_ERR_UNSUPPORTED, "the fused softmax combines its splits in a second kernel");
         // One tile's block is addressed through a 32-bit buffer offset.
         if (combine == GQA_AV_COMBINE_LAST && nsplit * gqa_av::padded_outputs(static_cast<int>(tile_outputs)) * 4 > INT32_MAX)
             return fail(GQA_AV_ERR_UNSUPPORTED, "a tile's split partials exceed 2 GB; use the kernel combine");
     }
     plan->combine = combine;
     plan->kv_heads_per_tile = ht;
-    plan->workspace_bytes = workspace_bytes(B, Hq, D, tiles, nsplit, tile_outputs, combine);
+    plan->workspace_bytes = workspace_bytes(B, Hq, D, tiles, nsplit, tile_outputs, combine, sm);
     plan->v_bytes_read = B * C * Hkv * D * es * heads_major;
+    plan->softmax = sm ? 1 : 0;
     return GQA_AV_OK;
 }
 
@@ -526,7 +559,8 @@ bool same_plan(const gqa_av_plan& a, const gqa_av_plan& b) {
            a.subgroups == b.subgroups && a.vec_bytes == b.vec_bytes && a.lanes_per_row == b.lanes_per_row &&
            a.row_slots == b.row_slots && a.d_tiles == b.d_tiles && a.nsplit == b.nsplit &&
            a.threads == b.threads && a.rows_per_split == b.rows_per_split && a.grid == b.grid &&
-           a.workspace_bytes == b.workspace_bytes && a.kv_heads_per_tile == b.kv_heads_per_tile;
+           a.workspace_bytes == b.workspace_bytes && a.kv_heads_per_tile == b.kv_heads_per_tile &&
+           a.softmax == b.softmax;
 }
 
 }  // namespace
@@ -570,11 +604,15 @@ constexpr int kRunPass1 = 1, kRunCombine = 2;
 // Validate (attn, V, out, sizes, plan) and launch the parts of the call named
 // by `which`. Validation is the same for every part, so a caller splitting
 // the call gets the same errors as gqa_av_decode_plan.
+// softmax: 1 for the fused softmax entry point (attn then holds the scores).
 int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
-             int64_t D, int v_dtype, const gqa_av_plan* plan, void* stream, int which) {
+             int64_t D, int v_dtype, const gqa_av_plan* plan, void* stream, int which, int softmax) {
     if (!plan) return fail(GQA_AV_ERR_INVALID_ARG, "plan is NULL");
     int rc = check_sizes(B, C, Hq, Hkv, D, v_dtype);
     if (rc != GQA_AV_OK) return rc;
+    if (plan->softmax != softmax)
+        return fail(GQA_AV_ERR_INVALID_ARG, softmax ? "not a fused softmax plan (plan->softmax == 0)"
+                                                    : "a fused softmax plan: run it with gqa_softmax_av_decode_plan");
     // Re-derive the plan from its own choices and insist it matches.
     gqa_av_hint h;
     std::memset(&h, 0, sizeof h);
@@ -583,6 +621,7 @@ int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C,
     h.v_align = plan->vec_bytes;
     h.combine = plan->combine;
     h.kv_tile = plan->kv_heads_per_tile;
+    h.softmax = plan->softmax;
     gqa_av_plan check;
     const int mode = plan->mode;
     // Re-plan with the split count fixed: rows_per_split then follows from C.
@@ -616,11 +655,11 @@ int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C,
         ? static_cast<int64_t>(plan->heads_per_tile) * D * plan->kv_heads_per_tile
         : static_cast<int64_t>(plan->heads_per_tile) * (plan->vec_bytes / elem_bytes(v_dtype)) * plan->lanes_per_row;
     if (plan->workspace_bytes !=
-        workspace_bytes(B, Hq, D, tiles_per_split, plan->nsplit, tile_outputs, plan->combine))
+        workspace_bytes(B, Hq, D, tiles_per_split, plan->nsplit, tile_outputs, plan->combine, plan->softmax == 1))
         return fail(GQA_AV_ERR_INVALID_ARG, "plan workspace does not match the problem");
 
     if (B == 0) return GQA_AV_OK;
-    if (!attn && C > 0) return fail(GQA_AV_ERR_INVALID_ARG, "attn is NULL");
+    if (!attn && C > 0) return fail(GQA_AV_ERR_INVALID_ARG, softmax ? "scores is NULL" : "attn is NULL");
     if (!V && C > 0) return fail(GQA_AV_ERR_INVALID_ARG, "V is NULL");
     if (!out) return fail(GQA_AV_ERR_INVALID_ARG, "out is NULL");
     if ((reinterpret_cast<uintptr_t>(attn) & 3u) || (reinterpret_cast<uintptr_t>(out) & 3u))
@@ -648,6 +687,7 @@ int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C,
     a.V = static_cast<const uint8_t*>(V);
     a.out = out;
     a.part = part;
+    a.stats = (softmax && plan->nsplit > 1) ? part + stats_offset(plan->nsplit, B, Hq, D) : nullptr;
     a.counters = counters;
     a.combine = last ? 1 : 0;
     a.C = C;
@@ -671,7 +711,31 @@ int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C,
         e = launch_pass1(v_dtype, *plan, D, a, s);
         if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "pass-1 launch: %s", hipGetErrorString(e));
     }
-    if ((which & kRunCombine) && plan->nsplit > 1 && !last) {
+    if ((which & kRunCombine) && plan->nsplit > 1 && softmax) {
+        if (plan->nsplit <= gqa_av::kCombineBatch) {
+            const int64_t threads = B * Hq * ceil_div(D, 4);
+            const int64_t blocks = ceil_div(threads, gqa_av::kThreads);
+            if (blocks > INT32_MAX) return fail(GQA_AV_ERR_UNSUPPORTED, "output too large for the softmax combine");
+            if (D % 4 == 0)
+                hipLaunchKernelGGL(gqa_av::av_pass2_softmax_combine_few<true>, dim3(static_cast<uint32_t>(blocks)),
+                                   dim3(gqa_av::kThreads), 0, s, static_cast<const float*>(part),
+                                   static_cast<const float*>(a.stats), out, a.D, B * Hq, a.nsplit);
+            else
+                hipLaunchKernelGGL(gqa_av::av_pass2_softmax_combine_few<false>, dim3(static_cast<uint32_t>(blocks)),
+                                   dim3(gqa_av::kThreads), 0, s, static_cast<const float*>(part),
+                                   static_cast<const float*>(a.stats), out, a.D, B * Hq, a.nsplit);
+        } else if (D % 4 == 0) {
+            hipLaunchKernelGGL(gqa_av::av_pass2_softmax_combine<true>, dim3(static_cast<uint32_t>(B * Hq)),
+                               dim3(gqa_av::kThreads), 0, s, static_cast<const float*>(part),
+                               static_cast<const float*>(a.stats), out, a.D, B * Hq, a.nsplit);
+        } else {
+            hipLaunchKernelGGL(gqa_av::av_pass2_softmax_combine<false>, dim3(static_cast<uint32_t>(B * Hq)),
+                               dim3(gqa_av::kThreads), 0, s, static_cast<const float*>(part),
+                               static_cast<const float*>(a.stats), out, a.D, B * Hq, a.nsplit);
+        }
+        e = hipGetLastError();
+        if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "softmax combine launch: %s", hipGetErrorString(e));
+    } else if ((which & kRunCombine) && plan->nsplit > 1 && !last) {
         const int64_t plane = B * Hq * D;
         const int64_t per_block = 4 * gqa_av::kQuadsPerBlock;
         const int64_t blocks = ceil_div(plane, per_block);
@@ -684,27 +748,9 @@ int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C,
     return GQA_AV_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int gqa_av_decode_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C, int64_t Hq,
-                       int64_t Hkv, int64_t D, int v_dtype, const gqa_av_plan* plan, void* stream) {
-    return run_plan(attn, V, out, B, C, Hq, Hkv, D, v_dtype, plan, stream, kRunPass1 | kRunCombine);
-}
-
-int gqa_av_decode_pass1(const float* attn, const void* V, float* out, int64_t B, int64_t C, int64_t Hq,
-                        int64_t Hkv, int64_t D, int v_dtype, const gqa_av_plan* plan, void* stream) {
-    return run_plan(attn, V, out, B, C, Hq, Hkv, D, v_dtype, plan, stream, kRunPass1);
-}
-
-int gqa_av_decode_combine(const float* attn, const void* V, float* out, int64_t B, int64_t C, int64_t Hq,
-                          int64_t Hkv, int64_t D, int v_dtype, const gqa_av_plan* plan, void* stream) {
-    return run_plan(attn, V, out, B, C, Hq, Hkv, D, v_dtype, plan, stream, kRunCombine);
-}
-
-int gqa_av_decode(const float* attn, const void* V, float* out, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
-                  int64_t D, int v_dtype, int mode, void* stream) {
+// The automatic plan for the current device and V's address alignment.
+int auto_plan(const void* V, int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dtype, int mode,
+              int softmax, gqa_av_plan* plan) {
     int rc = check_sizes(B, C, Hq, Hkv, D, v_dtype);
     if (rc != GQA_AV_OK) return rc;
     int dev = 0;
@@ -717,14 +763,62 @@ int gqa_av_decode(const float* attn, const void* V, float* out, int64_t B, int64
     std::memset(&h, 0, sizeof h);
     h.engine = GQA_AV_ENGINE_AUTO;
     h.cu_count = cus;
+    h.softmax = softmax;
     // Alignment of V's address: its lowest set bit, at most 16.
     const uintptr_t addr = reinterpret_cast<uintptr_t>(V);
     const uintptr_t low = addr & (~addr + 1);
     h.v_align = (addr == 0 || low >= 16) ? 16 : static_cast<int32_t>(low);
+    return plan_impl(B, C, Hq, Hkv, D, v_dtype, mode, &h, cus, plan);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_av_decode_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C, int64_t Hq,
+                       int64_t Hkv, int64_t D, int v_dtype, const gqa_av_plan* plan, void* stream) {
+    return run_plan(attn, V, out, B, C, Hq, Hkv, D, v_dtype, plan, stream, kRunPass1 | kRunCombine, 0);
+}
+
+int gqa_av_decode_pass1(const float* attn, const void* V, float* out, int64_t B, int64_t C, int64_t Hq,
+                        int64_t Hkv, int64_t D, int v_dtype, const gqa_av_plan* plan, void* stream) {
+    return run_plan(attn, V, out, B, C, Hq, Hkv, D, v_dtype, plan, stream, kRunPass1, 0);
+}
+
+int gqa_av_decode_combine(const float* attn, const void* V, float* out, int64_t B, int64_t C, int64_t Hq,
+                          int64_t Hkv, int64_t D, int v_dtype, const gqa_av_plan* plan, void* stream) {
+    return run_plan(attn, V, out, B, C, Hq, Hkv, D, v_dtype, plan, stream, kRunCombine, 0);
+}
+
+int gqa_av_decode(const float* attn, const void* V, float* out, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
+                  int64_t D, int v_dtype, int mode, void* stream) {
     gqa_av_plan plan;
-    rc = plan_impl(B, C, Hq, Hkv, D, v_dtype, mode, &h, cus, &plan);
+    int rc = auto_plan(V, B, C, Hq, Hkv, D, v_dtype, mode, 0, &plan);
     if (rc != GQA_AV_OK) return rc;
     return gqa_av_decode_plan(attn, V, out, B, C, Hq, Hkv, D, v_dtype, &plan, stream);
+}
+
+int gqa_softmax_av_decode(const float* scores, const void* V, float* out, int64_t B, int64_t C, int64_t Hq,
+                          int64_t Hkv, int64_t D, int v_dtype, int mode, void* stream) {
+    gqa_av_plan plan;
+    int rc = auto_plan(V, B, C, Hq, Hkv, D, v_dtype, mode, 1, &plan);
+    if (rc != GQA_AV_OK) return rc;
+    return gqa_softmax_av_decode_plan(scores, V, out, B, C, Hq, Hkv, D, v_dtype, &plan, stream);
+}
+
+int gqa_softmax_av_decode_plan(const float* scores, const void* V, float* out, int64_t B, int64_t C, int64_t Hq,
+                               int64_t Hkv, int64_t D, int v_dtype, const gqa_av_plan* plan, void* stream) {
+    return run_plan(scores, V, out, B, C, Hq, Hkv, D, v_dtype, plan, stream, kRunPass1 | kRunCombine, 1);
+}
+
+int gqa_softmax_av_decode_pass1(const float* scores, const void* V, float* out, int64_t B, int64_t C, int64_t Hq,
+                                int64_t Hkv, int64_t D, int v_dtype, const gqa_av_plan* plan, void* stream) {
+    return run_plan(scores, V, out, B, C, Hq, Hkv, D, v_dtype, plan, stream, kRunPass1, 1);
+}
+
+int gqa_softmax_av_decode_combine(const float* scores, const void* V, float* out, int64_t B, int64_t C, int64_t Hq,
+                                  int64_t Hkv, int64_t D, int v_dtype, const gqa_av_plan* plan, void* stream) {
+    return run_plan(scores, V, out, B, C, Hq, Hkv, D, v_dtype, plan, stream, kRunCombine, 1);
 }
 
 const char* gqa_av_status_string(int status) {

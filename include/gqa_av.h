@@ -45,7 +45,9 @@
  *
  * Workspace: when a plan splits the context (nsplit > 1) the library needs
  * nsplit blocks of partial sums and, for GQA_AV_COMBINE_LAST, one uint32
- * counter per tile (plan->workspace_bytes in total). It allocates them itself
+ * counter per tile, or, for a fused softmax plan (gqa_softmax_av.h), nsplit
+ * planes of partial sums and nsplit * B * Hq pairs of floats of per-split
+ * statistics (plan->workspace_bytes in total). It allocates them itself
  * (hipMalloc) per (device, stream) in two buffers, keeps them for reuse, grows
  * them on demand (synchronising that stream first) and frees them in
  * gqa_av_release(). The counters are zeroed when allocated and every call
@@ -113,7 +115,8 @@ typedef struct gqa_av_hint {
     int32_t v_align;    /* byte alignment of V's base address; auto = 16 */
     int32_t combine;    /* gqa_av_combine for context splits */
     int32_t kv_tile;    /* adjacent KV heads per VALU workgroup (their D-rows are contiguous) */
-    int32_t reserved[2];
+    int32_t softmax;    /* 1: plan the fused softmax product of gqa_softmax_av.h; 0: this header's product */
+    int32_t reserved[1];
 } gqa_av_hint;
 
 /* A launch plan: what gqa_av_decode_plan will run. Produced by gqa_av_make_plan. */
@@ -134,7 +137,9 @@ typedef struct gqa_av_plan {
     int64_t v_bytes_read;    /* V bytes the plan reads from memory (G x more for per-head) */
     int32_t combine;         /* resolved gqa_av_combine: KERNEL or LAST when nsplit > 1, else AUTO */
     int32_t kv_heads_per_tile; /* adjacent KV heads one workgroup streams (VALU reuse; else 1) */
-    int32_t reserved[2];
+    int32_t softmax;         /* 1: a plan of the fused softmax product (gqa_softmax_av.h), which only
+                                gqa_softmax_av_decode_plan runs; 0: a plan of this header's product */
+    int32_t reserved[1];
 } gqa_av_plan;
 
 /* Resolve `mode` for a head shape. Host-only: needs no GPU.

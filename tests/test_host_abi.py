@@ -23,7 +23,7 @@ def declared_functions():
     names = set()
     for h in sorted(glob.glob(os.path.join(os.path.dirname(HEADER), "*.h"))):
         text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
-        names |= set(re.findall(r"\b(gqa_(?:av|qk)_\w+)\s*\(", text))
+        names |= set(re.findall(r"\b(gqa_(?:av|qk|softmax_av)_\w+)\s*\(", text))
     return sorted(names)
 
 
@@ -32,6 +32,7 @@ def test_library_exports_every_declared_function():
     names = declared_functions()
     assert len(names) >= 10, names
     assert {"gqa_qk_decode", "gqa_qk_decode_plan", "gqa_qk_make_plan"} <= set(names)
+    assert {"gqa_softmax_av_decode", "gqa_softmax_av_decode_plan"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/ but not exported"
 
@@ -39,7 +40,7 @@ def test_library_exports_every_declared_function():
 def test_exports_are_c_symbols():
     # extern "C": no mangled gqa_av names in the dynamic symbol table
     out = os.popen(f"nm -D --defined-only {ga.LIB_PATH}").read()
-    exported = set(re.findall(r"\s(gqa_(?:av|qk)_\w+)$", out, flags=re.M))
+    exported = set(re.findall(r"\s(gqa_(?:av|qk|softmax_av)_\w+)$", out, flags=re.M))
     assert set(declared_functions()) <= exported
 
 
@@ -385,3 +386,58 @@ def test_qk_decode_plan_rejects_before_launch():
     assert lib.gqa_qk_decode_plan(odd, fake, fake, 2, 100, 8, 2, 64, 2, ctypes.c_float(1.0), ctypes.byref(p), None) == 1
     p0 = ga.qk_make_plan(0, 100, 8, 2, 64, "bf16")
     assert lib.gqa_qk_decode_plan(None, None, None, 0, 100, 8, 2, 64, 2, ctypes.c_float(1.0), ctypes.byref(p0), None) == 0
+
+
+@pytest.mark.parametrize("wname", list(WORKLOADS))
+def test_softmax_plans(wname):
+    """Fused softmax plans: the VALU or bf16 matrix engine, the kernel combine,
+    and a workspace with one (maximum, weight sum) pair per split and (b, q_h)."""
+    w = WORKLOADS[wname]
+    for mode in ("auto", "per_head"):
+        p = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, mode, softmax=True)
+        q = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, mode)
+        assert p.softmax == 1 and q.softmax == 0
+        assert p.engine in (1, 3)
+        if p.nsplit > 1:
+            assert p.combine == 1
+            planes = -(-p.nsplit * w.B * w.Hq * w.D // 4) * 4
+            assert p.workspace_bytes == planes * 4 + p.nsplit * w.B * w.Hq * 8
+        else:
+            assert p.workspace_bytes == 0
+
+
+def test_softmax_plan_refusals():
+    with pytest.raises(ga.GqaAvError) as e:
+        ga.make_plan(2, 1000, 16, 2, 128, "f16", "reuse", engine="mfma", softmax=True)
+    assert e.value.name == "UNSUPPORTED"
+    with pytest.raises(ga.GqaAvError) as e:
+        ga.make_plan(2, 1000, 16, 2, 128, "bf16", "reuse", nsplit=4, combine="last", softmax=True)
+    assert e.value.name == "UNSUPPORTED"
+    with pytest.raises(ga.GqaAvError) as e:
+        ga.make_plan(1, 1000, 16, 8, 32, "bf16", "reuse", engine="valu", kv_tile=8, softmax=True)
+    assert e.value.name == "UNSUPPORTED"
+    # f16 / f32 V with a large group: the automatic engine is VALU, not the fp32 matrix engine
+    assert ga.make_plan(2, 4096, 32, 2, 128, "f16", "reuse", softmax=True).engine == 1
+    assert ga.make_plan(2, 4096, 32, 2, 128, "f16", "reuse").engine == 2
+    h = ga.Hint()
+    h.softmax = 2
+    p = ga.Plan()
+    assert ga.load().gqa_av_make_plan(1, 10, 4, 2, 64, 2, -1, ctypes.byref(h), ctypes.byref(p)) == 1
+
+
+def test_softmax_and_plain_plans_do_not_mix():
+    """Each entry point refuses the other's plans before touching the GPU."""
+    lib = ga.load()
+    fake = ctypes.c_void_p(1 << 20)
+    sm = ga.make_plan(2, 100, 8, 2, 64, "bf16", softmax=True)
+    pl = ga.make_plan(2, 100, 8, 2, 64, "bf16")
+    for fn in ("gqa_av_decode_plan", "gqa_av_decode_pass1", "gqa_av_decode_combine"):
+        assert getattr(lib, fn)(fake, fake, fake, 2, 100, 8, 2, 64, 2, ctypes.byref(sm), None) == 1
+    for fn in ("gqa_softmax_av_decode_plan", "gqa_softmax_av_decode_pass1", "gqa_softmax_av_decode_combine"):
+        assert getattr(lib, fn)(fake, fake, fake, 2, 100, 8, 2, 64, 2, ctypes.byref(pl), None) == 1
+    # and the usual checks: wrong sizes, NULL scores, B = 0
+    assert lib.gqa_softmax_av_decode_plan(fake, fake, fake, 2, 5000, 8, 2, 64, 2, ctypes.byref(sm), None) == 1
+    assert lib.gqa_softmax_av_decode_plan(None, fake, fake, 2, 100, 8, 2, 64, 2, ctypes.byref(sm), None) == 1
+    assert "scores" in ga.load().gqa_av_last_error().decode()
+    sm0 = ga.make_plan(0, 100, 8, 2, 64, "bf16", softmax=True)
+    assert lib.gqa_softmax_av_decode_plan(None, None, None, 0, 100, 8, 2, 64, 2, ctypes.byref(sm0), None) == 0

@@ -80,6 +80,7 @@ def _check_plan(p, B, C, Hq, Hkv, D):
     assert p.lanes_per_row == HT * D // 8 and p.row_slots == 32 * WPH
     lanes = np.arange(64)
     cnt = np.zeros((B, Hq, D), np.int64)
+    scnt = np.zeros((ns, B, Hq), np.int64)          # fused softmax: split statistics written
     nkvt = Hkv // HT
     for blk in range(p.grid):
         t = _remap(blk, p.grid)
@@ -129,7 +130,17 @@ def _check_plan(p, B, C, Hq, Hkv, D):
             h = 16 * ss + 4 * (l >> 4) + i
             ok = h < nq
             np.add.at(cnt, (b, qf + k[ok] * G + h[ok], 16 * tt[ok] + (l[ok] & 15)), 1)
+            # the head the fused softmax normalises output idx by (nsplit == 1)
+            hs = 16 * ((reg >> 2) // (D // 16)) + 4 * ((e & 63) >> 4) + (reg & 3)
+            assert np.array_equal(hs, h)
+        if p.softmax and ns > 1:
+            for t2 in range(HT * GT):
+                k2, hh = t2 // GT, t2 % GT
+                if hh < nq:
+                    scnt[s, b, qf + k2 * G + hh] += 1
     assert (cnt == 1).all()
+    if p.softmax and ns > 1:
+        assert (scnt == 1).all(), "each split's statistics of each (b, q_h) are written once"
 
 
 @pytest.mark.parametrize("B,C,Hq,Hkv,D", [(1, 300, 16, 1, 128), (2, 1000, 16, 2, 64), (2, 130, 40, 2, 64),
@@ -137,12 +148,13 @@ def _check_plan(p, B, C, Hq, Hkv, D):
                                          (2, 700, 32, 4, 128), (1, 300, 48, 4, 256), (3, 1500, 16, 2, 64)])
 def test_bf16_engine_plan_bounds(B, C, Hq, Hkv, D):
     for ns in (0, 1, 3, 7):
-        for comb in ("kernel", "last"):
+        for comb, sm in (("kernel", False), ("last", False), ("kernel", True)):
             for ht in (0, 1, 2, 4):
                 if ht > 1 and Hkv % ht:
                     continue
                 p = ga.make_plan(B, C, Hq, Hkv, D, "bf16", "reuse", engine="mfma_bf16", nsplit=ns,
-                                 combine=comb, kv_tile=ht)
+                                 combine=comb, kv_tile=ht, softmax=sm)
+                assert p.softmax == int(sm)
                 _check_plan(p, B, C, Hq, Hkv, D)
 
 
@@ -169,6 +181,10 @@ def _check_valu_plan(p, B, C, Hq, Hkv, D, dt):
     r, j = tid // Lc, tid % Lc
     kvl = j // L
     cnt = np.zeros((B, Hq, D), np.int64)
+    scnt = np.zeros((ns, B, Hq), np.int64)          # fused softmax: split statistics written
+    if p.softmax:
+        CH = min(GT * E, 32)
+        assert HT <= 4 and rps * HT * GT <= CH * 256, "row-slot statistics must fit the reduction buffer"
     for blk in range(p.grid):
         t = _remap(blk, p.grid)
         minor = t % nminor; t //= nminor
@@ -221,7 +237,19 @@ def _check_valu_plan(p, B, C, Hq, Hkv, D, dt):
                 go = qf + kl * G - ql
                 for g in range(go, go + nq):
                     cnt[b, ql + g, ld * E:(ld + 1) * E] += 1
+        if p.softmax and ns > 1 and dtile == 0:
+            # every row slot has an active first lane per KV head of the tile
+            lead = active & (j - kvl * L == 0)
+            assert sorted(zip(r[lead], kvl[lead])) == [(rr, k) for rr in range(rps) for k in range(HT)]
+            for t2 in range(HT * GT):
+                kl, g = t2 // GT, t2 % GT
+                ql = min(qf + kl * G, Hq - GT)
+                go = qf + kl * G - ql
+                if go <= g < go + nq:
+                    scnt[s, b, ql + g] += 1
     assert (cnt == 1).all()
+    if p.softmax and ns > 1:
+        assert (scnt == 1).all(), "each split's statistics of each (b, q_h) are written once"
 
 
 @pytest.mark.parametrize("B,C,Hq,Hkv,D,dt", [
@@ -236,13 +264,15 @@ def test_valu_engine_plan_bounds(B, C, Hq, Hkv, D, dt):
                 if ht > 1 and (Hkv % ht or mode == "per_head"):
                     continue
                 for align in (0, 2):
-                    try:
-                        p = ga.make_plan(B, C, Hq, Hkv, D, dt, mode, engine="valu", nsplit=ns, kv_tile=ht,
-                                         v_align=align)
-                    except ga.GqaAvError as e:
-                        assert e.name == "UNSUPPORTED"
-                        continue
-                    _check_valu_plan(p, B, C, Hq, Hkv, D, dt)
+                    for sm in (False, True):
+                        try:
+                            p = ga.make_plan(B, C, Hq, Hkv, D, dt, mode, engine="valu", nsplit=ns, kv_tile=ht,
+                                             v_align=align, softmax=sm)
+                        except ga.GqaAvError as e:
+                            assert e.name == "UNSUPPORTED"
+                            continue
+                        assert p.softmax == int(sm)
+                        _check_valu_plan(p, B, C, Hq, Hkv, D, dt)
 
 
 # ---- decode score step -------------------------------------------------------

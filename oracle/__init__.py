@@ -10,7 +10,7 @@ exact fp32 x V products, kv_h = floor(q_h / G). It also holds the decode score
 step that precedes it (not on the page: scale * sum over d of q * K with the
 same head grouping, output in the attn layout) and the fused product that
 takes the scores and applies the softmax over c itself (the page's attn is
-that softmax). ``brute.py`` holds
+that softmax), and both over a paged V cache with per-sequence lengths. ``brute.py`` holds
 pure-Python correctly rounded versions of both for tiny shapes. Every function here is
 pinned by ``tests/test_oracle_pins.py``; none is "parity unpinned".
 """
@@ -61,6 +61,8 @@ class Oracle:
         lib.gqa_qk_oracle.restype = ip
         lib.gqa_softmax_av_oracle.argtypes = [vp, vp, ip, i64, i64, i64, i64, i64, vp, ip]
         lib.gqa_softmax_av_oracle.restype = ip
+        lib.gqa_av_paged_oracle.argtypes = [vp, vp, vp, vp, ip, ip, i64, i64, i64, i64, i64, i64, i64, i64, vp, ip]
+        lib.gqa_av_paged_oracle.restype = ip
         self.lib = lib
 
     @staticmethod
@@ -107,6 +109,25 @@ class Oracle:
         out = np.empty((B, Hq, D), dtype=np.float64)
         rc = self.lib.gqa_softmax_av_oracle(a.ctypes.data, v.ctypes.data, DTYPE_CODE[v_dtype],
                                             B, C, Hq, Hkv, D, out.ctypes.data, nthreads)
+        if rc != 0:
+            raise ValueError(f"oracle rejected the arguments (status {rc})")
+        return out
+
+    def paged(self, w, pages, block_table, seq_lens, v_dtype: str, softmax: bool = False,
+              nthreads: int = 0) -> np.ndarray:
+        """out[B, Hq, D] (float64) for weights (or scores) [B,C,Hq] fp32, pages
+        [num_pages, P, Hkv, D], block_table [B, max_pages] int32, seq_lens [B] int32."""
+        a, v = self._np_inputs(w, pages, v_dtype)
+        bt = np.ascontiguousarray(_as_numpy(block_table, np.int32), dtype=np.int32)
+        ln = np.ascontiguousarray(_as_numpy(seq_lens, np.int32), dtype=np.int32)
+        B, C, Hq = a.shape
+        num_pages, P, Hkv, D = v.shape
+        max_pages = bt.shape[1]
+        assert bt.shape[0] == B and ln.shape == (B,)
+        out = np.empty((B, Hq, D), dtype=np.float64)
+        rc = self.lib.gqa_av_paged_oracle(a.ctypes.data, v.ctypes.data, bt.ctypes.data, ln.ctypes.data,
+                                          DTYPE_CODE[v_dtype], int(bool(softmax)), B, C, Hq, Hkv, D, P, max_pages,
+                                          num_pages, out.ctypes.data, nthreads)
         if rc != 0:
             raise ValueError(f"oracle rejected the arguments (status {rc})")
         return out

@@ -52,6 +52,13 @@
  * e_c = exp(s_c - m) (libm), the sums of e_c * V and of e_c in increasing c,
  * and one division at the end. C = 0 gives zeros (an empty sum, as above); a
  * row whose scores are all -inf gives NaN, as the definition does.
+ *
+ * Paged V (a decode cache layout, not on the page): sequence b has seq_lens[b]
+ * context rows; row c of it lives in page block_table[b][c / page_size], at
+ * row c % page_size of that page, pages being [page_size][Hkv][D] blocks of
+ * one array. The weights (or scores) keep the dense [B][C][Hq] layout with C
+ * the capacity, and only rows c < seq_lens[b] take part: the sums above run
+ * over those rows (a sequence of length 0 gives zeros).
  */
 #include <math.h>
 #include <pthread.h>
@@ -273,6 +280,67 @@ int gqa_softmax_av_oracle(const float *scores, const void *V, int dtype,
 #endif
     for (int64_t i = 0; i < rows; ++i)
         orc_sav_row(scores, V, dtype, C, Hq, Hkv, D, i / Hq, i % Hq, out + i * D);
+    (void)nthreads;
+    return ORC_OK;
+}
+
+/* Paged V, one output row: the plain product (softmax = 0) or the fused
+ * softmax product (softmax = 1) over the rows c < len of sequence b. */
+static void orc_paged_row(const float *w, const void *pages, const int32_t *bt, int dtype, int softmax,
+                          int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int64_t P, int64_t max_pages,
+                          int64_t len, int64_t b, int64_t q, double *acc)
+{
+    const int64_t G = Hq / Hkv;
+    const int64_t kv = q / G;
+    for (int64_t d = 0; d < D; ++d) acc[d] = 0.0;
+    if (len == 0) return;
+    double m = 0.0, l = 0.0;
+    if (softmax) {
+        m = -INFINITY;
+        for (int64_t c = 0; c < len; ++c) {
+            const double s = (double)w[(b * C + c) * Hq + q];
+            if (s > m) m = s;
+        }
+    }
+    for (int64_t c = 0; c < len; ++c) {
+        const double x = (double)w[(b * C + c) * Hq + q];
+        const double a = softmax ? exp(x - m) : x;
+        l += a;
+        const int64_t page = bt[b * max_pages + c / P];
+        const int64_t row = ((page * P + c % P) * Hkv + kv) * D;
+        for (int64_t d = 0; d < D; ++d) acc[d] += a * orc_load(pages, dtype, row + d);
+    }
+    if (softmax)
+        for (int64_t d = 0; d < D; ++d) acc[d] /= l;
+}
+
+/* Full paged output: out[B][Hq][D] in double. Rejects lengths outside [0, C],
+ * block-table entries outside [0, num_pages) for used rows, and a capacity C
+ * above max_pages * P. */
+int gqa_av_paged_oracle(const float *w, const void *pages, const int32_t *block_table, const int32_t *seq_lens,
+                        int dtype, int softmax, int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D,
+                        int64_t P, int64_t max_pages, int64_t num_pages, double *out, int nthreads)
+{
+    int rc = orc_check(dtype, B, C, Hq, Hkv, D);
+    if (rc != ORC_OK) return rc;
+    if (P < 1 || max_pages < 0 || num_pages < 0 || C > max_pages * P) return ORC_BAD_ARG;
+    for (int64_t b = 0; b < B; ++b) {
+        const int64_t len = seq_lens[b];
+        if (len < 0 || len > C) return ORC_BAD_ARG;
+        for (int64_t c = 0; c < len; c += P) {
+            const int64_t page = block_table[b * max_pages + c / P];
+            if (page < 0 || page >= num_pages) return ORC_BAD_ARG;
+        }
+    }
+    pthread_once(&orc_f16_once, orc_f16_fill);
+    const int64_t rows = B * Hq;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int64_t i = 0; i < rows; ++i)
+        orc_paged_row(w, pages, block_table, dtype, softmax, C, Hq, Hkv, D, P, max_pages, seq_lens[i / Hq],
+                      i / Hq, i % Hq, out + i * D);
     (void)nthreads;
     return ORC_OK;
 }

@@ -51,6 +51,18 @@ The fused softmax product (out = softmax over c of the scores, times V):
   * sav_repeat_mha    GQA equals MHA over V repeated G times (bitwise).
   * sav_edges         C = 0 gives zeros; a row of all -inf gives NaN; B = 0
                       gives an empty result.
+
+Paged V (rows of sequence b in pages block_table[b][c // P], lengths seq_lens):
+  * paged_gather      gather each sequence's rows with numpy into a dense
+                      cache and run the dense oracles on its first len rows:
+                      equal bit for bit (plain and fused softmax).
+  * paged_identity    one page per sequence of P = C rows and full lengths is
+                      the dense layout: equal to the dense oracles bit for bit.
+  * paged_ignores_tail  weights, scores and V rows at or past a sequence's
+                      length, and unused pages, change nothing; length 0 gives
+                      zeros.
+  * paged_rejects     block-table entries outside the cache, lengths outside
+                      [0, C] and C above max_pages * P are rejected.
 """
 from __future__ import annotations
 
@@ -476,9 +488,97 @@ def pin_sav_edges(orc):
     assert np.isnan(o[0, 1]).all() and np.isfinite(o[0, 0]).all(), "sav: a row of all -inf gives NaN"
 
 
+def _paged_case(B, C, Hq, Hkv, D, P, dt, seed, lens=None):
+    """Random weights, a shuffled page pool with spare pages, a block table and lengths."""
+    g = torch.Generator().manual_seed(seed)
+    max_pages = -(-C // P)
+    num_pages = B * max_pages + 3
+    s, _ = make_scores_random(B, C, Hq, Hkv, D, "f32", seed=seed)
+    pages = torch.randn(num_pages, P, Hkv, D, generator=g).to({"f32": torch.float32, "f16": torch.float16,
+                                                               "bf16": torch.bfloat16}[dt])
+    perm = torch.randperm(num_pages, generator=g)[:B * max_pages].to(torch.int32)
+    bt = perm.view(B, max_pages).contiguous()
+    if lens is None:
+        lens = torch.randint(0, C + 1, (B,), generator=g, dtype=torch.int32)
+    return s, pages, bt, torch.as_tensor(lens, dtype=torch.int32)
+
+
+def _gather(pages, bt, b, n):
+    P = pages.shape[1]
+    rows = [pages[int(bt[b, c // P]), c % P] for c in range(n)]
+    return torch.stack(rows, 0) if rows else pages[:0, 0]
+
+
+def pin_paged_gather(orc):
+    for i, (B, C, Hq, Hkv, D, P, dt) in enumerate([(3, 50, 4, 2, 8, 16, "f32"), (2, 33, 6, 3, 5, 4, "bf16"),
+                                                   (2, 64, 8, 1, 16, 8, "f16"), (1, 7, 2, 2, 3, 1, "f32")]):
+        s, pages, bt, lens = _paged_case(B, C, Hq, Hkv, D, P, dt, seed=800 + i)
+        lens[0] = C
+        w = torch.softmax(s.double(), dim=1).float()
+        for sm, x in ((False, w), (True, s)):
+            o = orc.paged(x, pages, bt, lens, dt, softmax=sm)
+            for b in range(B):
+                n = int(lens[b])
+                Vb = _gather(pages, bt, b, n).unsqueeze(0).contiguous()
+                xb = x[b:b + 1, :n].contiguous()
+                ref = orc.softmax_av(xb, Vb, dt) if sm else orc.full(xb, Vb, dt)
+                assert np.array_equal(o[b], ref[0]), f"paged gather {dt} softmax={sm} b={b}"
+
+
+def pin_paged_identity(orc):
+    for dt in ("f32", "bf16"):
+        B, C, Hq, Hkv, D = 3, 21, 6, 2, 7
+        s, V = make_scores_random(B, C, Hq, Hkv, D, dt, seed=811)
+        bt = torch.arange(B, dtype=torch.int32).view(B, 1)
+        lens = torch.full((B,), C, dtype=torch.int32)
+        w = torch.softmax(s.double(), dim=1).float()
+        assert np.array_equal(orc.paged(w, V, bt, lens, dt), orc.full(w, V, dt)), f"paged identity {dt}"
+        assert np.array_equal(orc.paged(s, V, bt, lens, dt, softmax=True), orc.softmax_av(s, V, dt)), \
+            f"paged identity softmax {dt}"
+
+
+def pin_paged_ignores_tail(orc):
+    B, C, Hq, Hkv, D, P = 3, 40, 4, 2, 6, 8
+    s, pages, bt, lens = _paged_case(B, C, Hq, Hkv, D, P, "f32", seed=821, lens=[17, 0, 40])
+    for sm in (False, True):
+        a = orc.paged(s, pages, bt, lens, "f32", softmax=sm)
+        s2, p2 = s.clone(), pages.clone()
+        s2[0, 17:] = 99.0
+        s2[1] = -5.0
+        used = {int(bt[b, c // P]) for b in range(B) for c in range(int(lens[b]))}
+        for pg in range(pages.shape[0]):
+            if pg not in used:
+                p2[pg] = 1e30
+        p2[int(bt[0, 17 // P]), 17 % P:] = -7.0            # rows 17.. of sequence 0's third page
+        b2 = orc.paged(s2, p2, bt, lens, "f32", softmax=sm)
+        assert np.array_equal(a, b2), f"paged: rows past a length must not count (softmax={sm})"
+        assert (a[1] == 0).all(), "paged: a sequence of length 0 gives zeros"
+
+
+def pin_paged_rejects(orc):
+    B, C, Hq, Hkv, D, P = 2, 20, 4, 2, 4, 8
+    s, pages, bt, lens = _paged_case(B, C, Hq, Hkv, D, P, "f32", seed=831, lens=[20, 9])
+    for bad in ("page", "len", "neg", "capacity"):
+        bt2, ln2, s2 = bt.clone(), lens.clone(), s
+        if bad == "page":
+            bt2[1, 1] = pages.shape[0]
+        elif bad == "len":
+            ln2[0] = C + 1
+        elif bad == "neg":
+            ln2[1] = -1
+        else:
+            s2 = torch.zeros(B, bt.shape[1] * P + 1, Hq)
+        try:
+            orc.paged(s2, pages, bt2, ln2, "f32")
+        except ValueError:
+            continue
+        raise AssertionError(f"paged oracle accepted a bad {bad}")
+
+
 ALL_PINS = [pin_decode_table, pin_brute_force, pin_mha_einsum, pin_repeat_mha, pin_constant_v,
             pin_one_hot, pin_linearity, pin_permutation, pin_batch_independence, pin_points,
             pin_edges, pin_qk_brute_force, pin_qk_mha_einsum, pin_qk_repeat_mha, pin_qk_one_hot,
             pin_qk_scale_linear, pin_qk_composition, pin_qk_edges, pin_sav_library, pin_sav_shift,
             pin_sav_large, pin_sav_one_hot, pin_sav_uniform, pin_sav_two_rows, pin_sav_mask,
-            pin_sav_repeat_mha, pin_sav_edges]
+            pin_sav_repeat_mha, pin_sav_edges, pin_paged_gather, pin_paged_identity, pin_paged_ignores_tail,
+            pin_paged_rejects]

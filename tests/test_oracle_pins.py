@@ -61,6 +61,15 @@ PLANTS = [
      "for (int64_t c = 0; c < C - 1; ++c) {\n        const double e"),
     ("sav_weight_sum_squared", "l += e;", "l += e * e;"),
     ("sav_max_is_first", "if (s > m) m = s;", "if (c == 0) m = s;"),
+    # (paged plants keep every access inside the arrays: a mutant runs in this process)
+    ("paged_bt_no_row_stride", "const int64_t page = bt[b * max_pages + c / P];",
+     "const int64_t page = bt[b + c / P];"),
+    ("paged_reversed_in_page", "const int64_t row = ((page * P + c % P) * Hkv + kv) * D;",
+     "const int64_t row = ((page * P + (P - 1 - c % P)) * Hkv + kv) * D;"),
+    ("paged_ignores_len", "for (int64_t c = 0; c < len; ++c) {\n        const double x",
+     "for (int64_t c = 0; c < C; ++c) {\n        const double x"),
+    ("paged_bt_ignores_batch", "const int64_t page = bt[b * max_pages + c / P];",
+     "const int64_t page = bt[0 * max_pages + c / P];"),
 ]
 
 

@@ -27,6 +27,7 @@ __all__ = [
     "LIB_PATH", "GqaAvError", "Hint", "Plan", "load", "resolve_mode", "make_plan",
     "gqa_av_decode", "gqa_av_decode_plan", "bind", "BoundCall", "release", "status_string", "MODES", "DTYPES",
     "QkHint", "QkPlan", "qk_make_plan", "gqa_qk_decode", "bind_qk", "gqa_softmax_av_decode", "bind_softmax",
+    "gqa_av_paged_decode", "bind_paged",
 ]
 
 # GQA_AV_LIBRARY may name another build of the same library (tuning variants).
@@ -49,7 +50,7 @@ class GqaAvError(RuntimeError):
 class Hint(ctypes.Structure):
     _fields_ = [("engine", ctypes.c_int32), ("nsplit", ctypes.c_int32), ("cu_count", ctypes.c_int32),
                 ("v_align", ctypes.c_int32), ("combine", ctypes.c_int32), ("kv_tile", ctypes.c_int32),
-                ("softmax", ctypes.c_int32), ("reserved", ctypes.c_int32 * 1)]
+                ("softmax", ctypes.c_int32), ("page_size", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2)]
 
 
 class Plan(ctypes.Structure):
@@ -59,7 +60,7 @@ class Plan(ctypes.Structure):
                 ("threads", ctypes.c_int32), ("rows_per_split", ctypes.c_int64), ("grid", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_int64), ("v_bytes_read", ctypes.c_int64),
                 ("combine", ctypes.c_int32), ("kv_heads_per_tile", ctypes.c_int32), ("softmax", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 1)]
+                ("page_size", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
@@ -113,6 +114,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     for fn in ("gqa_softmax_av_decode_plan", "gqa_softmax_av_decode_pass1", "gqa_softmax_av_decode_combine"):
         getattr(lib, fn).argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ip, ctypes.POINTER(Plan), vp]
         getattr(lib, fn).restype = ip
+    lib.gqa_av_paged_decode.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, ip, ip, ip, vp]
+    lib.gqa_av_paged_decode.restype = ip
+    lib.gqa_av_paged_decode_plan.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, ip,
+                                             ctypes.POINTER(Plan), vp]
+    lib.gqa_av_paged_decode_plan.restype = ip
     lib.gqa_av_status_string.argtypes = [ip]
     lib.gqa_av_status_string.restype = ctypes.c_char_p
     lib.gqa_av_last_error.argtypes = []
@@ -158,17 +164,20 @@ def resolve_mode(Hq: int, Hkv: int, mode: Union[str, int] = "auto") -> str:
 
 def make_plan(B: int, C: int, Hq: int, Hkv: int, D: int, v_dtype: str, mode: Union[str, int] = "auto",
               engine: Union[str, int] = "auto", nsplit: int = 0, cu_count: int = 0, v_align: int = 0,
-              combine: Union[str, int] = "auto", kv_tile: int = 0, softmax: bool = False) -> Plan:
+              combine: Union[str, int] = "auto", kv_tile: int = 0, softmax: bool = False,
+              page_size: int = 0) -> Plan:
     """Host-only planning (no GPU needed). nsplit/cu_count/v_align/kv_tile <= 0 mean automatic.
 
     engine: "auto" | "valu" | "mfma" | "mfma_bf16"; combine: "auto" | "kernel" | "last";
-    kv_tile: adjacent KV heads per workgroup; softmax: plan the fused softmax product.
+    kv_tile: adjacent KV heads per workgroup; softmax: plan the fused softmax product;
+    page_size > 0: plan for a paged V cache with that many rows per page.
     """
     h = Hint()
     h.engine = ENGINES[engine] if isinstance(engine, str) else int(engine)
     h.combine = COMBINES[combine] if isinstance(combine, str) else int(combine)
     h.nsplit, h.cu_count, h.v_align, h.kv_tile = int(nsplit), int(cu_count), int(v_align), int(kv_tile)
     h.softmax = 1 if softmax else 0
+    h.page_size = int(page_size)
     p = Plan()
     rc = load().gqa_av_make_plan(B, C, Hq, Hkv, D, DTYPES[v_dtype], _mode(mode), ctypes.byref(h), ctypes.byref(p))
     if rc != 0:
@@ -325,6 +334,84 @@ def bind_softmax(scores, V, out=None, plan: Optional[Plan] = None, mode: Union[s
                  stream=None) -> BoundCall:
     """A BoundCall of the fused softmax product for (scores, V, out)."""
     return BoundCall(scores, V, out=out, plan=plan, mode=mode, stream=stream, softmax=True)
+
+
+def _check_paged(w, pages, block_table, seq_lens, out):
+    torch = _torch()
+    vmap = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
+    if w.dim() != 3 or pages.dim() != 4 or block_table.dim() != 2 or seq_lens.dim() != 1:
+        raise ValueError("w [B,C,Hq], pages [num_pages,page_size,Hkv,D], block_table [B,max_pages], seq_lens [B]")
+    B, C, Hq = w.shape
+    num_pages, P, Hkv, D = pages.shape
+    if block_table.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("block_table and seq_lens must have B rows")
+    if w.dtype != torch.float32 or pages.dtype not in vmap:
+        raise TypeError("w must be float32 and pages float32/float16/bfloat16")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_table and seq_lens must be int32")
+    ts = (w, pages, block_table, seq_lens)
+    if not all(t.is_cuda and t.device == w.device and t.is_contiguous() for t in ts):
+        raise ValueError("all tensors must be contiguous and on the same GPU")
+    if out is not None and (out.dtype != torch.float32 or tuple(out.shape) != (B, Hq, D) or not out.is_contiguous()
+                            or out.device != w.device):
+        raise ValueError(f"out must be a contiguous float32 [{B},{Hq},{D}] tensor on {w.device}")
+    return B, C, Hq, Hkv, D, P, block_table.shape[1], num_pages, vmap[pages.dtype]
+
+
+def gqa_av_paged_decode(w, pages, block_table, seq_lens, out=None, softmax: bool = False,
+                        mode: Union[str, int] = "auto", stream=None, plan: Optional[Plan] = None):
+    """The AV product (or, softmax=True, the fused softmax product on scores w)
+    over a paged V cache: row c of sequence b is pages[block_table[b, c // P], c % P];
+    only rows c < seq_lens[b] count. w: float32 [B,C,Hq] (C the capacity);
+    pages: [num_pages,P,Hkv,D]; block_table: int32 [B,max_pages]; seq_lens: int32 [B]."""
+    torch = _torch()
+    B, C, Hq, Hkv, D, P, maxp, npg, vdt = _check_paged(w, pages, block_table, seq_lens, out)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=w.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(w.device)
+    lib = load()
+    args = (w.data_ptr(), pages.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
+            B, C, Hq, Hkv, D, P, maxp, npg, DTYPES[vdt])
+    with torch.cuda.device(w.device):
+        if plan is None:
+            rc = lib.gqa_av_paged_decode(*args, 1 if softmax else 0, _mode(mode), stream.cuda_stream)
+        else:
+            rc = lib.gqa_av_paged_decode_plan(*args, ctypes.byref(plan), stream.cuda_stream)
+    if rc != 0:
+        _raise(rc)
+    return out
+
+
+class BoundPaged:
+    """A paged call with checked, bound arguments for loops (see BoundCall)."""
+
+    def __init__(self, w, pages, block_table, seq_lens, out=None, plan: Optional[Plan] = None, softmax: bool = False,
+                 mode: Union[str, int] = "auto", stream=None):
+        torch = _torch()
+        B, C, Hq, Hkv, D, P, maxp, npg, vdt = _check_paged(w, pages, block_table, seq_lens, out)
+        if out is None:
+            out = torch.empty((B, Hq, D), dtype=torch.float32, device=w.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(w.device)
+        if plan is None:
+            cu = torch.cuda.get_device_properties(w.device).multi_processor_count
+            plan = make_plan(B, C, Hq, Hkv, D, vdt, mode, cu_count=cu, softmax=softmax, page_size=P)
+        self.tensors, self.out, self.plan = (w, pages, block_table, seq_lens), out, plan
+        self._fn = load().gqa_av_paged_decode_plan
+        self._args = (w.data_ptr(), pages.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
+                      B, C, Hq, Hkv, D, P, maxp, npg, DTYPES[vdt], ctypes.byref(plan), stream.cuda_stream)
+
+    def __call__(self):
+        rc = self._fn(*self._args)
+        if rc != 0:
+            _raise(rc)
+        return self.out
+
+
+def bind_paged(w, pages, block_table, seq_lens, out=None, plan: Optional[Plan] = None, softmax: bool = False,
+               mode: Union[str, int] = "auto", stream=None) -> BoundPaged:
+    return BoundPaged(w, pages, block_table, seq_lens, out=out, plan=plan, softmax=softmax, mode=mode, stream=stream)
 
 
 def release() -> None:

@@ -48,6 +48,7 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kXcds = 8;          // MI355X: 8 accelerator complex dies, one L2 each
 constexpr int kMaxRowSlots = 64;  // rows a VALU workgroup loads side by side, at most
+constexpr int kMaxSplitPages = 1024;  // paged V: pages one context split may touch (its page list sits in LDS)
 
 // Tuning constants (compile-time; -D overrides build variants for sweeps).
 #ifndef GQA_AV_VALU_UNROLL
@@ -104,6 +105,11 @@ struct Pass1Args {
     float* part;            // combine in kernel: [tiles][nsplit][tile outputs]; else [nsplit][B][Hq][D]
     float* stats;           // fused softmax with nsplit > 1: [nsplit][B][Hq] pairs (maximum score, weight sum),
                             // 16-byte aligned
+    const int32_t* block_table;  // paged V: [B][max_pages], the page of each page-long run of a sequence's rows
+    const int32_t* seq_lens;     // paged V: [B] rows of each sequence (clamped into [0, C])
+    int64_t num_pages;           // paged V: pages in the cache (block-table entries are clamped into range)
+    int32_t page_shift;          // paged V: log2 of the rows per page
+    int32_t max_pages;           // paged V: length of a block-table row
     uint32_t* counters;     // combine in kernel: [tiles], zero between calls
     int32_t combine;        // 1: last workgroup of a tile adds the splits; 0: second kernel
     int64_t C;
@@ -401,8 +407,17 @@ constexpr int padded_heads() { return GT <= 2 ? GT : (GT + 3) / 4 * 4; }
 // to the workgroup's maximum before they are summed; the split's result is the
 // weighted sum divided by the weight sum, or, with several splits, the
 // unnormalised sum with its (maximum, weight sum) for the combine.
-template <int DT, int VB, int GT, int U, bool SM = false>
+//
+// PG: paged V. Sequence b has seq_lens[b] rows; row c is row c % P of page
+// block_table[b][c / P] (P = 2^page_shift rows of Hkv * D values). The
+// workgroup copies the block-table entries its split touches into LDS once
+// (clamped into the cache), and each lane computes its rows' addresses from
+// them; rows past the sequence's length take weight 0 (and read the split's
+// last valid row). The weights keep the dense [B][C][Hq] layout, C being the
+// capacity. Needs 16-byte lane loads.
+template <int DT, int VB, int GT, int U, bool SM = false, bool PG = false>
 __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
+    static_assert(!PG || VB == 16, "paged V takes 16-byte lane loads");
     constexpr int ES = esize<DT>();
     constexpr int E = VB / ES;
     constexpr int NACC = GT * E;
@@ -428,8 +443,13 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
     const bool active = (r < rps) && (lane_d < a.L);
 
     const int64_t cb = static_cast<int64_t>(T.s) * a.rows_per_split;
-    const int64_t ce = min(a.C, cb + a.rows_per_split);
-    const int64_t nrows_split = ce - cb;
+    int64_t ce_ = min(a.C, cb + a.rows_per_split);
+    if constexpr (PG) {
+        const int64_t len = a.seq_lens[T.b];
+        ce_ = min(ce_, len < 0 ? int64_t{0} : min(len, a.C));
+    }
+    const int64_t ce = ce_;
+    const int64_t nrows_split = ce > cb ? ce - cb : 0;
     const int R = rps * U;                           // rows per stage
 
     const size_t vrow = static_cast<size_t>(a.Hkv) * a.D * ES;   // bytes from row c to c+1
@@ -448,7 +468,7 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
     __shared__ float s_stat[2][4 * GT];              // SM: the workgroup's maximum and weight sum per head
 
 #if GQA_AV_VALU_STAGE_WEIGHTS
-    static_assert(!SM, "the fused softmax needs the per-lane weight path");
+    static_assert(!SM && !PG, "the fused softmax and paged V need the per-lane weight path");
     const uint8_t* vbase = a.V + (static_cast<size_t>(T.b) * a.C * a.Hkv + T.kv + kvl) * a.D * ES
                                + static_cast<size_t>(lane_d) * VB;
     const int q_lo = T.q_first;                      // accumulator g is head q_lo + g (tiles of one KV head)
@@ -572,7 +592,7 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
     // step is a full one, and a row's address is a per-lane constant plus a
     // workgroup-uniform offset held in a scalar register. The plan keeps a
     // split's span under 1 GB so 32-bit offsets suffice.
-    const int nrows = static_cast<int>(uniform64(ce - cb));
+    const int nrows = static_cast<int>(uniform64(nrows_split));
     const int vrow32 = static_cast<int>(vrow);
     const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(a.V) + ((static_cast<size_t>(T.b) * a.C + cb) * a.Hkv + T.kv) * a.D * ES, 0,
@@ -583,6 +603,20 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
     const int voff = r * vrow32 + (kvl * a.D * ES + lane_d * VB);
     const int woff = (r * a.Hq + q_lo) * 4;
     const int nsteps = (nrows + R - 1) / R;
+    // PG: the split's pages, from the block table into LDS.
+    __shared__ int32_t s_pages[PG ? kMaxSplitPages : 1];
+    const int64_t pg0 = PG ? (cb >> a.page_shift) : 0;
+    if constexpr (PG) {
+        const int npg = nrows > 0 ? static_cast<int>(((cb + nrows - 1) >> a.page_shift) - pg0 + 1) : 0;
+        const int32_t* const btr = a.block_table + static_cast<size_t>(T.b) * a.max_pages + pg0;
+        for (int i = tid; i < npg; i += kThreads) {
+            const int32_t pg = btr[i];
+            s_pages[i] = pg < 0 ? 0 : (pg >= a.num_pages ? static_cast<int32_t>(a.num_pages - 1) : pg);
+        }
+        __syncthreads();
+    }
+    const int64_t pmask = PG ? (int64_t{1} << a.page_shift) - 1 : 0;
+    const int pcol = (T.kv + kvl) * a.D * ES + lane_d * VB;     // PG: this lane's bytes inside a row of a page
     struct Buf {
         Raw<VB> v[U];
         float w[U][GT];
@@ -591,7 +625,14 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int row = st * R + u * rps;        // of this step's slot 0; the lane adds r
-            bf.v[u] = load_raw_buf<VB>(vres, voff, row * vrow32);
+            if constexpr (PG) {
+                // Rows past the split read its last row (their weight is 0).
+                const int64_t c = cb + min(row + r, nrows - 1);
+                const int64_t page = s_pages[(c >> a.page_shift) - pg0];
+                bf.v[u] = load_raw<VB>(a.V + ((page << a.page_shift) + (c & pmask)) * vrow + pcol);
+            } else {
+                bf.v[u] = load_raw_buf<VB>(vres, voff, row * vrow32);
+            }
             load_floats<GT>(wres, woff, row * a.Hq * 4, bf.w[u]);
         }
     };

@@ -8,6 +8,7 @@
 // also caps G at 8 and sends larger groups to the per-head kernel; that cap
 // is not kept: any G takes the reuse path (G > 16 in sub-groups of 16 heads).
 #include "gqa_av.h"
+#include "gqa_paged_av.h"
 #include "gqa_softmax_av.h"
 
 #include <hip/hip_runtime.h>
@@ -154,32 +155,38 @@ int check_sizes(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_
 
 // ---- kernel dispatch ----------------------------------------------------------
 
-template <int DT, int VB, int GT, bool SM>
+template <int DT, int VB, int GT, bool SM, bool PG>
 hipError_t launch_valu(const Pass1Args& a, hipStream_t s) {
     constexpr int U = gqa_av::valu_unroll(GT);
-    if constexpr (SM && GQA_AV_VALU_STAGE_WEIGHTS) {
+    if constexpr ((SM || PG) && GQA_AV_VALU_STAGE_WEIGHTS) {
         return hipErrorInvalidValue;                 // the plan refuses this combination
     } else {
-        hipLaunchKernelGGL((gqa_av::av_pass1_valu<DT, VB, GT, U, SM>), dim3(a.nblocks), dim3(gqa_av::kThreads), 0,
-                           s, a);
+        hipLaunchKernelGGL((gqa_av::av_pass1_valu<DT, VB, GT, U, SM, PG>), dim3(a.nblocks), dim3(gqa_av::kThreads),
+                           0, s, a);
         return hipGetLastError();
     }
 }
 
-template <int DT, int VB, bool SM>
+template <int DT, int VB, bool SM, bool PG = false>
 hipError_t launch_valu_gt(int GT, const Pass1Args& a, hipStream_t s) {
     switch (GT) {
-    case 1: return launch_valu<DT, VB, 1, SM>(a, s);
-    case 2: return launch_valu<DT, VB, 2, SM>(a, s);
-    case 3: return launch_valu<DT, VB, 3, SM>(a, s);
-    case 4: return launch_valu<DT, VB, 4, SM>(a, s);
-    case 5: return launch_valu<DT, VB, 5, SM>(a, s);
-    case 6: return launch_valu<DT, VB, 6, SM>(a, s);
-    case 7: return launch_valu<DT, VB, 7, SM>(a, s);
-    case 8: return launch_valu<DT, VB, 8, SM>(a, s);
-    case 16: return launch_valu<DT, VB, 16, SM>(a, s);
+    case 1: return launch_valu<DT, VB, 1, SM, PG>(a, s);
+    case 2: return launch_valu<DT, VB, 2, SM, PG>(a, s);
+    case 3: return launch_valu<DT, VB, 3, SM, PG>(a, s);
+    case 4: return launch_valu<DT, VB, 4, SM, PG>(a, s);
+    case 5: return launch_valu<DT, VB, 5, SM, PG>(a, s);
+    case 6: return launch_valu<DT, VB, 6, SM, PG>(a, s);
+    case 7: return launch_valu<DT, VB, 7, SM, PG>(a, s);
+    case 8: return launch_valu<DT, VB, 8, SM, PG>(a, s);
+    case 16: return launch_valu<DT, VB, 16, SM, PG>(a, s);
     default: return hipErrorInvalidValue;
     }
+}
+
+// Paged V: 16-byte lane loads only.
+template <int DT>
+hipError_t launch_valu_paged(bool sm, int GT, const Pass1Args& a, hipStream_t s) {
+    return sm ? launch_valu_gt<DT, 16, true, true>(GT, a, s) : launch_valu_gt<DT, 16, false, true>(GT, a, s);
 }
 
 template <int DT, bool SM>
@@ -255,6 +262,15 @@ hipError_t launch_mfma_de(int DE, int nset, const Pass1Args& a, hipStream_t s) {
 }
 
 hipError_t launch_pass1(int v_dtype, const gqa_av_plan& p, int64_t D, const Pass1Args& a, hipStream_t s) {
+    if (p.page_size > 0) {
+        if (p.engine != GQA_AV_ENGINE_VALU || p.vec_bytes != 16) return hipErrorInvalidValue;
+        switch (v_dtype) {
+        case GQA_AV_F32: return launch_valu_paged<gqa_av::kF32>(p.softmax, p.heads_per_tile, a, s);
+        case GQA_AV_F16: return launch_valu_paged<gqa_av::kF16>(p.softmax, p.heads_per_tile, a, s);
+        case GQA_AV_BF16: return launch_valu_paged<gqa_av::kBF16>(p.softmax, p.heads_per_tile, a, s);
+        default: return hipErrorInvalidValue;
+        }
+    }
     if (p.engine == GQA_AV_ENGINE_MFMA_BF16) {
         if (v_dtype != GQA_AV_BF16) return hipErrorInvalidValue;
         return p.softmax ? launch_mfma_bf16_pr<true>(D, p.heads_per_tile / 16, p.kv_heads_per_tile, a, s)
@@ -354,6 +370,16 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
         return fail(GQA_AV_ERR_INVALID_ARG, "unknown combine %d", h.combine);
     if (h.softmax != 0 && h.softmax != 1) return fail(GQA_AV_ERR_INVALID_ARG, "hint softmax must be 0 or 1");
     const bool sm = h.softmax == 1;
+    // Paged V: the VALU engine with 16-byte lane loads, the kernel combine,
+    // and splits short enough for their page list to fit in LDS.
+    const int64_t P = h.page_size;
+    const bool paged = P > 0;
+    if (P < 0 || (paged && (P & (P - 1)) != 0))
+        return fail(GQA_AV_ERR_INVALID_ARG, "page_size %lld must be a power of two", (long long)P);
+    if (paged && (h.engine == GQA_AV_ENGINE_MFMA || h.engine == GQA_AV_ENGINE_MFMA_BF16))
+        return fail(GQA_AV_ERR_UNSUPPORTED, "paged V runs on the VALU engine");
+    if (paged && GQA_AV_VALU_STAGE_WEIGHTS)
+        return fail(GQA_AV_ERR_UNSUPPORTED, "paged V needs the per-lane weight VALU build");
     const int cus = h.cu_count > 0 ? h.cu_count : cu_default;
     const int v_align = h.v_align > 0 ? h.v_align : 16;
 
@@ -370,6 +396,7 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
     const int nset16 = (G > 16 && mfma_bf16_fits(v_dtype, Hq, Hkv, D, v_align, 2)) ? 2 : 1;
     const bool mfma16_ok = resolved == GQA_AV_REUSE && mfma_bf16_fits(v_dtype, Hq, Hkv, D, v_align, nset16);
     int engine = h.engine;
+    if (engine == GQA_AV_ENGINE_AUTO && paged) engine = GQA_AV_ENGINE_VALU;
     if (engine == GQA_AV_ENGINE_AUTO) {
         engine = GQA_AV_ENGINE_VALU;
         if (G >= kMfmaMinGroup && mfma16_ok) engine = GQA_AV_ENGINE_MFMA_BF16;
@@ -457,6 +484,8 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
         }
         if (VB == 0)
             return fail(GQA_AV_ERR_UNSUPPORTED, "V must be aligned to its element size (%d bytes)", es);
+        if (paged && VB != 16)
+            return fail(GQA_AV_ERR_UNSUPPORTED, "paged V needs rows of whole 16-byte pieces and 16-byte aligned pages");
         const int64_t E = VB / es;
         const int64_t L = D / E;
         if (ht > 1) {
@@ -516,6 +545,18 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
             }
         }
     }
+    if (paged && C > 0) {
+        // A split of R rows touches at most ceil(R / P) + 1 pages.
+        const int64_t max_rows = (gqa_av::kMaxSplitPages - 1) * P;
+        if (rows_per_split > max_rows) {
+            if (h.nsplit > 0)
+                return fail(GQA_AV_ERR_UNSUPPORTED, "paged V: a split of %lld rows spans more than %d pages",
+                            (long long)rows_per_split, gqa_av::kMaxSplitPages);
+            rows_per_split = max_rows / rows_per_step * rows_per_step;
+            if (rows_per_split < 1) rows_per_split = max_rows;
+            nsplit = ceil_div(C, rows_per_split);
+        }
+    }
     if (nsplit > INT32_MAX) return fail(GQA_AV_ERR_UNSUPPORTED, "too many context splits");
     const int64_t grid = tiles * nsplit;
     if (grid > INT32_MAX) return fail(GQA_AV_ERR_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)grid);
@@ -540,7 +581,7 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
         // workload (the last-workgroup combine pays for device-coherent
         // stores and loads of the partials), so it is the automatic choice.
         if (combine == GQA_AV_COMBINE_AUTO) combine = GQA_AV_COMBINE_KERNEL;
-        if (sm && combine != GQA_AV_COMBINE_KERNEL)
+        if ((sm || paged) && combine != GQA_AV_COMBINE_KERNEL)
             return fail(GQA_AV_ERR_UNSUPPORTED, "the fused softmax combines its splits in a second kernel");
         // One tile's block is addressed through a 32-bit buffer offset.
         if (combine == GQA_AV_COMBINE_LAST && nsplit * gqa_av::padded_outputs(static_cast<int>(tile_outputs)) * 4 > INT32_MAX)
@@ -551,6 +592,7 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
     plan->workspace_bytes = workspace_bytes(B, Hq, D, tiles, nsplit, tile_outputs, combine, sm);
     plan->v_bytes_read = B * C * Hkv * D * es * heads_major;
     plan->softmax = sm ? 1 : 0;
+    plan->page_size = static_cast<int32_t>(P);
     return GQA_AV_OK;
 }
 
@@ -560,7 +602,7 @@ bool same_plan(const gqa_av_plan& a, const gqa_av_plan& b) {
            a.row_slots == b.row_slots && a.d_tiles == b.d_tiles && a.nsplit == b.nsplit &&
            a.threads == b.threads && a.rows_per_split == b.rows_per_split && a.grid == b.grid &&
            a.workspace_bytes == b.workspace_bytes && a.kv_heads_per_tile == b.kv_heads_per_tile &&
-           a.softmax == b.softmax;
+           a.softmax == b.softmax && a.page_size == b.page_size;
 }
 
 }  // namespace
@@ -604,12 +646,35 @@ constexpr int kRunPass1 = 1, kRunCombine = 2;
 // Validate (attn, V, out, sizes, plan) and launch the parts of the call named
 // by `which`. Validation is the same for every part, so a caller splitting
 // the call gets the same errors as gqa_av_decode_plan.
-// softmax: 1 for the fused softmax entry point (attn then holds the scores).
+// The paged-cache arguments of gqa_av_paged_decode_plan.
+struct PagedArgs {
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    int64_t page_size, max_pages, num_pages;
+};
+
+// softmax: 1 for the fused softmax entry points (attn then holds the scores);
+// pg: the paged cache (V then points at its pages), or NULL for dense V.
 int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
-             int64_t D, int v_dtype, const gqa_av_plan* plan, void* stream, int which, int softmax) {
+             int64_t D, int v_dtype, const gqa_av_plan* plan, void* stream, int which, int softmax,
+             const PagedArgs* pg = nullptr) {
     if (!plan) return fail(GQA_AV_ERR_INVALID_ARG, "plan is NULL");
     int rc = check_sizes(B, C, Hq, Hkv, D, v_dtype);
     if (rc != GQA_AV_OK) return rc;
+    if ((plan->page_size > 0) != (pg != nullptr))
+        return fail(GQA_AV_ERR_INVALID_ARG, pg ? "not a paged plan (plan->page_size == 0)"
+                                                : "a paged plan: run it with gqa_av_paged_decode_plan");
+    if (pg) {
+        if (pg->page_size != plan->page_size)
+            return fail(GQA_AV_ERR_INVALID_ARG, "page_size %lld does not match the plan's %d",
+                        (long long)pg->page_size, plan->page_size);
+        if (pg->max_pages < 1 || pg->max_pages > INT32_MAX || pg->num_pages < 1)
+            return fail(GQA_AV_ERR_INVALID_ARG, "max_pages and num_pages must be >= 1 (max_pages < 2^31)");
+        if (C > pg->max_pages * pg->page_size)
+            return fail(GQA_AV_ERR_INVALID_ARG, "capacity C=%lld exceeds max_pages * page_size", (long long)C);
+        if (B > 0 && (!pg->block_table || !pg->seq_lens))
+            return fail(GQA_AV_ERR_INVALID_ARG, "block_table and seq_lens must not be NULL");
+    }
     if (plan->softmax != softmax)
         return fail(GQA_AV_ERR_INVALID_ARG, softmax ? "not a fused softmax plan (plan->softmax == 0)"
                                                     : "a fused softmax plan: run it with gqa_softmax_av_decode_plan");
@@ -622,6 +687,7 @@ int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C,
     h.combine = plan->combine;
     h.kv_tile = plan->kv_heads_per_tile;
     h.softmax = plan->softmax;
+    h.page_size = plan->page_size;
     gqa_av_plan check;
     const int mode = plan->mode;
     // Re-plan with the split count fixed: rows_per_split then follows from C.
@@ -689,6 +755,13 @@ int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C,
     a.part = part;
     a.stats = (softmax && plan->nsplit > 1) ? part + stats_offset(plan->nsplit, B, Hq, D) : nullptr;
     a.counters = counters;
+    a.block_table = pg ? pg->block_table : nullptr;
+    a.seq_lens = pg ? pg->seq_lens : nullptr;
+    a.num_pages = pg ? pg->num_pages : 0;
+    a.max_pages = pg ? static_cast<int32_t>(pg->max_pages) : 0;
+    a.page_shift = 0;
+    if (pg)
+        while ((int64_t{1} << a.page_shift) < pg->page_size) ++a.page_shift;
     a.combine = last ? 1 : 0;
     a.C = C;
     a.rows_per_split = plan->rows_per_split;
@@ -750,7 +823,7 @@ int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C,
 
 // The automatic plan for the current device and V's address alignment.
 int auto_plan(const void* V, int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dtype, int mode,
-              int softmax, gqa_av_plan* plan) {
+              int softmax, gqa_av_plan* plan, int64_t page_size = 0) {
     int rc = check_sizes(B, C, Hq, Hkv, D, v_dtype);
     if (rc != GQA_AV_OK) return rc;
     int dev = 0;
@@ -764,6 +837,9 @@ int auto_plan(const void* V, int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int6
     h.engine = GQA_AV_ENGINE_AUTO;
     h.cu_count = cus;
     h.softmax = softmax;
+    if (page_size < 0 || page_size > INT32_MAX)
+        return fail(GQA_AV_ERR_INVALID_ARG, "page_size %lld out of range", (long long)page_size);
+    h.page_size = static_cast<int32_t>(page_size);
     // Alignment of V's address: its lowest set bit, at most 16.
     const uintptr_t addr = reinterpret_cast<uintptr_t>(V);
     const uintptr_t low = addr & (~addr + 1);
@@ -809,6 +885,28 @@ int gqa_softmax_av_decode(const float* scores, const void* V, float* out, int64_
 int gqa_softmax_av_decode_plan(const float* scores, const void* V, float* out, int64_t B, int64_t C, int64_t Hq,
                                int64_t Hkv, int64_t D, int v_dtype, const gqa_av_plan* plan, void* stream) {
     return run_plan(scores, V, out, B, C, Hq, Hkv, D, v_dtype, plan, stream, kRunPass1 | kRunCombine, 1);
+}
+
+int gqa_av_paged_decode(const float* w, const void* pages, const int32_t* block_table, const int32_t* seq_lens,
+                        float* out, int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int64_t page_size,
+                        int64_t max_pages, int64_t num_pages, int v_dtype, int softmax, int mode, void* stream) {
+    if (softmax != 0 && softmax != 1) return fail(GQA_AV_ERR_INVALID_ARG, "softmax must be 0 or 1");
+    if (page_size < 1) return fail(GQA_AV_ERR_INVALID_ARG, "page_size must be >= 1");
+    gqa_av_plan plan;
+    int rc = auto_plan(pages, B, C, Hq, Hkv, D, v_dtype, mode, softmax, &plan, page_size);
+    if (rc != GQA_AV_OK) return rc;
+    return gqa_av_paged_decode_plan(w, pages, block_table, seq_lens, out, B, C, Hq, Hkv, D, page_size, max_pages,
+                                    num_pages, v_dtype, &plan, stream);
+}
+
+int gqa_av_paged_decode_plan(const float* w, const void* pages, const int32_t* block_table,
+                             const int32_t* seq_lens, float* out, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
+                             int64_t D, int64_t page_size, int64_t max_pages, int64_t num_pages, int v_dtype,
+                             const gqa_av_plan* plan, void* stream) {
+    if (!plan) return fail(GQA_AV_ERR_INVALID_ARG, "plan is NULL");
+    PagedArgs pa{block_table, seq_lens, page_size, max_pages, num_pages};
+    return run_plan(w, pages, out, B, C, Hq, Hkv, D, v_dtype, plan, stream, kRunPass1 | kRunCombine, plan->softmax,
+                    &pa);
 }
 
 int gqa_softmax_av_decode_pass1(const float* scores, const void* V, float* out, int64_t B, int64_t C, int64_t Hq,

@@ -33,6 +33,7 @@ def test_library_exports_every_declared_function():
     assert len(names) >= 10, names
     assert {"gqa_qk_decode", "gqa_qk_decode_plan", "gqa_qk_make_plan"} <= set(names)
     assert {"gqa_softmax_av_decode", "gqa_softmax_av_decode_plan"} <= set(names)
+    assert {"gqa_av_paged_decode", "gqa_av_paged_decode_plan"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/ but not exported"
 
@@ -441,3 +442,58 @@ def test_softmax_and_plain_plans_do_not_mix():
     assert "scores" in ga.load().gqa_av_last_error().decode()
     sm0 = ga.make_plan(0, 100, 8, 2, 64, "bf16", softmax=True)
     assert lib.gqa_softmax_av_decode_plan(None, None, None, 0, 100, 8, 2, 64, 2, ctypes.byref(sm0), None) == 0
+
+
+@pytest.mark.parametrize("wname", list(WORKLOADS))
+def test_paged_plans(wname):
+    """Paged plans: the VALU engine with 16-byte loads, the kernel combine, and
+    splits whose page lists fit the kernel's LDS list (1024 pages)."""
+    w = WORKLOADS[wname]
+    for P in (1, 16, 256):
+        for sm in (False, True):
+            for mode in ("auto", "per_head"):
+                try:
+                    p = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, mode, page_size=P, softmax=sm)
+                except ga.GqaAvError as e:
+                    assert e.name == "UNSUPPORTED" and (w.D * (4 if w.v_dtype == "f32" else 2)) % 16
+                    continue
+                assert p.page_size == P and p.engine == 1 and p.vec_bytes == 16 and p.softmax == int(sm)
+                assert -(-p.rows_per_split // P) + 1 <= 1024
+                assert p.nsplit == 1 or p.combine == 1
+
+
+def test_paged_refusals():
+    for kw, name in ((dict(page_size=12), "INVALID_ARG"), (dict(page_size=16, engine="mfma_bf16"), "UNSUPPORTED"),
+                     (dict(page_size=16, engine="mfma"), "UNSUPPORTED"),
+                     (dict(page_size=16, nsplit=4, combine="last"), "UNSUPPORTED"),
+                     (dict(page_size=1, nsplit=1), "UNSUPPORTED")):          # 4000 rows on 1-row pages: 4000 pages
+        with pytest.raises(ga.GqaAvError) as e:
+            ga.make_plan(4, 4000, 16, 8, 128, "bf16", **kw)
+        assert e.value.name == name, kw
+    with pytest.raises(ga.GqaAvError) as e:
+        ga.make_plan(4, 1000, 16, 8, 100, "bf16", page_size=16)
+    assert e.value.name == "UNSUPPORTED"
+
+
+def test_paged_calls_reject_before_launch():
+    lib = ga.load()
+    fake = ctypes.c_void_p(1 << 20)
+    pg = ga.make_plan(2, 100, 8, 2, 64, "bf16", page_size=16)
+    dense = ga.make_plan(2, 100, 8, 2, 64, "bf16")
+
+    def call(plan, C=100, P=16, maxp=8, npg=16, bt=fake, ln=fake):
+        return lib.gqa_av_paged_decode_plan(fake, fake, bt, ln, fake, 2, C, 8, 2, 64, P, maxp, npg, 2,
+                                            ctypes.byref(plan), None)
+    assert call(dense) == 1                                   # not a paged plan
+    assert lib.gqa_av_decode_plan(fake, fake, fake, 2, 100, 8, 2, 64, 2, ctypes.byref(pg), None) == 1
+    assert call(pg, P=32) == 1                                # page size differs from the plan's
+    assert call(pg, maxp=6) == 1                              # capacity 100 > 6 * 16
+    assert call(pg, npg=0) == 1
+    assert call(pg, bt=None) == 1 and call(pg, ln=None) == 1
+    assert "block_table" in ga.load().gqa_av_last_error().decode()
+    odd = ctypes.c_void_p((1 << 20) + 8)                      # pages not 16-byte aligned
+    assert lib.gqa_av_paged_decode_plan(fake, odd, fake, fake, fake, 2, 100, 8, 2, 64, 16, 8, 16, 2,
+                                        ctypes.byref(pg), None) == 3
+    pg0 = ga.make_plan(0, 100, 8, 2, 64, "bf16", page_size=16)
+    assert lib.gqa_av_paged_decode_plan(None, None, None, None, None, 0, 100, 8, 2, 64, 16, 8, 16, 2,
+                                        ctypes.byref(pg0), None) == 0

@@ -203,6 +203,25 @@ def _check_valu_plan(p, B, C, Hq, Hkv, D, dt):
         ce = min(C, cb + p.rows_per_split)
         nrows = ce - cb
         assert nrows > 0
+        if p.page_size:
+            # paged V: the split's page list (one entry per page its rows touch,
+            # at most 1024) and every loaded row's entry in it, for a full-length
+            # sequence and for shorter ones (rows past the length read the
+            # split's last valid row)
+            P = p.page_size
+            shift = P.bit_length() - 1
+            for ln in {C, C // 2, cb + 1, cb}:
+                nr = max(0, min(ce, ln) - cb)
+                if nr == 0:
+                    continue
+                pg0 = cb >> shift
+                npg = ((cb + nr - 1) >> shift) - pg0 + 1
+                assert npg <= 1024 and (cb + nr - 1) // P < -(-C // P)
+                for step in range(-(-nr // R)):
+                    for u in range(U):
+                        rows = np.minimum(step * R + u * rps + r, nr - 1)
+                        idx = ((cb + rows) >> shift) - pg0
+                        assert idx.min() >= 0 and idx.max() < npg
         vrec = (nrows - 1) * vrow + HT * D * es
         assert ((b * C + cb) * Hkv + kv) * D * es + vrec <= B * C * Hkv * D * es and vrec < 2 ** 31
         wrec = nrows * Hq * 4
@@ -263,11 +282,11 @@ def test_valu_engine_plan_bounds(B, C, Hq, Hkv, D, dt):
             for ht in (0, 1, 2, 4):
                 if ht > 1 and (Hkv % ht or mode == "per_head"):
                     continue
-                for align in (0, 2):
+                for align, P in ((0, 0), (2, 0), (0, 1), (0, 16), (0, 64)):
                     for sm in (False, True):
                         try:
                             p = ga.make_plan(B, C, Hq, Hkv, D, dt, mode, engine="valu", nsplit=ns, kv_tile=ht,
-                                             v_align=align, softmax=sm)
+                                             v_align=align, softmax=sm, page_size=P)
                         except ga.GqaAvError as e:
                             assert e.name == "UNSUPPORTED"
                             continue

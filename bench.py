@@ -77,6 +77,9 @@ def parse():
     p.add_argument("--combine", default="auto", choices=["auto", "kernel", "last"],
                    help="how split partials are added (plan default: auto)")
     p.add_argument("--kv-tile", type=int, default=0, help="adjacent KV heads per VALU workgroup (0 = plan)")
+    p.add_argument("--page-size", type=int, default=0,
+                   help="av / softmax over a paged V cache with this many rows per page (shuffled pages, full "
+                        "lengths); 0 = dense V")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle time budget")
     p.add_argument("--rotate-mb", type=float, default=ROTATE_BYTES / 2 ** 20)
@@ -240,6 +243,64 @@ def _timed(calls, nrot, steps, stream):
 
 
 QK_METRIC = "GQA decode QK scores: µs/call and achieved HBM GB/s (% of MI355X peak)"
+PAGED_METRIC = "GQA decode AV over a paged V cache: µs/call and achieved HBM GB/s (% of MI355X peak)"
+
+
+def bench_paged(args, w, dev, props):
+    """The AV product (or the fused softmax product) with V as a paged cache:
+    the workload's V cut into pages of --page-size rows, stored in a shuffled
+    order, every sequence at full length. Same algorithmic bytes as the dense
+    call (plus the block table and lengths, which are negligible)."""
+    import torch
+
+    import gqa_reuse_attn_amd as ga
+    from workloads import make_inputs, make_scores
+
+    softmax = args.op == "softmax"
+    P = args.page_size
+    if w.C % P:
+        raise SystemExit(f"--page-size {P} must divide C={w.C}")
+    x_h, V_h = (make_scores if softmax else make_inputs)(w, seed=0)
+    maxp = w.C // P
+    npg = w.B * maxp
+    g = torch.Generator().manual_seed(0)
+    perm = torch.randperm(npg, generator=g)
+    chunks = V_h.reshape(npg, P, w.Hkv, w.D)
+    pages_h = torch.empty_like(chunks)
+    pages_h[perm] = chunks                           # chunk i (sequence i // maxp) lives in page perm[i]
+    bt = perm.to(torch.int32).view(w.B, maxp).contiguous().to(dev)
+    lens = torch.full((w.B,), w.C, dtype=torch.int32, device=dev)
+    plan = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, args.mode, nsplit=args.nsplit,
+                        cu_count=props.multi_processor_count, softmax=softmax, page_size=P)
+    per_set = w.algorithmic_bytes()
+    nrot = max(1, math.ceil(args.rotate_mb * 2 ** 20 / per_set))
+    x0, p0 = x_h.to(dev), pages_h.to(dev)
+    calls = []
+    for i in range(nrot):
+        x, pg = (x0, p0) if i == 0 else (x0.clone(), p0.clone())
+        calls.append(ga.bind_paged(x, pg, bt, lens, plan=plan))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    _warm(args, calls, nrot)
+    ms = _timed(calls, nrot, args.steps, stream)
+    gbs = w.algorithmic_bytes() / (ms / 1e3) / 1e9
+    print(f"[bench] paged P={P} {'softmax ' if softmax else ''}{ms * 1e3:.2f} us/call, {gbs:.1f} GB/s "
+          f"({100 * gbs / HBM_PEAK_GBS:.1f}% of peak); {nrot} rotation sets, plan {plan.as_dict()}",
+          file=sys.stderr, flush=True)
+    line = {
+        "metric": PAGED_METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "us_per_call": round(ms * 1e3, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"paged{P}{'-softmax' if softmax else ''}:{w.name}", "B": w.B, "C": w.C, "Hq": w.Hq,
+                   "Hkv": w.Hkv, "G": w.G, "D": w.D, "v_dtype": w.v_dtype, "mode": args.mode, "page_size": P,
+                   "algorithmic_bytes": w.algorithmic_bytes(), "rotation_sets": nrot, "plan": plan.as_dict()},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "whole call (pass 1 + combine)",
+                     "us_per_launch": round(ms * 1e3, 3),
+                     "timing": "HIP events around K back-to-back calls on the launch stream"},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
 
 
 def bench_qk(args, w, dev, props):
@@ -331,6 +392,9 @@ def main():
           file=sys.stderr, flush=True)
     if args.op == "qk":
         bench_qk(args, w, dev, props)
+        return
+    if args.page_size > 0:
+        bench_paged(args, w, dev, props)
         return
 
     softmax = args.op == "softmax"

@@ -694,11 +694,19 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
         // past ce reads zeros and is never computed).
         Buf bA, bB;
         int st = 0;
+        // PG: keep each step's loads ahead of the other buffer's arithmetic (the
+        // page lookups through LDS otherwise let the scheduler move the
+        // arithmetic first, which then waits for every load in flight).
+        auto fence = [] {
+            if constexpr (PG) __builtin_amdgcn_sched_barrier(0);
+        };
         if (nsteps > 0) load(bA, 0);
         for (; st + 1 < nsteps; st += 2) {
             load(bB, st + 1);
+            fence();
             compute(bA, st);
             load(bA, st + 2);
+            fence();
             compute(bB, st + 1);
         }
         if (st < nsteps) compute(bA, st);

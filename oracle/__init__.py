@@ -63,6 +63,10 @@ class Oracle:
         lib.gqa_softmax_av_oracle.restype = ip
         lib.gqa_av_paged_oracle.argtypes = [vp, vp, vp, vp, ip, ip, i64, i64, i64, i64, i64, i64, i64, i64, vp, ip]
         lib.gqa_av_paged_oracle.restype = ip
+        lib.gqa_fp8_oracle_decode.argtypes = [vp, i64, vp]
+        lib.gqa_fp8_oracle_decode.restype = ip
+        lib.gqa_fp8_oracle.argtypes = [vp, vp, vp, ip, i64, i64, i64, i64, i64, vp, ip]
+        lib.gqa_fp8_oracle.restype = ip
         self.lib = lib
 
     @staticmethod
@@ -132,6 +136,29 @@ class Oracle:
             raise ValueError(f"oracle rejected the arguments (status {rc})")
         return out
 
+    def fp8(self, w, V8, v_scale=None, softmax: bool = False, nthreads: int = 0) -> np.ndarray:
+        """out[B, Hq, D] (float64) for weights (or scores) [B,C,Hq] fp32, V8 [B,C,Hkv,D]
+        OCP FP8 E4M3 bytes (uint8 or torch.float8_e4m3fn) and v_scale [Hkv] fp32 or None."""
+        a = np.ascontiguousarray(_as_numpy(w, np.float32))
+        v = np.ascontiguousarray(_fp8_bytes(V8))
+        B, C, Hq = a.shape
+        B2, C2, Hkv, D = v.shape
+        assert (B2, C2) == (B, C)
+        sc = None if v_scale is None else np.ascontiguousarray(_as_numpy(v_scale, np.float32))
+        out = np.empty((B, Hq, D), dtype=np.float64)
+        rc = self.lib.gqa_fp8_oracle(a.ctypes.data, v.ctypes.data, None if sc is None else sc.ctypes.data,
+                                     int(bool(softmax)), B, C, Hq, Hkv, D, out.ctypes.data, nthreads)
+        if rc != 0:
+            raise ValueError(f"oracle rejected the arguments (status {rc})")
+        return out
+
+    def decode_fp8(self, raw) -> np.ndarray:
+        """Widen OCP FP8 E4M3 bytes to float64."""
+        v = np.ascontiguousarray(_fp8_bytes(raw))
+        out = np.empty(v.size, dtype=np.float64)
+        self.lib.gqa_fp8_oracle_decode(v.ctypes.data, v.size, out.ctypes.data)
+        return out.reshape(v.shape)
+
     def points(self, attn, V, v_dtype: str, idx: np.ndarray, nthreads: int = 0) -> np.ndarray:
         """Selected elements out[b, q, d] for idx rows (b, q, d)."""
         a, v = self._np_inputs(attn, V, v_dtype)
@@ -174,6 +201,20 @@ def _as_numpy(x, np_dtype):
     if np_dtype == np.uint16 and x.dtype == np.float16:
         return x.view(np.uint16)
     return x
+
+
+def _fp8_bytes(x) -> np.ndarray:
+    """The raw bytes of an fp8 tensor (torch float8 or uint8) or array."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu().contiguous()
+            if x.dtype != torch.uint8:
+                x = x.view(torch.uint8)
+            return x.numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(x, dtype=np.uint8)
 
 
 _DEFAULT: Optional[Oracle] = None

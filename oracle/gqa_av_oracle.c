@@ -53,6 +53,12 @@
  * and one division at the end. C = 0 gives zeros (an empty sum, as above); a
  * row whose scores are all -inf gives NaN, as the definition does.
  *
+ * fp8 V (a compressed cache, not on the page): V holds OCP FP8 E4M3 bytes
+ * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no infinities,
+ * S.1111.111 is NaN) and each KV head has a float32 scale: the value of an
+ * element is decode(byte) * v_scale[kv_h], exact in double. The products and
+ * sums are those of the plain or fused definitions above.
+ *
  * Paged V (a decode cache layout, not on the page): sequence b has seq_lens[b]
  * context rows; row c of it lives in page block_table[b][c / page_size], at
  * row c % page_size of that page, pages being [page_size][Hkv][D] blocks of
@@ -341,6 +347,70 @@ int gqa_av_paged_oracle(const float *w, const void *pages, const int32_t *block_
     for (int64_t i = 0; i < rows; ++i)
         orc_paged_row(w, pages, block_table, dtype, softmax, C, Hq, Hkv, D, P, max_pages, seq_lens[i / Hq],
                       i / Hq, i % Hq, out + i * D);
+    (void)nthreads;
+    return ORC_OK;
+}
+
+/* OCP FP8 E4M3: written out from the bit layout. */
+static double orc_e4m3(uint8_t x)
+{
+    const int sign = x >> 7, e = (x >> 3) & 15, m = x & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) v = ldexp((double)m, -9);                  /* subnormal: m / 8 * 2^-6 */
+    else v = ldexp((double)(8 + m), e - 10);               /* (1 + m / 8) * 2^(e - 7) */
+    return sign ? -v : v;
+}
+
+/* Widen n fp8 E4M3 bytes to double (exposed so tests can pin the decoder). */
+int gqa_fp8_oracle_decode(const uint8_t *V, int64_t n, double *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3(V[i]);
+    return ORC_OK;
+}
+
+/* fp8 V with per-KV-head scales, one output row: the plain product
+ * (softmax = 0) or the fused softmax product (softmax = 1). */
+static void orc_fp8_row(const float *w, const uint8_t *V, const float *v_scale, int softmax,
+                        int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int64_t b, int64_t q, double *acc)
+{
+    const int64_t G = Hq / Hkv;
+    const int64_t kv = q / G;
+    const double sc = v_scale ? (double)v_scale[kv] : 1.0;
+    for (int64_t d = 0; d < D; ++d) acc[d] = 0.0;
+    if (C == 0) return;
+    double m = 0.0, l = 0.0;
+    if (softmax) {
+        m = -INFINITY;
+        for (int64_t c = 0; c < C; ++c) {
+            const double x = (double)w[(b * C + c) * Hq + q];
+            if (x > m) m = x;
+        }
+    }
+    for (int64_t c = 0; c < C; ++c) {
+        const double x = (double)w[(b * C + c) * Hq + q];
+        const double a = softmax ? exp(x - m) : x;
+        l += a;
+        const uint8_t *r = V + ((b * C + c) * Hkv + kv) * D;
+        for (int64_t d = 0; d < D; ++d) acc[d] += a * (orc_e4m3(r[d]) * sc);
+    }
+    if (softmax)
+        for (int64_t d = 0; d < D; ++d) acc[d] /= l;
+}
+
+/* Full fp8 output: out[B][Hq][D] in double; v_scale [Hkv] or NULL (all 1). */
+int gqa_fp8_oracle(const float *w, const uint8_t *V, const float *v_scale, int softmax,
+                   int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, double *out, int nthreads)
+{
+    int rc = orc_check(ORC_F32, B, C, Hq, Hkv, D);
+    if (rc != ORC_OK) return rc;
+    const int64_t rows = B * Hq;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int64_t i = 0; i < rows; ++i)
+        orc_fp8_row(w, V, v_scale, softmax, C, Hq, Hkv, D, i / Hq, i % Hq, out + i * D);
     (void)nthreads;
     return ORC_OK;
 }

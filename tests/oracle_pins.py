@@ -63,6 +63,16 @@ Paged V (rows of sequence b in pages block_table[b][c // P], lengths seq_lens):
                       zeros.
   * paged_rejects     block-table entries outside the cache, lengths outside
                       [0, C] and C above max_pages * P are rejected.
+
+fp8 V (OCP FP8 E4M3 bytes times a float32 scale per KV head):
+  * fp8_decode        all 256 bit patterns against torch's float8_e4m3fn, and
+                      values the OCP format fixes (448 the largest, 2^-6 the
+                      smallest normal, 2^-9 the smallest subnormal, 1.0, -0, NaN).
+  * fp8_as_bf16       every E4M3 value is a bfloat16 value: with unit scales the
+                      fp8 oracle equals the bf16 oracles on the widened V, bit
+                      for bit (plain and fused softmax).
+  * fp8_scales        a power-of-two scale per KV head scales exactly that head's
+                      group of outputs; one head's scale leaves the others alone.
 """
 from __future__ import annotations
 
@@ -575,10 +585,60 @@ def pin_paged_rejects(orc):
         raise AssertionError(f"paged oracle accepted a bad {bad}")
 
 
+def _fp8_case(B, C, Hq, Hkv, D, seed):
+    g = torch.Generator().manual_seed(seed)
+    raw = torch.randint(0, 256, (B, C, Hkv, D), generator=g, dtype=torch.uint8)
+    raw[(raw & 0x7F) == 0x7F] = 0x3C                    # no NaN payloads in V
+    s, _ = make_scores_random(B, C, Hq, Hkv, D, "f32", seed=seed)
+    return s, raw
+
+
+def pin_fp8_decode(orc):
+    bits = torch.arange(256, dtype=torch.uint8)
+    d = orc.decode_fp8(bits)
+    ref = bits.view(torch.float8_e4m3fn).double().numpy()
+    same = (d == ref) | (np.isnan(d) & np.isnan(ref))
+    assert same.all(), f"fp8 decode differs from torch at {np.nonzero(~same)[0][:8]}"
+    fixed = {0x7E: 448.0, 0x08: 2.0 ** -6, 0x01: 2.0 ** -9, 0x38: 1.0, 0x07: 7 * 2.0 ** -9, 0xC0: -2.0,
+             0x77: 240.0}
+    for k, v in fixed.items():
+        assert d[k] == v, f"fp8 0x{k:02x}: {d[k]} != {v}"
+    assert d[0x80] == 0.0 and math.copysign(1.0, d[0x80]) < 0, "fp8 0x80 is -0"
+    assert np.isnan(d[0x7F]) and np.isnan(d[0xFF]), "fp8 S.1111.111 is NaN"
+
+
+def pin_fp8_as_bf16(orc):
+    for i, (B, C, Hq, Hkv, D) in enumerate([(2, 30, 6, 2, 8), (1, 17, 4, 4, 5), (2, 9, 8, 1, 3)]):
+        s, raw = _fp8_case(B, C, Hq, Hkv, D, seed=900 + i)
+        v16 = raw.view(torch.float8_e4m3fn).to(torch.bfloat16)
+        w = torch.softmax(s.double(), dim=1).float()
+        assert np.array_equal(orc.fp8(w, raw), orc.full(w, v16, "bf16")), "fp8 plain != bf16 oracle"
+        assert np.array_equal(orc.fp8(s, raw, softmax=True), orc.softmax_av(s, v16, "bf16")), "fp8 softmax != bf16"
+
+
+def pin_fp8_scales(orc):
+    B, C, Hq, Hkv, D = 2, 21, 8, 4, 6
+    s, raw = _fp8_case(B, C, Hq, Hkv, D, seed=911)
+    G = Hq // Hkv
+    base = orc.fp8(s, raw, softmax=True)
+    sc = torch.tensor([0.25, 1.0, 8.0, 2.0 ** -10])
+    o = orc.fp8(s, raw, sc, softmax=True)
+    for q in range(Hq):
+        assert np.array_equal(o[:, q], base[:, q] * float(sc[q // G])), f"fp8 scale of head {q}"
+    sc2 = torch.ones(Hkv)
+    sc2[2] = 3.0
+    o2 = orc.fp8(s, raw, sc2)
+    b2 = orc.fp8(s, raw)
+    for q in range(Hq):
+        if q // G != 2:
+            assert np.array_equal(o2[:, q], b2[:, q]), "fp8: one head's scale leaked into another head"
+    assert not np.array_equal(o2, b2)
+
+
 ALL_PINS = [pin_decode_table, pin_brute_force, pin_mha_einsum, pin_repeat_mha, pin_constant_v,
             pin_one_hot, pin_linearity, pin_permutation, pin_batch_independence, pin_points,
             pin_edges, pin_qk_brute_force, pin_qk_mha_einsum, pin_qk_repeat_mha, pin_qk_one_hot,
             pin_qk_scale_linear, pin_qk_composition, pin_qk_edges, pin_sav_library, pin_sav_shift,
             pin_sav_large, pin_sav_one_hot, pin_sav_uniform, pin_sav_two_rows, pin_sav_mask,
             pin_sav_repeat_mha, pin_sav_edges, pin_paged_gather, pin_paged_identity, pin_paged_ignores_tail,
-            pin_paged_rejects]
+            pin_paged_rejects, pin_fp8_decode, pin_fp8_as_bf16, pin_fp8_scales]

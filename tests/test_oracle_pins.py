@@ -68,6 +68,12 @@ PLANTS = [
      "const int64_t row = ((page * P + (P - 1 - c % P)) * Hkv + kv) * D;"),
     ("paged_ignores_len", "for (int64_t c = 0; c < len; ++c) {\n        const double x",
      "for (int64_t c = 0; c < C; ++c) {\n        const double x"),
+    ("fp8_bias_8", "else v = ldexp((double)(8 + m), e - 10);", "else v = ldexp((double)(8 + m), e - 11);"),
+    ("fp8_subnormal_scale", "if (e == 0) v = ldexp((double)m, -9);", "if (e == 0) v = ldexp((double)m, -10);"),
+    ("fp8_no_sign", "    return sign ? -v : v;\n}\n\n/* Widen n fp8", "    return v;\n}\n\n/* Widen n fp8"),
+    ("fp8_scale_of_query_head", "const double sc = v_scale ? (double)v_scale[kv] : 1.0;",
+     "const double sc = v_scale ? (double)v_scale[q % Hkv] : 1.0;"),
+    ("fp8_scale_ignored", "acc[d] += a * (orc_e4m3(r[d]) * sc);", "acc[d] += a * orc_e4m3(r[d]);"),
     ("paged_bt_ignores_batch", "const int64_t page = bt[b * max_pages + c / P];",
      "const int64_t page = bt[0 * max_pages + c / P];"),
 ]

@@ -77,6 +77,8 @@ def parse():
     p.add_argument("--combine", default="auto", choices=["auto", "kernel", "last"],
                    help="how split partials are added (plan default: auto)")
     p.add_argument("--kv-tile", type=int, default=0, help="adjacent KV heads per VALU workgroup (0 = plan)")
+    p.add_argument("--v-fp8", action="store_true",
+                   help="av / softmax with V quantized to OCP FP8 E4M3 with a scale per KV head (half the V bytes)")
     p.add_argument("--page-size", type=int, default=0,
                    help="av / softmax over a paged V cache with this many rows per page (shuffled pages, full "
                         "lengths); 0 = dense V")
@@ -243,6 +245,57 @@ def _timed(calls, nrot, steps, stream):
 
 
 QK_METRIC = "GQA decode QK scores: µs/call and achieved HBM GB/s (% of MI355X peak)"
+FP8_METRIC = "GQA decode AV with fp8 V: µs/call and achieved HBM GB/s (% of MI355X peak)"
+
+
+def bench_fp8(args, w, dev, props):
+    """The AV product (or the fused softmax product) with the workload's V
+    quantized to OCP FP8 E4M3 with a float32 scale per KV head (max |V| / 448).
+    Algorithmic bytes: V at one byte per value, the weights, the output."""
+    import torch
+
+    import gqa_reuse_attn_amd as ga
+    from workloads import make_inputs, make_scores
+
+    softmax = args.op == "softmax"
+    x_h, V_h = (make_scores if softmax else make_inputs)(w, seed=0)
+    Vf = V_h.float()
+    scale_h = (Vf.abs().amax(dim=(0, 1, 3)).clamp_min(1e-30) / 448.0).contiguous()
+    q_h = (Vf / scale_h.view(1, 1, -1, 1)).to(torch.float8_e4m3fn).contiguous()
+    del Vf
+    alg = w.B * w.C * w.Hkv * w.D + w.attn_bytes() + w.out_bytes()
+    plan = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, "fp8", args.mode, nsplit=args.nsplit,
+                        cu_count=props.multi_processor_count, softmax=softmax)
+    nrot = max(1, math.ceil(args.rotate_mb * 2 ** 20 / alg))
+    x0, q0, sc = x_h.to(dev), q_h.to(dev), scale_h.to(dev)
+    calls = []
+    for i in range(nrot):
+        x, q = (x0, q0) if i == 0 else (x0.clone(), q0.clone())
+        calls.append(ga.bind_fp8(x, q, sc, plan=plan))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    _warm(args, calls, nrot)
+    ms = _timed(calls, nrot, args.steps, stream)
+    gbs = alg / (ms / 1e3) / 1e9
+    print(f"[bench] fp8 {'softmax ' if softmax else ''}{ms * 1e3:.2f} us/call, {gbs:.1f} GB/s "
+          f"({100 * gbs / HBM_PEAK_GBS:.1f}% of peak); {nrot} rotation sets, plan {plan.as_dict()}",
+          file=sys.stderr, flush=True)
+    line = {
+        "metric": FP8_METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "us_per_call": round(ms * 1e3, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"fp8{'-softmax' if softmax else ''}:{w.name}", "B": w.B, "C": w.C, "Hq": w.Hq,
+                   "Hkv": w.Hkv, "G": w.G, "D": w.D, "v_dtype": "fp8_e4m3", "mode": args.mode,
+                   "algorithmic_bytes": alg, "rotation_sets": nrot, "plan": plan.as_dict()},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "whole call (pass 1 + combine)",
+                     "us_per_launch": round(ms * 1e3, 3),
+                     "timing": "HIP events around K back-to-back calls on the launch stream"},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 PAGED_METRIC = "GQA decode AV over a paged V cache: µs/call and achieved HBM GB/s (% of MI355X peak)"
 
 
@@ -395,6 +448,9 @@ def main():
         return
     if args.page_size > 0:
         bench_paged(args, w, dev, props)
+        return
+    if args.v_fp8:
+        bench_fp8(args, w, dev, props)
         return
 
     softmax = args.op == "softmax"

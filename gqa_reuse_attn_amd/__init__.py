@@ -27,7 +27,7 @@ __all__ = [
     "LIB_PATH", "GqaAvError", "Hint", "Plan", "load", "resolve_mode", "make_plan",
     "gqa_av_decode", "gqa_av_decode_plan", "bind", "BoundCall", "release", "status_string", "MODES", "DTYPES",
     "QkHint", "QkPlan", "qk_make_plan", "gqa_qk_decode", "bind_qk", "gqa_softmax_av_decode", "bind_softmax",
-    "gqa_av_paged_decode", "bind_paged",
+    "gqa_av_paged_decode", "bind_paged", "gqa_av_fp8_decode", "bind_fp8",
 ]
 
 # GQA_AV_LIBRARY may name another build of the same library (tuning variants).
@@ -36,7 +36,7 @@ LIB_PATH = os.environ.get("GQA_AV_LIBRARY") or os.path.join(os.path.dirname(os.p
 MODES = {"auto": -1, "per_head": 0, "reuse": 1}
 ENGINES = {"auto": 0, "valu": 1, "mfma": 2, "mfma_bf16": 3}
 COMBINES = {"auto": 0, "kernel": 1, "last": 2}
-DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3}   # fp8: OCP FP8 E4M3 (V only)
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "INELIGIBLE", 3: "UNSUPPORTED", 4: "HIP"}
 
 
@@ -119,6 +119,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gqa_av_paged_decode_plan.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, ip,
                                              ctypes.POINTER(Plan), vp]
     lib.gqa_av_paged_decode_plan.restype = ip
+    lib.gqa_av_fp8_decode.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ip, ip, vp]
+    lib.gqa_av_fp8_decode.restype = ip
+    lib.gqa_av_fp8_decode_plan.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.POINTER(Plan), vp]
+    lib.gqa_av_fp8_decode_plan.restype = ip
     lib.gqa_av_status_string.argtypes = [ip]
     lib.gqa_av_status_string.restype = ctypes.c_char_p
     lib.gqa_av_last_error.argtypes = []
@@ -192,7 +196,7 @@ def _torch():
 
 def _check(attn, V, out):
     torch = _torch()
-    vmap = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
+    vmap = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16", torch.float8_e4m3fn: "fp8"}
     if attn.dim() != 3 or V.dim() != 4:
         raise ValueError(f"attn must be [B,C,Hq] and V [B,C,Hkv,D]; got {tuple(attn.shape)} and {tuple(V.shape)}")
     B, C, Hq = attn.shape
@@ -202,7 +206,7 @@ def _check(attn, V, out):
     if attn.dtype != torch.float32:
         raise TypeError(f"attn must be float32, got {attn.dtype}")
     if V.dtype not in vmap:
-        raise TypeError(f"V must be float32, float16 or bfloat16, got {V.dtype}")
+        raise TypeError(f"V must be float32, float16, bfloat16 or float8_e4m3fn, got {V.dtype}")
     if not (attn.is_cuda and V.is_cuda):
         raise ValueError("attn and V must be GPU tensors")
     if attn.device != V.device:
@@ -334,6 +338,80 @@ def bind_softmax(scores, V, out=None, plan: Optional[Plan] = None, mode: Union[s
                  stream=None) -> BoundCall:
     """A BoundCall of the fused softmax product for (scores, V, out)."""
     return BoundCall(scores, V, out=out, plan=plan, mode=mode, stream=stream, softmax=True)
+
+
+def _check_scale(v_scale, Hkv, device):
+    if v_scale is None:
+        return None
+    torch = _torch()
+    if v_scale.dtype != torch.float32 or tuple(v_scale.shape) != (Hkv,) or not v_scale.is_contiguous() \
+            or v_scale.device != device:
+        raise ValueError(f"v_scale must be a contiguous float32 [{Hkv}] tensor on {device}")
+    return v_scale
+
+
+def gqa_av_fp8_decode(w, V, v_scale=None, out=None, softmax: bool = False, mode: Union[str, int] = "auto",
+                      stream=None, plan: Optional[Plan] = None):
+    """The AV product (or, softmax=True, the fused softmax product on scores w)
+    with V in OCP FP8 E4M3 (torch.float8_e4m3fn [B,C,Hkv,D]) and a float32 scale
+    per KV head (v_scale [Hkv], None = 1)."""
+    torch = _torch()
+    B, C, Hq, Hkv, D, vdt = _check(w, V, out)
+    if vdt != "fp8":
+        raise TypeError("V must be torch.float8_e4m3fn")
+    sc = _check_scale(v_scale, Hkv, w.device)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=w.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(w.device)
+    lib = load()
+    sp = sc.data_ptr() if sc is not None else None
+    with torch.cuda.device(w.device):
+        if plan is None:
+            rc = lib.gqa_av_fp8_decode(w.data_ptr(), V.data_ptr(), sp, out.data_ptr(), B, C, Hq, Hkv, D,
+                                       1 if softmax else 0, _mode(mode), stream.cuda_stream)
+        else:
+            rc = lib.gqa_av_fp8_decode_plan(w.data_ptr(), V.data_ptr(), sp, out.data_ptr(), B, C, Hq, Hkv, D,
+                                            ctypes.byref(plan), stream.cuda_stream)
+    if rc != 0:
+        _raise(rc)
+    return out
+
+
+class BoundFp8:
+    """An fp8 call with checked, bound arguments for loops (see BoundCall)."""
+
+    def __init__(self, w, V, v_scale=None, out=None, plan: Optional[Plan] = None, softmax: bool = False,
+                 mode: Union[str, int] = "auto", stream=None):
+        torch = _torch()
+        B, C, Hq, Hkv, D, vdt = _check(w, V, out)
+        if vdt != "fp8":
+            raise TypeError("V must be torch.float8_e4m3fn")
+        sc = _check_scale(v_scale, Hkv, w.device)
+        if out is None:
+            out = torch.empty((B, Hq, D), dtype=torch.float32, device=w.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(w.device)
+        if plan is None:
+            cu = torch.cuda.get_device_properties(w.device).multi_processor_count
+            addr = V.data_ptr()
+            plan = make_plan(B, C, Hq, Hkv, D, "fp8", mode, cu_count=cu, softmax=softmax,
+                             v_align=16 if addr % 16 == 0 else (addr & -addr))
+        self.tensors, self.out, self.plan = (w, V, sc), out, plan
+        self._fn = load().gqa_av_fp8_decode_plan
+        self._args = (w.data_ptr(), V.data_ptr(), sc.data_ptr() if sc is not None else None, out.data_ptr(),
+                      B, C, Hq, Hkv, D, ctypes.byref(plan), stream.cuda_stream)
+
+    def __call__(self):
+        rc = self._fn(*self._args)
+        if rc != 0:
+            _raise(rc)
+        return self.out
+
+
+def bind_fp8(w, V, v_scale=None, out=None, plan: Optional[Plan] = None, softmax: bool = False,
+             mode: Union[str, int] = "auto", stream=None) -> BoundFp8:
+    return BoundFp8(w, V, v_scale=v_scale, out=out, plan=plan, softmax=softmax, mode=mode, stream=stream)
 
 
 def _check_paged(w, pages, block_table, seq_lens, out):

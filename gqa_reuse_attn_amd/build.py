@@ -17,7 +17,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "gqa_av.hip")
 HEADERS = [os.path.join(PKG, "csrc", f) for f in ("av_kernels.hpp", "qk_kernels.hpp", "qk_host.hpp")] + \
-    [os.path.join(ROOT, "include", f) for f in ("gqa_av.h", "gqa_qk.h", "gqa_softmax_av.h", "gqa_paged_av.h")]
+    [os.path.join(ROOT, "include", f) for f in ("gqa_av.h", "gqa_qk.h", "gqa_softmax_av.h", "gqa_paged_av.h", "gqa_fp8_av.h")]
 LIB = os.path.join(PKG, "libgqa_av.so")
 ARCH = "gfx950"
 

@@ -75,7 +75,7 @@ constexpr int valu_unroll(int GT) {
 }
 constexpr int mfma_unroll(int NB) { return NB > 16 ? (GQA_AV_MFMA_UNROLL + 1) / 2 : GQA_AV_MFMA_UNROLL; }
 
-enum : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+enum : int { kF32 = 0, kF16 = 1, kBF16 = 2, kFP8 = 3 };   // kFP8: OCP FP8 E4M3 (V only)
 
 // Fused softmax: a weight is exp2((s - r) * log2(e)) for a running maximum r of
 // the scores. The difference is taken first (exact when s and r are within a
@@ -86,7 +86,7 @@ enum : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int DT>
-constexpr int esize() { return DT == kF32 ? 4 : 2; }
+constexpr int esize() { return DT == kF32 ? 4 : (DT == kFP8 ? 1 : 2); }
 
 // Workgroups are handed to the XCDs round-robin (block i -> XCD i % 8). Remap
 // so that each XCD walks a contiguous range of logical tiles: the KV heads of
@@ -110,6 +110,7 @@ struct Pass1Args {
     int64_t num_pages;           // paged V: pages in the cache (block-table entries are clamped into range)
     int32_t page_shift;          // paged V: log2 of the rows per page
     int32_t max_pages;           // paged V: length of a block-table row
+    const float* v_scale;        // fp8 V: [Hkv] scale of each KV head's values (NULL: 1)
     uint32_t* counters;     // combine in kernel: [tiles], zero between calls
     int32_t combine;        // 1: last workgroup of a tile adds the splits; 0: second kernel
     int64_t C;
@@ -249,7 +250,27 @@ __device__ inline float f16_bits_to_f32(uint32_t h) {
 // Widen the NB / esize elements of one lane-load to fp32 (exact for all three types).
 template <int DT, int NB>
 __device__ inline void widen(const Raw<NB>& r, float* f) {
-    if constexpr (DT == kF32) {
+    if constexpr (DT == kFP8) {
+        // v_cvt_pk_f32_fp8 decodes two OCP E4M3 bytes exactly on gfx950 (all 256
+        // patterns checked on MI355X against the format's definition).
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        static_assert(NB == 2 || NB % 4 == 0, "fp8 lane loads are 2, 4 or 8 bytes");
+        if constexpr (NB == 2) {
+            const f32x2 p = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(r.w[0]), false);
+            f[0] = p.x;
+            f[1] = p.y;
+        } else {
+#pragma unroll
+            for (int i = 0; i < NB / 4; ++i) {
+                const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(r.w[i]), false);
+                const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(r.w[i]), true);
+                f[4 * i] = lo.x;
+                f[4 * i + 1] = lo.y;
+                f[4 * i + 2] = hi.x;
+                f[4 * i + 3] = hi.y;
+            }
+        }
+    } else if constexpr (DT == kF32) {
 #pragma unroll
         for (int i = 0; i < NB / 4; ++i) f[i] = __uint_as_float(r.w[i]);
     } else if constexpr (NB == 2) {
@@ -788,6 +809,10 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
                 // combine does, from the statistics written below.
                 if (a.nsplit == 1)
                     sum = nrows_split > 0 ? sum / s_stat[1][(jj / a.L) * GT + k / E] : 0.0f;
+            }
+            if constexpr (DT == kFP8) {
+                // The KV head's scale, once per output (the sums are linear in V).
+                if (a.v_scale) sum *= a.v_scale[(lane_q_lo(jj / a.L) + k / E) / a.G];
             }
             if (in_kernel) {
                 store_coherent(blk + static_cast<size_t>(T.s) * TOP + k * Lc + jj, sum);

@@ -8,6 +8,7 @@
 // also caps G at 8 and sends larger groups to the per-head kernel; that cap
 // is not kept: any G takes the reuse path (G > 16 in sub-groups of 16 heads).
 #include "gqa_av.h"
+#include "gqa_fp8_av.h"
 #include "gqa_paged_av.h"
 #include "gqa_softmax_av.h"
 
@@ -40,7 +41,7 @@ int fail(int status, const char* fmt, ...) {
     return status;
 }
 
-int elem_bytes(int dt) { return dt == GQA_AV_F32 ? 4 : 2; }
+int elem_bytes(int dt) { return dt == GQA_AV_F32 ? 4 : (dt == GQA_AV_FP8_E4M3 ? 1 : 2); }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -145,7 +146,7 @@ int check_sizes(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_
         return fail(GQA_AV_ERR_INVALID_ARG, "Hq=%lld, Hkv=%lld and D=%lld must be >= 1", (long long)Hq, (long long)Hkv, (long long)D);
     if (Hq % Hkv != 0)
         return fail(GQA_AV_ERR_INVALID_ARG, "Hq=%lld is not a multiple of Hkv=%lld", (long long)Hq, (long long)Hkv);
-    if (v_dtype != GQA_AV_F32 && v_dtype != GQA_AV_F16 && v_dtype != GQA_AV_BF16)
+    if (v_dtype != GQA_AV_F32 && v_dtype != GQA_AV_F16 && v_dtype != GQA_AV_BF16 && v_dtype != GQA_AV_FP8_E4M3)
         return fail(GQA_AV_ERR_INVALID_ARG, "unknown v_dtype %d", v_dtype);
     // Index arithmetic inside the kernels keeps these in 32 bits.
     if (B > INT32_MAX || Hq > INT32_MAX || D > INT32_MAX)
@@ -174,19 +175,31 @@ hipError_t launch_valu_gt(int GT, const Pass1Args& a, hipStream_t s) {
     case 2: return launch_valu<DT, VB, 2, SM, PG>(a, s);
     case 3: return launch_valu<DT, VB, 3, SM, PG>(a, s);
     case 4: return launch_valu<DT, VB, 4, SM, PG>(a, s);
-    case 5: return launch_valu<DT, VB, 5, SM, PG>(a, s);
-    case 6: return launch_valu<DT, VB, 6, SM, PG>(a, s);
-    case 7: return launch_valu<DT, VB, 7, SM, PG>(a, s);
-    case 8: return launch_valu<DT, VB, 8, SM, PG>(a, s);
-    case 16: return launch_valu<DT, VB, 16, SM, PG>(a, s);
-    default: return hipErrorInvalidValue;
+    default: break;
+    }
+    // fp8 with 16-byte lane loads (16 values) only for tiles of up to 4 heads.
+    if constexpr (DT == gqa_av::kFP8 && VB == 16) {
+        return hipErrorInvalidValue;
+    } else {
+        switch (GT) {
+        case 5: return launch_valu<DT, VB, 5, SM, PG>(a, s);
+        case 6: return launch_valu<DT, VB, 6, SM, PG>(a, s);
+        case 7: return launch_valu<DT, VB, 7, SM, PG>(a, s);
+        case 8: return launch_valu<DT, VB, 8, SM, PG>(a, s);
+        case 16: return launch_valu<DT, VB, 16, SM, PG>(a, s);
+        default: return hipErrorInvalidValue;
+        }
     }
 }
 
 // Paged V: 16-byte lane loads only.
 template <int DT>
 hipError_t launch_valu_paged(bool sm, int GT, const Pass1Args& a, hipStream_t s) {
-    return sm ? launch_valu_gt<DT, 16, true, true>(GT, a, s) : launch_valu_gt<DT, 16, false, true>(GT, a, s);
+    if constexpr (DT == gqa_av::kFP8) {
+        return hipErrorInvalidValue;                 // the plan refuses paged fp8 V
+    } else {
+        return sm ? launch_valu_gt<DT, 16, true, true>(GT, a, s) : launch_valu_gt<DT, 16, false, true>(GT, a, s);
+    }
 }
 
 template <int DT, bool SM>
@@ -282,6 +295,7 @@ hipError_t launch_pass1(int v_dtype, const gqa_av_plan& p, int64_t D, const Pass
         case GQA_AV_F32: return launch_valu_vb<gqa_av::kF32, true>(p.vec_bytes, p.heads_per_tile, a, s);
         case GQA_AV_F16: return launch_valu_vb<gqa_av::kF16, true>(p.vec_bytes, p.heads_per_tile, a, s);
         case GQA_AV_BF16: return launch_valu_vb<gqa_av::kBF16, true>(p.vec_bytes, p.heads_per_tile, a, s);
+        case GQA_AV_FP8_E4M3: return launch_valu_vb<gqa_av::kFP8, true>(p.vec_bytes, p.heads_per_tile, a, s);
         default: return hipErrorInvalidValue;
         }
     }
@@ -298,6 +312,7 @@ hipError_t launch_pass1(int v_dtype, const gqa_av_plan& p, int64_t D, const Pass
     case GQA_AV_F32: return launch_valu_vb<gqa_av::kF32, false>(p.vec_bytes, p.heads_per_tile, a, s);
     case GQA_AV_F16: return launch_valu_vb<gqa_av::kF16, false>(p.vec_bytes, p.heads_per_tile, a, s);
     case GQA_AV_BF16: return launch_valu_vb<gqa_av::kBF16, false>(p.vec_bytes, p.heads_per_tile, a, s);
+    case GQA_AV_FP8_E4M3: return launch_valu_vb<gqa_av::kFP8, false>(p.vec_bytes, p.heads_per_tile, a, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -396,7 +411,7 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
     const int nset16 = (G > 16 && mfma_bf16_fits(v_dtype, Hq, Hkv, D, v_align, 2)) ? 2 : 1;
     const bool mfma16_ok = resolved == GQA_AV_REUSE && mfma_bf16_fits(v_dtype, Hq, Hkv, D, v_align, nset16);
     int engine = h.engine;
-    if (engine == GQA_AV_ENGINE_AUTO && paged) engine = GQA_AV_ENGINE_VALU;
+    if (engine == GQA_AV_ENGINE_AUTO && (paged || v_dtype == GQA_AV_FP8_E4M3)) engine = GQA_AV_ENGINE_VALU;
     if (engine == GQA_AV_ENGINE_AUTO) {
         engine = GQA_AV_ENGINE_VALU;
         if (G >= kMfmaMinGroup && mfma16_ok) engine = GQA_AV_ENGINE_MFMA_BF16;
@@ -404,6 +419,8 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
     }
     if (sm && engine == GQA_AV_ENGINE_MFMA)
         return fail(GQA_AV_ERR_UNSUPPORTED, "the fused softmax runs on the VALU or bf16 matrix engine");
+    if (v_dtype == GQA_AV_FP8_E4M3 && engine != GQA_AV_ENGINE_VALU)
+        return fail(GQA_AV_ERR_UNSUPPORTED, "fp8 V runs on the VALU engine");
     if (sm && engine == GQA_AV_ENGINE_VALU && GQA_AV_VALU_STAGE_WEIGHTS)
         return fail(GQA_AV_ERR_UNSUPPORTED, "the fused softmax needs the per-lane weight VALU build");
     if (engine == GQA_AV_ENGINE_MFMA && !mfma_ok)
@@ -477,9 +494,13 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
         rows_per_step = 4 * gqa_av::kWaves * gqa_av::mfma_unroll(VB);
         tile_outputs = static_cast<int64_t>(GT) * D;
     } else {
-        // Widest lane load that divides a D-row and respects V's alignment.
+        // Widest lane load that divides a D-row and respects V's alignment
+        // (fp8: 16 values per lane only for tiles of up to 4 heads, else 8, so
+        // a lane holds at most 64 or GT x 8 accumulators).
+        const int gt_planned = resolved == GQA_AV_REUSE ? head_capacity(G) : 1;
         VB = 0;
-        for (int cand = 16; cand >= es; cand /= 2) {
+        for (int cand = (v_dtype == GQA_AV_FP8_E4M3 && gt_planned > 4) ? 8 : 16; cand >= std::max(es, 2);
+             cand /= 2) {
             if ((D * es) % cand == 0 && v_align % cand == 0) { VB = cand; break; }
         }
         if (VB == 0)
@@ -657,7 +678,7 @@ struct PagedArgs {
 // pg: the paged cache (V then points at its pages), or NULL for dense V.
 int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
              int64_t D, int v_dtype, const gqa_av_plan* plan, void* stream, int which, int softmax,
-             const PagedArgs* pg = nullptr) {
+             const PagedArgs* pg = nullptr, const float* v_scale = nullptr) {
     if (!plan) return fail(GQA_AV_ERR_INVALID_ARG, "plan is NULL");
     int rc = check_sizes(B, C, Hq, Hkv, D, v_dtype);
     if (rc != GQA_AV_OK) return rc;
@@ -755,6 +776,7 @@ int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C,
     a.part = part;
     a.stats = (softmax && plan->nsplit > 1) ? part + stats_offset(plan->nsplit, B, Hq, D) : nullptr;
     a.counters = counters;
+    a.v_scale = v_scale;
     a.block_table = pg ? pg->block_table : nullptr;
     a.seq_lens = pg ? pg->seq_lens : nullptr;
     a.num_pages = pg ? pg->num_pages : 0;
@@ -885,6 +907,24 @@ int gqa_softmax_av_decode(const float* scores, const void* V, float* out, int64_
 int gqa_softmax_av_decode_plan(const float* scores, const void* V, float* out, int64_t B, int64_t C, int64_t Hq,
                                int64_t Hkv, int64_t D, int v_dtype, const gqa_av_plan* plan, void* stream) {
     return run_plan(scores, V, out, B, C, Hq, Hkv, D, v_dtype, plan, stream, kRunPass1 | kRunCombine, 1);
+}
+
+int gqa_av_fp8_decode(const float* w, const void* V, const float* v_scale, float* out, int64_t B, int64_t C,
+                      int64_t Hq, int64_t Hkv, int64_t D, int softmax, int mode, void* stream) {
+    if (softmax != 0 && softmax != 1) return fail(GQA_AV_ERR_INVALID_ARG, "softmax must be 0 or 1");
+    gqa_av_plan plan;
+    int rc = auto_plan(V, B, C, Hq, Hkv, D, GQA_AV_FP8_E4M3, mode, softmax, &plan);
+    if (rc != GQA_AV_OK) return rc;
+    return gqa_av_fp8_decode_plan(w, V, v_scale, out, B, C, Hq, Hkv, D, &plan, stream);
+}
+
+int gqa_av_fp8_decode_plan(const float* w, const void* V, const float* v_scale, float* out, int64_t B, int64_t C,
+                           int64_t Hq, int64_t Hkv, int64_t D, const gqa_av_plan* plan, void* stream) {
+    if (!plan) return fail(GQA_AV_ERR_INVALID_ARG, "plan is NULL");
+    if (v_scale && (reinterpret_cast<uintptr_t>(v_scale) & 3u))
+        return fail(GQA_AV_ERR_INVALID_ARG, "v_scale must be 4-byte aligned");
+    return run_plan(w, V, out, B, C, Hq, Hkv, D, GQA_AV_FP8_E4M3, plan, stream, kRunPass1 | kRunCombine,
+                    plan->softmax, nullptr, v_scale);
 }
 
 int gqa_av_paged_decode(const float* w, const void* pages, const int32_t* block_table, const int32_t* seq_lens,

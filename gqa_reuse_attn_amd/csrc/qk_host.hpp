@@ -21,6 +21,7 @@ int qk_plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int k
     const int resolved = gqa_av_resolve_mode(Hq, Hkv, mode);
     if (resolved < 0) return -resolved;
     if (!plan) return fail(GQA_AV_ERR_INVALID_ARG, "plan is NULL");
+    if (k_dtype == GQA_AV_FP8_E4M3) return fail(GQA_AV_ERR_UNSUPPORTED, "score step: K is fp32, fp16 or bf16");
     if (D % 32 != 0 || D > 256)
         return fail(GQA_AV_ERR_UNSUPPORTED, "score step: D=%lld must be a multiple of 32 and at most 256", (long long)D);
     const int es = elem_bytes(k_dtype);

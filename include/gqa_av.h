@@ -65,11 +65,14 @@
 extern "C" {
 #endif
 
-/* Element type of V. attn and out are always float32. */
+/* Element type of V (and of K in gqa_qk.h, which takes the first three). attn
+ * and out are always float32. */
 typedef enum gqa_av_dtype {
     GQA_AV_F32 = 0,
     GQA_AV_F16 = 1,   /* IEEE binary16 */
-    GQA_AV_BF16 = 2   /* bfloat16: the upper 16 bits of a binary32 */
+    GQA_AV_BF16 = 2,  /* bfloat16: the upper 16 bits of a binary32 */
+    GQA_AV_FP8_E4M3 = 3  /* OCP FP8 E4M3 (bias 7, no infinities, S.1111.111 = NaN): V only, on the
+                            VALU engine; here with unit scale, per-KV-head scales in gqa_fp8_av.h */
 } gqa_av_dtype;
 
 /* How V is shared across the query heads of a group (see above). */

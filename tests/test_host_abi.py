@@ -34,6 +34,7 @@ def test_library_exports_every_declared_function():
     assert {"gqa_qk_decode", "gqa_qk_decode_plan", "gqa_qk_make_plan"} <= set(names)
     assert {"gqa_softmax_av_decode", "gqa_softmax_av_decode_plan"} <= set(names)
     assert {"gqa_av_paged_decode", "gqa_av_paged_decode_plan"} <= set(names)
+    assert {"gqa_av_fp8_decode", "gqa_av_fp8_decode_plan"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/ but not exported"
 
@@ -497,3 +498,38 @@ def test_paged_calls_reject_before_launch():
     pg0 = ga.make_plan(0, 100, 8, 2, 64, "bf16", page_size=16)
     assert lib.gqa_av_paged_decode_plan(None, None, None, None, None, 0, 100, 8, 2, 64, 16, 8, 16, 2,
                                         ctypes.byref(pg0), None) == 0
+
+
+def test_fp8_plans():
+    """fp8 V: the VALU engine with lane loads of at most 8 bytes (8 values) for
+    tiles of more than 4 heads, 16 for smaller ones; V counted at one byte per value."""
+    for wname, w in WORKLOADS.items():
+        for sm in (False, True):
+            p = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, "fp8", softmax=sm)
+            assert p.engine == 1 and p.softmax == int(sm), wname
+            assert p.vec_bytes <= (16 if p.heads_per_tile <= 4 else 8), wname
+            G = w.Hq // w.Hkv
+            assert p.v_bytes_read == w.B * w.C * w.Hkv * w.D * (1 if G >= 2 else 1) * p.subgroups
+    assert ga.make_plan(1, 100, 8, 2, 6, "fp8").vec_bytes == 2
+    assert ga.make_plan(1, 100, 8, 2, 6, "fp8", v_align=2).vec_bytes == 2
+    for kw in (dict(engine="mfma"), dict(engine="mfma_bf16"), dict(page_size=16)):
+        with pytest.raises(ga.GqaAvError) as e:
+            ga.make_plan(2, 1000, 16, 2, 128, "fp8", "reuse", **kw)
+        assert e.value.name == "UNSUPPORTED", kw
+    with pytest.raises(ga.GqaAvError) as e:
+        ga.make_plan(2, 1000, 16, 2, 127, "fp8")            # odd D: no 2-byte lane load fits
+    assert e.value.name == "UNSUPPORTED"
+    with pytest.raises(ga.GqaAvError) as e:
+        ga.qk_make_plan(2, 1000, 16, 2, 128, "fp8")
+    assert e.value.name == "UNSUPPORTED"
+
+
+def test_fp8_calls_reject_before_launch():
+    lib = ga.load()
+    fake = ctypes.c_void_p(1 << 20)
+    p = ga.make_plan(2, 100, 8, 2, 64, "fp8")
+    bad_scale = ctypes.c_void_p((1 << 20) + 2)
+    assert lib.gqa_av_fp8_decode_plan(fake, fake, bad_scale, fake, 2, 100, 8, 2, 64, ctypes.byref(p), None) == 1
+    assert lib.gqa_av_fp8_decode_plan(fake, fake, None, fake, 2, 5000, 8, 2, 64, ctypes.byref(p), None) == 1
+    pb = ga.make_plan(2, 100, 8, 2, 64, "bf16")             # a bf16 plan for an fp8 call
+    assert lib.gqa_av_fp8_decode_plan(fake, fake, None, fake, 2, 100, 8, 2, 64, ctypes.byref(pb), None) == 1

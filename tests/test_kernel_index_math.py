@@ -162,7 +162,7 @@ ENGINE_VALU = 1
 
 
 def _esize(dt):
-    return 4 if dt == "f32" else 2
+    return {"f32": 4, "fp8": 1}.get(dt, 2)
 
 
 def _check_valu_plan(p, B, C, Hq, Hkv, D, dt):
@@ -274,7 +274,8 @@ def _check_valu_plan(p, B, C, Hq, Hkv, D, dt):
 @pytest.mark.parametrize("B,C,Hq,Hkv,D,dt", [
     (2, 1000, 8, 4, 128, "bf16"), (1, 300, 4, 2, 127, "bf16"), (2, 129, 6, 3, 1, "f16"), (1, 200, 1, 1, 64, "f32"),
     (2, 150, 64, 1, 64, "bf16"), (1, 90, 4, 2, 2048, "f32"), (3, 257, 10, 5, 80, "f16"), (2, 333, 24, 8, 96, "f16"),
-    (1, 64, 32, 8, 128, "bf16"), (2, 500, 14, 2, 256, "bf16"), (1, 777, 12, 3, 128, "f32")])
+    (1, 64, 32, 8, 128, "bf16"), (2, 500, 14, 2, 256, "bf16"), (1, 777, 12, 3, 128, "f32"),
+    (2, 300, 16, 8, 128, "fp8"), (1, 129, 6, 3, 96, "fp8"), (2, 65, 64, 1, 2, "fp8"), (1, 200, 8, 2, 46, "fp8")])
 def test_valu_engine_plan_bounds(B, C, Hq, Hkv, D, dt):
     modes = ("reuse", "per_head") if Hq // Hkv >= 2 else ("per_head",)
     for mode in modes:

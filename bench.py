@@ -40,10 +40,16 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 ROTATE_BYTES = 512 * 2 ** 20   # 2 x the 256 MB Infinity Cache
 DEFAULT_WORKLOAD = "g2-b4-c32768-hq16-hkv8-d128-bf16"
 PROFILES = os.path.join(ROOT, "profiles")
+_CSRC = os.path.join(ROOT, "gqa_reuse_attn_amd", "csrc")
+# The sources each operation's kernels are built from (a profile records their hash).
 KERNEL_SOURCES = {
-    "av": [os.path.join(ROOT, "gqa_reuse_attn_amd", "csrc", f) for f in ("av_kernels.hpp", "gqa_av.hip")],
-    "qk": [os.path.join(ROOT, "gqa_reuse_attn_amd", "csrc", f) for f in ("av_kernels.hpp", "qk_kernels.hpp",
-                                                                       "qk_host.hpp")],
+    "av": [os.path.join(_CSRC, f) for f in ("av_kernels.hpp", "combine_kernels.hpp", "dispatch.hpp",
+                                             "valu_launch.hpp", "mfma_bf16_launch.hpp", "gqa_av.hip")]
+          + sorted(glob.glob(os.path.join(_CSRC, "launch_valu_*.hip")))
+          + sorted(glob.glob(os.path.join(_CSRC, "launch_mfma*.hip"))),
+    "qk": [os.path.join(_CSRC, f) for f in ("av_kernels.hpp", "qk_kernels.hpp", "qk_host.hpp", "qk_launch.hpp",
+                                             "dispatch.hpp")]
+          + sorted(glob.glob(os.path.join(_CSRC, "launch_qk_*.hip"))),
 }
 KERNEL_SOURCES["softmax"] = KERNEL_SOURCES["av"]
 # Profile file prefix and the dominant kernel's name fragment, per operation.
@@ -210,6 +216,22 @@ def cpu_baseline(w, attn, V, budget_s: float, softmax: bool = False):
     }
 
 
+def _oracle_rate(fn, alg_bytes: int, budget_s: float, what: str):
+    """Time fn(nthreads) (an oracle call) repeatedly for ~budget_s on all host threads."""
+    threads = int(os.environ.get("OMP_NUM_THREADS") or 0) or len(os.sched_getaffinity(0))
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn(threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 1000:
+            break
+    per = el / reps
+    return {"value": round(alg_bytes / per / 1e9, 3), "unit": "GB/s", "us_per_call": round(per * 1e6, 1),
+            "cores": threads, "kind": "oracle",
+            "sample": f"full {what}, {reps} calls in {el:.1f} s (fp64 C oracle, OpenMP)"}
+
+
 # ---- benchmark --------------------------------------------------------------------
 
 def _warm(args, calls, nrot):
@@ -280,6 +302,12 @@ def bench_fp8(args, w, dev, props):
     print(f"[bench] fp8 {'softmax ' if softmax else ''}{ms * 1e3:.2f} us/call, {gbs:.1f} GB/s "
           f"({100 * gbs / HBM_PEAK_GBS:.1f}% of peak); {nrot} rotation sets, plan {plan.as_dict()}",
           file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        orc = oracle.get()
+        cpu = _oracle_rate(lambda n: orc.fp8(x_h, q_h, scale_h, softmax=softmax, nthreads=n), alg,
+                           args.cpu_seconds, f"fp8 {w.name}")
     line = {
         "metric": FP8_METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 6), "us_per_call": round(ms * 1e3, 3),
@@ -291,7 +319,7 @@ def bench_fp8(args, w, dev, props):
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "whole call (pass 1 + combine)",
                      "us_per_launch": round(ms * 1e3, 3),
                      "timing": "HIP events around K back-to-back calls on the launch stream"},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 
@@ -340,6 +368,13 @@ def bench_paged(args, w, dev, props):
     print(f"[bench] paged P={P} {'softmax ' if softmax else ''}{ms * 1e3:.2f} us/call, {gbs:.1f} GB/s "
           f"({100 * gbs / HBM_PEAK_GBS:.1f}% of peak); {nrot} rotation sets, plan {plan.as_dict()}",
           file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        orc = oracle.get()
+        bt_h, lens_h = bt.cpu(), lens.cpu()
+        cpu = _oracle_rate(lambda n: orc.paged(x_h, pages_h, bt_h, lens_h, w.v_dtype, softmax=softmax, nthreads=n),
+                           w.algorithmic_bytes(), args.cpu_seconds, f"paged P={P} {w.name}")
     line = {
         "metric": PAGED_METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 6), "us_per_call": round(ms * 1e3, 3),
@@ -351,7 +386,7 @@ def bench_paged(args, w, dev, props):
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "whole call (pass 1 + combine)",
                      "us_per_launch": round(ms * 1e3, 3),
                      "timing": "HIP events around K back-to-back calls on the launch stream"},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 

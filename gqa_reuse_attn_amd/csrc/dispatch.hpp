@@ -1,0 +1,30 @@
+// Kernel launches of libgqa_av.so, one entry per engine. Each is defined in a
+// translation unit of its own (launch_*.hip) that instantiates only its
+// engine's kernels, so the library's kernels compile in parallel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "av_kernels.hpp"
+#include "qk_kernels.hpp"
+
+namespace gqa_av_launch {
+
+// VALU engine, element type DT (gqa_av::kF32 ...), fused softmax SM: VB-byte
+// lane loads, GT heads per tile, paged V when `paged` (16-byte loads only).
+template <int DT, bool SM>
+hipError_t valu(int VB, int GT, bool paged, const gqa_av::Pass1Args& a, hipStream_t s);
+
+// fp32 matrix engine: DE = D / 16 values per lane, nset sets of 16 heads.
+hipError_t mfma(int DT, int DE, int nset, const gqa_av::Pass1Args& a, hipStream_t s);
+
+// bf16 matrix engine: D of 64, 128 or 256, nset sets of 16 heads, ht KV heads per tile.
+template <bool SM>
+hipError_t mfma_bf16(int64_t D, int nset, int ht, const gqa_av::Pass1Args& a, hipStream_t s);
+
+// Score step, K of element type KDT: D / 32 blocks, nset sets of 16 heads.
+template <int KDT>
+hipError_t qk(int64_t D, int nset, const gqa_av::QkArgs& a, hipStream_t s);
+
+}  // namespace gqa_av_launch

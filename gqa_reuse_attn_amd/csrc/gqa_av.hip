@@ -23,7 +23,8 @@
 #include <string>
 #include <utility>
 
-#include "av_kernels.hpp"
+#include "combine_kernels.hpp"
+#include "dispatch.hpp"
 
 namespace {
 
@@ -156,164 +157,34 @@ int check_sizes(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_
 
 // ---- kernel dispatch ----------------------------------------------------------
 
-template <int DT, int VB, int GT, bool SM, bool PG>
-hipError_t launch_valu(const Pass1Args& a, hipStream_t s) {
-    constexpr int U = gqa_av::valu_unroll(GT);
-    if constexpr ((SM || PG) && GQA_AV_VALU_STAGE_WEIGHTS) {
-        return hipErrorInvalidValue;                 // the plan refuses this combination
-    } else {
-        hipLaunchKernelGGL((gqa_av::av_pass1_valu<DT, VB, GT, U, SM, PG>), dim3(a.nblocks), dim3(gqa_av::kThreads),
-                           0, s, a);
-        return hipGetLastError();
-    }
-}
-
-template <int DT, int VB, bool SM, bool PG = false>
-hipError_t launch_valu_gt(int GT, const Pass1Args& a, hipStream_t s) {
-    switch (GT) {
-    case 1: return launch_valu<DT, VB, 1, SM, PG>(a, s);
-    case 2: return launch_valu<DT, VB, 2, SM, PG>(a, s);
-    case 3: return launch_valu<DT, VB, 3, SM, PG>(a, s);
-    case 4: return launch_valu<DT, VB, 4, SM, PG>(a, s);
-    default: break;
-    }
-    // fp8 with 16-byte lane loads (16 values) only for tiles of up to 4 heads.
-    if constexpr (DT == gqa_av::kFP8 && VB == 16) {
-        return hipErrorInvalidValue;
-    } else {
-        switch (GT) {
-        case 5: return launch_valu<DT, VB, 5, SM, PG>(a, s);
-        case 6: return launch_valu<DT, VB, 6, SM, PG>(a, s);
-        case 7: return launch_valu<DT, VB, 7, SM, PG>(a, s);
-        case 8: return launch_valu<DT, VB, 8, SM, PG>(a, s);
-        case 16: return launch_valu<DT, VB, 16, SM, PG>(a, s);
-        default: return hipErrorInvalidValue;
-        }
-    }
-}
-
-// Paged V: 16-byte lane loads only.
-template <int DT>
-hipError_t launch_valu_paged(bool sm, int GT, const Pass1Args& a, hipStream_t s) {
-    if constexpr (DT == gqa_av::kFP8) {
-        return hipErrorInvalidValue;                 // the plan refuses paged fp8 V
-    } else {
-        return sm ? launch_valu_gt<DT, 16, true, true>(GT, a, s) : launch_valu_gt<DT, 16, false, true>(GT, a, s);
-    }
-}
-
-template <int DT, bool SM>
-hipError_t launch_valu_vb(int VB, int GT, const Pass1Args& a, hipStream_t s) {
-    switch (VB) {
-    case 16: return launch_valu_gt<DT, 16, SM>(GT, a, s);
-    case 8: return launch_valu_gt<DT, 8, SM>(GT, a, s);
-    case 4: return launch_valu_gt<DT, 4, SM>(GT, a, s);
-    case 2:
-        if constexpr (DT != gqa_av::kF32) return launch_valu_gt<DT, 2, SM>(GT, a, s);
-        return hipErrorInvalidValue;
-    default: return hipErrorInvalidValue;
-    }
-}
-
-template <int DT, int DE, int NSET>
-hipError_t launch_mfma(const Pass1Args& a, hipStream_t s) {
-    constexpr int U = gqa_av::mfma_unroll(DE * gqa_av::esize<DT>());
-    hipLaunchKernelGGL((gqa_av::av_pass1_mfma<DT, DE, NSET, U>), dim3(a.nblocks), dim3(gqa_av::kThreads), 0, s, a);
-    return hipGetLastError();
-}
-
-template <int DT, int DE>
-hipError_t launch_mfma_set(int nset, const Pass1Args& a, hipStream_t s) {
-    if (nset == 1) return launch_mfma<DT, DE, 1>(a, s);
-    if constexpr (DE <= 8) {
-        if (nset == 2) return launch_mfma<DT, DE, 2>(a, s);
-    }
-    return hipErrorInvalidValue;
-}
-
-template <int PR, int NSET, int HT, bool SM>
-hipError_t launch_mfma_bf16(const Pass1Args& a, hipStream_t s) {
-    hipLaunchKernelGGL((gqa_av::av_pass1_mfma_bf16<PR, NSET, GQA_AV_MFMA_BF16_CHUNKS, HT, SM>), dim3(a.nblocks),
-                       dim3(gqa_av::kThreads), 0, s, a);
-    return hipGetLastError();
-}
-
-template <int PR, int NSET, bool SM>
-hipError_t launch_mfma_bf16_ht(int ht, const Pass1Args& a, hipStream_t s) {
-    switch (ht) {
-    case 1: return launch_mfma_bf16<PR, NSET, 1, SM>(a, s);
-    case 2: return launch_mfma_bf16<PR, NSET, 2, SM>(a, s);
-    case 4: return launch_mfma_bf16<PR, NSET, 4, SM>(a, s);
-    default: return hipErrorInvalidValue;
-    }
-}
-
-template <bool SM>
-hipError_t launch_mfma_bf16_pr(int64_t D, int nset, int ht, const Pass1Args& a, hipStream_t s) {
-    switch (D) {
-    case 64: return nset == 1 ? launch_mfma_bf16_ht<8, 1, SM>(ht, a, s) : launch_mfma_bf16_ht<8, 2, SM>(ht, a, s);
-    case 128: return nset == 1 ? launch_mfma_bf16_ht<16, 1, SM>(ht, a, s) : launch_mfma_bf16_ht<16, 2, SM>(ht, a, s);
-    case 256: return nset == 1 ? launch_mfma_bf16_ht<32, 1, SM>(ht, a, s) : hipErrorInvalidValue;
-    default: return hipErrorInvalidValue;
-    }
-}
-
-template <int DT>
-hipError_t launch_mfma_de(int DE, int nset, const Pass1Args& a, hipStream_t s) {
-    switch (DE) {
-    case 2: return launch_mfma_set<DT, 2>(nset, a, s);
-    case 4: return launch_mfma_set<DT, 4>(nset, a, s);
-    case 6:
-        if constexpr (DT != gqa_av::kF32) return launch_mfma_set<DT, 6>(nset, a, s);
-        return hipErrorInvalidValue;
-    case 8: return launch_mfma_set<DT, 8>(nset, a, s);
-    case 16:
-        if constexpr (DT != gqa_av::kF32) return launch_mfma_set<DT, 16>(nset, a, s);
-        return hipErrorInvalidValue;
-    default: return hipErrorInvalidValue;
-    }
-}
-
 hipError_t launch_pass1(int v_dtype, const gqa_av_plan& p, int64_t D, const Pass1Args& a, hipStream_t s) {
-    if (p.page_size > 0) {
-        if (p.engine != GQA_AV_ENGINE_VALU || p.vec_bytes != 16) return hipErrorInvalidValue;
-        switch (v_dtype) {
-        case GQA_AV_F32: return launch_valu_paged<gqa_av::kF32>(p.softmax, p.heads_per_tile, a, s);
-        case GQA_AV_F16: return launch_valu_paged<gqa_av::kF16>(p.softmax, p.heads_per_tile, a, s);
-        case GQA_AV_BF16: return launch_valu_paged<gqa_av::kBF16>(p.softmax, p.heads_per_tile, a, s);
-        default: return hipErrorInvalidValue;
-        }
-    }
+    const int dt = v_dtype == GQA_AV_F32 ? gqa_av::kF32
+                 : v_dtype == GQA_AV_F16 ? gqa_av::kF16
+                 : v_dtype == GQA_AV_BF16 ? gqa_av::kBF16 : gqa_av::kFP8;
     if (p.engine == GQA_AV_ENGINE_MFMA_BF16) {
-        if (v_dtype != GQA_AV_BF16) return hipErrorInvalidValue;
-        return p.softmax ? launch_mfma_bf16_pr<true>(D, p.heads_per_tile / 16, p.kv_heads_per_tile, a, s)
-                         : launch_mfma_bf16_pr<false>(D, p.heads_per_tile / 16, p.kv_heads_per_tile, a, s);
-    }
-    if (p.softmax) {
-        if (p.engine != GQA_AV_ENGINE_VALU) return hipErrorInvalidValue;
-        switch (v_dtype) {
-        case GQA_AV_F32: return launch_valu_vb<gqa_av::kF32, true>(p.vec_bytes, p.heads_per_tile, a, s);
-        case GQA_AV_F16: return launch_valu_vb<gqa_av::kF16, true>(p.vec_bytes, p.heads_per_tile, a, s);
-        case GQA_AV_BF16: return launch_valu_vb<gqa_av::kBF16, true>(p.vec_bytes, p.heads_per_tile, a, s);
-        case GQA_AV_FP8_E4M3: return launch_valu_vb<gqa_av::kFP8, true>(p.vec_bytes, p.heads_per_tile, a, s);
-        default: return hipErrorInvalidValue;
-        }
+        if (v_dtype != GQA_AV_BF16 || p.page_size > 0) return hipErrorInvalidValue;
+        return p.softmax ? gqa_av_launch::mfma_bf16<true>(D, p.heads_per_tile / 16, p.kv_heads_per_tile, a, s)
+                         : gqa_av_launch::mfma_bf16<false>(D, p.heads_per_tile / 16, p.kv_heads_per_tile, a, s);
     }
     if (p.engine == GQA_AV_ENGINE_MFMA) {
-        const int DE = static_cast<int>(D / 16), nset = p.heads_per_tile / 16;
-        switch (v_dtype) {
-        case GQA_AV_F32: return launch_mfma_de<gqa_av::kF32>(DE, nset, a, s);
-        case GQA_AV_F16: return launch_mfma_de<gqa_av::kF16>(DE, nset, a, s);
-        case GQA_AV_BF16: return launch_mfma_de<gqa_av::kBF16>(DE, nset, a, s);
-        default: return hipErrorInvalidValue;
-        }
+        if (p.softmax || p.page_size > 0 || v_dtype == GQA_AV_FP8_E4M3) return hipErrorInvalidValue;
+        return gqa_av_launch::mfma(dt, static_cast<int>(D / 16), p.heads_per_tile / 16, a, s);
     }
-    switch (v_dtype) {
-    case GQA_AV_F32: return launch_valu_vb<gqa_av::kF32, false>(p.vec_bytes, p.heads_per_tile, a, s);
-    case GQA_AV_F16: return launch_valu_vb<gqa_av::kF16, false>(p.vec_bytes, p.heads_per_tile, a, s);
-    case GQA_AV_BF16: return launch_valu_vb<gqa_av::kBF16, false>(p.vec_bytes, p.heads_per_tile, a, s);
-    case GQA_AV_FP8_E4M3: return launch_valu_vb<gqa_av::kFP8, false>(p.vec_bytes, p.heads_per_tile, a, s);
-    default: return hipErrorInvalidValue;
+    const bool pg = p.page_size > 0;
+    const int VB = p.vec_bytes, GT = p.heads_per_tile;
+    switch (dt) {
+    case gqa_av::kF32:
+        return p.softmax ? gqa_av_launch::valu<gqa_av::kF32, true>(VB, GT, pg, a, s)
+                         : gqa_av_launch::valu<gqa_av::kF32, false>(VB, GT, pg, a, s);
+    case gqa_av::kF16:
+        return p.softmax ? gqa_av_launch::valu<gqa_av::kF16, true>(VB, GT, pg, a, s)
+                         : gqa_av_launch::valu<gqa_av::kF16, false>(VB, GT, pg, a, s);
+    case gqa_av::kBF16:
+        return p.softmax ? gqa_av_launch::valu<gqa_av::kBF16, true>(VB, GT, pg, a, s)
+                         : gqa_av_launch::valu<gqa_av::kBF16, false>(VB, GT, pg, a, s);
+    default:
+        return p.softmax ? gqa_av_launch::valu<gqa_av::kFP8, true>(VB, GT, pg, a, s)
+                         : gqa_av_launch::valu<gqa_av::kFP8, false>(VB, GT, pg, a, s);
     }
 }
 

@@ -1,0 +1,4 @@
+// VALU engine kernels for bf16 V, plain product.
+#include "valu_launch.hpp"
+
+template hipError_t gqa_av_launch::valu<gqa_av::kBF16, false>(int, int, bool, const gqa_av::Pass1Args&, hipStream_t);

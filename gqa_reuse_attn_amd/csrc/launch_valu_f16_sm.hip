@@ -1,0 +1,4 @@
+// VALU engine kernels for f16 V, fused softmax.
+#include "valu_launch.hpp"
+
+template hipError_t gqa_av_launch::valu<gqa_av::kF16, true>(int, int, bool, const gqa_av::Pass1Args&, hipStream_t);

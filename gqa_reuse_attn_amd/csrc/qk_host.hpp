@@ -3,8 +3,8 @@
 // helpers it shares.
 #pragma once
 
+#include "dispatch.hpp"
 #include "gqa_qk.h"
-#include "qk_kernels.hpp"
 
 namespace {
 
@@ -94,41 +94,6 @@ int qk_plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int k
     return GQA_AV_OK;
 }
 
-template <int KDT, int NBLK, int NSET>
-hipError_t launch_qk_ht(const QkArgs& a, hipStream_t s) {
-    switch (a.ht) {
-    case 1: hipLaunchKernelGGL((gqa_av::qk_scores<KDT, NBLK, NSET, 1>), dim3(a.nblocks), dim3(gqa_av::kThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((gqa_av::qk_scores<KDT, NBLK, NSET, 2>), dim3(a.nblocks), dim3(gqa_av::kThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((gqa_av::qk_scores<KDT, NBLK, NSET, 4>), dim3(a.nblocks), dim3(gqa_av::kThreads), 0, s, a); break;
-    default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-}
-
-template <int KDT, int NBLK>
-hipError_t launch_qk_nset(int nset, const QkArgs& a, hipStream_t s) {
-    if (nset == 1) return launch_qk_ht<KDT, NBLK, 1>(a, s);
-    if constexpr (NBLK <= 4) {
-        if (nset == 2) return launch_qk_ht<KDT, NBLK, 2>(a, s);
-    }
-    return hipErrorInvalidValue;
-}
-
-template <int KDT>
-hipError_t launch_qk_nblk(int64_t D, int nset, const QkArgs& a, hipStream_t s) {
-    switch (D / 32) {
-    case 1: return launch_qk_nset<KDT, 1>(nset, a, s);
-    case 2: return launch_qk_nset<KDT, 2>(nset, a, s);
-    case 3: return launch_qk_nset<KDT, 3>(nset, a, s);
-    case 4: return launch_qk_nset<KDT, 4>(nset, a, s);
-    case 5: return launch_qk_nset<KDT, 5>(nset, a, s);
-    case 6: return launch_qk_nset<KDT, 6>(nset, a, s);
-    case 7: return launch_qk_nset<KDT, 7>(nset, a, s);
-    case 8: return launch_qk_nset<KDT, 8>(nset, a, s);
-    default: return hipErrorInvalidValue;
-    }
-}
-
 int qk_run(const float* q, const void* K, float* scores, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
            int64_t D, int k_dtype, float scale, const gqa_qk_plan* plan, void* stream) {
     if (!plan) return fail(GQA_AV_ERR_INVALID_ARG, "plan is NULL");
@@ -172,9 +137,9 @@ int qk_run(const float* q, const void* K, float* scores, int64_t B, int64_t C, i
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     switch (k_dtype) {
-    case GQA_AV_F32: e = launch_qk_nblk<gqa_av::kF32>(D, nset, a, s); break;
-    case GQA_AV_F16: e = launch_qk_nblk<gqa_av::kF16>(D, nset, a, s); break;
-    default: e = launch_qk_nblk<gqa_av::kBF16>(D, nset, a, s); break;
+    case GQA_AV_F32: e = gqa_av_launch::qk<gqa_av::kF32>(D, nset, a, s); break;
+    case GQA_AV_F16: e = gqa_av_launch::qk<gqa_av::kF16>(D, nset, a, s); break;
+    default: e = gqa_av_launch::qk<gqa_av::kBF16>(D, nset, a, s); break;
     }
     if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "score launch: %s", hipGetErrorString(e));
     return GQA_AV_OK;

@@ -42,6 +42,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace gqa_av {
 
 constexpr int kThreads = 256;
@@ -1026,9 +1028,19 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma(Pass1Args a) {
 // agree on the chunk's maximum through two lane exchanges, so every product
 // summed into one accumulator uses the same maximum. The waves of a KV head
 // are brought to their common maximum before they are added.
-template <int PR, int NSET, int U, int HT, bool SM = false>
+//
+// VDT: V's element type, kBF16 or kFP8. fp8 V (OCP E4M3) is loaded as 8-byte
+// pieces of 8 values and widened in registers to the same 16-byte bf16 pieces
+// before the LDS store -- exactly: every E4M3 value is a bfloat16 value -- so
+// everything after the store is the bf16 path; each output is then multiplied
+// by its KV head's scale.
+template <int PR, int NSET, int U, int HT, bool SM = false, int VDT = kBF16>
 __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
     static_assert(PR == 8 || PR == 16 || PR == 32, "D must be 64, 128 or 256");
+    static_assert(VDT == kBF16 || VDT == kFP8, "bf16 or fp8 V");
+    constexpr bool FP8 = VDT == kFP8;
+    constexpr int VES = FP8 ? 1 : 2;                 // bytes of one V element in memory
+    constexpr int PB = 8 * VES;                      // bytes of one 8-value piece in memory
     static_assert(HT == 1 || HT == 2 || HT == 4, "KV heads per tile must divide the waves");
     constexpr int D = PR * 8;
     constexpr int RB = PR * 16;                      // bytes of one D-row
@@ -1054,7 +1066,7 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
     const int64_t cb = uniform64(static_cast<int64_t>(T.s) * a.rows_per_split);
     const int64_t ce = uniform64(min(a.C, cb + a.rows_per_split));
     const int nrows = static_cast<int>(ce - cb);     // > 0: splits never start past C
-    const int vrow = a.Hkv * D * 2;                  // bytes between consecutive rows of V
+    const int vrow = a.Hkv * D * VES;                // bytes between consecutive rows of V
 
     // Both operands are read through buffer resources that end with the
     // split's last row: a row at or past ce reads as zero, so a partial last
@@ -1062,14 +1074,14 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
     // pipeline's unconditional reload) touches no memory. The plan keeps a
     // split's V span under 2 GB so 32-bit offsets suffice.
     const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(a.V) + ((static_cast<size_t>(T.b) * a.C + cb) * a.Hkv + T.kv) * D * 2, 0,
-        (nrows - 1) * vrow + HT * D * 2, kRawBufferFlags);
+        const_cast<uint8_t*>(a.V) + ((static_cast<size_t>(T.b) * a.C + cb) * a.Hkv + T.kv) * D * VES, 0,
+        (nrows - 1) * vrow + HT * D * VES, kRawBufferFlags);
     const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(a.attn) + (static_cast<size_t>(T.b) * a.C + cb) * a.Hq + T.q_first, 0,
         ((nrows - 1) * a.Hq + (HT - 1) * a.G + T.nq) * 4, kRawBufferFlags);
     // This lane's pieces of a chunk: load i covers rows RPI i .. RPI i + RPI - 1.
     const int prow = lane / PR, ppiece = lane % PR;
-    const int vlane = prow * vrow + kvl * D * 2 + ppiece * 16;
+    const int vlane = prow * vrow + kvl * D * VES + ppiece * PB;
     // Heads past the tile's nq read the tile's last head (in range); their A
     // rows only feed output rows that are never written.
     int wlane[NSET];
@@ -1114,8 +1126,9 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
     constexpr int RSTEP = 32 * WPH * U;             // rows per workgroup step
     const int nsteps = (nrows + RSTEP - 1) / RSTEP;
 
+    typedef typename std::conditional<FP8, u32x2, u32x4>::type Piece;
     struct Buf {
-        u32x4 v[U][LPI];
+        Piece v[U][LPI];
         float w[U][NSET][8];
     };
     // Chunk u of step st starts at split row 32 (st WPH U + u WPH + wh).
@@ -1124,8 +1137,13 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
         for (int u = 0; u < U; ++u) {
             const int r0 = 32 * (st * WPH * U + u * WPH + wh);
 #pragma unroll
-            for (int i = 0; i < LPI; ++i)
-                bf.v[u][i] = __builtin_amdgcn_raw_buffer_load_b128(vres, vlane, (r0 + RPI * i) * vrow, kCachePolicyNt);
+            for (int i = 0; i < LPI; ++i) {
+                if constexpr (FP8)
+                    bf.v[u][i] = __builtin_amdgcn_raw_buffer_load_b64(vres, vlane, (r0 + RPI * i) * vrow, kCachePolicyNt);
+                else
+                    bf.v[u][i] = __builtin_amdgcn_raw_buffer_load_b128(vres, vlane, (r0 + RPI * i) * vrow,
+                                                                       kCachePolicyNt);
+            }
 #pragma unroll
             for (int j = 0; j < 8; ++j)
 #pragma unroll
@@ -1141,8 +1159,23 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
             // order; LDS executes one wave's operations in order).
             asm volatile("" ::: "memory");
 #pragma unroll
-            for (int i = 0; i < LPI; ++i)
-                *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(region + st_off(i)) = bf.v[u][i];
+            for (int i = 0; i < LPI; ++i) {
+                u32x4 piece;
+                if constexpr (FP8) {
+                    // 8 E4M3 values -> 8 bfloat16 values (the upper halves of their exact fp32 forms)
+                    typedef float f32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(bf.v[u][i][h]), false);
+                        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(bf.v[u][i][h]), true);
+                        piece[2 * h] = (__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xffff0000u);
+                        piece[2 * h + 1] = (__float_as_uint(hi.x) >> 16) | (__float_as_uint(hi.y) & 0xffff0000u);
+                    }
+                } else {
+                    piece = bf.v[u][i];
+                }
+                *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(region + st_off(i)) = piece;
+            }
             asm volatile("" ::: "memory");
             float wt[NSET][8];
             if constexpr (SM) {
@@ -1327,6 +1360,9 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
                 const int reg = (e >> 6), h = 16 * ((reg >> 2) / NT) + 4 * ((e & 63) >> 4) + (reg & 3);
                 sum = nrows > 0 ? sum / s_tl[k][h] : 0.0f;
             }
+        }
+        if constexpr (FP8) {
+            if (a.v_scale) sum *= a.v_scale[T.kv + k];   // the tile's k-th KV head
         }
         if (in_kernel) {
             store_coherent(blk + static_cast<size_t>(T.s) * TOW + idx, sum);

@@ -162,9 +162,13 @@ hipError_t launch_pass1(int v_dtype, const gqa_av_plan& p, int64_t D, const Pass
                  : v_dtype == GQA_AV_F16 ? gqa_av::kF16
                  : v_dtype == GQA_AV_BF16 ? gqa_av::kBF16 : gqa_av::kFP8;
     if (p.engine == GQA_AV_ENGINE_MFMA_BF16) {
-        if (v_dtype != GQA_AV_BF16 || p.page_size > 0) return hipErrorInvalidValue;
-        return p.softmax ? gqa_av_launch::mfma_bf16<true>(D, p.heads_per_tile / 16, p.kv_heads_per_tile, a, s)
-                         : gqa_av_launch::mfma_bf16<false>(D, p.heads_per_tile / 16, p.kv_heads_per_tile, a, s);
+        if ((v_dtype != GQA_AV_BF16 && v_dtype != GQA_AV_FP8_E4M3) || p.page_size > 0) return hipErrorInvalidValue;
+        const int nset = p.heads_per_tile / 16, ht = p.kv_heads_per_tile;
+        if (v_dtype == GQA_AV_FP8_E4M3)
+            return p.softmax ? gqa_av_launch::mfma_bf16<gqa_av::kFP8, true>(D, nset, ht, a, s)
+                             : gqa_av_launch::mfma_bf16<gqa_av::kFP8, false>(D, nset, ht, a, s);
+        return p.softmax ? gqa_av_launch::mfma_bf16<gqa_av::kBF16, true>(D, nset, ht, a, s)
+                         : gqa_av_launch::mfma_bf16<gqa_av::kBF16, false>(D, nset, ht, a, s);
     }
     if (p.engine == GQA_AV_ENGINE_MFMA) {
         if (p.softmax || p.page_size > 0 || v_dtype == GQA_AV_FP8_E4M3) return hipErrorInvalidValue;
@@ -211,9 +215,10 @@ bool mfma_fits(int64_t D, int es, int v_align, int nset) {
 // swizzle), 16-byte aligned V, rows of V and attn of at most 1 MB, and the
 // same 64 KB bound on the four waves' tiles as the fp32 engine.
 bool mfma_bf16_fits(int v_dtype, int64_t Hq, int64_t Hkv, int64_t D, int v_align, int nset) {
-    if (v_dtype != GQA_AV_BF16 || !(D == 64 || D == 128 || D == 256)) return false;
-    if (Hkv * D * 2 > (int64_t{1} << 20) || Hq * 4 > (int64_t{1} << 20)) return false;  // row bytes for 32-bit offsets
-    if (v_align % 16 != 0) return false;
+    if ((v_dtype != GQA_AV_BF16 && v_dtype != GQA_AV_FP8_E4M3) || !(D == 64 || D == 128 || D == 256)) return false;
+    const int es = v_dtype == GQA_AV_FP8_E4M3 ? 1 : 2;
+    if (Hkv * D * es > (int64_t{1} << 20) || Hq * 4 > (int64_t{1} << 20)) return false;  // row bytes for 32-bit offsets
+    if (v_align % (8 * es) != 0) return false;       // 8-value pieces
     return nset * D <= 256;
 }
 
@@ -282,16 +287,16 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
     const int nset16 = (G > 16 && mfma_bf16_fits(v_dtype, Hq, Hkv, D, v_align, 2)) ? 2 : 1;
     const bool mfma16_ok = resolved == GQA_AV_REUSE && mfma_bf16_fits(v_dtype, Hq, Hkv, D, v_align, nset16);
     int engine = h.engine;
-    if (engine == GQA_AV_ENGINE_AUTO && (paged || v_dtype == GQA_AV_FP8_E4M3)) engine = GQA_AV_ENGINE_VALU;
+    if (engine == GQA_AV_ENGINE_AUTO && paged) engine = GQA_AV_ENGINE_VALU;
     if (engine == GQA_AV_ENGINE_AUTO) {
         engine = GQA_AV_ENGINE_VALU;
         if (G >= kMfmaMinGroup && mfma16_ok) engine = GQA_AV_ENGINE_MFMA_BF16;
-        else if (G >= kMfmaMinGroup && mfma_ok && !sm) engine = GQA_AV_ENGINE_MFMA;
+        else if (G >= kMfmaMinGroup && mfma_ok && !sm && v_dtype != GQA_AV_FP8_E4M3) engine = GQA_AV_ENGINE_MFMA;
     }
     if (sm && engine == GQA_AV_ENGINE_MFMA)
         return fail(GQA_AV_ERR_UNSUPPORTED, "the fused softmax runs on the VALU or bf16 matrix engine");
-    if (v_dtype == GQA_AV_FP8_E4M3 && engine != GQA_AV_ENGINE_VALU)
-        return fail(GQA_AV_ERR_UNSUPPORTED, "fp8 V runs on the VALU engine");
+    if (v_dtype == GQA_AV_FP8_E4M3 && engine == GQA_AV_ENGINE_MFMA)
+        return fail(GQA_AV_ERR_UNSUPPORTED, "fp8 V runs on the VALU or bf16 matrix engine");
     if (sm && engine == GQA_AV_ENGINE_VALU && GQA_AV_VALU_STAGE_WEIGHTS)
         return fail(GQA_AV_ERR_UNSUPPORTED, "the fused softmax needs the per-lane weight VALU build");
     if (engine == GQA_AV_ENGINE_MFMA && !mfma_ok)
@@ -299,7 +304,7 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
                     "MFMA engine needs reuse mode, D %% 16 == 0 with a 4/8/12/16/32-byte lane chunk and matching V alignment");
     if (engine == GQA_AV_ENGINE_MFMA_BF16 && !mfma16_ok)
         return fail(GQA_AV_ERR_UNSUPPORTED,
-                    "bf16 MFMA engine needs reuse mode, bf16 V, D of 64, 128 or 256 and 16-byte aligned V");
+                    "bf16 MFMA engine needs reuse mode, bf16 or fp8 V, D of 64, 128 or 256 and V aligned to 8 values");
     const bool matrix = engine == GQA_AV_ENGINE_MFMA || engine == GQA_AV_ENGINE_MFMA_BF16;
 
     // KV heads per tile: the VALU and bf16 matrix engines in reuse mode can
@@ -344,7 +349,7 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
     int64_t Lc, rps, ndt, rows_per_step, tile_outputs;
     int64_t heads_major;  // tiles along the head axis per KV head
     if (engine == GQA_AV_ENGINE_MFMA_BF16) {
-        VB = 16;
+        VB = v_dtype == GQA_AV_FP8_E4M3 ? 8 : 16;    // one 8-value piece per lane load
         GT = 16 * nset16;
         nsg = static_cast<int>(ceil_div(G, GT));
         heads_major = nsg;

@@ -131,17 +131,24 @@ def test_fp8_sweep(B, C, Hq, Hkv, D, std, oracle_lib):
                 if Hq // Hkv >= 2 and Hkv % ht == 0:
                     plans.append(ga.make_plan(B, C, Hq, Hkv, D, "fp8", "reuse", kv_tile=ht, nsplit=3,
                                               softmax=softmax))
+            if Hq // Hkv >= 2 and D in (64, 128, 256):        # the bf16 matrix engine at any G
+                for ht in (1, 2):
+                    if Hkv % ht == 0:
+                        plans.append(ga.make_plan(B, C, Hq, Hkv, D, "fp8", "reuse", engine="mfma_bf16", kv_tile=ht,
+                                                  nsplit=2, softmax=softmax))
             for plan in plans:
                 out = _run(x, q, sc, softmax, plan=plan)
                 _check(out, ref, x, q, sc if sc is not None else torch.ones(Hkv), softmax,
                        f"fp8 {(B, C, Hq, Hkv, D)} scale={sc is not None} {plan.as_dict()}")
 
 
-def test_fp8_every_byte_and_dense_entry_points(oracle_lib):
+@pytest.mark.parametrize("Hq", [8, 16])
+def test_fp8_every_byte_and_dense_entry_points(Hq, oracle_lib):
     """Every E4M3 byte but NaN appears in V; one-hot weights return V * scale
     exactly where the product is exact (scale a power of two); gqa_av_decode
-    with fp8 V equals the fp8 entry point with unit scales bit for bit."""
-    B, C, Hq, Hkv, D = 2, 254, 8, 2, 64
+    with fp8 V equals the fp8 entry point with unit scales bit for bit. G = 4
+    runs on the VALU engine, G = 8 on the bf16 matrix engine."""
+    B, C, Hkv, D = 2, 254, 2, 64
     g = torch.Generator().manual_seed(7)
     vals = torch.tensor([b for b in range(256) if (b & 0x7F) != 0x7F], dtype=torch.uint8)
     raw = vals[torch.randint(0, vals.numel(), (B, C, Hkv, D), generator=g)]

@@ -506,13 +506,17 @@ def test_fp8_plans():
     for wname, w in WORKLOADS.items():
         for sm in (False, True):
             p = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, "fp8", softmax=sm)
-            assert p.engine == 1 and p.softmax == int(sm), wname
-            assert p.vec_bytes <= (16 if p.heads_per_tile <= 4 else 8), wname
+            assert p.softmax == int(sm), wname
             G = w.Hq // w.Hkv
-            assert p.v_bytes_read == w.B * w.C * w.Hkv * w.D * (1 if G >= 2 else 1) * p.subgroups
+            if G >= 5 and w.D in (64, 128, 256):
+                assert p.engine == 3 and p.vec_bytes == 8, wname      # bf16 matrix engine, 8-value pieces
+            else:
+                assert p.engine == 1 and p.vec_bytes <= (16 if p.heads_per_tile <= 4 else 8), wname
+            assert p.v_bytes_read == w.B * w.C * w.Hkv * w.D * p.subgroups
     assert ga.make_plan(1, 100, 8, 2, 6, "fp8").vec_bytes == 2
     assert ga.make_plan(1, 100, 8, 2, 6, "fp8", v_align=2).vec_bytes == 2
-    for kw in (dict(engine="mfma"), dict(engine="mfma_bf16"), dict(page_size=16)):
+    assert ga.make_plan(2, 1000, 16, 2, 128, "fp8", "reuse", engine="mfma_bf16").engine == 3
+    for kw in (dict(engine="mfma"), dict(page_size=16)):
         with pytest.raises(ga.GqaAvError) as e:
             ga.make_plan(2, 1000, 16, 2, 128, "fp8", "reuse", **kw)
         assert e.value.name == "UNSUPPORTED", kw

@@ -69,12 +69,13 @@ def _remap(i, n):
     return x * (per + 1) + k if x < rem else rem * (per + 1) + (x - rem) * per + k
 
 
-def _check_plan(p, B, C, Hq, Hkv, D):
-    assert p.engine == ENGINE_BF16
+def _check_plan(p, B, C, Hq, Hkv, D, es=2):
+    """es: bytes of a V element (2: bf16; 1: fp8, loaded as 8-byte pieces of 8 values)."""
+    assert p.engine == ENGINE_BF16 and p.vec_bytes == 8 * es
     PR, HT = D // 8, p.kv_heads_per_tile
     RPI, LPI, WPH = 64 // PR, PR // 2, 4 // HT
     NSET = p.heads_per_tile // 16
-    RSTEP, vrow, G = 32 * WPH, Hkv * D * 2, Hq // Hkv
+    RSTEP, vrow, G = 32 * WPH, Hkv * D * es, Hq // Hkv
     GT, nsg, ns = 16 * NSET, p.subgroups, p.nsplit
     TO = GT * D
     assert p.lanes_per_row == HT * D // 8 and p.row_slots == 32 * WPH
@@ -93,8 +94,8 @@ def _check_plan(p, B, C, Hq, Hkv, D):
         ce = min(C, cb + p.rows_per_split)
         nrows = ce - cb
         assert nrows > 0
-        vrec = (nrows - 1) * vrow + HT * D * 2
-        assert ((b * C + cb) * Hkv + kv) * D * 2 + vrec <= B * C * Hkv * D * 2 and vrec < 2 ** 31
+        vrec = (nrows - 1) * vrow + HT * D * es
+        assert ((b * C + cb) * Hkv + kv) * D * es + vrec <= B * C * Hkv * D * es and vrec < 2 ** 31
         wrec = ((nrows - 1) * Hq + (HT - 1) * G + nq) * 4
         assert ((b * C + cb) * Hq + qf) * 4 + wrec <= B * C * Hq * 4 and wrec < 2 ** 31
         nsteps = -(-nrows // RSTEP)
@@ -108,9 +109,9 @@ def _check_plan(p, B, C, Hq, Hkv, D):
                 kvl, wh = wave // WPH, wave % WPH
                 r0 = 32 * (step * WPH + wh)
                 rows = r0 + RPI * np.arange(LPI)[:, None] + lanes[None, :] // PR
-                off = ((lanes // PR) * vrow + kvl * D * 2 + (lanes % PR) * 16
+                off = ((lanes // PR) * vrow + kvl * D * es + (lanes % PR) * 8 * es
                        + (r0 + RPI * np.arange(LPI)[:, None]) * vrow)
-                assert np.array_equal(off + 16 <= vrec, rows < nrows)
+                assert np.array_equal(off + 8 * es <= vrec, rows < nrows)
                 wrows = r0 + 8 * (lanes >> 4)[None, :] + np.arange(8)[:, None]
                 for sset in range(NSET):
                     woff = np.minimum((lanes & 15) + 16 * sset, nq - 1)
@@ -152,10 +153,13 @@ def test_bf16_engine_plan_bounds(B, C, Hq, Hkv, D):
             for ht in (0, 1, 2, 4):
                 if ht > 1 and Hkv % ht:
                     continue
-                p = ga.make_plan(B, C, Hq, Hkv, D, "bf16", "reuse", engine="mfma_bf16", nsplit=ns,
-                                 combine=comb, kv_tile=ht, softmax=sm)
-                assert p.softmax == int(sm)
-                _check_plan(p, B, C, Hq, Hkv, D)
+                for dt, es in (("bf16", 2), ("fp8", 1)):
+                    if dt == "fp8" and comb == "last":
+                        continue
+                    p = ga.make_plan(B, C, Hq, Hkv, D, dt, "reuse", engine="mfma_bf16", nsplit=ns,
+                                     combine=comb, kv_tile=ht, softmax=sm)
+                    assert p.softmax == int(sm)
+                    _check_plan(p, B, C, Hq, Hkv, D, es)
 
 
 ENGINE_VALU = 1

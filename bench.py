@@ -351,8 +351,8 @@ def bench_paged(args, w, dev, props):
     pages_h[perm] = chunks                           # chunk i (sequence i // maxp) lives in page perm[i]
     bt = perm.to(torch.int32).view(w.B, maxp).contiguous().to(dev)
     lens = torch.full((w.B,), w.C, dtype=torch.int32, device=dev)
-    plan = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, args.mode, nsplit=args.nsplit,
-                        cu_count=props.multi_processor_count, softmax=softmax, page_size=P)
+    plan = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, args.mode, engine=args.engine, nsplit=args.nsplit,
+                        cu_count=props.multi_processor_count, kv_tile=args.kv_tile, softmax=softmax, page_size=P)
     per_set = w.algorithmic_bytes()
     nrot = max(1, math.ceil(args.rotate_mb * 2 ** 20 / per_set))
     x0, p0 = x_h.to(dev), pages_h.to(dev)

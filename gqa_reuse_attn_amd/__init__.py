@@ -416,7 +416,7 @@ def bind_fp8(w, V, v_scale=None, out=None, plan: Optional[Plan] = None, softmax:
 
 def _check_paged(w, pages, block_table, seq_lens, out):
     torch = _torch()
-    vmap = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
+    vmap = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16", torch.float8_e4m3fn: "fp8"}
     if w.dim() != 3 or pages.dim() != 4 or block_table.dim() != 2 or seq_lens.dim() != 1:
         raise ValueError("w [B,C,Hq], pages [num_pages,page_size,Hkv,D], block_table [B,max_pages], seq_lens [B]")
     B, C, Hq = w.shape
@@ -424,7 +424,7 @@ def _check_paged(w, pages, block_table, seq_lens, out):
     if block_table.shape[0] != B or seq_lens.shape[0] != B:
         raise ValueError("block_table and seq_lens must have B rows")
     if w.dtype != torch.float32 or pages.dtype not in vmap:
-        raise TypeError("w must be float32 and pages float32/float16/bfloat16")
+        raise TypeError("w must be float32 and pages float32/float16/bfloat16/float8_e4m3fn")
     if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
         raise TypeError("block_table and seq_lens must be int32")
     ts = (w, pages, block_table, seq_lens)

@@ -1034,7 +1034,11 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma(Pass1Args a) {
 // before the LDS store -- exactly: every E4M3 value is a bfloat16 value -- so
 // everything after the store is the bf16 path; each output is then multiplied
 // by its KV head's scale.
-template <int PR, int NSET, int U, int HT, bool SM = false, int VDT = kBF16>
+//
+// PG: paged V (see av_pass1_valu): the split's page list in LDS, each lane's
+// row addresses from it, rows past the sequence's length reading the split's
+// last valid row with weight 0.
+template <int PR, int NSET, int U, int HT, bool SM = false, int VDT = kBF16, bool PG = false>
 __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
     static_assert(PR == 8 || PR == 16 || PR == 32, "D must be 64, 128 or 256");
     static_assert(VDT == kBF16 || VDT == kFP8, "bf16 or fp8 V");
@@ -1064,8 +1068,14 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
 
     // The split bounds are workgroup-uniform; keep them in scalar registers.
     const int64_t cb = uniform64(static_cast<int64_t>(T.s) * a.rows_per_split);
-    const int64_t ce = uniform64(min(a.C, cb + a.rows_per_split));
-    const int nrows = static_cast<int>(ce - cb);     // > 0: splits never start past C
+    int64_t ce_ = min(a.C, cb + a.rows_per_split);
+    if constexpr (PG) {
+        const int64_t len = a.seq_lens[T.b];
+        ce_ = min(ce_, len < 0 ? int64_t{0} : min(len, a.C));
+    }
+    const int64_t ce = uniform64(ce_);
+    // > 0 for dense V (splits never start past C); paged V may give 0
+    const int nrows = ce > cb ? static_cast<int>(ce - cb) : 0;
     const int vrow = a.Hkv * D * VES;                // bytes between consecutive rows of V
 
     // Both operands are read through buffer resources that end with the
@@ -1074,11 +1084,24 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
     // pipeline's unconditional reload) touches no memory. The plan keeps a
     // split's V span under 2 GB so 32-bit offsets suffice.
     const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(a.V) + ((static_cast<size_t>(T.b) * a.C + cb) * a.Hkv + T.kv) * D * VES, 0,
-        (nrows - 1) * vrow + HT * D * VES, kRawBufferFlags);
+        const_cast<uint8_t*>(a.V) + (PG ? 0 : ((static_cast<size_t>(T.b) * a.C + cb) * a.Hkv + T.kv) * D * VES), 0,
+        PG || nrows == 0 ? 0 : (nrows - 1) * vrow + HT * D * VES, kRawBufferFlags);
     const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(a.attn) + (static_cast<size_t>(T.b) * a.C + cb) * a.Hq + T.q_first, 0,
-        ((nrows - 1) * a.Hq + (HT - 1) * a.G + T.nq) * 4, kRawBufferFlags);
+        nrows == 0 ? 0 : ((nrows - 1) * a.Hq + (HT - 1) * a.G + T.nq) * 4, kRawBufferFlags);
+    // PG: the split's pages, from the block table into LDS.
+    __shared__ int32_t s_pages[PG ? kMaxSplitPages : 1];
+    const int64_t pg0 = PG ? (cb >> a.page_shift) : 0;
+    if constexpr (PG) {
+        const int npg = nrows > 0 ? static_cast<int>(((cb + nrows - 1) >> a.page_shift) - pg0 + 1) : 0;
+        const int32_t* const btr = a.block_table + static_cast<size_t>(T.b) * a.max_pages + pg0;
+        for (int i = threadIdx.x; i < npg; i += kThreads) {
+            const int32_t pg = btr[i];
+            s_pages[i] = pg < 0 ? 0 : (pg >= a.num_pages ? static_cast<int32_t>(a.num_pages - 1) : pg);
+        }
+        __syncthreads();
+    }
+    const int64_t pmask = PG ? (int64_t{1} << a.page_shift) - 1 : 0;
     // This lane's pieces of a chunk: load i covers rows RPI i .. RPI i + RPI - 1.
     const int prow = lane / PR, ppiece = lane % PR;
     const int vlane = prow * vrow + kvl * D * VES + ppiece * PB;
@@ -1138,11 +1161,19 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
             const int r0 = 32 * (st * WPH * U + u * WPH + wh);
 #pragma unroll
             for (int i = 0; i < LPI; ++i) {
-                if constexpr (FP8)
+                if constexpr (PG) {
+                    // Rows past the split read its last row (their weight is 0).
+                    const int64_t c = cb + min(r0 + RPI * i + prow, nrows - 1);
+                    const int64_t page = s_pages[(c >> a.page_shift) - pg0];
+                    const uint8_t* const p = a.V + ((page << a.page_shift) + (c & pmask)) * vrow +
+                                             (T.kv + kvl) * D * VES + ppiece * PB;
+                    bf.v[u][i] = __builtin_nontemporal_load(reinterpret_cast<const Piece*>(p));
+                } else if constexpr (FP8) {
                     bf.v[u][i] = __builtin_amdgcn_raw_buffer_load_b64(vres, vlane, (r0 + RPI * i) * vrow, kCachePolicyNt);
-                else
+                } else {
                     bf.v[u][i] = __builtin_amdgcn_raw_buffer_load_b128(vres, vlane, (r0 + RPI * i) * vrow,
                                                                        kCachePolicyNt);
+                }
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j)
@@ -1269,11 +1300,17 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
     // consuming bB.
     Buf bA, bB;
     int st = 0;
+    // PG: keep each step's loads ahead of the other buffer's work (see av_pass1_valu).
+    auto fence = [] {
+        if constexpr (PG) __builtin_amdgcn_sched_barrier(0);
+    };
     if (nsteps > 0) load(bA, 0);
     for (; st + 1 < nsteps; st += 2) {
         load(bB, st + 1);
+        fence();
         consume(bA, st);
         load(bA, st + 2);
+        fence();
         consume(bB, st + 1);
     }
     if (st < nsteps) consume(bA, st);

@@ -162,13 +162,21 @@ hipError_t launch_pass1(int v_dtype, const gqa_av_plan& p, int64_t D, const Pass
                  : v_dtype == GQA_AV_F16 ? gqa_av::kF16
                  : v_dtype == GQA_AV_BF16 ? gqa_av::kBF16 : gqa_av::kFP8;
     if (p.engine == GQA_AV_ENGINE_MFMA_BF16) {
-        if ((v_dtype != GQA_AV_BF16 && v_dtype != GQA_AV_FP8_E4M3) || p.page_size > 0) return hipErrorInvalidValue;
+        if (v_dtype != GQA_AV_BF16 && v_dtype != GQA_AV_FP8_E4M3) return hipErrorInvalidValue;
         const int nset = p.heads_per_tile / 16, ht = p.kv_heads_per_tile;
+        using namespace gqa_av_launch;
+        if (p.page_size > 0) {
+            if (v_dtype == GQA_AV_FP8_E4M3)
+                return p.softmax ? mfma_bf16<gqa_av::kFP8, true, true>(D, nset, ht, a, s)
+                                 : mfma_bf16<gqa_av::kFP8, false, true>(D, nset, ht, a, s);
+            return p.softmax ? mfma_bf16<gqa_av::kBF16, true, true>(D, nset, ht, a, s)
+                             : mfma_bf16<gqa_av::kBF16, false, true>(D, nset, ht, a, s);
+        }
         if (v_dtype == GQA_AV_FP8_E4M3)
-            return p.softmax ? gqa_av_launch::mfma_bf16<gqa_av::kFP8, true>(D, nset, ht, a, s)
-                             : gqa_av_launch::mfma_bf16<gqa_av::kFP8, false>(D, nset, ht, a, s);
-        return p.softmax ? gqa_av_launch::mfma_bf16<gqa_av::kBF16, true>(D, nset, ht, a, s)
-                         : gqa_av_launch::mfma_bf16<gqa_av::kBF16, false>(D, nset, ht, a, s);
+            return p.softmax ? mfma_bf16<gqa_av::kFP8, true>(D, nset, ht, a, s)
+                             : mfma_bf16<gqa_av::kFP8, false>(D, nset, ht, a, s);
+        return p.softmax ? mfma_bf16<gqa_av::kBF16, true>(D, nset, ht, a, s)
+                         : mfma_bf16<gqa_av::kBF16, false>(D, nset, ht, a, s);
     }
     if (p.engine == GQA_AV_ENGINE_MFMA) {
         if (p.softmax || p.page_size > 0 || v_dtype == GQA_AV_FP8_E4M3) return hipErrorInvalidValue;
@@ -261,16 +269,15 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
         return fail(GQA_AV_ERR_INVALID_ARG, "unknown combine %d", h.combine);
     if (h.softmax != 0 && h.softmax != 1) return fail(GQA_AV_ERR_INVALID_ARG, "hint softmax must be 0 or 1");
     const bool sm = h.softmax == 1;
-    // Paged V: the VALU engine with 16-byte lane loads, the kernel combine,
-    // and splits short enough for their page list to fit in LDS.
+    // Paged V: the VALU engine with 16-byte lane loads or the bf16 matrix
+    // engine, the kernel combine, and splits short enough for their page list
+    // to fit in LDS.
     const int64_t P = h.page_size;
     const bool paged = P > 0;
     if (P < 0 || (paged && (P & (P - 1)) != 0))
         return fail(GQA_AV_ERR_INVALID_ARG, "page_size %lld must be a power of two", (long long)P);
-    if (paged && (h.engine == GQA_AV_ENGINE_MFMA || h.engine == GQA_AV_ENGINE_MFMA_BF16))
-        return fail(GQA_AV_ERR_UNSUPPORTED, "paged V runs on the VALU engine");
-    if (paged && GQA_AV_VALU_STAGE_WEIGHTS)
-        return fail(GQA_AV_ERR_UNSUPPORTED, "paged V needs the per-lane weight VALU build");
+    if (paged && h.engine == GQA_AV_ENGINE_MFMA)
+        return fail(GQA_AV_ERR_UNSUPPORTED, "paged V runs on the VALU or bf16 matrix engine");
     const int cus = h.cu_count > 0 ? h.cu_count : cu_default;
     const int v_align = h.v_align > 0 ? h.v_align : 16;
 
@@ -287,12 +294,14 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
     const int nset16 = (G > 16 && mfma_bf16_fits(v_dtype, Hq, Hkv, D, v_align, 2)) ? 2 : 1;
     const bool mfma16_ok = resolved == GQA_AV_REUSE && mfma_bf16_fits(v_dtype, Hq, Hkv, D, v_align, nset16);
     int engine = h.engine;
-    if (engine == GQA_AV_ENGINE_AUTO && paged) engine = GQA_AV_ENGINE_VALU;
     if (engine == GQA_AV_ENGINE_AUTO) {
         engine = GQA_AV_ENGINE_VALU;
         if (G >= kMfmaMinGroup && mfma16_ok) engine = GQA_AV_ENGINE_MFMA_BF16;
-        else if (G >= kMfmaMinGroup && mfma_ok && !sm && v_dtype != GQA_AV_FP8_E4M3) engine = GQA_AV_ENGINE_MFMA;
+        else if (G >= kMfmaMinGroup && mfma_ok && !sm && !paged && v_dtype != GQA_AV_FP8_E4M3)
+            engine = GQA_AV_ENGINE_MFMA;
     }
+    if (paged && engine == GQA_AV_ENGINE_VALU && GQA_AV_VALU_STAGE_WEIGHTS)
+        return fail(GQA_AV_ERR_UNSUPPORTED, "paged V needs the per-lane weight VALU build");
     if (sm && engine == GQA_AV_ENGINE_MFMA)
         return fail(GQA_AV_ERR_UNSUPPORTED, "the fused softmax runs on the VALU or bf16 matrix engine");
     if (v_dtype == GQA_AV_FP8_E4M3 && engine == GQA_AV_ENGINE_MFMA)

@@ -28,9 +28,11 @@
  * [0, num_pages), so bad tables give wrong results, never a fault.
  *
  * Plans come from gqa_av_make_plan with hint->page_size = page_size (and
- * hint->softmax for the fused form); they carry plan->page_size and run on
- * the VALU engine with the kernel combine. Modes, workspace, asynchrony,
- * errors and threading are as in gqa_av.h.
+ * hint->softmax for the fused form); they carry plan->page_size and run with
+ * the kernel combine on the VALU engine or, in reuse mode for bf16 or fp8 V
+ * with D of 64, 128 or 256, the bf16 matrix engine (automatic for G >= 5, as
+ * for dense V); never on the fp32 matrix engine. Modes, workspace,
+ * asynchrony, errors and threading are as in gqa_av.h.
  */
 #ifndef GQA_PAGED_AV_H
 #define GQA_PAGED_AV_H

@@ -44,13 +44,17 @@ def _gpu_ready():
 
 def _paged_from_dense(V: torch.Tensor, P: int, seed: int, spare: int = 5):
     """Scatter a dense V [B, C, Hkv, D] into a shuffled pool of P-row pages with
-    spare pages (filled with large values that must never be read) and return
-    (pages, block_table). Rows past C in a sequence's last page are padding."""
+    spare pages (filled with large values that must never be read: 3e4, or
+    the E4M3 byte of 448 for uint8 V) and return (pages, block_table). Rows
+    past C in a sequence's last page are padding."""
     B, C, Hkv, D = V.shape
     maxp = -(-C // P)
     g = torch.Generator().manual_seed(seed)
     npg = B * maxp + spare
-    pages = torch.full((npg, P, Hkv, D), 3.0e4).to(V.dtype)
+    if V.dtype == torch.uint8:
+        pages = torch.full((npg, P, Hkv, D), 0x7E, dtype=torch.uint8)
+    else:
+        pages = torch.full((npg, P, Hkv, D), 3.0e4).to(V.dtype)
     perm = torch.randperm(npg, generator=g)[:B * maxp].to(torch.int32).view(B, maxp).contiguous()
     for b in range(B):
         for k in range(maxp):
@@ -123,12 +127,17 @@ def test_paged_sweep(B, C, Hq, Hkv, D, P, dt, oracle_lib):
     modes = ("auto", "per_head") if Hq // Hkv >= 2 else ("auto",)
     for softmax, w in ((False, attn), (True, s)):
         ref = oracle_lib.paged(w, pages, bt, lens, dt, softmax=softmax)
-        for mode in modes:
-            for ns in (0, 1, 7):
-                plan = ga.make_plan(B, C, Hq, Hkv, D, dt, mode, nsplit=ns, softmax=softmax, page_size=P)
-                out = _run(w, pages, bt, lens, softmax, plan=plan)
-                _bound_ok(out, ref, w, V, lens, dt, softmax, f"paged {(B, C, Hq, Hkv, D, P, dt)} {plan.as_dict()}")
-                assert (out[lens.numpy() == 0] == 0).all(), "a sequence of length 0 gives zeros"
+        plans = [ga.make_plan(B, C, Hq, Hkv, D, dt, mode, nsplit=ns, softmax=softmax, page_size=P)
+                 for mode in modes for ns in (0, 1, 7)]
+        if dt == "bf16" and Hq // Hkv >= 2:          # the bf16 matrix engine at any G
+            for ht, ns in ((1, 0), (2, 5), (4, 1)):
+                if Hkv % ht == 0 and (ns != 1 or C <= 1023 * P):
+                    plans.append(ga.make_plan(B, C, Hq, Hkv, D, dt, "reuse", engine="mfma_bf16", kv_tile=ht,
+                                              nsplit=ns, softmax=softmax, page_size=P))
+        for plan in plans:
+            out = _run(w, pages, bt, lens, softmax, plan=plan)
+            _bound_ok(out, ref, w, V, lens, dt, softmax, f"paged {(B, C, Hq, Hkv, D, P, dt)} {plan.as_dict()}")
+            assert (out[lens.numpy() == 0] == 0).all(), "a sequence of length 0 gives zeros"
 
 
 @pytest.mark.parametrize("wname,P", [("g2-b4-c32768-hq16-hkv8-d128-bf16", 16),
@@ -154,23 +163,55 @@ def test_paged_workloads(wname, P, oracle_lib):
         _bound_ok(out, ref, x, V, lens, w.v_dtype, softmax, f"paged {w.name} softmax={softmax}")
 
 
-@pytest.mark.parametrize("dt", ["bf16", "f32"])
-def test_paged_dense_layout_matches_dense_call(dt):
+@pytest.mark.parametrize("dt,engine", [("bf16", "valu"), ("f32", "valu"), ("bf16", "mfma_bf16"),
+                                       ("fp8", "mfma_bf16")])
+def test_paged_dense_layout_matches_dense_call(dt, engine):
     """One page per sequence (P = C, block_table[b] = b, full lengths) is the
-    dense layout: the paged call equals the dense call on the VALU engine with
-    the same splits and tiles bit for bit (same arithmetic, same order)."""
-    B, C, Hq, Hkv, D = 3, 512, 16, 4, 128
-    s, V = make_scores_random(B, C, Hq, Hkv, D, dt, seed=91)
+    dense layout: the paged call equals the dense call on the same engine with
+    the same splits and tiles bit for bit (same arithmetic, same order; rows
+    past a split weigh 0 on both sides). C = 500 leaves a partial last step."""
+    B, C, Hq, Hkv, D = 3, 500, 32, 4, 128
+    s, V = make_scores_random(B, C, Hq, Hkv, D, "f32" if dt == "fp8" else dt, seed=91)
+    if dt == "fp8":
+        V = (V / V.abs().max() * 400.0).to(torch.float8_e4m3fn).contiguous()
     attn = torch.softmax(s.double(), dim=1).float().contiguous()
+    P = 512                                          # a power of two >= C
     bt = torch.arange(B, dtype=torch.int32).view(B, 1)
     lens = torch.full((B,), C, dtype=torch.int32)
+    pages = torch.zeros((B, P, Hkv, D), dtype=V.dtype)
+    pages[:, :C] = V
     for softmax, x in ((False, attn), (True, s)):
-        pp = ga.make_plan(B, C, Hq, Hkv, D, dt, "reuse", page_size=C, softmax=softmax, nsplit=4, kv_tile=2)
-        dp = ga.make_plan(B, C, Hq, Hkv, D, dt, "reuse", engine="valu", softmax=softmax, nsplit=4, kv_tile=2)
-        a = _run(x, V, bt, lens, softmax, plan=pp)
+        pp = ga.make_plan(B, C, Hq, Hkv, D, dt, "reuse", engine=engine, page_size=P, softmax=softmax, nsplit=4,
+                          kv_tile=2)
+        dp = ga.make_plan(B, C, Hq, Hkv, D, dt, "reuse", engine=engine, softmax=softmax, nsplit=4, kv_tile=2)
+        assert pp.engine == dp.engine and pp.rows_per_split == dp.rows_per_split
+        a = _run(x, pages, bt, lens, softmax, plan=pp)
         fn = ga.gqa_softmax_av_decode if softmax else ga.gqa_av_decode
         b = fn(x.to(DEV), V.to(DEV), plan=dp).cpu().numpy().astype(np.float64)
-        assert np.array_equal(a, b), f"paged dense layout != dense call ({dt}, softmax={softmax})"
+        assert np.array_equal(a, b), f"paged dense layout != dense call ({dt}, {engine}, softmax={softmax})"
+
+
+@pytest.mark.parametrize("P", [1, 16, 128])
+def test_paged_fp8_matches_fp8_oracle(P, oracle_lib):
+    """fp8 pages (unit scale) at G = 8 on the bf16 matrix engine: the gathered
+    rows of each sequence against the fp8 oracle, with the weights (plain) or
+    scores (fused, -inf) of rows past its length removed on the oracle's side."""
+    B, C, Hq, Hkv, D = 3, 700, 32, 4, 128
+    s, Vf = make_scores_random(B, C, Hq, Hkv, D, "f32", seed=95 + P)
+    V = (Vf / Vf.abs().max() * 400.0).to(torch.float8_e4m3fn).contiguous()
+    pages, bt = _paged_from_dense(V.view(torch.uint8), P, seed=P)
+    pages = pages.view(torch.float8_e4m3fn)
+    lens = torch.tensor([C, 333, 1], dtype=torch.int32)
+    keep = torch.arange(C).view(1, C, 1) < lens.view(B, 1, 1)
+    attn = torch.softmax(s.double(), dim=1).float().contiguous()
+    for softmax, x in ((False, attn), (True, s)):
+        xo = torch.where(keep, x, torch.tensor(float("-inf") if softmax else 0.0)).contiguous()
+        ref = oracle_lib.fp8(xo, V, None, softmax=softmax)
+        for ns in (0, 3):
+            plan = ga.make_plan(B, C, Hq, Hkv, D, "fp8", "reuse", nsplit=ns, softmax=softmax, page_size=P)
+            assert plan.engine == 3
+            out = _run(x, pages, bt, lens, softmax, plan=plan)
+            _bound_ok(out, ref, x, V.float(), lens, "fp8", softmax, f"paged fp8 P={P} softmax={softmax} ns={ns}")
 
 
 def test_paged_deterministic_and_side_stream():

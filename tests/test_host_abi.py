@@ -447,8 +447,10 @@ def test_softmax_and_plain_plans_do_not_mix():
 
 @pytest.mark.parametrize("wname", list(WORKLOADS))
 def test_paged_plans(wname):
-    """Paged plans: the VALU engine with 16-byte loads, the kernel combine, and
-    splits whose page lists fit the kernel's LDS list (1024 pages)."""
+    """Paged plans: the VALU engine with 16-byte loads, or the bf16 matrix
+    engine for bf16 V in reuse mode at G >= 5 with D of 64, 128 or 256 (as for
+    dense V), the kernel combine, and splits whose page lists fit the kernels'
+    LDS list (1024 pages)."""
     w = WORKLOADS[wname]
     for P in (1, 16, 256):
         for sm in (False, True):
@@ -458,14 +460,17 @@ def test_paged_plans(wname):
                 except ga.GqaAvError as e:
                     assert e.name == "UNSUPPORTED" and (w.D * (4 if w.v_dtype == "f32" else 2)) % 16
                     continue
-                assert p.page_size == P and p.engine == 1 and p.vec_bytes == 16 and p.softmax == int(sm)
+                bf16_engine = (w.v_dtype == "bf16" and w.D in (64, 128, 256) and w.Hq // w.Hkv >= 5
+                               and mode == "auto")
+                assert p.engine == (3 if bf16_engine else 1) and p.vec_bytes == 16, (wname, P, sm, mode)
+                assert p.page_size == P and p.softmax == int(sm)
                 assert -(-p.rows_per_split // P) + 1 <= 1024
                 assert p.nsplit == 1 or p.combine == 1
 
 
 def test_paged_refusals():
-    for kw, name in ((dict(page_size=12), "INVALID_ARG"), (dict(page_size=16, engine="mfma_bf16"), "UNSUPPORTED"),
-                     (dict(page_size=16, engine="mfma"), "UNSUPPORTED"),
+    for kw, name in ((dict(page_size=12), "INVALID_ARG"), (dict(page_size=16, engine="mfma"), "UNSUPPORTED"),
+                     (dict(page_size=16, engine="mfma_bf16", mode="per_head"), "UNSUPPORTED"),
                      (dict(page_size=16, nsplit=4, combine="last"), "UNSUPPORTED"),
                      (dict(page_size=1, nsplit=1), "UNSUPPORTED")):          # 4000 rows on 1-row pages: 4000 pages
         with pytest.raises(ga.GqaAvError) as e:
@@ -516,10 +521,12 @@ def test_fp8_plans():
     assert ga.make_plan(1, 100, 8, 2, 6, "fp8").vec_bytes == 2
     assert ga.make_plan(1, 100, 8, 2, 6, "fp8", v_align=2).vec_bytes == 2
     assert ga.make_plan(2, 1000, 16, 2, 128, "fp8", "reuse", engine="mfma_bf16").engine == 3
-    for kw in (dict(engine="mfma"), dict(page_size=16)):
+    for kw in (dict(engine="mfma"), dict(page_size=16, engine="valu")):     # paged VALU: 16-byte loads only
         with pytest.raises(ga.GqaAvError) as e:
             ga.make_plan(2, 1000, 16, 2, 128, "fp8", "reuse", **kw)
         assert e.value.name == "UNSUPPORTED", kw
+    pf = ga.make_plan(2, 1000, 16, 2, 128, "fp8", "reuse", page_size=16)   # paged fp8 at G = 8: bf16 matrix engine
+    assert pf.engine == 3 and pf.vec_bytes == 8 and pf.page_size == 16
     with pytest.raises(ga.GqaAvError) as e:
         ga.make_plan(2, 1000, 16, 2, 127, "fp8")            # odd D: no 2-byte lane load fits
     assert e.value.name == "UNSUPPORTED"

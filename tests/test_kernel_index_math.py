@@ -94,6 +94,26 @@ def _check_plan(p, B, C, Hq, Hkv, D, es=2):
         ce = min(C, cb + p.rows_per_split)
         nrows = ce - cb
         assert nrows > 0
+        if p.page_size:
+            # paged V: the split's page list and every loaded row's entry in
+            # it, including the pipeline's reloads past the split (clamped to
+            # its last valid row), for full and shorter sequences
+            P = p.page_size
+            shift = P.bit_length() - 1
+            for ln in {C, C // 2, cb + 1, cb}:
+                nr = max(0, min(ce, ln) - cb)
+                if nr == 0:
+                    continue
+                pg0 = cb >> shift
+                npg = ((cb + nr - 1) >> shift) - pg0 + 1
+                assert npg <= 1024 and (cb + nr - 1) // P < -(-C // P)
+                ns_ = -(-nr // RSTEP)
+                for step in range(ns_ + (1 if ns_ > 1 else 0)):
+                    for wave in range(4):
+                        r0 = 32 * (step * WPH + wave % WPH)
+                        rows = np.minimum(r0 + RPI * np.arange(LPI)[:, None] + lanes[None, :] // PR, nr - 1)
+                        idx = ((cb + rows) >> shift) - pg0
+                        assert idx.min() >= 0 and idx.max() < npg
         vrec = (nrows - 1) * vrow + HT * D * es
         assert ((b * C + cb) * Hkv + kv) * D * es + vrec <= B * C * Hkv * D * es and vrec < 2 ** 31
         wrec = ((nrows - 1) * Hq + (HT - 1) * G + nq) * 4
@@ -154,12 +174,17 @@ def test_bf16_engine_plan_bounds(B, C, Hq, Hkv, D):
                 if ht > 1 and Hkv % ht:
                     continue
                 for dt, es in (("bf16", 2), ("fp8", 1)):
-                    if dt == "fp8" and comb == "last":
-                        continue
-                    p = ga.make_plan(B, C, Hq, Hkv, D, dt, "reuse", engine="mfma_bf16", nsplit=ns,
-                                     combine=comb, kv_tile=ht, softmax=sm)
-                    assert p.softmax == int(sm)
-                    _check_plan(p, B, C, Hq, Hkv, D, es)
+                    for P in (0,) + ((16,) if ht in (0, 2) else ()) + ((1, 256) if ns in (0, 3) and ht == 0 else ()):
+                        if (dt == "fp8" or P) and comb == "last":
+                            continue
+                        try:
+                            p = ga.make_plan(B, C, Hq, Hkv, D, dt, "reuse", engine="mfma_bf16", nsplit=ns,
+                                             combine=comb, kv_tile=ht, softmax=sm, page_size=P)
+                        except ga.GqaAvError as e:     # a forced split over more than 1024 pages
+                            assert e.name == "UNSUPPORTED" and P and ns and -(-C // ns) > 1023 * P
+                            continue
+                        assert p.softmax == int(sm) and p.page_size == P
+                        _check_plan(p, B, C, Hq, Hkv, D, es)
 
 
 ENGINE_VALU = 1

@@ -88,6 +88,9 @@ def parse():
     p.add_argument("--page-size", type=int, default=0,
                    help="av / softmax over a paged V cache with this many rows per page (shuffled pages, full "
                         "lengths); 0 = dense V")
+    p.add_argument("--graph", action="store_true",
+                   help="dense av / softmax: time the K whole calls as one captured HIP graph (no host launch "
+                        "cost between calls) instead of K stream launches")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle time budget")
     p.add_argument("--rotate-mb", type=float, default=ROTATE_BYTES / 2 ** 20)
@@ -506,13 +509,29 @@ def main():
         v = v0 if i == 0 else v0.clone()
         sets.append((a, v, torch.empty(w.B, w.Hq, w.D, device=dev)))
     torch.cuda.synchronize()
-    calls = [(ga.bind_softmax if softmax else ga.bind)(a, v, o, plan=plan) for a, v, o in sets]
-    stream = torch.cuda.current_stream(dev)
+    # --graph: the calls are bound to a side stream, which graph capture needs.
+    stream = torch.cuda.Stream(dev) if args.graph else torch.cuda.current_stream(dev)
+    calls = [(ga.bind_softmax if softmax else ga.bind)(a, v, o, plan=plan, stream=stream) for a, v, o in sets]
 
     _warm(args, calls, nrot)
 
     # Whole calls: the metric.
-    ms = _timed(calls, nrot, args.steps, stream)
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(args.steps):
+                calls[i % nrot]()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            graph.replay()                           # warm replay
+            g0.record(stream)
+            graph.replay()
+            g1.record(stream)
+        torch.cuda.synchronize()
+        ms = g0.elapsed_time(g1) / args.steps
+    else:
+        ms = _timed(calls, nrot, args.steps, stream)
     gbs = w.algorithmic_bytes() / (ms / 1e3) / 1e9
 
     # The dominant kernel alone: K back-to-back pass-1 launches over the same
@@ -557,6 +576,7 @@ def main():
             "G": w.G, "D": w.D,
             "v_dtype": w.v_dtype, "mode": args.mode, "algorithmic_bytes": w.algorithmic_bytes(),
             "rotation_sets": nrot, "kernels_per_call": 2 if split_kernel else 1, "plan": plan.as_dict(),
+            "launch": "one HIP graph of K calls" if args.graph else "K stream launches",
         },
         "roofline": {
             "bound": "hbm",

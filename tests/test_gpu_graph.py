@@ -1,0 +1,127 @@
+"""HIP graph capture of the bound calls (torch.cuda.CUDAGraph on a side
+stream): every entry point enqueues only kernel launches once its split
+workspace exists, so a decode loop can capture it. Each graph is replayed
+several times with new inputs written in place by eager work between the
+replays, and every replay must equal an eager call on the same inputs bit for
+bit (same plan, same kernels, fixed summation order). All tests need an
+MI355X and are marked ``gpu``.
+"""
+from __future__ import annotations
+
+import sys
+
+import pytest
+import torch
+
+import gqa_reuse_attn_amd as ga
+from workloads import make_qk_random, make_scores_random
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+REPLAYS = 4
+
+
+def _say(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ga.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _graph_matches_eager(label, bind, x, fresh):
+    """bind(stream) -> a bound call reading x; fresh(k) -> new contents of x."""
+    _say(f"[graph] {label}")
+    s = torch.cuda.Stream()
+    call = bind(s)
+    call()                                           # eager: allocates the stream's split workspace
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    torch.cuda.synchronize()
+    prev = None
+    for k in range(REPLAYS):
+        x.copy_(fresh(k))                            # eager work on the default stream
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = _out(call).clone()
+        call()                                       # the eager call on the same inputs
+        s.synchronize()
+        assert torch.equal(got, _out(call)), f"{label}: replay {k} differs from the eager call"
+        assert torch.isfinite(got).all(), f"{label}: replay {k} not finite"
+        if prev is not None:
+            assert not torch.equal(got, prev), f"{label}: replay {k} did not see the new inputs"
+        prev = got
+    del g
+
+
+def _out(call):
+    return call.scores if isinstance(call, ga.BoundQk) else call.out
+
+
+def _weights(B, C, Hq, Hkv, D, dt, seed, softmax):
+    s, V = make_scores_random(B, C, Hq, Hkv, D, dt, seed=seed, score_std=2.0)
+    x = s if softmax else torch.softmax(s.double(), dim=1).float()
+    return x.contiguous().to(DEV), V.to(DEV)
+
+
+def _fresh(x, seed):
+    g = torch.Generator().manual_seed(seed)
+
+    def f(k):
+        return (x.cpu() * (1.0 + 0.25 * torch.rand(x.shape, generator=g))).to(DEV)
+    return f
+
+
+@pytest.mark.parametrize("softmax", [False, True])
+@pytest.mark.parametrize("shape,engine,combine", [
+    ((2, 3000, 16, 8, 128, "bf16"), "auto", "auto"),     # VALU, split kernel combine
+    ((2, 3000, 64, 8, 128, "bf16"), "auto", "auto"),     # bf16 matrix engine
+    ((2, 3000, 32, 4, 64, "f32"), "mfma", "auto"),       # fp32 matrix engine (plain only)
+    ((2, 3000, 16, 8, 128, "f16"), "valu", "last"),      # last-workgroup combine (plain only)
+    ((1, 100, 8, 2, 64, "bf16"), "auto", "auto"),        # one split: a single launch
+])
+def test_graph_dense(shape, engine, combine, softmax):
+    if softmax and (engine == "mfma" or combine == "last"):
+        pytest.skip("the fused softmax runs on the VALU or bf16 matrix engine with the kernel combine")
+    B, C, Hq, Hkv, D, dt = shape
+    x, V = _weights(B, C, Hq, Hkv, D, dt, seed=C + Hq, softmax=softmax)
+    plan = ga.make_plan(B, C, Hq, Hkv, D, dt, engine=engine, combine=combine, softmax=softmax)
+    bind = ga.bind_softmax if softmax else ga.bind
+    _graph_matches_eager(f"dense {shape} {plan.as_dict()}", lambda s: bind(x, V, plan=plan, stream=s), x,
+                         _fresh(x, 1))
+
+
+@pytest.mark.parametrize("softmax", [False, True])
+def test_graph_paged_and_fp8(softmax):
+    B, C, Hq, Hkv, D, P = 3, 2048, 64, 8, 128, 16
+    x, V = _weights(B, C, Hq, Hkv, D, "bf16", seed=5, softmax=softmax)
+    maxp = C // P
+    perm = torch.randperm(B * maxp, generator=torch.Generator().manual_seed(2)).to(torch.int32)
+    pages = torch.empty((B * maxp, P, Hkv, D), dtype=V.dtype, device=DEV)
+    pages[perm.long().to(DEV)] = V.reshape(B * maxp, P, Hkv, D)
+    bt = perm.view(B, maxp).contiguous().to(DEV)
+    lens = torch.tensor([C, 1500, 7], dtype=torch.int32, device=DEV)
+    _graph_matches_eager(f"paged softmax={softmax}",
+                         lambda s: ga.bind_paged(x, pages, bt, lens, softmax=softmax, stream=s), x, _fresh(x, 2))
+    V8 = (V.float() / V.float().abs().max() * 400.0).to(torch.float8_e4m3fn).contiguous()
+    scale = torch.full((Hkv,), 0.5, device=DEV)
+    _graph_matches_eager(f"fp8 softmax={softmax}",
+                         lambda s: ga.bind_fp8(x, V8, scale, softmax=softmax, stream=s), x, _fresh(x, 3))
+
+
+@pytest.mark.parametrize("shape", [(2, 3000, 16, 8, 128, "bf16"), (2, 777, 64, 8, 128, "bf16")])
+def test_graph_qk(shape):
+    B, C, Hq, Hkv, D, dt = shape
+    q, K = make_qk_random(B, C, Hq, Hkv, D, dt, seed=4)
+    q, K = q.to(DEV), K.to(DEV)
+    _graph_matches_eager(f"qk {shape}", lambda s: ga.bind_qk(q, K, scale=D ** -0.5, stream=s), q, _fresh(q, 4))

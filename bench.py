@@ -289,8 +289,8 @@ def bench_fp8(args, w, dev, props):
     q_h = (Vf / scale_h.view(1, 1, -1, 1)).to(torch.float8_e4m3fn).contiguous()
     del Vf
     alg = w.B * w.C * w.Hkv * w.D + w.attn_bytes() + w.out_bytes()
-    plan = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, "fp8", args.mode, nsplit=args.nsplit,
-                        cu_count=props.multi_processor_count, softmax=softmax)
+    plan = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, "fp8", args.mode, engine=args.engine, nsplit=args.nsplit,
+                        cu_count=props.multi_processor_count, kv_tile=args.kv_tile, softmax=softmax)
     nrot = max(1, math.ceil(args.rotate_mb * 2 ** 20 / alg))
     x0, q0, sc = x_h.to(dev), q_h.to(dev), scale_h.to(dev)
     calls = []

@@ -324,17 +324,22 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
     // faster than one for VALU; a plain streaming read of 2 KB rows in
     // 512-byte slices runs at 7.1 TB/s against 6.8 TB/s in 256-byte slices;
     // the bf16 matrix engine on B = 64, C = 8192, Hkv = 8, G = 8 takes 193 us
-    // with one head per tile, 181 with two and 177 with four.
+    // with one head per tile, 181 with two and 177 with four. fp8 V differs:
+    // there two heads without a split take 112 us against 117.7 with four
+    // heads and two splits, and the VALU engine also takes four heads while a
+    // tile row stays within 512 bytes (G = 3, D = 96: 26.6 us against 28.1).
     int ht = h.kv_tile > 0 ? h.kv_tile : 1;
     const bool bf16_engine = engine == GQA_AV_ENGINE_MFMA_BF16;
     if (h.kv_tile <= 0 && resolved == GQA_AV_REUSE &&
         ((engine == GQA_AV_ENGINE_VALU && !GQA_AV_VALU_STAGE_WEIGHTS) || bf16_engine)) {
+        const bool fp8 = v_dtype == GQA_AV_FP8_E4M3;
         const int64_t lanes = (D * es) / 16 > 0 && (D * es) % 16 == 0 ? (D * es) / 16 : 0;
         const int64_t nsgw = ceil_div(G, bf16_engine ? 16 * nset16 : head_capacity(G));
         const int64_t target = (bf16_engine ? kTargetWgPerCuBf16 : kTargetWgPerCuValu) * cus;
         const int64_t min_rows = bf16_engine ? kMinRowsPerSplitBf16 : kMinRowsPerSplit;
         for (int cand : {4, 2}) {
-            if ((cand == 4 && !bf16_engine) || Hkv % cand != 0) continue;
+            const bool four = bf16_engine ? !fp8 : (fp8 && 4 * D * es <= 512);
+            if ((cand == 4 && !four) || Hkv % cand != 0) continue;
             const int64_t tiles_w = B * (Hkv / cand) * nsgw;
             if (lanes > 0 && (bf16_engine || cand * lanes <= gqa_av::kThreads) && v_align % 16 == 0 &&
                 tiles_w > 0 &&

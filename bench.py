@@ -162,11 +162,12 @@ def summarize_pmc(dirs, copy_mib: float, out: str, command: str, op: str = "av")
     print("\n".join(lines))
 
 
-def recorded_traffic(workload: str, mode: str, op: str = "av"):
-    """The dominant kernel's HBM bytes per launch from the committed PMC summary,
-    if it was taken on the current kernel sources (else None)."""
+def recorded_traffic(workload: str, mode: str, op: str = "av", variant: str = ""):
+    """The dominant kernel's HBM bytes per launch from the committed PMC summary
+    (variant: "" for dense V, "_fp8" or "_paged<P>"), if it was taken on the
+    current kernel sources (else None)."""
     prefix = OPS[op][0]
-    f = os.path.join(PROFILES, f"{prefix}_{workload}_{mode}_traffic.md")
+    f = os.path.join(PROFILES, f"{prefix}{variant}_{workload}_{mode}_traffic.md")
     if not os.path.exists(f):
         return None
     kv = {}
@@ -269,6 +270,28 @@ def _timed(calls, nrot, steps, stream):
     return start.elapsed_time(end) / steps
 
 
+def _timed_pass1(calls, nrot, steps, stream):
+    """ms per pass-1 launch over `steps` back-to-back pass-1 launches on the
+    rotating inputs, HIP events on the launch stream. (Events around each
+    single launch would add its dispatch latency, about 3 us.)"""
+    import torch
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0.record(stream)
+    for i in range(steps):
+        calls[i % nrot].pass1()
+    p1.record(stream)
+    torch.cuda.synchronize()
+    return p0.elapsed_time(p1) / steps
+
+
+def _pass1_roofline(alg: int, p1_ms: float, traffic):
+    gbs = alg / (p1_ms / 1e3) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": "pass 1 (V streaming)",
+            "us_per_launch": round(p1_ms * 1e3, 3),
+            "timing": "HIP events around K back-to-back pass-1 launches on the launch stream"}
+
+
 QK_METRIC = "GQA decode QK scores: µs/call and achieved HBM GB/s (% of MI355X peak)"
 FP8_METRIC = "GQA decode AV with fp8 V: µs/call and achieved HBM GB/s (% of MI355X peak)"
 
@@ -302,9 +325,11 @@ def bench_fp8(args, w, dev, props):
     _warm(args, calls, nrot)
     ms = _timed(calls, nrot, args.steps, stream)
     gbs = alg / (ms / 1e3) / 1e9
+    p1_ms = _timed_pass1(calls, nrot, args.steps, stream)
     print(f"[bench] fp8 {'softmax ' if softmax else ''}{ms * 1e3:.2f} us/call, {gbs:.1f} GB/s "
-          f"({100 * gbs / HBM_PEAK_GBS:.1f}% of peak); {nrot} rotation sets, plan {plan.as_dict()}",
-          file=sys.stderr, flush=True)
+          f"({100 * gbs / HBM_PEAK_GBS:.1f}% of peak); pass 1 {p1_ms * 1e3:.2f} us; {nrot} rotation sets, "
+          f"plan {plan.as_dict()}", file=sys.stderr, flush=True)
+    default_plan = args.nsplit == 0 and args.engine == "auto" and args.kv_tile == 0
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -318,10 +343,8 @@ def bench_fp8(args, w, dev, props):
         "config": {"workload": f"fp8{'-softmax' if softmax else ''}:{w.name}", "B": w.B, "C": w.C, "Hq": w.Hq,
                    "Hkv": w.Hkv, "G": w.G, "D": w.D, "v_dtype": "fp8_e4m3", "mode": args.mode,
                    "algorithmic_bytes": alg, "rotation_sets": nrot, "plan": plan.as_dict()},
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "whole call (pass 1 + combine)",
-                     "us_per_launch": round(ms * 1e3, 3),
-                     "timing": "HIP events around K back-to-back calls on the launch stream"},
+        "roofline": _pass1_roofline(alg, p1_ms, recorded_traffic(w.name, args.mode, args.op, "_fp8")
+                                    if default_plan else None),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -368,9 +391,11 @@ def bench_paged(args, w, dev, props):
     _warm(args, calls, nrot)
     ms = _timed(calls, nrot, args.steps, stream)
     gbs = w.algorithmic_bytes() / (ms / 1e3) / 1e9
+    p1_ms = _timed_pass1(calls, nrot, args.steps, stream)
     print(f"[bench] paged P={P} {'softmax ' if softmax else ''}{ms * 1e3:.2f} us/call, {gbs:.1f} GB/s "
-          f"({100 * gbs / HBM_PEAK_GBS:.1f}% of peak); {nrot} rotation sets, plan {plan.as_dict()}",
-          file=sys.stderr, flush=True)
+          f"({100 * gbs / HBM_PEAK_GBS:.1f}% of peak); pass 1 {p1_ms * 1e3:.2f} us; {nrot} rotation sets, "
+          f"plan {plan.as_dict()}", file=sys.stderr, flush=True)
+    default_plan = args.nsplit == 0 and args.engine == "auto" and args.kv_tile == 0
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -385,10 +410,8 @@ def bench_paged(args, w, dev, props):
         "config": {"workload": f"paged{P}{'-softmax' if softmax else ''}:{w.name}", "B": w.B, "C": w.C, "Hq": w.Hq,
                    "Hkv": w.Hkv, "G": w.G, "D": w.D, "v_dtype": w.v_dtype, "mode": args.mode, "page_size": P,
                    "algorithmic_bytes": w.algorithmic_bytes(), "rotation_sets": nrot, "plan": plan.as_dict()},
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "whole call (pass 1 + combine)",
-                     "us_per_launch": round(ms * 1e3, 3),
-                     "timing": "HIP events around K back-to-back calls on the launch stream"},
+        "roofline": _pass1_roofline(w.algorithmic_bytes(), p1_ms,
+                                    recorded_traffic(w.name, args.mode, args.op, f"_paged{P}") if default_plan else None),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -535,15 +558,8 @@ def main():
     gbs = w.algorithmic_bytes() / (ms / 1e3) / 1e9
 
     # The dominant kernel alone: K back-to-back pass-1 launches over the same
-    # rotating inputs, bracketed by events on the launch stream. (Events around
-    # each single launch would add its dispatch latency, about 3 us.)
-    p0, p1e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    p0.record(stream)
-    for i in range(args.steps):
-        calls[i % nrot].pass1()
-    p1e.record(stream)
-    torch.cuda.synchronize()
-    p1_ms = p0.elapsed_time(p1e) / args.steps
+    # rotating inputs, bracketed by events on the launch stream.
+    p1_ms = _timed_pass1(calls, nrot, args.steps, stream)
     p1_gbs = w.algorithmic_bytes() / (p1_ms / 1e3) / 1e9
     print(f"[bench] {ms * 1e3:.2f} us/call, {gbs:.1f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of peak); "
           f"pass 1 {p1_ms * 1e3:.2f} us = {p1_gbs:.1f} GB/s; {nrot} rotation sets, plan {plan.as_dict()}",

@@ -116,13 +116,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         getattr(lib, fn).restype = ip
     lib.gqa_av_paged_decode.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, ip, ip, ip, vp]
     lib.gqa_av_paged_decode.restype = ip
-    lib.gqa_av_paged_decode_plan.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, ip,
-                                             ctypes.POINTER(Plan), vp]
-    lib.gqa_av_paged_decode_plan.restype = ip
+    for fn in ("gqa_av_paged_decode_plan", "gqa_av_paged_decode_pass1", "gqa_av_paged_decode_combine"):
+        getattr(lib, fn).argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, ip,
+                                     ctypes.POINTER(Plan), vp]
+        getattr(lib, fn).restype = ip
     lib.gqa_av_fp8_decode.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ip, ip, vp]
     lib.gqa_av_fp8_decode.restype = ip
-    lib.gqa_av_fp8_decode_plan.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.POINTER(Plan), vp]
-    lib.gqa_av_fp8_decode_plan.restype = ip
+    for fn in ("gqa_av_fp8_decode_plan", "gqa_av_fp8_decode_pass1", "gqa_av_fp8_decode_combine"):
+        getattr(lib, fn).argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.POINTER(Plan), vp]
+        getattr(lib, fn).restype = ip
     lib.gqa_av_status_string.argtypes = [ip]
     lib.gqa_av_status_string.restype = ctypes.c_char_p
     lib.gqa_av_last_error.argtypes = []
@@ -398,12 +400,27 @@ class BoundFp8:
             plan = make_plan(B, C, Hq, Hkv, D, "fp8", mode, cu_count=cu, softmax=softmax,
                              v_align=16 if addr % 16 == 0 else (addr & -addr))
         self.tensors, self.out, self.plan = (w, V, sc), out, plan
-        self._fn = load().gqa_av_fp8_decode_plan
+        lib = load()
+        self._fn, self._pass1, self._combine = (lib.gqa_av_fp8_decode_plan, lib.gqa_av_fp8_decode_pass1,
+                                                lib.gqa_av_fp8_decode_combine)
         self._args = (w.data_ptr(), V.data_ptr(), sc.data_ptr() if sc is not None else None, out.data_ptr(),
                       B, C, Hq, Hkv, D, ctypes.byref(plan), stream.cuda_stream)
 
     def __call__(self):
         rc = self._fn(*self._args)
+        if rc != 0:
+            _raise(rc)
+        return self.out
+
+    def pass1(self):
+        """Only the V-streaming launch (see gqa_av_fp8_decode_pass1); combine() must follow."""
+        rc = self._pass1(*self._args)
+        if rc != 0:
+            _raise(rc)
+
+    def combine(self):
+        """The split combine launch; completes `out`."""
+        rc = self._combine(*self._args)
         if rc != 0:
             _raise(rc)
         return self.out
@@ -476,12 +493,27 @@ class BoundPaged:
             cu = torch.cuda.get_device_properties(w.device).multi_processor_count
             plan = make_plan(B, C, Hq, Hkv, D, vdt, mode, cu_count=cu, softmax=softmax, page_size=P)
         self.tensors, self.out, self.plan = (w, pages, block_table, seq_lens), out, plan
-        self._fn = load().gqa_av_paged_decode_plan
+        lib = load()
+        self._fn, self._pass1, self._combine = (lib.gqa_av_paged_decode_plan, lib.gqa_av_paged_decode_pass1,
+                                                lib.gqa_av_paged_decode_combine)
         self._args = (w.data_ptr(), pages.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
                       B, C, Hq, Hkv, D, P, maxp, npg, DTYPES[vdt], ctypes.byref(plan), stream.cuda_stream)
 
     def __call__(self):
         rc = self._fn(*self._args)
+        if rc != 0:
+            _raise(rc)
+        return self.out
+
+    def pass1(self):
+        """Only the V-streaming launch (see gqa_av_paged_decode_pass1); combine() must follow."""
+        rc = self._pass1(*self._args)
+        if rc != 0:
+            _raise(rc)
+
+    def combine(self):
+        """The split combine launch; completes `out`."""
+        rc = self._combine(*self._args)
         if rc != 0:
             _raise(rc)
         return self.out

@@ -808,13 +808,44 @@ int gqa_av_fp8_decode(const float* w, const void* V, const float* v_scale, float
     return gqa_av_fp8_decode_plan(w, V, v_scale, out, B, C, Hq, Hkv, D, &plan, stream);
 }
 
-int gqa_av_fp8_decode_plan(const float* w, const void* V, const float* v_scale, float* out, int64_t B, int64_t C,
-                           int64_t Hq, int64_t Hkv, int64_t D, const gqa_av_plan* plan, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int run_fp8(const float* w, const void* V, const float* v_scale, float* out, int64_t B, int64_t C, int64_t Hq,
+            int64_t Hkv, int64_t D, const gqa_av_plan* plan, void* stream, int which) {
     if (!plan) return fail(GQA_AV_ERR_INVALID_ARG, "plan is NULL");
     if (v_scale && (reinterpret_cast<uintptr_t>(v_scale) & 3u))
         return fail(GQA_AV_ERR_INVALID_ARG, "v_scale must be 4-byte aligned");
-    return run_plan(w, V, out, B, C, Hq, Hkv, D, GQA_AV_FP8_E4M3, plan, stream, kRunPass1 | kRunCombine,
-                    plan->softmax, nullptr, v_scale);
+    return run_plan(w, V, out, B, C, Hq, Hkv, D, GQA_AV_FP8_E4M3, plan, stream, which, plan->softmax, nullptr,
+                    v_scale);
+}
+
+int run_paged(const float* w, const void* pages, const int32_t* block_table, const int32_t* seq_lens, float* out,
+              int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int64_t page_size, int64_t max_pages,
+              int64_t num_pages, int v_dtype, const gqa_av_plan* plan, void* stream, int which) {
+    if (!plan) return fail(GQA_AV_ERR_INVALID_ARG, "plan is NULL");
+    PagedArgs pa{block_table, seq_lens, page_size, max_pages, num_pages};
+    return run_plan(w, pages, out, B, C, Hq, Hkv, D, v_dtype, plan, stream, which, plan->softmax, &pa);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_av_fp8_decode_plan(const float* w, const void* V, const float* v_scale, float* out, int64_t B, int64_t C,
+                           int64_t Hq, int64_t Hkv, int64_t D, const gqa_av_plan* plan, void* stream) {
+    return run_fp8(w, V, v_scale, out, B, C, Hq, Hkv, D, plan, stream, kRunPass1 | kRunCombine);
+}
+
+int gqa_av_fp8_decode_pass1(const float* w, const void* V, const float* v_scale, float* out, int64_t B, int64_t C,
+                            int64_t Hq, int64_t Hkv, int64_t D, const gqa_av_plan* plan, void* stream) {
+    return run_fp8(w, V, v_scale, out, B, C, Hq, Hkv, D, plan, stream, kRunPass1);
+}
+
+int gqa_av_fp8_decode_combine(const float* w, const void* V, const float* v_scale, float* out, int64_t B, int64_t C,
+                              int64_t Hq, int64_t Hkv, int64_t D, const gqa_av_plan* plan, void* stream) {
+    return run_fp8(w, V, v_scale, out, B, C, Hq, Hkv, D, plan, stream, kRunCombine);
 }
 
 int gqa_av_paged_decode(const float* w, const void* pages, const int32_t* block_table, const int32_t* seq_lens,
@@ -833,10 +864,24 @@ int gqa_av_paged_decode_plan(const float* w, const void* pages, const int32_t* b
                              const int32_t* seq_lens, float* out, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
                              int64_t D, int64_t page_size, int64_t max_pages, int64_t num_pages, int v_dtype,
                              const gqa_av_plan* plan, void* stream) {
-    if (!plan) return fail(GQA_AV_ERR_INVALID_ARG, "plan is NULL");
-    PagedArgs pa{block_table, seq_lens, page_size, max_pages, num_pages};
-    return run_plan(w, pages, out, B, C, Hq, Hkv, D, v_dtype, plan, stream, kRunPass1 | kRunCombine, plan->softmax,
-                    &pa);
+    return run_paged(w, pages, block_table, seq_lens, out, B, C, Hq, Hkv, D, page_size, max_pages, num_pages, v_dtype,
+                     plan, stream, kRunPass1 | kRunCombine);
+}
+
+int gqa_av_paged_decode_pass1(const float* w, const void* pages, const int32_t* block_table,
+                              const int32_t* seq_lens, float* out, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
+                              int64_t D, int64_t page_size, int64_t max_pages, int64_t num_pages, int v_dtype,
+                              const gqa_av_plan* plan, void* stream) {
+    return run_paged(w, pages, block_table, seq_lens, out, B, C, Hq, Hkv, D, page_size, max_pages, num_pages, v_dtype,
+                     plan, stream, kRunPass1);
+}
+
+int gqa_av_paged_decode_combine(const float* w, const void* pages, const int32_t* block_table,
+                                const int32_t* seq_lens, float* out, int64_t B, int64_t C, int64_t Hq,
+                                int64_t Hkv, int64_t D, int64_t page_size, int64_t max_pages, int64_t num_pages,
+                                int v_dtype, const gqa_av_plan* plan, void* stream) {
+    return run_paged(w, pages, block_table, seq_lens, out, B, C, Hq, Hkv, D, page_size, max_pages, num_pages, v_dtype,
+                     plan, stream, kRunCombine);
 }
 
 int gqa_softmax_av_decode_pass1(const float* scores, const void* V, float* out, int64_t B, int64_t C, int64_t Hq,

@@ -50,6 +50,17 @@ int gqa_av_fp8_decode_plan(const float *w, const void *V, const float *v_scale, 
                            int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D,
                            const gqa_av_plan *plan, void *stream);
 
+/* The two launches of gqa_av_fp8_decode_plan, for callers that schedule or
+ * time them separately: same arguments, checks and order as
+ * gqa_av_decode_pass1 / gqa_av_decode_combine (gqa_av.h); `out` is complete
+ * only after the combine. */
+int gqa_av_fp8_decode_pass1(const float *w, const void *V, const float *v_scale, float *out,
+                            int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D,
+                            const gqa_av_plan *plan, void *stream);
+int gqa_av_fp8_decode_combine(const float *w, const void *V, const float *v_scale, float *out,
+                              int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D,
+                              const gqa_av_plan *plan, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

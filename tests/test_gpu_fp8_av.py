@@ -175,3 +175,23 @@ def test_fp8_every_byte_and_dense_entry_points(Hq, oracle_lib):
         b2 = fn(x.to(DEV), q.to(DEV), plan=plan).cpu().numpy().astype(np.float64)
         assert np.array_equal(a, b2)
         _check(a, oracle_lib.fp8(x, q, None, softmax=softmax), x, q, torch.ones(Hkv), softmax, "fp8 dense entry")
+
+
+@pytest.mark.parametrize("softmax", [False, True])
+def test_fp8_pass1_then_combine_is_the_call(softmax):
+    """gqa_av_fp8_decode_pass1 then _combine on one stream equals
+    gqa_av_fp8_decode_plan bit for bit (VALU at G=2, bf16 matrix engine at G=8,
+    one split and several)."""
+    for Hq, ns in ((16, 0), (64, 0), (64, 1)):
+        B, C, Hkv, D = 3, 3000, 8, 128
+        s, V = make_scores_random(B, C, Hq, Hkv, D, "f32", seed=99 + Hq)
+        q, scale = _quantize(V)
+        x = s if softmax else torch.softmax(s.double(), dim=1).float().contiguous()
+        plan = ga.make_plan(B, C, Hq, Hkv, D, "fp8", nsplit=ns, softmax=softmax)
+        call = ga.bind_fp8(x.to(DEV), q.to(DEV), scale.to(DEV), plan=plan)
+        whole = call().clone()
+        call.out.fill_(float("nan"))
+        call.pass1()
+        got = call.combine()
+        torch.cuda.synchronize()
+        assert torch.equal(whole, got), (Hq, ns, softmax)

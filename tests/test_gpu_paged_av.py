@@ -227,3 +227,24 @@ def test_paged_deterministic_and_side_stream():
     st.synchronize()
     torch.cuda.synchronize()
     assert all(torch.equal(a[0], x) for x in a[1:]) and torch.equal(a[0], c.cpu())
+
+
+@pytest.mark.parametrize("softmax", [False, True])
+def test_paged_pass1_then_combine_is_the_call(softmax):
+    """gqa_av_paged_decode_pass1 then _combine on one stream equals
+    gqa_av_paged_decode_plan bit for bit (VALU at G=2, bf16 matrix engine at
+    G=8, one split and several)."""
+    for Hq, ns in ((16, 0), (64, 0), (64, 1)):
+        B, C, Hkv, D, P = 3, 3000, 8, 128, 16
+        s, V = make_scores_random(B, C, Hq, Hkv, D, "bf16", seed=97 + Hq)
+        pages, bt = _paged_from_dense(V, P, seed=4)
+        lens = torch.tensor([3000, 2048, 5], dtype=torch.int32)
+        x = s if softmax else torch.softmax(s.double(), dim=1).float().contiguous()
+        plan = ga.make_plan(B, C, Hq, Hkv, D, "bf16", nsplit=ns, softmax=softmax, page_size=P)
+        call = ga.bind_paged(x.to(DEV), pages.to(DEV), bt.to(DEV), lens.to(DEV), plan=plan)
+        whole = call().clone()
+        call.out.fill_(float("nan"))
+        call.pass1()
+        got = call.combine()
+        torch.cuda.synchronize()
+        assert torch.equal(whole, got), (Hq, ns, softmax)

@@ -57,17 +57,8 @@ constexpr int kMaxSplitPages = 1024;  // paged V: pages one context split may to
 #define GQA_AV_VALU_UNROLL 4      // rows per lane per iteration, groups of up to 4 heads (4 measured
                                   // best on MI355X: 3-4 % over 8, much better than 16 for D = 96)
 #endif
-#ifndef GQA_AV_VALU_PIPELINE
-#define GQA_AV_VALU_PIPELINE 0    // staged weights only: next stage's loads in flight during the current one
-#endif
-#ifndef GQA_AV_VALU_STAGE_WEIGHTS
-#define GQA_AV_VALU_STAGE_WEIGHTS 0  // 1: weights staged in LDS per stage; 0: each lane loads its row's weights
-#endif
 #ifndef GQA_AV_MFMA_UNROLL
 #define GQA_AV_MFMA_UNROLL 4      // row groups of four per wave and step (16-byte lanes)
-#endif
-#ifndef GQA_AV_MFMA_PIPELINE
-#define GQA_AV_MFMA_PIPELINE 1    // 1: the next step's loads in flight during the current step's MFMAs
 #endif
 #ifndef GQA_AV_MFMA_BF16_CHUNKS
 #define GQA_AV_MFMA_BF16_CHUNKS 1 // bf16 matrix engine: 32-row chunks per wave and buffer (two buffers)
@@ -223,14 +214,6 @@ __device__ inline void load_floats(__amdgpu_buffer_rsrc_t rs, int voffset, int s
     } else if constexpr (N % 4 == 1) {
         out[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, voffset + 4 * k, soffset, 0));
     }
-}
-
-template <int NB>
-__device__ inline Raw<NB> zero_raw() {
-    Raw<NB> r;
-#pragma unroll
-    for (int i = 0; i < (NB >= 4 ? NB / 4 : 1); ++i) r.w[i] = 0u;
-    return r;
 }
 
 // Exact split of an fp32 value w into three bfloat16 terms by truncation:
@@ -418,10 +401,6 @@ __device__ inline void combine_last(const Pass1Args& a, const Tile& T, const flo
 
 // ---- pass 1: VALU engine ----------------------------------------------------
 
-// GP: padded LDS row of staged weights (GT = 3 -> 4 so rows stay 16-byte aligned).
-template <int GT>
-constexpr int padded_heads() { return GT <= 2 ? GT : (GT + 3) / 4 * 4; }
-
 // SM: fused softmax. attn then holds raw scores s; a lane's weight for a row is
 // exp2((s - mx) log2 e) with mx the running maximum of the scores the lane has
 // seen (per head). When a step raises mx, the lane's accumulators and weight
@@ -446,15 +425,7 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
     constexpr int NACC = GT * E;
     constexpr int CH = NACC < 32 ? NACC : 32;       // accumulator slots per LDS reduction pass
     constexpr int RED = CH * kThreads;
-#if GQA_AV_VALU_STAGE_WEIGHTS
-    constexpr int GP = padded_heads<GT>();
-    constexpr int RMAX = kMaxRowSlots * U;           // rows per stage is rps * U
-    constexpr int WBUF = 2 * RMAX * GP;              // staged weights, double-buffered (worst case)
-    constexpr int SMEM = WBUF > RED ? WBUF : RED;
-#else
-    constexpr int SMEM = RED;
-#endif
-    __shared__ float smem[SMEM];
+    __shared__ float smem[RED];
 
     const Tile T = decode_tile(a, GT);
     const int tid = threadIdx.x;
@@ -490,118 +461,6 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
     }
     __shared__ float s_stat[2][4 * GT];              // SM: the workgroup's maximum and weight sum per head
 
-#if GQA_AV_VALU_STAGE_WEIGHTS
-    static_assert(!SM && !PG, "the fused softmax and paged V need the per-lane weight path");
-    const uint8_t* vbase = a.V + (static_cast<size_t>(T.b) * a.C * a.Hkv + T.kv + kvl) * a.D * ES
-                               + static_cast<size_t>(lane_d) * VB;
-    const int q_lo = T.q_first;                      // accumulator g is head q_lo + g (tiles of one KV head)
-    auto lane_q_lo = [&](int) { return q_lo; };
-    const float* abase = a.attn + static_cast<size_t>(T.b) * a.C * a.Hq + T.q_first;
-    const int64_t nstage = ce > cb ? (ce - cb + R - 1) / R : 0;
-
-    // Weight staging: element k of a stage is (row i = k / GT, head g = k % GT).
-    const int nstage_elems = R * GT;
-    constexpr int SPT = (RMAX * GT + kThreads - 1) / kThreads;  // staged words per thread (bound)
-    float wreg[SPT];
-    auto stage_load = [&](int64_t c0) {
-#pragma unroll
-        for (int k = 0; k < SPT; ++k) {
-            const int idx = tid + k * kThreads;
-            float v = 0.0f;
-            if (idx < nstage_elems) {
-                const int i = idx / GT, g = idx - (idx / GT) * GT;
-                const int64_t c = c0 + i;
-                if (g < T.nq && c < ce) v = abase[c * a.Hq + g];
-            }
-            wreg[k] = v;
-        }
-    };
-    auto stage_store = [&](int buf) {
-        float* w = smem + buf * (RMAX * GP);
-#pragma unroll
-        for (int k = 0; k < SPT; ++k) {
-            const int idx = tid + k * kThreads;
-            if (idx < nstage_elems) {
-                const int i = idx / GT, g = idx - (idx / GT) * GT;
-                w[i * GP + g] = wreg[k];
-            }
-        }
-    };
-    // V rows of the stage starting at c0: this lane's rows are c0 + r + u * rps.
-    auto load_v = [&](Raw<VB> (&raw)[U], int64_t c0) {
-        if (!active) return;
-        const uint8_t* p = vbase + static_cast<size_t>(c0 + r) * vrow;
-        const size_t step = static_cast<size_t>(rps) * vrow;
-        if (c0 + R <= ce) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) raw[u] = load_raw<VB>(p + u * step);
-        } else {
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                raw[u] = (c0 + r + u * rps < ce) ? load_raw<VB>(p + u * step) : zero_raw<VB>();
-        }
-    };
-    auto compute = [&](const Raw<VB> (&raw)[U], int buf) {
-        if (!active) return;
-        const float* w = smem + buf * (RMAX * GP);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const float* wr = w + (r + u * rps) * GP;
-            float wv[GT];
-#pragma unroll
-            for (int g = 0; g < GT; ++g) wv[g] = wr[g];
-            float f[E];
-            widen<DT, VB>(raw[u], f);
-#pragma unroll
-            for (int g = 0; g < GT; ++g)
-#pragma unroll
-                for (int e = 0; e < E; ++e) acc[g][e] = __builtin_fmaf(wv[g], f[e], acc[g][e]);
-        }
-    };
-
-    // Software pipeline over stages: the next stage's V rows and weights are in
-    // flight while the current stage is computed. Stage st uses weight buffer st & 1.
-    Raw<VB> rA[U];
-#if GQA_AV_VALU_PIPELINE
-    Raw<VB> rB[U];
-#endif
-    if (nstage > 0) {
-        load_v(rA, cb);
-        stage_load(cb);
-        stage_store(0);
-    }
-    __syncthreads();
-#if GQA_AV_VALU_PIPELINE
-    int64_t st = 0;
-    for (; st + 1 < nstage; st += 2) {
-        const int64_t c1 = cb + (st + 1) * R;
-        load_v(rB, c1);
-        stage_load(c1);
-        compute(rA, 0);
-        stage_store(1);
-        __syncthreads();
-        const bool more = st + 2 < nstage;
-        if (more) {
-            load_v(rA, c1 + R);
-            stage_load(c1 + R);
-        }
-        compute(rB, 1);
-        if (more) stage_store(0);
-        __syncthreads();
-    }
-    if (st < nstage) compute(rA, 0);
-#else
-    for (int64_t st = 0; st < nstage; ++st) {
-        const int buf = static_cast<int>(st & 1);
-        if (st > 0) load_v(rA, cb + st * R);
-        if (st + 1 < nstage) stage_load(cb + (st + 1) * R);
-        compute(rA, buf);
-        if (st + 1 < nstage) stage_store(buf ^ 1);
-        __syncthreads();
-    }
-#endif
-
-#else
     // The tile's weights are read as a window of GT consecutive heads starting at
     // q_lo, shifted down when the tile's last sub-group is short, so every lane
     // loads GT words at constant offsets and the window never leaves the attn
@@ -734,7 +593,6 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
         }
         if (st < nsteps) compute(bA, st);
     }
-#endif
     __syncthreads();                                  // LDS is reused below
 
     // SM: bring every row slot to the workgroup's maximum per (KV head of the
@@ -933,7 +791,6 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma(Pass1Args a) {
         }
     };
 
-#if GQA_AV_MFMA_PIPELINE
     Raw<NB> vA[U], vB[U];
     float wA[U][NSET], wB[U][NSET];
     int64_t st = 0;
@@ -946,14 +803,6 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma(Pass1Args a) {
         compute(vB, wB);
     }
     if (st < nsteps) compute(vA, wA);
-#else
-    for (int64_t st = 0; st < nsteps; ++st) {
-        Raw<NB> v[U];
-        float w[U][NSET];
-        load(v, w, cb + st * RSTEP);
-        compute(v, w);
-    }
-#endif
 
     // Add the four waves' 16 x D tiles. Register i of acc[s][e] in lane l is
     // head 16 s + 4 (l / 16) + i, element d = (l % 16) * DE + e; as a tile

@@ -300,14 +300,10 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
         else if (G >= kMfmaMinGroup && mfma_ok && !sm && !paged && v_dtype != GQA_AV_FP8_E4M3)
             engine = GQA_AV_ENGINE_MFMA;
     }
-    if (paged && engine == GQA_AV_ENGINE_VALU && GQA_AV_VALU_STAGE_WEIGHTS)
-        return fail(GQA_AV_ERR_UNSUPPORTED, "paged V needs the per-lane weight VALU build");
     if (sm && engine == GQA_AV_ENGINE_MFMA)
         return fail(GQA_AV_ERR_UNSUPPORTED, "the fused softmax runs on the VALU or bf16 matrix engine");
     if (v_dtype == GQA_AV_FP8_E4M3 && engine == GQA_AV_ENGINE_MFMA)
         return fail(GQA_AV_ERR_UNSUPPORTED, "fp8 V runs on the VALU or bf16 matrix engine");
-    if (sm && engine == GQA_AV_ENGINE_VALU && GQA_AV_VALU_STAGE_WEIGHTS)
-        return fail(GQA_AV_ERR_UNSUPPORTED, "the fused softmax needs the per-lane weight VALU build");
     if (engine == GQA_AV_ENGINE_MFMA && !mfma_ok)
         return fail(GQA_AV_ERR_UNSUPPORTED,
                     "MFMA engine needs reuse mode, D %% 16 == 0 with a 4/8/12/16/32-byte lane chunk and matching V alignment");
@@ -331,7 +327,7 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
     int ht = h.kv_tile > 0 ? h.kv_tile : 1;
     const bool bf16_engine = engine == GQA_AV_ENGINE_MFMA_BF16;
     if (h.kv_tile <= 0 && resolved == GQA_AV_REUSE &&
-        ((engine == GQA_AV_ENGINE_VALU && !GQA_AV_VALU_STAGE_WEIGHTS) || bf16_engine)) {
+        (engine == GQA_AV_ENGINE_VALU || bf16_engine)) {
         const bool fp8 = v_dtype == GQA_AV_FP8_E4M3;
         const int64_t lanes = (D * es) / 16 > 0 && (D * es) % 16 == 0 ? (D * es) / 16 : 0;
         const int64_t nsgw = ceil_div(G, bf16_engine ? 16 * nset16 : head_capacity(G));
@@ -350,7 +346,7 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
         }
     }
     if (ht > 1) {
-        if (resolved != GQA_AV_REUSE || !((engine == GQA_AV_ENGINE_VALU && !GQA_AV_VALU_STAGE_WEIGHTS) || bf16_engine))
+        if (resolved != GQA_AV_REUSE || !(engine == GQA_AV_ENGINE_VALU || bf16_engine))
             return fail(GQA_AV_ERR_UNSUPPORTED, "kv_tile > 1 needs the VALU or bf16 matrix engine in reuse mode");
         if (Hkv % ht != 0)
             return fail(GQA_AV_ERR_INVALID_ARG, "kv_tile %d does not divide Hkv=%lld", ht, (long long)Hkv);

@@ -10,13 +10,9 @@ namespace detail {
 template <int DT, int VB, int GT, bool SM, bool PG>
 hipError_t launch_valu(const gqa_av::Pass1Args& a, hipStream_t s) {
     constexpr int U = gqa_av::valu_unroll(GT);
-    if constexpr ((SM || PG) && GQA_AV_VALU_STAGE_WEIGHTS) {
-        return hipErrorInvalidValue;                 // the plan refuses this combination
-    } else {
-        hipLaunchKernelGGL((gqa_av::av_pass1_valu<DT, VB, GT, U, SM, PG>), dim3(a.nblocks), dim3(gqa_av::kThreads),
-                           0, s, a);
-        return hipGetLastError();
-    }
+    hipLaunchKernelGGL((gqa_av::av_pass1_valu<DT, VB, GT, U, SM, PG>), dim3(a.nblocks), dim3(gqa_av::kThreads), 0, s,
+                       a);
+    return hipGetLastError();
 }
 
 template <int DT, int VB, bool SM, bool PG = false>
@@ -43,16 +39,6 @@ hipError_t launch_valu_gt(int GT, const gqa_av::Pass1Args& a, hipStream_t s) {
     }
 }
 
-// Paged V: 16-byte lane loads only.
-template <int DT>
-hipError_t launch_valu_paged(bool sm, int GT, const gqa_av::Pass1Args& a, hipStream_t s) {
-    if constexpr (DT == gqa_av::kFP8) {
-        return hipErrorInvalidValue;                 // the plan refuses paged fp8 V
-    } else {
-        return sm ? launch_valu_gt<DT, 16, true, true>(GT, a, s) : launch_valu_gt<DT, 16, false, true>(GT, a, s);
-    }
-}
-
 template <int DT, bool SM>
 hipError_t launch_valu_vb(int VB, int GT, const gqa_av::Pass1Args& a, hipStream_t s) {
     switch (VB) {
@@ -70,13 +56,8 @@ hipError_t launch_valu_vb(int VB, int GT, const gqa_av::Pass1Args& a, hipStream_
 
 template <int DT, bool SM>
 hipError_t valu(int VB, int GT, bool paged, const gqa_av::Pass1Args& a, hipStream_t s) {
-    if (paged) {
-        if constexpr (DT == gqa_av::kFP8 || GQA_AV_VALU_STAGE_WEIGHTS) {
-            return hipErrorInvalidValue;             // the plan refuses these combinations
-        } else {
-            return VB == 16 ? detail::launch_valu_gt<DT, 16, SM, true>(GT, a, s) : hipErrorInvalidValue;
-        }
-    }
+    if (paged)   // paged V: 16-byte lane loads only (fp8: tiles of up to 4 heads)
+        return VB == 16 ? detail::launch_valu_gt<DT, 16, SM, true>(GT, a, s) : hipErrorInvalidValue;
     return detail::launch_valu_vb<DT, SM>(VB, GT, a, s);
 }
 

@@ -527,6 +527,8 @@ def test_fp8_plans():
         assert e.value.name == "UNSUPPORTED", kw
     pf = ga.make_plan(2, 1000, 16, 2, 128, "fp8", "reuse", page_size=16)   # paged fp8 at G = 8: bf16 matrix engine
     assert pf.engine == 3 and pf.vec_bytes == 8 and pf.page_size == 16
+    pv = ga.make_plan(2, 1000, 8, 2, 128, "fp8", "reuse", page_size=16)    # paged fp8 at G = 4: VALU, 16 values a lane
+    assert pv.engine == 1 and pv.vec_bytes == 16 and pv.page_size == 16
     with pytest.raises(ga.GqaAvError) as e:
         ga.make_plan(2, 1000, 16, 2, 127, "fp8")            # odd D: no 2-byte lane load fits
     assert e.value.name == "UNSUPPORTED"

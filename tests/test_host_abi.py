@@ -8,6 +8,7 @@ import ctypes
 import glob
 import os
 import re
+import threading
 
 import pytest
 
@@ -546,3 +547,30 @@ def test_fp8_calls_reject_before_launch():
     assert lib.gqa_av_fp8_decode_plan(fake, fake, None, fake, 2, 5000, 8, 2, 64, ctypes.byref(p), None) == 1
     pb = ga.make_plan(2, 100, 8, 2, 64, "bf16")             # a bf16 plan for an fp8 call
     assert lib.gqa_av_fp8_decode_plan(fake, fake, None, fake, 2, 100, 8, 2, 64, ctypes.byref(pb), None) == 1
+
+
+def test_error_detail_is_per_thread():
+    """A failing call in one thread leaves another thread's error detail alone."""
+    lib = ga.load()
+    seen = {}
+    gate = threading.Barrier(2)
+
+    def bad():
+        rc = lib.gqa_av_decode(None, None, None, 2, 100, 8, 3, 64, 2, -1, None)   # Hq % Hkv != 0
+        gate.wait()
+        gate.wait()
+        seen["bad"] = (rc, lib.gqa_av_last_error().decode())
+
+    def good():
+        gate.wait()
+        rc = lib.gqa_av_resolve_mode(16, 8, -1)
+        seen["good"] = (rc, lib.gqa_av_last_error().decode())
+        gate.wait()
+
+    ts = [threading.Thread(target=bad), threading.Thread(target=good)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert seen["bad"][0] != 0 and seen["bad"][1], seen
+    assert seen["good"][0] == 1 and seen["good"][1] == "", seen

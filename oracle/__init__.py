@@ -67,6 +67,8 @@ class Oracle:
         lib.gqa_fp8_oracle_decode.restype = ip
         lib.gqa_fp8_oracle.argtypes = [vp, vp, vp, ip, i64, i64, i64, i64, i64, vp, ip]
         lib.gqa_fp8_oracle.restype = ip
+        lib.gqa_qk_fp8_oracle.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_double, vp, ip]
+        lib.gqa_qk_fp8_oracle.restype = ip
         self.lib = lib
 
     @staticmethod
@@ -100,6 +102,22 @@ class Oracle:
         out = np.empty((B, C, Hq), dtype=np.float64)
         rc = self.lib.gqa_qk_oracle(qa.ctypes.data, k.ctypes.data, DTYPE_CODE[k_dtype],
                                     B, C, Hq, Hkv, D, float(scale), out.ctypes.data, nthreads)
+        if rc != 0:
+            raise ValueError(f"oracle rejected the arguments (status {rc})")
+        return out
+
+    def qk_fp8(self, q, K8, k_scale=None, scale: float = 1.0, nthreads: int = 0) -> np.ndarray:
+        """scores[B, C, Hq] (float64) for q [B,Hq,D] fp32, K8 [B,C,Hkv,D] OCP FP8
+        E4M3 bytes (uint8 or torch.float8_e4m3fn) and k_scale [Hkv] fp32 or None."""
+        qa = np.ascontiguousarray(_as_numpy(q, np.float32))
+        k = np.ascontiguousarray(_fp8_bytes(K8))
+        B, Hq, D = qa.shape
+        B2, C, Hkv, D2 = k.shape
+        assert B2 == B and D2 == D
+        ks = None if k_scale is None else np.ascontiguousarray(_as_numpy(k_scale, np.float32))
+        out = np.empty((B, C, Hq), dtype=np.float64)
+        rc = self.lib.gqa_qk_fp8_oracle(qa.ctypes.data, k.ctypes.data, None if ks is None else ks.ctypes.data,
+                                        B, C, Hq, Hkv, D, float(scale), out.ctypes.data, nthreads)
         if rc != 0:
             raise ValueError(f"oracle rejected the arguments (status {rc})")
         return out

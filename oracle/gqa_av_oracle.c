@@ -57,7 +57,9 @@
  * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no infinities,
  * S.1111.111 is NaN) and each KV head has a float32 scale: the value of an
  * element is decode(byte) * v_scale[kv_h], exact in double. The products and
- * sums are those of the plain or fused definitions above.
+ * sums are those of the plain or fused definitions above. fp8 K in the score
+ * step is read the same way, with its own per-KV-head k_scale:
+ * scores = scale * sum_d q * (decode(K byte) * k_scale[kv_h]).
  *
  * Paged V (a decode cache layout, not on the page): sequence b has seq_lens[b]
  * context rows; row c of it lives in page block_table[b][c / page_size], at
@@ -411,6 +413,42 @@ int gqa_fp8_oracle(const float *w, const uint8_t *V, const float *v_scale, int s
 #endif
     for (int64_t i = 0; i < rows; ++i)
         orc_fp8_row(w, V, v_scale, softmax, C, Hq, Hkv, D, i / Hq, i % Hq, out + i * D);
+    (void)nthreads;
+    return ORC_OK;
+}
+
+/* Score step over fp8 K with per-KV-head scales (k_scale [Hkv] or NULL: all
+ * 1): out[B][C][Hq] in double, the score definition above with each K element
+ * decode(byte) * k_scale[kv_h]; the dot product runs in increasing d. */
+static void orc_qk_fp8_row(const float *q, const uint8_t *K, const float *k_scale,
+                           int64_t C, int64_t Hq, int64_t Hkv, int64_t D,
+                           int64_t b, int64_t c, double scale, double *out)
+{
+    const int64_t G = Hq / Hkv;
+    for (int64_t h = 0; h < Hq; ++h) {
+        const int64_t kvh = h / G;
+        const double ks = k_scale ? (double)k_scale[kvh] : 1.0;
+        const float *qrow = q + (b * Hq + h) * D;
+        const uint8_t *krow = K + ((b * C + c) * Hkv + kvh) * D;
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; ++d) dot += (double)qrow[d] * (orc_e4m3(krow[d]) * ks);
+        out[h] = dot * scale;
+    }
+}
+
+int gqa_qk_fp8_oracle(const float *q, const uint8_t *K, const float *k_scale,
+                      int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D,
+                      double scale, double *out, int nthreads)
+{
+    int rc = orc_check(ORC_F32, B, C, Hq, Hkv, D);
+    if (rc != ORC_OK) return rc;
+    const int64_t rows = B * C;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 64) num_threads(nthreads)
+#endif
+    for (int64_t i = 0; i < rows; ++i)
+        orc_qk_fp8_row(q, K, k_scale, C, Hq, Hkv, D, i / C, i % C, scale, out + i * Hq);
     (void)nthreads;
     return ORC_OK;
 }

@@ -73,6 +73,15 @@ fp8 V (OCP FP8 E4M3 bytes times a float32 scale per KV head):
                       for bit (plain and fused softmax).
   * fp8_scales        a power-of-two scale per KV head scales exactly that head's
                       group of outputs; one head's scale leaves the others alone.
+
+fp8 K in the score step (same bytes and per-KV-head scales):
+  * qk_fp8_as_bf16    with unit scales the fp8 score oracle equals the bf16
+                      score oracle on K widened by torch's float8 -> bfloat16
+                      conversion, bit for bit.
+  * qk_fp8_brute      tiny shapes against Python's exact rational arithmetic
+                      (fractions) on torch's decoded K, correctly rounded.
+  * qk_fp8_scales     a power-of-two k_scale per KV head scales exactly that
+                      head's group of score columns; others are left alone.
 """
 from __future__ import annotations
 
@@ -635,10 +644,62 @@ def pin_fp8_scales(orc):
     assert not np.array_equal(o2, b2)
 
 
+def pin_qk_fp8_as_bf16(orc):
+    for i, (B, C, Hq, Hkv, D) in enumerate([(2, 13, 6, 2, 16), (1, 7, 4, 4, 9), (2, 5, 8, 1, 32)]):
+        q, _ = make_qk_random(B, C, Hq, Hkv, D, "f32", seed=930 + i)
+        _, raw = _fp8_case(B, C, Hq, Hkv, D, seed=940 + i)
+        k16 = raw.view(torch.float8_e4m3fn).to(torch.bfloat16)
+        for scale in (1.0, 0.125, 0.3):
+            a = orc.qk_fp8(q, raw, None, scale)
+            b = orc.qk(q, k16, "bf16", scale)
+            assert np.array_equal(a, b), f"fp8 scores != bf16 scores on the widened K (scale {scale})"
+
+
+def pin_qk_fp8_brute(orc):
+    from fractions import Fraction
+    for i, (B, C, Hq, Hkv, D) in enumerate([(1, 3, 4, 2, 5), (2, 2, 3, 1, 4)]):
+        q, _ = make_qk_random(B, C, Hq, Hkv, D, "f32", seed=950 + i)
+        _, raw = _fp8_case(B, C, Hq, Hkv, D, seed=960 + i)
+        kd = raw.view(torch.float8_e4m3fn).double()
+        ks = torch.tensor([0.5, 3.0][:Hkv])
+        out = orc.qk_fp8(q, raw, ks, 1.0)
+        G = Hq // Hkv
+        for b in range(B):
+            for c in range(C):
+                for h in range(Hq):
+                    kv = h // G
+                    terms = [Fraction(float(q[b, h, d])) * Fraction(float(kd[b, c, kv, d])) * Fraction(float(ks[kv]))
+                             for d in range(D)]
+                    exact, mag = sum(terms), sum(abs(t) for t in terms)
+                    # D - 1 double additions in increasing d: |err| <= gamma_{D-1} * sum |terms|
+                    assert abs(Fraction(out[b, c, h]) - exact) <= Fraction(gamma(D - 1)) * mag, \
+                        f"fp8 score ({b}, {c}, {h}) not the exact sum"
+
+
+def pin_qk_fp8_scales(orc):
+    B, C, Hq, Hkv, D = 2, 11, 8, 4, 12
+    q, _ = make_qk_random(B, C, Hq, Hkv, D, "f32", seed=971)
+    _, raw = _fp8_case(B, C, Hq, Hkv, D, seed=972)
+    G = Hq // Hkv
+    base = orc.qk_fp8(q, raw, None, 0.25)
+    sc = torch.tensor([0.25, 1.0, 8.0, 2.0 ** -10])
+    o = orc.qk_fp8(q, raw, sc, 0.25)
+    for h in range(Hq):
+        assert np.array_equal(o[:, :, h], base[:, :, h] * float(sc[h // G])), f"fp8 k_scale of head {h}"
+    sc2 = torch.ones(Hkv)
+    sc2[1] = 3.0
+    o2 = orc.qk_fp8(q, raw, sc2, 0.25)
+    for h in range(Hq):
+        if h // G != 1:
+            assert np.array_equal(o2[:, :, h], base[:, :, h]), "fp8 k_scale leaked into another head"
+    assert not np.array_equal(o2, base)
+
+
 ALL_PINS = [pin_decode_table, pin_brute_force, pin_mha_einsum, pin_repeat_mha, pin_constant_v,
             pin_one_hot, pin_linearity, pin_permutation, pin_batch_independence, pin_points,
             pin_edges, pin_qk_brute_force, pin_qk_mha_einsum, pin_qk_repeat_mha, pin_qk_one_hot,
             pin_qk_scale_linear, pin_qk_composition, pin_qk_edges, pin_sav_library, pin_sav_shift,
             pin_sav_large, pin_sav_one_hot, pin_sav_uniform, pin_sav_two_rows, pin_sav_mask,
             pin_sav_repeat_mha, pin_sav_edges, pin_paged_gather, pin_paged_identity, pin_paged_ignores_tail,
-            pin_paged_rejects, pin_fp8_decode, pin_fp8_as_bf16, pin_fp8_scales]
+            pin_paged_rejects, pin_fp8_decode, pin_fp8_as_bf16, pin_fp8_scales, pin_qk_fp8_as_bf16,
+            pin_qk_fp8_brute, pin_qk_fp8_scales]

@@ -74,6 +74,14 @@ PLANTS = [
     ("fp8_scale_of_query_head", "const double sc = v_scale ? (double)v_scale[kv] : 1.0;",
      "const double sc = v_scale ? (double)v_scale[q % Hkv] : 1.0;"),
     ("fp8_scale_ignored", "acc[d] += a * (orc_e4m3(r[d]) * sc);", "acc[d] += a * orc_e4m3(r[d]);"),
+    ("qk_fp8_scale_ignored", "dot += (double)qrow[d] * (orc_e4m3(krow[d]) * ks);",
+     "dot += (double)qrow[d] * orc_e4m3(krow[d]);"),
+    ("qk_fp8_scale_of_query_head", "const double ks = k_scale ? (double)k_scale[kvh] : 1.0;",
+     "const double ks = k_scale ? (double)k_scale[h % Hkv] : 1.0;"),
+    ("qk_fp8_no_outer_scale", "out[h] = dot * scale;\n    }\n}\n\nint gqa_qk_fp8_oracle",
+     "out[h] = dot;\n    }\n}\n\nint gqa_qk_fp8_oracle"),
+    ("qk_fp8_wrong_kv_head", "const uint8_t *krow = K + ((b * C + c) * Hkv + kvh) * D;",
+     "const uint8_t *krow = K + ((b * C + c) * Hkv + (Hkv - 1 - kvh)) * D;"),
     ("paged_bt_ignores_batch", "const int64_t page = bt[b * max_pages + c / P];",
      "const int64_t page = bt[0 * max_pages + c / P];"),
 ]

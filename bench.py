@@ -85,6 +85,8 @@ def parse():
     p.add_argument("--kv-tile", type=int, default=0, help="adjacent KV heads per VALU workgroup (0 = plan)")
     p.add_argument("--v-fp8", action="store_true",
                    help="av / softmax with V quantized to OCP FP8 E4M3 with a scale per KV head (half the V bytes)")
+    p.add_argument("--k-fp8", action="store_true",
+                   help="qk with K quantized to OCP FP8 E4M3 with a scale per KV head (half the K bytes)")
     p.add_argument("--page-size", type=int, default=0,
                    help="av / softmax over a paged V cache with this many rows per page (shuffled pages, full "
                         "lengths); 0 = dense V")
@@ -427,15 +429,24 @@ def bench_qk(args, w, dev, props):
     from workloads import make_qk_random
 
     q_h, K_h = make_qk_random(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, seed=0)
-    es = 4 if w.v_dtype == "f32" else 2
+    kdt, ks_h = w.v_dtype, None
+    if args.k_fp8:
+        # per-KV-head scale max|K| / 448 and the E4M3 bytes of K / scale
+        Kf = K_h.float()
+        ks_h = (Kf.abs().amax(dim=(0, 1, 3)).clamp_min(1e-30) / 448.0).contiguous()
+        K_h = (Kf / ks_h.view(1, 1, -1, 1)).to(torch.float8_e4m3fn).contiguous()
+        kdt = "fp8"
+        del Kf
+    es = {"f32": 4, "fp8": 1}.get(kdt, 2)
     alg = w.B * w.C * w.Hkv * w.D * es + 4 * w.B * w.Hq * w.D + 4 * w.B * w.C * w.Hq
-    plan = ga.qk_make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, args.mode, cu_count=props.multi_processor_count)
+    plan = ga.qk_make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, kdt, args.mode, cu_count=props.multi_processor_count)
     nrot = max(1, math.ceil(args.rotate_mb * 2 ** 20 / alg))
     q0, k0 = q_h.to(dev), K_h.to(dev)
+    ks = ks_h.to(dev) if ks_h is not None else None
     calls = []
     for i in range(nrot):
         calls.append(ga.bind_qk(q0 if i == 0 else q0.clone(), k0 if i == 0 else k0.clone(), scale=w.D ** -0.5,
-                                plan=plan))
+                                plan=plan, k_scale=ks))
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     _warm(args, calls, nrot)
@@ -450,23 +461,28 @@ def bench_qk(args, w, dev, props):
         threads = int(os.environ.get("OMP_NUM_THREADS") or 0) or len(os.sched_getaffinity(0))
         reps, t0 = 0, time.perf_counter()
         while True:
-            orc.qk(q_h, K_h, w.v_dtype, w.D ** -0.5, nthreads=threads)
+            if args.k_fp8:
+                orc.qk_fp8(q_h, K_h, ks_h, w.D ** -0.5, nthreads=threads)
+            else:
+                orc.qk(q_h, K_h, w.v_dtype, w.D ** -0.5, nthreads=threads)
             reps += 1
             el = time.perf_counter() - t0
             if el >= args.cpu_seconds or reps >= 1000:
                 break
         cpu = {"value": round(alg / (el / reps) / 1e9, 3), "unit": "GB/s", "us_per_call": round(el / reps * 1e6, 1),
                "cores": threads, "kind": "oracle",
-               "sample": f"full score step of {w.name}, {reps} calls in {el:.1f} s (fp64 C oracle, OpenMP)"}
+               "sample": f"full score step of {w.name}{' (fp8 K)' if args.k_fp8 else ''}, {reps} calls in {el:.1f} s "
+                         "(fp64 C oracle, OpenMP)"}
     line = {
         "metric": QK_METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 6), "us_per_call": round(ms * 1e3, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": f"qk:{w.name}", "B": w.B, "C": w.C, "Hq": w.Hq, "Hkv": w.Hkv, "G": w.G, "D": w.D,
-                   "k_dtype": w.v_dtype, "mode": args.mode, "algorithmic_bytes": alg, "rotation_sets": nrot,
+        "config": {"workload": f"qk{'-fp8' if args.k_fp8 else ''}:{w.name}", "B": w.B, "C": w.C, "Hq": w.Hq,
+                   "Hkv": w.Hkv, "G": w.G, "D": w.D, "k_dtype": "fp8_e4m3" if args.k_fp8 else w.v_dtype, "mode": args.mode, "algorithmic_bytes": alg, "rotation_sets": nrot,
                    "kernels_per_call": 1, "plan": plan.as_dict()},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(w.name, args.mode, "qk"),
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(w.name, args.mode, "qk", "_fp8" if args.k_fp8 else ""),
                      "kernel": "qk_scores", "us_per_launch": round(ms * 1e3, 3),
                      "timing": "HIP events around K back-to-back launches on the launch stream"},
         "cpu_baseline": cpu,

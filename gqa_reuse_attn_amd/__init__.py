@@ -135,6 +135,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gqa_qk_make_plan.restype = ip
     lib.gqa_qk_decode.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ip, ctypes.c_float, ip, vp]
     lib.gqa_qk_decode.restype = ip
+    lib.gqa_qk_fp8_decode.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, ip, vp]
+    lib.gqa_qk_fp8_decode.restype = ip
+    lib.gqa_qk_fp8_decode_plan.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
+                                           ctypes.POINTER(QkPlan), vp]
+    lib.gqa_qk_fp8_decode_plan.restype = ip
     lib.gqa_qk_decode_plan.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ip, ctypes.c_float,
                                        ctypes.POINTER(QkPlan), vp]
     lib.gqa_qk_decode_plan.restype = ip
@@ -547,7 +552,7 @@ def qk_make_plan(B: int, C: int, Hq: int, Hkv: int, D: int, k_dtype: str, mode: 
 
 def _check_qk(q, K, scores):
     torch = _torch()
-    kmap = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
+    kmap = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16", torch.float8_e4m3fn: "fp8"}
     if q.dim() != 3 or K.dim() != 4:
         raise ValueError(f"q must be [B,Hq,D] and K [B,C,Hkv,D]; got {tuple(q.shape)} and {tuple(K.shape)}")
     B, Hq, D = q.shape
@@ -557,7 +562,7 @@ def _check_qk(q, K, scores):
     if q.dtype != torch.float32:
         raise TypeError(f"q must be float32, got {q.dtype}")
     if K.dtype not in kmap:
-        raise TypeError(f"K must be float32, float16 or bfloat16, got {K.dtype}")
+        raise TypeError(f"K must be float32, float16, bfloat16 or float8_e4m3fn, got {K.dtype}")
     if not (q.is_cuda and K.is_cuda) or q.device != K.device:
         raise ValueError("q and K must be GPU tensors on one device")
     if not (q.is_contiguous() and K.is_contiguous()):
@@ -570,22 +575,32 @@ def _check_qk(q, K, scores):
 
 
 def gqa_qk_decode(q, K, scores=None, scale: float = 1.0, mode: Union[str, int] = "auto", stream=None,
-                  plan: Optional[QkPlan] = None):
+                  plan: Optional[QkPlan] = None, k_scale=None):
     """scores[b,c,q_h] = scale * sum_d q[b,q_h,d] * K[b,c,q_h//G,d] on the GPU; returns scores.
 
-    q: float32 [B,Hq,D]; K: float32/float16/bfloat16 [B,C,Hkv,D]; both
-    contiguous on one GPU. The result has the attn layout [B,C,Hq] of
-    gqa_av_decode.
+    q: float32 [B,Hq,D]; K: float32/float16/bfloat16 [B,C,Hkv,D], or
+    float8_e4m3fn with k_scale (float32 [Hkv], None = 1) multiplying each KV
+    head's K; both contiguous on one GPU. The result has the attn layout
+    [B,C,Hq] of gqa_av_decode.
     """
     torch = _torch()
     B, C, Hq, Hkv, D, kdt = _check_qk(q, K, scores)
+    ks = _qk_scale(k_scale, kdt, Hkv, q.device)
     if scores is None:
         scores = torch.empty((B, C, Hq), dtype=torch.float32, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     lib = load()
     with torch.cuda.device(q.device):
-        if plan is None:
+        if kdt == "fp8":
+            kp = ks.data_ptr() if ks is not None else None
+            if plan is None:
+                rc = lib.gqa_qk_fp8_decode(q.data_ptr(), K.data_ptr(), kp, scores.data_ptr(), B, C, Hq, Hkv, D,
+                                           float(scale), _mode(mode), stream.cuda_stream)
+            else:
+                rc = lib.gqa_qk_fp8_decode_plan(q.data_ptr(), K.data_ptr(), kp, scores.data_ptr(), B, C, Hq, Hkv, D,
+                                                float(scale), ctypes.byref(plan), stream.cuda_stream)
+        elif plan is None:
             rc = lib.gqa_qk_decode(q.data_ptr(), K.data_ptr(), scores.data_ptr(), B, C, Hq, Hkv, D, DTYPES[kdt],
                                    float(scale), _mode(mode), stream.cuda_stream)
         else:
@@ -596,13 +611,26 @@ def gqa_qk_decode(q, K, scores=None, scale: float = 1.0, mode: Union[str, int] =
     return scores
 
 
+def _qk_scale(k_scale, kdt, Hkv, device):
+    if k_scale is not None and kdt != "fp8":
+        raise ValueError("k_scale is for fp8 K (torch.float8_e4m3fn)")
+    if k_scale is None:
+        return None
+    torch = _torch()
+    if k_scale.dtype != torch.float32 or tuple(k_scale.shape) != (Hkv,) or not k_scale.is_contiguous() \
+            or k_scale.device != device:
+        raise ValueError(f"k_scale must be a contiguous float32 [{Hkv}] tensor on {device}")
+    return k_scale
+
+
 class BoundQk:
     """Pre-checked score-step call for loops (see BoundCall)."""
 
     def __init__(self, q, K, scores=None, scale: float = 1.0, plan: Optional[QkPlan] = None,
-                 mode: Union[str, int] = "auto", stream=None):
+                 mode: Union[str, int] = "auto", stream=None, k_scale=None):
         torch = _torch()
         B, C, Hq, Hkv, D, kdt = _check_qk(q, K, scores)
+        ks = _qk_scale(k_scale, kdt, Hkv, q.device)
         if scores is None:
             scores = torch.empty((B, C, Hq), dtype=torch.float32, device=q.device)
         if plan is None:
@@ -610,10 +638,15 @@ class BoundQk:
             plan = qk_make_plan(B, C, Hq, Hkv, D, kdt, mode, cu_count=cu)
         if stream is None:
             stream = torch.cuda.current_stream(q.device)
-        self.q, self.K, self.scores, self.plan = q, K, scores, plan
-        self._fn = load().gqa_qk_decode_plan
-        self._args = (q.data_ptr(), K.data_ptr(), scores.data_ptr(), B, C, Hq, Hkv, D, DTYPES[kdt],
-                      ctypes.c_float(scale), ctypes.byref(plan), stream.cuda_stream)
+        self.q, self.K, self.scores, self.plan, self.k_scale = q, K, scores, plan, ks
+        if kdt == "fp8":
+            self._fn = load().gqa_qk_fp8_decode_plan
+            self._args = (q.data_ptr(), K.data_ptr(), ks.data_ptr() if ks is not None else None, scores.data_ptr(),
+                          B, C, Hq, Hkv, D, ctypes.c_float(scale), ctypes.byref(plan), stream.cuda_stream)
+        else:
+            self._fn = load().gqa_qk_decode_plan
+            self._args = (q.data_ptr(), K.data_ptr(), scores.data_ptr(), B, C, Hq, Hkv, D, DTYPES[kdt],
+                          ctypes.c_float(scale), ctypes.byref(plan), stream.cuda_stream)
 
     def __call__(self):
         rc = self._fn(*self._args)
@@ -623,5 +656,5 @@ class BoundQk:
 
 
 def bind_qk(q, K, scores=None, scale: float = 1.0, plan: Optional[QkPlan] = None, mode: Union[str, int] = "auto",
-            stream=None) -> BoundQk:
-    return BoundQk(q, K, scores=scores, scale=scale, plan=plan, mode=mode, stream=stream)
+            stream=None, k_scale=None) -> BoundQk:
+    return BoundQk(q, K, scores=scores, scale=scale, plan=plan, mode=mode, stream=stream, k_scale=k_scale)

@@ -21,9 +21,10 @@ int qk_plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int k
     const int resolved = gqa_av_resolve_mode(Hq, Hkv, mode);
     if (resolved < 0) return -resolved;
     if (!plan) return fail(GQA_AV_ERR_INVALID_ARG, "plan is NULL");
-    if (k_dtype == GQA_AV_FP8_E4M3) return fail(GQA_AV_ERR_UNSUPPORTED, "score step: K is fp32, fp16 or bf16");
     if (D % 32 != 0 || D > 256)
         return fail(GQA_AV_ERR_UNSUPPORTED, "score step: D=%lld must be a multiple of 32 and at most 256", (long long)D);
+    if (k_dtype == GQA_AV_FP8_E4M3 && D % 64 != 0)
+        return fail(GQA_AV_ERR_UNSUPPORTED, "score step: fp8 K needs D a multiple of 64 (D=%lld)", (long long)D);
     const int es = elem_bytes(k_dtype);
     const int64_t G = Hq / Hkv;
     const int64_t krow = Hkv * D * es;
@@ -83,7 +84,7 @@ int qk_plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int k
 
     std::memset(plan, 0, sizeof *plan);
     plan->mode = resolved;
-    // The 16-bit matrix path for bf16 and fp16 K, the fp32 one for fp32 K.
+    // The 16-bit matrix path for bf16, fp16 and fp8 K, the fp32 one for fp32 K.
     plan->engine = k_dtype == GQA_AV_F32 ? GQA_AV_ENGINE_MFMA : GQA_AV_ENGINE_MFMA_BF16;
     plan->heads_per_tile = hpt;
     plan->subgroups = nsg;
@@ -95,7 +96,8 @@ int qk_plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int k
 }
 
 int qk_run(const float* q, const void* K, float* scores, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
-           int64_t D, int k_dtype, float scale, const gqa_qk_plan* plan, void* stream) {
+           int64_t D, int k_dtype, float scale, const gqa_qk_plan* plan, void* stream,
+           const float* k_scale = nullptr) {
     if (!plan) return fail(GQA_AV_ERR_INVALID_ARG, "plan is NULL");
     gqa_qk_plan check;
     int rc = qk_plan_impl(B, C, Hq, Hkv, D, k_dtype, plan->mode, plan->rows_per_block, kDefaultCUs,
@@ -111,12 +113,15 @@ int qk_run(const float* q, const void* K, float* scores, int64_t B, int64_t C, i
     if ((reinterpret_cast<uintptr_t>(q) & 3u) || (reinterpret_cast<uintptr_t>(scores) & 3u))
         return fail(GQA_AV_ERR_INVALID_ARG, "q and scores must be 4-byte aligned");
     if (reinterpret_cast<uintptr_t>(K) & 15u) return fail(GQA_AV_ERR_UNSUPPORTED, "K must be 16-byte aligned");
+    if (k_scale && (reinterpret_cast<uintptr_t>(k_scale) & 3u))
+        return fail(GQA_AV_ERR_INVALID_ARG, "k_scale must be 4-byte aligned");
 
     QkArgs a;
     a.q = q;
     a.K = static_cast<const uint8_t*>(K);
     a.scores = scores;
     a.scale = scale;
+    a.k_scale = k_scale;
     a.C = C;
     a.rows_per_block = static_cast<int32_t>(plan->rows_per_block);
     a.nchunk = static_cast<int32_t>(ceil_div(C, plan->rows_per_block));
@@ -139,6 +144,7 @@ int qk_run(const float* q, const void* K, float* scores, int64_t B, int64_t C, i
     switch (k_dtype) {
     case GQA_AV_F32: e = gqa_av_launch::qk<gqa_av::kF32>(D, nset, a, s); break;
     case GQA_AV_F16: e = gqa_av_launch::qk<gqa_av::kF16>(D, nset, a, s); break;
+    case GQA_AV_FP8_E4M3: e = gqa_av_launch::qk<gqa_av::kFP8>(D, nset, a, s); break;
     default: e = gqa_av_launch::qk<gqa_av::kBF16>(D, nset, a, s); break;
     }
     if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "score launch: %s", hipGetErrorString(e));
@@ -163,8 +169,12 @@ int gqa_qk_decode_plan(const float* q, const void* K, float* scores, int64_t B, 
     return qk_run(q, K, scores, B, C, Hq, Hkv, D, k_dtype, scale, plan, stream);
 }
 
-int gqa_qk_decode(const float* q, const void* K, float* scores, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
-                  int64_t D, int k_dtype, float scale, int mode, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int qk_auto(const float* q, const void* K, const float* k_scale, float* scores, int64_t B, int64_t C, int64_t Hq,
+            int64_t Hkv, int64_t D, int k_dtype, float scale, int mode, void* stream) {
     int rc = check_sizes(B, C, Hq, Hkv, D, k_dtype);
     if (rc != GQA_AV_OK) return rc;
     int dev = 0;
@@ -176,7 +186,27 @@ int gqa_qk_decode(const float* q, const void* K, float* scores, int64_t B, int64
     gqa_qk_plan plan;
     rc = qk_plan_impl(B, C, Hq, Hkv, D, k_dtype, mode, 0, cus, 0, &plan);
     if (rc != GQA_AV_OK) return rc;
-    return qk_run(q, K, scores, B, C, Hq, Hkv, D, k_dtype, scale, &plan, stream);
+    return qk_run(q, K, scores, B, C, Hq, Hkv, D, k_dtype, scale, &plan, stream, k_scale);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_qk_decode(const float* q, const void* K, float* scores, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
+                  int64_t D, int k_dtype, float scale, int mode, void* stream) {
+    return qk_auto(q, K, nullptr, scores, B, C, Hq, Hkv, D, k_dtype, scale, mode, stream);
+}
+
+int gqa_qk_fp8_decode(const float* q, const void* K, const float* k_scale, float* scores, int64_t B, int64_t C,
+                      int64_t Hq, int64_t Hkv, int64_t D, float scale, int mode, void* stream) {
+    return qk_auto(q, K, k_scale, scores, B, C, Hq, Hkv, D, GQA_AV_FP8_E4M3, scale, mode, stream);
+}
+
+int gqa_qk_fp8_decode_plan(const float* q, const void* K, const float* k_scale, float* scores, int64_t B,
+                           int64_t C, int64_t Hq, int64_t Hkv, int64_t D, float scale, const gqa_qk_plan* plan,
+                           void* stream) {
+    return qk_run(q, K, scores, B, C, Hq, Hkv, D, GQA_AV_FP8_E4M3, scale, plan, stream, k_scale);
 }
 
 }  // extern "C"

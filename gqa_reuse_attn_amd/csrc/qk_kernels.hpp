@@ -24,7 +24,12 @@
 //    and what the split drops is below 2^-33 of that head's largest q value
 //    (2^-38 of it near fp16's subnormal range), far under the fp32 rounding of
 //    the sums. The head's result column is multiplied by scale * 2^-e;
-//  * fp32 K: K as fp32 and v_mfma_f32_16x16x4_f32.
+//  * fp32 K: K as fp32 and v_mfma_f32_16x16x4_f32;
+//  * fp8 K (OCP FP8 E4M3, a float32 scale per KV head): every E4M3 value is a
+//    bfloat16 value, so each 16-byte piece of 16 fp8 values is widened exactly
+//    (v_cvt_pk_f32_fp8, then the upper half of each fp32) into two bf16
+//    pieces on its way into LDS, and the bf16 path runs from there; the KV
+//    head's scale joins the score scale on the head's result column.
 // The A operand wants lane 16 g + m to hold row m's d-range
 // [32 blk + 8 g, 32 blk + 8 g + 8). Loaded that way, one 64-lane load would
 // touch 16 rows at 64 bytes each, a pattern that streams 25 % slower on
@@ -42,6 +47,9 @@
 #ifndef GQA_QK_BLOCKS
 #define GQA_QK_BLOCKS 1   // 16-row blocks per wave and buffer (two buffers in flight); 2 and 4 measured slower
 #endif
+#ifndef GQA_QK_BLOCKS_FP8
+#define GQA_QK_BLOCKS_FP8 2   // fp8 K: half the bytes per block, so twice the blocks per step
+#endif
 
 namespace gqa_av {
 
@@ -58,8 +66,20 @@ struct QkArgs {
     int32_t nsg;             // head sub-groups per KV head (reuse)
     int32_t ht;              // adjacent KV heads per tile (reuse; 1 for per-head)
     int32_t vec4;            // 1: every tile's score run is whole rows of 16-byte groups, 16-byte aligned
+    const float* k_scale;    // fp8 K: [Hkv] scales, or NULL for 1
     uint32_t nblocks;
 };
+
+// Four OCP FP8 E4M3 values (one word, byte 0 first) as four bfloat16 values in
+// two words (low half first). Exact: an E4M3 value has at most 4 significant
+// bits, so its fp32 form ends in 16 zero bits.
+__device__ inline void fp8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+    lo = (__float_as_uint(a.x) >> 16) | (__float_as_uint(a.y) & 0xffff0000u);
+    hi = (__float_as_uint(b.x) >> 16) | (__float_as_uint(b.y) & 0xffff0000u);
+}
 
 // KDT: element type of K; NBLK = D / 32; NSET sets of 16 heads per tile; HT
 // adjacent KV heads per tile (1, 2 or 4).
@@ -67,15 +87,18 @@ template <int KDT, int NBLK, int NSET, int HT>
 __global__ __launch_bounds__(kThreads) void qk_scores(QkArgs a) {
     static_assert(HT == 1 || HT == 2 || HT == 4, "KV heads per tile must divide the waves");
     constexpr int WPH = kWaves / HT;                 // waves per KV head
-    constexpr int ES = esize<KDT>();
+    constexpr bool FP8 = KDT == kFP8;
+    constexpr int ES = esize<KDT>();                 // bytes of a K element in memory
+    constexpr int ESL = FP8 ? 2 : ES;                // and in LDS (fp8 widened to bf16)
     constexpr int D = 32 * NBLK;
     constexpr int PIECES = KDT == kF32 ? 2 : 1;      // 16-byte operand pieces per lane and block of 32 d
-    constexpr bool BF16 = KDT == kBF16;
+    constexpr bool BF16 = KDT == kBF16 || FP8;
     constexpr bool F16 = KDT == kF16;
     constexpr bool SPLIT = BF16 || F16;              // three 16-bit q terms on the 16x16x32 instruction
-    constexpr int NP = D * ES / 16;                  // 16-byte pieces per row (a multiple of 4)
+    constexpr int NP = D * ES / 16;                  // 16-byte pieces per row in memory
+    static_assert(NP % 4 == 0, "whole 64-lane loads per 16-row block");
     constexpr int NLD = NP / 4;                      // 64-lane loads per 16-row block
-    constexpr int RBP = D * ES + 16;                 // padded LDS row
+    constexpr int RBP = D * ESL + 16;                // padded LDS row
     __shared__ __align__(16) uint8_t stage[kWaves * 16 * RBP];
 
     // Logical tile order, fastest first: head sub-group (or the head's place in
@@ -115,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void qk_scores(QkArgs a) {
     for (int i = 0; i < NLD; ++i) {
         const int f = 64 * i + lane;
         koff[i] = (f / NP) * krow + kvl * D * ES + (f % NP) * 16;
-        soff[i] = (f / NP) * RBP + (f % NP) * 16;
+        soff[i] = (f / NP) * RBP + (f % NP) * 16 * (ESL / ES);
     }
     typedef __attribute__((address_space(3))) uint8_t lds_u8;
     lds_u8* const region = (lds_u8*)stage + wave * 16 * RBP;
@@ -127,12 +150,13 @@ __global__ __launch_bounds__(kThreads) void qk_scores(QkArgs a) {
     // (one contiguous run per row when nsg = 1), VE of them per lane: 4 (16-byte
     // stores) when every run is 16-byte aligned (a.vec4, set by the host),
     // else 1. Masked MI355X stores are not free, so a step issues only the
-    // rounds that hold entries (one round per set of 16 heads for VE = 4).
+    // rounds that hold entries: (R / 4) W / (64 VE) rounded up.
     // Rows past the chunk fall outside the score resource, which ends after the
     // chunk's last row of the tile's heads; lanes past the tile get an offset
     // beyond it. Every offset, plus the step's row offset, stays below 2^30
     // (the plan keeps a chunk's scores under it).
-    constexpr int R = 16 * WPH * GQA_QK_BLOCKS;      // rows per step
+    constexpr int UB = FP8 ? GQA_QK_BLOCKS_FP8 : GQA_QK_BLOCKS;   // 16-row blocks per wave and buffer
+    constexpr int R = 16 * WPH * UB;                 // rows per step
     constexpr int WMAX = HT * 16 * NSET;             // tile columns at most
     constexpr int OP = WMAX + 4;                     // LDS tile pitch in floats (4 spare columns)
     constexpr int NSR = R / kWaves * WMAX / 64;      // 4-byte store rounds per wave and step at most
@@ -141,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void qk_scores(QkArgs a) {
     const int W = HT * nq;
     const int VE = a.vec4 ? 4 : 1;
     const int WQ = W / VE;                           // lanes per tile row
-    const int nsr = a.vec4 ? NSET : (R / kWaves * W + 63) / 64;   // store rounds per step
+    const int nsr = (R / kWaves * W + 64 * VE - 1) / (64 * VE);   // store rounds per step (<= NSR)
     const int srow = a.Hq * 4;
     const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
         a.scores + (static_cast<size_t>(b) * a.C + r0) * a.Hq + q_tile, 0,
@@ -180,8 +204,9 @@ __global__ __launch_bounds__(kThreads) void qk_scores(QkArgs a) {
     // values sit in lanes m, m + 16, m + 32 and m + 48; its result column in
     // the same lanes.
     float out_scale[NSET];
+    const float kv_scale = FP8 && a.k_scale ? a.k_scale[kv] : 1.0f;
 #pragma unroll
-    for (int s = 0; s < NSET; ++s) out_scale[s] = a.scale;
+    for (int s = 0; s < NSET; ++s) out_scale[s] = a.scale * kv_scale;
     if constexpr (F16) {
 #pragma unroll
         for (int s = 0; s < NSET; ++s) {
@@ -242,7 +267,6 @@ __global__ __launch_bounds__(kThreads) void qk_scores(QkArgs a) {
         }
     }
 
-    constexpr int UB = GQA_QK_BLOCKS;                // 16-row blocks per wave and buffer
     struct Buf {
         u32x4 raw[UB][NLD];
     };
@@ -262,8 +286,18 @@ __global__ __launch_bounds__(kThreads) void qk_scores(QkArgs a) {
         // wave's LDS operations execute in order).
         asm volatile("" ::: "memory");
 #pragma unroll
-        for (int i = 0; i < NLD; ++i)
-            *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(region + soff[i]) = bfin[i];
+        for (int i = 0; i < NLD; ++i) {
+            typedef __attribute__((address_space(3))) u32x4 lds_u4;
+            if constexpr (FP8) {
+                uint32_t w[8];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) fp8x4_to_bf16x4(bfin[i][k], w[2 * k], w[2 * k + 1]);
+                *reinterpret_cast<lds_u4*>(region + soff[i]) = u32x4{w[0], w[1], w[2], w[3]};
+                *reinterpret_cast<lds_u4*>(region + soff[i] + 16) = u32x4{w[4], w[5], w[6], w[7]};
+            } else {
+                *reinterpret_cast<lds_u4*>(region + soff[i]) = bfin[i];
+            }
+        }
         asm volatile("" ::: "memory");
         struct {
             u32x4 raw[NBLK][PIECES];
@@ -273,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void qk_scores(QkArgs a) {
 #pragma unroll
             for (int p = 0; p < PIECES; ++p)
                 bf.raw[blk][p] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-                    region + m * RBP + (32 * blk + 8 * g) * ES + 16 * p);
+                    region + m * RBP + (32 * blk + 8 * g) * ESL + 16 * p);
         asm volatile("" ::: "memory");
         // Independent accumulators keep consecutive MFMAs off one dependency chain.
         constexpr int NACC = SPLIT ? 3 : 4;
@@ -315,7 +349,7 @@ __global__ __launch_bounds__(kThreads) void qk_scores(QkArgs a) {
             }
         }
         // Into the step's LDS tile: row 16 (j - first block of the step) + 4 g + i.
-        float* const tile = otile[tb] + (16 * (j - st * GQA_QK_BLOCKS * WPH) + 4 * g) * OP;
+        float* const tile = otile[tb] + (16 * (j - st * UB * WPH) + 4 * g) * OP;
 #pragma unroll
         for (int s = 0; s < NSET; ++s) {
             f32x4 sum = acc[0][s];
@@ -338,10 +372,11 @@ __global__ __launch_bounds__(kThreads) void qk_scores(QkArgs a) {
         __syncthreads();
         if (a.vec4) {
 #pragma unroll
-            for (int k = 0; k < NSET; ++k)
-                __builtin_amdgcn_raw_buffer_store_b128(
-                    __builtin_bit_cast(u32x4, *reinterpret_cast<const f32x4*>(&otile[tb][st_lds[k]])), sres,
-                    st_off[k], st * R * srow, 0);
+            for (int k = 0; k < NSR; ++k)
+                if (k < nsr)
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        __builtin_bit_cast(u32x4, *reinterpret_cast<const f32x4*>(&otile[tb][st_lds[k]])), sres,
+                        st_off[k], st * R * srow, 0);
         } else {
 #pragma unroll
             for (int k = 0; k < NSR; ++k)

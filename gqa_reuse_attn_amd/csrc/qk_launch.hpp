@@ -20,11 +20,15 @@ hipError_t launch_qk_ht(const gqa_av::QkArgs& a, hipStream_t s) {
 
 template <int KDT, int NBLK>
 hipError_t launch_qk_nset(int nset, const gqa_av::QkArgs& a, hipStream_t s) {
-    if (nset == 1) return launch_qk_ht<KDT, NBLK, 1>(a, s);
-    if constexpr (NBLK <= 4) {
-        if (nset == 2) return launch_qk_ht<KDT, NBLK, 2>(a, s);
+    if constexpr (KDT == gqa_av::kFP8 && NBLK % 2 != 0) {
+        return hipErrorInvalidValue;                 // fp8 K: D a multiple of 64 (the plan checks it)
+    } else {
+        if (nset == 1) return launch_qk_ht<KDT, NBLK, 1>(a, s);
+        if constexpr (NBLK <= 4) {
+            if (nset == 2) return launch_qk_ht<KDT, NBLK, 2>(a, s);
+        }
+        return hipErrorInvalidValue;
     }
-    return hipErrorInvalidValue;
 }
 
 template <int KDT>

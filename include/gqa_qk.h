@@ -19,7 +19,8 @@
  *
  * Memory layout: dense, row-major, no padding or strides.
  *   q       [B][Hq][D]      float32
- *   K       [B][C][Hkv][D]  float32, float16 or bfloat16 (k_dtype, a gqa_av_dtype)
+ *   K       [B][C][Hkv][D]  float32, float16, bfloat16 or OCP FP8 E4M3 bytes
+ *                           (k_dtype, a gqa_av_dtype)
  *   scores  [B][C][Hq]      float32, fully overwritten
  * All three are DEVICE pointers on the current HIP device, owned by the caller.
  * Accumulation is in float32: with bf16 K every product q * K is exact (q is
@@ -29,8 +30,15 @@
  * fp32 K the products are fp32 fused multiply-adds. The scale multiplies the
  * sum once at the end.
  *
- * Requirements of this build: D a multiple of 32 and at most 256, K 16-byte
- * aligned, q and scores 4-byte aligned; otherwise GQA_AV_ERR_UNSUPPORTED (or
+ * fp8 K (a compressed cache, not on the page): each element is decode(byte) *
+ * k_scale[kv_h], decode being OCP FP8 E4M3 (bias 7, no infinities,
+ * S.1111.111 NaN) and k_scale one float32 per KV head (gqa_qk_fp8_decode; the
+ * plain entry points take fp8 K with all scales 1). Every E4M3 value is a
+ * bfloat16 value, so K is widened exactly and the products are exact as for
+ * bf16 K; k_scale joins the scale on each head's sum.
+ *
+ * Requirements of this build: D a multiple of 32 (of 64 for fp8 K) and at
+ * most 256, K 16-byte aligned, q, scores and k_scale 4-byte aligned; otherwise GQA_AV_ERR_UNSUPPORTED (or
  * GQA_AV_ERR_INVALID_ARG for bad sizes, as in gqa_av.h). No workspace: the
  * context is never split.
  *
@@ -59,7 +67,7 @@ typedef struct gqa_qk_hint {
 /* Launch plan of the score step. */
 typedef struct gqa_qk_plan {
     int32_t mode;            /* resolved: GQA_AV_PER_HEAD or GQA_AV_REUSE */
-    int32_t engine;          /* GQA_AV_ENGINE_MFMA_BF16 (16-bit matrix path: bf16 and fp16 K) or GQA_AV_ENGINE_MFMA (fp32 K) */
+    int32_t engine;          /* GQA_AV_ENGINE_MFMA_BF16 (16-bit matrix path: bf16, fp16 and fp8 K) or GQA_AV_ENGINE_MFMA (fp32 K) */
     int32_t heads_per_tile;  /* query heads per KV head in one workgroup: 16 or 32 (reuse), 1 (per-head) */
     int32_t subgroups;       /* workgroups along the heads of one KV head (reuse: ceil(G / heads_per_tile)) */
     int64_t rows_per_block;  /* context rows per workgroup (a multiple of 64) */
@@ -84,6 +92,17 @@ int gqa_qk_decode(const float *q, const void *K, float *scores,
 int gqa_qk_decode_plan(const float *q, const void *K, float *scores,
                        int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D,
                        int k_dtype, float scale, const gqa_qk_plan *plan, void *stream);
+
+/* fp8 K with per-KV-head scales: K holds [B][C][Hkv][D] OCP FP8 E4M3 bytes
+ * and k_scale [Hkv] float32 on the device (NULL: all 1); the rest as
+ * gqa_qk_decode. The _plan form takes a plan made with k_dtype
+ * GQA_AV_FP8_E4M3. */
+int gqa_qk_fp8_decode(const float *q, const void *K, const float *k_scale, float *scores,
+                      int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D,
+                      float scale, int mode, void *stream);
+int gqa_qk_fp8_decode_plan(const float *q, const void *K, const float *k_scale, float *scores,
+                           int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D,
+                           float scale, const gqa_qk_plan *plan, void *stream);
 
 #ifdef __cplusplus
 }

@@ -1,8 +1,8 @@
 """GPU parity at the full large-batch size (B = 64, C = 8192, Hq = 64, Hkv = 8,
 D = 128, bf16) in the launch configurations the bench times, for the products
 whose other tests cut that workload to 8 sequences: the fused softmax product,
-the score step, paged V (16-row pages, shuffled, full lengths) and fp8 V
-(per-KV-head scales). The GPU computes all 64 sequences with the plan the
+the score step (bf16 and fp8 K), paged V (16-row pages, shuffled, full
+lengths) and fp8 V (per-KV-head scales). The GPU computes all 64 sequences with the plan the
 bench uses; sequences are independent, so the oracle checks a sample of them
 one by one, with the same gates as the per-product tests. All tests need an
 MI355X and are marked ``gpu``.
@@ -110,3 +110,17 @@ def test_full_size_qk(oracle_lib):
     for b in SAMPLE:
         ref = oracle_lib.qk(q[b:b + 1], K[b:b + 1], W.v_dtype, scale)
         assert_parity(out[b:b + 1], ref, W.v_dtype, W.D, f"full-size qk b={b}")
+
+
+def test_full_size_qk_fp8(oracle_lib):
+    from tests.test_gpu_qk import _quantize_k
+    q, K = make_qk_random(W.B, W.C, W.Hq, W.Hkv, W.D, W.v_dtype, seed=0)
+    K8, ks = _quantize_k(K)
+    scale = W.D ** -0.5
+    plan = ga.qk_make_plan(W.B, W.C, W.Hq, W.Hkv, W.D, "fp8", cu_count=_cus())
+    _say(f"[full] qk fp8 plan={plan.as_dict()}")
+    out = ga.gqa_qk_decode(q.to(DEV), K8.to(DEV), scale=scale, plan=plan, k_scale=ks.to(DEV))
+    out = out.cpu().numpy().astype(np.float64)
+    for b in SAMPLE:
+        ref = oracle_lib.qk_fp8(q[b:b + 1], K8[b:b + 1], ks, scale)
+        assert_parity(out[b:b + 1], ref, "bf16", W.D, f"full-size qk fp8 b={b}")

@@ -182,3 +182,94 @@ def test_qk_then_av_matches_attention(oracle_lib):
     ref_attn = (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
     ref = oracle_lib.full(torch.from_numpy(ref_attn), V, "bf16")
     assert_parity(out.cpu().numpy().astype(np.float64), ref, "bf16", C, "qk -> softmax -> av")
+
+
+# ---- fp8 K (OCP FP8 E4M3 with a float32 scale per KV head) -------------------
+
+def _quantize_k(K: torch.Tensor):
+    """Per-KV-head scale max|K| / 448 and the E4M3 bytes of K / scale (torch's
+    round-to-nearest cast): input preparation, not part of the step."""
+    Kf = K.float()
+    amax = Kf.abs().amax(dim=(0, 1, 3)).clamp_min(1e-30)
+    scale = (amax / 448.0).float().contiguous()
+    return (Kf / scale.view(1, 1, -1, 1)).to(torch.float8_e4m3fn).contiguous(), scale
+
+
+def _run_fp8(q, K8, k_scale, scale, plan=None, mode="auto"):
+    s = ga.gqa_qk_decode(q.to(DEV), K8.to(DEV), scale=scale, mode=mode, plan=plan,
+                         k_scale=None if k_scale is None else k_scale.to(DEV))
+    torch.cuda.synchronize()
+    return s.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("wname", [n for n, w in WORKLOADS.items() if w.D % 64 == 0])
+def test_qk_fp8_workloads(wname, oracle_lib):
+    """The workload shapes with D a multiple of 64, K quantized per KV head (the
+    large batch cut to 8 sequences; the full size is in test_gpu_full_size),
+    reuse and per-head."""
+    w = WORKLOADS[wname]
+    if w.B > 8:
+        w = w.replace(B=8)
+    _say(f"[qk fp8] {w.name}")
+    q, K = make_qk_random(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, seed=3)
+    K8, ks = _quantize_k(K)
+    scale = w.D ** -0.5
+    ref = oracle_lib.qk_fp8(q, K8, ks, scale)
+    for mode in ("auto", "per_head"):
+        assert_parity(_run_fp8(q, K8, ks, scale, mode=mode), ref, "bf16", w.D, f"qk fp8 {w.name} {mode}")
+
+
+def _qk_fp8_cases():
+    cases, k = [], 0
+    for G in (1, 2, 3, 4, 8, 16, 17):
+        for D in (64, 128, 192, 256):
+            for C in (1, 63, 65, 300):
+                if (G + D // 64 + C) % 3:
+                    continue
+                cases.append((1 + k % 2, C, G * (1, 2, 4)[k % 3], (1, 2, 4)[k % 3], D, (0, 64, 128)[k % 3]))
+                k += 1
+    return cases
+
+
+@pytest.mark.parametrize("B,C,Hq,Hkv,D,rows", _qk_fp8_cases())
+def test_qk_fp8_sweep(B, C, Hq, Hkv, D, rows, oracle_lib):
+    """Small shapes: G 1..17, D 64..256, ragged C, forced row blocks, 1/2/4 KV
+    heads per workgroup, with and without scales; the gate, the accumulation
+    bound and the elementwise bound 2 D 2^-24 scale sum_d |q K|."""
+    q, K = make_qk_random(B, C, Hq, Hkv, D, "f32", seed=B * 1000 + C + D + 7)
+    K8, ks = _quantize_k(K)
+    scale = 0.375
+    modes = ("auto", "per_head") if Hq // Hkv >= 2 else ("auto",)
+    plans = [ga.qk_make_plan(B, C, Hq, Hkv, D, "fp8", mode, rows_per_block=rows) for mode in modes]
+    plans += [ga.qk_make_plan(B, C, Hq, Hkv, D, "fp8", "reuse", rows_per_block=rows, kv_tile=ht)
+              for ht in (2, 4) if Hq // Hkv >= 2 and Hkv % ht == 0]
+    for sc in (ks, None):
+        ref = oracle_lib.qk_fp8(q, K8, sc, scale)
+        kd = K8.float() * (sc.view(1, 1, -1, 1) if sc is not None else 1.0)
+        bound = 2 * D * U32 * scale * abs_sum_qk(q, kd) + 1e-30
+        for plan in plans:
+            out = _run_fp8(q, K8, sc, scale, plan=plan)
+            label = f"qk fp8 {(B, C, Hq, Hkv, D)} scale={sc is not None} plan={plan.as_dict()}"
+            assert_parity(out, ref, "bf16", D, label)
+            assert (np.abs(out - ref) <= bound).all(), f"elementwise bound: {label}"
+
+
+def test_qk_fp8_equals_bf16_on_widened_k():
+    """With unit scales, fp8 K gives the scores of bf16 K holding the same
+    values, bit for bit (the kernel widens K exactly to bf16 before the same
+    products), on every plan shape; every non-NaN E4M3 byte appears in K."""
+    B, C, Hq, Hkv, D = 2, 700, 32, 4, 128
+    g = torch.Generator().manual_seed(17)
+    vals = torch.tensor([b for b in range(256) if (b & 0x7F) != 0x7F], dtype=torch.uint8)
+    raw = vals[torch.randint(0, vals.numel(), (B, C, Hkv, D), generator=g)]
+    raw[0, 0, 0, :] = vals[:D]
+    raw[0, 1, 0, :vals.numel() - D] = vals[D:]
+    K8 = raw.view(torch.float8_e4m3fn)
+    K16 = K8.to(torch.bfloat16)
+    q, _ = make_qk_random(B, C, Hq, Hkv, D, "f32", seed=18)
+    for mode, ht in (("auto", 0), ("per_head", 0), ("reuse", 1), ("reuse", 2)):
+        p8 = ga.qk_make_plan(B, C, Hq, Hkv, D, "fp8", mode, kv_tile=ht)
+        p16 = ga.qk_make_plan(B, C, Hq, Hkv, D, "bf16", mode, kv_tile=ht)
+        a = _run_fp8(q, K8, None, 0.25, plan=p8)
+        b = _run(q, K16, 0.25, plan=p16)
+        assert np.array_equal(a, b), (mode, ht)

@@ -533,8 +533,10 @@ def test_fp8_plans():
     with pytest.raises(ga.GqaAvError) as e:
         ga.make_plan(2, 1000, 16, 2, 127, "fp8")            # odd D: no 2-byte lane load fits
     assert e.value.name == "UNSUPPORTED"
+    pk = ga.qk_make_plan(2, 1000, 16, 2, 128, "fp8")           # fp8 K in the score step: the 16-bit matrix path
+    assert pk.engine == 3 and pk.k_bytes_read == 2 * 1000 * 2 * 128
     with pytest.raises(ga.GqaAvError) as e:
-        ga.qk_make_plan(2, 1000, 16, 2, 128, "fp8")
+        ga.qk_make_plan(2, 1000, 16, 2, 96, "fp8")            # fp8 K needs D % 64 == 0
     assert e.value.name == "UNSUPPORTED"
 
 

@@ -327,6 +327,7 @@ def test_valu_engine_plan_bounds(B, C, Hq, Hkv, D, dt):
 # ---- decode score step -------------------------------------------------------
 
 QK_BLOCKS = 1   # 16-row blocks per wave and buffer in the score kernel
+QK_BLOCKS_FP8 = 2   # the same for fp8 K
 OUT_OF_RANGE = 0x40000000   # kOutOfRange: a buffer offset past every resource
 
 
@@ -397,7 +398,7 @@ def _check_qk_plan(p, B, C, Hq, Hkv, D, dt, UB=QK_BLOCKS, vec4=False):
         srec = (nrows - 1) * srow + 4 * ((HT - 1) * G + nq)
         assert sbase + srec <= 4 * B * C * Hq and srec <= 2 ** 30
         VE = 4 if vec4 else 1
-        nsr = (1 if per_head else NSET) if vec4 else -(-(R // 4 * W) // 64)
+        nsr = -(-(R // 4 * W) // (64 * VE))
         assert nsr <= NSR
         for step in range(nsteps):
             tile = {}
@@ -441,7 +442,8 @@ def _check_qk_plan(p, B, C, Hq, Hkv, D, dt, UB=QK_BLOCKS, vec4=False):
 @pytest.mark.parametrize("B,C,Hq,Hkv,D,dt", [
     (2, 300, 8, 2, 64, "bf16"), (1, 65, 16, 1, 128, "f16"), (2, 129, 6, 3, 32, "f32"), (1, 1, 4, 4, 96, "bf16"),
     (2, 500, 64, 2, 256, "bf16"), (1, 1000, 40, 1, 128, "f16"), (3, 77, 24, 8, 96, "f32"), (1, 257, 68, 2, 160, "bf16"),
-    (2, 700, 32, 4, 128, "bf16"), (1, 333, 24, 8, 96, "f16")])
+    (2, 700, 32, 4, 128, "bf16"), (1, 333, 24, 8, 96, "f16"), (2, 300, 16, 8, 128, "fp8"), (1, 129, 64, 1, 64, "fp8"),
+    (2, 77, 12, 2, 256, "fp8"), (2, 300, 16, 1, 128, "fp8"), (1, 200, 64, 2, 64, "bf16")])
 def test_qk_plan_bounds(B, C, Hq, Hkv, D, dt):
     modes = ("auto", "per_head") if Hq // Hkv >= 2 else ("auto",)
     for mode in modes:
@@ -454,26 +456,32 @@ def test_qk_plan_bounds(B, C, Hq, Hkv, D, dt):
                 # 16-byte aligned), 4-byte stores always possible
                 v4 = p.mode == 1 and p.subgroups == 1 and (p.kv_heads_per_tile * (Hq // Hkv)) % 4 == 0 and Hq % 4 == 0
                 for vec4 in ((False, True) if v4 else (False,)):
-                    _check_qk_plan(p, B, C, Hq, Hkv, D, dt, vec4=vec4)
+                    _check_qk_plan(p, B, C, Hq, Hkv, D, dt, UB=QK_BLOCKS_FP8 if dt == "fp8" else QK_BLOCKS, vec4=vec4)
 
 
-@pytest.mark.parametrize("D,dt", [(32, "bf16"), (96, "f16"), (128, "bf16"), (160, "f32"), (256, "f32"), (224, "f16")])
+@pytest.mark.parametrize("D,dt", [(32, "bf16"), (96, "f16"), (128, "bf16"), (160, "f32"), (256, "f32"), (224, "f16"),
+                                  (64, "fp8"), (128, "fp8"), (192, "fp8"), (256, "fp8")])
 def test_qk_lds_relayout(D, dt):
     """The score kernel's LDS re-layout: every 16-byte piece of the 16-row block
-    is stored once inside the wave's region, and lane (m, g) reads back row m's
+    is stored once inside the wave's region (fp8: a 16-byte piece of 16 values
+    becomes two 16-byte bf16 pieces), and lane (m, g) reads back row m's
     d-range [32 blk + 8 g, +8) for each block of 32 d (16-row reads in
     distinct 16-byte bank groups)."""
     es = _esize(dt)
-    NP, RBP = D * es // 16, D * es + 16
+    esl = 2 if dt == "fp8" else es                       # LDS element size
+    NP, RBP = D * es // 16, D * esl + 16
+    assert NP % 4 == 0
     where = {}
     for i in range(NP // 4):
         for lane in range(64):
             f = 64 * i + lane
             row, piece = f // NP, f % NP
-            off = row * RBP + piece * 16
-            assert 0 <= off and off + 16 <= 16 * RBP and off not in where.values()
-            where[(row, piece)] = off
-    assert len(where) == 16 * NP
+            for half in range(esl // es):               # fp8: the widened piece's two halves
+                off = row * RBP + piece * 16 * (esl // es) + 16 * half
+                assert 0 <= off and off + 16 <= 16 * RBP and off not in where.values()
+                where[(row, piece * (esl // es) + half)] = off
+    assert len(where) == 16 * NP * (esl // es)
+    es = esl                                             # the operand reads see LDS elements
     pieces_per_op = 2 if dt == "f32" else 1
     for blk in range(D // 32):
         for pc in range(pieces_per_op):

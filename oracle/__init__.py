@@ -69,6 +69,9 @@ class Oracle:
         lib.gqa_fp8_oracle.restype = ip
         lib.gqa_qk_fp8_oracle.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_double, vp, ip]
         lib.gqa_qk_fp8_oracle.restype = ip
+        lib.gqa_qk_paged_oracle.argtypes = [vp, vp, vp, vp, ip, vp, i64, i64, i64, i64, i64, i64, i64, i64,
+                                            ctypes.c_double, vp, ip]
+        lib.gqa_qk_paged_oracle.restype = ip
         self.lib = lib
 
     @staticmethod
@@ -118,6 +121,35 @@ class Oracle:
         out = np.empty((B, C, Hq), dtype=np.float64)
         rc = self.lib.gqa_qk_fp8_oracle(qa.ctypes.data, k.ctypes.data, None if ks is None else ks.ctypes.data,
                                         B, C, Hq, Hkv, D, float(scale), out.ctypes.data, nthreads)
+        if rc != 0:
+            raise ValueError(f"oracle rejected the arguments (status {rc})")
+        return out
+
+    def qk_paged(self, q, pages, block_table, seq_lens, k_dtype: str, scale: float = 1.0, k_scale=None,
+                 C: Optional[int] = None, nthreads: int = 0) -> np.ndarray:
+        """scores[B, C, Hq] (float64) for q [B,Hq,D] fp32 over paged K: pages
+        [num_pages,P,Hkv,D] of k_dtype ("fp8": E4M3 bytes with k_scale [Hkv] or
+        None), block_table [B,max_pages] int32, seq_lens [B] int32; C is the
+        capacity (default max_pages * P). Rows at or past a sequence's length
+        are NaN."""
+        qa = np.ascontiguousarray(_as_numpy(q, np.float32))
+        if k_dtype == "fp8":
+            k, code = np.ascontiguousarray(_fp8_bytes(pages)), 3
+        else:
+            _, k = self._np_inputs(qa, pages, k_dtype)
+            code = DTYPE_CODE[k_dtype]
+        bt = np.ascontiguousarray(_as_numpy(block_table, np.int32), dtype=np.int32)
+        ln = np.ascontiguousarray(_as_numpy(seq_lens, np.int32), dtype=np.int32)
+        B, Hq, D = qa.shape
+        num_pages, P, Hkv, D2 = k.shape
+        assert D2 == D and bt.shape[0] == B and ln.shape == (B,)
+        max_pages = bt.shape[1]
+        C = max_pages * P if C is None else C
+        ks = None if k_scale is None else np.ascontiguousarray(_as_numpy(k_scale, np.float32))
+        out = np.empty((B, C, Hq), dtype=np.float64)
+        rc = self.lib.gqa_qk_paged_oracle(qa.ctypes.data, k.ctypes.data, bt.ctypes.data, ln.ctypes.data, code,
+                                          None if ks is None else ks.ctypes.data, B, C, Hq, Hkv, D, P, max_pages,
+                                          num_pages, float(scale), out.ctypes.data, nthreads)
         if rc != 0:
             raise ValueError(f"oracle rejected the arguments (status {rc})")
         return out

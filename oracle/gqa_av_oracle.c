@@ -66,7 +66,10 @@
  * row c % page_size of that page, pages being [page_size][Hkv][D] blocks of
  * one array. The weights (or scores) keep the dense [B][C][Hq] layout with C
  * the capacity, and only rows c < seq_lens[b] take part: the sums above run
- * over those rows (a sequence of length 0 gives zeros).
+ * over those rows (a sequence of length 0 gives zeros). Paged K in the score
+ * step uses the same layout and tables: the scores of rows c < seq_lens[b]
+ * follow the score definition with K's row c read from its page; rows at or
+ * past the length have no score (NaN here: the kernel leaves them unwritten).
  */
 #include <math.h>
 #include <pthread.h>
@@ -449,6 +452,60 @@ int gqa_qk_fp8_oracle(const float *q, const uint8_t *K, const float *k_scale,
 #endif
     for (int64_t i = 0; i < rows; ++i)
         orc_qk_fp8_row(q, K, k_scale, C, Hq, Hkv, D, i / C, i % C, scale, out + i * Hq);
+    (void)nthreads;
+    return ORC_OK;
+}
+
+/* Score step over paged K: out[B][C][Hq] in double, rows c < seq_lens[b] as
+ * the score definition with K row c from its page, other rows NaN. dtype as
+ * for K (0..2), or 3 for fp8 E4M3 bytes with k_scale [Hkv] (NULL: all 1).
+ * Rejects what gqa_av_paged_oracle rejects. */
+int gqa_qk_paged_oracle(const float *q, const void *pages, const int32_t *block_table, const int32_t *seq_lens,
+                        int dtype, const float *k_scale, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
+                        int64_t D, int64_t P, int64_t max_pages, int64_t num_pages, double scale, double *out,
+                        int nthreads)
+{
+    int rc = orc_check(dtype == 3 ? ORC_F32 : dtype, B, C, Hq, Hkv, D);
+    if (rc != ORC_OK) return rc;
+    if (P < 1 || max_pages < 0 || num_pages < 0 || C > max_pages * P) return ORC_BAD_ARG;
+    for (int64_t b = 0; b < B; ++b) {
+        const int64_t len = seq_lens[b];
+        if (len < 0 || len > C) return ORC_BAD_ARG;
+        for (int64_t c = 0; c < len; c += P) {
+            const int64_t page = block_table[b * max_pages + c / P];
+            if (page < 0 || page >= num_pages) return ORC_BAD_ARG;
+        }
+    }
+    pthread_once(&orc_f16_once, orc_f16_fill);
+    const int64_t G = Hq / Hkv;
+    const int64_t rows = B * C;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 64) num_threads(nthreads)
+#endif
+    for (int64_t i = 0; i < rows; ++i) {
+        const int64_t b = i / C, c = i % C;
+        double *o = out + i * Hq;
+        if (c >= seq_lens[b]) {
+            for (int64_t h = 0; h < Hq; ++h) o[h] = NAN;
+            continue;
+        }
+        const int64_t page = block_table[b * max_pages + c / P];
+        for (int64_t h = 0; h < Hq; ++h) {
+            const int64_t kvh = h / G;
+            const int64_t row = ((page * P + c % P) * Hkv + kvh) * D;
+            const float *qrow = q + (b * Hq + h) * D;
+            double dot = 0.0;
+            if (dtype == 3) {
+                const double ks = k_scale ? (double)k_scale[kvh] : 1.0;
+                const uint8_t *kr = (const uint8_t *)pages + row;
+                for (int64_t d = 0; d < D; ++d) dot += (double)qrow[d] * (orc_e4m3(kr[d]) * ks);
+            } else {
+                for (int64_t d = 0; d < D; ++d) dot += (double)qrow[d] * orc_load(pages, dtype, row + d);
+            }
+            o[h] = dot * scale;
+        }
+    }
     (void)nthreads;
     return ORC_OK;
 }

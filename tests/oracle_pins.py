@@ -74,6 +74,18 @@ fp8 V (OCP FP8 E4M3 bytes times a float32 scale per KV head):
   * fp8_scales        a power-of-two scale per KV head scales exactly that head's
                       group of outputs; one head's scale leaves the others alone.
 
+Paged K in the score step (the paged-V layout and tables):
+  * qk_paged_gather   the scores of rows below each length equal the dense
+                      score oracle on the sequence's gathered rows (all K
+                      types, fp8 with scales), bit for bit; rows past the
+                      length are NaN (no score).
+  * qk_paged_identity one page per sequence holding the dense K is the dense
+                      score oracle, bit for bit.
+  * qk_paged_tail     K rows at or past the length and unused pages change
+                      nothing.
+  * qk_paged_rejects  bad block-table entries, lengths and capacities are
+                      rejected.
+
 fp8 K in the score step (same bytes and per-KV-head scales):
   * qk_fp8_as_bf16    with unit scales the fp8 score oracle equals the bf16
                       score oracle on K widened by torch's float8 -> bfloat16
@@ -695,6 +707,85 @@ def pin_qk_fp8_scales(orc):
     assert not np.array_equal(o2, base)
 
 
+def _qk_paged_case(B, C, Hq, Hkv, D, P, dt, seed, lens):
+    """Dense K scattered into shuffled pages (spare pages filled with 7.0),
+    with the block table and lengths."""
+    q, K = make_qk_random(B, C, Hq, Hkv, D, "f32" if dt == "fp8" else dt, seed=seed)
+    if dt == "fp8":
+        g = torch.Generator().manual_seed(seed + 1)
+        K = torch.randint(0, 256, (B, C, Hkv, D), generator=g, dtype=torch.uint8)
+        K[(K & 0x7F) == 0x7F] = 0x3C
+    maxp = -(-C // P)
+    npg = B * maxp + 3
+    g = torch.Generator().manual_seed(seed + 2)
+    perm = torch.randperm(npg, generator=g)[:B * maxp].to(torch.int32).view(B, maxp).contiguous()
+    pages = torch.full((npg, P, Hkv, D), 7.0).to(K.dtype) if dt != "fp8" else \
+        torch.full((npg, P, Hkv, D), 0x48, dtype=torch.uint8)
+    for b in range(B):
+        for k in range(maxp):
+            rows = K[b, k * P:(k + 1) * P]
+            pages[int(perm[b, k]), :rows.shape[0]] = rows
+    return q, K, pages, perm, torch.tensor(lens, dtype=torch.int32)
+
+
+def pin_qk_paged_gather(orc):
+    for i, (dt, P) in enumerate([("bf16", 4), ("f16", 1), ("f32", 8), ("fp8", 2), ("bf16", 16)]):
+        B, C, Hq, Hkv, D = 3, 13, 6, 2, 16
+        lens = [13, 6, 0]
+        q, K, pages, bt, ln = _qk_paged_case(B, C, Hq, Hkv, D, P, dt, seed=1000 + i, lens=lens)
+        ks = torch.tensor([0.5, 4.0]) if dt == "fp8" else None
+        out = orc.qk_paged(q, pages, bt, ln, dt, 0.25, ks, C=C)
+        for b in range(B):
+            n = lens[b]
+            if n:
+                dense = orc.qk_fp8(q[b:b + 1], K[b:b + 1, :n], ks, 0.25) if dt == "fp8" else \
+                    orc.qk(q[b:b + 1], K[b:b + 1, :n], dt, 0.25)
+                assert np.array_equal(out[b:b + 1, :n], dense), f"paged scores != dense ({dt}, P={P}, b={b})"
+            assert np.isnan(out[b, n:]).all(), f"rows past the length must have no score ({dt}, b={b})"
+
+
+def pin_qk_paged_identity(orc):
+    for dt in ("bf16", "f32"):
+        q, K = make_qk_random(2, 9, 4, 2, 12, dt, seed=1010)
+        bt = torch.arange(2, dtype=torch.int32).view(2, 1)
+        out = orc.qk_paged(q, K, bt, torch.tensor([9, 9], dtype=torch.int32), dt, 0.5)
+        assert np.array_equal(out, orc.qk(q, K, dt, 0.5)), f"identity paging != dense ({dt})"
+
+
+def pin_qk_paged_tail(orc):
+    B, C, Hq, Hkv, D, P = 2, 11, 4, 2, 8, 4
+    lens = [7, 11]
+    q, K, pages, bt, ln = _qk_paged_case(B, C, Hq, Hkv, D, P, "bf16", seed=1020, lens=lens)
+    base = orc.qk_paged(q, pages, bt, ln, "bf16", 1.0, C=C)
+    p2 = pages.clone()
+    used = {int(bt[b, c // P]) for b in range(B) for c in range(lens[b])}
+    for pg in range(p2.shape[0]):
+        if pg not in used:
+            p2[pg] = -3.0
+    p2[int(bt[0, 7 // P]), 7 % P:] = 99.0                  # sequence 0's rows 7.. (past its length)
+    out = orc.qk_paged(q, p2, bt, ln, "bf16", 1.0, C=C)
+    same = (out == base) | (np.isnan(out) & np.isnan(base))
+    assert same.all(), "K past the length or in unused pages changed a score"
+
+
+def pin_qk_paged_rejects(orc):
+    q, K, pages, bt, ln = _qk_paged_case(2, 8, 4, 2, 8, 4, "bf16", seed=1030, lens=[8, 5])
+    npg = pages.shape[0]
+    for bad, args in (("page index", (bt.clone().fill_(npg), ln)), ("negative page", (bt.clone().fill_(-1), ln)),
+                      ("length", (bt, torch.tensor([9, 5], dtype=torch.int32))),
+                      ("negative length", (bt, torch.tensor([-1, 5], dtype=torch.int32)))):
+        try:
+            orc.qk_paged(q, pages, args[0], args[1], "bf16", 1.0, C=8)
+        except ValueError:
+            continue
+        raise AssertionError(f"paged score oracle accepted a bad {bad}")
+    try:
+        orc.qk_paged(q, pages, bt, ln, "bf16", 1.0, C=9)       # capacity above max_pages * P
+    except ValueError:
+        return
+    raise AssertionError("paged score oracle accepted C > max_pages * P")
+
+
 ALL_PINS = [pin_decode_table, pin_brute_force, pin_mha_einsum, pin_repeat_mha, pin_constant_v,
             pin_one_hot, pin_linearity, pin_permutation, pin_batch_independence, pin_points,
             pin_edges, pin_qk_brute_force, pin_qk_mha_einsum, pin_qk_repeat_mha, pin_qk_one_hot,
@@ -702,4 +793,5 @@ ALL_PINS = [pin_decode_table, pin_brute_force, pin_mha_einsum, pin_repeat_mha, p
             pin_sav_large, pin_sav_one_hot, pin_sav_uniform, pin_sav_two_rows, pin_sav_mask,
             pin_sav_repeat_mha, pin_sav_edges, pin_paged_gather, pin_paged_identity, pin_paged_ignores_tail,
             pin_paged_rejects, pin_fp8_decode, pin_fp8_as_bf16, pin_fp8_scales, pin_qk_fp8_as_bf16,
-            pin_qk_fp8_brute, pin_qk_fp8_scales]
+            pin_qk_fp8_brute, pin_qk_fp8_scales, pin_qk_paged_gather, pin_qk_paged_identity, pin_qk_paged_tail,
+            pin_qk_paged_rejects]

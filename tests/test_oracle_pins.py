@@ -82,6 +82,12 @@ PLANTS = [
      "out[h] = dot;\n    }\n}\n\nint gqa_qk_fp8_oracle"),
     ("qk_fp8_wrong_kv_head", "const uint8_t *krow = K + ((b * C + c) * Hkv + kvh) * D;",
      "const uint8_t *krow = K + ((b * C + c) * Hkv + (Hkv - 1 - kvh)) * D;"),
+    ("qk_paged_no_row_stride", "const int64_t page = block_table[b * max_pages + c / P];\n        for (int64_t h",
+     "const int64_t page = block_table[b + c / P];\n        for (int64_t h"),
+    ("qk_paged_reversed_in_page", "const int64_t row = ((page * P + c % P) * Hkv + kvh) * D;",
+     "const int64_t row = ((page * P + (P - 1 - c % P)) * Hkv + kvh) * D;"),
+    ("qk_paged_ignores_len", "if (c >= seq_lens[b]) {", "if (c >= C) {"),
+    ("qk_paged_fp8_no_scale", "dot += (double)qrow[d] * (orc_e4m3(kr[d]) * ks);", "dot += (double)qrow[d] * orc_e4m3(kr[d]);"),
     ("paged_bt_ignores_batch", "const int64_t page = bt[b * max_pages + c / P];",
      "const int64_t page = bt[0 * max_pages + c / P];"),
 ]

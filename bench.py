@@ -88,8 +88,8 @@ def parse():
     p.add_argument("--k-fp8", action="store_true",
                    help="qk with K quantized to OCP FP8 E4M3 with a scale per KV head (half the K bytes)")
     p.add_argument("--page-size", type=int, default=0,
-                   help="av / softmax over a paged V cache with this many rows per page (shuffled pages, full "
-                        "lengths); 0 = dense V")
+                   help="av / softmax over a paged V cache (qk: a paged K cache) with this many rows per page "
+                        "(shuffled pages, full lengths); 0 = dense")
     p.add_argument("--graph", action="store_true",
                    help="dense av / softmax: time the K whole calls as one captured HIP graph (no host launch "
                         "cost between calls) instead of K stream launches")
@@ -439,14 +439,32 @@ def bench_qk(args, w, dev, props):
         del Kf
     es = {"f32": 4, "fp8": 1}.get(kdt, 2)
     alg = w.B * w.C * w.Hkv * w.D * es + 4 * w.B * w.Hq * w.D + 4 * w.B * w.C * w.Hq
-    plan = ga.qk_make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, kdt, args.mode, cu_count=props.multi_processor_count)
+    P = args.page_size
+    plan = ga.qk_make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, kdt, args.mode, cu_count=props.multi_processor_count,
+                           page_size=P)
     nrot = max(1, math.ceil(args.rotate_mb * 2 ** 20 / alg))
     q0, k0 = q_h.to(dev), K_h.to(dev)
     ks = ks_h.to(dev) if ks_h is not None else None
     calls = []
-    for i in range(nrot):
-        calls.append(ga.bind_qk(q0 if i == 0 else q0.clone(), k0 if i == 0 else k0.clone(), scale=w.D ** -0.5,
-                                plan=plan, k_scale=ks))
+    if P > 0:
+        # paged K: the workload's K cut into pages of P rows in a shuffled order, full lengths
+        if w.C % P:
+            raise SystemExit(f"--page-size {P} must divide C={w.C}")
+        maxp = w.C // P
+        perm = torch.randperm(w.B * maxp, generator=torch.Generator().manual_seed(0))
+        pages_h = torch.empty((w.B * maxp, P, w.Hkv, w.D), dtype=K_h.dtype)
+        pages_h.view(torch.uint8 if kdt == "fp8" else K_h.dtype)[perm] = \
+            K_h.view(torch.uint8 if kdt == "fp8" else K_h.dtype).reshape(w.B * maxp, P, w.Hkv, w.D)
+        bt = perm.to(torch.int32).view(w.B, maxp).contiguous().to(dev)
+        lens = torch.full((w.B,), w.C, dtype=torch.int32, device=dev)
+        p0 = pages_h.to(dev)
+        for i in range(nrot):
+            calls.append(ga.BoundQkPaged(q0 if i == 0 else q0.clone(), p0 if i == 0 else p0.clone(), bt, lens,
+                                         C=w.C, scale=w.D ** -0.5, plan=plan, k_scale=ks))
+    else:
+        for i in range(nrot):
+            calls.append(ga.bind_qk(q0 if i == 0 else q0.clone(), k0 if i == 0 else k0.clone(), scale=w.D ** -0.5,
+                                    plan=plan, k_scale=ks))
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     _warm(args, calls, nrot)
@@ -477,12 +495,14 @@ def bench_qk(args, w, dev, props):
         "metric": QK_METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 6), "us_per_call": round(ms * 1e3, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": f"qk{'-fp8' if args.k_fp8 else ''}:{w.name}", "B": w.B, "C": w.C, "Hq": w.Hq,
+        "config": {"workload": f"qk{'-fp8' if args.k_fp8 else ''}{f'-paged{P}' if P else ''}:{w.name}", "B": w.B,
+                   "C": w.C, "Hq": w.Hq, "page_size": P,
                    "Hkv": w.Hkv, "G": w.G, "D": w.D, "k_dtype": "fp8_e4m3" if args.k_fp8 else w.v_dtype, "mode": args.mode, "algorithmic_bytes": alg, "rotation_sets": nrot,
                    "kernels_per_call": 1, "plan": plan.as_dict()},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(w.name, args.mode, "qk", "_fp8" if args.k_fp8 else ""),
+                     "traffic": recorded_traffic(w.name, args.mode, "qk", ("_fp8" if args.k_fp8 else "") +
+                                                 (f"_paged{P}" if P else "")),
                      "kernel": "qk_scores", "us_per_launch": round(ms * 1e3, 3),
                      "timing": "HIP events around K back-to-back launches on the launch stream"},
         "cpu_baseline": cpu,

@@ -71,14 +71,14 @@ class Plan(ctypes.Structure):
 
 class QkHint(ctypes.Structure):
     _fields_ = [("rows_per_block", ctypes.c_int64), ("cu_count", ctypes.c_int32), ("kv_tile", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 4)]
+                ("page_size", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
 
 
 class QkPlan(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("engine", ctypes.c_int32), ("heads_per_tile", ctypes.c_int32),
                 ("subgroups", ctypes.c_int32), ("rows_per_block", ctypes.c_int64), ("grid", ctypes.c_int64),
                 ("k_bytes_read", ctypes.c_int64), ("kv_heads_per_tile", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 3)]
+                ("page_size", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
@@ -140,6 +140,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gqa_qk_fp8_decode_plan.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
                                            ctypes.POINTER(QkPlan), vp]
     lib.gqa_qk_fp8_decode_plan.restype = ip
+    lib.gqa_qk_paged_decode.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, ip,
+                                        ctypes.c_float, ip, vp]
+    lib.gqa_qk_paged_decode.restype = ip
+    lib.gqa_qk_paged_decode_plan.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, ip,
+                                             ctypes.c_float, ctypes.POINTER(QkPlan), vp]
+    lib.gqa_qk_paged_decode_plan.restype = ip
     lib.gqa_qk_decode_plan.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ip, ctypes.c_float,
                                        ctypes.POINTER(QkPlan), vp]
     lib.gqa_qk_decode_plan.restype = ip
@@ -539,10 +545,12 @@ def release() -> None:
 # ---- decode score step ----------------------------------------------------------
 
 def qk_make_plan(B: int, C: int, Hq: int, Hkv: int, D: int, k_dtype: str, mode: Union[str, int] = "auto",
-                 rows_per_block: int = 0, cu_count: int = 0, kv_tile: int = 0) -> QkPlan:
-    """Host-only planning of the score step (no GPU needed); 0 means automatic."""
+                 rows_per_block: int = 0, cu_count: int = 0, kv_tile: int = 0, page_size: int = 0) -> QkPlan:
+    """Host-only planning of the score step (no GPU needed); 0 means automatic
+    (page_size: 0 for dense K, else paged K with that many rows per page)."""
     h = QkHint()
     h.rows_per_block, h.cu_count, h.kv_tile = int(rows_per_block), int(cu_count), int(kv_tile)
+    h.page_size = int(page_size)
     p = QkPlan()
     rc = load().gqa_qk_make_plan(B, C, Hq, Hkv, D, DTYPES[k_dtype], _mode(mode), ctypes.byref(h), ctypes.byref(p))
     if rc != 0:
@@ -658,3 +666,86 @@ class BoundQk:
 def bind_qk(q, K, scores=None, scale: float = 1.0, plan: Optional[QkPlan] = None, mode: Union[str, int] = "auto",
             stream=None, k_scale=None) -> BoundQk:
     return BoundQk(q, K, scores=scores, scale=scale, plan=plan, mode=mode, stream=stream, k_scale=k_scale)
+
+
+def _check_qk_paged(q, pages, block_table, seq_lens, scores, C):
+    """Shapes, dtypes and devices of a paged score call; returns (B, C, Hq, Hkv, D, P, max_pages, num_pages, kdt)."""
+    torch = _torch()
+    kmap = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16", torch.float8_e4m3fn: "fp8"}
+    if q.dim() != 3 or pages.dim() != 4 or block_table.dim() != 2 or seq_lens.dim() != 1:
+        raise ValueError("q [B,Hq,D], pages [num_pages,P,Hkv,D], block_table [B,max_pages], seq_lens [B]")
+    B, Hq, D = q.shape
+    num_pages, P, Hkv, D2 = pages.shape
+    if D2 != D:
+        raise ValueError(f"q's D={D} does not match the pages' D={D2}")
+    if q.dtype != torch.float32 or pages.dtype not in kmap:
+        raise TypeError("q must be float32 and pages float32, float16, bfloat16 or float8_e4m3fn")
+    if block_table.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("block_table and seq_lens must have B rows")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_table and seq_lens must be int32")
+    for t in (q, pages, block_table, seq_lens):
+        if not t.is_cuda or t.device != q.device or not t.is_contiguous():
+            raise ValueError("q, pages, block_table and seq_lens must be contiguous GPU tensors on one device")
+    max_pages = block_table.shape[1]
+    if C is None:
+        C = scores.shape[1] if scores is not None else max_pages * P
+    if scores is not None and (scores.dtype != torch.float32 or tuple(scores.shape) != (B, C, Hq)
+                               or not scores.is_contiguous() or scores.device != q.device):
+        raise ValueError(f"scores must be a contiguous float32 [{B},{C},{Hq}] tensor on {q.device}")
+    return B, C, Hq, Hkv, D, P, max_pages, num_pages, kmap[pages.dtype]
+
+
+def gqa_qk_paged_decode(q, pages, block_table, seq_lens, scores=None, C: Optional[int] = None, scale: float = 1.0,
+                        mode: Union[str, int] = "auto", stream=None, plan: Optional[QkPlan] = None, k_scale=None):
+    """The score step over a paged K cache: row c of sequence b is
+    pages[block_table[b, c // P], c % P]; the scores of rows c < seq_lens[b]
+    are written, the rest of scores [B, C, Hq] (C the capacity, default
+    max_pages * P; a new scores tensor starts as zeros) is left as it was."""
+    torch = _torch()
+    B, C, Hq, Hkv, D, P, maxp, npg, kdt = _check_qk_paged(q, pages, block_table, seq_lens, scores, C)
+    ks = _qk_scale(k_scale, kdt, Hkv, q.device)
+    if scores is None:
+        scores = torch.zeros((B, C, Hq), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    lib = load()
+    args = (q.data_ptr(), pages.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(),
+            ks.data_ptr() if ks is not None else None, scores.data_ptr(), B, C, Hq, Hkv, D, P, maxp, npg, DTYPES[kdt],
+            float(scale))
+    with torch.cuda.device(q.device):
+        if plan is None:
+            rc = lib.gqa_qk_paged_decode(*args, _mode(mode), stream.cuda_stream)
+        else:
+            rc = lib.gqa_qk_paged_decode_plan(*args, ctypes.byref(plan), stream.cuda_stream)
+    if rc != 0:
+        _raise(rc)
+    return scores
+
+
+class BoundQkPaged:
+    """A paged score call with checked, bound arguments for loops (see BoundCall)."""
+
+    def __init__(self, q, pages, block_table, seq_lens, scores=None, C: Optional[int] = None, scale: float = 1.0,
+                 plan: Optional[QkPlan] = None, mode: Union[str, int] = "auto", stream=None, k_scale=None):
+        torch = _torch()
+        B, C, Hq, Hkv, D, P, maxp, npg, kdt = _check_qk_paged(q, pages, block_table, seq_lens, scores, C)
+        ks = _qk_scale(k_scale, kdt, Hkv, q.device)
+        if scores is None:
+            scores = torch.zeros((B, C, Hq), dtype=torch.float32, device=q.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        if plan is None:
+            cu = torch.cuda.get_device_properties(q.device).multi_processor_count
+            plan = qk_make_plan(B, C, Hq, Hkv, D, kdt, mode, cu_count=cu, page_size=P)
+        self.tensors, self.scores, self.plan, self.k_scale = (q, pages, block_table, seq_lens), scores, plan, ks
+        self._fn = load().gqa_qk_paged_decode_plan
+        self._args = (q.data_ptr(), pages.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(),
+                      ks.data_ptr() if ks is not None else None, scores.data_ptr(), B, C, Hq, Hkv, D, P, maxp, npg,
+                      DTYPES[kdt], ctypes.c_float(scale), ctypes.byref(plan), stream.cuda_stream)
+
+    def __call__(self):
+        rc = self._fn(*self._args)
+        if rc != 0:
+            _raise(rc)
+        return self.scores

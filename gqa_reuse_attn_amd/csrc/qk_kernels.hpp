@@ -67,6 +67,13 @@ struct QkArgs {
     int32_t ht;              // adjacent KV heads per tile (reuse; 1 for per-head)
     int32_t vec4;            // 1: every tile's score run is whole rows of 16-byte groups, 16-byte aligned
     const float* k_scale;    // fp8 K: [Hkv] scales, or NULL for 1
+    // Paged K (block_table != NULL): K points at pages [num_pages][2^page_shift][Hkv][D];
+    // row c of sequence b is row c % P of page block_table[b][c / P]; rows c >= seq_lens[b] get no score.
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    int64_t num_pages;
+    int32_t page_shift;
+    int32_t max_pages;
     uint32_t nblocks;
 };
 
@@ -82,8 +89,12 @@ __device__ inline void fp8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
 }
 
 // KDT: element type of K; NBLK = D / 32; NSET sets of 16 heads per tile; HT
-// adjacent KV heads per tile (1, 2 or 4).
-template <int KDT, int NBLK, int NSET, int HT>
+// adjacent KV heads per tile (1, 2 or 4); PG: paged K. A paged workgroup
+// copies the block-table entries of its rows into LDS (clamped into the
+// cache), takes each lane's row address from them (rows past the sequence's
+// length read its last row), and its score resource ends at that length, so
+// rows past it are not written.
+template <int KDT, int NBLK, int NSET, int HT, bool PG = false>
 __global__ __launch_bounds__(kThreads) void qk_scores(QkArgs a) {
     static_assert(HT == 1 || HT == 2 || HT == 4, "KV heads per tile must divide the waves");
     constexpr int WPH = kWaves / HT;                 // waves per KV head
@@ -113,7 +124,13 @@ __global__ __launch_bounds__(kThreads) void qk_scores(QkArgs a) {
     const int chunk = t % a.nchunk; t /= a.nchunk;
     const int b = static_cast<int>(t);
     const int64_t r0 = uniform64(static_cast<int64_t>(chunk) * a.rows_per_block);
-    const int nrows = static_cast<int>(uniform64(min(static_cast<int64_t>(a.rows_per_block), a.C - r0)));
+    int64_t end = min(r0 + a.rows_per_block, a.C);
+    if constexpr (PG) {
+        const int64_t len = a.seq_lens[b];
+        end = min(end, len < 0 ? int64_t{0} : min(len, a.C));
+    }
+    const int nrows = static_cast<int>(uniform64(end > r0 ? end - r0 : 0));
+    if (PG && nrows == 0) return;                    // the whole chunk is past the length (uniform)
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -129,15 +146,30 @@ __global__ __launch_bounds__(kThreads) void qk_scores(QkArgs a) {
     // read as zero (their scores are never stored).
     const int krow = a.Hkv * D * ES;
     const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(a.K) + ((static_cast<size_t>(b) * a.C + r0) * a.Hkv + kv0) * D * ES, 0,
-        (nrows - 1) * krow + HT * D * ES, kRawBufferFlags);
+        const_cast<uint8_t*>(a.K) + (PG ? 0 : ((static_cast<size_t>(b) * a.C + r0) * a.Hkv + kv0) * D * ES), 0,
+        PG ? 0 : (nrows - 1) * krow + HT * D * ES, kRawBufferFlags);
+    // PG: the chunk's pages, from the block table into LDS.
+    __shared__ int32_t s_pages[PG ? kMaxSplitPages : 1];
+    const int64_t pg0 = PG ? (r0 >> a.page_shift) : 0;
+    if constexpr (PG) {
+        const int npg = static_cast<int>(((r0 + nrows - 1) >> a.page_shift) - pg0 + 1);
+        const int32_t* const btr = a.block_table + static_cast<size_t>(b) * a.max_pages + pg0;
+        for (int i = threadIdx.x; i < npg; i += kThreads) {
+            const int32_t pg = btr[i];
+            s_pages[i] = pg < 0 ? 0 : (pg >= a.num_pages ? static_cast<int32_t>(a.num_pages - 1) : pg);
+        }
+        __syncthreads();
+    }
+    const int64_t pmask = PG ? (int64_t{1} << a.page_shift) - 1 : 0;
     // Load i of a block: lane l takes piece f = 64 i + l, i.e. row f / NP,
     // piece f % NP (whole rows, consecutive in memory within each row).
-    int koff[NLD], soff[NLD];
+    int koff[NLD], soff[NLD], prow[NLD], pcol[NLD];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
         const int f = 64 * i + lane;
         koff[i] = (f / NP) * krow + kvl * D * ES + (f % NP) * 16;
+        prow[i] = f / NP;                            // PG: this lane's row inside a 16-row block ...
+        pcol[i] = (f % NP) * 16;                     // ... and its piece of that row's KV-head slice
         soff[i] = (f / NP) * RBP + (f % NP) * 16 * (ESL / ES);
     }
     typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -277,9 +309,19 @@ __global__ __launch_bounds__(kThreads) void qk_scores(QkArgs a) {
 #pragma unroll
         for (int u = 0; u < UB; ++u)
 #pragma unroll
-            for (int i = 0; i < NLD; ++i)
-                bf.raw[u][i] = __builtin_amdgcn_raw_buffer_load_b128(kres, koff[i], 16 * block_of(st, u) * krow,
-                                                                     kCachePolicyNt);
+            for (int i = 0; i < NLD; ++i) {
+                if constexpr (PG) {
+                    // Rows past the chunk read its last row (their scores are not stored).
+                    const int64_t c = r0 + min(16 * block_of(st, u) + prow[i], nrows - 1);
+                    const int64_t page = s_pages[(c >> a.page_shift) - pg0];
+                    const uint8_t* const p =
+                        a.K + (((page << a.page_shift) + (c & pmask)) * a.Hkv + kv) * D * ES + pcol[i];
+                    bf.raw[u][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+                } else {
+                    bf.raw[u][i] = __builtin_amdgcn_raw_buffer_load_b128(kres, koff[i], 16 * block_of(st, u) * krow,
+                                                                         kCachePolicyNt);
+                }
+            }
     };
     auto compute_store = [&](const u32x4 (&bfin)[NLD], int j, int st, int tb) {
         // Re-layout through the wave's LDS region (in program order: one
@@ -385,13 +427,20 @@ __global__ __launch_bounds__(kThreads) void qk_scores(QkArgs a) {
                                                           st * R * srow, 0);
         }
     };
+    // PG: keep each step's loads ahead of the other buffer's work (the page
+    // lookups would otherwise let the scheduler sink them).
+    auto fence = [] {
+        if constexpr (PG) __builtin_amdgcn_sched_barrier(0);
+    };
     Buf bA, bB;
     int st = 0;
     if (nsteps > 0) load(bA, 0);
     for (; st + 1 < nsteps; st += 2) {
         load(bB, st + 1);
+        fence();
         consume(bA, st, 0);
         load(bA, st + 2);
+        fence();
         consume(bB, st + 1, 1);
     }
     if (st < nsteps) consume(bA, st, 0);

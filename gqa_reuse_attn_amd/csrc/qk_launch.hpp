@@ -7,15 +7,22 @@
 namespace gqa_av_launch {
 namespace detail {
 
-template <int KDT, int NBLK, int NSET>
-hipError_t launch_qk_ht(const gqa_av::QkArgs& a, hipStream_t s) {
+template <int KDT, int NBLK, int NSET, bool PG>
+hipError_t launch_qk_pg(const gqa_av::QkArgs& a, hipStream_t s) {
+    const dim3 grid(a.nblocks), block(gqa_av::kThreads);
     switch (a.ht) {
-    case 1: hipLaunchKernelGGL((gqa_av::qk_scores<KDT, NBLK, NSET, 1>), dim3(a.nblocks), dim3(gqa_av::kThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((gqa_av::qk_scores<KDT, NBLK, NSET, 2>), dim3(a.nblocks), dim3(gqa_av::kThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((gqa_av::qk_scores<KDT, NBLK, NSET, 4>), dim3(a.nblocks), dim3(gqa_av::kThreads), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((gqa_av::qk_scores<KDT, NBLK, NSET, 1, PG>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((gqa_av::qk_scores<KDT, NBLK, NSET, 2, PG>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((gqa_av::qk_scores<KDT, NBLK, NSET, 4, PG>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+// Paged K when the arguments carry a block table.
+template <int KDT, int NBLK, int NSET>
+hipError_t launch_qk_ht(const gqa_av::QkArgs& a, hipStream_t s) {
+    return a.block_table ? launch_qk_pg<KDT, NBLK, NSET, true>(a, s) : launch_qk_pg<KDT, NBLK, NSET, false>(a, s);
 }
 
 template <int KDT, int NBLK>

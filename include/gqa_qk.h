@@ -61,7 +61,8 @@ typedef struct gqa_qk_hint {
     int64_t rows_per_block;  /* context rows per workgroup (rounded up to a multiple of 64) */
     int32_t cu_count;        /* compute units to plan for (make_plan: 256; decode: the device's) */
     int32_t kv_tile;         /* adjacent KV heads per workgroup in reuse mode: 1, 2 or 4 */
-    int32_t reserved[4];
+    int32_t page_size;       /* paged K (gqa_qk_paged_decode_plan): rows per page, a power of two; 0: dense */
+    int32_t reserved[3];
 } gqa_qk_hint;
 
 /* Launch plan of the score step. */
@@ -74,7 +75,8 @@ typedef struct gqa_qk_plan {
     int64_t grid;            /* workgroups launched */
     int64_t k_bytes_read;    /* K bytes the plan reads from memory (G x more for per-head) */
     int32_t kv_heads_per_tile; /* adjacent KV heads one workgroup streams (reuse: 1, 2 or 4; per-head: 1) */
-    int32_t reserved[3];
+    int32_t page_size;         /* paged K: rows per page (rows_per_block then <= 1023 pages); 0: dense K */
+    int32_t reserved[2];
 } gqa_qk_plan;
 
 /* Build the plan. Host-only: needs no GPU. hint may be NULL. Returns a gqa_av_status. */
@@ -103,6 +105,26 @@ int gqa_qk_fp8_decode(const float *q, const void *K, const float *k_scale, float
 int gqa_qk_fp8_decode_plan(const float *q, const void *K, const float *k_scale, float *scores,
                            int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D,
                            float scale, const gqa_qk_plan *plan, void *stream);
+
+/* Paged K (a decode cache layout, not on the page; the layout and tables of
+ * gqa_paged_av.h): pages [num_pages][page_size][Hkv][D] of k_dtype, row c of
+ * sequence b being row c % page_size of page block_table[b][c / page_size]
+ * (block_table [B][max_pages] int32, seq_lens [B] int32, device data). scores
+ * keeps the dense [B][C][Hq] layout with C the capacity (C <= max_pages *
+ * page_size); the scores of rows c < seq_lens[b] are written as defined
+ * above and the rows past each length are left as they were. k_scale [Hkv]
+ * (fp8 K only; NULL: 1). page_size a power of two; lengths are clamped into
+ * [0, C] and block-table entries into [0, num_pages), so bad tables give
+ * wrong numbers, never a fault. The _plan form takes a plan made with
+ * hint->page_size = page_size (plan->page_size). */
+int gqa_qk_paged_decode(const float *q, const void *pages, const int32_t *block_table, const int32_t *seq_lens,
+                        const float *k_scale, float *scores, int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D,
+                        int64_t page_size, int64_t max_pages, int64_t num_pages, int k_dtype, float scale, int mode,
+                        void *stream);
+int gqa_qk_paged_decode_plan(const float *q, const void *pages, const int32_t *block_table, const int32_t *seq_lens,
+                             const float *k_scale, float *scores, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
+                             int64_t D, int64_t page_size, int64_t max_pages, int64_t num_pages, int k_dtype,
+                             float scale, const gqa_qk_plan *plan, void *stream);
 
 #ifdef __cplusplus
 }

@@ -273,3 +273,122 @@ def test_qk_fp8_equals_bf16_on_widened_k():
         a = _run_fp8(q, K8, None, 0.25, plan=p8)
         b = _run(q, K16, 0.25, plan=p16)
         assert np.array_equal(a, b), (mode, ht)
+
+
+# ---- paged K (the paged-V layout and tables) ---------------------------------
+
+SENTINEL = -12345.5
+
+
+def _paged_k(K: torch.Tensor, P: int, seed: int, spare: int = 3):
+    """Scatter a dense K [B, C, Hkv, D] into a shuffled pool of P-row pages
+    (spare pages hold a large value that must never be read)."""
+    B, C, Hkv, D = K.shape
+    maxp = -(-C // P)
+    g = torch.Generator().manual_seed(seed)
+    npg = B * maxp + spare
+    if K.dtype == torch.float8_e4m3fn:
+        pages = torch.full((npg, P, Hkv, D), 0x7E, dtype=torch.uint8).view(torch.float8_e4m3fn)
+    else:
+        pages = torch.full((npg, P, Hkv, D), 3.0e4).to(K.dtype)
+    perm = torch.randperm(npg, generator=g)[:B * maxp].to(torch.int32).view(B, maxp).contiguous()
+    for b in range(B):
+        for k in range(maxp):
+            rows = K[b, k * P:(k + 1) * P]
+            pages[int(perm[b, k]), :rows.shape[0]] = rows
+    return pages, perm
+
+
+def _run_paged(q, pages, bt, lens, C, scale, k_scale=None, plan=None):
+    scores = torch.full((q.shape[0], C, q.shape[1]), SENTINEL, device=DEV)
+    ga.gqa_qk_paged_decode(q.to(DEV), pages.to(DEV), bt.to(DEV), lens.to(DEV), scores=scores, scale=scale, plan=plan,
+                           k_scale=None if k_scale is None else k_scale.to(DEV))
+    torch.cuda.synchronize()
+    return scores.cpu().numpy().astype(np.float64)
+
+
+def _check_paged(out, ref, lens, dt, D, label):
+    """Rows below each length: the gate and accumulation bound per sequence;
+    rows past it: untouched (the sentinel)."""
+    for b, n in enumerate(lens.tolist()):
+        if n:
+            assert_parity(out[b, :n], ref[b, :n], "bf16" if dt == "fp8" else dt, D, f"{label} b={b}")
+        assert (out[b, n:] == SENTINEL).all(), f"{label} b={b}: a row past the length was written"
+
+
+def _qk_paged_cases():
+    cases, k = [], 0
+    for G in (1, 2, 3, 8, 16):
+        for D in (64, 128, 256):
+            for P in (1, 16, 64):
+                if (G + D // 64 + P) % 2:
+                    continue
+                dt = ("bf16", "f16", "f32", "fp8")[k % 4]
+                Hkv = (1, 2, 4)[k % 3]
+                C = (300, 1000, 77)[k % 3]
+                cases.append((2 + k % 3, C, G * Hkv, Hkv, D, P, dt))
+                k += 1
+    return cases
+
+
+@pytest.mark.parametrize("B,C,Hq,Hkv,D,P,dt", _qk_paged_cases())
+def test_qk_paged_sweep(B, C, Hq, Hkv, D, P, dt, oracle_lib):
+    """G 1..16, D 64..256, pages of 1..64 rows, all K types (fp8 with scales),
+    lengths full / partial / 1 / 0, reuse and per-head, 1/2/4 KV heads per
+    workgroup; rows past each length keep the value they had."""
+    q, K = make_qk_random(B, C, Hq, Hkv, D, "f32" if dt == "fp8" else dt, seed=C + D + P)
+    ks = None
+    if dt == "fp8":
+        K, ks = _quantize_k(K)
+    pages, bt = _paged_k(K, P, seed=P + B)
+    lens = torch.tensor([C, C // 2 + 3, 1, 0][:B], dtype=torch.int32)
+    scale = 0.375
+    ref = oracle_lib.qk_paged(q, pages, bt, lens, dt, scale, ks, C=C)
+    modes = ("auto", "per_head") if Hq // Hkv >= 2 else ("auto",)
+    plans = [ga.qk_make_plan(B, C, Hq, Hkv, D, dt, m, page_size=P) for m in modes]
+    plans += [ga.qk_make_plan(B, C, Hq, Hkv, D, dt, "reuse", kv_tile=ht, rows_per_block=128, page_size=P)
+              for ht in (2, 4) if Hq // Hkv >= 2 and Hkv % ht == 0]
+    for plan in plans:
+        out = _run_paged(q, pages, bt, lens, C, scale, ks, plan=plan)
+        _check_paged(out, ref, lens, dt, D, f"qk paged {(B, C, Hq, Hkv, D, P, dt)} {plan.as_dict()}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp8"])
+def test_qk_paged_dense_layout_matches_dense_call(dt):
+    """One page per sequence holding its dense K (P = C, block_table[b] = b,
+    full lengths) gives the dense call's scores bit for bit."""
+    B, C, Hq, Hkv, D = 3, 512, 32, 4, 128
+    q, K = make_qk_random(B, C, Hq, Hkv, D, "f32" if dt == "fp8" else dt, seed=71)
+    ks = None
+    if dt == "fp8":
+        K, ks = _quantize_k(K)
+    bt = torch.arange(B, dtype=torch.int32).view(B, 1)
+    lens = torch.full((B,), C, dtype=torch.int32)
+    for mode in ("auto", "per_head"):
+        pp = ga.qk_make_plan(B, C, Hq, Hkv, D, dt, mode, page_size=C)
+        dp = ga.qk_make_plan(B, C, Hq, Hkv, D, dt, mode)
+        assert pp.rows_per_block == dp.rows_per_block
+        a = _run_paged(q, K, bt, lens, C, 0.125, ks, plan=pp)
+        b = (_run_fp8(q, K, ks, 0.125, plan=dp) if dt == "fp8" else _run(q, K, 0.125, plan=dp))
+        assert np.array_equal(a, b), (dt, mode)
+
+
+@pytest.mark.parametrize("wname,P", [("g2-b4-c32768-hq16-hkv8-d128-bf16", 16),
+                                     ("batch64-b64-c8192-hq64-hkv8-d128-bf16", 256),
+                                     ("mqa16-b4-c32768-hq16-hkv1-d128-bf16", 32)])
+def test_qk_paged_workloads(wname, P, oracle_lib):
+    """Workload shapes (the large batch cut to 8 sequences) as paged K with
+    lengths between half and all of the capacity."""
+    w = WORKLOADS[wname]
+    if w.B > 8:
+        w = w.replace(B=8)
+    _say(f"[qk paged] {w.name} P={P}")
+    q, K = make_qk_random(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, seed=5)
+    pages, bt = _paged_k(K, P, seed=1)
+    g = torch.Generator().manual_seed(2)
+    lens = torch.randint(w.C // 2, w.C + 1, (w.B,), generator=g, dtype=torch.int32)
+    lens[0] = w.C
+    scale = w.D ** -0.5
+    ref = oracle_lib.qk_paged(q, pages, bt, lens, w.v_dtype, scale, C=w.C)
+    out = _run_paged(q, pages, bt, lens, w.C, scale)
+    _check_paged(out, ref, lens, w.v_dtype, w.D, f"qk paged {w.name}")

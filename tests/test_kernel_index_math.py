@@ -360,6 +360,28 @@ def _check_qk_plan(p, B, C, Hq, Hkv, D, dt, UB=QK_BLOCKS, vec4=False):
         r0 = chunk * rows
         nrows = min(rows, C - r0)
         assert nrows > 0
+        if p.page_size:
+            # paged K: the chunk's page list (at most 1024 entries) and every
+            # loaded row's entry in it, reloads past the chunk clamped to its
+            # last row, for full and shorter sequences
+            P = p.page_size
+            shift = P.bit_length() - 1
+            for ln in {C, C // 2, r0 + 1, r0}:
+                nr = max(0, min(r0 + rows, C, ln) - r0)
+                if nr == 0:
+                    continue
+                pg0 = r0 >> shift
+                npg = ((r0 + nr - 1) >> shift) - pg0 + 1
+                assert npg <= 1024 and (r0 + nr - 1) // P < -(-C // P)
+                nsteps_ = -(-(-(-nr // 16)) // (WPH * UB))
+                for step in range(nsteps_ + (1 if nsteps_ > 1 else 0)):
+                    for u in range(UB):
+                        for wh in range(WPH):
+                            j = (step * UB + u) * WPH + wh
+                            for i in range(NP // 4):
+                                rows_ = np.minimum(16 * j + (64 * i + lanes) // NP, nr - 1)
+                                idx = ((r0 + rows_) >> shift) - pg0
+                                assert idx.min() >= 0 and idx.max() < npg
         kbase = ((b * C + r0) * Hkv + kv0) * D * es
         krec = (nrows - 1) * krow + HT * D * es
         assert kbase + krec <= B * C * Hkv * D * es
@@ -447,11 +469,12 @@ def _check_qk_plan(p, B, C, Hq, Hkv, D, dt, UB=QK_BLOCKS, vec4=False):
 def test_qk_plan_bounds(B, C, Hq, Hkv, D, dt):
     modes = ("auto", "per_head") if Hq // Hkv >= 2 else ("auto",)
     for mode in modes:
-        for rows in (0, 64, 128, 192):
-            for ht in (0, 1, 2, 4):
+        for rows, P in ((0, 0), (64, 0), (128, 0), (192, 0), (0, 1), (192, 16), (0, 64)):
+            for ht in ((0, 1, 2, 4) if not P else (0,)):
                 if ht > 1 and (Hkv % ht or mode == "per_head" or Hq // Hkv < 2):
                     continue
-                p = ga.qk_make_plan(B, C, Hq, Hkv, D, dt, mode, rows_per_block=rows, kv_tile=ht)
+                p = ga.qk_make_plan(B, C, Hq, Hkv, D, dt, mode, rows_per_block=rows, kv_tile=ht, page_size=P)
+                assert p.page_size == P
                 # 16-byte score stores when the host would choose them (scores
                 # 16-byte aligned), 4-byte stores always possible
                 v4 = p.mode == 1 and p.subgroups == 1 and (p.kv_heads_per_tile * (Hq // Hkv)) % 4 == 0 and Hq % 4 == 0

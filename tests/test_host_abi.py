@@ -576,3 +576,33 @@ def test_error_detail_is_per_thread():
         t.join()
     assert seen["bad"][0] != 0 and seen["bad"][1], seen
     assert seen["good"][0] == 1 and seen["good"][1] == "", seen
+
+
+def test_qk_paged_plans_and_refusals():
+    """Paged score plans: page_size recorded, rows per block capped so a block's
+    page list fits in LDS (<= 1023 pages), bad sizes refused before any
+    launch, dense and paged plans not interchangeable."""
+    for P in (1, 16, 256):
+        p = ga.qk_make_plan(4, 32768, 16, 8, 128, "bf16", page_size=P)
+        assert p.page_size == P and p.rows_per_block % 64 == 0 and -(-p.rows_per_block // P) + 1 <= 1024
+    for kw, name in ((dict(page_size=12), "INVALID_ARG"), (dict(page_size=-4), "INVALID_ARG")):
+        with pytest.raises(ga.GqaAvError) as e:
+            ga.qk_make_plan(4, 1000, 16, 8, 128, "bf16", **kw)
+        assert e.value.name == name, kw
+    lib = ga.load()
+    fake = ctypes.c_void_p(1 << 20)
+    pg = ga.qk_make_plan(2, 100, 8, 2, 64, "bf16", page_size=16)
+    dense = ga.qk_make_plan(2, 100, 8, 2, 64, "bf16")
+
+    def call(plan, C=100, P=16, maxp=8, npg=16, bt=fake, ln=fake, ks=None, dt=2):
+        return lib.gqa_qk_paged_decode_plan(fake, fake, bt, ln, ks, fake, 2, C, 8, 2, 64, P, maxp, npg, dt,
+                                            ctypes.c_float(1.0), ctypes.byref(plan), None)
+    assert call(dense) == 1                                   # not a paged plan
+    assert lib.gqa_qk_decode_plan(fake, fake, fake, 2, 100, 8, 2, 64, 2, ctypes.c_float(1.0), ctypes.byref(pg),
+                                  None) == 1                  # a paged plan on the dense entry point
+    assert call(pg, P=32) == 1                                # page size differs from the plan's
+    assert call(pg, maxp=6) == 1                              # capacity 100 > 6 * 16
+    assert call(pg, npg=0) == 1
+    assert call(pg, bt=None) == 1 and call(pg, ln=None) == 1
+    assert call(pg, ks=fake) == 1                             # k_scale is for fp8 K
+    assert "k_scale" in ga.load().gqa_av_last_error().decode()

@@ -72,6 +72,8 @@ class Oracle:
         lib.gqa_qk_paged_oracle.argtypes = [vp, vp, vp, vp, ip, vp, i64, i64, i64, i64, i64, i64, i64, i64,
                                             ctypes.c_double, vp, ip]
         lib.gqa_qk_paged_oracle.restype = ip
+        lib.gqa_attention_oracle.argtypes = [vp, vp, vp, ip, i64, i64, i64, i64, i64, ctypes.c_double, vp, ip]
+        lib.gqa_attention_oracle.restype = ip
         self.lib = lib
 
     @staticmethod
@@ -150,6 +152,21 @@ class Oracle:
         rc = self.lib.gqa_qk_paged_oracle(qa.ctypes.data, k.ctypes.data, bt.ctypes.data, ln.ctypes.data, code,
                                           None if ks is None else ks.ctypes.data, B, C, Hq, Hkv, D, P, max_pages,
                                           num_pages, float(scale), out.ctypes.data, nthreads)
+        if rc != 0:
+            raise ValueError(f"oracle rejected the arguments (status {rc})")
+        return out
+
+    def attention(self, q, K, V, kv_dtype: str, scale: float = 1.0, nthreads: int = 0) -> np.ndarray:
+        """out[B, Hq, D] (float64): softmax over c of scale * q . K, times V;
+        q [B,Hq,D] fp32, K and V [B,C,Hkv,D] of kv_dtype."""
+        qa, k = self._np_inputs(q, K, kv_dtype)
+        _, v = self._np_inputs(q, V, kv_dtype)
+        B, Hq, D = qa.shape
+        B2, C, Hkv, D2 = k.shape
+        assert B2 == B and D2 == D and v.shape == k.shape
+        out = np.empty((B, Hq, D), dtype=np.float64)
+        rc = self.lib.gqa_attention_oracle(qa.ctypes.data, k.ctypes.data, v.ctypes.data, DTYPE_CODE[kv_dtype],
+                                           B, C, Hq, Hkv, D, float(scale), out.ctypes.data, nthreads)
         if rc != 0:
             raise ValueError(f"oracle rejected the arguments (status {rc})")
         return out

@@ -53,6 +53,16 @@
  * and one division at the end. C = 0 gives zeros (an empty sum, as above); a
  * row whose scores are all -inf gives NaN, as the definition does.
  *
+ * Fused decode attention (the score step, the softmax and the product in one
+ * pass; the page covers the product only):
+ *
+ *   out[b, q_h, d] = sum_c p_c V[b, c, kv_h, d],  p = softmax_c(s),
+ *   s_c = scale * sum_d q[b, q_h, d] * K[b, c, kv_h, d]
+ *
+ * written out in double: each score from exact products summed in increasing
+ * d and multiplied by scale, then the maximum, exp(s_c - m) (libm), the sums
+ * of exp * V and of exp in increasing c, and one division.
+ *
  * fp8 V (a compressed cache, not on the page): V holds OCP FP8 E4M3 bytes
  * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no infinities,
  * S.1111.111 is NaN) and each KV head has a float32 scale: the value of an
@@ -505,6 +515,50 @@ int gqa_qk_paged_oracle(const float *q, const void *pages, const int32_t *block_
             }
             o[h] = dot * scale;
         }
+    }
+    (void)nthreads;
+    return ORC_OK;
+}
+
+/* Fused decode attention: out[B][Hq][D] in double (definition above). K and
+ * V share dtype (0..2). C = 0 gives zeros. */
+int gqa_attention_oracle(const float *q, const void *K, const void *V, int dtype,
+                         int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, double scale, double *out,
+                         int nthreads)
+{
+    int rc = orc_check(dtype, B, C, Hq, Hkv, D);
+    if (rc != ORC_OK) return rc;
+    pthread_once(&orc_f16_once, orc_f16_fill);
+    const int64_t G = Hq / Hkv;
+    const int64_t rows = B * Hq;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int64_t i = 0; i < rows; ++i) {
+        const int64_t b = i / Hq, h = i % Hq, kv = h / G;
+        double *o = out + i * D;
+        for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+        if (C == 0) continue;
+        const float *qrow = q + (b * Hq + h) * D;
+        double m = -INFINITY;
+        for (int64_t c = 0; c < C; ++c) {
+            const int64_t krow = ((b * C + c) * Hkv + kv) * D;
+            double dot = 0.0;
+            for (int64_t d = 0; d < D; ++d) dot += (double)qrow[d] * orc_load(K, dtype, krow + d);
+            const double sc = dot * scale;
+            if (sc > m) m = sc;
+        }
+        double l = 0.0;
+        for (int64_t c = 0; c < C; ++c) {
+            const int64_t krow = ((b * C + c) * Hkv + kv) * D;
+            double dot = 0.0;
+            for (int64_t d = 0; d < D; ++d) dot += (double)qrow[d] * orc_load(K, dtype, krow + d);
+            const double e = exp(dot * scale - m);
+            l += e;
+            for (int64_t d = 0; d < D; ++d) o[d] += e * orc_load(V, dtype, krow + d);
+        }
+        for (int64_t d = 0; d < D; ++d) o[d] /= l;
     }
     (void)nthreads;
     return ORC_OK;

@@ -86,6 +86,16 @@ Paged K in the score step (the paged-V layout and tables):
   * qk_paged_rejects  bad block-table entries, lengths and capacities are
                       rejected.
 
+Fused decode attention (softmax of the scaled scores, times V, in one pass):
+  * attn_composition  with dyadic q and small-integer K every score is exact in
+                      fp32, and the oracle equals the score oracle followed by
+                      the fused softmax-V oracle bit for bit.
+  * attn_numpy        numpy's einsum and scipy's softmax in fp64 (an independent
+                      route) agree to 1e-12, also for scores near 700.
+  * attn_zero_q       q = 0 gives the mean of V over the context.
+  * attn_repeat_mha   GQA equals MHA over K and V repeated G times (bitwise).
+  * attn_edges        C = 0 gives zeros; B = 0 gives an empty result.
+
 fp8 K in the score step (same bytes and per-KV-head scales):
   * qk_fp8_as_bf16    with unit scales the fp8 score oracle equals the bf16
                       score oracle on K widened by torch's float8 -> bfloat16
@@ -786,6 +796,65 @@ def pin_qk_paged_rejects(orc):
     raise AssertionError("paged score oracle accepted C > max_pages * P")
 
 
+def pin_attn_composition(orc):
+    g = torch.Generator().manual_seed(1100)
+    for dt in ("bf16", "f16", "f32"):
+        B, C, Hq, Hkv, D = 2, 37, 6, 2, 16
+        q = torch.randint(-8, 9, (B, Hq, D), generator=g).float() / 4.0
+        K = torch.randint(-4, 5, (B, C, Hkv, D), generator=g).float().to({"bf16": torch.bfloat16,
+                                                                           "f16": torch.float16,
+                                                                           "f32": torch.float32}[dt])
+        _, V = make_qk_random(B, C, Hq, Hkv, D, dt, seed=1101)
+        scores = orc.qk(q, K, dt, 0.5)
+        s32 = torch.from_numpy(scores).float()
+        assert np.array_equal(s32.double().numpy(), scores), "dyadic scores must be exact in fp32"
+        assert np.array_equal(orc.attention(q, K, V, dt, 0.5), orc.softmax_av(s32, V, dt)), f"attention != composition ({dt})"
+
+
+def pin_attn_numpy(orc):
+    from scipy.special import softmax
+    for i, (B, C, Hq, Hkv, D, sc) in enumerate([(2, 29, 8, 2, 16, 0.25), (1, 40, 4, 4, 8, 1.0), (2, 9, 6, 3, 32, 40.0)]):
+        q, K = make_qk_random(B, C, Hq, Hkv, D, "bf16", seed=1110 + i)
+        _, V = make_qk_random(B, C, Hq, Hkv, D, "bf16", seed=1120 + i)
+        G = Hq // Hkv
+        qd, kd, vd = q.double().numpy(), K.double().numpy(), V.double().numpy()
+        kq, vq = np.repeat(kd, G, axis=2), np.repeat(vd, G, axis=2)
+        s_ = sc * np.einsum("bhd,bchd->bch", qd, kq)
+        p_ = softmax(s_, axis=1)
+        ref = np.einsum("bch,bchd->bhd", p_, vq)
+        out = orc.attention(q, K, V, "bf16", sc)
+        assert np.allclose(out, ref, rtol=1e-12, atol=1e-12 * np.abs(vd).max()), f"attention vs numpy (case {i})"
+        assert np.abs(s_).max() < 2000.0
+
+
+def pin_attn_zero_q(orc):
+    B, C, Hq, Hkv, D = 2, 50, 4, 2, 8
+    _, K = make_qk_random(B, C, Hq, Hkv, D, "f32", seed=1130)
+    _, V = make_qk_random(B, C, Hq, Hkv, D, "f32", seed=1131)
+    out = orc.attention(torch.zeros(B, Hq, D), K, V, "f32", 1.0)
+    mean = V.double().numpy().mean(axis=1)                       # [B, Hkv, D]
+    ref = np.repeat(mean, Hq // Hkv, axis=1)
+    assert np.allclose(out, ref, rtol=1e-14, atol=1e-15), "q = 0 must average V"
+
+
+def pin_attn_repeat_mha(orc):
+    B, C, Hq, Hkv, D = 2, 21, 6, 2, 12
+    q, K = make_qk_random(B, C, Hq, Hkv, D, "bf16", seed=1140)
+    _, V = make_qk_random(B, C, Hq, Hkv, D, "bf16", seed=1141)
+    G = Hq // Hkv
+    Kr = K.repeat_interleave(G, dim=2).contiguous()
+    Vr = V.repeat_interleave(G, dim=2).contiguous()
+    assert np.array_equal(orc.attention(q, K, V, "bf16", 0.3), orc.attention(q, Kr, Vr, "bf16", 0.3)), "GQA != MHA"
+
+
+def pin_attn_edges(orc):
+    q, K = make_qk_random(2, 0, 4, 2, 8, "bf16", seed=1150)
+    V = K.clone()
+    assert (orc.attention(q, K, V, "bf16", 1.0) == 0).all(), "C = 0 gives zeros"
+    q0, K0 = make_qk_random(0, 5, 4, 2, 8, "bf16", seed=1151)
+    assert orc.attention(q0, K0, K0.clone(), "bf16", 1.0).size == 0
+
+
 ALL_PINS = [pin_decode_table, pin_brute_force, pin_mha_einsum, pin_repeat_mha, pin_constant_v,
             pin_one_hot, pin_linearity, pin_permutation, pin_batch_independence, pin_points,
             pin_edges, pin_qk_brute_force, pin_qk_mha_einsum, pin_qk_repeat_mha, pin_qk_one_hot,
@@ -794,4 +863,5 @@ ALL_PINS = [pin_decode_table, pin_brute_force, pin_mha_einsum, pin_repeat_mha, p
             pin_sav_repeat_mha, pin_sav_edges, pin_paged_gather, pin_paged_identity, pin_paged_ignores_tail,
             pin_paged_rejects, pin_fp8_decode, pin_fp8_as_bf16, pin_fp8_scales, pin_qk_fp8_as_bf16,
             pin_qk_fp8_brute, pin_qk_fp8_scales, pin_qk_paged_gather, pin_qk_paged_identity, pin_qk_paged_tail,
-            pin_qk_paged_rejects]
+            pin_qk_paged_rejects, pin_attn_composition, pin_attn_numpy, pin_attn_zero_q, pin_attn_repeat_mha,
+            pin_attn_edges]

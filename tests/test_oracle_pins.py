@@ -88,6 +88,12 @@ PLANTS = [
      "const int64_t row = ((page * P + (P - 1 - c % P)) * Hkv + kvh) * D;"),
     ("qk_paged_ignores_len", "if (c >= seq_lens[b]) {", "if (c >= C) {"),
     ("qk_paged_fp8_no_scale", "dot += (double)qrow[d] * (orc_e4m3(kr[d]) * ks);", "dot += (double)qrow[d] * orc_e4m3(kr[d]);"),
+    ("attn_max_unscaled", "const double sc = dot * scale;\n            if (sc > m) m = sc;",
+     "const double sc = dot;\n            if (sc > m) m = sc;"),
+    ("attn_exp_unscaled", "const double e = exp(dot * scale - m);", "const double e = exp(dot - m);"),
+    ("attn_no_max", "const double e = exp(dot * scale - m);", "const double e = exp(dot * scale);"),
+    ("attn_v_from_k", "o[d] += e * orc_load(V, dtype, krow + d);", "o[d] += e * orc_load(K, dtype, krow + d);"),
+    ("attn_kv_of_query", "const int64_t b = i / Hq, h = i % Hq, kv = h / G;", "const int64_t b = i / Hq, h = i % Hq, kv = h % Hkv;"),
     ("paged_bt_ignores_batch", "const int64_t page = bt[b * max_pages + c / P];",
      "const int64_t page = bt[0 * max_pages + c / P];"),
 ]

@@ -52,8 +52,10 @@ KERNEL_SOURCES = {
           + sorted(glob.glob(os.path.join(_CSRC, "launch_qk_*.hip"))),
 }
 KERNEL_SOURCES["softmax"] = KERNEL_SOURCES["av"]
+KERNEL_SOURCES["attn"] = KERNEL_SOURCES["av"]
 # Profile file prefix and the dominant kernel's name fragment, per operation.
-OPS = {"av": ("pass1", "pass1"), "qk": ("qk", "qk_scores"), "softmax": ("softmax_pass1", "pass1")}
+OPS = {"av": ("pass1", "pass1"), "qk": ("qk", "qk_scores"), "softmax": ("softmax_pass1", "pass1"),
+       "attn": ("attn_pass1", "pass1")}
 SOFTMAX_METRIC = "GQA decode fused softmax x V: µs/call and achieved HBM GB/s (% of MI355X peak)"
 
 
@@ -69,9 +71,10 @@ def source_hash(op: str = "av") -> str:
 def parse():
     p = argparse.ArgumentParser(description=__doc__.splitlines()[1])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--op", default="av", choices=["av", "qk", "softmax"],
+    p.add_argument("--op", default="av", choices=["av", "qk", "softmax", "attn"],
                    help="av: attention-times-V (the headline); qk: the decode score step before it; "
-                        "softmax: the fused softmax x V product on the scores")
+                        "softmax: the fused softmax x V product on the scores; attn: fused decode attention "
+                        "(scores, softmax and product in one pass over bf16 K and V)")
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=-1,
                    help="untimed warmup steps; -1 (default): at least 20 and about 0.25 s of GPU work, "
@@ -510,6 +513,68 @@ def bench_qk(args, w, dev, props):
     print(json.dumps(line), flush=True)
 
 
+ATTN_METRIC = "GQA fused decode attention (q.K, softmax, x V in one pass): µs/call and achieved HBM GB/s (% of MI355X peak)"
+
+
+def bench_attn(args, w, dev, props):
+    """Fused decode attention on the workload's shape (bf16 K and V, D of 64,
+    128 or 256): K and V once + q + out per call. The score step followed by
+    the fused softmax product on the same inputs is timed beside it."""
+    import torch
+
+    import gqa_reuse_attn_amd as ga
+    from workloads import make_inputs, make_qk_random
+
+    if w.v_dtype != "bf16" or w.D not in (64, 128, 256):
+        raise SystemExit("--op attn takes the bf16 workloads with D of 64, 128 or 256")
+    q_h, K_h = make_qk_random(w.B, w.C, w.Hq, w.Hkv, w.D, "bf16", seed=0)
+    _, V_h = make_inputs(w, seed=0)
+    scale = w.D ** -0.5
+    alg = 2 * w.v_bytes() + 4 * w.B * w.Hq * w.D + w.out_bytes()
+    plan = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, "bf16", args.mode, nsplit=args.nsplit, kv_tile=args.kv_tile,
+                        cu_count=props.multi_processor_count, attention=True)
+    nrot = max(1, math.ceil(args.rotate_mb * 2 ** 20 / alg))
+    q0, k0, v0 = q_h.to(dev), K_h.to(dev), V_h.to(dev)
+    sets = [(q0, k0, v0) if i == 0 else (q0.clone(), k0.clone(), v0.clone()) for i in range(nrot)]
+    calls = [ga.BoundAttention(q, k, v, scale=scale, plan=plan) for q, k, v in sets]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    _warm(args, calls, nrot)
+    ms = _timed(calls, nrot, args.steps, stream)
+    gbs = alg / (ms / 1e3) / 1e9
+    p1_ms = _timed_pass1(calls, nrot, args.steps, stream)
+    # the unfused pair on the same inputs: score step, then the fused softmax product
+    scores = [torch.empty((w.B, w.C, w.Hq), device=dev) for _ in range(nrot)]
+    qk = [ga.bind_qk(q, k, scores=sc, scale=scale) for (q, k, _), sc in zip(sets, scores)]
+    sav = [ga.bind_softmax(sc, v) for (_, _, v), sc in zip(sets, scores)]
+    pair = [lambda i=i: (qk[i](), sav[i]()) for i in range(nrot)]
+    _warm(args, pair, nrot)
+    pair_ms = _timed(pair, nrot, args.steps, stream)
+    print(f"[bench] attn {ms * 1e3:.2f} us/call, {gbs:.1f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of peak); pass 1 "
+          f"{p1_ms * 1e3:.2f} us; score step + fused softmax {pair_ms * 1e3:.2f} us; {nrot} rotation sets, "
+          f"plan {plan.as_dict()}", file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        orc = oracle.get()
+        nb = max(1, min(w.B, int(2e8 // max(1, w.C * w.Hq * w.D * 4))))    # a bounded sample of sequences
+        part = alg * nb // w.B
+        cpu = _oracle_rate(lambda n: orc.attention(q_h[:nb], K_h[:nb], V_h[:nb], "bf16", scale, nthreads=n), part,
+                           args.cpu_seconds, f"attention of {nb} of the {w.B} sequences of {w.name}")
+    line = {
+        "metric": ATTN_METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "us_per_call": round(ms * 1e3, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"attn:{w.name}", "B": w.B, "C": w.C, "Hq": w.Hq, "Hkv": w.Hkv, "G": w.G, "D": w.D,
+                   "kv_dtype": "bf16", "mode": args.mode, "algorithmic_bytes": alg, "rotation_sets": nrot,
+                   "unfused_us_per_call": round(pair_ms * 1e3, 3), "plan": plan.as_dict()},
+        "roofline": _pass1_roofline(alg, p1_ms, recorded_traffic(w.name, args.mode, "attn")
+                                    if args.nsplit == 0 and args.kv_tile == 0 else None),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_trace:
@@ -542,6 +607,9 @@ def main():
           file=sys.stderr, flush=True)
     if args.op == "qk":
         bench_qk(args, w, dev, props)
+        return
+    if args.op == "attn":
+        bench_attn(args, w, dev, props)
         return
     if args.page_size > 0:
         bench_paged(args, w, dev, props)

@@ -50,7 +50,8 @@ class GqaAvError(RuntimeError):
 class Hint(ctypes.Structure):
     _fields_ = [("engine", ctypes.c_int32), ("nsplit", ctypes.c_int32), ("cu_count", ctypes.c_int32),
                 ("v_align", ctypes.c_int32), ("combine", ctypes.c_int32), ("kv_tile", ctypes.c_int32),
-                ("softmax", ctypes.c_int32), ("page_size", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2)]
+                ("softmax", ctypes.c_int32), ("page_size", ctypes.c_int32), ("attention", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 1)]
 
 
 class Plan(ctypes.Structure):
@@ -60,7 +61,7 @@ class Plan(ctypes.Structure):
                 ("threads", ctypes.c_int32), ("rows_per_split", ctypes.c_int64), ("grid", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_int64), ("v_bytes_read", ctypes.c_int64),
                 ("combine", ctypes.c_int32), ("kv_heads_per_tile", ctypes.c_int32), ("softmax", ctypes.c_int32),
-                ("page_size", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2)]
+                ("page_size", ctypes.c_int32), ("attention", ctypes.c_int32), ("reserved", ctypes.c_int32 * 1)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
@@ -78,7 +79,7 @@ class QkPlan(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("engine", ctypes.c_int32), ("heads_per_tile", ctypes.c_int32),
                 ("subgroups", ctypes.c_int32), ("rows_per_block", ctypes.c_int64), ("grid", ctypes.c_int64),
                 ("k_bytes_read", ctypes.c_int64), ("kv_heads_per_tile", ctypes.c_int32),
-                ("page_size", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2)]
+                ("page_size", ctypes.c_int32), ("attention", ctypes.c_int32), ("reserved", ctypes.c_int32 * 1)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
@@ -122,6 +123,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         getattr(lib, fn).restype = ip
     lib.gqa_av_fp8_decode.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ip, ip, vp]
     lib.gqa_av_fp8_decode.restype = ip
+    lib.gqa_attention_decode.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ip, ctypes.c_float, ip, vp]
+    lib.gqa_attention_decode.restype = ip
+    for fn in ("gqa_attention_decode_plan", "gqa_attention_decode_pass1", "gqa_attention_decode_combine"):
+        getattr(lib, fn).argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ip, ctypes.c_float,
+                                     ctypes.POINTER(Plan), vp]
+        getattr(lib, fn).restype = ip
     for fn in ("gqa_av_fp8_decode_plan", "gqa_av_fp8_decode_pass1", "gqa_av_fp8_decode_combine"):
         getattr(lib, fn).argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.POINTER(Plan), vp]
         getattr(lib, fn).restype = ip
@@ -182,12 +189,13 @@ def resolve_mode(Hq: int, Hkv: int, mode: Union[str, int] = "auto") -> str:
 def make_plan(B: int, C: int, Hq: int, Hkv: int, D: int, v_dtype: str, mode: Union[str, int] = "auto",
               engine: Union[str, int] = "auto", nsplit: int = 0, cu_count: int = 0, v_align: int = 0,
               combine: Union[str, int] = "auto", kv_tile: int = 0, softmax: bool = False,
-              page_size: int = 0) -> Plan:
+              page_size: int = 0, attention: bool = False) -> Plan:
     """Host-only planning (no GPU needed). nsplit/cu_count/v_align/kv_tile <= 0 mean automatic.
 
     engine: "auto" | "valu" | "mfma" | "mfma_bf16"; combine: "auto" | "kernel" | "last";
     kv_tile: adjacent KV heads per workgroup; softmax: plan the fused softmax product;
-    page_size > 0: plan for a paged V cache with that many rows per page.
+    page_size > 0: plan for a paged V cache with that many rows per page;
+    attention: plan the fused decode attention (scores from q and K; bf16).
     """
     h = Hint()
     h.engine = ENGINES[engine] if isinstance(engine, str) else int(engine)
@@ -195,6 +203,7 @@ def make_plan(B: int, C: int, Hq: int, Hkv: int, D: int, v_dtype: str, mode: Uni
     h.nsplit, h.cu_count, h.v_align, h.kv_tile = int(nsplit), int(cu_count), int(v_align), int(kv_tile)
     h.softmax = 1 if softmax else 0
     h.page_size = int(page_size)
+    h.attention = 1 if attention else 0
     p = Plan()
     rc = load().gqa_av_make_plan(B, C, Hq, Hkv, D, DTYPES[v_dtype], _mode(mode), ctypes.byref(h), ctypes.byref(p))
     if rc != 0:
@@ -749,3 +758,85 @@ class BoundQkPaged:
         if rc != 0:
             _raise(rc)
         return self.scores
+
+
+# ---- fused decode attention ----------------------------------------------------
+
+def _check_attention(q, K, V, out):
+    torch = _torch()
+    if q.dim() != 3 or K.dim() != 4 or tuple(V.shape) != tuple(K.shape):
+        raise ValueError("q [B,Hq,D], K and V [B,C,Hkv,D] of one shape")
+    B, Hq, D = q.shape
+    _, C, Hkv, D2 = K.shape
+    if K.shape[0] != B or D2 != D:
+        raise ValueError(f"K {tuple(K.shape)} does not match q {tuple(q.shape)} in B or D")
+    if q.dtype != torch.float32 or K.dtype != torch.bfloat16 or V.dtype != torch.bfloat16:
+        raise TypeError("q must be float32, K and V bfloat16")
+    for t in (q, K, V):
+        if not t.is_cuda or t.device != q.device or not t.is_contiguous():
+            raise ValueError("q, K and V must be contiguous GPU tensors on one device")
+    if out is not None and (out.dtype != torch.float32 or tuple(out.shape) != (B, Hq, D) or not out.is_contiguous()
+                            or out.device != q.device):
+        raise ValueError(f"out must be a contiguous float32 [{B},{Hq},{D}] tensor on {q.device}")
+    return B, C, Hq, Hkv, D
+
+
+def gqa_attention_decode(q, K, V, out=None, scale: float = 1.0, mode: Union[str, int] = "auto", stream=None,
+                         plan: Optional[Plan] = None):
+    """Fused decode attention on the GPU: out[b,q_h] = softmax_c(scale * q[b,q_h] . K[b,c,q_h//G]) @ V[b,:,q_h//G];
+    q float32 [B,Hq,D], K and V bfloat16 [B,C,Hkv,D] (D of 64, 128 or 256); returns out [B,Hq,D] float32."""
+    torch = _torch()
+    B, C, Hq, Hkv, D = _check_attention(q, K, V, out)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    lib = load()
+    args = (q.data_ptr(), K.data_ptr(), V.data_ptr(), out.data_ptr(), B, C, Hq, Hkv, D, DTYPES["bf16"], float(scale))
+    with torch.cuda.device(q.device):
+        if plan is None:
+            rc = lib.gqa_attention_decode(*args, _mode(mode), stream.cuda_stream)
+        else:
+            rc = lib.gqa_attention_decode_plan(*args, ctypes.byref(plan), stream.cuda_stream)
+    if rc != 0:
+        _raise(rc)
+    return out
+
+
+class BoundAttention:
+    """A fused attention call with checked, bound arguments for loops (see BoundCall)."""
+
+    def __init__(self, q, K, V, out=None, scale: float = 1.0, plan: Optional[Plan] = None,
+                 mode: Union[str, int] = "auto", stream=None):
+        torch = _torch()
+        B, C, Hq, Hkv, D = _check_attention(q, K, V, out)
+        if out is None:
+            out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        if plan is None:
+            cu = torch.cuda.get_device_properties(q.device).multi_processor_count
+            plan = make_plan(B, C, Hq, Hkv, D, "bf16", mode, cu_count=cu, attention=True)
+        self.tensors, self.out, self.plan = (q, K, V), out, plan
+        lib = load()
+        self._fn, self._pass1, self._combine = (lib.gqa_attention_decode_plan, lib.gqa_attention_decode_pass1,
+                                                lib.gqa_attention_decode_combine)
+        self._args = (q.data_ptr(), K.data_ptr(), V.data_ptr(), out.data_ptr(), B, C, Hq, Hkv, D, DTYPES["bf16"],
+                      ctypes.c_float(scale), ctypes.byref(plan), stream.cuda_stream)
+
+    def __call__(self):
+        rc = self._fn(*self._args)
+        if rc != 0:
+            _raise(rc)
+        return self.out
+
+    def pass1(self):
+        rc = self._pass1(*self._args)
+        if rc != 0:
+            _raise(rc)
+
+    def combine(self):
+        rc = self._combine(*self._args)
+        if rc != 0:
+            _raise(rc)
+        return self.out

@@ -104,6 +104,9 @@ struct Pass1Args {
     int32_t page_shift;          // paged V: log2 of the rows per page
     int32_t max_pages;           // paged V: length of a block-table row
     const float* v_scale;        // fp8 V: [Hkv] scale of each KV head's values (NULL: 1)
+    const float* q;              // fused attention: [B][Hq][D] queries (the scores are computed, not read)
+    const uint8_t* K;            // fused attention: [B][C][Hkv][D] keys, V's element type
+    float qk_scale;              // fused attention: the scores are qk_scale * q . K
     uint32_t* counters;     // combine in kernel: [tiles], zero between calls
     int32_t combine;        // 1: last workgroup of a tile adds the splits; 0: second kernel
     int64_t C;
@@ -887,8 +890,18 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma(Pass1Args a) {
 // PG: paged V (see av_pass1_valu): the split's page list in LDS, each lane's
 // row addresses from it, rows past the sequence's length reading the split's
 // last valid row with weight 0.
-template <int PR, int NSET, int U, int HT, bool SM = false, int VDT = kBF16, bool PG = false>
+//
+// QK: fused decode attention (with SM, bf16 K and V, dense). Each chunk's K rows
+// go through the same LDS region as its V rows; S = Q K^T for the tile's 16
+// heads and the chunk's 32 rows comes from v_mfma_f32_16x16x32_bf16 with the
+// queries as the A operand, split exactly into three bf16 terms, and the K
+// rows as the B operand (16 bytes of one row per lane, read straight from the
+// swizzled region); S times qk_scale then passes through the region once more
+// to reach the weights' layout, and the fused softmax runs on it as on scores
+// read from memory.
+template <int PR, int NSET, int U, int HT, bool SM = false, int VDT = kBF16, bool PG = false, bool QK = false>
 __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
+    static_assert(!QK || (SM && VDT == kBF16 && !PG), "fused attention: bf16 K and V, dense, fused softmax");
     static_assert(PR == 8 || PR == 16 || PR == 32, "D must be 64, 128 or 256");
     static_assert(VDT == kBF16 || VDT == kFP8, "bf16 or fp8 V");
     constexpr bool FP8 = VDT == kFP8;
@@ -959,6 +972,32 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
     int wlane[NSET];
 #pragma unroll
     for (int s = 0; s < NSET; ++s) wlane[s] = (8 * g * a.Hq + kvl * a.G + min(m + 16 * s, T.nq - 1)) * 4;
+    // QK: K through a resource like V's, and this lane's query operand: head
+    // m + 16 s of the wave's KV head (heads past the tile read its last head),
+    // d = 32 kk + 8 g .. + 7, as three exact bf16 terms.
+    const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(QK ? a.K : a.V) + ((static_cast<size_t>(T.b) * a.C + cb) * a.Hkv + T.kv) * D * VES, 0,
+        QK && nrows > 0 ? (nrows - 1) * vrow + HT * D * VES : 0, kRawBufferFlags);
+    constexpr int NKK = QK ? D / 32 : 1;             // 32-wide d blocks of a score
+    u32x4 qa[3][NSET][NKK];
+    if constexpr (QK) {
+#pragma unroll
+        for (int s = 0; s < NSET; ++s) {
+            const float* qrow = a.q + (static_cast<size_t>(T.b) * a.Hq + T.q_first + kvl * a.G +
+                                       min(m + 16 * s, T.nq - 1)) * D + 8 * g;
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    uint32_t th[2], tm[2], tl[2];
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) split_bf16x3(qrow[32 * kk + 2 * p + e], th[e], tm[e], tl[e]);
+                    qa[0][s][kk][p] = (th[0] >> 16) | th[1];
+                    qa[1][s][kk][p] = (tm[0] >> 16) | tm[1];
+                    qa[2][s][kk][p] = (tl[0] >> 16) | tl[1];
+                }
+        }
+    }
 
     // LDS region of this wave: 32 rows of RB bytes, each row cut into 32-byte
     // column pairs (16 columns) whose order is XORed with swz(row) so that
@@ -1001,7 +1040,8 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
     typedef typename std::conditional<FP8, u32x2, u32x4>::type Piece;
     struct Buf {
         Piece v[U][LPI];
-        float w[U][NSET][8];
+        Piece k[QK ? U : 1][QK ? LPI : 1];           // QK: the chunk's K pieces
+        float w[U][NSET][QK ? 1 : 8];                // weights or scores read from memory (not with QK)
     };
     // Chunk u of step st starts at split row 32 (st WPH U + u WPH + wh).
     auto load = [&](Buf& bf, int st) {
@@ -1022,14 +1062,19 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
                 } else {
                     bf.v[u][i] = __builtin_amdgcn_raw_buffer_load_b128(vres, vlane, (r0 + RPI * i) * vrow,
                                                                        kCachePolicyNt);
+                    if constexpr (QK)
+                        bf.k[u][i] = __builtin_amdgcn_raw_buffer_load_b128(kres, vlane, (r0 + RPI * i) * vrow,
+                                                                           kCachePolicyNt);
                 }
             }
+            if constexpr (!QK) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+                for (int j = 0; j < 8; ++j)
 #pragma unroll
-                for (int s = 0; s < NSET; ++s)
-                    bf.w[u][s][j] = __uint_as_float(
-                        __builtin_amdgcn_raw_buffer_load_b32(wres, wlane[s], (r0 + j) * a.Hq * 4, 0));
+                    for (int s = 0; s < NSET; ++s)
+                        bf.w[u][s][j] = __uint_as_float(
+                            __builtin_amdgcn_raw_buffer_load_b32(wres, wlane[s], (r0 + j) * a.Hq * 4, 0));
+            }
         }
     };
     auto consume = [&](const Buf& bf, int st) {
@@ -1038,6 +1083,60 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
             // The region's previous contents have been read (in program
             // order; LDS executes one wave's operations in order).
             asm volatile("" ::: "memory");
+            // QK: the chunk's scores, in the weights' layout (head m + 16 s, rows 8 g .. 8 g + 7).
+            float sc[QK ? NSET : 1][QK ? 8 : 1];
+            if constexpr (QK) {
+#pragma unroll
+                for (int i = 0; i < LPI; ++i)
+                    *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(region + st_off(i)) = bf.k[u][i];
+                asm volatile("" ::: "memory");
+                // B operand: lane 16 g + n holds row 16 t2 + n, d = 32 kk + 8 g .. + 7 (piece 4 kk + g).
+                f32x4 sacc[NSET][2];
+#pragma unroll
+                for (int s = 0; s < NSET; ++s)
+#pragma unroll
+                    for (int t2 = 0; t2 < 2; ++t2) sacc[s][t2] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+                    for (int kk = 0; kk < NKK; ++kk) {
+                        const int row = 16 * t2 + m, piece = 4 * kk + g;
+                        const u32x4 kb = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+                            region + row * RB + 32 * ((piece >> 1) ^ swz(row)) + 16 * (piece & 1));
+#pragma unroll
+                        for (int k = 0; k < 3; ++k)
+#pragma unroll
+                            for (int s = 0; s < NSET; ++s)
+                                sacc[s][t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    __builtin_bit_cast(bf16x8, qa[k][s][kk]), __builtin_bit_cast(bf16x8, kb),
+                                    sacc[s][t2], 0, 0, 0);
+                    }
+                asm volatile("" ::: "memory");
+                // Register i of sacc[s][t2] in lane 16 g' + n' is head 16 s + 4 g' + i, row 16 t2 + n';
+                // through the region as [head][32 rows] floats to head m + 16 s, rows 8 g .. 8 g + 7.
+                typedef __attribute__((address_space(3))) float lds_f;
+                lds_f* const sreg = reinterpret_cast<lds_f*>(region);
+#pragma unroll
+                for (int s = 0; s < NSET; ++s)
+#pragma unroll
+                    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            sreg[(16 * s + 4 * g + i) * 32 + 16 * t2 + m] = sacc[s][t2][i] * a.qk_scale;
+                asm volatile("" ::: "memory");
+#pragma unroll
+                for (int s = 0; s < NSET; ++s) {
+                    typedef __attribute__((address_space(3))) f32x4 lds_f4;
+                    const f32x4 lo = *reinterpret_cast<const lds_f4*>(sreg + (16 * s + m) * 32 + 8 * g);
+                    const f32x4 hi = *reinterpret_cast<const lds_f4*>(sreg + (16 * s + m) * 32 + 8 * g + 4);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        sc[s][j] = lo[j];
+                        sc[s][4 + j] = hi[j];
+                    }
+                }
+                asm volatile("" ::: "memory");
+            }
 #pragma unroll
             for (int i = 0; i < LPI; ++i) {
                 u32x4 piece;
@@ -1069,7 +1168,10 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
                     float t = -INFINITY;
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
-                        wt[s][j] = rb + j < nrows ? bf.w[u][s][j] : -INFINITY;
+                        float x;
+                        if constexpr (QK) x = sc[s][j];
+                        else x = bf.w[u][s][j];
+                        wt[s][j] = rb + j < nrows ? x : -INFINITY;
                         t = fmaxf(t, wt[s][j]);
                     }
                     t = fmaxf(t, __shfl_xor(t, 16));

@@ -20,8 +20,9 @@ hipError_t valu(int VB, int GT, bool paged, const gqa_av::Pass1Args& a, hipStrea
 hipError_t mfma(int DT, int DE, int nset, const gqa_av::Pass1Args& a, hipStream_t s);
 
 // bf16 matrix engine, V of element type VDT (gqa_av::kBF16 or kFP8), paged V
-// when PG: D of 64, 128 or 256, nset sets of 16 heads, ht KV heads per tile.
-template <int VDT, bool SM, bool PG = false>
+// when PG, fused attention (scores from q and K) when QK: D of 64, 128 or
+// 256, nset sets of 16 heads, ht KV heads per tile.
+template <int VDT, bool SM, bool PG = false, bool QK = false>
 hipError_t mfma_bf16(int64_t D, int nset, int ht, const gqa_av::Pass1Args& a, hipStream_t s);
 
 // Score step, K of element type KDT: D / 32 blocks, nset sets of 16 heads.

@@ -10,6 +10,7 @@
 #include "gqa_av.h"
 #include "gqa_fp8_av.h"
 #include "gqa_paged_av.h"
+#include "gqa_attention.h"
 #include "gqa_softmax_av.h"
 
 #include <hip/hip_runtime.h>
@@ -161,6 +162,12 @@ hipError_t launch_pass1(int v_dtype, const gqa_av_plan& p, int64_t D, const Pass
     const int dt = v_dtype == GQA_AV_F32 ? gqa_av::kF32
                  : v_dtype == GQA_AV_F16 ? gqa_av::kF16
                  : v_dtype == GQA_AV_BF16 ? gqa_av::kBF16 : gqa_av::kFP8;
+    if (p.attention) {
+        if (v_dtype != GQA_AV_BF16 || p.engine != GQA_AV_ENGINE_MFMA_BF16 || p.page_size > 0 || !p.softmax)
+            return hipErrorInvalidValue;
+        return gqa_av_launch::mfma_bf16<gqa_av::kBF16, true, false, true>(D, p.heads_per_tile / 16,
+                                                                           p.kv_heads_per_tile, a, s);
+    }
     if (p.engine == GQA_AV_ENGINE_MFMA_BF16) {
         if (v_dtype != GQA_AV_BF16 && v_dtype != GQA_AV_FP8_E4M3) return hipErrorInvalidValue;
         const int nset = p.heads_per_tile / 16, ht = p.kv_heads_per_tile;
@@ -268,6 +275,18 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
     if (h.combine < GQA_AV_COMBINE_AUTO || h.combine > GQA_AV_COMBINE_LAST)
         return fail(GQA_AV_ERR_INVALID_ARG, "unknown combine %d", h.combine);
     if (h.softmax != 0 && h.softmax != 1) return fail(GQA_AV_ERR_INVALID_ARG, "hint softmax must be 0 or 1");
+    if (h.attention != 0 && h.attention != 1) return fail(GQA_AV_ERR_INVALID_ARG, "hint attention must be 0 or 1");
+    // Fused attention: the fused softmax product on the bf16 matrix engine, its
+    // scores computed from q and K.
+    const bool attention = h.attention == 1;
+    if (attention) {
+        if (v_dtype != GQA_AV_BF16 || h.page_size != 0)
+            return fail(GQA_AV_ERR_UNSUPPORTED, "fused attention takes dense bf16 K and V");
+        if (h.engine != GQA_AV_ENGINE_AUTO && h.engine != GQA_AV_ENGINE_MFMA_BF16)
+            return fail(GQA_AV_ERR_UNSUPPORTED, "fused attention runs on the bf16 matrix engine");
+        h.softmax = 1;
+        h.engine = GQA_AV_ENGINE_MFMA_BF16;
+    }
     const bool sm = h.softmax == 1;
     // Paged V: the VALU engine with 16-byte lane loads or the bf16 matrix
     // engine, the kernel combine, and splits short enough for their page list
@@ -500,6 +519,7 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
     plan->v_bytes_read = B * C * Hkv * D * es * heads_major;
     plan->softmax = sm ? 1 : 0;
     plan->page_size = static_cast<int32_t>(P);
+    plan->attention = attention ? 1 : 0;
     return GQA_AV_OK;
 }
 
@@ -509,7 +529,7 @@ bool same_plan(const gqa_av_plan& a, const gqa_av_plan& b) {
            a.row_slots == b.row_slots && a.d_tiles == b.d_tiles && a.nsplit == b.nsplit &&
            a.threads == b.threads && a.rows_per_split == b.rows_per_split && a.grid == b.grid &&
            a.workspace_bytes == b.workspace_bytes && a.kv_heads_per_tile == b.kv_heads_per_tile &&
-           a.softmax == b.softmax && a.page_size == b.page_size;
+           a.softmax == b.softmax && a.page_size == b.page_size && a.attention == b.attention;
 }
 
 }  // namespace
@@ -560,14 +580,24 @@ struct PagedArgs {
     int64_t page_size, max_pages, num_pages;
 };
 
+// The query and key arguments of the fused attention entry points.
+struct AttnArgs {
+    const float* q;
+    const void* K;
+    float scale;
+};
+
 // softmax: 1 for the fused softmax entry points (attn then holds the scores);
 // pg: the paged cache (V then points at its pages), or NULL for dense V.
 int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
              int64_t D, int v_dtype, const gqa_av_plan* plan, void* stream, int which, int softmax,
-             const PagedArgs* pg = nullptr, const float* v_scale = nullptr) {
+             const PagedArgs* pg = nullptr, const float* v_scale = nullptr, const AttnArgs* at = nullptr) {
     if (!plan) return fail(GQA_AV_ERR_INVALID_ARG, "plan is NULL");
     int rc = check_sizes(B, C, Hq, Hkv, D, v_dtype);
     if (rc != GQA_AV_OK) return rc;
+    if ((plan->attention == 1) != (at != nullptr))
+        return fail(GQA_AV_ERR_INVALID_ARG, at ? "not a fused attention plan (plan->attention == 0)"
+                                                : "a fused attention plan: run it with gqa_attention_decode_plan");
     if ((plan->page_size > 0) != (pg != nullptr))
         return fail(GQA_AV_ERR_INVALID_ARG, pg ? "not a paged plan (plan->page_size == 0)"
                                                 : "a paged plan: run it with gqa_av_paged_decode_plan");
@@ -595,6 +625,7 @@ int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C,
     h.kv_tile = plan->kv_heads_per_tile;
     h.softmax = plan->softmax;
     h.page_size = plan->page_size;
+    h.attention = plan->attention;
     gqa_av_plan check;
     const int mode = plan->mode;
     // Re-plan with the split count fixed: rows_per_split then follows from C.
@@ -632,7 +663,14 @@ int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C,
         return fail(GQA_AV_ERR_INVALID_ARG, "plan workspace does not match the problem");
 
     if (B == 0) return GQA_AV_OK;
-    if (!attn && C > 0) return fail(GQA_AV_ERR_INVALID_ARG, softmax ? "scores is NULL" : "attn is NULL");
+    if (at) {
+        if (C > 0 && (!at->q || !at->K)) return fail(GQA_AV_ERR_INVALID_ARG, "q and K must not be NULL");
+        if (reinterpret_cast<uintptr_t>(at->q) & 3u) return fail(GQA_AV_ERR_INVALID_ARG, "q must be 4-byte aligned");
+        if (reinterpret_cast<uintptr_t>(at->K) % static_cast<uintptr_t>(load_alignment(plan->vec_bytes)))
+            return fail(GQA_AV_ERR_UNSUPPORTED, "K is not aligned to the plan's %d-byte loads", plan->vec_bytes);
+    } else if (!attn && C > 0) {
+        return fail(GQA_AV_ERR_INVALID_ARG, softmax ? "scores is NULL" : "attn is NULL");
+    }
     if (!V && C > 0) return fail(GQA_AV_ERR_INVALID_ARG, "V is NULL");
     if (!out) return fail(GQA_AV_ERR_INVALID_ARG, "out is NULL");
     if ((reinterpret_cast<uintptr_t>(attn) & 3u) || (reinterpret_cast<uintptr_t>(out) & 3u))
@@ -663,6 +701,9 @@ int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C,
     a.stats = (softmax && plan->nsplit > 1) ? part + stats_offset(plan->nsplit, B, Hq, D) : nullptr;
     a.counters = counters;
     a.v_scale = v_scale;
+    a.q = at ? at->q : nullptr;
+    a.K = at ? static_cast<const uint8_t*>(at->K) : nullptr;
+    a.qk_scale = at ? at->scale : 0.0f;
     a.block_table = pg ? pg->block_table : nullptr;
     a.seq_lens = pg ? pg->seq_lens : nullptr;
     a.num_pages = pg ? pg->num_pages : 0;
@@ -731,7 +772,7 @@ int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C,
 
 // The automatic plan for the current device and V's address alignment.
 int auto_plan(const void* V, int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dtype, int mode,
-              int softmax, gqa_av_plan* plan, int64_t page_size = 0) {
+              int softmax, gqa_av_plan* plan, int64_t page_size = 0, int attention = 0) {
     int rc = check_sizes(B, C, Hq, Hkv, D, v_dtype);
     if (rc != GQA_AV_OK) return rc;
     int dev = 0;
@@ -745,6 +786,7 @@ int auto_plan(const void* V, int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int6
     h.engine = GQA_AV_ENGINE_AUTO;
     h.cu_count = cus;
     h.softmax = softmax;
+    h.attention = attention;
     if (page_size < 0 || page_size > INT32_MAX)
         return fail(GQA_AV_ERR_INVALID_ARG, "page_size %lld out of range", (long long)page_size);
     h.page_size = static_cast<int32_t>(page_size);
@@ -888,6 +930,36 @@ int gqa_softmax_av_decode_pass1(const float* scores, const void* V, float* out, 
 int gqa_softmax_av_decode_combine(const float* scores, const void* V, float* out, int64_t B, int64_t C, int64_t Hq,
                                   int64_t Hkv, int64_t D, int v_dtype, const gqa_av_plan* plan, void* stream) {
     return run_plan(scores, V, out, B, C, Hq, Hkv, D, v_dtype, plan, stream, kRunCombine, 1);
+}
+
+int gqa_attention_decode_plan(const float* q, const void* K, const void* V, float* out, int64_t B, int64_t C,
+                              int64_t Hq, int64_t Hkv, int64_t D, int kv_dtype, float scale, const gqa_av_plan* plan,
+                              void* stream) {
+    const AttnArgs at{q, K, scale};
+    return run_plan(nullptr, V, out, B, C, Hq, Hkv, D, kv_dtype, plan, stream, kRunPass1 | kRunCombine, 1, nullptr,
+                    nullptr, &at);
+}
+
+int gqa_attention_decode_pass1(const float* q, const void* K, const void* V, float* out, int64_t B, int64_t C,
+                               int64_t Hq, int64_t Hkv, int64_t D, int kv_dtype, float scale,
+                               const gqa_av_plan* plan, void* stream) {
+    const AttnArgs at{q, K, scale};
+    return run_plan(nullptr, V, out, B, C, Hq, Hkv, D, kv_dtype, plan, stream, kRunPass1, 1, nullptr, nullptr, &at);
+}
+
+int gqa_attention_decode_combine(const float* q, const void* K, const void* V, float* out, int64_t B, int64_t C,
+                                 int64_t Hq, int64_t Hkv, int64_t D, int kv_dtype, float scale,
+                                 const gqa_av_plan* plan, void* stream) {
+    const AttnArgs at{q, K, scale};
+    return run_plan(nullptr, V, out, B, C, Hq, Hkv, D, kv_dtype, plan, stream, kRunCombine, 1, nullptr, nullptr, &at);
+}
+
+int gqa_attention_decode(const float* q, const void* K, const void* V, float* out, int64_t B, int64_t C, int64_t Hq,
+                         int64_t Hkv, int64_t D, int kv_dtype, float scale, int mode, void* stream) {
+    gqa_av_plan plan;
+    int rc = auto_plan(V, B, C, Hq, Hkv, D, kv_dtype, mode, 1, &plan, 0, 1);
+    if (rc != GQA_AV_OK) return rc;
+    return gqa_attention_decode_plan(q, K, V, out, B, C, Hq, Hkv, D, kv_dtype, scale, &plan, stream);
 }
 
 const char* gqa_av_status_string(int status) {

@@ -120,7 +120,8 @@ typedef struct gqa_av_hint {
     int32_t kv_tile;    /* adjacent KV heads per VALU workgroup (their D-rows are contiguous) */
     int32_t softmax;    /* 1: plan the fused softmax product of gqa_softmax_av.h; 0: this header's product */
     int32_t page_size;  /* > 0: plan for a paged V cache of this many rows per page (gqa_paged_av.h) */
-    int32_t reserved[2];
+    int32_t attention;  /* 1: plan the fused decode attention of gqa_attention.h (implies softmax = 1) */
+    int32_t reserved[1];
 } gqa_av_hint;
 
 /* A launch plan: what gqa_av_decode_plan will run. Produced by gqa_av_make_plan. */
@@ -145,7 +146,9 @@ typedef struct gqa_av_plan {
                                 gqa_softmax_av_decode_plan runs; 0: a plan of this header's product */
     int32_t page_size;       /* > 0: a plan for a paged V cache (gqa_paged_av.h) with this many rows per
                                 page, which only gqa_av_paged_decode_plan runs; 0: dense V */
-    int32_t reserved[2];
+    int32_t attention;       /* 1: a plan of the fused decode attention (gqa_attention.h), which only
+                                gqa_attention_decode_plan runs */
+    int32_t reserved[1];
 } gqa_av_plan;
 
 /* Resolve `mode` for a head shape. Host-only: needs no GPU.

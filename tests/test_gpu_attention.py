@@ -1,0 +1,159 @@
+"""GPU parity of fused decode attention (scores, softmax and product in one
+pass over bf16 K and V) through the C ABI, against the fp64 attention oracle.
+
+Bound: the scores carry the score step's fp32 error, |ds_c| <= 2 D 2^-24
+scale sum_d |q K| (every product exact, fp32 sums); a softmax weight moves by
+at most a factor exp(2 max |ds|); on top comes the fused softmax product's
+own arithmetic bound (tests/test_gpu_softmax_av.py). So
+||err|| <= ((2 rng + 512) 2^-24 + 2 max|ds| + 8 sqrt(C) 2^-24) ||A|| with
+A = sum_c p_c |V_c| and rng the range of the exact scores; plus the gate of
+tests/parity.py. All tests need an MI355X and are marked ``gpu``.
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import gqa_reuse_attn_amd as ga
+from tests.parity import gate
+from workloads import WORKLOADS, make_qk_random
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+U32 = 2.0 ** -24
+
+
+def _say(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ga.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _inputs(B, C, Hq, Hkv, D, seed, qscale=1.0):
+    q, K = make_qk_random(B, C, Hq, Hkv, D, "bf16", seed=seed)
+    _, V = make_qk_random(B, C, Hq, Hkv, D, "bf16", seed=seed + 1)
+    return (q * qscale).contiguous(), K, V
+
+
+def _check(out, ref, q, K, V, scale, label):
+    ok, msg = gate(out, ref, "bf16")
+    assert ok, f"{label}: gate failed: {msg}"
+    B, Hq, D = q.shape
+    C, Hkv = K.shape[1], K.shape[2]
+    if C == 0:
+        assert (out == 0).all()
+        return
+    G = Hq // Hkv
+    qd, kd, vd = q.double().numpy(), K.double().numpy(), V.double().numpy()
+    kq = np.repeat(kd, G, axis=2)                          # [B, C, Hq, D]
+    s = scale * np.einsum("bhd,bchd->bch", qd, kq)
+    ds = 2 * D * U32 * abs(scale) * np.einsum("bhd,bchd->bch", np.abs(qd), np.abs(kq))
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    A = np.einsum("bch,bchd->bhd", p, np.abs(np.repeat(vd, G, axis=2)))
+    rng = float(s.max() - s.min())
+    eps = (2.0 * rng + 512.0) * U32 + 2.0 * float(ds.max()) + 8.0 * math.sqrt(C) * U32
+    err = np.linalg.norm((out - ref).ravel())
+    assert err <= eps * np.linalg.norm(A.ravel()) + 1e-30, f"{label}: ||err||={err:.3e} above {eps:.3e} ||A||"
+
+
+def _run(q, K, V, scale, plan=None):
+    out = ga.gqa_attention_decode(q.to(DEV), K.to(DEV), V.to(DEV), scale=scale, plan=plan)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("wname", [n for n, w in WORKLOADS.items() if w.D in (64, 128, 256) and w.v_dtype == "bf16"])
+def test_attention_workloads(wname, oracle_lib):
+    """The bf16 workload shapes (the large batch cut to 8 sequences; the full
+    size is in test_gpu_full_size), scale 1/sqrt(D)."""
+    w = WORKLOADS[wname]
+    if w.B > 8:
+        w = w.replace(B=8)
+    _say(f"[attention] {w.name}")
+    q, K, V = _inputs(w.B, w.C, w.Hq, w.Hkv, w.D, seed=11)
+    scale = w.D ** -0.5
+    _check(_run(q, K, V, scale), oracle_lib.attention(q, K, V, "bf16", scale), q, K, V, scale, f"attention {w.name}")
+
+
+def _cases():
+    cases, k = [], 0
+    for G in (2, 3, 4, 5, 8, 16, 17, 32):
+        for D in (64, 128, 256):
+            for C in (1, 63, 65, 700):
+                if (G + D // 64 + C) % 3 or (G > 16 and D > 128):
+                    continue
+                Hkv = (1, 2, 4)[k % 3]
+                cases.append((1 + k % 2, C, G * Hkv, Hkv, D, (0.125, 1.0, 4.0)[k % 3]))
+                k += 1
+    return cases
+
+
+@pytest.mark.parametrize("B,C,Hq,Hkv,D,qscale", _cases())
+def test_attention_sweep(B, C, Hq, Hkv, D, qscale, oracle_lib):
+    """G 2..32, D 64..256, ragged C, forced splits, 1/2/4 KV heads per
+    workgroup, flat to peaky score distributions."""
+    q, K, V = _inputs(B, C, Hq, Hkv, D, seed=B * 1000 + C + D, qscale=qscale)
+    scale = D ** -0.5
+    ref = oracle_lib.attention(q, K, V, "bf16", scale)
+    plans = [ga.make_plan(B, C, Hq, Hkv, D, "bf16", nsplit=ns, attention=True) for ns in (0, 1, 5)]
+    plans += [ga.make_plan(B, C, Hq, Hkv, D, "bf16", kv_tile=ht, nsplit=3, attention=True)
+              for ht in (2, 4) if Hkv % ht == 0]
+    for plan in plans:
+        _check(_run(q, K, V, scale, plan=plan), ref, q, K, V, scale, f"attention {(B, C, Hq, Hkv, D)} {plan.as_dict()}")
+
+
+def test_attention_pass1_then_combine_is_the_call():
+    B, C, Hq, Hkv, D = 3, 3000, 64, 8, 128
+    q, K, V = _inputs(B, C, Hq, Hkv, D, seed=21)
+    for ns in (0, 1):
+        plan = ga.make_plan(B, C, Hq, Hkv, D, "bf16", nsplit=ns, attention=True)
+        call = ga.BoundAttention(q.to(DEV), K.to(DEV), V.to(DEV), scale=0.1, plan=plan)
+        whole = call().clone()
+        call.out.fill_(float("nan"))
+        call.pass1()
+        got = call.combine()
+        torch.cuda.synchronize()
+        assert torch.equal(whole, got), ns
+
+
+def test_attention_matches_unfused_composition(oracle_lib):
+    """Fused attention against the score step followed by the fused softmax
+    product: both within the oracle's bound, and close to each other."""
+    B, C, Hq, Hkv, D = 2, 2000, 32, 4, 128
+    q, K, V = _inputs(B, C, Hq, Hkv, D, seed=31)
+    scale = D ** -0.5
+    fused = _run(q, K, V, scale)
+    s = ga.gqa_qk_decode(q.to(DEV), K.to(DEV), scale=scale)
+    two = ga.gqa_softmax_av_decode(s, V.to(DEV)).cpu().numpy().astype(np.float64)
+    ref = oracle_lib.attention(q, K, V, "bf16", scale)
+    _check(fused, ref, q, K, V, scale, "fused")
+    _check(two, ref, q, K, V, scale, "score step + fused softmax")
+
+
+def test_attention_edges():
+    q, K, V = _inputs(2, 0, 16, 2, 128, seed=41)
+    out = torch.full((2, 16, 128), float("nan"), device=DEV)
+    ga.gqa_attention_decode(q.to(DEV), K.to(DEV), V.to(DEV), out=out, scale=1.0)
+    torch.cuda.synchronize()
+    assert (out == 0).all(), "C = 0 writes zeros"
+    qq, KK, VV = _inputs(1, 10, 4, 4, 64, seed=42)
+    with pytest.raises(ga.GqaAvError) as e:                # G = 1: no group to reuse over
+        ga.gqa_attention_decode(qq.to(DEV), KK.to(DEV), VV.to(DEV))
+    assert e.value.name == "UNSUPPORTED"
+    with pytest.raises(ga.GqaAvError) as e:
+        ga.gqa_attention_decode(qq.to(DEV), KK.to(DEV), VV.to(DEV), mode="reuse")
+    assert e.value.name == "INELIGIBLE"

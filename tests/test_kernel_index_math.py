@@ -63,6 +63,51 @@ def test_lds_transpose_layout(PR):
             assert max(len(v) for v in banks.values()) <= 2
 
 
+@pytest.mark.parametrize("PR,NSET", [(8, 1), (8, 2), (16, 1), (16, 2), (32, 1)])
+def test_attention_lds_reads(PR, NSET):
+    """Fused attention in the bf16 matrix engine: with K rows stored like V rows,
+    lane 16 g + n's 16-byte read for row 16 t2 + n and d-block kk returns
+    K[row][32 kk + 8 g .. + 7]; the scores pass through the region as
+    [16 NSET heads][32 rows] floats, inside the region, and each lane reads
+    back head m + 16 s, rows 8 g .. 8 g + 7 of what the MFMA result layout
+    wrote (register i of lane 16 g' + n': head 4 g' + i, row n')."""
+    RB, RPI, LPI, D = PR * 16, 64 // PR, PR // 2, PR * 8
+    mem = {}
+    for i in range(LPI):
+        for lane in range(64):
+            prow, pp = lane // PR, lane % PR
+            row = RPI * i + prow
+            off = row * RB + 32 * ((pp >> 1) ^ _swz(PR, row)) + 16 * (pp & 1)
+            for e in range(8):
+                mem[off + 2 * e] = (row, 8 * pp + e)
+    for t2 in range(2):
+        for kk in range(D // 32):
+            for lane in range(64):
+                g, n = lane >> 4, lane & 15
+                row, piece = 16 * t2 + n, 4 * kk + g
+                off = row * RB + 32 * ((piece >> 1) ^ _swz(PR, row)) + 16 * (piece & 1)
+                assert off % 16 == 0 and off + 16 <= 32 * RB
+                assert [mem[off + 2 * e] for e in range(8)] == [(row, 32 * kk + 8 * g + e) for e in range(8)]
+    # scores: written [head][32 rows], read back by (g, m)
+    assert 16 * NSET * 32 * 4 <= 32 * RB, "the score tile fits in the wave's region"
+    wrote = {}
+    for s_ in range(NSET):
+        for t2 in range(2):
+            for lane in range(64):
+                gp, npr = lane >> 4, lane & 15
+                for i in range(4):
+                    idx = (16 * s_ + 4 * gp + i) * 32 + 16 * t2 + npr
+                    assert idx not in wrote
+                    wrote[idx] = (16 * s_ + 4 * gp + i, 16 * t2 + npr)
+    assert len(wrote) == 16 * NSET * 32
+    for s_ in range(NSET):
+        for lane in range(64):
+            g, m = lane >> 4, lane & 15
+            base = (16 * s_ + m) * 32 + 8 * g
+            assert (base * 4) % 16 == 0
+            assert [wrote[base + j] for j in range(8)] == [(16 * s_ + m, 8 * g + j) for j in range(8)]
+
+
 def _remap(i, n):
     per, rem = n // 8, n % 8
     x, k = i % 8, i // 8

@@ -55,7 +55,7 @@ KERNEL_SOURCES["softmax"] = KERNEL_SOURCES["av"]
 KERNEL_SOURCES["attn"] = KERNEL_SOURCES["av"]
 # Profile file prefix and the dominant kernel's name fragment, per operation.
 OPS = {"av": ("pass1", "pass1"), "qk": ("qk", "qk_scores"), "softmax": ("softmax_pass1", "pass1"),
-       "attn": ("attn_pass1", "pass1")}
+       "attn": ("attn_pass1", "false, true>")}   # the fused instantiation (dense, with scores from q and K)
 SOFTMAX_METRIC = "GQA decode fused softmax x V: µs/call and achieved HBM GB/s (% of MI355X peak)"
 
 

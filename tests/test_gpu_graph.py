@@ -125,3 +125,11 @@ def test_graph_qk(shape):
     q, K = make_qk_random(B, C, Hq, Hkv, D, dt, seed=4)
     q, K = q.to(DEV), K.to(DEV)
     _graph_matches_eager(f"qk {shape}", lambda s: ga.bind_qk(q, K, scale=D ** -0.5, stream=s), q, _fresh(q, 4))
+
+
+def test_graph_attention():
+    B, C, Hq, Hkv, D = 2, 3000, 64, 8, 128
+    q, K = make_qk_random(B, C, Hq, Hkv, D, "bf16", seed=6)
+    _, V = make_qk_random(B, C, Hq, Hkv, D, "bf16", seed=7)
+    q, K, V = q.to(DEV), K.to(DEV), V.to(DEV)
+    _graph_matches_eager("attention", lambda s: ga.BoundAttention(q, K, V, scale=0.125, stream=s), q, _fresh(q, 5))

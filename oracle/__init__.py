@@ -74,6 +74,8 @@ class Oracle:
         lib.gqa_qk_paged_oracle.restype = ip
         lib.gqa_attention_oracle.argtypes = [vp, vp, vp, ip, i64, i64, i64, i64, i64, ctypes.c_double, vp, ip]
         lib.gqa_attention_oracle.restype = ip
+        lib.gqa_attention_fp8_oracle.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_double, vp, ip]
+        lib.gqa_attention_fp8_oracle.restype = ip
         self.lib = lib
 
     @staticmethod
@@ -167,6 +169,24 @@ class Oracle:
         out = np.empty((B, Hq, D), dtype=np.float64)
         rc = self.lib.gqa_attention_oracle(qa.ctypes.data, k.ctypes.data, v.ctypes.data, DTYPE_CODE[kv_dtype],
                                            B, C, Hq, Hkv, D, float(scale), out.ctypes.data, nthreads)
+        if rc != 0:
+            raise ValueError(f"oracle rejected the arguments (status {rc})")
+        return out
+
+    def attention_fp8(self, q, K8, V8, k_scale=None, v_scale=None, scale: float = 1.0, nthreads: int = 0) -> np.ndarray:
+        """out[B, Hq, D] (float64): fused attention over fp8 K and V (E4M3 bytes,
+        uint8 or torch.float8_e4m3fn) with per-KV-head scales ([Hkv] fp32 or None)."""
+        qa = np.ascontiguousarray(_as_numpy(q, np.float32))
+        k, v = np.ascontiguousarray(_fp8_bytes(K8)), np.ascontiguousarray(_fp8_bytes(V8))
+        B, Hq, D = qa.shape
+        B2, C, Hkv, D2 = k.shape
+        assert B2 == B and D2 == D and v.shape == k.shape
+        ks = None if k_scale is None else np.ascontiguousarray(_as_numpy(k_scale, np.float32))
+        vs = None if v_scale is None else np.ascontiguousarray(_as_numpy(v_scale, np.float32))
+        out = np.empty((B, Hq, D), dtype=np.float64)
+        rc = self.lib.gqa_attention_fp8_oracle(qa.ctypes.data, k.ctypes.data, None if ks is None else ks.ctypes.data,
+                                               v.ctypes.data, None if vs is None else vs.ctypes.data,
+                                               B, C, Hq, Hkv, D, float(scale), out.ctypes.data, nthreads)
         if rc != 0:
             raise ValueError(f"oracle rejected the arguments (status {rc})")
         return out

@@ -563,3 +563,50 @@ int gqa_attention_oracle(const float *q, const void *K, const void *V, int dtype
     (void)nthreads;
     return ORC_OK;
 }
+
+/* Fused decode attention over fp8 K and V (OCP E4M3 bytes) with per-KV-head
+ * scales (NULL: all 1): the definition above with K and V elements
+ * decode(byte) * k_scale[kv_h] and decode(byte) * v_scale[kv_h]. */
+int gqa_attention_fp8_oracle(const float *q, const uint8_t *K, const float *k_scale, const uint8_t *V,
+                             const float *v_scale, int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D,
+                             double scale, double *out, int nthreads)
+{
+    int rc = orc_check(ORC_F32, B, C, Hq, Hkv, D);
+    if (rc != ORC_OK) return rc;
+    const int64_t G = Hq / Hkv;
+    const int64_t rows = B * Hq;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int64_t i = 0; i < rows; ++i) {
+        const int64_t b = i / Hq, h = i % Hq, kv = h / G;
+        const double ks = k_scale ? (double)k_scale[kv] : 1.0;
+        const double vs = v_scale ? (double)v_scale[kv] : 1.0;
+        double *o = out + i * D;
+        for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+        if (C == 0) continue;
+        const float *qrow = q + (b * Hq + h) * D;
+        double m = -INFINITY;
+        for (int64_t c = 0; c < C; ++c) {
+            const uint8_t *kr = K + ((b * C + c) * Hkv + kv) * D;
+            double dot = 0.0;
+            for (int64_t d = 0; d < D; ++d) dot += (double)qrow[d] * (orc_e4m3(kr[d]) * ks);
+            const double sc = dot * scale;
+            if (sc > m) m = sc;
+        }
+        double l = 0.0;
+        for (int64_t c = 0; c < C; ++c) {
+            const uint8_t *kr = K + ((b * C + c) * Hkv + kv) * D;
+            const uint8_t *vr = V + ((b * C + c) * Hkv + kv) * D;
+            double dot = 0.0;
+            for (int64_t d = 0; d < D; ++d) dot += (double)qrow[d] * (orc_e4m3(kr[d]) * ks);
+            const double e = exp(dot * scale - m);
+            l += e;
+            for (int64_t d = 0; d < D; ++d) o[d] += e * (orc_e4m3(vr[d]) * vs);
+        }
+        for (int64_t d = 0; d < D; ++d) o[d] /= l;
+    }
+    (void)nthreads;
+    return ORC_OK;
+}

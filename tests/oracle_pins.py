@@ -96,6 +96,14 @@ Fused decode attention (softmax of the scaled scores, times V, in one pass):
   * attn_repeat_mha   GQA equals MHA over K and V repeated G times (bitwise).
   * attn_edges        C = 0 gives zeros; B = 0 gives an empty result.
 
+Fused attention over fp8 K and V (E4M3 bytes, per-KV-head scales):
+  * attn_fp8_as_bf16  with unit scales it equals the bf16 attention oracle on K
+                      and V widened by torch's float8 -> bfloat16 conversion,
+                      bit for bit.
+  * attn_fp8_scales   a power-of-two v_scale scales exactly its head group's
+                      outputs; a power-of-two k_scale equals the bf16
+                      attention oracle with scale * k_scale, bit for bit.
+
 fp8 K in the score step (same bytes and per-KV-head scales):
   * qk_fp8_as_bf16    with unit scales the fp8 score oracle equals the bf16
                       score oracle on K widened by torch's float8 -> bfloat16
@@ -855,6 +863,35 @@ def pin_attn_edges(orc):
     assert orc.attention(q0, K0, K0.clone(), "bf16", 1.0).size == 0
 
 
+def pin_attn_fp8_as_bf16(orc):
+    for i, (B, C, Hq, Hkv, D) in enumerate([(2, 23, 6, 2, 16), (1, 40, 8, 1, 8)]):
+        q, _ = make_qk_random(B, C, Hq, Hkv, D, "f32", seed=1200 + i)
+        _, k8 = _fp8_case(B, C, Hq, Hkv, D, seed=1210 + i)
+        _, v8 = _fp8_case(B, C, Hq, Hkv, D, seed=1220 + i)
+        k16 = k8.view(torch.float8_e4m3fn).to(torch.bfloat16)
+        v16 = v8.view(torch.float8_e4m3fn).to(torch.bfloat16)
+        a = orc.attention_fp8(q, k8, v8, None, None, 0.05)
+        assert np.array_equal(a, orc.attention(q, k16, v16, "bf16", 0.05)), f"fp8 attention != bf16 (case {i})"
+
+
+def pin_attn_fp8_scales(orc):
+    B, C, Hq, Hkv, D = 2, 19, 8, 4, 8
+    q, _ = make_qk_random(B, C, Hq, Hkv, D, "f32", seed=1230)
+    _, k8 = _fp8_case(B, C, Hq, Hkv, D, seed=1231)
+    _, v8 = _fp8_case(B, C, Hq, Hkv, D, seed=1232)
+    G = Hq // Hkv
+    base = orc.attention_fp8(q, k8, v8, None, None, 0.02)
+    vs = torch.tensor([0.25, 1.0, 8.0, 2.0 ** -10])
+    o = orc.attention_fp8(q, k8, v8, None, vs, 0.02)
+    for h in range(Hq):
+        assert np.array_equal(o[:, h], base[:, h] * float(vs[h // G])), f"fp8 attention v_scale of head {h}"
+    k16 = k8.view(torch.float8_e4m3fn).to(torch.bfloat16)
+    v16 = v8.view(torch.float8_e4m3fn).to(torch.bfloat16)
+    for ks in (0.5, 4.0):
+        o2 = orc.attention_fp8(q, k8, v8, torch.full((Hkv,), ks), None, 0.02)
+        assert np.array_equal(o2, orc.attention(q, k16, v16, "bf16", 0.02 * ks)), f"fp8 attention k_scale {ks}"
+
+
 ALL_PINS = [pin_decode_table, pin_brute_force, pin_mha_einsum, pin_repeat_mha, pin_constant_v,
             pin_one_hot, pin_linearity, pin_permutation, pin_batch_independence, pin_points,
             pin_edges, pin_qk_brute_force, pin_qk_mha_einsum, pin_qk_repeat_mha, pin_qk_one_hot,
@@ -864,4 +901,4 @@ ALL_PINS = [pin_decode_table, pin_brute_force, pin_mha_einsum, pin_repeat_mha, p
             pin_paged_rejects, pin_fp8_decode, pin_fp8_as_bf16, pin_fp8_scales, pin_qk_fp8_as_bf16,
             pin_qk_fp8_brute, pin_qk_fp8_scales, pin_qk_paged_gather, pin_qk_paged_identity, pin_qk_paged_tail,
             pin_qk_paged_rejects, pin_attn_composition, pin_attn_numpy, pin_attn_zero_q, pin_attn_repeat_mha,
-            pin_attn_edges]
+            pin_attn_edges, pin_attn_fp8_as_bf16, pin_attn_fp8_scales]

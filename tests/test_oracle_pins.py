@@ -94,6 +94,10 @@ PLANTS = [
     ("attn_no_max", "const double e = exp(dot * scale - m);", "const double e = exp(dot * scale);"),
     ("attn_v_from_k", "o[d] += e * orc_load(V, dtype, krow + d);", "o[d] += e * orc_load(K, dtype, krow + d);"),
     ("attn_kv_of_query", "const int64_t b = i / Hq, h = i % Hq, kv = h / G;", "const int64_t b = i / Hq, h = i % Hq, kv = h % Hkv;"),
+    ("attn_fp8_v_scale_of_k", "const double vs = v_scale ? (double)v_scale[kv] : 1.0;",
+     "const double vs = k_scale ? (double)k_scale[kv] : 1.0;"),
+    ("attn_fp8_k_unscaled", "for (int64_t d = 0; d < D; ++d) dot += (double)qrow[d] * (orc_e4m3(kr[d]) * ks);\n            const double e",
+     "for (int64_t d = 0; d < D; ++d) dot += (double)qrow[d] * orc_e4m3(kr[d]);\n            const double e"),
     ("paged_bt_ignores_batch", "const int64_t page = bt[b * max_pages + c / P];",
      "const int64_t page = bt[0 * max_pages + c / P];"),
 ]

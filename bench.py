@@ -530,13 +530,25 @@ def bench_attn(args, w, dev, props):
     q_h, K_h = make_qk_random(w.B, w.C, w.Hq, w.Hkv, w.D, "bf16", seed=0)
     _, V_h = make_inputs(w, seed=0)
     scale = w.D ** -0.5
-    alg = 2 * w.v_bytes() + 4 * w.B * w.Hq * w.D + w.out_bytes()
-    plan = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, "bf16", args.mode, nsplit=args.nsplit, kv_tile=args.kv_tile,
+    kvdt, ks_h, vs_h = "bf16", None, None
+    if args.v_fp8:
+        # fp8 K and V: per-KV-head scale max|x| / 448 and the E4M3 bytes of x / scale
+        def quant(X):
+            Xf = X.float()
+            sc = (Xf.abs().amax(dim=(0, 1, 3)).clamp_min(1e-30) / 448.0).contiguous()
+            return (Xf / sc.view(1, 1, -1, 1)).to(torch.float8_e4m3fn).contiguous(), sc
+        (K_h, ks_h), (V_h, vs_h) = quant(K_h), quant(V_h)
+        kvdt = "fp8"
+    kv_bytes = w.v_bytes() // (2 if args.v_fp8 else 1)
+    alg = 2 * kv_bytes + 4 * w.B * w.Hq * w.D + w.out_bytes()
+    plan = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, kvdt, args.mode, nsplit=args.nsplit, kv_tile=args.kv_tile,
                         cu_count=props.multi_processor_count, attention=True)
     nrot = max(1, math.ceil(args.rotate_mb * 2 ** 20 / alg))
     q0, k0, v0 = q_h.to(dev), K_h.to(dev), V_h.to(dev)
+    ks = ks_h.to(dev) if ks_h is not None else None
+    vs = vs_h.to(dev) if vs_h is not None else None
     sets = [(q0, k0, v0) if i == 0 else (q0.clone(), k0.clone(), v0.clone()) for i in range(nrot)]
-    calls = [ga.BoundAttention(q, k, v, scale=scale, plan=plan) for q, k, v in sets]
+    calls = [ga.BoundAttention(q, k, v, scale=scale, plan=plan, k_scale=ks, v_scale=vs) for q, k, v in sets]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     _warm(args, calls, nrot)
@@ -545,8 +557,9 @@ def bench_attn(args, w, dev, props):
     p1_ms = _timed_pass1(calls, nrot, args.steps, stream)
     # the unfused pair on the same inputs: score step, then the fused softmax product
     scores = [torch.empty((w.B, w.C, w.Hq), device=dev) for _ in range(nrot)]
-    qk = [ga.bind_qk(q, k, scores=sc, scale=scale) for (q, k, _), sc in zip(sets, scores)]
-    sav = [ga.bind_softmax(sc, v) for (_, _, v), sc in zip(sets, scores)]
+    qk = [ga.bind_qk(q, k, scores=sc, scale=scale, k_scale=ks) for (q, k, _), sc in zip(sets, scores)]
+    sav = [(ga.BoundFp8(sc, v, vs, softmax=True) if args.v_fp8 else ga.bind_softmax(sc, v))
+           for (_, _, v), sc in zip(sets, scores)]
     pair = [lambda i=i: (qk[i](), sav[i]()) for i in range(nrot)]
     _warm(args, pair, nrot)
     pair_ms = _timed(pair, nrot, args.steps, stream)
@@ -559,16 +572,19 @@ def bench_attn(args, w, dev, props):
         orc = oracle.get()
         nb = max(1, min(w.B, int(2e8 // max(1, w.C * w.Hq * w.D * 4))))    # a bounded sample of sequences
         part = alg * nb // w.B
-        cpu = _oracle_rate(lambda n: orc.attention(q_h[:nb], K_h[:nb], V_h[:nb], "bf16", scale, nthreads=n), part,
-                           args.cpu_seconds, f"attention of {nb} of the {w.B} sequences of {w.name}")
+        if args.v_fp8:
+            fn = lambda n: orc.attention_fp8(q_h[:nb], K_h[:nb], V_h[:nb], ks_h, vs_h, scale, nthreads=n)  # noqa: E731
+        else:
+            fn = lambda n: orc.attention(q_h[:nb], K_h[:nb], V_h[:nb], "bf16", scale, nthreads=n)  # noqa: E731
+        cpu = _oracle_rate(fn, part, args.cpu_seconds, f"attention of {nb} of the {w.B} sequences of {w.name}")
     line = {
         "metric": ATTN_METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 6), "us_per_call": round(ms * 1e3, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": f"attn:{w.name}", "B": w.B, "C": w.C, "Hq": w.Hq, "Hkv": w.Hkv, "G": w.G, "D": w.D,
-                   "kv_dtype": "bf16", "mode": args.mode, "algorithmic_bytes": alg, "rotation_sets": nrot,
+        "config": {"workload": f"attn{'-fp8' if args.v_fp8 else ''}:{w.name}", "B": w.B, "C": w.C, "Hq": w.Hq,
+                   "Hkv": w.Hkv, "G": w.G, "D": w.D, "kv_dtype": "fp8_e4m3" if args.v_fp8 else "bf16", "mode": args.mode, "algorithmic_bytes": alg, "rotation_sets": nrot,
                    "unfused_us_per_call": round(pair_ms * 1e3, 3), "plan": plan.as_dict()},
-        "roofline": _pass1_roofline(alg, p1_ms, recorded_traffic(w.name, args.mode, "attn")
+        "roofline": _pass1_roofline(alg, p1_ms, recorded_traffic(w.name, args.mode, "attn", "_fp8" if args.v_fp8 else "")
                                     if args.nsplit == 0 and args.kv_tile == 0 else None),
         "cpu_baseline": cpu,
     }

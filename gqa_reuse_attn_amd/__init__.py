@@ -125,6 +125,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gqa_av_fp8_decode.restype = ip
     lib.gqa_attention_decode.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ip, ctypes.c_float, ip, vp]
     lib.gqa_attention_decode.restype = ip
+    lib.gqa_attention_fp8_decode.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, ip, vp]
+    lib.gqa_attention_fp8_decode.restype = ip
+    for fn in ("gqa_attention_fp8_decode_plan", "gqa_attention_fp8_decode_pass1", "gqa_attention_fp8_decode_combine"):
+        getattr(lib, fn).argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
+                                     ctypes.POINTER(Plan), vp]
+        getattr(lib, fn).restype = ip
     for fn in ("gqa_attention_decode_plan", "gqa_attention_decode_pass1", "gqa_attention_decode_combine"):
         getattr(lib, fn).argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ip, ctypes.c_float,
                                      ctypes.POINTER(Plan), vp]
@@ -770,34 +776,51 @@ def _check_attention(q, K, V, out):
     _, C, Hkv, D2 = K.shape
     if K.shape[0] != B or D2 != D:
         raise ValueError(f"K {tuple(K.shape)} does not match q {tuple(q.shape)} in B or D")
-    if q.dtype != torch.float32 or K.dtype != torch.bfloat16 or V.dtype != torch.bfloat16:
-        raise TypeError("q must be float32, K and V bfloat16")
+    if q.dtype != torch.float32 or K.dtype != V.dtype or K.dtype not in (torch.bfloat16, torch.float8_e4m3fn):
+        raise TypeError("q must be float32, K and V both bfloat16 or both float8_e4m3fn")
     for t in (q, K, V):
         if not t.is_cuda or t.device != q.device or not t.is_contiguous():
             raise ValueError("q, K and V must be contiguous GPU tensors on one device")
     if out is not None and (out.dtype != torch.float32 or tuple(out.shape) != (B, Hq, D) or not out.is_contiguous()
                             or out.device != q.device):
         raise ValueError(f"out must be a contiguous float32 [{B},{Hq},{D}] tensor on {q.device}")
-    return B, C, Hq, Hkv, D
+    return B, C, Hq, Hkv, D, ("fp8" if K.dtype == torch.float8_e4m3fn else "bf16")
+
+
+def _attention_args(q, K, V, out, B, C, Hq, Hkv, D, kvdt, scale, k_scale, v_scale):
+    """The C arguments (before mode/plan and stream) of the bf16 or fp8 entry points."""
+    if kvdt != "fp8":
+        if k_scale is not None or v_scale is not None:
+            raise ValueError("k_scale and v_scale are for fp8 K and V")
+        return (q.data_ptr(), K.data_ptr(), V.data_ptr(), out.data_ptr(), B, C, Hq, Hkv, D, DTYPES["bf16"],
+                ctypes.c_float(scale))
+    ks = _check_scale(k_scale, Hkv, q.device)
+    vs = _check_scale(v_scale, Hkv, q.device)
+    return (q.data_ptr(), K.data_ptr(), ks.data_ptr() if ks is not None else None, V.data_ptr(),
+            vs.data_ptr() if vs is not None else None, out.data_ptr(), B, C, Hq, Hkv, D, ctypes.c_float(scale))
 
 
 def gqa_attention_decode(q, K, V, out=None, scale: float = 1.0, mode: Union[str, int] = "auto", stream=None,
-                         plan: Optional[Plan] = None):
+                         plan: Optional[Plan] = None, k_scale=None, v_scale=None):
     """Fused decode attention on the GPU: out[b,q_h] = softmax_c(scale * q[b,q_h] . K[b,c,q_h//G]) @ V[b,:,q_h//G];
-    q float32 [B,Hq,D], K and V bfloat16 [B,C,Hkv,D] (D of 64, 128 or 256); returns out [B,Hq,D] float32."""
+    q float32 [B,Hq,D], K and V bfloat16 [B,C,Hkv,D] (D of 64, 128 or 256), or both float8_e4m3fn with
+    per-KV-head scales k_scale and v_scale (float32 [Hkv], None = 1); returns out [B,Hq,D] float32."""
     torch = _torch()
-    B, C, Hq, Hkv, D = _check_attention(q, K, V, out)
+    B, C, Hq, Hkv, D, kvdt = _check_attention(q, K, V, out)
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     lib = load()
-    args = (q.data_ptr(), K.data_ptr(), V.data_ptr(), out.data_ptr(), B, C, Hq, Hkv, D, DTYPES["bf16"], float(scale))
+    args = _attention_args(q, K, V, out, B, C, Hq, Hkv, D, kvdt, scale, k_scale, v_scale)
+    fp8 = kvdt == "fp8"
     with torch.cuda.device(q.device):
         if plan is None:
-            rc = lib.gqa_attention_decode(*args, _mode(mode), stream.cuda_stream)
+            fn = lib.gqa_attention_fp8_decode if fp8 else lib.gqa_attention_decode
+            rc = fn(*args, _mode(mode), stream.cuda_stream)
         else:
-            rc = lib.gqa_attention_decode_plan(*args, ctypes.byref(plan), stream.cuda_stream)
+            fn = lib.gqa_attention_fp8_decode_plan if fp8 else lib.gqa_attention_decode_plan
+            rc = fn(*args, ctypes.byref(plan), stream.cuda_stream)
     if rc != 0:
         _raise(rc)
     return out
@@ -807,22 +830,27 @@ class BoundAttention:
     """A fused attention call with checked, bound arguments for loops (see BoundCall)."""
 
     def __init__(self, q, K, V, out=None, scale: float = 1.0, plan: Optional[Plan] = None,
-                 mode: Union[str, int] = "auto", stream=None):
+                 mode: Union[str, int] = "auto", stream=None, k_scale=None, v_scale=None):
         torch = _torch()
-        B, C, Hq, Hkv, D = _check_attention(q, K, V, out)
+        B, C, Hq, Hkv, D, kvdt = _check_attention(q, K, V, out)
         if out is None:
             out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
         if stream is None:
             stream = torch.cuda.current_stream(q.device)
         if plan is None:
             cu = torch.cuda.get_device_properties(q.device).multi_processor_count
-            plan = make_plan(B, C, Hq, Hkv, D, "bf16", mode, cu_count=cu, attention=True)
-        self.tensors, self.out, self.plan = (q, K, V), out, plan
+            plan = make_plan(B, C, Hq, Hkv, D, kvdt, mode, cu_count=cu, attention=True)
+        self.tensors, self.out, self.plan = (q, K, V, k_scale, v_scale), out, plan
         lib = load()
-        self._fn, self._pass1, self._combine = (lib.gqa_attention_decode_plan, lib.gqa_attention_decode_pass1,
-                                                lib.gqa_attention_decode_combine)
-        self._args = (q.data_ptr(), K.data_ptr(), V.data_ptr(), out.data_ptr(), B, C, Hq, Hkv, D, DTYPES["bf16"],
-                      ctypes.c_float(scale), ctypes.byref(plan), stream.cuda_stream)
+        if kvdt == "fp8":
+            self._fn, self._pass1, self._combine = (lib.gqa_attention_fp8_decode_plan,
+                                                    lib.gqa_attention_fp8_decode_pass1,
+                                                    lib.gqa_attention_fp8_decode_combine)
+        else:
+            self._fn, self._pass1, self._combine = (lib.gqa_attention_decode_plan, lib.gqa_attention_decode_pass1,
+                                                    lib.gqa_attention_decode_combine)
+        self._args = _attention_args(q, K, V, out, B, C, Hq, Hkv, D, kvdt, scale, k_scale, v_scale) + \
+            (ctypes.byref(plan), stream.cuda_stream)
 
     def __call__(self):
         rc = self._fn(*self._args)

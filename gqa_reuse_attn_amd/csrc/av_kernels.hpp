@@ -107,6 +107,7 @@ struct Pass1Args {
     const float* q;              // fused attention: [B][Hq][D] queries (the scores are computed, not read)
     const uint8_t* K;            // fused attention: [B][C][Hkv][D] keys, V's element type
     float qk_scale;              // fused attention: the scores are qk_scale * q . K
+    const float* k_scale;        // fused attention over fp8 K: [Hkv] scale of each KV head's keys (NULL: 1)
     uint32_t* counters;     // combine in kernel: [tiles], zero between calls
     int32_t combine;        // 1: last workgroup of a tile adds the splits; 0: second kernel
     int64_t C;
@@ -891,7 +892,7 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma(Pass1Args a) {
 // row addresses from it, rows past the sequence's length reading the split's
 // last valid row with weight 0.
 //
-// QK: fused decode attention (with SM, bf16 K and V, dense). Each chunk's K rows
+// QK: fused decode attention (with SM, dense bf16 or fp8 K and V). Each chunk's K rows
 // go through the same LDS region as its V rows; S = Q K^T for the tile's 16
 // heads and the chunk's 32 rows comes from v_mfma_f32_16x16x32_bf16 with the
 // queries as the A operand, split exactly into three bf16 terms, and the K
@@ -901,7 +902,7 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma(Pass1Args a) {
 // read from memory.
 template <int PR, int NSET, int U, int HT, bool SM = false, int VDT = kBF16, bool PG = false, bool QK = false>
 __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
-    static_assert(!QK || (SM && VDT == kBF16 && !PG), "fused attention: bf16 K and V, dense, fused softmax");
+    static_assert(!QK || (SM && !PG), "fused attention: dense K and V, fused softmax");
     static_assert(PR == 8 || PR == 16 || PR == 32, "D must be 64, 128 or 256");
     static_assert(VDT == kBF16 || VDT == kFP8, "bf16 or fp8 V");
     constexpr bool FP8 = VDT == kFP8;
@@ -1059,6 +1060,9 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
                     bf.v[u][i] = __builtin_nontemporal_load(reinterpret_cast<const Piece*>(p));
                 } else if constexpr (FP8) {
                     bf.v[u][i] = __builtin_amdgcn_raw_buffer_load_b64(vres, vlane, (r0 + RPI * i) * vrow, kCachePolicyNt);
+                    if constexpr (QK)
+                        bf.k[u][i] = __builtin_amdgcn_raw_buffer_load_b64(kres, vlane, (r0 + RPI * i) * vrow,
+                                                                          kCachePolicyNt);
                 } else {
                     bf.v[u][i] = __builtin_amdgcn_raw_buffer_load_b128(vres, vlane, (r0 + RPI * i) * vrow,
                                                                        kCachePolicyNt);
@@ -1077,6 +1081,26 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
             }
         }
     };
+    // A memory piece as 8 bfloat16 values: bf16 as it is; fp8 widened (8 E4M3
+    // values -> the upper halves of their exact fp32 forms).
+    auto to_bf16 = [](const Piece& pc) -> u32x4 {
+        if constexpr (FP8) {
+            typedef float f32x2 __attribute__((ext_vector_type(2)));
+            u32x4 piece;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(pc[h]), false);
+                const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(pc[h]), true);
+                piece[2 * h] = (__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xffff0000u);
+                piece[2 * h + 1] = (__float_as_uint(hi.x) >> 16) | (__float_as_uint(hi.y) & 0xffff0000u);
+            }
+            return piece;
+        } else {
+            return pc;
+        }
+    };
+    // QK: the factor on a score: the score scale, times the KV head's fp8 key scale.
+    const float s_mul = QK ? a.qk_scale * (FP8 && a.k_scale ? a.k_scale[T.kv + kvl] : 1.0f) : 0.0f;
     auto consume = [&](const Buf& bf, int st) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -1088,7 +1112,7 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
             if constexpr (QK) {
 #pragma unroll
                 for (int i = 0; i < LPI; ++i)
-                    *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(region + st_off(i)) = bf.k[u][i];
+                    *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(region + st_off(i)) = to_bf16(bf.k[u][i]);
                 asm volatile("" ::: "memory");
                 // B operand: lane 16 g + n holds row 16 t2 + n, d = 32 kk + 8 g .. + 7 (piece 4 kk + g).
                 f32x4 sacc[NSET][2];
@@ -1122,7 +1146,7 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
                     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
-                            sreg[(16 * s + 4 * g + i) * 32 + 16 * t2 + m] = sacc[s][t2][i] * a.qk_scale;
+                            sreg[(16 * s + 4 * g + i) * 32 + 16 * t2 + m] = sacc[s][t2][i] * s_mul;
                 asm volatile("" ::: "memory");
 #pragma unroll
                 for (int s = 0; s < NSET; ++s) {
@@ -1138,23 +1162,8 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
                 asm volatile("" ::: "memory");
             }
 #pragma unroll
-            for (int i = 0; i < LPI; ++i) {
-                u32x4 piece;
-                if constexpr (FP8) {
-                    // 8 E4M3 values -> 8 bfloat16 values (the upper halves of their exact fp32 forms)
-                    typedef float f32x2 __attribute__((ext_vector_type(2)));
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(bf.v[u][i][h]), false);
-                        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(bf.v[u][i][h]), true);
-                        piece[2 * h] = (__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xffff0000u);
-                        piece[2 * h + 1] = (__float_as_uint(hi.x) >> 16) | (__float_as_uint(hi.y) & 0xffff0000u);
-                    }
-                } else {
-                    piece = bf.v[u][i];
-                }
-                *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(region + st_off(i)) = piece;
-            }
+            for (int i = 0; i < LPI; ++i)
+                *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(region + st_off(i)) = to_bf16(bf.v[u][i]);
             asm volatile("" ::: "memory");
             float wt[NSET][8];
             if constexpr (SM) {

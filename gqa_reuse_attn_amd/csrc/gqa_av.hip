@@ -163,10 +163,12 @@ hipError_t launch_pass1(int v_dtype, const gqa_av_plan& p, int64_t D, const Pass
                  : v_dtype == GQA_AV_F16 ? gqa_av::kF16
                  : v_dtype == GQA_AV_BF16 ? gqa_av::kBF16 : gqa_av::kFP8;
     if (p.attention) {
-        if (v_dtype != GQA_AV_BF16 || p.engine != GQA_AV_ENGINE_MFMA_BF16 || p.page_size > 0 || !p.softmax)
+        if ((v_dtype != GQA_AV_BF16 && v_dtype != GQA_AV_FP8_E4M3) || p.engine != GQA_AV_ENGINE_MFMA_BF16 ||
+            p.page_size > 0 || !p.softmax)
             return hipErrorInvalidValue;
-        return gqa_av_launch::mfma_bf16<gqa_av::kBF16, true, false, true>(D, p.heads_per_tile / 16,
-                                                                           p.kv_heads_per_tile, a, s);
+        const int nset = p.heads_per_tile / 16, ht = p.kv_heads_per_tile;
+        return v_dtype == GQA_AV_FP8_E4M3 ? gqa_av_launch::mfma_bf16<gqa_av::kFP8, true, false, true>(D, nset, ht, a, s)
+                                          : gqa_av_launch::mfma_bf16<gqa_av::kBF16, true, false, true>(D, nset, ht, a, s);
     }
     if (p.engine == GQA_AV_ENGINE_MFMA_BF16) {
         if (v_dtype != GQA_AV_BF16 && v_dtype != GQA_AV_FP8_E4M3) return hipErrorInvalidValue;
@@ -280,8 +282,8 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
     // scores computed from q and K.
     const bool attention = h.attention == 1;
     if (attention) {
-        if (v_dtype != GQA_AV_BF16 || h.page_size != 0)
-            return fail(GQA_AV_ERR_UNSUPPORTED, "fused attention takes dense bf16 K and V");
+        if ((v_dtype != GQA_AV_BF16 && v_dtype != GQA_AV_FP8_E4M3) || h.page_size != 0)
+            return fail(GQA_AV_ERR_UNSUPPORTED, "fused attention takes dense bf16 or fp8 K and V");
         if (h.engine != GQA_AV_ENGINE_AUTO && h.engine != GQA_AV_ENGINE_MFMA_BF16)
             return fail(GQA_AV_ERR_UNSUPPORTED, "fused attention runs on the bf16 matrix engine");
         h.softmax = 1;
@@ -585,6 +587,7 @@ struct AttnArgs {
     const float* q;
     const void* K;
     float scale;
+    const float* k_scale;   // fp8 K: [Hkv] or NULL
 };
 
 // softmax: 1 for the fused softmax entry points (attn then holds the scores);
@@ -704,6 +707,7 @@ int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C,
     a.q = at ? at->q : nullptr;
     a.K = at ? static_cast<const uint8_t*>(at->K) : nullptr;
     a.qk_scale = at ? at->scale : 0.0f;
+    a.k_scale = at ? at->k_scale : nullptr;
     a.block_table = pg ? pg->block_table : nullptr;
     a.seq_lens = pg ? pg->seq_lens : nullptr;
     a.num_pages = pg ? pg->num_pages : 0;
@@ -935,7 +939,7 @@ int gqa_softmax_av_decode_combine(const float* scores, const void* V, float* out
 int gqa_attention_decode_plan(const float* q, const void* K, const void* V, float* out, int64_t B, int64_t C,
                               int64_t Hq, int64_t Hkv, int64_t D, int kv_dtype, float scale, const gqa_av_plan* plan,
                               void* stream) {
-    const AttnArgs at{q, K, scale};
+    const AttnArgs at{q, K, scale, nullptr};
     return run_plan(nullptr, V, out, B, C, Hq, Hkv, D, kv_dtype, plan, stream, kRunPass1 | kRunCombine, 1, nullptr,
                     nullptr, &at);
 }
@@ -943,14 +947,14 @@ int gqa_attention_decode_plan(const float* q, const void* K, const void* V, floa
 int gqa_attention_decode_pass1(const float* q, const void* K, const void* V, float* out, int64_t B, int64_t C,
                                int64_t Hq, int64_t Hkv, int64_t D, int kv_dtype, float scale,
                                const gqa_av_plan* plan, void* stream) {
-    const AttnArgs at{q, K, scale};
+    const AttnArgs at{q, K, scale, nullptr};
     return run_plan(nullptr, V, out, B, C, Hq, Hkv, D, kv_dtype, plan, stream, kRunPass1, 1, nullptr, nullptr, &at);
 }
 
 int gqa_attention_decode_combine(const float* q, const void* K, const void* V, float* out, int64_t B, int64_t C,
                                  int64_t Hq, int64_t Hkv, int64_t D, int kv_dtype, float scale,
                                  const gqa_av_plan* plan, void* stream) {
-    const AttnArgs at{q, K, scale};
+    const AttnArgs at{q, K, scale, nullptr};
     return run_plan(nullptr, V, out, B, C, Hq, Hkv, D, kv_dtype, plan, stream, kRunCombine, 1, nullptr, nullptr, &at);
 }
 
@@ -960,6 +964,52 @@ int gqa_attention_decode(const float* q, const void* K, const void* V, float* ou
     int rc = auto_plan(V, B, C, Hq, Hkv, D, kv_dtype, mode, 1, &plan, 0, 1);
     if (rc != GQA_AV_OK) return rc;
     return gqa_attention_decode_plan(q, K, V, out, B, C, Hq, Hkv, D, kv_dtype, scale, &plan, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int run_attention_fp8(const float* q, const void* K, const float* k_scale, const void* V, const float* v_scale,
+                      float* out, int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, float scale,
+                      const gqa_av_plan* plan, void* stream, int which) {
+    if ((k_scale && (reinterpret_cast<uintptr_t>(k_scale) & 3u)) ||
+        (v_scale && (reinterpret_cast<uintptr_t>(v_scale) & 3u)))
+        return fail(GQA_AV_ERR_INVALID_ARG, "k_scale and v_scale must be 4-byte aligned");
+    const AttnArgs at{q, K, scale, k_scale};
+    return run_plan(nullptr, V, out, B, C, Hq, Hkv, D, GQA_AV_FP8_E4M3, plan, stream, which, 1, nullptr, v_scale, &at);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_attention_fp8_decode_plan(const float* q, const void* K, const float* k_scale, const void* V,
+                                  const float* v_scale, float* out, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
+                                  int64_t D, float scale, const gqa_av_plan* plan, void* stream) {
+    return run_attention_fp8(q, K, k_scale, V, v_scale, out, B, C, Hq, Hkv, D, scale, plan, stream,
+                             kRunPass1 | kRunCombine);
+}
+
+int gqa_attention_fp8_decode_pass1(const float* q, const void* K, const float* k_scale, const void* V,
+                                   const float* v_scale, float* out, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
+                                   int64_t D, float scale, const gqa_av_plan* plan, void* stream) {
+    return run_attention_fp8(q, K, k_scale, V, v_scale, out, B, C, Hq, Hkv, D, scale, plan, stream, kRunPass1);
+}
+
+int gqa_attention_fp8_decode_combine(const float* q, const void* K, const float* k_scale, const void* V,
+                                     const float* v_scale, float* out, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
+                                     int64_t D, float scale, const gqa_av_plan* plan, void* stream) {
+    return run_attention_fp8(q, K, k_scale, V, v_scale, out, B, C, Hq, Hkv, D, scale, plan, stream, kRunCombine);
+}
+
+int gqa_attention_fp8_decode(const float* q, const void* K, const float* k_scale, const void* V,
+                             const float* v_scale, float* out, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
+                             int64_t D, float scale, int mode, void* stream) {
+    gqa_av_plan plan;
+    int rc = auto_plan(V, B, C, Hq, Hkv, D, GQA_AV_FP8_E4M3, mode, 1, &plan, 0, 1);
+    if (rc != GQA_AV_OK) return rc;
+    return gqa_attention_fp8_decode_plan(q, K, k_scale, V, v_scale, out, B, C, Hq, Hkv, D, scale, &plan, stream);
 }
 
 const char* gqa_av_status_string(int status) {

@@ -19,7 +19,7 @@
  * in gqa_av.h).
  *
  * Memory layout: q [B][Hq][D] float32; K and V [B][C][Hkv][D] bfloat16
- * (kv_dtype GQA_AV_BF16); out [B][Hq][D] float32. All DEVICE pointers on the
+ * (kv_dtype GQA_AV_BF16; fp8 below); out [B][Hq][D] float32. All DEVICE pointers on the
  * current HIP device, owned by the caller; q and out 4-byte aligned, K and V
  * 16-byte aligned. D must be 64, 128 or 256; otherwise GQA_AV_ERR_UNSUPPORTED.
  *
@@ -65,6 +65,26 @@ int gqa_attention_decode_pass1(const float *q, const void *K, const void *V, flo
 int gqa_attention_decode_combine(const float *q, const void *K, const void *V, float *out,
                                  int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D,
                                  int kv_dtype, float scale, const gqa_av_plan *plan, void *stream);
+
+/* fp8 K and V (an fp8 KV cache, not on the page): K and V hold OCP FP8 E4M3
+ * bytes [B][C][Hkv][D] (8-byte aligned) with float32 scales per KV head,
+ * k_scale and v_scale [Hkv] on the device (NULL: 1): each element is
+ * decode(byte) * scale[kv_h]. The values widen exactly to bfloat16 and run
+ * as above; k_scale joins scale on the scores, v_scale multiplies each
+ * output once. Plans: gqa_av_make_plan with hint->attention = 1 and v_dtype
+ * GQA_AV_FP8_E4M3. */
+int gqa_attention_fp8_decode(const float *q, const void *K, const float *k_scale, const void *V,
+                             const float *v_scale, float *out, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
+                             int64_t D, float scale, int mode, void *stream);
+int gqa_attention_fp8_decode_plan(const float *q, const void *K, const float *k_scale, const void *V,
+                                  const float *v_scale, float *out, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
+                                  int64_t D, float scale, const gqa_av_plan *plan, void *stream);
+int gqa_attention_fp8_decode_pass1(const float *q, const void *K, const float *k_scale, const void *V,
+                                   const float *v_scale, float *out, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
+                                   int64_t D, float scale, const gqa_av_plan *plan, void *stream);
+int gqa_attention_fp8_decode_combine(const float *q, const void *K, const float *k_scale, const void *V,
+                                     const float *v_scale, float *out, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
+                                     int64_t D, float scale, const gqa_av_plan *plan, void *stream);
 
 #ifdef __cplusplus
 }

@@ -157,3 +157,70 @@ def test_attention_edges():
     with pytest.raises(ga.GqaAvError) as e:
         ga.gqa_attention_decode(qq.to(DEV), KK.to(DEV), VV.to(DEV), mode="reuse")
     assert e.value.name == "INELIGIBLE"
+
+
+# ---- fp8 K and V (OCP FP8 E4M3 with a float32 scale per KV head) ---------------
+
+def _quantize(X: torch.Tensor):
+    """Per-KV-head scale max|X| / 448 and the E4M3 bytes of X / scale (torch's
+    round-to-nearest cast): input preparation."""
+    Xf = X.float()
+    sc = (Xf.abs().amax(dim=(0, 1, 3)).clamp_min(1e-30) / 448.0).contiguous()
+    return (Xf / sc.view(1, 1, -1, 1)).to(torch.float8_e4m3fn).contiguous(), sc
+
+
+def _run_fp8(q, K8, ks, V8, vs, scale, plan=None):
+    out = ga.gqa_attention_decode(q.to(DEV), K8.to(DEV), V8.to(DEV), scale=scale, plan=plan,
+                                  k_scale=None if ks is None else ks.to(DEV), v_scale=None if vs is None else vs.to(DEV))
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def _fp8_cases():
+    cases, k = [], 0
+    for G in (2, 4, 5, 8, 16, 17):
+        for D in (64, 128, 256):
+            for C in (1, 65, 700):
+                if (G + D // 64 + C) % 3 or (G > 16 and D > 128):
+                    continue
+                Hkv = (1, 2, 4)[k % 3]
+                cases.append((1 + k % 2, C, G * Hkv, Hkv, D))
+                k += 1
+    return cases
+
+
+@pytest.mark.parametrize("B,C,Hq,Hkv,D", _fp8_cases())
+def test_attention_fp8_sweep(B, C, Hq, Hkv, D, oracle_lib):
+    """fp8 K and V quantized per KV head: G 2..17, D 64..256, ragged C,
+    forced splits, 1/2 KV heads per workgroup, with and without scales,
+    against the fp8 attention oracle (same bound, on the decoded values)."""
+    q, K, V = _inputs(B, C, Hq, Hkv, D, seed=B * 100 + C + D)
+    K8, ks = _quantize(K)
+    V8, vs = _quantize(V)
+    scale = D ** -0.5
+    plans = [ga.make_plan(B, C, Hq, Hkv, D, "fp8", nsplit=ns, attention=True) for ns in (0, 1, 4)]
+    plans += [ga.make_plan(B, C, Hq, Hkv, D, "fp8", kv_tile=2, nsplit=3, attention=True)] if Hkv % 2 == 0 else []
+    for k_s, v_s in ((ks, vs), (None, None)):
+        ref = oracle_lib.attention_fp8(q, K8, V8, k_s, v_s, scale)
+        kd = K8.float() * (k_s.view(1, 1, -1, 1) if k_s is not None else 1.0)
+        vd = V8.float() * (v_s.view(1, 1, -1, 1) if v_s is not None else 1.0)
+        for plan in plans:
+            out = _run_fp8(q, K8, k_s, V8, v_s, scale, plan=plan)
+            _check(out, ref, q, kd, vd, scale, f"attention fp8 {(B, C, Hq, Hkv, D)} scales={k_s is not None} "
+                                               f"{plan.as_dict()}")
+
+
+def test_attention_fp8_equals_bf16_on_widened_values():
+    """With unit scales, fp8 K and V give the bf16 call's output on the same
+    values bit for bit (exact widening, same products and sums)."""
+    B, C, Hq, Hkv, D = 2, 900, 32, 4, 128
+    q, K, V = _inputs(B, C, Hq, Hkv, D, seed=51)
+    K8, _ = _quantize(K)
+    V8, _ = _quantize(V)
+    for ns in (0, 1):
+        p8 = ga.make_plan(B, C, Hq, Hkv, D, "fp8", nsplit=ns, kv_tile=1, attention=True)
+        p16 = ga.make_plan(B, C, Hq, Hkv, D, "bf16", nsplit=ns, kv_tile=1, attention=True)
+        assert p8.rows_per_split == p16.rows_per_split
+        a = _run_fp8(q, K8, None, V8, None, 0.1, plan=p8)
+        b = _run(q, K8.to(torch.bfloat16), V8.to(torch.bfloat16), 0.1, plan=p16)
+        assert np.array_equal(a, b), ns

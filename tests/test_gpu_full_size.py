@@ -2,7 +2,7 @@
 D = 128, bf16) in the launch configurations the bench times, for the products
 whose other tests cut that workload to 8 sequences: the fused softmax product,
 the score step (bf16 and fp8 K), paged V (16-row pages, shuffled, full
-lengths), fp8 V (per-KV-head scales) and fused decode attention. The GPU computes all 64 sequences with the plan the
+lengths), fp8 V (per-KV-head scales) and fused decode attention (bf16, and fp8 K and V). The GPU computes all 64 sequences with the plan the
 bench uses; sequences are independent, so the oracle checks a sample of them
 one by one, with the same gates as the per-product tests. All tests need an
 MI355X and are marked ``gpu``.
@@ -138,3 +138,22 @@ def test_full_size_attention(oracle_lib):
     for b in SAMPLE:
         ref = oracle_lib.attention(q[b:b + 1], K[b:b + 1], V[b:b + 1], "bf16", scale)
         _check(out[b:b + 1], ref, q[b:b + 1], K[b:b + 1], V[b:b + 1], scale, f"full-size attention b={b}")
+
+
+def test_full_size_attention_fp8(oracle_lib):
+    from tests.test_gpu_attention import _check, _quantize
+    q, K = make_qk_random(W.B, W.C, W.Hq, W.Hkv, W.D, "bf16", seed=0)
+    _, V = make_qk_random(W.B, W.C, W.Hq, W.Hkv, W.D, "bf16", seed=1)
+    K8, ks = _quantize(K)
+    V8, vs = _quantize(V)
+    scale = W.D ** -0.5
+    plan = ga.make_plan(W.B, W.C, W.Hq, W.Hkv, W.D, "fp8", cu_count=_cus(), attention=True)
+    _say(f"[full] attention fp8 plan={plan.as_dict()}")
+    out = ga.gqa_attention_decode(q.to(DEV), K8.to(DEV), V8.to(DEV), scale=scale, plan=plan,
+                                  k_scale=ks.to(DEV), v_scale=vs.to(DEV))
+    out = out.cpu().numpy().astype(np.float64)
+    kd = K8.float() * ks.view(1, 1, -1, 1)
+    vd = V8.float() * vs.view(1, 1, -1, 1)
+    for b in SAMPLE:
+        ref = oracle_lib.attention_fp8(q[b:b + 1], K8[b:b + 1], V8[b:b + 1], ks, vs, scale)
+        _check(out[b:b + 1], ref, q[b:b + 1], kd[b:b + 1], vd[b:b + 1], scale, f"full-size attention fp8 b={b}")

@@ -68,6 +68,15 @@ constexpr int64_t kTargetWgPerCuValu = 2;
 constexpr int64_t kTargetWgPerCuMfma = 1;
 constexpr int64_t kMinRowsPerSplitBf16 = 512;  // bf16 matrix engine: measured best for MQA at B = 4, C = 32768
 constexpr int64_t kTargetWgPerCuBf16 = 1;
+// Fused attention over fp8 K and V does twice the matrix and LDS work per
+// byte read and runs better with two workgroups per CU. Measured on MI355X:
+// B = 64, C = 8192, Hkv = 8, G = 8 takes 204 us on 512 workgroups against
+// 225 on 256; B = 4, C = 32768, Hkv = 8, G = 2 takes 60 against 64.5.
+constexpr int64_t kTargetWgPerCuBf16Fp8Attn = 2;
+// Fused attention on grids smaller than the chip (B = 1, C = 4096, Hkv = 8,
+// G = 4): 32 splits of 128 rows take 10.2 us (fp8 K and V: 11.2) against
+// 14.2 (16.3) for 8 splits of 512 rows.
+constexpr int64_t kMinRowsPerSplitAttn = 128;
 
 // Split-C workspace of one (device, stream). The per-tile counters live in a
 // buffer of their own: they must be zero before a call, every call leaves the
@@ -347,12 +356,14 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
     // tile row stays within 512 bytes (G = 3, D = 96: 26.6 us against 28.1).
     int ht = h.kv_tile > 0 ? h.kv_tile : 1;
     const bool bf16_engine = engine == GQA_AV_ENGINE_MFMA_BF16;
+    const int64_t wg_per_cu_bf16 =
+        attention && v_dtype == GQA_AV_FP8_E4M3 ? kTargetWgPerCuBf16Fp8Attn : kTargetWgPerCuBf16;
     if (h.kv_tile <= 0 && resolved == GQA_AV_REUSE &&
         (engine == GQA_AV_ENGINE_VALU || bf16_engine)) {
         const bool fp8 = v_dtype == GQA_AV_FP8_E4M3;
         const int64_t lanes = (D * es) / 16 > 0 && (D * es) % 16 == 0 ? (D * es) / 16 : 0;
         const int64_t nsgw = ceil_div(G, bf16_engine ? 16 * nset16 : head_capacity(G));
-        const int64_t target = (bf16_engine ? kTargetWgPerCuBf16 : kTargetWgPerCuValu) * cus;
+        const int64_t target = (bf16_engine ? wg_per_cu_bf16 : kTargetWgPerCuValu) * cus;
         const int64_t min_rows = bf16_engine ? kMinRowsPerSplitBf16 : kMinRowsPerSplit;
         for (int cand : {4, 2}) {
             const bool four = bf16_engine ? !fp8 : (fp8 && 4 * D * es <= 512);
@@ -451,11 +462,16 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
             rows_per_split = ceil_div(C, nsplit);
         } else {
             const int64_t target =
-                (bf16_engine ? kTargetWgPerCuBf16 : matrix ? kTargetWgPerCuMfma : kTargetWgPerCuValu) * cus;
+                (bf16_engine ? wg_per_cu_bf16 : matrix ? kTargetWgPerCuMfma : kTargetWgPerCuValu) * cus;
             nsplit = tiles > 0 ? ceil_div(target, tiles) : 1;
             const int64_t cap =
                 ceil_div(C, bf16_engine ? kMinRowsPerSplitBf16 : matrix ? kMinRowsPerSplitMfma : kMinRowsPerSplit);
             if (nsplit > cap) nsplit = cap;
+            if (attention && tiles * nsplit < cus) {
+                // Fused attention with fewer workgroups than CUs: shorter
+                // splits, down to kMinRowsPerSplitAttn rows, give each CU one.
+                nsplit = std::min(ceil_div(cus, tiles), ceil_div(C, kMinRowsPerSplitAttn));
+            }
             if (nsplit < 1) nsplit = 1;
             rows_per_split = ceil_div(ceil_div(C, nsplit), rows_per_step) * rows_per_step;
         }

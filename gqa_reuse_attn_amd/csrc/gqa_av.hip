@@ -68,11 +68,14 @@ constexpr int64_t kTargetWgPerCuValu = 2;
 constexpr int64_t kTargetWgPerCuMfma = 1;
 constexpr int64_t kMinRowsPerSplitBf16 = 512;  // bf16 matrix engine: measured best for MQA at B = 4, C = 32768
 constexpr int64_t kTargetWgPerCuBf16 = 1;
-// Fused attention over fp8 K and V does twice the matrix and LDS work per
-// byte read and runs better with two workgroups per CU. Measured on MI355X:
-// B = 64, C = 8192, Hkv = 8, G = 8 takes 204 us on 512 workgroups against
-// 225 on 256; B = 4, C = 32768, Hkv = 8, G = 2 takes 60 against 64.5.
-constexpr int64_t kTargetWgPerCuBf16Fp8Attn = 2;
+// The fused softmax product and fused attention over fp8 values do twice the
+// matrix, LDS and exp work per byte read and run better with two workgroups
+// per CU. Measured on MI355X, B = 64, C = 8192, Hkv = 8, G = 8: attention
+// takes 204 us on 512 workgroups against 225 on 256, the fused softmax
+// product 130 against 143; attention at B = 4, C = 32768, Hkv = 8, G = 2
+// takes 60 against 64.5. (The plain fp8 product stays at one: 112.6 against
+// 118.4.)
+constexpr int64_t kTargetWgPerCuBf16Fp8Sm = 2;
 // Fused attention on grids smaller than the chip (B = 1, C = 4096, Hkv = 8,
 // G = 4): 32 splits of 128 rows take 10.2 us (fp8 K and V: 11.2) against
 // 14.2 (16.3) for 8 splits of 512 rows.
@@ -357,7 +360,7 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
     int ht = h.kv_tile > 0 ? h.kv_tile : 1;
     const bool bf16_engine = engine == GQA_AV_ENGINE_MFMA_BF16;
     const int64_t wg_per_cu_bf16 =
-        attention && v_dtype == GQA_AV_FP8_E4M3 ? kTargetWgPerCuBf16Fp8Attn : kTargetWgPerCuBf16;
+        h.softmax == 1 && v_dtype == GQA_AV_FP8_E4M3 ? kTargetWgPerCuBf16Fp8Sm : kTargetWgPerCuBf16;
     if (h.kv_tile <= 0 && resolved == GQA_AV_REUSE &&
         (engine == GQA_AV_ENGINE_VALU || bf16_engine)) {
         const bool fp8 = v_dtype == GQA_AV_FP8_E4M3;

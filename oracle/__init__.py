@@ -75,6 +75,9 @@ class Oracle:
         lib.gqa_attention_oracle.argtypes = [vp, vp, vp, ip, i64, i64, i64, i64, i64, ctypes.c_double, vp, ip]
         lib.gqa_attention_oracle.restype = ip
         lib.gqa_attention_fp8_oracle.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_double, vp, ip]
+        lib.gqa_attention_paged_oracle.argtypes = [vp, vp, vp, vp, vp, ip, vp, vp, i64, i64, i64, i64, i64, i64, i64,
+                                                   i64, ctypes.c_double, vp, ip]
+        lib.gqa_attention_paged_oracle.restype = ip
         lib.gqa_attention_fp8_oracle.restype = ip
         self.lib = lib
 
@@ -187,6 +190,40 @@ class Oracle:
         rc = self.lib.gqa_attention_fp8_oracle(qa.ctypes.data, k.ctypes.data, None if ks is None else ks.ctypes.data,
                                                v.ctypes.data, None if vs is None else vs.ctypes.data,
                                                B, C, Hq, Hkv, D, float(scale), out.ctypes.data, nthreads)
+        if rc != 0:
+            raise ValueError(f"oracle rejected the arguments (status {rc})")
+        return out
+
+    def attention_paged(self, q, k_pages, v_pages, block_table, seq_lens, kv_dtype: str, scale: float = 1.0,
+                        k_scale=None, v_scale=None, C: Optional[int] = None, nthreads: int = 0) -> np.ndarray:
+        """out[B, Hq, D] (float64): fused attention over a paged K and V cache,
+        two page pools [num_pages,P,Hkv,D] of kv_dtype ("fp8": E4M3 bytes with
+        k_scale and v_scale [Hkv] or None) sharing block_table [B,max_pages]
+        int32; only rows c < seq_lens[b] count; C is the capacity (default
+        max_pages * P)."""
+        qa = np.ascontiguousarray(_as_numpy(q, np.float32))
+        if kv_dtype == "fp8":
+            k, v, code = np.ascontiguousarray(_fp8_bytes(k_pages)), np.ascontiguousarray(_fp8_bytes(v_pages)), 3
+        else:
+            _, k = self._np_inputs(qa, k_pages, kv_dtype)
+            _, v = self._np_inputs(qa, v_pages, kv_dtype)
+            code = DTYPE_CODE[kv_dtype]
+            if k_scale is not None or v_scale is not None:
+                raise ValueError("k_scale and v_scale are for fp8 pages")
+        bt = np.ascontiguousarray(_as_numpy(block_table, np.int32), dtype=np.int32)
+        ln = np.ascontiguousarray(_as_numpy(seq_lens, np.int32), dtype=np.int32)
+        B, Hq, D = qa.shape
+        num_pages, P, Hkv, D2 = k.shape
+        assert D2 == D and v.shape == k.shape and bt.shape[0] == B and ln.shape == (B,)
+        max_pages = bt.shape[1]
+        C = max_pages * P if C is None else C
+        ks = None if k_scale is None else np.ascontiguousarray(_as_numpy(k_scale, np.float32))
+        vs = None if v_scale is None else np.ascontiguousarray(_as_numpy(v_scale, np.float32))
+        out = np.empty((B, Hq, D), dtype=np.float64)
+        rc = self.lib.gqa_attention_paged_oracle(qa.ctypes.data, k.ctypes.data, v.ctypes.data, bt.ctypes.data,
+                                                 ln.ctypes.data, code, None if ks is None else ks.ctypes.data,
+                                                 None if vs is None else vs.ctypes.data, B, C, Hq, Hkv, D, P,
+                                                 max_pages, num_pages, float(scale), out.ctypes.data, nthreads)
         if rc != 0:
             raise ValueError(f"oracle rejected the arguments (status {rc})")
         return out

@@ -610,3 +610,72 @@ int gqa_attention_fp8_oracle(const float *q, const uint8_t *K, const float *k_sc
     (void)nthreads;
     return ORC_OK;
 }
+
+/* One element of a paged K or V cache: dtype 0..2 as for V, or 3 for fp8
+ * E4M3 bytes times the KV head's scale (NULL: 1). */
+static double orc_kv_elem(const void *pages, int dtype, const float *sc, int64_t kv, int64_t i)
+{
+    if (dtype == 3) return orc_e4m3(((const uint8_t *)pages)[i]) * (sc ? (double)sc[kv] : 1.0);
+    return orc_load(pages, dtype, i);
+}
+
+/* Fused decode attention over a paged K and V cache: out[B][Hq][D] in double.
+ * K and V live in two page pools of one layout [num_pages][P][Hkv][D] that
+ * share the block table: row c of sequence b is row c mod P of page
+ * block_table[b][c / P] in both. Only rows c < seq_lens[b] take part; a
+ * length of 0 gives zeros. dtype 0..2, or 3 for fp8 E4M3 with k_scale and
+ * v_scale [Hkv] (NULL: all 1). Rejects what gqa_av_paged_oracle rejects. */
+int gqa_attention_paged_oracle(const float *q, const void *k_pages, const void *v_pages, const int32_t *block_table,
+                               const int32_t *seq_lens, int dtype, const float *k_scale, const float *v_scale,
+                               int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int64_t P,
+                               int64_t max_pages, int64_t num_pages, double scale, double *out, int nthreads)
+{
+    int rc = orc_check(dtype == 3 ? ORC_F32 : dtype, B, C, Hq, Hkv, D);
+    if (rc != ORC_OK) return rc;
+    if (P < 1 || max_pages < 0 || num_pages < 0 || C > max_pages * P) return ORC_BAD_ARG;
+    for (int64_t b = 0; b < B; ++b) {
+        const int64_t len = seq_lens[b];
+        if (len < 0 || len > C) return ORC_BAD_ARG;
+        for (int64_t c = 0; c < len; c += P) {
+            const int64_t page = block_table[b * max_pages + c / P];
+            if (page < 0 || page >= num_pages) return ORC_BAD_ARG;
+        }
+    }
+    pthread_once(&orc_f16_once, orc_f16_fill);
+    const int64_t G = Hq / Hkv;
+    const int64_t rows = B * Hq;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int64_t i = 0; i < rows; ++i) {
+        const int64_t b = i / Hq, h = i % Hq, kv = h / G;
+        const int64_t len = seq_lens[b];
+        double *o = out + i * D;
+        for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+        if (len == 0) continue;
+        const float *qrow = q + (b * Hq + h) * D;
+        double m = -INFINITY;
+        for (int64_t c = 0; c < len; ++c) {
+            const int64_t page = block_table[b * max_pages + c / P];
+            const int64_t row = ((page * P + c % P) * Hkv + kv) * D;
+            double dot = 0.0;
+            for (int64_t d = 0; d < D; ++d) dot += (double)qrow[d] * orc_kv_elem(k_pages, dtype, k_scale, kv, row + d);
+            const double sc = dot * scale;
+            if (sc > m) m = sc;
+        }
+        double l = 0.0;
+        for (int64_t c = 0; c < len; ++c) {
+            const int64_t page = block_table[b * max_pages + c / P];
+            const int64_t row = ((page * P + c % P) * Hkv + kv) * D;
+            double dot = 0.0;
+            for (int64_t d = 0; d < D; ++d) dot += (double)qrow[d] * orc_kv_elem(k_pages, dtype, k_scale, kv, row + d);
+            const double e = exp(dot * scale - m);
+            l += e;
+            for (int64_t d = 0; d < D; ++d) o[d] += e * orc_kv_elem(v_pages, dtype, v_scale, kv, row + d);
+        }
+        for (int64_t d = 0; d < D; ++d) o[d] /= l;
+    }
+    (void)nthreads;
+    return ORC_OK;
+}

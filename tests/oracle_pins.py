@@ -104,6 +104,17 @@ Fused attention over fp8 K and V (E4M3 bytes, per-KV-head scales):
                       outputs; a power-of-two k_scale equals the bf16
                       attention oracle with scale * k_scale, bit for bit.
 
+Fused attention over a paged K and V cache (two page pools, one block table):
+  * attn_paged_gather with shuffled pages of 1, 2, 4, 8 and 16 rows, every
+                      dtype and fp8 with distinct K and V scales, it equals
+                      dense attention on each sequence's first len rows
+                      gathered through the table, bit for bit; length 0 gives
+                      zeros.
+  * attn_paged_tail   NaN in rows past a length and in unused pages changes
+                      nothing.
+  * attn_paged_rejects bad block-table entries, lengths and capacities are
+                      rejected.
+
 fp8 K in the score step (same bytes and per-KV-head scales):
   * qk_fp8_as_bf16    with unit scales the fp8 score oracle equals the bf16
                       score oracle on K widened by torch's float8 -> bfloat16
@@ -892,6 +903,85 @@ def pin_attn_fp8_scales(orc):
         assert np.array_equal(o2, orc.attention(q, k16, v16, "bf16", 0.02 * ks)), f"fp8 attention k_scale {ks}"
 
 
+def _attn_paged_case(B, C, Hq, Hkv, D, P, dt, seed, lens):
+    """q, two shuffled page pools (K and V, with spare pages) sharing one block
+    table, the lengths, and the dense K and V the table describes."""
+    g = torch.Generator().manual_seed(seed)
+    max_pages = -(-C // P)
+    num_pages = B * max_pages + 2
+    q, _ = make_qk_random(B, C, Hq, Hkv, D, "f32", seed=seed)
+    pools = []
+    for _ in range(2):
+        if dt == "fp8":
+            raw = torch.randint(0, 256, (num_pages, P, Hkv, D), generator=g, dtype=torch.uint8)
+            raw[(raw & 0x7F) == 0x7F] = 0x3C                # no NaN payloads
+            pools.append(raw)
+        else:
+            pools.append(torch.randn(num_pages, P, Hkv, D, generator=g).to(
+                {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dt]))
+    perm = torch.randperm(num_pages, generator=g)[:B * max_pages].to(torch.int32)
+    bt = perm.view(B, max_pages).contiguous()
+    K = torch.stack([_gather(pools[0], bt, b, C) for b in range(B)], 0)
+    V = torch.stack([_gather(pools[1], bt, b, C) for b in range(B)], 0)
+    return q, pools[0], pools[1], bt, torch.as_tensor(lens, dtype=torch.int32), K, V
+
+
+def pin_attn_paged_gather(orc):
+    """Paged attention equals dense attention on each sequence's first len rows
+    gathered through the table, bit for bit; length 0 gives zeros."""
+    for i, (dt, P) in enumerate([("bf16", 4), ("f16", 1), ("f32", 8), ("fp8", 2), ("bf16", 16)]):
+        B, C, Hq, Hkv, D = 3, 13, 6, 2, 16
+        lens = [13, 6, 0]
+        q, kp, vp, bt, ln, K, V = _attn_paged_case(B, C, Hq, Hkv, D, P, dt, seed=1300 + i, lens=lens)
+        ks, vs = (torch.tensor([0.5, 0.01]), torch.tensor([4.0, 0.25])) if dt == "fp8" else (None, None)
+        sc = 0.003 if dt == "fp8" else 0.25
+        out = orc.attention_paged(q, kp, vp, bt, ln, dt, sc, ks, vs, C=C)
+        for b in range(B):
+            n = lens[b]
+            if n:
+                dense = orc.attention_fp8(q[b:b + 1], K[b:b + 1, :n], V[b:b + 1, :n], ks, vs, sc) if dt == "fp8" \
+                    else orc.attention(q[b:b + 1], K[b:b + 1, :n], V[b:b + 1, :n], dt, sc)
+                assert np.array_equal(out[b:b + 1], dense), f"paged attention != dense ({dt}, P={P}, b={b})"
+            else:
+                assert (out[b] == 0).all(), f"length 0 gives zeros ({dt})"
+
+
+def pin_attn_paged_tail(orc):
+    """K and V rows past a length, and pages no table entry uses, take no part:
+    NaN there leaves every output as it was."""
+    B, C, Hq, Hkv, D, P = 2, 11, 4, 2, 8, 4
+    lens = [7, 11]
+    q, kp, vp, bt, ln, _, _ = _attn_paged_case(B, C, Hq, Hkv, D, P, "bf16", seed=1320, lens=lens)
+    base = orc.attention_paged(q, kp, vp, bt, ln, "bf16", 0.5, C=C)
+    used = {int(bt[b, c // P]) for b in range(B) for c in range(lens[b])}
+    k2, v2 = kp.clone(), vp.clone()
+    for t in (k2, v2):
+        for pg in range(t.shape[0]):
+            if pg not in used:
+                t[pg] = float("nan")
+        t[int(bt[0, 7 // P]), 7 % P:] = float("nan")        # sequence 0's rows 7.. (past its length)
+    out = orc.attention_paged(q, k2, v2, bt, ln, "bf16", 0.5, C=C)
+    assert np.array_equal(out, base), "K or V past the length or in unused pages changed an output"
+
+
+def pin_attn_paged_rejects(orc):
+    q, kp, vp, bt, ln, _, _ = _attn_paged_case(2, 8, 4, 2, 8, 4, "bf16", seed=1330, lens=[8, 5])
+    npg = kp.shape[0]
+    for bad, args in (("page index", (bt.clone().fill_(npg), ln)), ("negative page", (bt.clone().fill_(-1), ln)),
+                      ("length", (bt, torch.tensor([9, 5], dtype=torch.int32))),
+                      ("negative length", (bt, torch.tensor([-1, 5], dtype=torch.int32)))):
+        try:
+            orc.attention_paged(q, kp, vp, args[0], args[1], "bf16", 1.0, C=8)
+        except ValueError:
+            continue
+        raise AssertionError(f"paged attention oracle accepted a bad {bad}")
+    try:
+        orc.attention_paged(q, kp, vp, bt, ln, "bf16", 1.0, C=9)
+    except ValueError:
+        return
+    raise AssertionError("paged attention oracle accepted a capacity above max_pages * P")
+
+
 ALL_PINS = [pin_decode_table, pin_brute_force, pin_mha_einsum, pin_repeat_mha, pin_constant_v,
             pin_one_hot, pin_linearity, pin_permutation, pin_batch_independence, pin_points,
             pin_edges, pin_qk_brute_force, pin_qk_mha_einsum, pin_qk_repeat_mha, pin_qk_one_hot,
@@ -901,4 +991,5 @@ ALL_PINS = [pin_decode_table, pin_brute_force, pin_mha_einsum, pin_repeat_mha, p
             pin_paged_rejects, pin_fp8_decode, pin_fp8_as_bf16, pin_fp8_scales, pin_qk_fp8_as_bf16,
             pin_qk_fp8_brute, pin_qk_fp8_scales, pin_qk_paged_gather, pin_qk_paged_identity, pin_qk_paged_tail,
             pin_qk_paged_rejects, pin_attn_composition, pin_attn_numpy, pin_attn_zero_q, pin_attn_repeat_mha,
-            pin_attn_edges, pin_attn_fp8_as_bf16, pin_attn_fp8_scales]
+            pin_attn_edges, pin_attn_fp8_as_bf16, pin_attn_fp8_scales, pin_attn_paged_gather, pin_attn_paged_tail,
+            pin_attn_paged_rejects]

@@ -100,6 +100,21 @@ PLANTS = [
      "for (int64_t d = 0; d < D; ++d) dot += (double)qrow[d] * orc_e4m3(kr[d]);\n            const double e"),
     ("paged_bt_ignores_batch", "const int64_t page = bt[b * max_pages + c / P];",
      "const int64_t page = bt[0 * max_pages + c / P];"),
+    ("attn_paged_v_from_k_pool", "o[d] += e * orc_kv_elem(v_pages, dtype, v_scale, kv, row + d);",
+     "o[d] += e * orc_kv_elem(k_pages, dtype, v_scale, kv, row + d);"),
+    ("attn_paged_v_scale_of_k", "o[d] += e * orc_kv_elem(v_pages, dtype, v_scale, kv, row + d);",
+     "o[d] += e * orc_kv_elem(v_pages, dtype, k_scale, kv, row + d);"),
+    ("attn_paged_sum_past_len", "double l = 0.0;\n        for (int64_t c = 0; c < len; ++c) {",
+     "double l = 0.0;\n        for (int64_t c = 0; c < C; ++c) {"),
+    ("attn_paged_bt_no_row_stride",
+     "const int64_t page = block_table[b * max_pages + c / P];\n            const int64_t row = ((page * P + c % P) * Hkv"
+     " + kv) * D;\n            double dot = 0.0;\n            for (int64_t d = 0; d < D; ++d) dot += (double)qrow[d] * "
+     "orc_kv_elem(k_pages, dtype, k_scale, kv, row + d);\n            const double e",
+     "const int64_t page = block_table[b + c / P];\n            const int64_t row = ((page * P + c % P) * Hkv"
+     " + kv) * D;\n            double dot = 0.0;\n            for (int64_t d = 0; d < D; ++d) dot += (double)qrow[d] * "
+     "orc_kv_elem(k_pages, dtype, k_scale, kv, row + d);\n            const double e"),
+    ("attn_paged_elem_unscaled", "return orc_e4m3(((const uint8_t *)pages)[i]) * (sc ? (double)sc[kv] : 1.0);",
+     "return orc_e4m3(((const uint8_t *)pages)[i]);"),
 ]
 
 

@@ -541,14 +541,33 @@ def bench_attn(args, w, dev, props):
         kvdt = "fp8"
     kv_bytes = w.v_bytes() // (2 if args.v_fp8 else 1)
     alg = 2 * kv_bytes + 4 * w.B * w.Hq * w.D + w.out_bytes()
+    P = args.page_size
     plan = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, kvdt, args.mode, nsplit=args.nsplit, kv_tile=args.kv_tile,
-                        cu_count=props.multi_processor_count, attention=True)
+                        cu_count=props.multi_processor_count, attention=True, page_size=P)
     nrot = max(1, math.ceil(args.rotate_mb * 2 ** 20 / alg))
+    if P:
+        # A paged cache: K and V cut into pages of P rows, both pools in one
+        # shuffled order (one block table), every sequence at full length.
+        if w.C % P:
+            raise SystemExit(f"--page-size {P} must divide C={w.C}")
+        maxp = w.C // P
+        perm = torch.randperm(w.B * maxp, generator=torch.Generator().manual_seed(0))
+        K_d, V_d = K_h, V_h
+        K_h, V_h = torch.empty_like(K_d).view(-1, P, w.Hkv, w.D), torch.empty_like(V_d).view(-1, P, w.Hkv, w.D)
+        K_h[perm] = K_d.reshape(-1, P, w.Hkv, w.D)
+        V_h[perm] = V_d.reshape(-1, P, w.Hkv, w.D)
+        bt_h = perm.to(torch.int32).view(w.B, maxp).contiguous()
+        lens_h = torch.full((w.B,), w.C, dtype=torch.int32)
+        bt, lens = bt_h.to(dev), lens_h.to(dev)
     q0, k0, v0 = q_h.to(dev), K_h.to(dev), V_h.to(dev)
     ks = ks_h.to(dev) if ks_h is not None else None
     vs = vs_h.to(dev) if vs_h is not None else None
     sets = [(q0, k0, v0) if i == 0 else (q0.clone(), k0.clone(), v0.clone()) for i in range(nrot)]
-    calls = [ga.BoundAttention(q, k, v, scale=scale, plan=plan, k_scale=ks, v_scale=vs) for q, k, v in sets]
+    if P:
+        calls = [ga.BoundAttentionPaged(q, k, v, bt, lens, scale=scale, plan=plan, k_scale=ks, v_scale=vs)
+                 for q, k, v in sets]
+    else:
+        calls = [ga.BoundAttention(q, k, v, scale=scale, plan=plan, k_scale=ks, v_scale=vs) for q, k, v in sets]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     _warm(args, calls, nrot)
@@ -557,9 +576,14 @@ def bench_attn(args, w, dev, props):
     p1_ms = _timed_pass1(calls, nrot, args.steps, stream)
     # the unfused pair on the same inputs: score step, then the fused softmax product
     scores = [torch.empty((w.B, w.C, w.Hq), device=dev) for _ in range(nrot)]
-    qk = [ga.bind_qk(q, k, scores=sc, scale=scale, k_scale=ks) for (q, k, _), sc in zip(sets, scores)]
-    sav = [(ga.BoundFp8(sc, v, vs, softmax=True) if args.v_fp8 else ga.bind_softmax(sc, v))
-           for (_, _, v), sc in zip(sets, scores)]
+    if P:
+        # (the paged product takes no V scale: the same work with unit scales)
+        qk = [ga.BoundQkPaged(q, k, bt, lens, scores=sc, scale=scale, k_scale=ks) for (q, k, _), sc in zip(sets, scores)]
+        sav = [ga.bind_paged(sc, v, bt, lens, softmax=True) for (_, _, v), sc in zip(sets, scores)]
+    else:
+        qk = [ga.bind_qk(q, k, scores=sc, scale=scale, k_scale=ks) for (q, k, _), sc in zip(sets, scores)]
+        sav = [(ga.BoundFp8(sc, v, vs, softmax=True) if args.v_fp8 else ga.bind_softmax(sc, v))
+               for (_, _, v), sc in zip(sets, scores)]
     pair = [lambda i=i: (qk[i](), sav[i]()) for i in range(nrot)]
     _warm(args, pair, nrot)
     pair_ms = _timed(pair, nrot, args.steps, stream)
@@ -572,7 +596,10 @@ def bench_attn(args, w, dev, props):
         orc = oracle.get()
         nb = max(1, min(w.B, int(2e8 // max(1, w.C * w.Hq * w.D * 4))))    # a bounded sample of sequences
         part = alg * nb // w.B
-        if args.v_fp8:
+        if P:
+            fn = lambda n: orc.attention_paged(q_h[:nb], K_h, V_h, bt_h[:nb], lens_h[:nb], kvdt, scale, ks_h,  # noqa: E731
+                                               vs_h, C=w.C, nthreads=n)
+        elif args.v_fp8:
             fn = lambda n: orc.attention_fp8(q_h[:nb], K_h[:nb], V_h[:nb], ks_h, vs_h, scale, nthreads=n)  # noqa: E731
         else:
             fn = lambda n: orc.attention(q_h[:nb], K_h[:nb], V_h[:nb], "bf16", scale, nthreads=n)  # noqa: E731
@@ -581,10 +608,12 @@ def bench_attn(args, w, dev, props):
         "metric": ATTN_METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 6), "us_per_call": round(ms * 1e3, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": f"attn{'-fp8' if args.v_fp8 else ''}:{w.name}", "B": w.B, "C": w.C, "Hq": w.Hq,
+        "config": {"workload": f"attn{'-fp8' if args.v_fp8 else ''}{f'-paged{P}' if P else ''}:{w.name}", "B": w.B,
+                   "C": w.C, "Hq": w.Hq, "page_size": P,
                    "Hkv": w.Hkv, "G": w.G, "D": w.D, "kv_dtype": "fp8_e4m3" if args.v_fp8 else "bf16", "mode": args.mode, "algorithmic_bytes": alg, "rotation_sets": nrot,
                    "unfused_us_per_call": round(pair_ms * 1e3, 3), "plan": plan.as_dict()},
-        "roofline": _pass1_roofline(alg, p1_ms, recorded_traffic(w.name, args.mode, "attn", "_fp8" if args.v_fp8 else "")
+        "roofline": _pass1_roofline(alg, p1_ms, recorded_traffic(w.name, args.mode, "attn", ("_fp8" if args.v_fp8 else "")
+                                                                 + (f"_paged{P}" if P else ""))
                                     if args.nsplit == 0 and args.kv_tile == 0 else None),
         "cpu_baseline": cpu,
     }

@@ -131,6 +131,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         getattr(lib, fn).argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
                                      ctypes.POINTER(Plan), vp]
         getattr(lib, fn).restype = ip
+    lib.gqa_attention_paged_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64,
+                                               i64, ip, ctypes.c_float, ip, vp]
+    lib.gqa_attention_paged_decode.restype = ip
+    for fn in ("gqa_attention_paged_decode_plan", "gqa_attention_paged_decode_pass1",
+               "gqa_attention_paged_decode_combine"):
+        getattr(lib, fn).argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, ip,
+                                     ctypes.c_float, ctypes.POINTER(Plan), vp]
+        getattr(lib, fn).restype = ip
     for fn in ("gqa_attention_decode_plan", "gqa_attention_decode_pass1", "gqa_attention_decode_combine"):
         getattr(lib, fn).argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ip, ctypes.c_float,
                                      ctypes.POINTER(Plan), vp]
@@ -850,6 +858,114 @@ class BoundAttention:
             self._fn, self._pass1, self._combine = (lib.gqa_attention_decode_plan, lib.gqa_attention_decode_pass1,
                                                     lib.gqa_attention_decode_combine)
         self._args = _attention_args(q, K, V, out, B, C, Hq, Hkv, D, kvdt, scale, k_scale, v_scale) + \
+            (ctypes.byref(plan), stream.cuda_stream)
+
+    def __call__(self):
+        rc = self._fn(*self._args)
+        if rc != 0:
+            _raise(rc)
+        return self.out
+
+    def pass1(self):
+        rc = self._pass1(*self._args)
+        if rc != 0:
+            _raise(rc)
+
+    def combine(self):
+        rc = self._combine(*self._args)
+        if rc != 0:
+            _raise(rc)
+        return self.out
+
+
+def _check_attention_paged(q, k_pages, v_pages, block_table, seq_lens, out, C):
+    torch = _torch()
+    if q.dim() != 3 or k_pages.dim() != 4 or tuple(v_pages.shape) != tuple(k_pages.shape) or \
+            block_table.dim() != 2 or seq_lens.dim() != 1:
+        raise ValueError("q [B,Hq,D], k_pages and v_pages [num_pages,page_size,Hkv,D] of one shape, "
+                         "block_table [B,max_pages], seq_lens [B]")
+    B, Hq, D = q.shape
+    num_pages, P, Hkv, D2 = k_pages.shape
+    if D2 != D or block_table.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("pages, block_table and seq_lens do not match q")
+    if q.dtype != torch.float32 or k_pages.dtype != v_pages.dtype or \
+            k_pages.dtype not in (torch.bfloat16, torch.float8_e4m3fn):
+        raise TypeError("q must be float32, k_pages and v_pages both bfloat16 or both float8_e4m3fn")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_table and seq_lens must be int32")
+    for t in (q, k_pages, v_pages, block_table, seq_lens):
+        if not t.is_cuda or t.device != q.device or not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous and on the same GPU")
+    if out is not None and (out.dtype != torch.float32 or tuple(out.shape) != (B, Hq, D) or not out.is_contiguous()
+                            or out.device != q.device):
+        raise ValueError(f"out must be a contiguous float32 [{B},{Hq},{D}] tensor on {q.device}")
+    maxp = block_table.shape[1]
+    C = maxp * P if C is None else int(C)
+    return B, C, Hq, Hkv, D, P, maxp, num_pages, ("fp8" if k_pages.dtype == torch.float8_e4m3fn else "bf16")
+
+
+def _attention_paged_args(q, k_pages, v_pages, block_table, seq_lens, out, B, C, Hq, Hkv, D, P, maxp, npg, kvdt,
+                          scale, k_scale, v_scale):
+    if kvdt != "fp8" and (k_scale is not None or v_scale is not None):
+        raise ValueError("k_scale and v_scale are for fp8 K and V")
+    ks = _check_scale(k_scale, Hkv, q.device)
+    vs = _check_scale(v_scale, Hkv, q.device)
+    return (q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(),
+            ks.data_ptr() if ks is not None else None, vs.data_ptr() if vs is not None else None, out.data_ptr(),
+            B, C, Hq, Hkv, D, P, maxp, npg, DTYPES[kvdt], ctypes.c_float(scale))
+
+
+def gqa_attention_paged_decode(q, k_pages, v_pages, block_table, seq_lens, out=None, scale: float = 1.0,
+                               C: Optional[int] = None, mode: Union[str, int] = "auto", stream=None,
+                               plan: Optional[Plan] = None, k_scale=None, v_scale=None):
+    """Fused decode attention over a paged K and V cache: k_pages and v_pages
+    [num_pages,P,Hkv,D] (bfloat16, or float8_e4m3fn with per-KV-head scales)
+    share block_table int32 [B,max_pages]; row c of sequence b is row c % P of
+    page block_table[b, c // P]; only rows c < seq_lens[b] count. C is the
+    capacity (default max_pages * P). Returns out [B,Hq,D] float32."""
+    torch = _torch()
+    B, C, Hq, Hkv, D, P, maxp, npg, kvdt = _check_attention_paged(q, k_pages, v_pages, block_table, seq_lens, out, C)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    lib = load()
+    args = _attention_paged_args(q, k_pages, v_pages, block_table, seq_lens, out, B, C, Hq, Hkv, D, P, maxp, npg,
+                                 kvdt, scale, k_scale, v_scale)
+    with torch.cuda.device(q.device):
+        if plan is None:
+            rc = lib.gqa_attention_paged_decode(*args, _mode(mode), stream.cuda_stream)
+        else:
+            rc = lib.gqa_attention_paged_decode_plan(*args, ctypes.byref(plan), stream.cuda_stream)
+    if rc != 0:
+        _raise(rc)
+    return out
+
+
+class BoundAttentionPaged:
+    """A paged fused attention call with checked, bound arguments for loops (see BoundCall)."""
+
+    def __init__(self, q, k_pages, v_pages, block_table, seq_lens, out=None, scale: float = 1.0,
+                 C: Optional[int] = None, plan: Optional[Plan] = None, mode: Union[str, int] = "auto", stream=None,
+                 k_scale=None, v_scale=None):
+        torch = _torch()
+        B, C, Hq, Hkv, D, P, maxp, npg, kvdt = _check_attention_paged(q, k_pages, v_pages, block_table, seq_lens,
+                                                                      out, C)
+        if out is None:
+            out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        if plan is None:
+            cu = torch.cuda.get_device_properties(q.device).multi_processor_count
+            plan = make_plan(B, C, Hq, Hkv, D, kvdt, mode, cu_count=cu, attention=True, page_size=P)
+        self.tensors = (q, k_pages, v_pages, block_table, seq_lens, k_scale, v_scale)
+        self.out, self.plan = out, plan
+        lib = load()
+        self._fn, self._pass1, self._combine = (lib.gqa_attention_paged_decode_plan,
+                                                lib.gqa_attention_paged_decode_pass1,
+                                                lib.gqa_attention_paged_decode_combine)
+        self._args = _attention_paged_args(q, k_pages, v_pages, block_table, seq_lens, out, B, C, Hq, Hkv, D, P,
+                                           maxp, npg, kvdt, scale, k_scale, v_scale) + \
             (ctypes.byref(plan), stream.cuda_stream)
 
     def __call__(self):

@@ -694,8 +694,12 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
             const int go = T.q_first + kl * a.G - ql;
             if (g >= go && g < go + T.nq) {
                 float* const st = a.stats + ((static_cast<size_t>(T.s) * a.B + T.b) * a.Hq + ql + g) * 2;
-                st[0] = s_stat[0][tid];
-                st[1] = s_stat[1][tid];
+                // PG: a sequence of length 0 (its first split is empty) hands the
+                // combine maximum 0 and weight sum 1 beside zero partials, so its
+                // outputs come out as zeros rather than 0 / 0.
+                const bool empty = PG && T.s == 0 && nrows_split == 0;
+                st[0] = empty ? 0.0f : s_stat[0][tid];
+                st[1] = empty ? 1.0f : s_stat[1][tid];
             }
         }
     }
@@ -902,7 +906,7 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma(Pass1Args a) {
 // read from memory.
 template <int PR, int NSET, int U, int HT, bool SM = false, int VDT = kBF16, bool PG = false, bool QK = false>
 __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
-    static_assert(!QK || (SM && !PG), "fused attention: dense K and V, fused softmax");
+    static_assert(!QK || SM, "fused attention runs the fused softmax");
     static_assert(PR == 8 || PR == 16 || PR == 32, "D must be 64, 128 or 256");
     static_assert(VDT == kBF16 || VDT == kFP8, "bf16 or fp8 V");
     constexpr bool FP8 = VDT == kFP8;
@@ -977,8 +981,8 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
     // m + 16 s of the wave's KV head (heads past the tile read its last head),
     // d = 32 kk + 8 g .. + 7, as three exact bf16 terms.
     const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(QK ? a.K : a.V) + ((static_cast<size_t>(T.b) * a.C + cb) * a.Hkv + T.kv) * D * VES, 0,
-        QK && nrows > 0 ? (nrows - 1) * vrow + HT * D * VES : 0, kRawBufferFlags);
+        const_cast<uint8_t*>(QK ? a.K : a.V) + (PG ? 0 : ((static_cast<size_t>(T.b) * a.C + cb) * a.Hkv + T.kv) * D * VES),
+        0, QK && !PG && nrows > 0 ? (nrows - 1) * vrow + HT * D * VES : 0, kRawBufferFlags);
     constexpr int NKK = QK ? D / 32 : 1;             // 32-wide d blocks of a score
     u32x4 qa[3][NSET][NKK];
     if constexpr (QK) {
@@ -1053,11 +1057,14 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
             for (int i = 0; i < LPI; ++i) {
                 if constexpr (PG) {
                     // Rows past the split read its last row (their weight is 0).
+                    // QK: K rows come from K's page pool at the same offsets.
                     const int64_t c = cb + min(r0 + RPI * i + prow, nrows - 1);
                     const int64_t page = s_pages[(c >> a.page_shift) - pg0];
-                    const uint8_t* const p = a.V + ((page << a.page_shift) + (c & pmask)) * vrow +
-                                             (T.kv + kvl) * D * VES + ppiece * PB;
-                    bf.v[u][i] = __builtin_nontemporal_load(reinterpret_cast<const Piece*>(p));
+                    const size_t off = static_cast<size_t>(((page << a.page_shift) + (c & pmask)) * vrow +
+                                                           (T.kv + kvl) * D * VES + ppiece * PB);
+                    bf.v[u][i] = __builtin_nontemporal_load(reinterpret_cast<const Piece*>(a.V + off));
+                    if constexpr (QK)
+                        bf.k[u][i] = __builtin_nontemporal_load(reinterpret_cast<const Piece*>(a.K + off));
                 } else if constexpr (FP8) {
                     bf.v[u][i] = __builtin_amdgcn_raw_buffer_load_b64(vres, vlane, (r0 + RPI * i) * vrow, kCachePolicyNt);
                     if constexpr (QK)
@@ -1322,8 +1329,12 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
                 const float mw = s_wm[k * WPH + w][hh];
                 L += mw == -INFINITY ? 0.0f : s_wl[k * WPH + w][hh] * __builtin_amdgcn_exp2f((mw - M) * kLog2e);
             }
-            s_tm[k][hh] = M;
-            s_tl[k][hh] = L;
+            // PG: a sequence of length 0 (its first split is empty) hands the
+            // combine maximum 0 and weight sum 1 beside zero partials, so its
+            // outputs come out as zeros rather than 0 / 0.
+            const bool empty = PG && T.s == 0 && nrows == 0;
+            s_tm[k][hh] = empty ? 0.0f : M;
+            s_tl[k][hh] = empty ? 1.0f : L;
         }
     }
     float* const red = reinterpret_cast<float*>(smem);

@@ -176,11 +176,15 @@ hipError_t launch_pass1(int v_dtype, const gqa_av_plan& p, int64_t D, const Pass
                  : v_dtype == GQA_AV_BF16 ? gqa_av::kBF16 : gqa_av::kFP8;
     if (p.attention) {
         if ((v_dtype != GQA_AV_BF16 && v_dtype != GQA_AV_FP8_E4M3) || p.engine != GQA_AV_ENGINE_MFMA_BF16 ||
-            p.page_size > 0 || !p.softmax)
+            !p.softmax)
             return hipErrorInvalidValue;
         const int nset = p.heads_per_tile / 16, ht = p.kv_heads_per_tile;
-        return v_dtype == GQA_AV_FP8_E4M3 ? gqa_av_launch::mfma_bf16<gqa_av::kFP8, true, false, true>(D, nset, ht, a, s)
-                                          : gqa_av_launch::mfma_bf16<gqa_av::kBF16, true, false, true>(D, nset, ht, a, s);
+        using namespace gqa_av_launch;
+        if (p.page_size > 0)
+            return v_dtype == GQA_AV_FP8_E4M3 ? mfma_bf16<gqa_av::kFP8, true, true, true>(D, nset, ht, a, s)
+                                              : mfma_bf16<gqa_av::kBF16, true, true, true>(D, nset, ht, a, s);
+        return v_dtype == GQA_AV_FP8_E4M3 ? mfma_bf16<gqa_av::kFP8, true, false, true>(D, nset, ht, a, s)
+                                          : mfma_bf16<gqa_av::kBF16, true, false, true>(D, nset, ht, a, s);
     }
     if (p.engine == GQA_AV_ENGINE_MFMA_BF16) {
         if (v_dtype != GQA_AV_BF16 && v_dtype != GQA_AV_FP8_E4M3) return hipErrorInvalidValue;
@@ -294,8 +298,8 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
     // scores computed from q and K.
     const bool attention = h.attention == 1;
     if (attention) {
-        if ((v_dtype != GQA_AV_BF16 && v_dtype != GQA_AV_FP8_E4M3) || h.page_size != 0)
-            return fail(GQA_AV_ERR_UNSUPPORTED, "fused attention takes dense bf16 or fp8 K and V");
+        if (v_dtype != GQA_AV_BF16 && v_dtype != GQA_AV_FP8_E4M3)
+            return fail(GQA_AV_ERR_UNSUPPORTED, "fused attention takes bf16 or fp8 K and V");
         if (h.engine != GQA_AV_ENGINE_AUTO && h.engine != GQA_AV_ENGINE_MFMA_BF16)
             return fail(GQA_AV_ERR_UNSUPPORTED, "fused attention runs on the bf16 matrix engine");
         h.softmax = 1;
@@ -1029,6 +1033,74 @@ int gqa_attention_fp8_decode(const float* q, const void* K, const float* k_scale
     int rc = auto_plan(V, B, C, Hq, Hkv, D, GQA_AV_FP8_E4M3, mode, 1, &plan, 0, 1);
     if (rc != GQA_AV_OK) return rc;
     return gqa_attention_fp8_decode_plan(q, K, k_scale, V, v_scale, out, B, C, Hq, Hkv, D, scale, &plan, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int run_attention_paged(const float* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                        const int32_t* seq_lens, const float* k_scale, const float* v_scale, float* out, int64_t B,
+                        int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int64_t page_size, int64_t max_pages,
+                        int64_t num_pages, int kv_dtype, float scale, const gqa_av_plan* plan, void* stream,
+                        int which) {
+    if (kv_dtype != GQA_AV_BF16 && kv_dtype != GQA_AV_FP8_E4M3)
+        return fail(GQA_AV_ERR_UNSUPPORTED, "fused attention takes bf16 or fp8 K and V");
+    if (kv_dtype != GQA_AV_FP8_E4M3 && (k_scale || v_scale))
+        return fail(GQA_AV_ERR_INVALID_ARG, "k_scale and v_scale are for fp8 K and V");
+    if ((k_scale && (reinterpret_cast<uintptr_t>(k_scale) & 3u)) ||
+        (v_scale && (reinterpret_cast<uintptr_t>(v_scale) & 3u)))
+        return fail(GQA_AV_ERR_INVALID_ARG, "k_scale and v_scale must be 4-byte aligned");
+    const PagedArgs pa{block_table, seq_lens, page_size, max_pages, num_pages};
+    const AttnArgs at{q, k_pages, scale, k_scale};
+    return run_plan(nullptr, v_pages, out, B, C, Hq, Hkv, D, kv_dtype, plan, stream, which, 1, &pa, v_scale, &at);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_attention_paged_decode_plan(const float* q, const void* k_pages, const void* v_pages,
+                                    const int32_t* block_table, const int32_t* seq_lens, const float* k_scale,
+                                    const float* v_scale, float* out, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
+                                    int64_t D, int64_t page_size, int64_t max_pages, int64_t num_pages, int kv_dtype,
+                                    float scale, const gqa_av_plan* plan, void* stream) {
+    return run_attention_paged(q, k_pages, v_pages, block_table, seq_lens, k_scale, v_scale, out, B, C, Hq, Hkv, D,
+                               page_size, max_pages, num_pages, kv_dtype, scale, plan, stream,
+                               kRunPass1 | kRunCombine);
+}
+
+int gqa_attention_paged_decode_pass1(const float* q, const void* k_pages, const void* v_pages,
+                                     const int32_t* block_table, const int32_t* seq_lens, const float* k_scale,
+                                     const float* v_scale, float* out, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
+                                     int64_t D, int64_t page_size, int64_t max_pages, int64_t num_pages, int kv_dtype,
+                                     float scale, const gqa_av_plan* plan, void* stream) {
+    return run_attention_paged(q, k_pages, v_pages, block_table, seq_lens, k_scale, v_scale, out, B, C, Hq, Hkv, D,
+                               page_size, max_pages, num_pages, kv_dtype, scale, plan, stream, kRunPass1);
+}
+
+int gqa_attention_paged_decode_combine(const float* q, const void* k_pages, const void* v_pages,
+                                       const int32_t* block_table, const int32_t* seq_lens, const float* k_scale,
+                                       const float* v_scale, float* out, int64_t B, int64_t C, int64_t Hq,
+                                       int64_t Hkv, int64_t D, int64_t page_size, int64_t max_pages,
+                                       int64_t num_pages, int kv_dtype, float scale, const gqa_av_plan* plan,
+                                       void* stream) {
+    return run_attention_paged(q, k_pages, v_pages, block_table, seq_lens, k_scale, v_scale, out, B, C, Hq, Hkv, D,
+                               page_size, max_pages, num_pages, kv_dtype, scale, plan, stream, kRunCombine);
+}
+
+int gqa_attention_paged_decode(const float* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                               const int32_t* seq_lens, const float* k_scale, const float* v_scale, float* out,
+                               int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int64_t page_size,
+                               int64_t max_pages, int64_t num_pages, int kv_dtype, float scale, int mode,
+                               void* stream) {
+    if (page_size < 1) return fail(GQA_AV_ERR_INVALID_ARG, "page_size must be >= 1");
+    gqa_av_plan plan;
+    int rc = auto_plan(v_pages, B, C, Hq, Hkv, D, kv_dtype, mode, 1, &plan, page_size, 1);
+    if (rc != GQA_AV_OK) return rc;
+    return gqa_attention_paged_decode_plan(q, k_pages, v_pages, block_table, seq_lens, k_scale, v_scale, out, B, C,
+                                           Hq, Hkv, D, page_size, max_pages, num_pages, kv_dtype, scale, &plan,
+                                           stream);
 }
 
 const char* gqa_av_status_string(int status) {

@@ -86,6 +86,40 @@ int gqa_attention_fp8_decode_combine(const float *q, const void *K, const float 
                                      const float *v_scale, float *out, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
                                      int64_t D, float scale, const gqa_av_plan *plan, void *stream);
 
+/* A paged K and V cache (the serving layout; not on the page): K and V each
+ * live in a page pool [num_pages][page_size][Hkv][D] of kv_dtype (bf16, or
+ * fp8 E4M3 with k_scale and v_scale as above; with bf16 both scales must be
+ * NULL), and the two pools share one block table: row c of sequence b is row
+ * c mod page_size of page block_table[b][c / page_size] in both. block_table
+ * [B][max_pages] and seq_lens [B] are int32 device arrays; only rows
+ * c < seq_lens[b] take part, and a length of 0 writes zeros. C is the
+ * capacity (C <= max_pages * page_size; lengths are clamped into [0, C] and
+ * table entries into [0, num_pages) on the device, so a bad table gives wrong
+ * numbers, never a fault, as in gqa_paged_av.h). page_size is a power of two;
+ * the pools are aligned as K and V above. Plans: gqa_av_make_plan with
+ * hint->attention = 1 and hint->page_size = page_size. */
+int gqa_attention_paged_decode(const float *q, const void *k_pages, const void *v_pages, const int32_t *block_table,
+                               const int32_t *seq_lens, const float *k_scale, const float *v_scale, float *out,
+                               int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int64_t page_size,
+                               int64_t max_pages, int64_t num_pages, int kv_dtype, float scale, int mode,
+                               void *stream);
+int gqa_attention_paged_decode_plan(const float *q, const void *k_pages, const void *v_pages,
+                                    const int32_t *block_table, const int32_t *seq_lens, const float *k_scale,
+                                    const float *v_scale, float *out, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
+                                    int64_t D, int64_t page_size, int64_t max_pages, int64_t num_pages, int kv_dtype,
+                                    float scale, const gqa_av_plan *plan, void *stream);
+int gqa_attention_paged_decode_pass1(const float *q, const void *k_pages, const void *v_pages,
+                                     const int32_t *block_table, const int32_t *seq_lens, const float *k_scale,
+                                     const float *v_scale, float *out, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
+                                     int64_t D, int64_t page_size, int64_t max_pages, int64_t num_pages, int kv_dtype,
+                                     float scale, const gqa_av_plan *plan, void *stream);
+int gqa_attention_paged_decode_combine(const float *q, const void *k_pages, const void *v_pages,
+                                       const int32_t *block_table, const int32_t *seq_lens, const float *k_scale,
+                                       const float *v_scale, float *out, int64_t B, int64_t C, int64_t Hq,
+                                       int64_t Hkv, int64_t D, int64_t page_size, int64_t max_pages,
+                                       int64_t num_pages, int kv_dtype, float scale, const gqa_av_plan *plan,
+                                       void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -224,3 +224,105 @@ def test_attention_fp8_equals_bf16_on_widened_values():
         a = _run_fp8(q, K8, None, V8, None, 0.1, plan=p8)
         b = _run(q, K8.to(torch.bfloat16), V8.to(torch.bfloat16), 0.1, plan=p16)
         assert np.array_equal(a, b), ns
+
+
+# ---- paged K and V (two page pools sharing one block table) ---------------------
+
+def _page(K, V, P, seed, spare=3):
+    """K and V [B,C,Hkv,D] cut into pages of P rows, both pools in one shuffled
+    order with spare pages (filled with NaN: never read), and the block table."""
+    B, C, Hkv, D = K.shape
+    maxp = -(-C // P)
+    npg = B * maxp + spare
+    g = torch.Generator().manual_seed(seed)
+    perm = torch.randperm(npg, generator=g)[:B * maxp]
+    pools = []
+    for X in (K, V):
+        pool = torch.empty((npg, P, Hkv, D), dtype=X.dtype)
+        raw = pool.view(torch.uint8) if X.element_size() == 1 else pool.view(torch.int16)
+        raw.fill_(0x7F if X.element_size() == 1 else 0x7FC0)            # NaN in E4M3 / bf16
+        pad = torch.zeros((B, maxp * P, Hkv, D), dtype=X.dtype)
+        pad[:, :C] = X
+        pool[perm] = pad.reshape(B * maxp, P, Hkv, D)
+        pools.append(pool)
+    return pools[0], pools[1], perm.to(torch.int32).view(B, maxp).contiguous()
+
+
+def _paged_cases():
+    cases, k = [], 0
+    for dt in ("bf16", "fp8"):
+        for G, D, C, P in ((2, 128, 700, 16), (4, 64, 1000, 1), (8, 128, 2100, 64), (16, 256, 333, 8),
+                           (5, 128, 257, 256), (17, 64, 1500, 32)):
+            cases.append((dt, 1 + k % 3, C, G * (1, 2, 4)[k % 3], (1, 2, 4)[k % 3], D, P))
+            k += 1
+    return cases
+
+
+@pytest.mark.parametrize("dt,B,C,Hq,Hkv,D,P", _paged_cases())
+def test_attention_paged_sweep(dt, B, C, Hq, Hkv, D, P, oracle_lib):
+    """Paged K and V, bf16 and fp8 (per-KV-head scales): G 2..17, D 64..256,
+    pages of 1..256 rows, shuffled pools with NaN spare pages, lengths from 0
+    to the capacity, forced splits; against the paged attention oracle with
+    the dense bound on each sequence's first len rows."""
+    q, K, V = _inputs(B, C, Hq, Hkv, D, seed=B * 7 + C + P)
+    ks = vs = None
+    if dt == "fp8":
+        K, ks = _quantize(K)
+        V, vs = _quantize(V)
+    kp, vp, bt = _page(K, V, P, seed=C + P)
+    g = torch.Generator().manual_seed(C)
+    lens = torch.randint(0, C + 1, (B,), generator=g, dtype=torch.int32)
+    lens[0] = C
+    if B > 2:
+        lens[2] = 0
+    scale = D ** -0.5
+    ref = oracle_lib.attention_paged(q, kp, vp, bt, lens, dt, scale, ks, vs, C=C)
+    plans = [ga.make_plan(B, C, Hq, Hkv, D, dt, nsplit=ns, attention=True, page_size=P) for ns in (0, 1, 3)]
+    if Hkv % 2 == 0:
+        plans.append(ga.make_plan(B, C, Hq, Hkv, D, dt, nsplit=2, kv_tile=2, attention=True, page_size=P))
+    kd = K.float() * (ks.view(1, 1, -1, 1) if ks is not None else 1.0)
+    vd = V.float() * (vs.view(1, 1, -1, 1) if vs is not None else 1.0)
+    for plan in plans:
+        out = ga.gqa_attention_paged_decode(q.to(DEV), kp.to(DEV), vp.to(DEV), bt.to(DEV), lens.to(DEV), scale=scale,
+                                            C=C, plan=plan, k_scale=None if ks is None else ks.to(DEV),
+                                            v_scale=None if vs is None else vs.to(DEV))
+        out = out.cpu().numpy().astype(np.float64)
+        for b in range(B):
+            n = int(lens[b])
+            label = f"paged attention {dt} {(B, C, Hq, Hkv, D)} P={P} b={b} len={n} {plan.as_dict()}"
+            if n == 0:
+                assert (out[b] == 0).all(), label
+                continue
+            _check(out[b:b + 1], ref[b:b + 1], q[b:b + 1], kd[b:b + 1, :n], vd[b:b + 1, :n], scale, label)
+
+
+def test_attention_paged_in_order_equals_dense():
+    """Pages in order at full length give the dense call's output bit for bit
+    (same splits, same arithmetic)."""
+    B, C, Hq, Hkv, D, P = 2, 1024, 32, 4, 128, 16
+    q, K, V = _inputs(B, C, Hq, Hkv, D, seed=61)
+    kp, vp = K.reshape(-1, P, Hkv, D).contiguous(), V.reshape(-1, P, Hkv, D).contiguous()
+    bt = torch.arange(B * C // P, dtype=torch.int32).view(B, C // P).contiguous()
+    lens = torch.full((B,), C, dtype=torch.int32)
+    for ns, ht in ((1, 1), (4, 2)):
+        pd = ga.make_plan(B, C, Hq, Hkv, D, "bf16", nsplit=ns, kv_tile=ht, attention=True)
+        pp = ga.make_plan(B, C, Hq, Hkv, D, "bf16", nsplit=ns, kv_tile=ht, attention=True, page_size=P)
+        assert pd.rows_per_split == pp.rows_per_split
+        a = _run(q, K, V, 0.1, plan=pd)
+        b = ga.gqa_attention_paged_decode(q.to(DEV), kp.to(DEV), vp.to(DEV), bt.to(DEV), lens.to(DEV), scale=0.1,
+                                          plan=pp).cpu().numpy().astype(np.float64)
+        assert np.array_equal(a, b), (ns, ht)
+
+
+def test_attention_paged_pass1_then_combine_is_the_call():
+    B, C, Hq, Hkv, D, P = 3, 3000, 64, 8, 128, 16
+    q, K, V = _inputs(B, C, Hq, Hkv, D, seed=71)
+    kp, vp, bt = _page(K, V, P, seed=72)
+    lens = torch.tensor([3000, 17, 2048], dtype=torch.int32)
+    call = ga.BoundAttentionPaged(q.to(DEV), kp.to(DEV), vp.to(DEV), bt.to(DEV), lens.to(DEV), scale=0.1, C=C)
+    whole = call().clone()
+    call.out.fill_(float("nan"))
+    call.pass1()
+    got = call.combine()
+    torch.cuda.synchronize()
+    assert torch.equal(whole, got)

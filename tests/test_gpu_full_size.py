@@ -2,7 +2,7 @@
 D = 128, bf16) in the launch configurations the bench times, for the products
 whose other tests cut that workload to 8 sequences: the fused softmax product,
 the score step (bf16 and fp8 K), paged V (16-row pages, shuffled, full
-lengths), fp8 V (per-KV-head scales) and fused decode attention (bf16, and fp8 K and V). The GPU computes all 64 sequences with the plan the
+lengths), fp8 V (per-KV-head scales) and fused decode attention (bf16, fp8 K and V, and both paged). The GPU computes all 64 sequences with the plan the
 bench uses; sequences are independent, so the oracle checks a sample of them
 one by one, with the same gates as the per-product tests. All tests need an
 MI355X and are marked ``gpu``.
@@ -157,3 +157,29 @@ def test_full_size_attention_fp8(oracle_lib):
     for b in SAMPLE:
         ref = oracle_lib.attention_fp8(q[b:b + 1], K8[b:b + 1], V8[b:b + 1], ks, vs, scale)
         _check(out[b:b + 1], ref, q[b:b + 1], kd[b:b + 1], vd[b:b + 1], scale, f"full-size attention fp8 b={b}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp8"])
+def test_full_size_attention_paged(dt, oracle_lib):
+    """Paged K and V in 16-row pages (shuffled, full lengths), as the bench runs it."""
+    from tests.test_gpu_attention import _check, _page, _quantize
+    q, K = make_qk_random(W.B, W.C, W.Hq, W.Hkv, W.D, "bf16", seed=0)
+    _, V = make_qk_random(W.B, W.C, W.Hq, W.Hkv, W.D, "bf16", seed=1)
+    ks = vs = None
+    if dt == "fp8":
+        K, ks = _quantize(K)
+        V, vs = _quantize(V)
+    kp, vp, bt = _page(K, V, 16, seed=0, spare=0)
+    lens = torch.full((W.B,), W.C, dtype=torch.int32)
+    scale = W.D ** -0.5
+    plan = ga.make_plan(W.B, W.C, W.Hq, W.Hkv, W.D, dt, cu_count=_cus(), attention=True, page_size=16)
+    _say(f"[full] attention paged {dt} plan={plan.as_dict()}")
+    out = ga.gqa_attention_paged_decode(q.to(DEV), kp.to(DEV), vp.to(DEV), bt.to(DEV), lens.to(DEV), scale=scale,
+                                        plan=plan, k_scale=None if ks is None else ks.to(DEV),
+                                        v_scale=None if vs is None else vs.to(DEV))
+    out = out.cpu().numpy().astype(np.float64)
+    kd = K.float() * (ks.view(1, 1, -1, 1) if ks is not None else 1.0)
+    vd = V.float() * (vs.view(1, 1, -1, 1) if vs is not None else 1.0)
+    for b in SAMPLE:
+        ref = oracle_lib.attention_paged(q[b:b + 1], kp, vp, bt[b:b + 1], lens[b:b + 1], dt, scale, ks, vs, C=W.C)
+        _check(out[b:b + 1], ref, q[b:b + 1], kd[b:b + 1], vd[b:b + 1], scale, f"full-size attention paged {dt} b={b}")

@@ -122,7 +122,8 @@ def test_paged_sweep(B, C, Hq, Hkv, D, P, dt, oracle_lib):
     (full, partial, 1 and 0), plain and fused, automatic and forced splits."""
     s, V = make_scores_random(B, C, Hq, Hkv, D, dt, seed=C + D + P, score_std=2.0)
     pages, bt = _paged_from_dense(V, P, seed=P + B)
-    lens = torch.tensor([C, C // 2 + 3, 1, 0][:B], dtype=torch.int32)
+    # full, partial, 1 and 0 rows over the cases (a length of 0 under split plans too)
+    lens = torch.tensor([C, 0] if B == 2 else [C // 2 + 3, 1, 0], dtype=torch.int32)
     attn = torch.softmax(s.double(), dim=1).float().contiguous()
     modes = ("auto", "per_head") if Hq // Hkv >= 2 else ("auto",)
     for softmax, w in ((False, attn), (True, s)):

@@ -606,3 +606,45 @@ def test_qk_paged_plans_and_refusals():
     assert call(pg, bt=None) == 1 and call(pg, ln=None) == 1
     assert call(pg, ks=fake) == 1                             # k_scale is for fp8 K
     assert "k_scale" in ga.load().gqa_av_last_error().decode()
+
+
+@pytest.mark.parametrize("kvdt", ["bf16", "fp8"])
+def test_attention_plans(kvdt):
+    """Fused attention plans: the bf16 matrix engine with the fused softmax,
+    dense or paged, D of 64/128/256; splits tile C; refusals."""
+    for B, C, Hq, Hkv, D, P in [(64, 8192, 64, 8, 128, 0), (4, 32768, 16, 8, 128, 16), (1, 4096, 32, 8, 128, 0),
+                                (4, 32768, 16, 1, 128, 64), (2, 700, 40, 2, 256, 8), (3, 1, 8, 4, 64, 1)]:
+        p = ga.make_plan(B, C, Hq, Hkv, D, kvdt, attention=True, page_size=P, cu_count=256)
+        assert p.attention == 1 and p.softmax == 1 and p.engine == 3 and p.page_size == P
+        assert p.nsplit == -(-C // p.rows_per_split)
+        if P:
+            assert p.rows_per_split <= (1024 - 1) * P             # a split's pages fit the LDS list
+    for bad in (dict(v_dtype="f16"), dict(D=96), dict(engine="valu"), dict(mode="per_head")):
+        kw = dict(B=2, C=100, Hq=8, Hkv=2, D=128, v_dtype=kvdt)
+        kw.update(bad)
+        with pytest.raises(ga.GqaAvError):
+            ga.make_plan(kw.pop("B"), kw.pop("C"), kw.pop("Hq"), kw.pop("Hkv"), kw.pop("D"), kw.pop("v_dtype"),
+                         attention=True, **kw)
+
+
+def test_attention_calls_reject_before_launch():
+    lib = ga.load()
+    fake = ctypes.c_void_p(1 << 20)
+    f = ctypes.c_float(1.0)
+    dense = ga.make_plan(2, 100, 8, 2, 128, "bf16", attention=True)
+    pg = ga.make_plan(2, 100, 8, 2, 128, "bf16", attention=True, page_size=16)
+    plain = ga.make_plan(2, 100, 8, 2, 128, "bf16", softmax=True)
+
+    def paged(plan, ks=None, P=16, maxp=8, dt=2, kp=fake):
+        return lib.gqa_attention_paged_decode_plan(fake, kp, fake, fake, fake, ks, None, fake, 2, 100, 8, 2, 128,
+                                                   P, maxp, 16, dt, f, ctypes.byref(plan), None)
+    assert paged(dense) == 1                                  # not a paged plan
+    assert paged(plain) == 1                                  # not an attention plan
+    assert lib.gqa_attention_decode_plan(fake, fake, fake, fake, 2, 100, 8, 2, 128, 2, f, ctypes.byref(pg), None) == 1
+    assert paged(pg, ks=fake) == 1                            # scales are for fp8
+    assert "k_scale" in lib.gqa_av_last_error().decode()
+    assert paged(pg, P=32) == 1 and paged(pg, maxp=6) == 1    # page size, capacity
+    assert paged(pg, dt=1) == 3                               # f16 K and V
+    assert paged(pg, kp=ctypes.c_void_p((1 << 20) + 8)) == 3  # K pages not 16-byte aligned
+    pg8 = ga.make_plan(2, 100, 8, 2, 128, "fp8", attention=True, page_size=16)
+    assert paged(pg8, dt=3, ks=ctypes.c_void_p((1 << 20) + 2)) == 1   # misaligned k_scale

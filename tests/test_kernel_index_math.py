@@ -153,12 +153,37 @@ def _check_plan(p, B, C, Hq, Hkv, D, es=2):
                 npg = ((cb + nr - 1) >> shift) - pg0 + 1
                 assert npg <= 1024 and (cb + nr - 1) // P < -(-C // P)
                 ns_ = -(-nr // RSTEP)
+                uniform = es == 1 and P >= RPI and cb % RPI == 0 and P * vrow <= 2 ** 31 - 1   # fp8 only
                 for step in range(ns_ + (1 if ns_ > 1 else 0)):
                     for wave in range(4):
                         r0 = 32 * (step * WPH + wave % WPH)
                         rows = np.minimum(r0 + RPI * np.arange(LPI)[:, None] + lanes[None, :] // PR, nr - 1)
                         idx = ((cb + rows) >> shift) - pg0
                         assert idx.min() >= 0 and idx.max() < npg
+                        if not uniform:
+                            continue
+                        # pages of >= RPI rows: one page per load, through a
+                        # resource from the page's row 0 (head kv) that ends
+                        # with the split's last row in it
+                        kvl = wave // WPH
+                        vlane = (lanes // PR) * vrow + kvl * D * es + (lanes % PR) * 8 * es
+                        for i in range(LPI):
+                            r = cb + r0 + RPI * i
+                            assert r % RPI == 0
+                            pidx = min((r >> shift) - pg0, npg - 1)
+                            assert 0 <= pidx < npg
+                            pstart = r & ~(P - 1)
+                            vr = min(P, cb + nr - pstart)
+                            nrec = vr * vrow - kv * D * es if vr > 0 else 0
+                            assert 0 <= nrec <= P * vrow - kv * D * es and nrec < 2 ** 31
+                            off = vlane + (r & (P - 1)) * vrow
+                            c = r + lanes // PR                  # the rows the lanes load
+                            live = c < cb + nr
+                            assert np.array_equal(off + 8 * es <= nrec, live)
+                            # a live lane reads its own row's piece of its page
+                            assert (c[live] >> shift == r >> shift).all()
+                            assert np.array_equal(off[live], ((c[live] & (P - 1)) * vrow + kvl * D * es
+                                                              + (lanes[live] % PR) * 8 * es))
         vrec = (nrows - 1) * vrow + HT * D * es
         assert ((b * C + cb) * Hkv + kv) * D * es + vrec <= B * C * Hkv * D * es and vrec < 2 ** 31
         wrec = ((nrows - 1) * Hq + (HT - 1) * G + nq) * 4

@@ -27,6 +27,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import statistics
 import sys
 import time
@@ -54,8 +55,9 @@ KERNEL_SOURCES = {
 KERNEL_SOURCES["softmax"] = KERNEL_SOURCES["av"]
 KERNEL_SOURCES["attn"] = KERNEL_SOURCES["av"]
 # Profile file prefix and the dominant kernel's name fragment, per operation.
+# op: (profile prefix, regular expression for the dominant kernel's name)
 OPS = {"av": ("pass1", "pass1"), "qk": ("qk", "qk_scores"), "softmax": ("softmax_pass1", "pass1"),
-       "attn": ("attn_pass1", "false, true>")}   # the fused instantiation (dense, with scores from q and K)
+       "attn": ("attn_pass1", r"av_pass1_mfma_bf16<[^>]*, true>")}   # scores from q and K (dense or paged)
 SOFTMAX_METRIC = "GQA decode fused softmax x V: µs/call and achieved HBM GB/s (% of MI355X peak)"
 
 
@@ -159,7 +161,7 @@ def summarize_pmc(dirs, copy_mib: float, out: str, command: str, op: str = "av")
         traffic = v * 1024 * ff + w * 1024 * wf
         lines.append(f"| {k[:90]} | {v:.1f} | {w:.1f} | {traffic:.0f} |")
         prefix, fragment = OPS[op]
-        if fragment in k:
+        if re.search(fragment, k):
             extra.append(f"{prefix}_traffic_bytes: {traffic:.0f}")
     lines += [""] + extra
     with open(out, "w") as fh:

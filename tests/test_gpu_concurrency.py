@@ -47,6 +47,10 @@ def _problems():
     out.append(("softmax G=3 f16", lambda st, s=s.to(DEV), V=V.to(DEV): ga.bind_softmax(s, V, stream=st)))
     q, K = make_qk_random(2, 7000, 32, 8, 128, "bf16", seed=4)
     out.append(("qk G=4", lambda st, q=q.to(DEV), K=K.to(DEV): ga.bind_qk(q, K, scale=0.125, stream=st)))
+    q, K = make_qk_random(2, 5000, 64, 8, 128, "bf16", seed=5)
+    _, V = make_qk_random(2, 5000, 64, 8, 128, "bf16", seed=6)
+    out.append(("attention G=8", lambda st, q=q.to(DEV), K=K.to(DEV), V=V.to(DEV):
+                ga.BoundAttention(q, K, V, scale=0.125, stream=st)))
     return out
 
 

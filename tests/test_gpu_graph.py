@@ -133,3 +133,24 @@ def test_graph_attention():
     _, V = make_qk_random(B, C, Hq, Hkv, D, "bf16", seed=7)
     q, K, V = q.to(DEV), K.to(DEV), V.to(DEV)
     _graph_matches_eager("attention", lambda s: ga.BoundAttention(q, K, V, scale=0.125, stream=s), q, _fresh(q, 5))
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_graph_attention_paged(fp8):
+    """Paged K and V (16-row pages in shuffled order, ragged lengths), bf16 or
+    fp8 with per-KV-head scales, captured and replayed."""
+    from tests.test_gpu_attention import _page, _quantize
+    B, C, Hq, Hkv, D = 3, 3000, 64, 8, 128
+    q, K = make_qk_random(B, C, Hq, Hkv, D, "bf16", seed=8)
+    _, V = make_qk_random(B, C, Hq, Hkv, D, "bf16", seed=9)
+    ks = vs = None
+    if fp8:
+        K, ks = _quantize(K)
+        V, vs = _quantize(V)
+        ks, vs = ks.to(DEV), vs.to(DEV)
+    kp, vp, bt = _page(K, V, 16, seed=10)
+    lens = torch.tensor([3000, 1234, 17], dtype=torch.int32, device=DEV)
+    q, kp, vp, bt = q.to(DEV), kp.to(DEV), vp.to(DEV), bt.to(DEV)
+    _graph_matches_eager(f"attention paged fp8={fp8}",
+                         lambda s: ga.BoundAttentionPaged(q, kp, vp, bt, lens, scale=0.125, C=C, stream=s,
+                                                          k_scale=ks, v_scale=vs), q, _fresh(q, 11))

@@ -1066,6 +1066,14 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int r0 = 32 * (st * WPH * U + u * WPH + wh);
+            // UNI: the chunk's page-list entries, all read before the first
+            // is used (one wait for the lot).
+            int pl[UNI ? LPI : 1];
+            if constexpr (UNI) {
+#pragma unroll
+                for (int i = 0; i < LPI; ++i)
+                    pl[i] = s_pages[min(static_cast<int>(((cb + r0 + RPI * i) >> a.page_shift) - pg0), npg - 1)];
+            }
 #pragma unroll
             for (int i = 0; i < LPI; ++i) {
                 if constexpr (UNI) {
@@ -1075,8 +1083,7 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
                     // touches no memory. QK: K from its pool at the same offsets.
                     const int64_t r = cb + r0 + RPI * i;            // the load's first row
                     const int64_t pstart = r & ~pmask;
-                    const int pix = __builtin_amdgcn_readfirstlane(
-                        s_pages[min(static_cast<int>((r >> a.page_shift) - pg0), npg - 1)]);
+                    const int pix = __builtin_amdgcn_readfirstlane(pl[i]);
                     const int64_t vr = min(pmask + 1, cb + nrows - pstart);   // valid rows of the page
                     const size_t pbase = (static_cast<size_t>(pix) << a.page_shift) * vrow + T.kv * D * VES;
                     const int nrec = vr > 0 ? static_cast<int>(vr * vrow - T.kv * D * VES) : 0;

@@ -1,5 +1,6 @@
 """GPU parity of fused decode attention (scores, softmax and product in one
-pass over bf16 K and V) through the C ABI, against the fp64 attention oracle.
+pass over K and V: bf16, fp8 with per-KV-head scales, dense or paged) through
+the C ABI, against the fp64 attention oracles.
 
 Bound: the scores carry the score step's fp32 error, |ds_c| <= 2 D 2^-24
 scale sum_d |q K| (every product exact, fp32 sums); a softmax weight moves by

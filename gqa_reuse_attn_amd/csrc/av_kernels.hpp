@@ -995,6 +995,16 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
         const_cast<uint8_t*>(QK ? a.K : a.V) + (PG ? 0 : ((static_cast<size_t>(T.b) * a.C + cb) * a.Hkv + T.kv) * D * VES),
         0, QK && !PG && nrows > 0 ? (nrows - 1) * vrow + HT * D * VES : 0, kRawBufferFlags);
     constexpr int NKK = QK ? D / 32 : 1;             // 32-wide d blocks of a score
+    // Dense bf16 K loads straight into the B operand's layout (KD): load i of
+    // a chunk is rows 16 t2 + n (t2 = i / NKK), piece 4 kk + g (kk = i % NKK),
+    // so lane 16 g + n already holds what the score MFMAs take and K skips
+    // LDS. Measured on MI355X (B = 64, C = 8192, Hkv = 8, G = 8): bf16
+    // attention 319.4 -> 312.8 us, G = 2 88.7 -> 85.1; fp8 the other way
+    // (193.0 -> 262.7: each 8-byte load then touches 16 rows' cache lines
+    // instead of 4), so fp8 and paged K keep the row-major loads through LDS.
+    constexpr bool KD = QK && !PG && !FP8;
+    static_assert(!QK || LPI == 2 * NKK, "one K load per B operand");
+    const int klane = (lane & 15) * vrow + kvl * D * VES + (lane >> 4) * PB;
     u32x4 qa[3][NSET][NKK];
     if constexpr (QK) {
 #pragma unroll
@@ -1110,13 +1120,19 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
                         bf.k[u][i] = __builtin_nontemporal_load(reinterpret_cast<const Piece*>(a.K + off));
                 } else if constexpr (FP8) {
                     bf.v[u][i] = __builtin_amdgcn_raw_buffer_load_b64(vres, vlane, (r0 + RPI * i) * vrow, kCachePolicyNt);
-                    if constexpr (QK)
+                    if constexpr (KD)
+                        bf.k[u][i] = __builtin_amdgcn_raw_buffer_load_b64(
+                            kres, klane, (r0 + 16 * (i / NKK)) * vrow + 4 * (i % NKK) * PB, kCachePolicyNt);
+                    else if constexpr (QK)
                         bf.k[u][i] = __builtin_amdgcn_raw_buffer_load_b64(kres, vlane, (r0 + RPI * i) * vrow,
                                                                           kCachePolicyNt);
                 } else {
                     bf.v[u][i] = __builtin_amdgcn_raw_buffer_load_b128(vres, vlane, (r0 + RPI * i) * vrow,
                                                                        kCachePolicyNt);
-                    if constexpr (QK)
+                    if constexpr (KD)
+                        bf.k[u][i] = __builtin_amdgcn_raw_buffer_load_b128(
+                            kres, klane, (r0 + 16 * (i / NKK)) * vrow + 4 * (i % NKK) * PB, kCachePolicyNt);
+                    else if constexpr (QK)
                         bf.k[u][i] = __builtin_amdgcn_raw_buffer_load_b128(kres, vlane, (r0 + RPI * i) * vrow,
                                                                            kCachePolicyNt);
                 }
@@ -1162,10 +1178,13 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
             // QK: the chunk's scores, in the weights' layout (head m + 16 s, rows 8 g .. 8 g + 7).
             float sc[QK ? NSET : 1][QK ? 8 : 1];
             if constexpr (QK) {
+                if constexpr (!KD) {
 #pragma unroll
-                for (int i = 0; i < LPI; ++i)
-                    *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(region + st_off(i)) = to_bf16(bf.k[u][i]);
-                asm volatile("" ::: "memory");
+                    for (int i = 0; i < LPI; ++i)
+                        *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(region + st_off(i)) =
+                            to_bf16(bf.k[u][i]);
+                    asm volatile("" ::: "memory");
+                }
                 // B operand: lane 16 g + n holds row 16 t2 + n, d = 32 kk + 8 g .. + 7 (piece 4 kk + g).
                 f32x4 sacc[NSET][2];
 #pragma unroll
@@ -1177,8 +1196,12 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
 #pragma unroll
                     for (int kk = 0; kk < NKK; ++kk) {
                         const int row = 16 * t2 + m, piece = 4 * kk + g;
-                        const u32x4 kb = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-                            region + row * RB + 32 * ((piece >> 1) ^ swz(row)) + 16 * (piece & 1));
+                        u32x4 kb;
+                        if constexpr (KD)
+                            kb = to_bf16(bf.k[u][t2 * NKK + kk]);
+                        else
+                            kb = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+                                region + row * RB + 32 * ((piece >> 1) ^ swz(row)) + 16 * (piece & 1));
 #pragma unroll
                         for (int k = 0; k < 3; ++k)
 #pragma unroll

@@ -587,3 +587,34 @@ def test_qk_lds_relayout(D, dt):
                 if g == 0:
                     groups.add((off // 16) % 16)
             assert len(groups) == 16                      # the 16 rows of one lane group: distinct bank groups
+
+
+@pytest.mark.parametrize("D,es", [(64, 2), (128, 2), (256, 2)])
+def test_attention_direct_k_loads(D, es):
+    """Dense bf16 fused attention loads K straight into the score MFMA's B layout:
+    load i of a chunk gives lane 16 g + n piece 4 kk + g of row 16 t2 + n
+    (t2 = i / NKK, kk = i % NKK) of its KV head, through the K resource that
+    ends with the split's last row; rows past the split read as zero."""
+    PR, NKK = D // 8, D // 32
+    LPI, PB = PR // 2, 8 * es
+    assert LPI == 2 * NKK
+    lanes = np.arange(64)
+    g, n = lanes >> 4, lanes & 15
+    for Hkv, HT in ((1, 1), (4, 2), (8, 4)):
+        vrow = Hkv * D * es
+        for kv in range(0, Hkv, HT):
+            for nrows in (1, 17, 32, 45, 100):
+                krec = (nrows - 1) * vrow + HT * D * es
+                for kvl in range(HT):
+                    klane = n * vrow + kvl * D * es + g * PB
+                    for r0 in range(0, ((nrows + 31) // 32 + 1) * 32, 32):   # with the pipeline's reload past the end
+                        for i in range(LPI):
+                            t2, kk = i // NKK, i % NKK
+                            off = klane + (r0 + 16 * t2) * vrow + 4 * kk * PB
+                            row = r0 + 16 * t2 + n
+                            piece = 4 * kk + g
+                            # the element the lane must hold: row, KV head kv + kvl, d = 8 piece .. + 7
+                            assert np.array_equal(off, row * vrow + kvl * D * es + piece * PB)
+                            assert (piece < D // 8).all()
+                            assert np.array_equal(off + PB <= krec, row < nrows)
+                            assert (off[row < nrows] >= 0).all()

@@ -648,3 +648,27 @@ def test_attention_calls_reject_before_launch():
     assert paged(pg, kp=ctypes.c_void_p((1 << 20) + 8)) == 3  # K pages not 16-byte aligned
     pg8 = ga.make_plan(2, 100, 8, 2, 128, "fp8", attention=True, page_size=16)
     assert paged(pg8, dt=3, ks=ctypes.c_void_p((1 << 20) + 2)) == 1   # misaligned k_scale
+
+
+def test_tuned_plan_choices():
+    """The automatic plans the measurements chose (256 CUs): two workgroups per
+    CU for the fp8 fused softmax and fused attention, one for the plain fp8
+    product and for bf16; attention splits down to 128 rows on a grid smaller
+    than the chip; splits of at least 512 rows otherwise."""
+    def plan(*shape, dt, **kw):
+        return ga.make_plan(*shape, dt, cu_count=256, **kw)
+    big = (64, 8192, 64, 8, 128)
+    assert plan(*big, dt="fp8", softmax=True).grid == 512
+    assert plan(*big, dt="fp8", attention=True).grid == 512
+    assert plan(*big, dt="fp8").grid == 256
+    assert plan(*big, dt="bf16", attention=True).grid == 256
+    assert plan(*big, dt="bf16", softmax=True).grid == 256
+    small = (1, 4096, 32, 8, 128)                     # 8 tiles: 32 splits of 128 rows
+    for dt in ("bf16", "fp8"):
+        p = plan(*small, dt=dt, attention=True)
+        assert (p.nsplit, p.rows_per_split, p.grid) == (32, 128, 256)
+    mqa = (4, 32768, 16, 1, 128)                      # 64 splits of 512 rows in every variant
+    for dt in ("bf16", "fp8"):
+        for kw in (dict(attention=True), dict(softmax=True), {}):
+            p = plan(*mqa, dt=dt, **kw)
+            assert (p.nsplit, p.rows_per_split, p.grid) == (64, 512, 256), (dt, kw)

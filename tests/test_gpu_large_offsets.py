@@ -1,7 +1,7 @@
 """GPU parity with V, K or the page pool larger than 4 GiB, so that the byte
 offsets of later sequences (and of high page numbers) do not fit in 32 bits:
-the plain and fused products on both engines, the score step, paged V and
-fp8 V. Inputs are drawn on the GPU from a seeded generator (torch's, not this
+the plain and fused products on both engines, the score step, paged V, fp8
+V and paged fused attention. Inputs are drawn on the GPU from a seeded generator (torch's, not this
 library); the oracle checks the first, a middle and the last sequence one by
 one, after copying only those slices to the host. All tests need an MI355X
 and are marked ``gpu``.
@@ -140,3 +140,45 @@ def test_fp8_beyond_4gib(oracle_lib):
             _check(out[b:b + 1].cpu().numpy().astype(np.float64), ref, xb, qb, scale.cpu(), softmax,
                    f"4GiB fp8 b={b} softmax={softmax}")
     del V8, s, out
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_attention_paged_beyond_4gib(fp8, oracle_lib):
+    """Paged fused attention over K and V pools each larger than 4 GiB (16-row
+    pages shuffled over the whole pool, full and partial lengths), bf16 or fp8
+    with per-KV-head scales. Wrong page addressing gives gross errors, so the
+    sampled sequences are checked with the parity gate against the paged
+    attention oracle (the full error bound would need 2 GB host arrays here)."""
+    from tests.parity import gate
+    B, P, Hq = (33 if fp8 else 17), 16, 16
+    maxp = C // P
+    shape = (B * maxp, P, Hkv, D)
+    ks = vs = None
+    if fp8:
+        kp = (_big(shape, torch.bfloat16, 11) * 32.0).to(torch.float8_e4m3fn)   # |x| < 448: 14 sigma
+        vp = (_big(shape, torch.bfloat16, 12) * 32.0).to(torch.float8_e4m3fn)
+        ks = torch.full((Hkv,), 1.0 / 32.0, device=DEV)
+        vs = torch.full((Hkv,), 0.125, device=DEV)
+    else:
+        kp = _big(shape, torch.bfloat16, 11)
+        vp = _big(shape, torch.bfloat16, 12)
+    assert kp.numel() * kp.element_size() > 2 ** 32 and vp.numel() * vp.element_size() > 2 ** 32
+    perm = torch.randperm(B * maxp, generator=torch.Generator().manual_seed(13)).to(torch.int32)
+    bt = perm.view(B, maxp).contiguous()
+    lens = torch.full((B,), C, dtype=torch.int32)
+    lens[B // 2] = C // 2 + 7
+    q = _big((B, Hq, D), torch.float32, 14)
+    scale = D ** -0.5
+    _say(f"[4GiB] attention paged fp8={fp8}")
+    out = ga.gqa_attention_paged_decode(q, kp, vp, bt.to(DEV), lens.to(DEV), scale=scale, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    for b in _sample(B):
+        idx = bt[b].long().to(DEV)
+        kb, vb = kp[idx].cpu(), vp[idx].cpu()                 # this sequence's pages, in its order
+        btb = torch.arange(maxp, dtype=torch.int32).view(1, maxp)
+        ref = oracle_lib.attention_paged(q[b:b + 1].cpu(), kb, vb, btb, lens[b:b + 1], "fp8" if fp8 else "bf16",
+                                         scale, None if ks is None else ks.cpu(), None if vs is None else vs.cpu(),
+                                         C=C)
+        ok, msg = gate(out[b:b + 1].cpu().numpy().astype(np.float64), ref, "bf16")
+        assert ok, f"4GiB attention paged fp8={fp8} b={b}: {msg}"
+    del kp, vp, out

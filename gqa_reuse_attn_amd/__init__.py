@@ -27,7 +27,7 @@ __all__ = [
     "LIB_PATH", "GqaAvError", "Hint", "Plan", "load", "resolve_mode", "make_plan",
     "gqa_av_decode", "gqa_av_decode_plan", "bind", "BoundCall", "release", "status_string", "MODES", "DTYPES",
     "QkHint", "QkPlan", "qk_make_plan", "gqa_qk_decode", "bind_qk", "gqa_softmax_av_decode", "bind_softmax",
-    "gqa_av_paged_decode", "bind_paged", "gqa_av_fp8_decode", "bind_fp8",
+    "gqa_av_paged_decode", "bind_paged", "gqa_av_fp8_decode", "bind_fp8", "stream_read",
 ]
 
 # GQA_AV_LIBRARY may name another build of the same library (tuning variants).
@@ -35,7 +35,8 @@ LIB_PATH = os.environ.get("GQA_AV_LIBRARY") or os.path.join(os.path.dirname(os.p
 
 MODES = {"auto": -1, "per_head": 0, "reuse": 1}
 ENGINES = {"auto": 0, "valu": 1, "mfma": 2, "mfma_bf16": 3}
-COMBINES = {"auto": 0, "kernel": 1, "last": 2}
+COMBINES = {"auto": 0, "kernel": 1}
+SPLIT_ORDERS = {"auto": 0, "contiguous": 1, "interleaved": 2}
 DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3}   # fp8: OCP FP8 E4M3 (V only)
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "INELIGIBLE", 3: "UNSUPPORTED", 4: "HIP"}
 
@@ -51,7 +52,7 @@ class Hint(ctypes.Structure):
     _fields_ = [("engine", ctypes.c_int32), ("nsplit", ctypes.c_int32), ("cu_count", ctypes.c_int32),
                 ("v_align", ctypes.c_int32), ("combine", ctypes.c_int32), ("kv_tile", ctypes.c_int32),
                 ("softmax", ctypes.c_int32), ("page_size", ctypes.c_int32), ("attention", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 1)]
+                ("waves", ctypes.c_int32), ("split_order", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2)]
 
 
 class Plan(ctypes.Structure):
@@ -61,7 +62,7 @@ class Plan(ctypes.Structure):
                 ("threads", ctypes.c_int32), ("rows_per_split", ctypes.c_int64), ("grid", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_int64), ("v_bytes_read", ctypes.c_int64),
                 ("combine", ctypes.c_int32), ("kv_heads_per_tile", ctypes.c_int32), ("softmax", ctypes.c_int32),
-                ("page_size", ctypes.c_int32), ("attention", ctypes.c_int32), ("reserved", ctypes.c_int32 * 1)]
+                ("page_size", ctypes.c_int32), ("attention", ctypes.c_int32), ("interleave", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
@@ -170,9 +171,26 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gqa_qk_decode_plan.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ip, ctypes.c_float,
                                        ctypes.POINTER(QkPlan), vp]
     lib.gqa_qk_decode_plan.restype = ip
-    del i32
+    lib.gqa_bench_stream_read.argtypes = [vp, i64, i32, i32, vp, vp]
+    lib.gqa_bench_stream_read.restype = ip
     _lib = lib
     return lib
+
+
+def stream_read(buf, nbytes: int, workgroups: int, loads_in_flight: int, sink, stream=None) -> None:
+    """Enqueue the plain streaming read of gqa_bench.h over the first nbytes of
+    the GPU tensor `buf` (a measurement aid: the bandwidth ceiling, no part of
+    the product). sink: a GPU uint32/int32 tensor of at least 256 elements."""
+    torch = _torch()
+    if not (buf.is_cuda and sink.is_cuda) or nbytes > buf.numel() * buf.element_size() or sink.numel() < 256 \
+            or sink.element_size() != 4:
+        raise ValueError("buf must be a GPU tensor of at least nbytes bytes and sink 256 32-bit GPU words")
+    if stream is None:
+        stream = torch.cuda.current_stream(buf.device)
+    rc = load().gqa_bench_stream_read(buf.data_ptr(), int(nbytes), int(workgroups), int(loads_in_flight),
+                                      sink.data_ptr(), stream.cuda_stream)
+    if rc != 0:
+        _raise(rc)
 
 
 def status_string(status: int) -> str:
@@ -203,13 +221,16 @@ def resolve_mode(Hq: int, Hkv: int, mode: Union[str, int] = "auto") -> str:
 def make_plan(B: int, C: int, Hq: int, Hkv: int, D: int, v_dtype: str, mode: Union[str, int] = "auto",
               engine: Union[str, int] = "auto", nsplit: int = 0, cu_count: int = 0, v_align: int = 0,
               combine: Union[str, int] = "auto", kv_tile: int = 0, softmax: bool = False,
-              page_size: int = 0, attention: bool = False) -> Plan:
+              page_size: int = 0, attention: bool = False, waves: int = 0,
+              split_order: Union[str, int] = "auto") -> Plan:
     """Host-only planning (no GPU needed). nsplit/cu_count/v_align/kv_tile <= 0 mean automatic.
 
-    engine: "auto" | "valu" | "mfma" | "mfma_bf16"; combine: "auto" | "kernel" | "last";
+    engine: "auto" | "valu" | "mfma" | "mfma_bf16"; combine: "auto" | "kernel";
     kv_tile: adjacent KV heads per workgroup; softmax: plan the fused softmax product;
     page_size > 0: plan for a paged V cache with that many rows per page;
-    attention: plan the fused decode attention (scores from q and K; bf16).
+    attention: plan the fused decode attention (scores from q and K; bf16);
+    waves: waves per workgroup (4, or 8 for the plain product on the bf16 matrix engine);
+    split_order: "auto" | "contiguous" | "interleaved" (how a split context is cut).
     """
     h = Hint()
     h.engine = ENGINES[engine] if isinstance(engine, str) else int(engine)
@@ -218,6 +239,8 @@ def make_plan(B: int, C: int, Hq: int, Hkv: int, D: int, v_dtype: str, mode: Uni
     h.softmax = 1 if softmax else 0
     h.page_size = int(page_size)
     h.attention = 1 if attention else 0
+    h.waves = int(waves)
+    h.split_order = SPLIT_ORDERS[split_order] if isinstance(split_order, str) else int(split_order)
     p = Plan()
     rc = load().gqa_av_make_plan(B, C, Hq, Hkv, D, DTYPES[v_dtype], _mode(mode), ctypes.byref(h), ctypes.byref(p))
     if rc != 0:

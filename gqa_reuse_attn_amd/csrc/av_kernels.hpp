@@ -6,22 +6,14 @@
 // it produce the G outputs of that head's group from one read of each V row;
 // its per-query-head shader (kept here as the baseline) reads V once per head.
 //
-// A workgroup (256 threads = 4 wave64) owns a tile = (b, kv_h, head
-// sub-group, D-tile) -- or (b, q_h, D-tile) for the per-head baseline -- and
-// one context split [cb, ce). It streams the tile's V rows of that split once
-// and keeps fp32 accumulators for every query head of the tile. Without a
-// context split it writes `out` directly. With one, the split partial sums
-// are added in increasing split order, either
-//  * in the same kernel: every workgroup stores its partials with
-//    agent-scope (device-coherent) stores, waits for them to complete, and
-//    counts itself in on a per-tile counter; the workgroup that arrives last
-//    reads the tile's partials back with agent-scope loads and writes `out`.
-//    Because the partials themselves are coherent at device scope, no L2
-//    write-back or invalidate is needed (a release/acquire fence at agent
-//    scope costs a whole-L2 maintenance operation per workgroup on the
-//    per-XCD L2s of MI355X), or
-//  * in a second kernel over split planes (the kernel boundary orders them).
-// Both sum in the same fixed order, so a plan is bitwise reproducible.
+// A workgroup owns a tile = (b, kv_h, head sub-group, D-tile) -- or
+// (b, q_h, D-tile) for the per-head baseline -- and one context split
+// [cb, ce). It streams the tile's V rows of that split once and keeps fp32
+// accumulators for every query head of the tile. Without a context split it
+// writes `out` directly. With one, it writes its split's partial sums to a
+// plane of the workspace and a second kernel adds the planes in a fixed
+// order (the kernel boundary orders them), so a plan is bitwise
+// reproducible.
 //
 // Two inner-product engines, both fp32 FMA arithmetic:
 //  * VALU  -- any G and D. Lc lanes cover a D-row with VB-byte loads (one
@@ -95,7 +87,7 @@ struct Pass1Args {
     const float* attn;      // [B][C][Hq]
     const uint8_t* V;       // [B][C][Hkv][D] of DT
     float* out;             // [B][Hq][D]
-    float* part;            // combine in kernel: [tiles][nsplit][tile outputs]; else [nsplit][B][Hq][D]
+    float* part;            // nsplit > 1: [nsplit][B][Hq][D] partial sums
     float* stats;           // fused softmax with nsplit > 1: [nsplit][B][Hq] pairs (maximum score, weight sum),
                             // 16-byte aligned
     const int32_t* block_table;  // paged V: [B][max_pages], the page of each page-long run of a sequence's rows
@@ -108,10 +100,9 @@ struct Pass1Args {
     const uint8_t* K;            // fused attention: [B][C][Hkv][D] keys, V's element type
     float qk_scale;              // fused attention: the scores are qk_scale * q . K
     const float* k_scale;        // fused attention over fp8 K: [Hkv] scale of each KV head's keys (NULL: 1)
-    uint32_t* counters;     // combine in kernel: [tiles], zero between calls
-    int32_t combine;        // 1: last workgroup of a tile adds the splits; 0: second kernel
     int64_t C;
-    int64_t rows_per_split;
+    int64_t rows_per_split;  // contiguous splits: rows of each; interleaved: rows of one block (a pipeline step)
+    int32_t interleave;      // 1: split s takes the blocks s, s + nsplit, s + 2 nsplit, ... of the sequence
     int32_t B, Hq, Hkv, D;
     int32_t G;              // Hq / Hkv
     int32_t per_head;       // 0: reuse tiles, 1: one query head per tile
@@ -290,7 +281,6 @@ __device__ inline int64_t uniform64(int64_t x) {
 
 struct Tile {
     int b, kv, s, dt, q_first, nq;
-    uint32_t id;    // tile index without the split: counter and partial block
 };
 
 // Logical order, fastest first: (sub-group, D-tile), kv_h, split, b, and for
@@ -307,7 +297,6 @@ __device__ inline Tile decode_tile(const Pass1Args& a, int GT) {
     T.s = t % a.nsplit; t /= a.nsplit;
     T.b = t % a.B; t /= a.B;
     const uint32_t major = t;
-    T.id = ((major * a.B + T.b) * nkvt + kvt) * nminor + minor;
     if (a.per_head) {
         T.dt = minor;
         T.q_first = T.kv * a.G + major;
@@ -321,87 +310,11 @@ __device__ inline Tile decode_tile(const Pass1Args& a, int GT) {
     return T;
 }
 
-// ---- in-kernel split combine ------------------------------------------------
+// ---- split partials ---------------------------------------------------------
 
-// Split partials are added as kSplitGroups contiguous ranges of splits (see
-// combine_last and av_pass2_combine).
+// The fused softmax's second-kernel combine adds split partials as
+// kSplitGroups contiguous ranges of splits (see av_pass2_softmax_combine).
 constexpr int kSplitGroups = 8;
-
-// Agent-scope relaxed atomics: on gfx950 these are plain loads and stores with
-// the device-coherence cache policy, so they bypass the XCD-private cache state.
-__device__ inline void store_coherent(float* p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline float load_coherent(const float* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Floats of one (tile, split) block of partials: the tile's outputs rounded up
-// to whole float4s, so every block starts 16-byte aligned.
-__device__ __host__ constexpr int padded_outputs(int TO) { return (TO + 3) / 4 * 4; }
-
-constexpr int kQuadsPerBlock = kThreads / kSplitGroups;
-
-// Called by all threads of a workgroup after each stored its share of the
-// split's TO partial sums with store_coherent() into blk = the tile's block
-// [nsplit][padded_outputs(TO)]. In the one workgroup that arrives last, every
-// tile output k is summed over the splits in the fixed association of
-// av_pass2_combine (kSplitGroups contiguous split ranges, each summed from
-// +0 in increasing split order, then the range sums in range order) and
-// handed to emit(k, sum). Each thread owns whole float4s of outputs and
-// issues their split loads in batches, with no barrier between batches.
-template <typename Emit>
-__device__ inline void combine_last(const Pass1Args& a, const Tile& T, const float* blk, int TO, Emit emit) {
-    __shared__ uint32_t s_last;
-    // The partials must have reached device scope before this workgroup counts
-    // itself in: wait for every outstanding store of this wave, then barrier.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(a.counters + T.id, 1u, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        s_last = prev == static_cast<uint32_t>(a.nsplit - 1);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    const int ns = a.nsplit;
-    const int TOP = padded_outputs(TO), nquads = TOP / 4;
-    // Device-coherent float4 reads of the tile's block; the resource bounds
-    // every access to the block.
-    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(blk), 0, ns * TOP * 4, kRawBufferFlags);
-    constexpr int kBatch = 16;
-    for (int quad = threadIdx.x; quad < nquads; quad += kThreads) {
-        f32x4 total = {0.0f, 0.0f, 0.0f, 0.0f}, part = {0.0f, 0.0f, 0.0f, 0.0f};
-        int g = 0;
-        int gend = ns / kSplitGroups;                // first split past group 0
-        auto close_group = [&]() {
-            total = g == 0 ? part : total + part;
-            part = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            ++g;
-            gend = static_cast<int>((static_cast<int64_t>(ns) * (g + 1)) / kSplitGroups);
-        };
-        for (int s0 = 0; s0 < ns; s0 += kBatch) {
-            f32x4 v[kBatch];
-#pragma unroll
-            for (int k = 0; k < kBatch; ++k)
-                if (s0 + k < ns)
-                    v[k] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, ((s0 + k) * TOP + quad * 4) * 4, 0,
-                                                                 kCachePolicySc1);
-#pragma unroll
-            for (int k = 0; k < kBatch; ++k) {
-                if (s0 + k >= ns) break;
-                while (s0 + k >= gend) close_group();
-                part += v[k];
-            }
-        }
-        while (g < kSplitGroups) close_group();
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            if (quad * 4 + c < TO) emit(quad * 4 + c, total[c]);
-    }
-    if (threadIdx.x == 0) __hip_atomic_store(a.counters + T.id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // ---- pass 1: VALU engine ----------------------------------------------------
 
@@ -440,8 +353,14 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
     const int lane_d = T.dt * Lc + (j - kvl * a.L);  // which VB-chunk of that head's D-row
     const bool active = (r < rps) && (lane_d < a.L);
 
-    const int64_t cb = static_cast<int64_t>(T.s) * a.rows_per_split;
-    int64_t ce_ = min(a.C, cb + a.rows_per_split);
+    // Rows of the split: contiguous, [cb, ce); or interleaved (dense V), the
+    // blocks of R rows s, s + nsplit, s + 2 nsplit, ... of the whole sequence
+    // (then cb = 0 and ce = C), so the splits of a tile, which run at the same
+    // time, stream neighbouring rows (a plain read over such blocks runs a few
+    // per cent faster on MI355X than one contiguous slice per workgroup).
+    const bool il = !PG && a.interleave;
+    const int64_t cb = il ? 0 : static_cast<int64_t>(T.s) * a.rows_per_split;
+    int64_t ce_ = il ? a.C : min(a.C, cb + a.rows_per_split);
     if constexpr (PG) {
         const int64_t len = a.seq_lens[T.b];
         ce_ = min(ce_, len < 0 ? int64_t{0} : min(len, a.C));
@@ -488,7 +407,10 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
         kRawBufferFlags);
     const int voff = r * vrow32 + (kvl * a.D * ES + lane_d * VB);
     const int woff = (r * a.Hq + q_lo) * 4;
-    const int nsteps = (nrows + R - 1) / R;
+    const int nblk = (nrows + R - 1) / R;           // blocks of R rows in [cb, ce)
+    const int nsteps = il ? (nblk > T.s ? (nblk - T.s + a.nsplit - 1) / a.nsplit : 0) : nblk;
+    // First row (from cb) of this workgroup's step st.
+    auto step_row = [&](int st) { return (il ? st * a.nsplit + T.s : st) * R; };
     // PG: the split's pages, from the block table into LDS.
     __shared__ int32_t s_pages[PG ? kMaxSplitPages : 1];
     const int64_t pg0 = PG ? (cb >> a.page_shift) : 0;
@@ -510,7 +432,7 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
     auto load = [&](Buf& bf, int st) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int row = st * R + u * rps;        // of this step's slot 0; the lane adds r
+            const int row = step_row(st) + u * rps;  // of this step's slot 0; the lane adds r
             if constexpr (PG) {
                 // Rows past the split read its last row (their weight is 0).
                 const int64_t c = cb + min(row + r, nrows - 1);
@@ -528,7 +450,7 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
             float x[U][GT], nm[GT];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const bool ok = st * R + u * rps + r < nrows;
+                const bool ok = step_row(st) + u * rps + r < nrows;
 #pragma unroll
                 for (int g = 0; g < GT; ++g) x[u][g] = ok ? bf.w[u][g] : -INFINITY;
             }
@@ -639,10 +561,7 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
     // Sum the row slots: slot kk of thread tid lives at smem[kk * 256 + tid].
     // Output slot k = g * E + e of lane chunk jj is tile output k * Lc + jj.
     const int TO = NACC * Lc;
-    const bool in_kernel = a.nsplit > 1 && a.combine;
-    const int TOP = padded_outputs(TO);
-    float* const blk = in_kernel ? a.part + static_cast<size_t>(T.id) * a.nsplit * TOP : nullptr;
-    float* const plane = (a.nsplit > 1 && !a.combine) ? a.part + static_cast<size_t>(T.s) * a.B * a.Hq * a.D : a.out;
+    float* const plane = a.nsplit > 1 ? a.part + static_cast<size_t>(T.s) * a.B * a.Hq * a.D : a.out;
     auto out_index = [&](int k, int jj, size_t* o) -> bool {
         const int g = k / E, e = k - (k / E) * E;
         const int kl = jj / a.L;
@@ -678,12 +597,8 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
                 // The KV head's scale, once per output (the sums are linear in V).
                 if (a.v_scale) sum *= a.v_scale[(lane_q_lo(jj / a.L) + k / E) / a.G];
             }
-            if (in_kernel) {
-                store_coherent(blk + static_cast<size_t>(T.s) * TOP + k * Lc + jj, sum);
-            } else {
-                size_t o;
-                if (out_index(k, jj, &o)) plane[o] = sum;
-            }
+            size_t o;
+            if (out_index(k, jj, &o)) plane[o] = sum;
         }
         __syncthreads();
     }
@@ -702,13 +617,6 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
                 st[1] = empty ? 1.0f : s_stat[1][tid];
             }
         }
-    }
-    if (in_kernel) {
-        combine_last(a, T, blk, TO, [&](int idx, float v) {
-            const int k = idx / Lc, jj = idx - (idx / Lc) * Lc;
-            size_t o;
-            if (out_index(k, jj, &o)) a.out[o] = v;
-        });
     }
 }
 
@@ -822,10 +730,7 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma(Pass1Args a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) red[wave * TO + ((s * DE + e) * 4 + i) * 64 + lane] = acc[s][e][i];
     __syncthreads();
-    const bool in_kernel = a.nsplit > 1 && a.combine;
-    static_assert(TO % 4 == 0, "MFMA tile outputs come in whole float4s");
-    float* const blk = in_kernel ? a.part + static_cast<size_t>(T.id) * a.nsplit * TO : nullptr;
-    float* const plane = (a.nsplit > 1 && !a.combine) ? a.part + static_cast<size_t>(T.s) * a.B * a.Hq * a.D : a.out;
+    float* const plane = a.nsplit > 1 ? a.part + static_cast<size_t>(T.s) * a.B * a.Hq * a.D : a.out;
     auto out_index = [&](int idx, size_t* o) -> bool {
         const int l = idx & 63, reg = idx >> 6;
         const int i = reg & 3, se = reg >> 2;
@@ -838,18 +743,8 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma(Pass1Args a) {
         float sum = red[idx];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w) sum += red[w * TO + idx];
-        if (in_kernel) {
-            store_coherent(blk + static_cast<size_t>(T.s) * TO + idx, sum);
-        } else {
-            size_t o;
-            if (out_index(idx, &o)) plane[o] = sum;
-        }
-    }
-    if (in_kernel) {
-        combine_last(a, T, blk, TO, [&](int idx, float v) {
-            size_t o;
-            if (out_index(idx, &o)) a.out[o] = v;
-        });
+        size_t o;
+        if (out_index(idx, &o)) plane[o] = sum;
     }
 }
 
@@ -876,9 +771,10 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma(Pass1Args a) {
 // lane groups of a column read hit different banks.
 //
 // PR = D / 8 16-byte pieces per row (8, 16 or 32); NSET sets of 16 heads; U
-// chunks of 32 rows per wave and buffer, two buffers in flight; HT adjacent
-// KV heads per workgroup (1, 2 or 4), each streamed by kWaves / HT waves, so
-// the workgroup reads HT * 2 D contiguous bytes of every row.
+// chunks of 32 rows per wave and buffer, two buffers in flight; NW waves per
+// workgroup (4 or 8); HT adjacent KV heads per workgroup (1, 2 or 4), each
+// streamed by NW / HT waves, so the workgroup reads HT * 2 D contiguous bytes
+// of every row.
 //
 // SM: fused softmax (see av_pass1_valu). A wave keeps one running maximum per
 // head for its rows: the four lane groups holding a head's weights of a chunk
@@ -904,25 +800,27 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma(Pass1Args a) {
 // swizzled region); S times qk_scale then passes through the region once more
 // to reach the weights' layout, and the fused softmax runs on it as on scores
 // read from memory.
-template <int PR, int NSET, int U, int HT, bool SM = false, int VDT = kBF16, bool PG = false, bool QK = false>
-__global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
+template <int PR, int NSET, int U, int HT, bool SM = false, int VDT = kBF16, bool PG = false, bool QK = false,
+          int NW = kWaves>
+__global__ __launch_bounds__(64 * NW) void av_pass1_mfma_bf16(Pass1Args a) {
+    constexpr int NTH = 64 * NW;                     // threads of the workgroup
     static_assert(!QK || SM, "fused attention runs the fused softmax");
     static_assert(PR == 8 || PR == 16 || PR == 32, "D must be 64, 128 or 256");
     static_assert(VDT == kBF16 || VDT == kFP8, "bf16 or fp8 V");
     constexpr bool FP8 = VDT == kFP8;
     constexpr int VES = FP8 ? 1 : 2;                 // bytes of one V element in memory
     constexpr int PB = 8 * VES;                      // bytes of one 8-value piece in memory
-    static_assert(HT == 1 || HT == 2 || HT == 4, "KV heads per tile must divide the waves");
+    static_assert((HT == 1 || HT == 2 || HT == 4) && NW % HT == 0, "KV heads per tile must divide the waves");
     constexpr int D = PR * 8;
     constexpr int RB = PR * 16;                      // bytes of one D-row
     constexpr int NT = D / 16;                       // 16-column output tiles
     constexpr int LPI = PR / 2;                      // 16-byte loads per lane and chunk
     constexpr int RPI = 64 / PR;                     // rows one 64-lane load covers
-    constexpr int WPH = kWaves / HT;                 // waves per KV head
+    constexpr int WPH = NW / HT;                     // waves per KV head
     constexpr int TO = 16 * NSET * D;                // outputs of one KV head's tile
     constexpr int TOW = HT * TO;                     // outputs of the workgroup
-    constexpr int STAGE = kWaves * 32 * RB;          // bytes: one 32-row region per wave
-    constexpr int RED = kWaves * TO * 4;             // bytes: the final cross-wave sum
+    constexpr int STAGE = NW * 32 * RB;              // bytes: one 32-row region per wave
+    constexpr int RED = NW * TO * 4;                 // bytes: the final cross-wave sum
     __shared__ __align__(16) uint8_t smem[STAGE > RED ? STAGE : RED];
 
     const Tile T = decode_tile(a, 16 * NSET);
@@ -934,8 +832,11 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
     const int wh = wave % WPH;                       // which of that head's waves
 
     // The split bounds are workgroup-uniform; keep them in scalar registers.
-    const int64_t cb = uniform64(static_cast<int64_t>(T.s) * a.rows_per_split);
-    int64_t ce_ = min(a.C, cb + a.rows_per_split);
+    // Interleaved splits (dense V; see av_pass1_valu): cb = 0, ce = C, and the
+    // workgroup takes the steps s, s + nsplit, ... of the sequence.
+    const bool il = !PG && !QK && a.interleave;
+    const int64_t cb = il ? 0 : uniform64(static_cast<int64_t>(T.s) * a.rows_per_split);
+    int64_t ce_ = il ? a.C : min(a.C, cb + a.rows_per_split);
     if constexpr (PG) {
         const int64_t len = a.seq_lens[T.b];
         ce_ = min(ce_, len < 0 ? int64_t{0} : min(len, a.C));
@@ -962,7 +863,7 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
     const int npg = PG && nrows > 0 ? static_cast<int>(((cb + nrows - 1) >> a.page_shift) - pg0 + 1) : 0;
     if constexpr (PG) {
         const int32_t* const btr = a.block_table + static_cast<size_t>(T.b) * a.max_pages + pg0;
-        for (int i = threadIdx.x; i < npg; i += kThreads) {
+        for (int i = threadIdx.x; i < npg; i += NTH) {
             const int32_t pg = btr[i];
             s_pages[i] = pg < 0 ? 0 : (pg >= a.num_pages ? static_cast<int32_t>(a.num_pages - 1) : pg);
         }
@@ -1061,7 +962,10 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
     }
 
     constexpr int RSTEP = 32 * WPH * U;             // rows per workgroup step
-    const int nsteps = (nrows + RSTEP - 1) / RSTEP;
+    const int nblk = (nrows + RSTEP - 1) / RSTEP;   // steps of the rows [cb, ce)
+    const int nsteps = il ? (nblk > T.s ? (nblk - T.s + a.nsplit - 1) / a.nsplit : 0) : nblk;
+    // First row (from cb) of this workgroup's step st.
+    auto step_row = [&](int st) { return (il ? st * a.nsplit + T.s : st) * RSTEP; };
 
     typedef typename std::conditional<FP8, u32x2, u32x4>::type Piece;
     struct Buf {
@@ -1069,13 +973,13 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
         Piece k[QK ? U : 1][QK ? LPI : 1];           // QK: the chunk's K pieces
         float w[U][NSET][QK ? 1 : 8];                // weights or scores read from memory (not with QK)
     };
-    // Chunk u of step st starts at split row 32 (st WPH U + u WPH + wh).
+    // Chunk u of step st starts at split row step_row(st) + 32 (u WPH + wh).
     // UNI: PG with pages of at least RPI rows (see page_uniform).
     auto load = [&](Buf& bf, int st, auto uni) {
         constexpr bool UNI = decltype(uni)::value;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int r0 = 32 * (st * WPH * U + u * WPH + wh);
+            const int r0 = step_row(st) + 32 * (u * WPH + wh);
             // UNI: the chunk's page-list entries, all read before the first
             // is used (one wait for the lot).
             int pl[UNI ? LPI : 1];
@@ -1244,7 +1148,7 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
             if constexpr (SM) {
                 // Scores of rows 8 g .. 8 g + 7 of the chunk; rows past the
                 // split read as zero and must not count.
-                const int rb = 32 * (st * WPH * U + u * WPH + wh) + 8 * g;
+                const int rb = step_row(st) + 32 * (u * WPH + wh) + 8 * g;
                 float nm[NSET];
                 bool up = false;
 #pragma unroll
@@ -1363,7 +1267,7 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
     // SM: each wave's maximum and weight sum per head (lane group 0 holds head
     // m + 16 s after the sum over the four lane groups).
     constexpr int GH = 16 * NSET;
-    __shared__ float s_wm[kWaves][GH], s_wl[kWaves][GH], s_tm[HT][GH], s_tl[HT][GH];
+    __shared__ float s_wm[NW][GH], s_wl[NW][GH], s_tm[HT][GH], s_tl[HT][GH];
     if constexpr (SM) {
 #pragma unroll
         for (int s = 0; s < NSET; ++s) {
@@ -1423,9 +1327,7 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) red[wave * TO + ((s * NT + t) * 4 + i) * 64 + lane] = acc[s][t][i];
     __syncthreads();
-    const bool in_kernel = a.nsplit > 1 && a.combine;
-    float* const blk = in_kernel ? a.part + static_cast<size_t>(T.id) * a.nsplit * TOW : nullptr;
-    float* const plane = (a.nsplit > 1 && !a.combine) ? a.part + static_cast<size_t>(T.s) * a.B * a.Hq * D : a.out;
+    float* const plane = a.nsplit > 1 ? a.part + static_cast<size_t>(T.s) * a.B * a.Hq * D : a.out;
     auto out_index = [&](int idx, size_t* o) -> bool {
         const int k = idx / TO, e = idx - k * TO;
         const int l = e & 63, reg = e >> 6;
@@ -1435,7 +1337,7 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
         *o = (static_cast<size_t>(T.b) * a.Hq + T.q_first + k * a.G + h) * D + 16 * t + (l & 15);
         return h < T.nq;
     };
-    for (int idx = threadIdx.x; idx < TOW; idx += kThreads) {
+    for (int idx = threadIdx.x; idx < TOW; idx += NTH) {
         const int k = idx / TO, e = idx - k * TO;
         float sum = red[k * WPH * TO + e];
 #pragma unroll
@@ -1450,12 +1352,8 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
         if constexpr (FP8) {
             if (a.v_scale) sum *= a.v_scale[T.kv + k];   // the tile's k-th KV head
         }
-        if (in_kernel) {
-            store_coherent(blk + static_cast<size_t>(T.s) * TOW + idx, sum);
-        } else {
-            size_t o;
-            if (out_index(idx, &o)) plane[o] = sum;
-        }
+        size_t o;
+        if (out_index(idx, &o)) plane[o] = sum;
     }
     if constexpr (SM) {
         if (a.nsplit > 1 && threadIdx.x < HT * GH) {
@@ -1467,12 +1365,6 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma_bf16(Pass1Args a) {
                 stp[1] = s_tl[k][hh];
             }
         }
-    }
-    if (in_kernel) {
-        combine_last(a, T, blk, TOW, [&](int idx, float v) {
-            size_t o;
-            if (out_index(idx, &o)) a.out[o] = v;
-        });
     }
 }
 

@@ -8,38 +8,53 @@ namespace gqa_av {
 
 // ---- pass 2: split-C combine -------------------------------------------------
 
-// out[i] = sum over s of part[s][i] for the `plane` outputs, in a fixed order:
-// the splits are cut into kSplitGroups contiguous ranges, each summed in
-// increasing s by its own thread, and the range sums are then added in
-// increasing range order. Each thread covers four consecutive outputs.
+// out[i] = sum over s of part[s][i] for the `plane` outputs, in a fixed order.
+// A workgroup covers kThreads / S quads (4 consecutive outputs) with S split
+// groups each: group g of a quad sums the contiguous split range
+// [nsplit * g / S, nsplit * (g + 1) / S) in increasing s, and the S group sums
+// are then added in increasing g. S (a power of two, 8 to 64) is chosen by
+// the host so that a group holds at most four splits when it can: a thread's
+// loads of a batch of four are issued together (addresses clamped into its
+// range, values masked afterwards), so the kernel costs about one memory
+// round trip.
+constexpr int kCombineLoads = 4;     // loads a thread issues together
+template <int S>
 __global__ __launch_bounds__(kThreads) void av_pass2_combine(const float* __restrict__ part,
                                                              float* __restrict__ out,
                                                              int64_t plane, int32_t nsplit) {
-    __shared__ f32x4 red[kSplitGroups][kQuadsPerBlock];
-    const int q = threadIdx.x % kQuadsPerBlock;
-    const int sg = threadIdx.x / kQuadsPerBlock;
-    const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * kQuadsPerBlock + q) * 4;
-    const int s0 = static_cast<int>((static_cast<int64_t>(nsplit) * sg) / kSplitGroups);
-    const int s1 = static_cast<int>((static_cast<int64_t>(nsplit) * (sg + 1)) / kSplitGroups);
+    static_assert(S >= 1 && S <= kThreads && (S & (S - 1)) == 0, "split groups: a power of two");
+    constexpr int Q = kThreads / S;
+    __shared__ f32x4 red[kThreads];
+    const int q = threadIdx.x % Q;
+    const int g = threadIdx.x / Q;
+    const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * Q + q) * 4;
+    const int s0 = static_cast<int>((static_cast<int64_t>(nsplit) * g) / S);
+    const int s1 = static_cast<int>((static_cast<int64_t>(nsplit) * (g + 1)) / S);
     // Whole float4 loads need a plane of whole quads; the store needs `out` 16-byte aligned.
     const bool quads = (plane & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15u) == 0;
     f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
     if (quads && i0 + 3 < plane) {
-#pragma unroll 4
-        for (int s = s0; s < s1; ++s)
-            sum += *reinterpret_cast<const f32x4*>(part + static_cast<size_t>(s) * plane + i0);
+        for (int sb = s0; sb < s1; sb += kCombineLoads) {
+            f32x4 v[kCombineLoads];
+#pragma unroll
+            for (int k = 0; k < kCombineLoads; ++k)
+                v[k] = *reinterpret_cast<const f32x4*>(part + static_cast<size_t>(min(sb + k, s1 - 1)) * plane + i0);
+#pragma unroll
+            for (int k = 0; k < kCombineLoads; ++k)
+                if (sb + k < s1) sum += v[k];
+        }
     } else {
         for (int s = s0; s < s1; ++s)
 #pragma unroll
             for (int c = 0; c < 4; ++c)
                 if (i0 + c < plane) sum[c] += part[static_cast<size_t>(s) * plane + i0 + c];
     }
-    red[sg][q] = sum;
+    red[g * Q + q] = sum;
     __syncthreads();
-    if (sg == 0) {
-        f32x4 t = red[0][q];
+    if (g == 0) {
+        f32x4 t = red[q];
 #pragma unroll
-        for (int k = 1; k < kSplitGroups; ++k) t += red[k][q];
+        for (int k = 1; k < S; ++k) t += red[k * Q + q];
         if (quads && i0 + 3 < plane) {
             *reinterpret_cast<f32x4*>(out + i0) = t;
         } else {
@@ -48,6 +63,14 @@ __global__ __launch_bounds__(kThreads) void av_pass2_combine(const float* __rest
                 if (i0 + c < plane) out[i0 + c] = t[c];
         }
     }
+}
+
+// Split groups of av_pass2_combine for nsplit splits: the smallest power of
+// two from 8 up that leaves each group at most four splits, at most 64.
+inline int combine_groups(int nsplit) {
+    int S = 8;
+    while (S < 64 && S * 4 < nsplit) S *= 2;
+    return S;
 }
 
 // Fused softmax, several splits: split s left the unnormalised sum

@@ -21,12 +21,19 @@ hipError_t mfma(int DT, int DE, int nset, const gqa_av::Pass1Args& a, hipStream_
 
 // bf16 matrix engine, V of element type VDT (gqa_av::kBF16 or kFP8), paged V
 // when PG, fused attention (scores from q and K) when QK: D of 64, 128 or
-// 256, nset sets of 16 heads, ht KV heads per tile.
+// 256, nset sets of 16 heads, ht KV heads per tile, nw waves per workgroup
+// (4, or 8 for the plain product).
 template <int VDT, bool SM, bool PG = false, bool QK = false>
-hipError_t mfma_bf16(int64_t D, int nset, int ht, const gqa_av::Pass1Args& a, hipStream_t s);
+hipError_t mfma_bf16(int64_t D, int nset, int ht, int nw, const gqa_av::Pass1Args& a, hipStream_t s);
 
 // Score step, K of element type KDT: D / 32 blocks, nset sets of 16 heads.
 template <int KDT>
 hipError_t qk(int64_t D, int nset, const gqa_av::QkArgs& a, hipStream_t s);
+
+// Plain streaming read of `bytes` from src (the bandwidth ceiling): nblocks
+// workgroups of `slice` contiguous bytes each, loads_in_flight 16-byte loads
+// per lane and batch (4, 8 or 16).
+hipError_t stream_read(const uint8_t* src, int64_t bytes, int64_t slice, int nblocks, int loads_in_flight,
+                       uint32_t* sink, hipStream_t s);
 
 }  // namespace gqa_av_launch

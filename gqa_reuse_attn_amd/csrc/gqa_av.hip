@@ -11,6 +11,7 @@
 #include "gqa_fp8_av.h"
 #include "gqa_paged_av.h"
 #include "gqa_attention.h"
+#include "gqa_bench.h"
 #include "gqa_softmax_av.h"
 
 #include <hip/hip_runtime.h>
@@ -23,6 +24,7 @@
 #include <mutex>
 #include <string>
 #include <utility>
+#include <vector>
 
 #include "combine_kernels.hpp"
 #include "dispatch.hpp"
@@ -81,19 +83,19 @@ constexpr int64_t kTargetWgPerCuBf16Fp8Sm = 2;
 // 14.2 (16.3) for 8 splits of 512 rows.
 constexpr int64_t kMinRowsPerSplitAttn = 128;
 
-// Split-C workspace of one (device, stream). The per-tile counters live in a
-// buffer of their own: they must be zero before a call, every call leaves the
-// ones it used at zero again, and no partial sum may ever land on them,
-// whatever the next plan's layout.
+// Split-C workspace of one (device, stream): the buffer the split partials of
+// the calls on that stream go to. A HIP graph captured from such a call keeps
+// the buffer's address, so a buffer that has been handed out is never freed
+// before gqa_av_release(): when a later call needs more, the old buffer is
+// retired (kept) and a larger one takes its place.
 struct Workspace {
-    void* counters = nullptr;
-    size_t counter_bytes = 0;
     void* part = nullptr;
     size_t part_bytes = 0;
 };
 
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+std::vector<std::pair<int, void*>> g_ws_retired;   // (device, buffer), freed by gqa_av_release
 
 std::mutex g_cu_mutex;
 std::map<int, int> g_cu_count;
@@ -113,43 +115,42 @@ int device_cus(int dev, int* cus) {
     return GQA_AV_OK;
 }
 
-// Grow `*buf` to at least `bytes`. Earlier calls on `stream` may still use the
-// old buffer, so the stream is synchronised before it is freed. A new counter
-// buffer is zeroed on the stream.
-int grow(void** buf, size_t* have, size_t bytes, hipStream_t stream, bool zero) {
-    if (*have >= bytes) return GQA_AV_OK;
-    if (*buf) {
-        hipError_t e = hipStreamSynchronize(stream);
-        if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
-        e = hipFree(*buf);
-        *buf = nullptr;
-        *have = 0;
-        if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "hipFree: %s", hipGetErrorString(e));
-    }
-    void* p = nullptr;
-    hipError_t e = hipMalloc(&p, bytes);
-    if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "hipMalloc(%zu) for split-C workspace: %s", bytes, hipGetErrorString(e));
-    if (zero) {
-        e = hipMemsetAsync(p, 0, bytes, stream);
-        if (e != hipSuccess) {
-            (void)hipFree(p);
-            return fail(GQA_AV_ERR_HIP, "hipMemsetAsync: %s", hipGetErrorString(e));
-        }
-    }
-    *buf = p;
-    *have = bytes;
+// Is `stream` being captured into a HIP graph?
+int stream_capturing(hipStream_t stream, bool* capturing) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    const hipError_t e = hipStreamIsCapturing(stream, &st);
+    if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "hipStreamIsCapturing: %s", hipGetErrorString(e));
+    *capturing = st != hipStreamCaptureStatusNone;
     return GQA_AV_OK;
 }
 
-int get_workspace(int dev, hipStream_t stream, size_t counter_bytes, size_t part_bytes, uint32_t** counters,
-                  float** part) {
+// The split workspace of (dev, stream), at least `bytes` long. Growing it
+// allocates (hipMalloc, rounded up to a power of two so that the retired
+// buffers of a growing caller total less than the live one) and is refused
+// while the stream is being captured: a graph must not record an allocation,
+// and the call that first needs the space has to run outside the capture.
+int get_workspace(int dev, hipStream_t stream, size_t bytes, float** part) {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace& ws = g_ws[{dev, stream}];
-    int rc = GQA_AV_OK;
-    if (counter_bytes > 0) rc = grow(&ws.counters, &ws.counter_bytes, counter_bytes, stream, true);
-    if (rc == GQA_AV_OK) rc = grow(&ws.part, &ws.part_bytes, part_bytes, stream, false);
-    if (rc != GQA_AV_OK) return rc;
-    *counters = static_cast<uint32_t*>(ws.counters);
+    if (ws.part_bytes < bytes) {
+        bool capturing = false;
+        int rc = stream_capturing(stream, &capturing);
+        if (rc != GQA_AV_OK) return rc;
+        if (capturing)
+            return fail(GQA_AV_ERR_UNSUPPORTED,
+                        "the split workspace of this stream must grow to %zu bytes, which cannot happen during "
+                        "graph capture: make one call with this plan (or a larger one) on the stream before "
+                        "capturing", bytes);
+        size_t n = size_t{1} << 16;
+        while (n < bytes) n <<= 1;
+        void* p = nullptr;
+        const hipError_t e = hipMalloc(&p, n);
+        if (e != hipSuccess)
+            return fail(GQA_AV_ERR_HIP, "hipMalloc(%zu) for the split-C workspace: %s", n, hipGetErrorString(e));
+        if (ws.part) g_ws_retired.emplace_back(dev, ws.part);
+        ws.part = p;
+        ws.part_bytes = n;
+    }
     *part = static_cast<float*>(ws.part);
     return GQA_AV_OK;
 }
@@ -178,30 +179,30 @@ hipError_t launch_pass1(int v_dtype, const gqa_av_plan& p, int64_t D, const Pass
         if ((v_dtype != GQA_AV_BF16 && v_dtype != GQA_AV_FP8_E4M3) || p.engine != GQA_AV_ENGINE_MFMA_BF16 ||
             !p.softmax)
             return hipErrorInvalidValue;
-        const int nset = p.heads_per_tile / 16, ht = p.kv_heads_per_tile;
+        const int nset = p.heads_per_tile / 16, ht = p.kv_heads_per_tile, nw = p.threads / 64;
         using namespace gqa_av_launch;
         if (p.page_size > 0)
-            return v_dtype == GQA_AV_FP8_E4M3 ? mfma_bf16<gqa_av::kFP8, true, true, true>(D, nset, ht, a, s)
-                                              : mfma_bf16<gqa_av::kBF16, true, true, true>(D, nset, ht, a, s);
-        return v_dtype == GQA_AV_FP8_E4M3 ? mfma_bf16<gqa_av::kFP8, true, false, true>(D, nset, ht, a, s)
-                                          : mfma_bf16<gqa_av::kBF16, true, false, true>(D, nset, ht, a, s);
+            return v_dtype == GQA_AV_FP8_E4M3 ? mfma_bf16<gqa_av::kFP8, true, true, true>(D, nset, ht, nw, a, s)
+                                              : mfma_bf16<gqa_av::kBF16, true, true, true>(D, nset, ht, nw, a, s);
+        return v_dtype == GQA_AV_FP8_E4M3 ? mfma_bf16<gqa_av::kFP8, true, false, true>(D, nset, ht, nw, a, s)
+                                          : mfma_bf16<gqa_av::kBF16, true, false, true>(D, nset, ht, nw, a, s);
     }
     if (p.engine == GQA_AV_ENGINE_MFMA_BF16) {
         if (v_dtype != GQA_AV_BF16 && v_dtype != GQA_AV_FP8_E4M3) return hipErrorInvalidValue;
-        const int nset = p.heads_per_tile / 16, ht = p.kv_heads_per_tile;
+        const int nset = p.heads_per_tile / 16, ht = p.kv_heads_per_tile, nw = p.threads / 64;
         using namespace gqa_av_launch;
         if (p.page_size > 0) {
             if (v_dtype == GQA_AV_FP8_E4M3)
-                return p.softmax ? mfma_bf16<gqa_av::kFP8, true, true>(D, nset, ht, a, s)
-                                 : mfma_bf16<gqa_av::kFP8, false, true>(D, nset, ht, a, s);
-            return p.softmax ? mfma_bf16<gqa_av::kBF16, true, true>(D, nset, ht, a, s)
-                             : mfma_bf16<gqa_av::kBF16, false, true>(D, nset, ht, a, s);
+                return p.softmax ? mfma_bf16<gqa_av::kFP8, true, true>(D, nset, ht, nw, a, s)
+                                 : mfma_bf16<gqa_av::kFP8, false, true>(D, nset, ht, nw, a, s);
+            return p.softmax ? mfma_bf16<gqa_av::kBF16, true, true>(D, nset, ht, nw, a, s)
+                             : mfma_bf16<gqa_av::kBF16, false, true>(D, nset, ht, nw, a, s);
         }
         if (v_dtype == GQA_AV_FP8_E4M3)
-            return p.softmax ? mfma_bf16<gqa_av::kFP8, true>(D, nset, ht, a, s)
-                             : mfma_bf16<gqa_av::kFP8, false>(D, nset, ht, a, s);
-        return p.softmax ? mfma_bf16<gqa_av::kBF16, true>(D, nset, ht, a, s)
-                         : mfma_bf16<gqa_av::kBF16, false>(D, nset, ht, a, s);
+            return p.softmax ? mfma_bf16<gqa_av::kFP8, true>(D, nset, ht, nw, a, s)
+                             : mfma_bf16<gqa_av::kFP8, false>(D, nset, ht, nw, a, s);
+        return p.softmax ? mfma_bf16<gqa_av::kBF16, true>(D, nset, ht, nw, a, s)
+                         : mfma_bf16<gqa_av::kBF16, false>(D, nset, ht, nw, a, s);
     }
     if (p.engine == GQA_AV_ENGINE_MFMA) {
         if (p.softmax || p.page_size > 0 || v_dtype == GQA_AV_FP8_E4M3) return hipErrorInvalidValue;
@@ -257,22 +258,14 @@ bool mfma_bf16_fits(int v_dtype, int64_t Hq, int64_t Hkv, int64_t D, int v_align
 
 constexpr int64_t kMfmaMinGroup = 5;     // below this the VALU engine does less work
 
-constexpr int64_t kCounterBytes = 256;          // the counter block is padded to this
-
-int64_t counter_bytes(int64_t tiles) { return ceil_div(tiles * 4, kCounterBytes) * kCounterBytes; }
-
 // Floats from the start of the split planes to the fused softmax's statistics
 // (the planes rounded up to whole 16-byte groups).
 int64_t stats_offset(int64_t nsplit, int64_t B, int64_t Hq, int64_t D) { return (nsplit * B * Hq * D + 3) / 4 * 4; }
 
-// KERNEL: one fp32 plane of `out` per split, and for the fused softmax one
-// (maximum, weight sum) pair per split and (b, q_h) after the planes. LAST:
-// [tiles][nsplit][tile outputs] partials plus one counter per tile.
-int64_t workspace_bytes(int64_t B, int64_t Hq, int64_t D, int64_t tiles, int64_t nsplit, int64_t tile_outputs,
-                        int combine, bool softmax) {
+// One fp32 plane of `out` per split, and for the fused softmax one (maximum,
+// weight sum) pair per split and (b, q_h) after the planes.
+int64_t workspace_bytes(int64_t B, int64_t Hq, int64_t D, int64_t nsplit, bool softmax) {
     if (nsplit <= 1) return 0;
-    if (combine == GQA_AV_COMBINE_LAST)
-        return counter_bytes(tiles) + tiles * nsplit * gqa_av::padded_outputs(static_cast<int>(tile_outputs)) * 4;
     if (softmax) return stats_offset(nsplit, B, Hq, D) * 4 + nsplit * B * Hq * 2 * 4;
     return nsplit * B * Hq * D * 4;
 }
@@ -290,10 +283,12 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
     if (hint) h = *hint;
     if (h.engine < GQA_AV_ENGINE_AUTO || h.engine > GQA_AV_ENGINE_MFMA_BF16)
         return fail(GQA_AV_ERR_INVALID_ARG, "unknown engine %d", h.engine);
-    if (h.combine < GQA_AV_COMBINE_AUTO || h.combine > GQA_AV_COMBINE_LAST)
+    if (h.combine < GQA_AV_COMBINE_AUTO || h.combine > GQA_AV_COMBINE_KERNEL)
         return fail(GQA_AV_ERR_INVALID_ARG, "unknown combine %d", h.combine);
     if (h.softmax != 0 && h.softmax != 1) return fail(GQA_AV_ERR_INVALID_ARG, "hint softmax must be 0 or 1");
     if (h.attention != 0 && h.attention != 1) return fail(GQA_AV_ERR_INVALID_ARG, "hint attention must be 0 or 1");
+    if (h.waves != 0 && h.waves != 4 && h.waves != 8)
+        return fail(GQA_AV_ERR_INVALID_ARG, "hint waves must be 0 (automatic), 4 or 8");
     // Fused attention: the fused softmax product on the bf16 matrix engine, its
     // scores computed from q and K.
     const bool attention = h.attention == 1;
@@ -394,6 +389,16 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
         if (sm && ht > 4) return fail(GQA_AV_ERR_UNSUPPORTED, "the fused softmax takes at most 4 KV heads per tile");
     }
 
+    // Waves per workgroup: four, or eight for the plain product on the bf16
+    // matrix engine (more rows in flight per workgroup without more splits).
+    int nw = gqa_av::kWaves;
+    if (h.waves > 0 && h.waves != nw) {
+        if (!bf16_engine || sm)
+            return fail(GQA_AV_ERR_UNSUPPORTED, "%d waves per workgroup: only the plain product on the bf16 matrix "
+                        "engine takes eight", h.waves);
+        nw = h.waves;
+    }
+
     int VB, GT, nsg;
     int64_t Lc, rps, ndt, rows_per_step, tile_outputs;
     int64_t heads_major;  // tiles along the head axis per KV head
@@ -403,7 +408,7 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
         nsg = static_cast<int>(ceil_div(G, GT));
         heads_major = nsg;
         Lc = ht * D / 8;                // 16-byte pieces of a tile row
-        rps = 32 * gqa_av::kWaves / ht; // one 32-row chunk per wave, kWaves / ht waves per KV head
+        rps = 32 * nw / ht;             // one 32-row chunk per wave, nw / ht waves per KV head
         ndt = 1;
         rows_per_step = rps * GQA_AV_MFMA_BF16_CHUNKS;
         tile_outputs = static_cast<int64_t>(ht) * GT * D;
@@ -508,6 +513,32 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
             nsplit = ceil_div(C, rows_per_split);
         }
     }
+    // Interleaved splits (dense V on the VALU and bf16 matrix engines): split
+    // s takes the pipeline steps s, s + nsplit, ... of the whole sequence, so
+    // the splits of a tile, which run side by side, stream neighbouring rows.
+    // The buffer resources then span the whole sequence: its rows, plus the
+    // pipeline's reloads up to two steps of every split past the end, must
+    // stay under 1 GB for 32-bit offsets.
+    bool interleave = false;
+    if (h.split_order < 0 || h.split_order > 2)
+        return fail(GQA_AV_ERR_INVALID_ARG, "hint split_order must be 0 (automatic), 1 (contiguous) or 2 (interleaved)");
+    if (h.split_order != 1 && C > 0 && nsplit > 1) {
+        const int64_t row_bytes = std::max<int64_t>(Hkv * D * es, Hq * 4);
+        const bool can = !paged && !attention && engine != GQA_AV_ENGINE_MFMA &&
+                         (C + 3 * nsplit * rows_per_step) * row_bytes < (int64_t{1} << 30);
+        if (h.split_order == 2 && !can)
+            return fail(GQA_AV_ERR_UNSUPPORTED, "interleaved splits need dense V on the VALU or bf16 matrix engine "
+                        "(not fused attention) and a sequence under 1 GB of V");
+        // Automatic: interleaved for the plain product (measured on MI355X),
+        // contiguous for the fused softmax and fused attention.
+        interleave = can && (h.split_order == 2 || !sm);
+    }
+    if (interleave) {
+        rows_per_split = rows_per_step;            // one block per step
+        nsplit = std::min(nsplit, ceil_div(C, rows_per_step));
+        interleave = nsplit > 1;
+        if (!interleave) rows_per_split = C;
+    }
     if (nsplit > INT32_MAX) return fail(GQA_AV_ERR_UNSUPPORTED, "too many context splits");
     const int64_t grid = tiles * nsplit;
     if (grid > INT32_MAX) return fail(GQA_AV_ERR_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)grid);
@@ -522,25 +553,14 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
     plan->row_slots = static_cast<int32_t>(rps);
     plan->d_tiles = static_cast<int32_t>(ndt);
     plan->nsplit = static_cast<int32_t>(nsplit);
-    plan->threads = gqa_av::kThreads;
+    plan->threads = 64 * nw;
     plan->rows_per_split = rows_per_split;
+    plan->interleave = interleave ? 1 : 0;
     plan->grid = grid;
-    int combine = GQA_AV_COMBINE_AUTO;
-    if (nsplit > 1) {
-        combine = h.combine;
-        // Measured on MI355X: the second kernel is faster on every decode
-        // workload (the last-workgroup combine pays for device-coherent
-        // stores and loads of the partials), so it is the automatic choice.
-        if (combine == GQA_AV_COMBINE_AUTO) combine = GQA_AV_COMBINE_KERNEL;
-        if ((sm || paged) && combine != GQA_AV_COMBINE_KERNEL)
-            return fail(GQA_AV_ERR_UNSUPPORTED, "the fused softmax combines its splits in a second kernel");
-        // One tile's block is addressed through a 32-bit buffer offset.
-        if (combine == GQA_AV_COMBINE_LAST && nsplit * gqa_av::padded_outputs(static_cast<int>(tile_outputs)) * 4 > INT32_MAX)
-            return fail(GQA_AV_ERR_UNSUPPORTED, "a tile's split partials exceed 2 GB; use the kernel combine");
-    }
-    plan->combine = combine;
+    // Split partials are added by a second kernel.
+    plan->combine = nsplit > 1 ? GQA_AV_COMBINE_KERNEL : GQA_AV_COMBINE_AUTO;
     plan->kv_heads_per_tile = ht;
-    plan->workspace_bytes = workspace_bytes(B, Hq, D, tiles, nsplit, tile_outputs, combine, sm);
+    plan->workspace_bytes = workspace_bytes(B, Hq, D, nsplit, sm);
     plan->v_bytes_read = B * C * Hkv * D * es * heads_major;
     plan->softmax = sm ? 1 : 0;
     plan->page_size = static_cast<int32_t>(P);
@@ -554,7 +574,8 @@ bool same_plan(const gqa_av_plan& a, const gqa_av_plan& b) {
            a.row_slots == b.row_slots && a.d_tiles == b.d_tiles && a.nsplit == b.nsplit &&
            a.threads == b.threads && a.rows_per_split == b.rows_per_split && a.grid == b.grid &&
            a.workspace_bytes == b.workspace_bytes && a.kv_heads_per_tile == b.kv_heads_per_tile &&
-           a.softmax == b.softmax && a.page_size == b.page_size && a.attention == b.attention;
+           a.softmax == b.softmax && a.page_size == b.page_size && a.attention == b.attention &&
+           a.interleave == b.interleave;
 }
 
 }  // namespace
@@ -652,24 +673,33 @@ int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C,
     h.softmax = plan->softmax;
     h.page_size = plan->page_size;
     h.attention = plan->attention;
+    h.waves = plan->threads / 64;
+    h.split_order = plan->interleave ? 2 : 1;
     gqa_av_plan check;
     const int mode = plan->mode;
     // Re-plan with the split count fixed: rows_per_split then follows from C.
     rc = plan_impl(B, C, Hq, Hkv, D, v_dtype, mode, &h, kDefaultCUs, &check);
     if (rc != GQA_AV_OK) return rc;
+    if (plan->interleave && check.rows_per_split != plan->rows_per_split)
+        return fail(GQA_AV_ERR_INVALID_ARG, "an interleaved plan's blocks must be one pipeline step of %lld rows",
+                    (long long)check.rows_per_split);
     check.rows_per_split = plan->rows_per_split;
     check.nsplit = plan->nsplit;
     check.grid = plan->grid;
     check.workspace_bytes = plan->workspace_bytes;
     check.combine = plan->combine;
     if (!same_plan(check, *plan)) return fail(GQA_AV_ERR_INVALID_ARG, "plan does not belong to this problem");
-    if (plan->nsplit > 1 ? (plan->combine != GQA_AV_COMBINE_KERNEL && plan->combine != GQA_AV_COMBINE_LAST)
-                         : plan->combine != GQA_AV_COMBINE_AUTO)
+    if (plan->nsplit > 1 ? plan->combine != GQA_AV_COMBINE_KERNEL : plan->combine != GQA_AV_COMBINE_AUTO)
         return fail(GQA_AV_ERR_INVALID_ARG, "plan combine %d does not fit nsplit %d", plan->combine, plan->nsplit);
-    // The split fields must still tile [0, C) exactly.
+    // The split fields must still tile [0, C) exactly: contiguous splits of
+    // rows_per_split rows, or (interleaved) blocks of one pipeline step, at
+    // least one per split.
     if (C > 0) {
+        if (plan->interleave != 0 && plan->interleave != 1)
+            return fail(GQA_AV_ERR_INVALID_ARG, "plan interleave must be 0 or 1");
         if (plan->nsplit < 1 || plan->rows_per_split < 1 ||
-            ceil_div(C, plan->rows_per_split) != plan->nsplit)
+            (plan->interleave ? plan->nsplit > ceil_div(C, plan->rows_per_split) || plan->nsplit < 2
+                              : ceil_div(C, plan->rows_per_split) != plan->nsplit))
             return fail(GQA_AV_ERR_INVALID_ARG, "plan splits do not cover C=%lld", (long long)C);
     } else if (plan->nsplit != 1) {
         return fail(GQA_AV_ERR_INVALID_ARG, "C == 0 needs nsplit == 1");
@@ -681,11 +711,7 @@ int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C,
     if (plan->grid % plan->nsplit != 0 ||
         tiles_per_split != B * (Hkv / plan->kv_heads_per_tile) * heads_major * plan->d_tiles)
         return fail(GQA_AV_ERR_INVALID_ARG, "plan grid does not match the problem");
-    const int64_t tile_outputs = (plan->engine == GQA_AV_ENGINE_MFMA || plan->engine == GQA_AV_ENGINE_MFMA_BF16)
-        ? static_cast<int64_t>(plan->heads_per_tile) * D * plan->kv_heads_per_tile
-        : static_cast<int64_t>(plan->heads_per_tile) * (plan->vec_bytes / elem_bytes(v_dtype)) * plan->lanes_per_row;
-    if (plan->workspace_bytes !=
-        workspace_bytes(B, Hq, D, tiles_per_split, plan->nsplit, tile_outputs, plan->combine, plan->softmax == 1))
+    if (plan->workspace_bytes != workspace_bytes(B, Hq, D, plan->nsplit, plan->softmax == 1))
         return fail(GQA_AV_ERR_INVALID_ARG, "plan workspace does not match the problem");
 
     if (B == 0) return GQA_AV_OK;
@@ -710,12 +736,8 @@ int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C,
     if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
 
     float* part = nullptr;
-    uint32_t* counters = nullptr;
-    const bool last = plan->nsplit > 1 && plan->combine == GQA_AV_COMBINE_LAST;
     if (plan->nsplit > 1) {
-        const int64_t cbytes = last ? counter_bytes(tiles_per_split) : 0;
-        rc = get_workspace(dev, s, static_cast<size_t>(cbytes), static_cast<size_t>(plan->workspace_bytes - cbytes),
-                           &counters, &part);
+        rc = get_workspace(dev, s, static_cast<size_t>(plan->workspace_bytes), &part);
         if (rc != GQA_AV_OK) return rc;
     }
 
@@ -725,7 +747,6 @@ int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C,
     a.out = out;
     a.part = part;
     a.stats = (softmax && plan->nsplit > 1) ? part + stats_offset(plan->nsplit, B, Hq, D) : nullptr;
-    a.counters = counters;
     a.v_scale = v_scale;
     a.q = at ? at->q : nullptr;
     a.K = at ? static_cast<const uint8_t*>(at->K) : nullptr;
@@ -738,9 +759,9 @@ int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C,
     a.page_shift = 0;
     if (pg)
         while ((int64_t{1} << a.page_shift) < pg->page_size) ++a.page_shift;
-    a.combine = last ? 1 : 0;
     a.C = C;
     a.rows_per_split = plan->rows_per_split;
+    a.interleave = plan->interleave;
     a.B = static_cast<int32_t>(B);
     a.Hq = static_cast<int32_t>(Hq);
     a.Hkv = static_cast<int32_t>(Hkv);
@@ -784,13 +805,20 @@ int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C,
         }
         e = hipGetLastError();
         if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "softmax combine launch: %s", hipGetErrorString(e));
-    } else if ((which & kRunCombine) && plan->nsplit > 1 && !last) {
+    } else if ((which & kRunCombine) && plan->nsplit > 1) {
         const int64_t plane = B * Hq * D;
-        const int64_t per_block = 4 * gqa_av::kQuadsPerBlock;
+        const int groups = gqa_av::combine_groups(a.nsplit);
+        const int64_t per_block = 4 * (gqa_av::kThreads / groups);
         const int64_t blocks = ceil_div(plane, per_block);
         if (blocks > INT32_MAX) return fail(GQA_AV_ERR_UNSUPPORTED, "output too large for the split-C combine");
-        hipLaunchKernelGGL(gqa_av::av_pass2_combine, dim3(static_cast<uint32_t>(blocks)), dim3(gqa_av::kThreads),
-                           0, s, static_cast<const float*>(part), out, plane, a.nsplit);
+        const dim3 grid(static_cast<uint32_t>(blocks)), block(gqa_av::kThreads);
+        const float* const pp = part;
+        switch (groups) {
+        case 8: hipLaunchKernelGGL(gqa_av::av_pass2_combine<8>, grid, block, 0, s, pp, out, plane, a.nsplit); break;
+        case 16: hipLaunchKernelGGL(gqa_av::av_pass2_combine<16>, grid, block, 0, s, pp, out, plane, a.nsplit); break;
+        case 32: hipLaunchKernelGGL(gqa_av::av_pass2_combine<32>, grid, block, 0, s, pp, out, plane, a.nsplit); break;
+        default: hipLaunchKernelGGL(gqa_av::av_pass2_combine<64>, grid, block, 0, s, pp, out, plane, a.nsplit); break;
+        }
         e = hipGetLastError();
         if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "pass-2 launch: %s", hipGetErrorString(e));
     }
@@ -1116,22 +1144,46 @@ const char* gqa_av_status_string(int status) {
 
 const char* gqa_av_last_error(void) { return g_last_error.c_str(); }
 
+int gqa_bench_stream_read(const void* src, int64_t bytes, int32_t workgroups, int32_t loads_in_flight,
+                          uint32_t* sink, void* stream) {
+    if (!src || !sink) return fail(GQA_AV_ERR_INVALID_ARG, "src and sink must not be NULL");
+    if ((reinterpret_cast<uintptr_t>(src) & 15u) || (reinterpret_cast<uintptr_t>(sink) & 3u))
+        return fail(GQA_AV_ERR_INVALID_ARG, "src must be 16-byte and sink 4-byte aligned");
+    if (bytes <= 0 || bytes % 16 != 0) return fail(GQA_AV_ERR_INVALID_ARG, "bytes must be > 0 and a multiple of 16");
+    if (workgroups < 1) return fail(GQA_AV_ERR_INVALID_ARG, "workgroups must be >= 1");
+    if (loads_in_flight != 4 && loads_in_flight != 8 && loads_in_flight != 16)
+        return fail(GQA_AV_ERR_INVALID_ARG, "loads_in_flight must be 4, 8 or 16");
+    const int64_t slice = ceil_div(ceil_div(bytes, workgroups), 16) * 16;
+    if (slice > INT32_MAX) return fail(GQA_AV_ERR_INVALID_ARG, "a slice of %lld bytes exceeds 2^31", (long long)slice);
+    const hipError_t e = gqa_av_launch::stream_read(static_cast<const uint8_t*>(src), bytes, slice, workgroups,
+                                                    loads_in_flight, sink, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "stream read launch: %s", hipGetErrorString(e));
+    return GQA_AV_OK;
+}
+
 int gqa_av_release(void) {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     int prev = 0;
     bool have_prev = hipGetDevice(&prev) == hipSuccess;
     int status = GQA_AV_OK;
-    for (auto& kv : g_ws) {
-        Workspace& ws = kv.second;
-        if (!ws.counters && !ws.part) continue;
-        hipError_t e = hipSetDevice(kv.first.first);
-        if (e == hipSuccess) e = hipDeviceSynchronize();
-        if (e == hipSuccess && ws.counters) e = hipFree(ws.counters);
-        if (e == hipSuccess && ws.part) e = hipFree(ws.part);
+    // Every buffer ever handed out, live or retired, per device.
+    std::vector<std::pair<int, void*>> bufs = g_ws_retired;
+    for (auto& kv : g_ws)
+        if (kv.second.part) bufs.emplace_back(kv.first.first, kv.second.part);
+    std::sort(bufs.begin(), bufs.end());
+    int synced = -1;
+    for (auto& db : bufs) {
+        hipError_t e = hipSuccess;
+        if (db.first != synced) {
+            e = hipSetDevice(db.first);
+            if (e == hipSuccess) e = hipDeviceSynchronize();
+            synced = db.first;
+        }
+        if (e == hipSuccess) e = hipFree(db.second);
         if (e != hipSuccess) status = fail(GQA_AV_ERR_HIP, "release: %s", hipGetErrorString(e));
-        ws = Workspace();
     }
     g_ws.clear();
+    g_ws_retired.clear();
     if (have_prev) (void)hipSetDevice(prev);
     return status;
 }

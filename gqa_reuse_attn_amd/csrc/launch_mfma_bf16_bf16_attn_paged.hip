@@ -1,5 +1,5 @@
 // bf16 matrix engine kernels, fused decode attention over a paged bf16 K and V cache.
 #include "mfma_bf16_launch.hpp"
 
-template hipError_t gqa_av_launch::mfma_bf16<gqa_av::kBF16, true, true, true>(int64_t, int, int,
+template hipError_t gqa_av_launch::mfma_bf16<gqa_av::kBF16, true, true, true>(int64_t, int, int, int,
                                                                             const gqa_av::Pass1Args&, hipStream_t);

@@ -7,29 +7,44 @@
 namespace gqa_av_launch {
 namespace detail {
 
-template <int VDT, int PR, int NSET, int HT, bool SM, bool PG, bool QK>
+template <int VDT, int PR, int NSET, int HT, bool SM, bool PG, bool QK, int NW>
 hipError_t launch_mfma_bf16(const gqa_av::Pass1Args& a, hipStream_t s) {
-    hipLaunchKernelGGL((gqa_av::av_pass1_mfma_bf16<PR, NSET, GQA_AV_MFMA_BF16_CHUNKS, HT, SM, VDT, PG, QK>),
-                       dim3(a.nblocks), dim3(gqa_av::kThreads), 0, s, a);
+    hipLaunchKernelGGL((gqa_av::av_pass1_mfma_bf16<PR, NSET, GQA_AV_MFMA_BF16_CHUNKS, HT, SM, VDT, PG, QK, NW>),
+                       dim3(a.nblocks), dim3(64 * NW), 0, s, a);
     return hipGetLastError();
 }
 
+// Eight waves per workgroup only for the plain product (the fused softmax and
+// fused attention keep four).
+template <int VDT, int PR, int NSET, int HT, bool SM, bool PG, bool QK>
+hipError_t launch_mfma_bf16_nw(int nw, const gqa_av::Pass1Args& a, hipStream_t s) {
+    if (nw == 4) return launch_mfma_bf16<VDT, PR, NSET, HT, SM, PG, QK, 4>(a, s);
+    if constexpr (!SM && !QK) {
+        if (nw == 8) return launch_mfma_bf16<VDT, PR, NSET, HT, SM, PG, QK, 8>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
 template <int VDT, int PR, int NSET, bool SM, bool PG, bool QK>
-hipError_t launch_mfma_bf16_ht(int ht, const gqa_av::Pass1Args& a, hipStream_t s) {
+hipError_t launch_mfma_bf16_ht(int ht, int nw, const gqa_av::Pass1Args& a, hipStream_t s) {
     switch (ht) {
-    case 1: return launch_mfma_bf16<VDT, PR, NSET, 1, SM, PG, QK>(a, s);
-    case 2: return launch_mfma_bf16<VDT, PR, NSET, 2, SM, PG, QK>(a, s);
-    case 4: return launch_mfma_bf16<VDT, PR, NSET, 4, SM, PG, QK>(a, s);
+    case 1: return launch_mfma_bf16_nw<VDT, PR, NSET, 1, SM, PG, QK>(nw, a, s);
+    case 2: return launch_mfma_bf16_nw<VDT, PR, NSET, 2, SM, PG, QK>(nw, a, s);
+    case 4: return launch_mfma_bf16_nw<VDT, PR, NSET, 4, SM, PG, QK>(nw, a, s);
     default: return hipErrorInvalidValue;
     }
 }
 
 template <int VDT, bool SM, bool PG, bool QK>
-hipError_t mfma_bf16_pr(int64_t D, int nset, int ht, const gqa_av::Pass1Args& a, hipStream_t s) {
+hipError_t mfma_bf16_pr(int64_t D, int nset, int ht, int nw, const gqa_av::Pass1Args& a, hipStream_t s) {
     switch (D) {
-    case 64: return nset == 1 ? launch_mfma_bf16_ht<VDT, 8, 1, SM, PG, QK>(ht, a, s) : launch_mfma_bf16_ht<VDT, 8, 2, SM, PG, QK>(ht, a, s);
-    case 128: return nset == 1 ? launch_mfma_bf16_ht<VDT, 16, 1, SM, PG, QK>(ht, a, s) : launch_mfma_bf16_ht<VDT, 16, 2, SM, PG, QK>(ht, a, s);
-    case 256: return nset == 1 ? launch_mfma_bf16_ht<VDT, 32, 1, SM, PG, QK>(ht, a, s) : hipErrorInvalidValue;
+    case 64:
+        return nset == 1 ? launch_mfma_bf16_ht<VDT, 8, 1, SM, PG, QK>(ht, nw, a, s)
+                         : launch_mfma_bf16_ht<VDT, 8, 2, SM, PG, QK>(ht, nw, a, s);
+    case 128:
+        return nset == 1 ? launch_mfma_bf16_ht<VDT, 16, 1, SM, PG, QK>(ht, nw, a, s)
+                         : launch_mfma_bf16_ht<VDT, 16, 2, SM, PG, QK>(ht, nw, a, s);
+    case 256: return nset == 1 ? launch_mfma_bf16_ht<VDT, 32, 1, SM, PG, QK>(ht, nw, a, s) : hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
     }
 }
@@ -37,8 +52,8 @@ hipError_t mfma_bf16_pr(int64_t D, int nset, int ht, const gqa_av::Pass1Args& a,
 }  // namespace detail
 
 template <int VDT, bool SM, bool PG, bool QK>
-hipError_t mfma_bf16(int64_t D, int nset, int ht, const gqa_av::Pass1Args& a, hipStream_t s) {
-    return detail::mfma_bf16_pr<VDT, SM, PG, QK>(D, nset, ht, a, s);
+hipError_t mfma_bf16(int64_t D, int nset, int ht, int nw, const gqa_av::Pass1Args& a, hipStream_t s) {
+    return detail::mfma_bf16_pr<VDT, SM, PG, QK>(D, nset, ht, nw, a, s);
 }
 
 }  // namespace gqa_av_launch

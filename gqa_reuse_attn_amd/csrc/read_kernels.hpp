@@ -1,0 +1,55 @@
+// A plain streaming read: the bandwidth ceiling the AV kernels are compared
+// against on the same device. Nothing of the product is computed here; the
+// kernel reads every byte of a buffer once, the way the AV kernels read V
+// (16-byte non-temporal buffer loads, each workgroup a contiguous slice, two
+// batches of loads in flight), and folds the words into one value so the
+// loads stay live.
+#pragma once
+
+#include "av_kernels.hpp"
+
+namespace gqa_av {
+
+// Workgroup i reads bytes [i * slice, min((i + 1) * slice, bytes)) of src
+// (slice a multiple of 16 below 2^31). U 16-byte loads per lane and batch.
+// The buffer resource ends with the workgroup's slice, so a batch that runs
+// past it reads zeros and touches no memory.
+template <int U>
+__global__ __launch_bounds__(kThreads) void stream_read(const uint8_t* src, int64_t bytes, int64_t slice,
+                                                        uint32_t* sink) {
+    const int64_t start = static_cast<int64_t>(blockIdx.x) * slice;
+    if (start >= bytes) return;
+    const int n = static_cast<int>(min(slice, bytes - start));
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(src) + start, 0, n, kRawBufferFlags);
+    constexpr int kBatch = kThreads * 16 * U;   // bytes of one batch of the workgroup
+    const int nb = (n + kBatch - 1) / kBatch;
+    const int lane_off = static_cast<int>(threadIdx.x) * 16;
+    u32x4 a[U], b[U];
+    uint32_t x = 0;
+    auto load = [&](u32x4* v, int batch) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane_off + u * kThreads * 16, batch * kBatch,
+                                                         kCachePolicyNt);
+    };
+    auto fold = [&](const u32x4* v) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    };
+    // Two batches in flight; the reload of `a` is unconditional (past the
+    // slice it reads zeros).
+    int i = 0;
+    if (nb > 0) load(a, 0);
+    for (; i + 1 < nb; i += 2) {
+        load(b, i + 1);
+        fold(a);
+        load(a, i + 2);
+        fold(b);
+    }
+    if (i < nb) fold(a);
+    // A write that in practice never happens keeps the reads from being dropped.
+    if (x == 0x9e3779b9u) sink[blockIdx.x & 255] = x;
+}
+
+}  // namespace gqa_av

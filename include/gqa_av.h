@@ -44,15 +44,20 @@
  * for the calling thread's last failing call.
  *
  * Workspace: when a plan splits the context (nsplit > 1) the library needs
- * nsplit blocks of partial sums and, for GQA_AV_COMBINE_LAST, one uint32
- * counter per tile, or, for a fused softmax plan (gqa_softmax_av.h), nsplit
- * planes of partial sums and nsplit * B * Hq pairs of floats of per-split
- * statistics (plan->workspace_bytes in total). It allocates them itself
- * (hipMalloc) per (device, stream) in two buffers, keeps them for reuse, grows
- * them on demand (synchronising that stream first) and frees them in
- * gqa_av_release(). The counters are zeroed when allocated and every call
- * leaves them at zero. Calls on different streams never share a workspace;
- * calls on one stream are ordered by the stream.
+ * nsplit planes of partial sums, plus, for a fused softmax plan
+ * (gqa_softmax_av.h), nsplit * B * Hq pairs of floats of per-split statistics
+ * (plan->workspace_bytes in total). It allocates that itself (hipMalloc) per
+ * (device, stream), keeps it for reuse, and grows it on demand: the larger
+ * buffer replaces the old one, which is kept (not freed) until
+ * gqa_av_release(), so a HIP graph captured from an earlier call on the
+ * stream stays valid. Growth allocates and is therefore refused while the
+ * stream is being captured (GQA_AV_ERR_UNSUPPORTED, nothing launched): make
+ * one call with the largest plan on the stream before capturing. Calls on
+ * different streams never share a workspace; calls on one stream are ordered
+ * by the stream. A captured graph uses the workspace of the stream it was
+ * captured from, wherever it is replayed: do not replay it concurrently with
+ * calls on that stream or with other replays of graphs captured from it. No
+ * call clears memory with a memset.
  *
  * Thread safety: all entry points may be called from several host threads.
  */
@@ -101,12 +106,12 @@ typedef enum gqa_av_engine {
                                     product is exact and the sums are fp32 as in the others */
 } gqa_av_engine;
 
-/* How the partial sums of a split context are added (both in increasing
- * split order, so results are reproducible bit for bit). */
+/* How the partial sums of a split context are added: a second kernel over
+ * per-split planes, in a fixed order, so results are reproducible bit for bit.
+ * (A plan without splits records AUTO.) */
 typedef enum gqa_av_combine {
     GQA_AV_COMBINE_AUTO = 0,
-    GQA_AV_COMBINE_KERNEL = 1,   /* a second kernel over per-split planes */
-    GQA_AV_COMBINE_LAST = 2      /* in pass 1: the last workgroup of each tile adds them */
+    GQA_AV_COMBINE_KERNEL = 1    /* a second kernel over per-split planes */
 } gqa_av_combine;
 
 /* Optional planning hints. Zero-initialise, then set what you want to force:
@@ -116,12 +121,17 @@ typedef struct gqa_av_hint {
     int32_t nsplit;     /* number of context splits */
     int32_t cu_count;   /* compute units to plan for; auto = the device's (decode) or 256 (make_plan) */
     int32_t v_align;    /* byte alignment of V's base address; auto = 16 */
-    int32_t combine;    /* gqa_av_combine for context splits */
+    int32_t combine;    /* gqa_av_combine for context splits (AUTO or KERNEL; others are INVALID_ARG) */
     int32_t kv_tile;    /* adjacent KV heads per VALU workgroup (their D-rows are contiguous) */
     int32_t softmax;    /* 1: plan the fused softmax product of gqa_softmax_av.h; 0: this header's product */
     int32_t page_size;  /* > 0: plan for a paged V cache of this many rows per page (gqa_paged_av.h) */
     int32_t attention;  /* 1: plan the fused decode attention of gqa_attention.h (implies softmax = 1) */
-    int32_t reserved[1];
+    int32_t waves;      /* waves (of 64 threads) per workgroup: 4, or 8 for the plain product on the bf16
+                           matrix engine; other values are INVALID_ARG */
+    int32_t split_order;/* how a split context is cut: 0 automatic, 1 contiguous ranges, 2 interleaved
+                           blocks (dense V on the VALU or bf16 matrix engine, not fused attention;
+                           UNSUPPORTED elsewhere) */
+    int32_t reserved[2];
 } gqa_av_hint;
 
 /* A launch plan: what gqa_av_decode_plan will run. Produced by gqa_av_make_plan. */
@@ -135,12 +145,13 @@ typedef struct gqa_av_plan {
     int32_t row_slots;       /* rows a workgroup loads side by side (MFMA_BF16: four waves x 32) */
     int32_t d_tiles;         /* workgroups along D */
     int32_t nsplit;          /* context splits (1 = no partial sums) */
-    int32_t threads;         /* threads per workgroup */
-    int64_t rows_per_split;  /* context rows per split (last split may be shorter) */
+    int32_t threads;         /* threads per workgroup (256, or 512 on the bf16 matrix engine) */
+    int64_t rows_per_split;  /* contiguous splits: context rows per split (the last may be shorter);
+                                interleaved: rows of one block (see interleave) */
     int64_t grid;            /* workgroups launched by the first kernel */
     int64_t workspace_bytes; /* device workspace the plan needs (0 if nsplit == 1) */
     int64_t v_bytes_read;    /* V bytes the plan reads from memory (G x more for per-head) */
-    int32_t combine;         /* resolved gqa_av_combine: KERNEL or LAST when nsplit > 1, else AUTO */
+    int32_t combine;         /* resolved gqa_av_combine: KERNEL when nsplit > 1, else AUTO */
     int32_t kv_heads_per_tile; /* adjacent KV heads one workgroup streams (VALU reuse; else 1) */
     int32_t softmax;         /* 1: a plan of the fused softmax product (gqa_softmax_av.h), which only
                                 gqa_softmax_av_decode_plan runs; 0: a plan of this header's product */
@@ -148,7 +159,9 @@ typedef struct gqa_av_plan {
                                 page, which only gqa_av_paged_decode_plan runs; 0: dense V */
     int32_t attention;       /* 1: a plan of the fused decode attention (gqa_attention.h), which only
                                 gqa_attention_decode_plan runs */
-    int32_t reserved[1];
+    int32_t interleave;      /* 1: split s takes the blocks s, s + nsplit, s + 2 nsplit, ... of
+                                rows_per_split rows of the sequence (every split at least one);
+                                0: split s takes rows [s rows_per_split, (s + 1) rows_per_split) */
 } gqa_av_plan;
 
 /* Resolve `mode` for a head shape. Host-only: needs no GPU.
@@ -181,8 +194,8 @@ int gqa_av_decode_plan(const float *attn, const void *V, float *out,
 
 /* The two launches of gqa_av_decode_plan, for callers that schedule or time
  * them separately (same arguments and checks). gqa_av_decode_pass1 streams V
- * and writes `out` directly when plan->nsplit == 1 or the combine is
- * GQA_AV_COMBINE_LAST; otherwise it leaves the split partials in the
+ * and writes `out` directly when plan->nsplit == 1; otherwise it leaves the
+ * split partials in the
  * workspace of (current device, stream), and gqa_av_decode_combine, enqueued
  * next on the same stream, adds them into `out` (a no-op for the other
  * cases). Calling both in this order on one stream is exactly
@@ -200,8 +213,11 @@ const char *gqa_av_status_string(int status);
 /* Detail of the calling thread's last failing call ("" if none). */
 const char *gqa_av_last_error(void);
 
-/* Free every cached workspace, after synchronising the devices that hold one.
- * Returns a gqa_av_status. Safe to call at any time; later calls allocate again. */
+/* Free every workspace buffer the library has allocated (live and retired),
+ * after synchronising the devices that hold one. Returns a gqa_av_status.
+ * Later calls allocate again. A HIP graph captured from a split call refers
+ * to its stream's workspace: release invalidates every such graph, so call
+ * it only when no captured graph will be replayed again. */
 int gqa_av_release(void);
 
 #ifdef __cplusplus

@@ -38,7 +38,7 @@
  * plan for this call comes from gqa_av_make_plan with hint->softmax = 1 and
  * carries plan->softmax = 1: its engine is GQA_AV_ENGINE_VALU or
  * GQA_AV_ENGINE_MFMA_BF16 (forcing GQA_AV_ENGINE_MFMA is UNSUPPORTED), its
- * combine GQA_AV_COMBINE_KERNEL (forcing LAST is UNSUPPORTED), at most 4 KV
+ * combine GQA_AV_COMBINE_KERNEL, at most 4 KV
  * heads per tile. gqa_av_decode_plan and its split entry points refuse such a
  * plan (INVALID_ARG), and this call refuses the others.
  */

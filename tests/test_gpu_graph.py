@@ -87,12 +87,12 @@ def _fresh(x, seed):
     ((2, 3000, 16, 8, 128, "bf16"), "auto", "auto"),     # VALU, split kernel combine
     ((2, 3000, 64, 8, 128, "bf16"), "auto", "auto"),     # bf16 matrix engine
     ((2, 3000, 32, 4, 64, "f32"), "mfma", "auto"),       # fp32 matrix engine (plain only)
-    ((2, 3000, 16, 8, 128, "f16"), "valu", "last"),      # last-workgroup combine (plain only)
+    ((2, 3000, 24, 8, 96, "f16"), "valu", "kernel"),     # f16 VALU, G = 3, split kernel combine
     ((1, 100, 8, 2, 64, "bf16"), "auto", "auto"),        # one split: a single launch
 ])
 def test_graph_dense(shape, engine, combine, softmax):
-    if softmax and (engine == "mfma" or combine == "last"):
-        pytest.skip("the fused softmax runs on the VALU or bf16 matrix engine with the kernel combine")
+    if softmax and engine == "mfma":
+        pytest.skip("the fused softmax runs on the VALU or bf16 matrix engine")
     B, C, Hq, Hkv, D, dt = shape
     x, V = _weights(B, C, Hq, Hkv, D, dt, seed=C + Hq, softmax=softmax)
     plan = ga.make_plan(B, C, Hq, Hkv, D, dt, engine=engine, combine=combine, softmax=softmax)
@@ -154,3 +154,65 @@ def test_graph_attention_paged(fp8):
     _graph_matches_eager(f"attention paged fp8={fp8}",
                          lambda s: ga.BoundAttentionPaged(q, kp, vp, bt, lens, scale=0.125, C=C, stream=s,
                                                           k_scale=ks, v_scale=vs), q, _fresh(q, 11))
+
+
+def test_first_split_call_under_capture_is_refused():
+    """A split call whose stream has no workspace yet would have to allocate
+    inside the capture: it is refused with UNSUPPORTED, nothing is enqueued,
+    and the same call made eagerly afterwards succeeds."""
+    B, C, Hq, Hkv, D = 2, 3000, 16, 8, 128
+    x, V = _weights(B, C, Hq, Hkv, D, "bf16", seed=17, softmax=False)
+    plan = ga.make_plan(B, C, Hq, Hkv, D, "bf16", nsplit=6)
+    assert plan.nsplit == 6 and plan.workspace_bytes > 0
+    s = torch.cuda.Stream()
+    call = ga.bind(x, V, plan=plan, stream=s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        with pytest.raises(ga.GqaAvError) as e:
+            call()
+    assert e.value.name == "UNSUPPORTED" and "capture" in str(e.value)
+    torch.cuda.synchronize()
+    call()                                           # eagerly: allocates, then runs
+    s.synchronize()
+    assert torch.isfinite(call.out).all()
+    del g
+
+
+def test_graph_survives_workspace_growth():
+    """A graph captured with a small split plan keeps its workspace address:
+    a later, larger plan on the same stream grows the workspace (the old buffer
+    is retired, not freed), and replaying the first graph still equals an
+    eager call of its plan bit for bit."""
+    s = torch.cuda.Stream()
+    xs, Vs = _weights(1, 2000, 16, 8, 128, "bf16", seed=21, softmax=False)
+    small = ga.bind(xs, Vs, plan=ga.make_plan(1, 2000, 16, 8, 128, "bf16", nsplit=4), stream=s)
+    small()
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        small()
+    torch.cuda.synchronize()
+    xl, Vl = _weights(4, 6000, 64, 8, 128, "bf16", seed=22, softmax=False)
+    large = ga.bind(xl, Vl, plan=ga.make_plan(4, 6000, 64, 8, 128, "bf16", nsplit=24), stream=s)
+    assert large.plan.workspace_bytes > 4 * small.plan.workspace_bytes
+    large()                                          # grows the stream's workspace
+    s.synchronize()
+    want_large = large.out.clone()
+    fresh = _fresh(xs, 3)
+    prev = None
+    for k in range(REPLAYS):
+        xs.copy_(fresh(k))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = small.out.clone()
+        small()
+        s.synchronize()
+        assert torch.equal(got, small.out), f"replay {k} after growth differs from the eager call"
+        if prev is not None:
+            assert not torch.equal(got, prev)
+        prev = got
+        large()                                      # interleave the large plan's eager calls
+        s.synchronize()
+        assert torch.equal(large.out, want_large)
+    del g

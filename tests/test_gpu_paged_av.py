@@ -184,8 +184,9 @@ def test_paged_dense_layout_matches_dense_call(dt, engine):
     for softmax, x in ((False, attn), (True, s)):
         pp = ga.make_plan(B, C, Hq, Hkv, D, dt, "reuse", engine=engine, page_size=P, softmax=softmax, nsplit=4,
                           kv_tile=2)
-        dp = ga.make_plan(B, C, Hq, Hkv, D, dt, "reuse", engine=engine, softmax=softmax, nsplit=4, kv_tile=2)
-        assert pp.engine == dp.engine and pp.rows_per_split == dp.rows_per_split
+        dp = ga.make_plan(B, C, Hq, Hkv, D, dt, "reuse", engine=engine, softmax=softmax, nsplit=4, kv_tile=2,
+                          split_order="contiguous")
+        assert pp.engine == dp.engine and pp.rows_per_split == dp.rows_per_split and pp.interleave == dp.interleave
         a = _run(x, pages, bt, lens, softmax, plan=pp)
         fn = ga.gqa_softmax_av_decode if softmax else ga.gqa_av_decode
         b = fn(x.to(DEV), V.to(DEV), plan=dp).cpu().numpy().astype(np.float64)

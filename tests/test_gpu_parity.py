@@ -80,7 +80,7 @@ def _sweep_cases():
 
 def _plans(B, C, Hq, Hkv, D, dt, ns):
     """The automatic plan, per-head, each reuse engine that can take the shape,
-    and both ways of adding split partials."""
+    and both ways of cutting a split context (interleaved blocks, contiguous)."""
     plans = [("auto", ga.make_plan(B, C, Hq, Hkv, D, dt, "auto", nsplit=ns))]
     if Hq // Hkv >= 2:
         plans.append(("per_head", ga.make_plan(B, C, Hq, Hkv, D, dt, "per_head", nsplit=ns)))
@@ -98,15 +98,14 @@ def _plans(B, C, Hq, Hkv, D, dt, ns):
                                                                           nsplit=ns, kv_tile=ht)))
                     except ga.GqaAvError as e:
                         assert e.name == "UNSUPPORTED"
+    # the other way of cutting a split context: contiguous ranges (the
+    # automatic plans interleave blocks of one step)
     for name, p in list(plans):
-        if p.nsplit > 1:
-            other = "last" if p.combine == 1 else "kernel"
-            mode = "per_head" if p.mode == 0 else ("reuse" if name != "auto" else "auto")
+        if p.nsplit > 1 and p.interleave:
+            mode = "per_head" if p.mode == 0 else "reuse"
             eng = {1: "valu", 2: "mfma", 3: "mfma_bf16"}[p.engine]
-            if name.startswith("kv_tile"):
-                mode = "reuse"
-            plans.append((f"{name}/{other}", ga.make_plan(B, C, Hq, Hkv, D, dt, mode, engine=eng, nsplit=ns,
-                                                          combine=other, kv_tile=p.kv_heads_per_tile)))
+            plans.append((f"{name}/contiguous", ga.make_plan(B, C, Hq, Hkv, D, dt, mode, engine=eng, nsplit=ns,
+                                                             kv_tile=p.kv_heads_per_tile, split_order="contiguous")))
     return plans
 
 
@@ -126,20 +125,22 @@ def test_sweep_small(B, C, Hq, Hkv, D, dt, ns, oracle_lib):
 
 
 @pytest.mark.parametrize("wname", list(WORKLOADS))
-def test_workload_other_combine(wname, oracle_lib):
-    """Full-size workloads with split partials added the other way than the automatic plan."""
+def test_workload_contiguous_splits(wname, oracle_lib):
+    """Full-size workloads with the split context cut into contiguous ranges
+    (the automatic plan interleaves blocks of one pipeline step)."""
     w = WORKLOADS[wname]
     cu = torch.cuda.get_device_properties(0).multi_processor_count
     auto = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, cu_count=cu)
     if auto.nsplit == 1:
         pytest.skip("automatic plan does not split the context")
-    other = "last" if auto.combine == 1 else "kernel"
-    _say(f"[parity] {wname} combine={other}")
+    assert auto.interleave == 1
+    _say(f"[parity] {wname} contiguous splits")
     attn, V = make_inputs(w, seed=0)
     ref = oracle_lib.full(attn, V, w.v_dtype)
-    plan = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, cu_count=cu, combine=other)
+    plan = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, cu_count=cu, split_order="contiguous")
+    assert plan.interleave == 0 and plan.nsplit == auto.nsplit
     out = _run(attn, V, plan=plan)
-    assert_parity(out, ref, w.v_dtype, w.C, f"{wname}/{other} plan={plan.as_dict()}")
+    assert_parity(out, ref, w.v_dtype, w.C, f"{wname}/contiguous plan={plan.as_dict()}")
 
 
 @pytest.mark.parametrize("wname,engine", [
@@ -179,15 +180,15 @@ def test_one_hot_is_exact(dt):
             sel[b, q] = c
     Vd = V.to(torch.float32).numpy()
     for mode, ns, eng, comb in (("auto", 0, "auto", "auto"), ("auto", 5, "auto", "kernel"),
-                                ("auto", 5, "auto", "last"), ("per_head", 3, "auto", "last"),
-                                ("auto", 1, "auto", "auto"), ("reuse", 0, "mfma", "kernel"),
-                                ("reuse", 4, "mfma", "last"), ("reuse", 1, "mfma", "auto")):
+                                ("per_head", 3, "auto", "kernel"), ("auto", 1, "auto", "auto"),
+                                ("reuse", 0, "mfma", "kernel"), ("reuse", 4, "mfma", "kernel"),
+                                ("reuse", 1, "mfma", "auto")):
         plan = ga.make_plan(B, C, Hq, Hkv, D, dt, mode, nsplit=ns, engine=eng, combine=comb)
         out = _run(attn, V, plan=plan).astype(np.float32)
         for (b, q), c in sel.items():
             assert np.array_equal(out[b, q], Vd[b, c, q // G]), (mode, ns, b, q)
     if dt == "bf16":
-        for ns, comb in ((0, "kernel"), (4, "last"), (1, "auto")):
+        for ns, comb in ((0, "kernel"), (4, "kernel"), (1, "auto")):
             plan = ga.make_plan(B, C, Hq, Hkv, D, dt, "reuse", nsplit=ns, engine="mfma_bf16", combine=comb)
             out = _run(attn, V, plan=plan).astype(np.float32)
             for (b, q), c in sel.items():
@@ -217,7 +218,7 @@ def test_bf16_engine_splits_weights_exactly():
     pw = torch.pow(2.0, torch.randint(-20, 20, (B, C, Hkv, D), generator=gen).float())
     V.copy_(pw.to(torch.bfloat16))
     Vd = V.to(torch.float64).numpy()
-    for ns, comb, ht in ((1, "auto", 1), (3, "kernel", 1), (5, "last", 1), (1, "auto", 2), (4, "last", 2)):
+    for ns, comb, ht in ((1, "auto", 1), (3, "kernel", 1), (5, "kernel", 1), (1, "auto", 2), (4, "kernel", 2)):
         plan = ga.make_plan(B, C, Hq, Hkv, D, "bf16", "reuse", nsplit=ns, engine="mfma_bf16", combine=comb,
                             kv_tile=ht)
         out = _run(attn, V, plan=plan)
@@ -226,19 +227,14 @@ def test_bf16_engine_splits_weights_exactly():
             assert np.array_equal(out[b, q].astype(np.float32), want), (ns, b, q, w[b, q].item())
 
 
-@pytest.mark.parametrize("combine", ["kernel", "last"])
-def test_deterministic_run_to_run(combine):
+def test_deterministic_run_to_run():
     w = WORKLOADS["mqa16-b4-c32768-hq16-hkv1-d128-bf16"]
     attn, V = make_inputs(w, seed=1)
     a, v = attn.to(DEV), V.to(DEV)
-    plan = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, combine=combine, nsplit=64)
+    plan = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, nsplit=64)
     outs = [ga.gqa_av_decode(a, v, plan=plan).cpu() for _ in range(3)]
     torch.cuda.synchronize()
     assert all(torch.equal(outs[0], o) for o in outs[1:])
-    # both ways of adding the splits use the same order: identical bits
-    other = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, combine="last" if combine == "kernel" else "kernel",
-                         nsplit=64)
-    assert torch.equal(outs[0], ga.gqa_av_decode(a, v, plan=other).cpu())
 
 
 def test_zero_context_writes_zeros():
@@ -323,8 +319,8 @@ def test_bf16_rounded_weights_would_fail_accumulation_bound(oracle_lib):
 
 
 def test_workspace_reuse_across_plans(oracle_lib):
-    """Plans with different tile counts share one cached workspace: each must find
-    its split counters at zero, whatever partial sums the previous plans wrote."""
+    """Plans of different layouts share one cached workspace: each must add only
+    its own split partials, whatever the previous plans wrote there."""
     shapes = [(4, 3000, 64, 8, 128, "bf16", "auto"),     # large workspace first
               (1, 3000, 8, 2, 128, "bf16", "per_head"),  # few tiles, many partials
               (2, 3000, 24, 8, 96, "f16", "per_head"),   # more tiles than the previous call
@@ -336,8 +332,8 @@ def test_workspace_reuse_across_plans(oracle_lib):
         cases.append((attn, V, dt, C, mode, oracle_lib.full(attn, V, dt)))
     for rnd in range(4):
         for attn, V, dt, C, mode, ref in cases:
-            plan = ga.make_plan(*attn.shape[:2], attn.shape[2], V.shape[2], V.shape[3], dt, mode, nsplit=9,
-                                combine="last" if rnd % 2 == 0 else "kernel")
+            plan = ga.make_plan(*attn.shape[:2], attn.shape[2], V.shape[2], V.shape[3], dt, mode,
+                                nsplit=9 if rnd % 2 == 0 else 4)
             out = _run(attn, V, plan=plan)
             assert_parity(out, ref, dt, C, f"round {rnd} {tuple(V.shape)} {mode} plan={plan.as_dict()}")
 
@@ -356,17 +352,17 @@ def test_bound_call_matches_decode(oracle_lib):
 
 
 @pytest.mark.parametrize("G", [5, 6, 7])
-@pytest.mark.parametrize("combine", ["kernel", "last"])
-def test_valu_groups_of_5_to_7(G, combine, oracle_lib):
+@pytest.mark.parametrize("ns", [1, 6])
+def test_valu_groups_of_5_to_7(G, ns, oracle_lib):
     """VALU tiles of 5-7 heads with 8 elements per lane: 40-56 accumulators, a
     number that is not a multiple of the 32-slot reduction chunk."""
     B, C, Hkv, D = 2, 700, 2, 256
     attn, V = make_random(B, C, G * Hkv, Hkv, D, "bf16", seed=G)
     ref = oracle_lib.full(attn, V, "bf16")
-    plan = ga.make_plan(B, C, G * Hkv, Hkv, D, "bf16", "reuse", engine="valu", nsplit=6, combine=combine)
+    plan = ga.make_plan(B, C, G * Hkv, Hkv, D, "bf16", "reuse", engine="valu", nsplit=ns)
     assert plan.heads_per_tile == G
     out = _run(attn, V, plan=plan)
-    assert_parity(out, ref, "bf16", C, f"G={G} {combine}")
+    assert_parity(out, ref, "bf16", C, f"G={G} nsplit={ns}")
 
 
 @pytest.mark.parametrize("wname", ["g2-b4-c32768-hq16-hkv8-d128-bf16", "mqa16-b4-c32768-hq16-hkv1-d128-bf16",
@@ -405,16 +401,35 @@ def test_workload_kv_tiles(wname, ht, engine, oracle_lib):
 
 @pytest.mark.parametrize("B,C,G,Hkv,D", [(2, 1000, 8, 4, 128), (1, 777, 16, 8, 64), (3, 301, 5, 4, 256),
                                          (2, 515, 32, 4, 128), (1, 64, 12, 8, 128)])
-def test_bf16_engine_kv_tiles_small(B, C, G, Hkv, D, oracle_lib):
-    """bf16 matrix engine with 1, 2 and 4 KV heads per workgroup, ragged splits,
-    both combines; 32-head sets at G = 32."""
+@pytest.mark.parametrize("waves", [4, 8])
+def test_bf16_engine_kv_tiles_small(B, C, G, Hkv, D, waves, oracle_lib):
+    """bf16 matrix engine with 1, 2 and 4 KV heads per workgroup, four or eight
+    waves per workgroup, ragged splits, one and several splits; 32-head sets
+    at G = 32."""
     Hq = G * Hkv
     attn, V = make_random(B, C, Hq, Hkv, D, "bf16", seed=C + G, attn_kind="softmax")
     ref = oracle_lib.full(attn, V, "bf16")
     for ht in (1, 2, 4):
-        for ns, comb in ((1, "auto"), (3, "kernel"), (7, "last")):
+        for ns, comb in ((1, "auto"), (3, "kernel"), (7, "kernel")):
             plan = ga.make_plan(B, C, Hq, Hkv, D, "bf16", "reuse", engine="mfma_bf16", kv_tile=ht, nsplit=ns,
-                                combine=comb)
-            assert plan.kv_heads_per_tile == ht
+                                combine=comb, waves=waves)
+            assert plan.kv_heads_per_tile == ht and plan.threads == 64 * waves
             out = _run(attn, V, plan=plan)
-            assert_parity(out, ref, "bf16", C, f"{(B, C, G, Hkv, D)} kv_tile={ht} ns={ns} {comb}")
+            assert_parity(out, ref, "bf16", C, f"{(B, C, G, Hkv, D)} kv_tile={ht} ns={ns} waves={waves}")
+
+
+@pytest.mark.parametrize("wname,ht,ns", [
+    ("mqa16-b4-c32768-hq16-hkv1-d128-bf16", 1, 0), ("mqa16-b4-c32768-hq16-hkv1-d128-bf16", 1, 32),
+    ("batch64-b64-c8192-hq64-hkv8-d128-bf16", 2, 1), ("batch64-b64-c8192-hq64-hkv8-d128-bf16", 4, 2),
+])
+def test_workload_eight_waves(wname, ht, ns, oracle_lib):
+    """Full-size workloads on the bf16 matrix engine with eight waves per workgroup."""
+    w = WORKLOADS[wname]
+    _say(f"[parity] {wname} waves=8 kv_tile={ht} nsplit={ns}")
+    attn, V = make_inputs(w, seed=0)
+    ref = oracle_lib.full(attn, V, w.v_dtype)
+    plan = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, "reuse", engine="mfma_bf16", kv_tile=ht, nsplit=ns,
+                        waves=8, cu_count=torch.cuda.get_device_properties(0).multi_processor_count)
+    assert plan.threads == 512
+    out = _run(attn, V, plan=plan)
+    assert_parity(out, ref, w.v_dtype, w.C, f"{wname} waves=8 plan={plan.as_dict()}")

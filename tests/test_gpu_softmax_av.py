@@ -131,6 +131,10 @@ def test_softmax_sweep(B, C, Hq, Hkv, D, dt, std, oracle_lib):
     for mode in modes:
         for ns in (0, 1, 2, 7, 12):                 # 12: the grouped combine (more than 8 splits)
             plans.append(ga.make_plan(B, C, Hq, Hkv, D, dt, mode, nsplit=ns, softmax=True))
+        for ns in (2, 7, 12):                       # splits cut into interleaved blocks of one step
+            p = ga.make_plan(B, C, Hq, Hkv, D, dt, mode, nsplit=ns, softmax=True, split_order="interleaved")
+            assert p.interleave == (p.nsplit > 1)
+            plans.append(p)
     if Hq // Hkv >= 2:
         for eng in ("valu", "mfma_bf16"):
             for ht in (1, 2, 4):

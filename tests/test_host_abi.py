@@ -24,7 +24,7 @@ def declared_functions():
     names = set()
     for h in sorted(glob.glob(os.path.join(os.path.dirname(HEADER), "*.h"))):
         text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
-        names |= set(re.findall(r"\b(gqa_(?:av|qk|softmax_av)_\w+)\s*\(", text))
+        names |= set(re.findall(r"\b(gqa_\w+)\s*\(", text))
     return sorted(names)
 
 
@@ -36,6 +36,7 @@ def test_library_exports_every_declared_function():
     assert {"gqa_softmax_av_decode", "gqa_softmax_av_decode_plan"} <= set(names)
     assert {"gqa_av_paged_decode", "gqa_av_paged_decode_plan"} <= set(names)
     assert {"gqa_av_fp8_decode", "gqa_av_fp8_decode_plan"} <= set(names)
+    assert {"gqa_attention_decode", "gqa_attention_paged_decode_plan", "gqa_bench_stream_read"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/ but not exported"
 
@@ -43,7 +44,7 @@ def test_library_exports_every_declared_function():
 def test_exports_are_c_symbols():
     # extern "C": no mangled gqa_av names in the dynamic symbol table
     out = os.popen(f"nm -D --defined-only {ga.LIB_PATH}").read()
-    exported = set(re.findall(r"\s(gqa_(?:av|qk|softmax_av)_\w+)$", out, flags=re.M))
+    exported = set(re.findall(r"\s(gqa_\w+)$", out, flags=re.M))
     assert set(declared_functions()) <= exported
 
 
@@ -111,7 +112,10 @@ def _check_plan(p, B, C, Hq, Hkv, D, v_dtype, mode):
         assert p.nsplit == 1
     else:
         assert p.nsplit >= 1 and p.rows_per_split >= 1
-        assert -(-C // p.rows_per_split) == p.nsplit       # splits tile [0, C) exactly
+        if p.interleave:                                   # blocks of one step, at least one per split
+            assert p.nsplit >= 2 and p.page_size == 0 and p.nsplit <= -(-C // p.rows_per_split)
+        else:
+            assert -(-C // p.rows_per_split) == p.nsplit   # splits tile [0, C) exactly
     if p.mode == 1:
         assert p.heads_per_tile >= min(G, 8) and (p.engine in (2, 3) or p.heads_per_tile <= Hq)
         assert p.subgroups == -(-G // p.heads_per_tile)
@@ -124,8 +128,6 @@ def _check_plan(p, B, C, Hq, Hkv, D, v_dtype, mode):
     assert p.grid == tiles * p.nsplit
     if p.nsplit == 1:
         assert p.combine == 0 and p.workspace_bytes == 0
-    elif p.combine == 2:                                # last workgroup adds: counters + tile blocks
-        assert p.workspace_bytes == -(-tiles * 4 // 256) * 256 + tiles * p.nsplit * (-(-tile_out // 4) * 4) * 4
     else:
         assert p.combine == 1 and p.workspace_bytes == p.nsplit * B * Hq * D * 4
 
@@ -157,11 +159,17 @@ def test_plan_edges(B, C, Hq, Hkv, D, dt):
 @pytest.mark.parametrize("nsplit", [1, 2, 7, 64, 10 ** 6])
 def test_forced_nsplit(nsplit):
     C = 1000
-    p = ga.make_plan(2, C, 8, 2, 128, "bf16", "auto", nsplit=nsplit)
-    assert p.nsplit <= min(nsplit, C)
+    p = ga.make_plan(2, C, 8, 2, 128, "bf16", "auto", nsplit=nsplit, split_order="contiguous")
+    assert p.nsplit <= min(nsplit, C) and p.interleave == 0
     assert -(-C // p.rows_per_split) == p.nsplit
     if nsplit <= 64:
         assert p.nsplit == nsplit or C % nsplit != 0
+    q = ga.make_plan(2, C, 8, 2, 128, "bf16", "auto", nsplit=nsplit)     # interleaved blocks of one step (64 rows)
+    assert q.interleave == (q.nsplit > 1)
+    if q.interleave:
+        assert q.rows_per_split == 64 and q.nsplit == min(p.nsplit, -(-C // 64))
+    else:
+        assert q.nsplit == 1 and q.rows_per_split == C
 
 
 def test_alignment_narrows_loads():
@@ -295,13 +303,23 @@ def test_forced_engines():
     assert ga.make_plan(1, 300, 16, 1, 128, "bf16", v_align=8).engine == 1
 
 
-@pytest.mark.parametrize("combine,code", [("kernel", 1), ("last", 2)])
-def test_forced_combine(combine, code):
+@pytest.mark.parametrize("combine", ["auto", "kernel"])
+def test_forced_combine(combine):
     p = ga.make_plan(2, 5000, 16, 8, 128, "bf16", combine=combine, nsplit=9)
-    assert p.nsplit == 9 and p.combine == code
+    assert p.nsplit == 9 and p.combine == 1
     _check_plan(p, 2, 5000, 16, 8, 128, "bf16", "auto")
     p1 = ga.make_plan(2, 5000, 16, 8, 128, "bf16", combine=combine, nsplit=1)
     assert p1.nsplit == 1 and p1.combine == 0 and p1.workspace_bytes == 0
+
+
+def test_removed_last_workgroup_combine_is_refused():
+    """The in-kernel (last arriving workgroup) combine measured slower than the
+    second kernel on every workload and is gone: its old value 2 is refused."""
+    lib = ga.load()
+    h, p = ga.Hint(), ga.Plan()
+    h.combine, h.nsplit = 2, 9
+    assert lib.gqa_av_make_plan(2, 5000, 16, 8, 128, 2, -1, ctypes.byref(h), ctypes.byref(p)) == 1
+    assert b"combine" in lib.gqa_av_last_error()
 
 
 def test_zeroed_hint_means_automatic():
@@ -414,9 +432,6 @@ def test_softmax_plan_refusals():
         ga.make_plan(2, 1000, 16, 2, 128, "f16", "reuse", engine="mfma", softmax=True)
     assert e.value.name == "UNSUPPORTED"
     with pytest.raises(ga.GqaAvError) as e:
-        ga.make_plan(2, 1000, 16, 2, 128, "bf16", "reuse", nsplit=4, combine="last", softmax=True)
-    assert e.value.name == "UNSUPPORTED"
-    with pytest.raises(ga.GqaAvError) as e:
         ga.make_plan(1, 1000, 16, 8, 32, "bf16", "reuse", engine="valu", kv_tile=8, softmax=True)
     assert e.value.name == "UNSUPPORTED"
     # f16 / f32 V with a large group: the automatic engine is VALU, not the fp32 matrix engine
@@ -472,7 +487,6 @@ def test_paged_plans(wname):
 def test_paged_refusals():
     for kw, name in ((dict(page_size=12), "INVALID_ARG"), (dict(page_size=16, engine="mfma"), "UNSUPPORTED"),
                      (dict(page_size=16, engine="mfma_bf16", mode="per_head"), "UNSUPPORTED"),
-                     (dict(page_size=16, nsplit=4, combine="last"), "UNSUPPORTED"),
                      (dict(page_size=1, nsplit=1), "UNSUPPORTED")):          # 4000 rows on 1-row pages: 4000 pages
         with pytest.raises(ga.GqaAvError) as e:
             ga.make_plan(4, 4000, 16, 8, 128, "bf16", **kw)
@@ -671,4 +685,7 @@ def test_tuned_plan_choices():
     for dt in ("bf16", "fp8"):
         for kw in (dict(attention=True), dict(softmax=True), {}):
             p = plan(*mqa, dt=dt, **kw)
-            assert (p.nsplit, p.rows_per_split, p.grid) == (64, 512, 256), (dt, kw)
+            # the plain product cuts its splits into interleaved blocks of one
+            # step (four waves of 32 rows), the fused ones into contiguous ranges
+            want = (64, 128, 256, 1) if not kw else (64, 512, 256, 0)
+            assert (p.nsplit, p.rows_per_split, p.grid, p.interleave) == want, (dt, kw)

@@ -117,8 +117,9 @@ def _remap(i, n):
 def _check_plan(p, B, C, Hq, Hkv, D, es=2):
     """es: bytes of a V element (2: bf16; 1: fp8, loaded as 8-byte pieces of 8 values)."""
     assert p.engine == ENGINE_BF16 and p.vec_bytes == 8 * es
-    PR, HT = D // 8, p.kv_heads_per_tile
-    RPI, LPI, WPH = 64 // PR, PR // 2, 4 // HT
+    PR, HT, NW = D // 8, p.kv_heads_per_tile, p.threads // 64
+    assert NW in (4, 8) and NW % HT == 0 and (NW == 4 or not p.softmax)
+    RPI, LPI, WPH = 64 // PR, PR // 2, NW // HT
     NSET = p.heads_per_tile // 16
     RSTEP, vrow, G = 32 * WPH, Hkv * D * es, Hq // Hkv
     GT, nsg, ns = 16 * NSET, p.subgroups, p.nsplit
@@ -127,6 +128,7 @@ def _check_plan(p, B, C, Hq, Hkv, D, es=2):
     lanes = np.arange(64)
     cnt = np.zeros((B, Hq, D), np.int64)
     scnt = np.zeros((ns, B, Hq), np.int64)          # fused softmax: split statistics written
+    seen = {}                                       # rows each (b, KV head, head set) is streamed for, all splits
     nkvt = Hkv // HT
     for blk in range(p.grid):
         t = _remap(blk, p.grid)
@@ -135,8 +137,15 @@ def _check_plan(p, B, C, Hq, Hkv, D, es=2):
         s = t % ns; t //= ns
         b = t % B
         qf, nq = kv * G + sg * GT, min(GT, G - sg * GT)
-        cb = s * p.rows_per_split
-        ce = min(C, cb + p.rows_per_split)
+        il = bool(p.interleave) and not p.page_size
+        assert p.interleave in (0, 1) and not (p.interleave and p.page_size)
+        if il:
+            # interleaved: split s takes the steps s, s + ns, ... of RSTEP rows of the sequence
+            assert p.rows_per_split == RSTEP and 2 <= ns <= -(-C // RSTEP)
+            cb, ce = 0, C
+        else:
+            cb = s * p.rows_per_split
+            ce = min(C, cb + p.rows_per_split)
         nrows = ce - cb
         assert nrows > 0
         if p.page_size:
@@ -155,7 +164,7 @@ def _check_plan(p, B, C, Hq, Hkv, D, es=2):
                 ns_ = -(-nr // RSTEP)
                 uniform = es == 1 and P >= RPI and cb % RPI == 0 and P * vrow <= 2 ** 31 - 1   # fp8 only
                 for step in range(ns_ + (1 if ns_ > 1 else 0)):
-                    for wave in range(4):
+                    for wave in range(NW):
                         r0 = 32 * (step * WPH + wave % WPH)
                         rows = np.minimum(r0 + RPI * np.arange(LPI)[:, None] + lanes[None, :] // PR, nr - 1)
                         idx = ((cb + rows) >> shift) - pg0
@@ -188,16 +197,20 @@ def _check_plan(p, B, C, Hq, Hkv, D, es=2):
         assert ((b * C + cb) * Hkv + kv) * D * es + vrec <= B * C * Hkv * D * es and vrec < 2 ** 31
         wrec = ((nrows - 1) * Hq + (HT - 1) * G + nq) * 4
         assert ((b * C + cb) * Hq + qf) * 4 + wrec <= B * C * Hq * 4 and wrec < 2 ** 31
-        nsteps = -(-nrows // RSTEP)
+        nblk = -(-nrows // RSTEP)
+        nsteps = (-(-(nblk - s) // ns) if nblk > s else 0) if il else nblk
+        step_row = (lambda st: (st * ns + s) * RSTEP) if il else (lambda st: st * RSTEP)
         loaded, st = ([0] if nsteps else []), 0
         while st + 1 < nsteps:                  # the pipeline's loads, including its unconditional reload
             loaded += [st + 1, st + 2]
             st += 2
-        seen = {k: [] for k in range(HT)}
+        for k in range(HT):
+            seen.setdefault((b, kv + k, sg), [])
         for step in loaded:
-            for wave in range(4):
+            for wave in range(NW):
                 kvl, wh = wave // WPH, wave % WPH
-                r0 = 32 * (step * WPH + wh)
+                r0 = step_row(step) + 32 * wh
+                assert (r0 + 32 + 2 * RSTEP) * max(vrow, Hq * 4) < 2 ** 31
                 rows = r0 + RPI * np.arange(LPI)[:, None] + lanes[None, :] // PR
                 off = ((lanes // PR) * vrow + kvl * D * es + (lanes % PR) * 8 * es
                        + (r0 + RPI * np.arange(LPI)[:, None]) * vrow)
@@ -209,9 +222,7 @@ def _check_plan(p, B, C, Hq, Hkv, D, es=2):
                           + (r0 + np.arange(8)[:, None]) * Hq * 4)
                     assert np.array_equal(wo + 4 <= wrec, wrows < nrows)
                 if step < nsteps:
-                    seen[kvl] += [r for r in range(r0, r0 + 32) if r < nrows]
-        for k in range(HT):
-            assert sorted(seen[k]) == list(range(nrows))
+                    seen[(b, kv + kvl, sg)] += [cb + r for r in range(r0, r0 + 32) if r < nrows]
         if s == 0:
             idx = np.arange(HT * TO)
             k, e = idx // TO, idx % TO
@@ -232,6 +243,8 @@ def _check_plan(p, B, C, Hq, Hkv, D, es=2):
     assert (cnt == 1).all()
     if p.softmax and ns > 1:
         assert (scnt == 1).all(), "each split's statistics of each (b, q_h) are written once"
+    for key, rows in seen.items():
+        assert sorted(rows) == list(range(C)), f"{key}: every row streamed by exactly one split"
 
 
 @pytest.mark.parametrize("B,C,Hq,Hkv,D", [(1, 300, 16, 1, 128), (2, 1000, 16, 2, 64), (2, 130, 40, 2, 64),
@@ -239,22 +252,27 @@ def _check_plan(p, B, C, Hq, Hkv, D, es=2):
                                          (2, 700, 32, 4, 128), (1, 300, 48, 4, 256), (3, 1500, 16, 2, 64)])
 def test_bf16_engine_plan_bounds(B, C, Hq, Hkv, D):
     for ns in (0, 1, 3, 7):
-        for comb, sm in (("kernel", False), ("last", False), ("kernel", True)):
+        for comb, sm in (("kernel", False), ("auto", False), ("kernel", True)):
             for ht in (0, 1, 2, 4):
                 if ht > 1 and Hkv % ht:
                     continue
                 for dt, es in (("bf16", 2), ("fp8", 1)):
                     for P in (0,) + ((16,) if ht in (0, 2) else ()) + ((1, 256) if ns in (0, 3) and ht == 0 else ()):
-                        if (dt == "fp8" or P) and comb == "last":
-                            continue
-                        try:
-                            p = ga.make_plan(B, C, Hq, Hkv, D, dt, "reuse", engine="mfma_bf16", nsplit=ns,
-                                             combine=comb, kv_tile=ht, softmax=sm, page_size=P)
-                        except ga.GqaAvError as e:     # a forced split over more than 1024 pages
-                            assert e.name == "UNSUPPORTED" and P and ns and -(-C // ns) > 1023 * P
-                            continue
-                        assert p.softmax == int(sm) and p.page_size == P
-                        _check_plan(p, B, C, Hq, Hkv, D, es)
+                        for nw, order in (((0, "auto"), (0, "interleaved")) if sm else
+                                          ((0, "auto"), (8, "auto"), (0, "contiguous"), (8, "contiguous"))):
+                            try:
+                                p = ga.make_plan(B, C, Hq, Hkv, D, dt, "reuse", engine="mfma_bf16", nsplit=ns,
+                                                 combine=comb, kv_tile=ht, softmax=sm, page_size=P, waves=nw,
+                                                 split_order=order)
+                            except ga.GqaAvError as e:     # a forced split over more than 1024 pages, or
+                                assert e.name == "UNSUPPORTED" and P and (   # interleaved splits of paged V
+                                    (ns and -(-C // ns) > 1023 * P) or order == "interleaved")
+                                continue
+                            assert p.softmax == int(sm) and p.page_size == P
+                            assert nw == 0 or p.threads == 64 * nw
+                            assert p.interleave == ((order == "interleaved" or (order == "auto" and not sm))
+                                                    and not P and p.nsplit > 1)
+                            _check_plan(p, B, C, Hq, Hkv, D, es)
 
 
 ENGINE_VALU = 1
@@ -281,6 +299,7 @@ def _check_valu_plan(p, B, C, Hq, Hkv, D, dt):
     kvl = j // L
     cnt = np.zeros((B, Hq, D), np.int64)
     scnt = np.zeros((ns, B, Hq), np.int64)          # fused softmax: split statistics written
+    rows_of = {}                                    # rows each tile's splits stream, over all splits
     if p.softmax:
         CH = min(GT * E, 32)
         assert HT <= 4 and rps * HT * GT <= CH * 256, "row-slot statistics must fit the reduction buffer"
@@ -298,8 +317,15 @@ def _check_valu_plan(p, B, C, Hq, Hkv, D, dt):
             qf, nq = kv * G + sg * GT, min(GT, G - sg * GT)
         lane_d = dtile * Lc + (j - kvl * L)
         active = (r < rps) & (lane_d < L)
-        cb = s * p.rows_per_split
-        ce = min(C, cb + p.rows_per_split)
+        il = bool(p.interleave) and not p.page_size
+        assert p.interleave in (0, 1) and not (p.interleave and p.page_size)
+        if il:
+            # interleaved: split s takes the blocks s, s + ns, ... of R rows of the sequence
+            assert p.rows_per_split == R and 2 <= ns <= -(-C // R)
+            cb, ce = 0, C
+        else:
+            cb = s * p.rows_per_split
+            ce = min(C, cb + p.rows_per_split)
         nrows = ce - cb
         assert nrows > 0
         if p.page_size:
@@ -328,16 +354,22 @@ def _check_valu_plan(p, B, C, Hq, Hkv, D, dt):
         q_lo = np.minimum(qf + kvl * G, Hq - GT)
         voff = r * vrow + kvl * D * es + lane_d * VB
         woff = (r * Hq + q_lo) * 4
-        nsteps = -(-nrows // R)
+        nblk = -(-nrows // R)
+        nsteps = (-(-(nblk - s) // ns) if nblk > s else 0) if il else nblk
+        step_row = (lambda st: (st * ns + s) * R) if il else (lambda st: st * R)
         loaded, st = ([0] if nsteps else []), 0
         while st + 1 < nsteps:
             loaded += [st + 1, st + 2]
             st += 2
+        tile = (b, kvt, minor, major)
+        rows_of.setdefault(tile, [])
         for step in loaded:
             for u in range(U):
-                row = step * R + u * rps
+                row = step_row(step) + u * rps
                 assert (row + 2 * R) * vrow < 2 ** 31 and (row + 2 * R) * Hq * 4 < 2 ** 31
                 inrow = (row + r) < nrows
+                if step < nsteps:
+                    rows_of[tile] += [cb + row + rr for rr in range(rps) if row + rr < nrows]
                 off = voff + row * vrow
                 assert np.array_equal((off + VB <= vrec)[active], inrow[active])
                 assert (off[active] >= 0).all()
@@ -368,6 +400,9 @@ def _check_valu_plan(p, B, C, Hq, Hkv, D, dt):
     assert (cnt == 1).all()
     if p.softmax and ns > 1:
         assert (scnt == 1).all(), "each split's statistics of each (b, q_h) are written once"
+    if not p.page_size:
+        for tile, rows in rows_of.items():
+            assert sorted(rows) == list(range(C)), f"tile {tile}: every row streamed by exactly one split"
 
 
 @pytest.mark.parametrize("B,C,Hq,Hkv,D,dt", [
@@ -384,14 +419,17 @@ def test_valu_engine_plan_bounds(B, C, Hq, Hkv, D, dt):
                     continue
                 for align, P in ((0, 0), (2, 0), (0, 1), (0, 16), (0, 64)):
                     for sm in (False, True):
-                        try:
-                            p = ga.make_plan(B, C, Hq, Hkv, D, dt, mode, engine="valu", nsplit=ns, kv_tile=ht,
-                                             v_align=align, softmax=sm, page_size=P)
-                        except ga.GqaAvError as e:
-                            assert e.name == "UNSUPPORTED"
-                            continue
-                        assert p.softmax == int(sm)
-                        _check_valu_plan(p, B, C, Hq, Hkv, D, dt)
+                        # contiguous splits of paged or narrowed V are the automatic plan already
+                        for order in (("auto", "contiguous") if (align, P) == (0, 0) else ("auto",)):
+                            try:
+                                p = ga.make_plan(B, C, Hq, Hkv, D, dt, mode, engine="valu", nsplit=ns, kv_tile=ht,
+                                                 v_align=align, softmax=sm, page_size=P, split_order=order)
+                            except ga.GqaAvError as e:
+                                assert e.name == "UNSUPPORTED"
+                                continue
+                            assert p.softmax == int(sm)
+                            assert p.interleave == (order == "auto" and not P and p.nsplit > 1 and not sm)
+                            _check_valu_plan(p, B, C, Hq, Hkv, D, dt)
 
 
 # ---- decode score step -------------------------------------------------------

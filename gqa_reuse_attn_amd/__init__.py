@@ -111,6 +111,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     for fn in ("gqa_av_decode_plan", "gqa_av_decode_pass1", "gqa_av_decode_combine"):
         getattr(lib, fn).argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ip, ctypes.POINTER(Plan), vp]
         getattr(lib, fn).restype = ip
+    lib.gqa_av_decode_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ip, ip, vp]
+    lib.gqa_av_decode_noalloc.restype = ip
     lib.gqa_softmax_av_decode.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ip, ip, vp]
     lib.gqa_softmax_av_decode.restype = ip
     for fn in ("gqa_softmax_av_decode_plan", "gqa_softmax_av_decode_pass1", "gqa_softmax_av_decode_combine"):

@@ -97,14 +97,18 @@ std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 std::vector<std::pair<int, void*>> g_ws_retired;   // (device, buffer), freed by gqa_av_release
 
+// Per-device state lives in fixed tables (no host allocation on the call path).
+constexpr int kMaxDevices = 64;
+
 std::mutex g_cu_mutex;
-std::map<int, int> g_cu_count;
+int g_cu_count[kMaxDevices];   // 0: not asked yet
 
 int device_cus(int dev, int* cus) {
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(GQA_AV_ERR_UNSUPPORTED, "device %d: this library handles devices 0 .. %d", dev, kMaxDevices - 1);
     std::lock_guard<std::mutex> lock(g_cu_mutex);
-    auto it = g_cu_count.find(dev);
-    if (it != g_cu_count.end()) {
-        *cus = it->second;
+    if (g_cu_count[dev] > 0) {
+        *cus = g_cu_count[dev];
         return GQA_AV_OK;
     }
     int n = 0;
@@ -152,6 +156,36 @@ int get_workspace(int dev, hipStream_t stream, size_t bytes, float** part) {
         ws.part_bytes = n;
     }
     *part = static_cast<float*>(ws.part);
+    return GQA_AV_OK;
+}
+
+}  // namespace
+
+// Split partials of gqa_av_decode_noalloc: a fixed device array instead of an
+// allocated workspace. Host code never passes this name to a kernel or a copy
+// (on the host it is only a stand-in); it uses the device address that
+// hipGetSymbolAddress gives for the current device, kept per device below.
+static __device__ __align__(256) uint8_t scratch[GQA_AV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device, once looked up
+
+// The device address of `scratch` on device `dev`, which must be current:
+// looked up once per device (hipGetSymbolAddress allocates nothing).
+int scratch_address(int dev, float** p) {
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(GQA_AV_ERR_UNSUPPORTED, "device %d: this library handles devices 0 .. %d", dev, kMaxDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* q = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !q)
+            return fail(GQA_AV_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = q;
+    }
+    *p = static_cast<float*>(g_scratch_ptr[dev]);
     return GQA_AV_OK;
 }
 
@@ -636,9 +670,12 @@ struct AttnArgs {
 
 // softmax: 1 for the fused softmax entry points (attn then holds the scores);
 // pg: the paged cache (V then points at its pages), or NULL for dense V.
+// no_alloc: the split partials go to the fixed `scratch` array instead of the
+// stream's workspace (gqa_av_decode_noalloc).
 int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
              int64_t D, int v_dtype, const gqa_av_plan* plan, void* stream, int which, int softmax,
-             const PagedArgs* pg = nullptr, const float* v_scale = nullptr, const AttnArgs* at = nullptr) {
+             const PagedArgs* pg = nullptr, const float* v_scale = nullptr, const AttnArgs* at = nullptr,
+             bool no_alloc = false) {
     if (!plan) return fail(GQA_AV_ERR_INVALID_ARG, "plan is NULL");
     int rc = check_sizes(B, C, Hq, Hkv, D, v_dtype);
     if (rc != GQA_AV_OK) return rc;
@@ -737,7 +774,16 @@ int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C,
 
     float* part = nullptr;
     if (plan->nsplit > 1) {
-        rc = get_workspace(dev, s, static_cast<size_t>(plan->workspace_bytes), &part);
+        if (no_alloc) {
+            if (plan->workspace_bytes > static_cast<int64_t>(GQA_AV_NOALLOC_SCRATCH_BYTES))
+                return fail(GQA_AV_ERR_UNSUPPORTED,
+                            "the plan needs %lld bytes of split partials; the allocation-free entry point has a "
+                            "fixed %d-byte scratch array (use gqa_av_decode)",
+                            (long long)plan->workspace_bytes, GQA_AV_NOALLOC_SCRATCH_BYTES);
+            rc = scratch_address(dev, &part);
+        } else {
+            rc = get_workspace(dev, s, static_cast<size_t>(plan->workspace_bytes), &part);
+        }
         if (rc != GQA_AV_OK) return rc;
     }
 
@@ -877,6 +923,15 @@ int gqa_av_decode(const float* attn, const void* V, float* out, int64_t B, int64
     int rc = auto_plan(V, B, C, Hq, Hkv, D, v_dtype, mode, 0, &plan);
     if (rc != GQA_AV_OK) return rc;
     return gqa_av_decode_plan(attn, V, out, B, C, Hq, Hkv, D, v_dtype, &plan, stream);
+}
+
+int gqa_av_decode_noalloc(const float* attn, const void* V, float* out, int64_t B, int64_t C, int64_t Hq,
+                          int64_t Hkv, int64_t D, int v_dtype, int mode, void* stream) {
+    gqa_av_plan plan;
+    int rc = auto_plan(V, B, C, Hq, Hkv, D, v_dtype, mode, 0, &plan);
+    if (rc != GQA_AV_OK) return rc;
+    return run_plan(attn, V, out, B, C, Hq, Hkv, D, v_dtype, &plan, stream, kRunPass1 | kRunCombine, 0, nullptr,
+                    nullptr, nullptr, true);
 }
 
 int gqa_softmax_av_decode(const float* scores, const void* V, float* out, int64_t B, int64_t C, int64_t Hq,

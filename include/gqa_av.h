@@ -207,6 +207,25 @@ int gqa_av_decode_combine(const float *attn, const void *V, float *out,
                           int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D,
                           int v_dtype, const gqa_av_plan *plan, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, hosts that forbid hipMalloc): gqa_av_decode
+ * with the same automatic plan and kernels, its split partials kept in a
+ * fixed device array of GQA_AV_NOALLOC_SCRATCH_BYTES (8 MiB) inside the
+ * library instead of an allocated workspace. It calls no hipMalloc, hipFree
+ * or other allocating routine; the array exists once per device the library
+ * runs on and lives until the process ends. A problem whose plan needs more
+ * partial-sum space (plan->workspace_bytes) is refused with
+ * GQA_AV_ERR_UNSUPPORTED before anything is launched. Every call on one
+ * device shares that device's array, which keeps the last call's partials
+ * (nothing in it needs clearing: each call writes all it reads): calls that
+ * overlap in time on one device (other streams, concurrent graph replays)
+ * race and must be ordered by the caller. Same arguments, results and
+ * errors as gqa_av_decode otherwise. */
+#define GQA_AV_NOALLOC_SCRATCH_BYTES (8 << 20)
+int gqa_av_decode_noalloc(const float *attn, const void *V, float *out,
+                          int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D,
+                          int v_dtype, int mode, void *stream);
+
 /* Static description of a status code. */
 const char *gqa_av_status_string(int status);
 

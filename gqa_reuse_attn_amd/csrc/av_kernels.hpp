@@ -560,7 +560,6 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
 
     // Sum the row slots: slot kk of thread tid lives at smem[kk * 256 + tid].
     // Output slot k = g * E + e of lane chunk jj is tile output k * Lc + jj.
-    const int TO = NACC * Lc;
     float* const plane = a.nsplit > 1 ? a.part + static_cast<size_t>(T.s) * a.B * a.Hq * a.D : a.out;
     auto out_index = [&](int k, int jj, size_t* o) -> bool {
         const int g = k / E, e = k - (k / E) * E;
@@ -817,10 +816,10 @@ __global__ __launch_bounds__(64 * NW) void av_pass1_mfma_bf16(Pass1Args a) {
     constexpr int LPI = PR / 2;                      // 16-byte loads per lane and chunk
     constexpr int RPI = 64 / PR;                     // rows one 64-lane load covers
     constexpr int WPH = NW / HT;                     // waves per KV head
-    constexpr int TO = 16 * NSET * D;                // outputs of one KV head's tile
-    constexpr int TOW = HT * TO;                     // outputs of the workgroup
     constexpr int STAGE = NW * 32 * RB;              // bytes: one 32-row region per wave
-    constexpr int RED = NW * TO * 4;                 // bytes: the final cross-wave sum
+    constexpr int GH = 16 * NSET;                    // heads of a KV head's tile
+    constexpr int RP = D + 4;                        // floats per row of the final sum (padded)
+    constexpr int RED = NW * GH * RP * 4;            // bytes: the final cross-wave sum
     __shared__ __align__(16) uint8_t smem[STAGE > RED ? STAGE : RED];
 
     const Tile T = decode_tile(a, 16 * NSET);
@@ -1266,7 +1265,6 @@ __global__ __launch_bounds__(64 * NW) void av_pass1_mfma_bf16(Pass1Args a) {
 
     // SM: each wave's maximum and weight sum per head (lane group 0 holds head
     // m + 16 s after the sum over the four lane groups).
-    constexpr int GH = 16 * NSET;
     __shared__ float s_wm[NW][GH], s_wl[NW][GH], s_tm[HT][GH], s_tl[HT][GH];
     if constexpr (SM) {
 #pragma unroll
@@ -1281,9 +1279,11 @@ __global__ __launch_bounds__(64 * NW) void av_pass1_mfma_bf16(Pass1Args a) {
     }
 
     // Add the tiles of each KV head's waves. Register i of acc[s][t] in lane
-    // l is head 16 s + 4 (l / 16) + i, column 16 t + l % 16; as an output
-    // index of the KV head's tile: ((s * NT + t) * 4 + i) * 64 + l. The
-    // workgroup's outputs are the HT heads' tiles one after another.
+    // l is head 16 s + 4 (l / 16) + i, column 16 t + l % 16. Each wave puts
+    // its tile into LDS as [head][column] rows of RP floats (the padding puts
+    // the four lane groups of one store on different banks); a thread then
+    // adds four consecutive columns of one head over the KV head's waves, in
+    // wave order, and writes them with one 16-byte store.
     __syncthreads();                                 // every wave is done with its region
     if constexpr (SM) {
         // Bring this wave's tile to the maximum of its KV head's waves.
@@ -1325,35 +1325,37 @@ __global__ __launch_bounds__(64 * NW) void av_pass1_mfma_bf16(Pass1Args a) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) red[wave * TO + ((s * NT + t) * 4 + i) * 64 + lane] = acc[s][t][i];
+            for (int i = 0; i < 4; ++i)
+                red[(wave * GH + 16 * s + 4 * (lane >> 4) + i) * RP + 16 * t + (lane & 15)] = acc[s][t][i];
     __syncthreads();
     float* const plane = a.nsplit > 1 ? a.part + static_cast<size_t>(T.s) * a.B * a.Hq * D : a.out;
-    auto out_index = [&](int idx, size_t* o) -> bool {
-        const int k = idx / TO, e = idx - k * TO;
-        const int l = e & 63, reg = e >> 6;
-        const int i = reg & 3, st2 = reg >> 2;
-        const int t = st2 % NT, s = st2 / NT;
-        const int h = 16 * s + 4 * (l >> 4) + i;
-        *o = (static_cast<size_t>(T.b) * a.Hq + T.q_first + k * a.G + h) * D + 16 * t + (l & 15);
-        return h < T.nq;
-    };
-    for (int idx = threadIdx.x; idx < TOW; idx += NTH) {
-        const int k = idx / TO, e = idx - k * TO;
-        float sum = red[k * WPH * TO + e];
+    // `out` need only be 4-byte aligned; the split planes are 16-byte aligned.
+    const bool vec_store = (reinterpret_cast<uintptr_t>(plane) & 15u) == 0;
+    constexpr int Q4 = D / 4;                        // column quads of a head's row
+    typedef __attribute__((address_space(3))) f32x4 lds_f4;
+    for (int qi = threadIdx.x; qi < HT * GH * Q4; qi += NTH) {
+        const int k = qi / (GH * Q4), hh = (qi / Q4) % GH, c4 = qi % Q4;
+        typedef __attribute__((address_space(3))) float lds_fl;
+        const lds_f4* const r0 = (const lds_f4*)((lds_fl*)(smem) + (k * WPH * GH + hh) * RP + 4 * c4);
+        f32x4 sum = r0[0];
 #pragma unroll
-        for (int w = 1; w < WPH; ++w) sum += red[(k * WPH + w) * TO + e];
+        for (int w = 1; w < WPH; ++w) sum += r0[w * GH * RP / 4];
         if constexpr (SM) {
             // One split: normalise here; several: the combine does.
-            if (a.nsplit == 1) {
-                const int reg = (e >> 6), h = 16 * ((reg >> 2) / NT) + 4 * ((e & 63) >> 4) + (reg & 3);
-                sum = nrows > 0 ? sum / s_tl[k][h] : 0.0f;
-            }
+            if (a.nsplit == 1) sum = nrows > 0 ? sum / s_tl[k][hh] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         }
         if constexpr (FP8) {
             if (a.v_scale) sum *= a.v_scale[T.kv + k];   // the tile's k-th KV head
         }
-        size_t o;
-        if (out_index(idx, &o)) plane[o] = sum;
+        if (hh < T.nq) {
+            float* const o = plane + (static_cast<size_t>(T.b) * a.Hq + T.q_first + k * a.G + hh) * D + 4 * c4;
+            if (vec_store) {
+                *reinterpret_cast<f32x4*>(o) = sum;
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) o[c] = sum[c];
+            }
+        }
     }
     if constexpr (SM) {
         if (a.nsplit > 1 && threadIdx.x < HT * GH) {

@@ -426,6 +426,9 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
     // Waves per workgroup: four, or eight for the plain product on the bf16
     // matrix engine (more rows in flight per workgroup without more splits).
     int nw = gqa_av::kWaves;
+    // Automatic: eight waves for the plain product on the bf16 matrix engine
+    // when a workgroup streams one KV head (set below, once the KV heads per
+    // tile are known).
     if (h.waves > 0 && h.waves != nw) {
         if (!bf16_engine || sm)
             return fail(GQA_AV_ERR_UNSUPPORTED, "%d waves per workgroup: only the plain product on the bf16 matrix "
@@ -437,6 +440,12 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
     int64_t Lc, rps, ndt, rows_per_step, tile_outputs;
     int64_t heads_major;  // tiles along the head axis per KV head
     if (engine == GQA_AV_ENGINE_MFMA_BF16) {
+        // Eight waves when one KV head per workgroup: more rows in flight per
+        // CU without more splits. Measured on MI355X, B = 4, C = 32768,
+        // Hq = 16, Hkv = 1: pass 1 10.4 -> 9.9 us; with four KV heads per
+        // workgroup (B = 64, C = 8192, Hq = 64, Hkv = 8) eight waves were
+        // slower (176 -> 190 us).
+        if (h.waves == 0 && ht == 1 && !sm) nw = 8;
         VB = v_dtype == GQA_AV_FP8_E4M3 ? 8 : 16;    // one 8-value piece per lane load
         GT = 16 * nset16;
         nsg = static_cast<int>(ceil_div(G, GT));

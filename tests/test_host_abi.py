@@ -85,7 +85,7 @@ def test_resolve_mode_errors(Hq, Hkv, mode, status):
 def _check_plan(p, B, C, Hq, Hkv, D, v_dtype, mode):
     es = 4 if v_dtype == "f32" else 2
     G = Hq // Hkv
-    assert p.threads == 256
+    assert p.threads == 256 or (p.threads == 512 and p.engine == 3)
     if p.engine == 2:                                   # MFMA: 16 lanes x D/16 elements per row
         assert p.mode == 1 and D % 16 == 0
         assert p.vec_bytes == D // 16 * es and p.lanes_per_row == 16 and p.row_slots == 16 and p.d_tiles == 1
@@ -94,7 +94,10 @@ def _check_plan(p, B, C, Hq, Hkv, D, v_dtype, mode):
     elif p.engine == 3:                                 # bf16 MFMA: 16-byte pieces, 32-row chunk per wave
         ht = p.kv_heads_per_tile
         assert p.mode == 1 and v_dtype == "bf16" and D in (64, 128, 256) and ht in (1, 2, 4) and Hkv % ht == 0
-        assert p.vec_bytes == 16 and p.lanes_per_row == ht * D // 8 and p.row_slots == 128 // ht and p.d_tiles == 1
+        assert p.vec_bytes == 16 and p.lanes_per_row == ht * D // 8 and p.d_tiles == 1
+        assert p.row_slots == 32 * (p.threads // 64) // ht
+        # automatic: eight waves for the plain product with one KV head per workgroup
+        assert p.threads == 256 or (ht == 1 and not p.softmax)
         assert p.heads_per_tile in (16, 32) and p.heads_per_tile * D <= 4096
         tile_out = ht * p.heads_per_tile * D
     else:
@@ -685,7 +688,8 @@ def test_tuned_plan_choices():
     for dt in ("bf16", "fp8"):
         for kw in (dict(attention=True), dict(softmax=True), {}):
             p = plan(*mqa, dt=dt, **kw)
-            # the plain product cuts its splits into interleaved blocks of one
-            # step (four waves of 32 rows), the fused ones into contiguous ranges
-            want = (64, 128, 256, 1) if not kw else (64, 512, 256, 0)
-            assert (p.nsplit, p.rows_per_split, p.grid, p.interleave) == want, (dt, kw)
+            # the plain product runs eight waves and cuts its splits into
+            # interleaved blocks of one step (eight waves of 32 rows), the
+            # fused ones four waves and contiguous ranges
+            want = (64, 256, 256, 1, 512) if not kw else (64, 512, 256, 0, 256)
+            assert (p.nsplit, p.rows_per_split, p.grid, p.interleave, p.threads) == want, (dt, kw)

@@ -123,7 +123,6 @@ def _check_plan(p, B, C, Hq, Hkv, D, es=2):
     NSET = p.heads_per_tile // 16
     RSTEP, vrow, G = 32 * WPH, Hkv * D * es, Hq // Hkv
     GT, nsg, ns = 16 * NSET, p.subgroups, p.nsplit
-    TO = GT * D
     assert p.lanes_per_row == HT * D // 8 and p.row_slots == 32 * WPH
     lanes = np.arange(64)
     cnt = np.zeros((B, Hq, D), np.int64)
@@ -224,17 +223,28 @@ def _check_plan(p, B, C, Hq, Hkv, D, es=2):
                 if step < nsteps:
                     seen[(b, kv + kvl, sg)] += [cb + r for r in range(r0, r0 + 32) if r < nrows]
         if s == 0:
-            idx = np.arange(HT * TO)
-            k, e = idx // TO, idx % TO
-            l, reg = e & 63, e >> 6
-            i, st2 = reg & 3, reg >> 2
-            tt, ss = st2 % (D // 16), st2 // (D // 16)
-            h = 16 * ss + 4 * (l >> 4) + i
-            ok = h < nq
-            np.add.at(cnt, (b, qf + k[ok] * G + h[ok], 16 * tt[ok] + (l[ok] & 15)), 1)
-            # the head the fused softmax normalises output idx by (nsplit == 1)
-            hs = 16 * ((reg >> 2) // (D // 16)) + 4 * ((e & 63) >> 4) + (reg & 3)
-            assert np.array_equal(hs, h)
+            # the final sum: wave w writes head row 16 s + 4 (l / 16) + i, column
+            # 16 t + l % 16 of its [GH][RP] region; thread q then adds four
+            # columns of head hh over its KV head's waves and stores them
+            RP = D + 4
+            lw = np.arange(64)
+            for w in range(NW):
+                for sset in range(NSET):
+                    for t in range(D // 16):
+                        for i in range(4):
+                            off = (w * GT + 16 * sset + 4 * (lw >> 4) + i) * RP + 16 * t + (lw & 15)
+                            assert off.min() >= 0 and off.max() < NW * GT * RP
+                            # the four lane groups of one store land on different banks (64 banks)
+                            assert len(set(off % 64)) == 64
+            Q4 = D // 4
+            q = np.arange(HT * GT * Q4)
+            k, hh, c4 = q // (GT * Q4), (q // Q4) % GT, q % Q4
+            for w in range(WPH):
+                off = ((k * WPH + w) * GT + hh) * RP + 4 * c4
+                assert off.min() >= 0 and off.max() + 3 < NW * GT * RP and (off % 4 == 0).all()
+            ok = hh < nq
+            for c in range(4):
+                np.add.at(cnt, (b, qf + k[ok] * G + hh[ok], 4 * c4[ok] + c), 1)
         if p.softmax and ns > 1:
             for t2 in range(HT * GT):
                 k2, hh = t2 // GT, t2 % GT

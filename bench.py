@@ -61,7 +61,8 @@ SUITE = ["tiny-f32-b1-c256-hq8-hkv2-d64", "llama3-8b-b1-c4096-hq32-hkv8-d128-bf1
          "g3-b8-c16384-hq24-hkv8-d96-f16", "g2-b4-c32768-hq16-hkv8-d128-bf16",
          "mqa16-b4-c32768-hq16-hkv1-d128-bf16", HEADLINE]
 READ_GRIDS = (256, 512, 1024, 2048)    # plain-read sweep: workgroups ...
-READ_LOADS = (4, 8, 16)                # ... x 16-byte loads per lane and batch
+READ_LOADS = (4, 8, 16)                # ... x 16-byte loads per lane and batch ...
+READ_PATTERNS = (0, 1)                 # ... x contiguous slices / grid-stride batches
 PROFILES = os.path.join(ROOT, "profiles")
 _CSRC = os.path.join(ROOT, "gqa_reuse_attn_amd", "csrc")
 # The sources each operation's kernels are built from (a profile records their hash).
@@ -385,18 +386,23 @@ def read_ceiling(args, sets: DeviceSets, nbytes: int, stream) -> dict | None:
         return None
     sink = torch.zeros(256, dtype=torch.int32, device=stream.device)
     best = None
-    for wg in READ_GRIDS:
-        for lif in READ_LOADS:
-            fns = [lambda i=i, wg=wg, lif=lif: ga.stream_read(sets.base(i), nbytes, wg, lif, sink, stream)
-                   for i in range(sets.nrot)]
-            for f in fns[:8]:
-                f()
-            t = trials(fns, args.steps, stream, min_trials=3, max_trials=10, rel_se=0.01)
-            if best is None or t["median_us"] < best["us"]:
-                best = {"us": t["median_us"], "se_us": t["se_us"], "workgroups": wg, "loads_in_flight": lif}
+    for pat in READ_PATTERNS:
+        for wg in READ_GRIDS:
+            for lif in READ_LOADS:
+                if pat == 1 and nbytes < 256 * 16 * lif * wg:
+                    continue                       # the grid-stride pattern needs a batch per workgroup
+                fns = [lambda i=i, wg=wg, lif=lif, pat=pat: ga.stream_read(sets.base(i), nbytes, wg, lif, sink,
+                                                                           stream, pattern=pat)
+                       for i in range(sets.nrot)]
+                for f in fns[:8]:
+                    f()
+                t = trials(fns, args.steps, stream, min_trials=3, max_trials=10, rel_se=0.01)
+                if best is None or t["median_us"] < best["us"]:
+                    best = {"us": t["median_us"], "se_us": t["se_us"], "workgroups": wg, "loads_in_flight": lif,
+                            "pattern": "grid-stride batches" if pat else "contiguous slice per workgroup"}
     best.update(rate(nbytes, best["us"]))
     best["bytes"] = nbytes
-    best["kernel"] = "gqa_bench_stream_read: 16-byte non-temporal loads, contiguous slice per workgroup"
+    best["kernel"] = "gqa_bench_stream_read: 16-byte non-temporal loads, best of both patterns"
     return best
 
 

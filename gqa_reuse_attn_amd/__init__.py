@@ -27,7 +27,7 @@ __all__ = [
     "LIB_PATH", "GqaAvError", "Hint", "Plan", "load", "resolve_mode", "make_plan",
     "gqa_av_decode", "gqa_av_decode_plan", "bind", "BoundCall", "release", "status_string", "MODES", "DTYPES",
     "QkHint", "QkPlan", "qk_make_plan", "gqa_qk_decode", "bind_qk", "gqa_softmax_av_decode", "bind_softmax",
-    "gqa_av_paged_decode", "bind_paged", "gqa_av_fp8_decode", "bind_fp8", "stream_read",
+    "gqa_av_paged_decode", "bind_paged", "gqa_av_fp8_decode", "bind_fp8", "stream_read", "gqa_av_decode_strided",
 ]
 
 # GQA_AV_LIBRARY may name another build of the same library (tuning variants).
@@ -111,6 +111,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     for fn in ("gqa_av_decode_plan", "gqa_av_decode_pass1", "gqa_av_decode_combine"):
         getattr(lib, fn).argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ip, ctypes.POINTER(Plan), vp]
         getattr(lib, fn).restype = ip
+    lib.gqa_av_decode_strided.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, ip, ip, vp]
+    lib.gqa_av_decode_strided.restype = ip
+    lib.gqa_av_decode_strided_plan.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, ip, ctypes.POINTER(Plan),
+                                               vp]
+    lib.gqa_av_decode_strided_plan.restype = ip
     lib.gqa_av_decode_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ip, ip, vp]
     lib.gqa_av_decode_noalloc.restype = ip
     lib.gqa_softmax_av_decode.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ip, ip, vp]
@@ -173,16 +178,18 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gqa_qk_decode_plan.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ip, ctypes.c_float,
                                        ctypes.POINTER(QkPlan), vp]
     lib.gqa_qk_decode_plan.restype = ip
-    lib.gqa_bench_stream_read.argtypes = [vp, i64, i32, i32, vp, vp]
+    lib.gqa_bench_stream_read.argtypes = [vp, i64, i32, i32, i32, vp, vp]
     lib.gqa_bench_stream_read.restype = ip
     _lib = lib
     return lib
 
 
-def stream_read(buf, nbytes: int, workgroups: int, loads_in_flight: int, sink, stream=None) -> None:
+def stream_read(buf, nbytes: int, workgroups: int, loads_in_flight: int, sink, stream=None,
+                pattern: int = 0) -> None:
     """Enqueue the plain streaming read of gqa_bench.h over the first nbytes of
     the GPU tensor `buf` (a measurement aid: the bandwidth ceiling, no part of
-    the product). sink: a GPU uint32/int32 tensor of at least 256 elements."""
+    the product). sink: a GPU uint32/int32 tensor of at least 256 elements;
+    pattern 0: a contiguous slice per workgroup, 1: grid-stride batches."""
     torch = _torch()
     if not (buf.is_cuda and sink.is_cuda) or nbytes > buf.numel() * buf.element_size() or sink.numel() < 256 \
             or sink.element_size() != 4:
@@ -190,7 +197,7 @@ def stream_read(buf, nbytes: int, workgroups: int, loads_in_flight: int, sink, s
     if stream is None:
         stream = torch.cuda.current_stream(buf.device)
     rc = load().gqa_bench_stream_read(buf.data_ptr(), int(nbytes), int(workgroups), int(loads_in_flight),
-                                      sink.data_ptr(), stream.cuda_stream)
+                                      int(pattern), sink.data_ptr(), stream.cuda_stream)
     if rc != 0:
         _raise(rc)
 
@@ -303,6 +310,42 @@ def gqa_av_decode(attn, V, out=None, mode: Union[str, int] = "auto", stream=None
         else:
             rc = lib.gqa_av_decode_plan(attn.data_ptr(), V.data_ptr(), out.data_ptr(), B, C, Hq, Hkv, D,
                                         DTYPES[vdt], ctypes.byref(plan), stream.cuda_stream)
+    if rc != 0:
+        _raise(rc)
+    return out
+
+
+def gqa_av_decode_strided(attn, V, C: int, out=None, mode: Union[str, int] = "auto", stream=None,
+                          plan: Optional[Plan] = None):
+    """The product over a capacity-strided V cache: V [B, C_max, Hkv, D] (any
+    C_max >= C, contiguous), rows c < C of each sequence; attn [B, C, Hq]
+    float32; returns out [B, Hq, D] float32."""
+    torch = _torch()
+    vmap = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16", torch.float8_e4m3fn: "fp8"}
+    if attn.dim() != 3 or V.dim() != 4 or attn.shape[1] != C or V.shape[1] < C or V.shape[0] != attn.shape[0]:
+        raise ValueError(f"attn must be [B,{C},Hq] and V [B,C_max>={C},Hkv,D]; got {tuple(attn.shape)} and "
+                         f"{tuple(V.shape)}")
+    if attn.dtype != torch.float32 or V.dtype not in vmap:
+        raise TypeError("attn must be float32 and V float32, float16, bfloat16 or float8_e4m3fn")
+    if not (attn.is_cuda and V.is_cuda and attn.device == V.device and attn.is_contiguous() and V.is_contiguous()):
+        raise ValueError("attn and V must be contiguous tensors on one GPU")
+    B, _, Hq = attn.shape
+    C_max, Hkv, D = V.shape[1], V.shape[2], V.shape[3]
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=attn.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (B, Hq, D) or not out.is_contiguous() \
+            or out.device != attn.device:
+        raise ValueError(f"out must be a contiguous float32 [{B},{Hq},{D}] tensor on {attn.device}")
+    if stream is None:
+        stream = torch.cuda.current_stream(attn.device)
+    lib = load()
+    with torch.cuda.device(attn.device):
+        if plan is None:
+            rc = lib.gqa_av_decode_strided(attn.data_ptr(), V.data_ptr(), out.data_ptr(), B, C, C_max, Hq, Hkv, D,
+                                           DTYPES[vmap[V.dtype]], _mode(mode), stream.cuda_stream)
+        else:
+            rc = lib.gqa_av_decode_strided_plan(attn.data_ptr(), V.data_ptr(), out.data_ptr(), B, C, C_max, Hq, Hkv,
+                                                D, DTYPES[vmap[V.dtype]], ctypes.byref(plan), stream.cuda_stream)
     if rc != 0:
         _raise(rc)
     return out

@@ -101,6 +101,7 @@ struct Pass1Args {
     float qk_scale;              // fused attention: the scores are qk_scale * q . K
     const float* k_scale;        // fused attention over fp8 K: [Hkv] scale of each KV head's keys (NULL: 1)
     int64_t C;
+    int64_t v_seq_rows;      // rows of V from one sequence to the next (C, or a larger capacity)
     int64_t rows_per_split;  // contiguous splits: rows of each; interleaved: rows of one block (a pipeline step)
     int32_t interleave;      // 1: split s takes the blocks s, s + nsplit, s + 2 nsplit, ... of the sequence
     int32_t B, Hq, Hkv, D;
@@ -400,7 +401,7 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
     const int nrows = static_cast<int>(uniform64(nrows_split));
     const int vrow32 = static_cast<int>(vrow);
     const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(a.V) + ((static_cast<size_t>(T.b) * a.C + cb) * a.Hkv + T.kv) * a.D * ES, 0,
+        const_cast<uint8_t*>(a.V) + ((static_cast<size_t>(T.b) * a.v_seq_rows + cb) * a.Hkv + T.kv) * a.D * ES, 0,
         nrows > 0 ? (nrows - 1) * vrow32 + a.ht * a.D * ES : 0, kRawBufferFlags);
     const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(a.attn) + (static_cast<size_t>(T.b) * a.C + cb) * a.Hq, 0, nrows * a.Hq * 4,
@@ -642,7 +643,7 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma(Pass1Args a) {
     const int64_t cb = static_cast<int64_t>(T.s) * a.rows_per_split;
     const int64_t ce = min(a.C, cb + a.rows_per_split);
     const size_t vrow = static_cast<size_t>(a.Hkv) * a.D * ES;
-    const uint8_t* vbase = a.V + (static_cast<size_t>(T.b) * a.C * a.Hkv + T.kv) * a.D * ES
+    const uint8_t* vbase = a.V + (static_cast<size_t>(T.b) * a.v_seq_rows * a.Hkv + T.kv) * a.D * ES
                                + static_cast<size_t>(n) * NB;
     // Lane n of set s reads head q_first + 16 s + n. Heads past the tile's nq
     // read the tile's last head instead (a valid address): their A-operand row
@@ -851,7 +852,7 @@ __global__ __launch_bounds__(64 * NW) void av_pass1_mfma_bf16(Pass1Args a) {
     // pipeline's unconditional reload) touches no memory. The plan keeps a
     // split's V span under 2 GB so 32-bit offsets suffice.
     const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(a.V) + (PG ? 0 : ((static_cast<size_t>(T.b) * a.C + cb) * a.Hkv + T.kv) * D * VES), 0,
+        const_cast<uint8_t*>(a.V) + (PG ? 0 : ((static_cast<size_t>(T.b) * a.v_seq_rows + cb) * a.Hkv + T.kv) * D * VES), 0,
         PG || nrows == 0 ? 0 : (nrows - 1) * vrow + HT * D * VES, kRawBufferFlags);
     const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(a.attn) + (static_cast<size_t>(T.b) * a.C + cb) * a.Hq + T.q_first, 0,

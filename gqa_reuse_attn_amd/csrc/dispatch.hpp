@@ -31,9 +31,9 @@ template <int KDT>
 hipError_t qk(int64_t D, int nset, const gqa_av::QkArgs& a, hipStream_t s);
 
 // Plain streaming read of `bytes` from src (the bandwidth ceiling): nblocks
-// workgroups of `slice` contiguous bytes each, loads_in_flight 16-byte loads
-// per lane and batch (4, 8 or 16).
-hipError_t stream_read(const uint8_t* src, int64_t bytes, int64_t slice, int nblocks, int loads_in_flight,
-                       uint32_t* sink, hipStream_t s);
+// workgroups, loads_in_flight 16-byte loads per lane and batch (4, 8 or 16);
+// pattern 0: `slice` contiguous bytes per workgroup; 1: grid-stride batches.
+hipError_t stream_read(int pattern, const uint8_t* src, int64_t bytes, int64_t slice, int nblocks,
+                       int loads_in_flight, uint32_t* sink, hipStream_t s);
 
 }  // namespace gqa_av_launch

@@ -684,7 +684,7 @@ struct AttnArgs {
 int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C, int64_t Hq, int64_t Hkv,
              int64_t D, int v_dtype, const gqa_av_plan* plan, void* stream, int which, int softmax,
              const PagedArgs* pg = nullptr, const float* v_scale = nullptr, const AttnArgs* at = nullptr,
-             bool no_alloc = false) {
+             bool no_alloc = false, int64_t v_seq_rows = -1) {
     if (!plan) return fail(GQA_AV_ERR_INVALID_ARG, "plan is NULL");
     int rc = check_sizes(B, C, Hq, Hkv, D, v_dtype);
     if (rc != GQA_AV_OK) return rc;
@@ -815,6 +815,7 @@ int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C,
     if (pg)
         while ((int64_t{1} << a.page_shift) < pg->page_size) ++a.page_shift;
     a.C = C;
+    a.v_seq_rows = v_seq_rows < 0 ? C : v_seq_rows;
     a.rows_per_split = plan->rows_per_split;
     a.interleave = plan->interleave;
     a.B = static_cast<int32_t>(B);
@@ -941,6 +942,43 @@ int gqa_av_decode_noalloc(const float* attn, const void* V, float* out, int64_t 
     if (rc != GQA_AV_OK) return rc;
     return run_plan(attn, V, out, B, C, Hq, Hkv, D, v_dtype, &plan, stream, kRunPass1 | kRunCombine, 0, nullptr,
                     nullptr, nullptr, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+int check_capacity(int64_t B, int64_t C, int64_t C_max, int64_t Hq, int64_t Hkv, int64_t D, int v_dtype) {
+    int rc = check_sizes(B, C, Hq, Hkv, D, v_dtype);
+    if (rc != GQA_AV_OK) return rc;
+    if (C_max < C) return fail(GQA_AV_ERR_INVALID_ARG, "capacity C_max=%lld is below C=%lld", (long long)C_max,
+                               (long long)C);
+    if (C_max > INT64_MAX / (Hkv * D * elem_bytes(v_dtype)) / (B > 0 ? B : 1))
+        return fail(GQA_AV_ERR_INVALID_ARG, "B * C_max rows of V overflow 64-bit offsets");
+    return GQA_AV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_av_decode_strided_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C, int64_t C_max,
+                               int64_t Hq, int64_t Hkv, int64_t D, int v_dtype, const gqa_av_plan* plan,
+                               void* stream) {
+    int rc = check_capacity(B, C, C_max, Hq, Hkv, D, v_dtype);
+    if (rc != GQA_AV_OK) return rc;
+    return run_plan(attn, V, out, B, C, Hq, Hkv, D, v_dtype, plan, stream, kRunPass1 | kRunCombine, 0, nullptr,
+                    nullptr, nullptr, false, C_max);
+}
+
+int gqa_av_decode_strided(const float* attn, const void* V, float* out, int64_t B, int64_t C, int64_t C_max,
+                          int64_t Hq, int64_t Hkv, int64_t D, int v_dtype, int mode, void* stream) {
+    int rc = check_capacity(B, C, C_max, Hq, Hkv, D, v_dtype);
+    if (rc != GQA_AV_OK) return rc;
+    gqa_av_plan plan;
+    rc = auto_plan(V, B, C, Hq, Hkv, D, v_dtype, mode, 0, &plan);
+    if (rc != GQA_AV_OK) return rc;
+    return gqa_av_decode_strided_plan(attn, V, out, B, C, C_max, Hq, Hkv, D, v_dtype, &plan, stream);
 }
 
 int gqa_softmax_av_decode(const float* scores, const void* V, float* out, int64_t B, int64_t C, int64_t Hq,
@@ -1209,7 +1247,8 @@ const char* gqa_av_status_string(int status) {
 const char* gqa_av_last_error(void) { return g_last_error.c_str(); }
 
 int gqa_bench_stream_read(const void* src, int64_t bytes, int32_t workgroups, int32_t loads_in_flight,
-                          uint32_t* sink, void* stream) {
+                          int32_t pattern, uint32_t* sink, void* stream) {
+    if (pattern != 0 && pattern != 1) return fail(GQA_AV_ERR_INVALID_ARG, "pattern must be 0 or 1");
     if (!src || !sink) return fail(GQA_AV_ERR_INVALID_ARG, "src and sink must not be NULL");
     if ((reinterpret_cast<uintptr_t>(src) & 15u) || (reinterpret_cast<uintptr_t>(sink) & 3u))
         return fail(GQA_AV_ERR_INVALID_ARG, "src must be 16-byte and sink 4-byte aligned");
@@ -1219,8 +1258,9 @@ int gqa_bench_stream_read(const void* src, int64_t bytes, int32_t workgroups, in
         return fail(GQA_AV_ERR_INVALID_ARG, "loads_in_flight must be 4, 8 or 16");
     const int64_t slice = ceil_div(ceil_div(bytes, workgroups), 16) * 16;
     if (slice > INT32_MAX) return fail(GQA_AV_ERR_INVALID_ARG, "a slice of %lld bytes exceeds 2^31", (long long)slice);
-    const hipError_t e = gqa_av_launch::stream_read(static_cast<const uint8_t*>(src), bytes, slice, workgroups,
-                                                    loads_in_flight, sink, static_cast<hipStream_t>(stream));
+    const hipError_t e = gqa_av_launch::stream_read(pattern, static_cast<const uint8_t*>(src), bytes, slice,
+                                                    workgroups, loads_in_flight, sink,
+                                                    static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "stream read launch: %s", hipGetErrorString(e));
     return GQA_AV_OK;
 }

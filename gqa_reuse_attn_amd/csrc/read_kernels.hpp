@@ -1,9 +1,10 @@
 // A plain streaming read: the bandwidth ceiling the AV kernels are compared
 // against on the same device. Nothing of the product is computed here; the
-// kernel reads every byte of a buffer once, the way the AV kernels read V
-// (16-byte non-temporal buffer loads, each workgroup a contiguous slice, two
-// batches of loads in flight), and folds the words into one value so the
-// loads stay live.
+// kernel reads every byte of a buffer once with 16-byte non-temporal buffer
+// loads and folds the words into one value so the loads stay live. Two access
+// patterns: each workgroup a contiguous slice (two batches of loads in
+// flight), or batches dealt to the workgroups in turn (grid stride), which
+// keeps the workgroups on neighbouring addresses.
 #pragma once
 
 #include "av_kernels.hpp"
@@ -49,6 +50,28 @@ __global__ __launch_bounds__(kThreads) void stream_read(const uint8_t* src, int6
     }
     if (i < nb) fold(a);
     // A write that in practice never happens keeps the reads from being dropped.
+    if (x == 0x9e3779b9u) sink[blockIdx.x & 255] = x;
+}
+
+// Grid stride: batch j (kThreads * 16 * U bytes) of the buffer is read by
+// workgroup j % gridDim.x, one batch in flight per workgroup. Each batch has
+// a buffer resource of exactly its bytes.
+template <int U>
+__global__ __launch_bounds__(kThreads) void stream_read_strided(const uint8_t* src, int64_t bytes, uint32_t* sink) {
+    constexpr int kBatch = kThreads * 16 * U;
+    const int64_t nbt = bytes / kBatch;
+    const int lane_off = static_cast<int>(threadIdx.x) * 16;
+    uint32_t x = 0;
+    for (int64_t j = blockIdx.x; j < nbt; j += gridDim.x) {
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(src) + j * kBatch, 0, kBatch, kRawBufferFlags);
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane_off + u * kThreads * 16, 0, kCachePolicyNt);
+#pragma unroll
+        for (int u = 0; u < U; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
     if (x == 0x9e3779b9u) sink[blockIdx.x & 255] = x;
 }
 

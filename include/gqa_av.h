@@ -25,7 +25,8 @@
  *                    otherwise (the page's dispatch bullet, without its cap of
  *                    8 on G: any G is accepted here).
  *
- * Memory layout: dense, row-major, no padding or strides.
+ * Memory layout: dense, row-major, no padding or strides (a V cache with a
+ * per-sequence capacity stride: gqa_av_decode_strided below).
  *   attn  [B][C][Hq]      float32
  *   V     [B][C][Hkv][D]  float32, float16 or bfloat16 (v_dtype)
  *   out   [B][Hq][D]      float32, fully overwritten
@@ -225,6 +226,22 @@ int gqa_av_decode_combine(const float *attn, const void *V, float *out,
 int gqa_av_decode_noalloc(const float *attn, const void *V, float *out,
                           int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D,
                           int v_dtype, int mode, void *stream);
+
+/* The same product over a capacity-strided V cache: V is [B][C_max][Hkv][D]
+ * (each sequence owns C_max rows, C_max >= C, any value) and rows c < C of
+ * every sequence take part; attn [B][C][Hq] and out [B][Hq][D] are dense as
+ * above. This is the dense layout of a decode cache allocated for a maximum
+ * length (ExecuTorch PR #21063, "...GEMV", introduction: each V row is read
+ * once for its group; the page keeps no stride), with all sequences at the
+ * same length C (per-sequence lengths: gqa_paged_av.h). The plan is the
+ * dense one for (B, C, Hq, Hkv, D); C_max changes only where a sequence's
+ * rows start. Errors as gqa_av_decode, plus INVALID_ARG for C_max < C. */
+int gqa_av_decode_strided(const float *attn, const void *V, float *out,
+                          int64_t B, int64_t C, int64_t C_max, int64_t Hq, int64_t Hkv, int64_t D,
+                          int v_dtype, int mode, void *stream);
+int gqa_av_decode_strided_plan(const float *attn, const void *V, float *out,
+                               int64_t B, int64_t C, int64_t C_max, int64_t Hq, int64_t Hkv, int64_t D,
+                               int v_dtype, const gqa_av_plan *plan, void *stream);
 
 /* Static description of a status code. */
 const char *gqa_av_status_string(int status);

@@ -18,7 +18,10 @@
  * The weights -- or, with softmax, the scores -- keep the dense layout
  * w [B][C][Hq] float32, C being the capacity (C <= max_pages * page_size);
  * out [B][Hq][D] float32. A dense cache V[B][C][Hkv][D] with per-sequence
- * lengths is the case page_size = C, block_table[b][0] = b.
+ * lengths is the case page_size = C, block_table[b][0] = b, when C is a power
+ * of two; for any capacity it is pages of one row, block_table[b][c] =
+ * b * C + c (or, with every sequence at the same length,
+ * gqa_av_decode_strided in gqa_av.h).
  *
  * All pointers are DEVICE pointers on the current HIP device, owned by the
  * caller. pages must be 16-byte aligned and (D * element size) a multiple of

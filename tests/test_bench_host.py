@@ -48,11 +48,12 @@ def test_stream_read_rejects_bad_arguments_before_launch():
     import gqa_reuse_attn_amd as ga
     lib = ga.load()
     # NULL source, unaligned sizes, bad load counts: INVALID_ARG, nothing launched
-    assert lib.gqa_bench_stream_read(None, 1024, 8, 4, None, None) == 1
-    assert lib.gqa_bench_stream_read(16, 1000, 8, 4, 16, None) == 1
-    assert lib.gqa_bench_stream_read(16, 1024, 0, 4, 16, None) == 1
-    assert lib.gqa_bench_stream_read(16, 1024, 8, 3, 16, None) == 1
-    assert lib.gqa_bench_stream_read(16, 1 << 40, 1, 4, 16, None) == 1   # slice past 2^31
+    assert lib.gqa_bench_stream_read(None, 1024, 8, 4, 0, None, None) == 1
+    assert lib.gqa_bench_stream_read(16, 1000, 8, 4, 0, 16, None) == 1
+    assert lib.gqa_bench_stream_read(16, 1024, 0, 4, 0, 16, None) == 1
+    assert lib.gqa_bench_stream_read(16, 1024, 8, 3, 0, 16, None) == 1
+    assert lib.gqa_bench_stream_read(16, 1024, 8, 4, 2, 16, None) == 1    # unknown pattern
+    assert lib.gqa_bench_stream_read(16, 1 << 40, 1, 4, 0, 16, None) == 1   # slice past 2^31
     assert b"2^31" in lib.gqa_av_last_error()
 
 

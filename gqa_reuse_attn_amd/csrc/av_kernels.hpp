@@ -343,7 +343,7 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
     constexpr int NACC = GT * E;
     constexpr int CH = NACC < 32 ? NACC : 32;       // accumulator slots per LDS reduction pass
     constexpr int RED = CH * kThreads;
-    __shared__ float smem[RED];
+    __shared__ __align__(16) float smem[RED];
 
     const Tile T = decode_tile(a, GT);
     const int tid = threadIdx.x;
@@ -559,46 +559,81 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
         __syncthreads();
     }
 
-    // Sum the row slots: slot kk of thread tid lives at smem[kk * 256 + tid].
-    // Output slot k = g * E + e of lane chunk jj is tile output k * Lc + jj.
+    // Sum the row slots, CHH heads at a time (CHH * E <= 32 accumulators of a
+    // lane): every active thread stores its E consecutive columns of each head
+    // of the chunk into LDS rows [row slot][KV head of the tile][head][column]
+    // of RL floats (the workgroup's columns of one KV head), 16 bytes at a
+    // time when E allows; then each thread adds a quad of columns (or one
+    // column) of one head over the row slots, in slot order, and writes it
+    // with one store.
+    constexpr int CHH = E >= 32 ? 1 : (32 / E < GT ? 32 / E : GT);   // heads per chunk
+    constexpr int QW = E % 4 == 0 ? 4 : 1;           // columns a reader adds and stores at once
+    const int Lh = Lc / a.ht;                        // lane chunks of one KV head in the workgroup
+    const int RL = Lh * E;                           // columns of one KV head in the workgroup
+    const int jl = j - kvl * a.L;                    // this lane's chunk within its KV head
     float* const plane = a.nsplit > 1 ? a.part + static_cast<size_t>(T.s) * a.B * a.Hq * a.D : a.out;
-    auto out_index = [&](int k, int jj, size_t* o) -> bool {
-        const int g = k / E, e = k - (k / E) * E;
-        const int kl = jj / a.L;
-        const int ld = T.dt * Lc + (jj - kl * a.L);
-        const int ql = lane_q_lo(kl);
-        const int go = T.q_first + kl * a.G - ql;    // accumulator of the tile's first head
-        *o = (static_cast<size_t>(T.b) * a.Hq + ql + g) * a.D + static_cast<size_t>(ld) * E + e;
-        return g >= go && g < go + T.nq && ld < a.L;
-    };
+    const bool vec_store = QW == 4 && (reinterpret_cast<uintptr_t>(plane) & 15u) == 0;
+    typedef __attribute__((address_space(3))) float lds_fl;
+    typedef __attribute__((address_space(3))) f32x4 lds_f4;
+    lds_fl* const red = (lds_fl*)(smem);
 #pragma unroll
-    for (int k0 = 0; k0 < NACC; k0 += CH) {
-        // The last chunk may be short (NACC need not be a multiple of CH).
-        const int nk = NACC - k0 < CH ? NACC - k0 : CH;
+    for (int g0 = 0; g0 < GT; g0 += CHH) {
+        if (active) {
 #pragma unroll
-        for (int kk = 0; kk < CH; ++kk) {
-            const int k = k0 + kk;
-            if (k < NACC) smem[kk * kThreads + tid] = acc[k / E][k % E];
+            for (int gl = 0; gl < CHH; ++gl) {
+                if (g0 + gl >= GT) break;
+                lds_fl* const dst = red + ((r * a.ht + kvl) * CHH + gl) * RL + jl * E;
+                if constexpr (E % 4 == 0) {
+#pragma unroll
+                    for (int e = 0; e < E; e += 4)
+                        *(lds_f4*)(dst + e) = f32x4{acc[g0 + gl][e], acc[g0 + gl][e + 1], acc[g0 + gl][e + 2],
+                                                    acc[g0 + gl][e + 3]};
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) dst[e] = acc[g0 + gl][e];
+                }
+            }
         }
         __syncthreads();
-        const int nout = Lc * nk;
-        for (int idx = tid; idx < nout; idx += kThreads) {
-            const int kk = idx / Lc, jj = idx - (idx / Lc) * Lc;
-            float sum = 0.0f;
-            for (int rr = 0; rr < rps; ++rr) sum += smem[kk * kThreads + rr * Lc + jj];
-            const int k = k0 + kk;
+        const int nh = GT - g0 < CHH ? GT - g0 : CHH;
+        const int units = a.ht * nh * (RL / QW);
+        for (int q = tid; q < units; q += kThreads) {
+            const int kl = q / (nh * (RL / QW));
+            const int gl = (q / (RL / QW)) % nh;
+            const int dl = (q % (RL / QW)) * QW;       // column within the workgroup's columns of the KV head
+            const int d = (a.ht > 1 ? 0 : T.dt * Lc * E) + dl;
+            const int g = g0 + gl;
+            const int ql = lane_q_lo(kl);
+            const int go = T.q_first + kl * a.G - ql;  // accumulator of the tile's first head
+            if (d >= a.D || g < go || g >= go + T.nq) continue;
+            f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int rr = 0; rr < rps; ++rr) {
+                const lds_fl* const src = red + ((rr * a.ht + kl) * CHH + gl) * RL + dl;
+                if constexpr (QW == 4) {
+                    sum += *(const lds_f4*)src;
+                } else {
+                    sum[0] += src[0];
+                }
+            }
             if constexpr (SM) {
                 // One split: normalise here (C = 0 gives zeros); several: the
                 // combine does, from the statistics written below.
-                if (a.nsplit == 1)
-                    sum = nrows_split > 0 ? sum / s_stat[1][(jj / a.L) * GT + k / E] : 0.0f;
+                if (a.nsplit == 1) {
+                    const float l = s_stat[1][kl * GT + g];
+                    sum = nrows_split > 0 ? sum / l : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                }
             }
             if constexpr (DT == kFP8) {
                 // The KV head's scale, once per output (the sums are linear in V).
-                if (a.v_scale) sum *= a.v_scale[(lane_q_lo(jj / a.L) + k / E) / a.G];
+                if (a.v_scale) sum *= a.v_scale[(ql + g) / a.G];
             }
-            size_t o;
-            if (out_index(k, jj, &o)) plane[o] = sum;
+            float* const o = plane + (static_cast<size_t>(T.b) * a.Hq + ql + g) * a.D + d;
+            if (vec_store) {
+                *reinterpret_cast<f32x4*>(o) = sum;
+            } else {
+#pragma unroll
+                for (int c = 0; c < QW; ++c) o[c] = sum[c];
+            }
         }
         __syncthreads();
     }

@@ -388,15 +388,41 @@ def _check_valu_plan(p, B, C, Hq, Hkv, D, dt):
                     n = min(4, GT - k0)
                     assert np.array_equal((wo + 4 * k0 + 4 * n <= wrec)[active], inrow[active])
         if s == 0:
-            for jj in range(Lc):
-                kl = jj // L
-                ld = dtile * Lc + (jj - kl * L)
-                if ld >= L:
-                    continue
-                ql = min(qf + kl * G, Hq - GT)
+            # epilogue: writers put their E columns of CHH heads at a time into
+            # LDS rows [slot][KV head][head][RL columns]; readers add QW columns
+            # of one head over the slots and store them at (b, ql + g, d)
+            CHH = min(32 // E, GT) if E < 32 else 1
+            QW = 4 if E % 4 == 0 else 1
+            Lh = Lc // HT
+            RL = Lh * E
+            assert Lc % HT == 0 and RL % QW == 0
+            jl = j - kvl * L
+            red = min(GT * E, 32) * 256
+            for g0 in range(0, GT, CHH):
+                for gl in range(min(CHH, GT - g0)):
+                    dst = ((r * HT + kvl) * CHH + gl) * RL + jl * E
+                    assert (dst[active] >= 0).all() and (dst[active] + E <= red).all()
+                    if QW == 4:
+                        assert (dst[active] % 4 == 0).all()
+                    # no two active lanes share an LDS word
+                    assert len(set(dst[active].tolist())) == int(active.sum())
+                nh = min(CHH, GT - g0)
+                q = np.arange(HT * nh * (RL // QW))
+                kl, gl = q // (nh * (RL // QW)), (q // (RL // QW)) % nh
+                dl = (q % (RL // QW)) * QW
+                d = (0 if HT > 1 else dtile * Lc * E) + dl
+                g = g0 + gl
+                ql = np.minimum(qf + kl * G, Hq - GT)
                 go = qf + kl * G - ql
-                for g in range(go, go + nq):
-                    cnt[b, ql + g, ld * E:(ld + 1) * E] += 1
+                keep = (d < D) & (g >= go) & (g < go + nq)
+                assert (d[keep] + QW <= D).all()
+                # the last slot's words of the kept units lie in the buffer, and
+                # the lane that wrote them (slot rr, chunk kl * L + dl / E) is active
+                src = (((rps - 1) * HT + kl) * CHH + gl) * RL + dl
+                assert (src[keep] + QW <= red).all()
+                assert (dtile * Lc + dl[keep] // E < L).all()
+                for c in range(QW):
+                    np.add.at(cnt, (b, (ql + g)[keep], d[keep] + c), 1)
         if p.softmax and ns > 1 and dtile == 0:
             # every row slot has an active first lane per KV head of the tile
             lead = active & (j - kvl * L == 0)

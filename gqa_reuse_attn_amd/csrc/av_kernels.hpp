@@ -507,7 +507,7 @@ __global__ __launch_bounds__(kThreads) void av_pass1_valu(Pass1Args a) {
         // page lookups through LDS otherwise let the scheduler move the
         // arithmetic first, which then waits for every load in flight).
         auto fence = [] {
-            if constexpr (PG) __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_sched_barrier(0);
         };
         if (nsteps > 0) load(bA, 0);
         for (; st + 1 < nsteps; st += 2) {
@@ -1272,10 +1272,8 @@ __global__ __launch_bounds__(64 * NW) void av_pass1_mfma_bf16(Pass1Args a) {
     // reads zeros): a conditional load would leave the compiler unsure whether
     // it is outstanding, and it would then wait for every load before
     // consuming bB.
-    // PG: keep each step's loads ahead of the other buffer's work (see av_pass1_valu).
-    auto fence = [] {
-        if constexpr (PG) __builtin_amdgcn_sched_barrier(0);
-    };
+    // Keep each step's loads ahead of the other buffer's work (see av_pass1_valu).
+    auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
     // The pipeline, once per load kind, so that each loop holds one kind of
     // load (with both in one loop the compiler waits for loads it need not).
     auto run = [&](auto uni) {

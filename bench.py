@@ -33,6 +33,7 @@ Other modes (measurement plumbing, no JSON line):
                             the FETCH_SIZE / WRITE_SIZE counters
     --summarize-trace DIR   write a kernel-trace summary from rocprofv3 CSV output
     --summarize-pmc ...     write a traffic summary from four rocprofv3 --pmc runs
+    --summarize-counters DIR  per-kernel medians of any rocprofv3 --pmc counters
 """
 from __future__ import annotations
 
@@ -137,6 +138,7 @@ def parse(argv=None):
     p.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB")
     p.add_argument("--summarize-trace", metavar="DIR")
     p.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
+    p.add_argument("--summarize-counters", metavar="DIR", help="per-kernel medians of any --pmc counters")
     p.add_argument("--copy-bytes", type=float, default=1024.0, help="MiB per copy in the calibration runs")
     p.add_argument("--out", help="summary file to write (with --summarize-*)")
     p.add_argument("--command", default="", help="the command line the summarized data came from")
@@ -201,6 +203,22 @@ def summarize_pmc(dirs, copy_mib: float, out: str, command: str, op: str = "av")
         if re.search(fragment, k):
             extra.append(f"{prefix}_traffic_bytes: {traffic:.0f}")
     lines += [""] + extra
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_counters(d: str, out: str, command: str, op: str = "av"):
+    """Per-kernel medians over dispatches of whatever counters a rocprofv3
+    --pmc run collected (derived ones included), one column per counter."""
+    vals = _counter_medians(d)
+    kernels = sorted({k for k, _ in vals if "gqa_av" in k})
+    counters = sorted({c for _, c in vals})
+    lines = ["# rocprofv3 --pmc counter summary (median over dispatches)", f"command: {command}",
+             f"kernel_sources_sha256: {source_hash(op)}", "",
+             "| kernel | " + " | ".join(counters) + " |", "|---|" + "---|" * len(counters)]
+    for k in kernels:
+        lines.append(f"| {k[:90]} | " + " | ".join(f"{vals.get((k, c), float('nan')):.2f}" for c in counters) + " |")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -863,6 +881,9 @@ def main(argv=None):
         return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc, args.copy_bytes, args.out, args.command, args.op)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.out, args.command, args.op)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this path has no "

@@ -229,9 +229,11 @@ def test_attention_fp8_equals_bf16_on_widened_values():
 
 # ---- paged K and V (two page pools sharing one block table) ---------------------
 
-def _page(K, V, P, seed, spare=3):
+def _page(K, V, P, seed, spare=3, lens=None):
     """K and V [B,C,Hkv,D] cut into pages of P rows, both pools in one shuffled
-    order with spare pages (filled with NaN: never read), and the block table."""
+    order with spare pages (filled with NaN: never read), and the block table.
+    With lens, every row of sequence b at or past lens[b] (the padding past C
+    included) holds NaN in both pools as well."""
     B, C, Hkv, D = K.shape
     maxp = -(-C // P)
     npg = B * maxp + spare
@@ -244,6 +246,10 @@ def _page(K, V, P, seed, spare=3):
         raw.fill_(0x7F if X.element_size() == 1 else 0x7FC0)            # NaN in E4M3 / bf16
         pad = torch.zeros((B, maxp * P, Hkv, D), dtype=X.dtype)
         pad[:, :C] = X
+        if lens is not None:
+            padraw = pad.view(torch.uint8) if X.element_size() == 1 else pad.view(torch.int16)
+            for b in range(B):
+                padraw[b, int(lens[b]):] = 0x7F if X.element_size() == 1 else 0x7FC0
         pool[perm] = pad.reshape(B * maxp, P, Hkv, D)
         pools.append(pool)
     return pools[0], pools[1], perm.to(torch.int32).view(B, maxp).contiguous()
@@ -262,20 +268,21 @@ def _paged_cases():
 @pytest.mark.parametrize("dt,B,C,Hq,Hkv,D,P", _paged_cases())
 def test_attention_paged_sweep(dt, B, C, Hq, Hkv, D, P, oracle_lib):
     """Paged K and V, bf16 and fp8 (per-KV-head scales): G 2..17, D 64..256,
-    pages of 1..256 rows, shuffled pools with NaN spare pages, lengths from 0
-    to the capacity, forced splits; against the paged attention oracle with
-    the dense bound on each sequence's first len rows."""
+    pages of 1..256 rows, shuffled pools with NaN spare pages and NaN in every
+    row at or past a sequence's length, lengths from 0 to the capacity, forced
+    splits; against the paged attention oracle with the dense bound on each
+    sequence's first len rows."""
     q, K, V = _inputs(B, C, Hq, Hkv, D, seed=B * 7 + C + P)
     ks = vs = None
     if dt == "fp8":
         K, ks = _quantize(K)
         V, vs = _quantize(V)
-    kp, vp, bt = _page(K, V, P, seed=C + P)
     g = torch.Generator().manual_seed(C)
     lens = torch.randint(0, C + 1, (B,), generator=g, dtype=torch.int32)
     lens[0] = C
     if B > 2:
         lens[2] = 0
+    kp, vp, bt = _page(K, V, P, seed=C + P, lens=lens)
     scale = D ** -0.5
     ref = oracle_lib.attention_paged(q, kp, vp, bt, lens, dt, scale, ks, vs, C=C)
     plans = [ga.make_plan(B, C, Hq, Hkv, D, dt, nsplit=ns, attention=True, page_size=P) for ns in (0, 1, 3)]

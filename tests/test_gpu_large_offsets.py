@@ -142,15 +142,19 @@ def test_fp8_beyond_4gib(oracle_lib):
     del V8, s, out
 
 
-@pytest.mark.parametrize("fp8", [False, True])
-def test_attention_paged_beyond_4gib(fp8, oracle_lib):
-    """Paged fused attention over K and V pools each larger than 4 GiB (16-row
-    pages shuffled over the whole pool, full and partial lengths), bf16 or fp8
-    with per-KV-head scales. Wrong page addressing gives gross errors, so the
-    sampled sequences are checked with the parity gate against the paged
-    attention oracle (the full error bound would need 2 GB host arrays here)."""
+@pytest.mark.parametrize("fp8,P", [(False, 16), (True, 16), (True, 2)])
+def test_attention_paged_beyond_4gib(fp8, P, oracle_lib):
+    """Paged fused attention over K and V pools each larger than 4 GiB (pages
+    shuffled over the whole pool, full and partial lengths), bf16 or fp8 with
+    per-KV-head scales. fp8 runs with 16-row pages, where a 64-lane load's
+    four rows lie in one page (one page resource per load), and with 2-row
+    pages, where they do not and every lane computes its own 64-bit page
+    address. Wrong page addressing gives gross errors, so the sampled
+    sequences, each holding pages above the 4 GiB mark, are checked with the
+    parity gate against the paged attention oracle (the full error bound would
+    need 2 GB host arrays here)."""
     from tests.parity import gate
-    B, P, Hq = (33 if fp8 else 17), 16, 16
+    B, Hq = (33 if fp8 else 17), 16
     maxp = C // P
     shape = (B * maxp, P, Hkv, D)
     ks = vs = None
@@ -169,7 +173,10 @@ def test_attention_paged_beyond_4gib(fp8, oracle_lib):
     lens[B // 2] = C // 2 + 7
     q = _big((B, Hq, D), torch.float32, 14)
     scale = D ** -0.5
-    _say(f"[4GiB] attention paged fp8={fp8}")
+    page_bytes = P * Hkv * D * kp.element_size()
+    for b in _sample(B):
+        assert ((bt[b].long() + 1) * page_bytes > 2 ** 32).any(), "a sampled sequence has pages past 4 GiB"
+    _say(f"[4GiB] attention paged fp8={fp8} P={P}")
     out = ga.gqa_attention_paged_decode(q, kp, vp, bt.to(DEV), lens.to(DEV), scale=scale, k_scale=ks, v_scale=vs)
     torch.cuda.synchronize()
     for b in _sample(B):
@@ -180,5 +187,5 @@ def test_attention_paged_beyond_4gib(fp8, oracle_lib):
                                          scale, None if ks is None else ks.cpu(), None if vs is None else vs.cpu(),
                                          C=C)
         ok, msg = gate(out[b:b + 1].cpu().numpy().astype(np.float64), ref, "bf16")
-        assert ok, f"4GiB attention paged fp8={fp8} b={b}: {msg}"
+        assert ok, f"4GiB attention paged fp8={fp8} P={P} b={b}: {msg}"
     del kp, vp, out

@@ -63,6 +63,26 @@ def _paged_from_dense(V: torch.Tensor, P: int, seed: int, spare: int = 5):
     return pages, perm
 
 
+def _poison_tails(pages: torch.Tensor, bt: torch.Tensor, lens: torch.Tensor, P: int) -> torch.Tensor:
+    """NaN (0x7F for E4M3 bytes) in every row of a sequence's pages at or past
+    its length, the padding past C included: a kernel that let such a row reach
+    an output would return NaN there."""
+    pages = pages.clone()
+    nan = 0x7F if pages.dtype == torch.uint8 else float("nan")
+    for b in range(bt.shape[0]):
+        c = torch.arange(int(lens[b]), bt.shape[1] * P)
+        pages[bt[b].long()[c // P], c % P] = nan
+    return pages
+
+
+def _poison_rows(w: torch.Tensor, lens: torch.Tensor) -> torch.Tensor:
+    """NaN in the weights (or scores) of every row at or past a sequence's length."""
+    w = w.clone()
+    for b in range(w.shape[0]):
+        w[b, int(lens[b]):] = float("nan")
+    return w
+
+
 def _bound_ok(out, ref, w, V, lens, dt, softmax, label):
     keep = np.isfinite(ref)
     ok, msg = gate(np.where(keep, out, 0.0), np.where(keep, ref, 0.0), dt)
@@ -119,12 +139,15 @@ def _cases():
 @pytest.mark.parametrize("B,C,Hq,Hkv,D,P,dt", _cases())
 def test_paged_sweep(B, C, Hq, Hkv, D, P, dt, oracle_lib):
     """G 1..16, D 64..256, pages of 1..256 rows, all dtypes, ragged lengths
-    (full, partial, 1 and 0), plain and fused, automatic and forced splits."""
+    (full, partial, 1 and 0), plain and fused, automatic and forced splits.
+    Every V row, weight and score at or past a sequence's length holds NaN."""
     s, V = make_scores_random(B, C, Hq, Hkv, D, dt, seed=C + D + P, score_std=2.0)
     pages, bt = _paged_from_dense(V, P, seed=P + B)
     # full, partial, 1 and 0 rows over the cases (a length of 0 under split plans too)
     lens = torch.tensor([C, 0] if B == 2 else [C // 2 + 3, 1, 0], dtype=torch.int32)
-    attn = torch.softmax(s.double(), dim=1).float().contiguous()
+    pages = _poison_tails(pages, bt, lens, P)
+    attn = _poison_rows(torch.softmax(s.double(), dim=1).float(), lens).contiguous()
+    s = _poison_rows(s, lens).contiguous()
     modes = ("auto", "per_head") if Hq // Hkv >= 2 else ("auto",)
     for softmax, w in ((False, attn), (True, s)):
         ref = oracle_lib.paged(w, pages, bt, lens, dt, softmax=softmax)
@@ -147,7 +170,8 @@ def test_paged_sweep(B, C, Hq, Hkv, D, P, dt, oracle_lib):
                                      ("mqa16-b4-c32768-hq16-hkv1-d128-bf16", 32)])
 def test_paged_workloads(wname, P, oracle_lib):
     """Workload shapes (the large batch cut to 8 sequences) as paged caches with
-    lengths between half and all of the capacity, plain and fused."""
+    lengths between half and all of the capacity, plain and fused; rows past
+    each length hold NaN in V, the weights and the scores."""
     w = WORKLOADS[wname]
     if w.B > 8:
         w = w.replace(B=8)
@@ -157,7 +181,9 @@ def test_paged_workloads(wname, P, oracle_lib):
     g = torch.Generator().manual_seed(2)
     lens = torch.randint(w.C // 2, w.C + 1, (w.B,), generator=g, dtype=torch.int32)
     lens[0] = w.C
-    attn = torch.softmax(s.double(), dim=1).float().contiguous()
+    pages = _poison_tails(pages, bt, lens, P)
+    attn = _poison_rows(torch.softmax(s.double(), dim=1).float(), lens).contiguous()
+    s = _poison_rows(s, lens).contiguous()
     for softmax, x in ((False, attn), (True, s)):
         ref = oracle_lib.paged(x, pages, bt, lens, w.v_dtype, softmax=softmax)
         out = _run(x, pages, bt, lens, softmax)

@@ -12,8 +12,9 @@ namespace gqa_av {
 // A workgroup covers kThreads / S quads (4 consecutive outputs) with S split
 // groups each: group g of a quad sums the contiguous split range
 // [nsplit * g / S, nsplit * (g + 1) / S) in increasing s, and the S group sums
-// are then added in increasing g. S (a power of two, 8 to 64) is chosen by
-// the host so that a group holds at most four splits when it can: a thread's
+// are then added in increasing g (S = 1: one thread sums every split of its
+// quad and stores it, no LDS). S (a power of two, 1 to 64) is chosen by the
+// host so that a group holds at most four splits when it can: a thread's
 // loads of a batch of four are issued together (addresses clamped into its
 // range, values masked afterwards), so the kernel costs about one memory
 // round trip.
@@ -49,6 +50,16 @@ __global__ __launch_bounds__(kThreads) void av_pass2_combine(const float* __rest
             for (int c = 0; c < 4; ++c)
                 if (i0 + c < plane) sum[c] += part[static_cast<size_t>(s) * plane + i0 + c];
     }
+    if constexpr (S == 1) {
+        if (quads && i0 + 3 < plane) {
+            *reinterpret_cast<f32x4*>(out + i0) = sum;
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (i0 + c < plane) out[i0 + c] = sum[c];
+        }
+        return;
+    }
     red[g * Q + q] = sum;
     __syncthreads();
     if (g == 0) {
@@ -65,10 +76,14 @@ __global__ __launch_bounds__(kThreads) void av_pass2_combine(const float* __rest
     }
 }
 
-// Split groups of av_pass2_combine for nsplit splits: the smallest power of
-// two from 8 up that leaves each group at most four splits, at most 64.
-inline int combine_groups(int nsplit) {
-    int S = 8;
+// Split groups of av_pass2_combine for nsplit splits over `plane` outputs:
+// the smallest power of two, at most 64, that leaves each group at most four
+// splits, starting from 8 (more threads for small outputs), or from 1 when
+// one thread per quad already makes at least 512 workgroups (the large batch
+// with two splits: 512 workgroups of single threads adding two quads, where
+// eight groups left six of every eight threads idle).
+inline int combine_groups(int nsplit, int64_t plane) {
+    int S = plane >= int64_t{512} * kThreads * 4 ? 1 : 8;
     while (S < 64 && S * 4 < nsplit) S *= 2;
     return S;
 }

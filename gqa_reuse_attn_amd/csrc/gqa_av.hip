@@ -863,13 +863,16 @@ int run_plan(const float* attn, const void* V, float* out, int64_t B, int64_t C,
         if (e != hipSuccess) return fail(GQA_AV_ERR_HIP, "softmax combine launch: %s", hipGetErrorString(e));
     } else if ((which & kRunCombine) && plan->nsplit > 1) {
         const int64_t plane = B * Hq * D;
-        const int groups = gqa_av::combine_groups(a.nsplit);
+        const int groups = gqa_av::combine_groups(a.nsplit, plane);
         const int64_t per_block = 4 * (gqa_av::kThreads / groups);
         const int64_t blocks = ceil_div(plane, per_block);
         if (blocks > INT32_MAX) return fail(GQA_AV_ERR_UNSUPPORTED, "output too large for the split-C combine");
         const dim3 grid(static_cast<uint32_t>(blocks)), block(gqa_av::kThreads);
         const float* const pp = part;
         switch (groups) {
+        case 1: hipLaunchKernelGGL(gqa_av::av_pass2_combine<1>, grid, block, 0, s, pp, out, plane, a.nsplit); break;
+        case 2: hipLaunchKernelGGL(gqa_av::av_pass2_combine<2>, grid, block, 0, s, pp, out, plane, a.nsplit); break;
+        case 4: hipLaunchKernelGGL(gqa_av::av_pass2_combine<4>, grid, block, 0, s, pp, out, plane, a.nsplit); break;
         case 8: hipLaunchKernelGGL(gqa_av::av_pass2_combine<8>, grid, block, 0, s, pp, out, plane, a.nsplit); break;
         case 16: hipLaunchKernelGGL(gqa_av::av_pass2_combine<16>, grid, block, 0, s, pp, out, plane, a.nsplit); break;
         case 32: hipLaunchKernelGGL(gqa_av::av_pass2_combine<32>, grid, block, 0, s, pp, out, plane, a.nsplit); break;

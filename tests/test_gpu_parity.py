@@ -7,6 +7,7 @@ bf16/fp16 V) plus the fp32-accumulation bound.
 """
 from __future__ import annotations
 
+import ctypes
 import sys
 
 import numpy as np
@@ -269,6 +270,34 @@ def test_edge_shapes(B, C, Hq, Hkv, D, dt, oracle_lib):
     for mode in (["auto", "per_head"] if Hq // Hkv >= 2 else ["auto"]):
         out = _run(attn, V, mode)
         assert_parity(out, ref, dt, C, f"{(B, C, Hq, Hkv, D, dt, mode)}")
+
+
+@pytest.mark.parametrize("B,C,Hq,Hkv,D,dt,ns", [
+    (64, 70, 64, 8, 128, "bf16", 2),     # one thread per quad, two splits
+    (64, 1000, 64, 8, 128, "bf16", 7),   # two split groups of at most four
+    (455, 40, 9, 3, 129, "f32", 3),      # an output of 528255 floats: not whole quads
+])
+def test_combine_on_large_outputs(B, C, Hq, Hkv, D, dt, ns, oracle_lib):
+    """Outputs of at least 2^19 floats take the combine with one thread per
+    quad (or a few split groups), scalar when the output is not whole quads;
+    and the same with `out` 4 bytes past a 16-byte boundary (scalar stores)."""
+    attn, V = make_random(B, C, Hq, Hkv, D, dt, seed=B + C + ns, attn_kind="signed")
+    ref = oracle_lib.full(attn, V, dt)
+    assert B * Hq * D >= 2 ** 19
+    plan = ga.make_plan(B, C, Hq, Hkv, D, dt, nsplit=ns)
+    assert plan.nsplit == ns
+    a, v = attn.to(DEV), V.to(DEV)
+    out = ga.gqa_av_decode(a, v, plan=plan)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    assert_parity(got, ref, dt, C, f"{(B, C, Hq, Hkv, D, dt, ns)}")
+    lib = ga.load()
+    buf = torch.full((B * Hq * D + 1,), float("nan"), device=DEV)
+    rc = lib.gqa_av_decode_plan(a.data_ptr(), v.data_ptr(), buf.data_ptr() + 4, B, C, Hq, Hkv, D, ga.DTYPES[dt],
+                                ctypes.byref(plan), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert rc == 0, lib.gqa_av_last_error()
+    assert torch.equal(buf[1:].view(B, Hq, D), out), "misaligned out gives the same bits"
 
 
 def test_misaligned_v_narrows_loads(oracle_lib):

@@ -81,7 +81,7 @@ KERNEL_SOURCES["attn"] = KERNEL_SOURCES["av"]
 # Profile file prefix and the dominant kernel's name fragment, per operation.
 # op: (profile prefix, regular expression for the dominant kernel's name)
 OPS = {"av": ("pass1", "pass1"), "qk": ("qk", "qk_scores"), "softmax": ("softmax_pass1", "pass1"),
-       "attn": ("attn_pass1", r"av_pass1_mfma_bf16<[^>]*, true>")}   # scores from q and K (dense or paged)
+       "attn": ("attn_pass1", r"av_pass1_mfma_bf16<(?:[^,>]+, ){7}true\b")}   # QK: scores from q and K (dense or paged)
 SOFTMAX_METRIC = "GQA decode fused softmax x V: µs/call and achieved HBM GB/s (% of MI355X peak)"
 QK_METRIC = "GQA decode QK scores: µs/call and achieved HBM GB/s (% of MI355X peak)"
 FP8_METRIC = "GQA decode AV with fp8 V: µs/call and achieved HBM GB/s (% of MI355X peak)"

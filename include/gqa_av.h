@@ -78,7 +78,8 @@ typedef enum gqa_av_dtype {
     GQA_AV_F16 = 1,   /* IEEE binary16 */
     GQA_AV_BF16 = 2,  /* bfloat16: the upper 16 bits of a binary32 */
     GQA_AV_FP8_E4M3 = 3  /* OCP FP8 E4M3 (bias 7, no infinities, S.1111.111 = NaN): V only, on the
-                            VALU engine; here with unit scale, per-KV-head scales in gqa_fp8_av.h */
+                            VALU and bf16 matrix engines; here with unit scale, per-KV-head scales
+                            in gqa_fp8_av.h */
 } gqa_av_dtype;
 
 /* How V is shared across the query heads of a group (see above). */
@@ -138,12 +139,13 @@ typedef struct gqa_av_hint {
 /* A launch plan: what gqa_av_decode_plan will run. Produced by gqa_av_make_plan. */
 typedef struct gqa_av_plan {
     int32_t mode;            /* resolved: GQA_AV_PER_HEAD or GQA_AV_REUSE */
-    int32_t engine;          /* resolved gqa_av_engine (VALU or MFMA) */
+    int32_t engine;          /* resolved gqa_av_engine (VALU, MFMA or MFMA_BF16) */
     int32_t heads_per_tile;  /* query heads one workgroup computes (reuse: VALU 1-8 or 16; MFMA engines 16 or 32; per-head: 1) */
     int32_t subgroups;       /* workgroups that share one KV head's rows (ceil(G / heads_per_tile)) */
     int32_t vec_bytes;       /* bytes of V each lane loads per row (VALU: 16, 8, 4, 2; MFMA: D/16 elements; MFMA_BF16: 16) */
     int32_t lanes_per_row;   /* lanes covering one row of the tile (kv_heads_per_tile D-rows) */
-    int32_t row_slots;       /* rows a workgroup loads side by side (MFMA_BF16: four waves x 32) */
+    int32_t row_slots;       /* rows a workgroup loads side by side for one KV head (MFMA_BF16: 32 per
+                                wave streaming that KV head) */
     int32_t d_tiles;         /* workgroups along D */
     int32_t nsplit;          /* context splits (1 = no partial sums) */
     int32_t threads;         /* threads per workgroup (256, or 512 on the bf16 matrix engine) */

@@ -62,3 +62,23 @@ def test_parse_defaults_run_the_suite():
     assert a.workload is None and a.ramp_seconds >= 0.25 and a.gpus == 1
     a = bench.parse(["--gpus", "1", "--steps", "20", "--warmup", "5"])
     assert (a.steps, a.warmup) == (20, 5)
+
+
+def test_dominant_kernel_patterns_pick_the_right_kernel():
+    """The traffic summaries key each operation's dominant kernel by a name
+    pattern; a fused-attention bench also runs the unfused pair (score step,
+    then the fused softmax kernel), so the attention pattern must take only
+    the kernel whose QK template argument (the eighth) is true, whatever
+    follows it."""
+    import re
+    attn = bench.OPS["attn"][1]
+    fused = "void gqa_av::av_pass1_mfma_bf16<16, 1, 1, 4, true, 2, false, true, 4>(gqa_av::Pass1Args)"
+    fused_paged_fp8 = "void gqa_av::av_pass1_mfma_bf16<16, 1, 1, 2, true, 3, true, true, 4>(gqa_av::Pass1Args)"
+    softmax_only = "void gqa_av::av_pass1_mfma_bf16<16, 1, 1, 4, true, 2, false, false, 4>(gqa_av::Pass1Args)"
+    scores = "void gqa_av::qk_scores<2, 4, 1, 4, true>(gqa_av::QkArgs)"
+    assert re.search(attn, fused) and re.search(attn, fused_paged_fp8)
+    assert not re.search(attn, softmax_only) and not re.search(attn, scores)
+    assert re.search(bench.OPS["qk"][1], scores) and not re.search(bench.OPS["qk"][1], fused)
+    for op in ("av", "softmax"):
+        assert re.search(bench.OPS[op][1], softmax_only)
+        assert re.search(bench.OPS[op][1], "void gqa_av::av_pass1_valu<2, 16, 2, 4, false, false>(gqa_av::Pass1Args)")

@@ -46,8 +46,8 @@ constexpr int kMaxSplitPages = 1024;  // paged V: pages one context split may to
 
 // Tuning constants (compile-time; -D overrides build variants for sweeps).
 #ifndef GQA_AV_VALU_UNROLL
-#define GQA_AV_VALU_UNROLL 4      // rows per lane per iteration, groups of up to 4 heads (4 measured
-                                  // best on MI355X: 3-4 % over 8, much better than 16 for D = 96)
+#define GQA_AV_VALU_UNROLL 4      // rows per lane per iteration, groups of up to 4 heads (see valu_unroll;
+                                  // 4 measured best on MI355X for 2 and 4 heads: 6 and 8 cost 0.5-1 us at G = 2)
 #endif
 #ifndef GQA_AV_MFMA_UNROLL
 #define GQA_AV_MFMA_UNROLL 4      // row groups of four per wave and step (16-byte lanes)
@@ -55,12 +55,22 @@ constexpr int kMaxSplitPages = 1024;  // paged V: pages one context split may to
 #ifndef GQA_AV_MFMA_BF16_CHUNKS
 #define GQA_AV_MFMA_BF16_CHUNKS 1 // bf16 matrix engine: 32-row chunks per wave and buffer (two buffers)
 #endif
-constexpr int valu_unroll(int GT) {
-    return GT <= 4 ? GQA_AV_VALU_UNROLL : (GT <= 8 ? (GQA_AV_VALU_UNROLL + 1) / 2 : (GQA_AV_VALU_UNROLL + 3) / 4);
-}
 constexpr int mfma_unroll(int NB) { return NB > 16 ? (GQA_AV_MFMA_UNROLL + 1) / 2 : GQA_AV_MFMA_UNROLL; }
 
 enum : int { kF32 = 0, kF16 = 1, kBF16 = 2, kFP8 = 3 };   // kFP8: OCP FP8 E4M3 (V only)
+
+// Rows per lane and step of the VALU engine for GT heads per tile, element
+// type DT, fused softmax SM, paged V PG (the planner's step and the kernel's
+// template argument both come from here). Tiles of three heads over dense
+// fp16 V take twice the rows: measured on MI355X (B = 8, C = 16384, Hkv = 8,
+// G = 3, D = 96), pass 1 33.7-33.8 us against 34.05-34.08 with four, while
+// the paged, fp8 and fused softmax products of that shape lost 1-1.6 us.
+constexpr int valu_unroll(int GT, int DT, bool SM, bool PG) {
+    return GT == 3 && DT == kF16 && !SM && !PG ? 2 * GQA_AV_VALU_UNROLL
+           : GT <= 4                           ? GQA_AV_VALU_UNROLL
+           : GT <= 8                           ? (GQA_AV_VALU_UNROLL + 1) / 2
+                                               : (GQA_AV_VALU_UNROLL + 3) / 4;
+}
 
 // Fused softmax: a weight is exp2((s - r) * log2(e)) for a running maximum r of
 // the scores. The difference is taken first (exact when s and r are within a
@@ -1273,7 +1283,14 @@ __global__ __launch_bounds__(64 * NW) void av_pass1_mfma_bf16(Pass1Args a) {
     // it is outstanding, and it would then wait for every load before
     // consuming bB.
     // Keep each step's loads ahead of the other buffer's work (see av_pass1_valu).
-    auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+    // Not in dense fused attention: the barrier keeps both buffers' K and V
+    // pieces live across the score MFMAs, which takes its fp8 kernel (and the
+    // bf16 one at D = 64 with 32-head sets) past 256 registers, to one wave per
+    // SIMD where the plan runs two workgroups per CU (fp8 at B = 64, C = 8192,
+    // Hkv = 8, G = 8: 209 us against 178).
+    auto fence = [] {
+        if constexpr (PG || !QK) __builtin_amdgcn_sched_barrier(0);
+    };
     // The pipeline, once per load kind, so that each loop holds one kind of
     // load (with both in one loop the compiler waits for loads it need not).
     auto run = [&](auto uni) {

@@ -505,7 +505,7 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
             nsg = 1;
             heads_major = G;
         }
-        rows_per_step = rps * gqa_av::valu_unroll(GT);
+        rows_per_step = rps * gqa_av::valu_unroll(static_cast<int>(GT), v_dtype, h.softmax == 1, paged);
         tile_outputs = static_cast<int64_t>(GT) * E * Lc;
     }
     const int64_t tiles = B * (Hkv / ht) * heads_major * ndt;

@@ -9,7 +9,7 @@ namespace detail {
 
 template <int DT, int VB, int GT, bool SM, bool PG>
 hipError_t launch_valu(const gqa_av::Pass1Args& a, hipStream_t s) {
-    constexpr int U = gqa_av::valu_unroll(GT);
+    constexpr int U = gqa_av::valu_unroll(GT, DT, SM, PG);
     hipLaunchKernelGGL((gqa_av::av_pass1_valu<DT, VB, GT, U, SM, PG>), dim3(a.nblocks), dim3(gqa_av::kThreads), 0, s,
                        a);
     return hipGetLastError();

@@ -299,7 +299,9 @@ def _check_valu_plan(p, B, C, Hq, Hkv, D, dt):
     E, L = VB // es, D * es // VB
     per_head = p.mode == 0
     GT = 1 if per_head else p.heads_per_tile
-    U = 4 if GT <= 4 else (2 if GT <= 8 else 1)
+    # rows per lane and step (valu_unroll): eight for three-head tiles over dense fp16 V
+    U = 8 if (GT == 3 and dt == "f16" and not p.softmax and not p.page_size) else (
+        4 if GT <= 4 else (2 if GT <= 8 else 1))
     R, vrow, ns = rps * U, Hkv * D * es, p.nsplit
     assert rps * Lc <= 256 and GT <= Hq
     nminor = ndt if per_head else p.subgroups * ndt

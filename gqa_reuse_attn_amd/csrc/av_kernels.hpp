@@ -817,9 +817,9 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma(Pass1Args a) {
 //
 // PR = D / 8 16-byte pieces per row (8, 16 or 32); NSET sets of 16 heads; U
 // chunks of 32 rows per wave and buffer, two buffers in flight; NW waves per
-// workgroup (4 or 8); HT adjacent KV heads per workgroup (1, 2 or 4), each
-// streamed by NW / HT waves, so the workgroup reads HT * 2 D contiguous bytes
-// of every row.
+// workgroup (4 or 8); HT adjacent KV heads per workgroup (1, 2 or 4; 8 for
+// the plain product with eight waves), each streamed by NW / HT waves, so the
+// workgroup reads HT * 2 D contiguous bytes of every row.
 //
 // SM: fused softmax (see av_pass1_valu). A wave keeps one running maximum per
 // head for its rows: the four lane groups holding a head's weights of a chunk
@@ -855,7 +855,8 @@ __global__ __launch_bounds__(64 * NW) void av_pass1_mfma_bf16(Pass1Args a) {
     constexpr bool FP8 = VDT == kFP8;
     constexpr int VES = FP8 ? 1 : 2;                 // bytes of one V element in memory
     constexpr int PB = 8 * VES;                      // bytes of one 8-value piece in memory
-    static_assert((HT == 1 || HT == 2 || HT == 4) && NW % HT == 0, "KV heads per tile must divide the waves");
+    static_assert((HT == 1 || HT == 2 || HT == 4 || (HT == 8 && !SM)) && NW % HT == 0,
+                  "KV heads per tile must divide the waves (eight: the plain product, a wave per KV head)");
     constexpr int D = PR * 8;
     constexpr int RB = PR * 16;                      // bytes of one D-row
     constexpr int NT = D / 16;                       // 16-column output tiles

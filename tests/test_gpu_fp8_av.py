@@ -111,7 +111,7 @@ def _cases():
                 Hkv = (1, 2, 4)[k % 3]
                 cases.append((1 + k % 2, C, G * Hkv, Hkv, D, (1.0, 3.0)[k % 2]))
                 k += 1
-    return cases
+    return cases + [(2, 700, 64, 8, 128, 1.0)]      # eight KV heads
 
 
 @pytest.mark.parametrize("B,C,Hq,Hkv,D,std", _cases())
@@ -132,8 +132,8 @@ def test_fp8_sweep(B, C, Hq, Hkv, D, std, oracle_lib):
                     plans.append(ga.make_plan(B, C, Hq, Hkv, D, "fp8", "reuse", kv_tile=ht, nsplit=3,
                                               softmax=softmax))
             if Hq // Hkv >= 2 and D in (64, 128, 256):        # the bf16 matrix engine at any G
-                for ht in (1, 2):
-                    if Hkv % ht == 0:
+                for ht in (1, 2, 8):                      # eight KV heads: the plain product
+                    if Hkv % ht == 0 and not (ht == 8 and softmax):
                         plans.append(ga.make_plan(B, C, Hq, Hkv, D, "fp8", "reuse", engine="mfma_bf16", kv_tile=ht,
                                                   nsplit=2, softmax=softmax))
             for plan in plans:

@@ -133,7 +133,8 @@ def _cases():
                 C = (300, 1000, 77)[k % 3]
                 cases.append((2 + k % 2, C, G * Hkv, Hkv, D, P, dt))
                 k += 1
-    return cases
+    # eight KV heads (the bf16 engine's eight-head tiles)
+    return cases + [(2, 1000, 64, 8, 128, 16, "bf16"), (3, 300, 16, 8, 64, 1, "bf16")]
 
 
 @pytest.mark.parametrize("B,C,Hq,Hkv,D,P,dt", _cases())
@@ -154,8 +155,8 @@ def test_paged_sweep(B, C, Hq, Hkv, D, P, dt, oracle_lib):
         plans = [ga.make_plan(B, C, Hq, Hkv, D, dt, mode, nsplit=ns, softmax=softmax, page_size=P)
                  for mode in modes for ns in (0, 1, 7)]
         if dt == "bf16" and Hq // Hkv >= 2:          # the bf16 matrix engine at any G
-            for ht, ns in ((1, 0), (2, 5), (4, 1)):
-                if Hkv % ht == 0 and (ns != 1 or C <= 1023 * P):
+            for ht, ns in ((1, 0), (2, 5), (4, 1), (8, 3)):   # eight KV heads: the plain product
+                if Hkv % ht == 0 and (ns != 1 or C <= 1023 * P) and not (ht == 8 and softmax):
                     plans.append(ga.make_plan(B, C, Hq, Hkv, D, dt, "reuse", engine="mfma_bf16", kv_tile=ht,
                                               nsplit=ns, softmax=softmax, page_size=P))
         for plan in plans:

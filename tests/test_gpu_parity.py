@@ -432,13 +432,13 @@ def test_workload_kv_tiles(wname, ht, engine, oracle_lib):
                                          (2, 515, 32, 4, 128), (1, 64, 12, 8, 128)])
 @pytest.mark.parametrize("waves", [4, 8])
 def test_bf16_engine_kv_tiles_small(B, C, G, Hkv, D, waves, oracle_lib):
-    """bf16 matrix engine with 1, 2 and 4 KV heads per workgroup, four or eight
-    waves per workgroup, ragged splits, one and several splits; 32-head sets
-    at G = 32."""
+    """bf16 matrix engine with 1, 2, 4 and (eight waves) 8 KV heads per
+    workgroup, four or eight waves per workgroup, ragged splits, one and
+    several splits; 32-head sets at G = 32."""
     Hq = G * Hkv
     attn, V = make_random(B, C, Hq, Hkv, D, "bf16", seed=C + G, attn_kind="softmax")
     ref = oracle_lib.full(attn, V, "bf16")
-    for ht in (1, 2, 4):
+    for ht in (1, 2, 4) + ((8,) if Hkv == 8 and waves == 8 else ()):
         for ns, comb in ((1, "auto"), (3, "kernel"), (7, "kernel")):
             plan = ga.make_plan(B, C, Hq, Hkv, D, "bf16", "reuse", engine="mfma_bf16", kv_tile=ht, nsplit=ns,
                                 combine=comb, waves=waves)
@@ -450,6 +450,7 @@ def test_bf16_engine_kv_tiles_small(B, C, G, Hkv, D, waves, oracle_lib):
 @pytest.mark.parametrize("wname,ht,ns", [
     ("mqa16-b4-c32768-hq16-hkv1-d128-bf16", 1, 0), ("mqa16-b4-c32768-hq16-hkv1-d128-bf16", 1, 32),
     ("batch64-b64-c8192-hq64-hkv8-d128-bf16", 2, 1), ("batch64-b64-c8192-hq64-hkv8-d128-bf16", 4, 2),
+    ("batch64-b64-c8192-hq64-hkv8-d128-bf16", 8, 2), ("batch64-b64-c8192-hq64-hkv8-d128-bf16", 8, 0),
 ])
 def test_workload_eight_waves(wname, ht, ns, oracle_lib):
     """Full-size workloads on the bf16 matrix engine with eight waves per workgroup."""

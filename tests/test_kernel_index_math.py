@@ -259,17 +259,20 @@ def _check_plan(p, B, C, Hq, Hkv, D, es=2):
 
 @pytest.mark.parametrize("B,C,Hq,Hkv,D", [(1, 300, 16, 1, 128), (2, 1000, 16, 2, 64), (2, 130, 40, 2, 64),
                                          (1, 257, 24, 1, 256), (2, 31, 16, 1, 128), (1, 1, 16, 1, 64),
-                                         (2, 700, 32, 4, 128), (1, 300, 48, 4, 256), (3, 1500, 16, 2, 64)])
+                                         (2, 700, 32, 4, 128), (1, 300, 48, 4, 256), (3, 1500, 16, 2, 64),
+                                         (2, 700, 64, 8, 128), (1, 300, 16, 8, 64)])
 def test_bf16_engine_plan_bounds(B, C, Hq, Hkv, D):
     for ns in (0, 1, 3, 7):
         for comb, sm in (("kernel", False), ("auto", False), ("kernel", True)):
-            for ht in (0, 1, 2, 4):
-                if ht > 1 and Hkv % ht:
+            for ht in (0, 1, 2, 4, 8):
+                if ht > 1 and Hkv % ht or (ht == 8 and sm):   # eight KV heads: the plain product
                     continue
                 for dt, es in (("bf16", 2), ("fp8", 1)):
-                    for P in (0,) + ((16,) if ht in (0, 2) else ()) + ((1, 256) if ns in (0, 3) and ht == 0 else ()):
+                    for P in (0,) + ((16,) if ht in (0, 2, 8) else ()) + ((1, 256) if ns in (0, 3) and ht == 0 else ()):
                         for nw, order in (((0, "auto"), (0, "interleaved")) if sm else
                                           ((0, "auto"), (8, "auto"), (0, "contiguous"), (8, "contiguous"))):
+                            if ht == 8 and nw not in (0, 8):
+                                continue
                             try:
                                 p = ga.make_plan(B, C, Hq, Hkv, D, dt, "reuse", engine="mfma_bf16", nsplit=ns,
                                                  combine=comb, kv_tile=ht, softmax=sm, page_size=P, waves=nw,

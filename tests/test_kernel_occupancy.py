@@ -29,7 +29,7 @@ NEED = {
     "launch_valu_bf16_plain.hip": [(r"av_pass1_valuILi2ELi16ELi[24]ELi4ELb0ELb0E", 2)],
     "launch_valu_f16_plain.hip": [(r"av_pass1_valuILi1ELi16ELi3ELi8ELb0ELb0E", 2)],
     "launch_valu_bf16_sm.hip": [(r"av_pass1_valuILi2ELi16ELi[24]ELi4ELb1ELb0E", 2)],
-    "launch_mfma_bf16_bf16_plain.hip": [(r"av_pass1_mfma_bf16ILi16ELi1ELi1ELi1ELb0ELi2ELb0ELb0ELi8E", 2),
+    "launch_mfma_bf16_bf16_plain.hip": [(r"av_pass1_mfma_bf16ILi16ELi1ELi1ELi[18]ELb0ELi2ELb0ELb0ELi8E", 2),
                                         (r"av_pass1_mfma_bf16ILi16ELi1ELi1ELi4ELb0ELi2ELb0ELb0ELi4E", 1)],
     "launch_mfma_bf16_fp8_attn.hip": [(r"av_pass1_mfma_bf16ILi16ELi1ELi1ELi[124]ELb1ELi3ELb0ELb1ELi4E", 2)],
     "launch_mfma_bf16_fp8_sm.hip": [(r"av_pass1_mfma_bf16ILi16ELi1ELi1ELi[124]ELb1ELi3ELb0ELb0ELi4E", 2)],

@@ -124,12 +124,16 @@ typedef struct gqa_av_hint {
     int32_t cu_count;   /* compute units to plan for; auto = the device's (decode) or 256 (make_plan) */
     int32_t v_align;    /* byte alignment of V's base address; auto = 16 */
     int32_t combine;    /* gqa_av_combine for context splits (AUTO or KERNEL; others are INVALID_ARG) */
-    int32_t kv_tile;    /* adjacent KV heads per VALU workgroup (their D-rows are contiguous) */
+    int32_t kv_tile;    /* adjacent KV heads per workgroup (their D-rows are contiguous), reuse mode on
+                           the VALU engine (a divisor of Hkv, tile rows within 256 lanes) or the bf16
+                           matrix engine (1, 2, 4; 8 for the plain product, on eight waves); a value
+                           that does not divide Hkv is INVALID_ARG, other misfits UNSUPPORTED */
     int32_t softmax;    /* 1: plan the fused softmax product of gqa_softmax_av.h; 0: this header's product */
     int32_t page_size;  /* > 0: plan for a paged V cache of this many rows per page (gqa_paged_av.h) */
     int32_t attention;  /* 1: plan the fused decode attention of gqa_attention.h (implies softmax = 1) */
     int32_t waves;      /* waves (of 64 threads) per workgroup: 4, or 8 for the plain product on the bf16
-                           matrix engine; other values are INVALID_ARG */
+                           matrix engine (eight KV heads per tile take 8: UNSUPPORTED with 4); other
+                           values are INVALID_ARG */
     int32_t split_order;/* how a split context is cut: 0 automatic, 1 contiguous ranges, 2 interleaved
                            blocks (dense V on the VALU or bf16 matrix engine, not fused attention;
                            UNSUPPORTED elsewhere) */

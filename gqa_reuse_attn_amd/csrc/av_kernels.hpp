@@ -855,8 +855,8 @@ __global__ __launch_bounds__(64 * NW) void av_pass1_mfma_bf16(Pass1Args a) {
     constexpr bool FP8 = VDT == kFP8;
     constexpr int VES = FP8 ? 1 : 2;                 // bytes of one V element in memory
     constexpr int PB = 8 * VES;                      // bytes of one 8-value piece in memory
-    static_assert((HT == 1 || HT == 2 || HT == 4 || (HT == 8 && !SM)) && NW % HT == 0,
-                  "KV heads per tile must divide the waves (eight: the plain product, a wave per KV head)");
+    static_assert((HT == 1 || HT == 2 || HT == 4 || (HT == 8 && !QK)) && NW % HT == 0,
+                  "KV heads per tile must divide the waves (eight: not fused attention, a wave per KV head)");
     constexpr int D = PR * 8;
     constexpr int RB = PR * 16;                      // bytes of one D-row
     constexpr int NT = D / 16;                       // 16-column output tiles

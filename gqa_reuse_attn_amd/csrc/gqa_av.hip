@@ -71,8 +71,9 @@ constexpr int64_t kTargetWgPerCuMfma = 1;
 constexpr int64_t kMinRowsPerSplitBf16 = 512;  // bf16 matrix engine: measured best for MQA at B = 4, C = 32768
 constexpr int64_t kTargetWgPerCuBf16 = 1;
 // Eight KV heads per workgroup on the bf16 matrix engine (see the KV-tile
-// choice below) only while every split keeps at least this many rows.
+// choice below) only while every split keeps at least this many rows ...
 constexpr int64_t kMinRowsPerSplitBf16Wide = 1024;
+constexpr int64_t kMaxSplitsBf16Wide = 8;     // ... and the grid fills with at most this many splits
 // The fused softmax product and fused attention over fp8 values do twice the
 // matrix, LDS and exp work per byte read and run better with two workgroups
 // per CU. Measured on MI355X, B = 64, C = 8192, Hkv = 8, G = 8: attention
@@ -393,16 +394,22 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
     // there two heads without a split take 112 us against 117.7 with four
     // heads and two splits, and the VALU engine also takes four heads while a
     // tile row stays within 512 bytes (G = 3, D = 96: 26.6 us against 28.1).
-    // The plain bf16 product at G = 8 and D <= 128 goes one step further, to
-    // eight heads (eight waves, a wave per head), while splits keep 1024 rows:
-    // measured on MI355X (calls, four heads -> eight), B = 64, C = 8192,
-    // Hkv = 8: 177.4 -> 174.8 us; B = 48: 185.0 -> 180.3; B = 32: 93.5 ->
-    // 92.7; Hkv = 16, B = 32: 184.2 -> 177.5; D = 64: 100.1 -> 98.6; B = 64,
-    // C = 4096: 92.3 -> 91.7; B = 128, C = 4096 and B = 16, C = 16384 even.
-    // Other head ratios lose with eight heads (G = 4: 166.3 -> 172.2, G = 5:
+    // bf16 V at G = 8 goes one step further, to eight heads (eight waves, a
+    // wave per head: a workgroup streams whole rows), while the grid fills
+    // with at most 8 splits of at least 1024 rows; D <= 128 for the plain
+    // product, D = 128 for the fused softmax. Measured on MI355X (calls,
+    // four heads -> eight), plain product, B = 64, C = 8192, Hkv = 8:
+    // 177.4 -> 174.8 us; B = 48: 185.0 -> 180.3; B = 32: 93.5 -> 92.7;
+    // Hkv = 16, B = 32: 184.2 -> 177.5; D = 64: 100.1 -> 98.6; B = 64,
+    // C = 4096: 92.3 -> 91.7; B = 128, C = 4096 and B = 16, C = 16384 even;
+    // fused softmax, B = 64: 179.7 -> 177.4; B = 48: 190.8 -> 183.9; B = 32:
+    // 95.0 -> 93.6; Hkv = 16: 186.7 -> 180.7; D = 64: 97.2 -> 100.1. Other
+    // head ratios lose with eight heads (G = 4: 166.3 -> 172.2, G = 5:
     // 166.1 -> 175.4, G = 6: 168.3 -> 180.2, G = 16: 101.7 -> 102.9 and
-    // 56.4 -> 58.5), so do D = 256 (169.0 -> 196.0) and splits of 512 rows
-    // (B = 4, C = 32768: 50.1 -> 50.5).
+    // 56.4 -> 58.5), so do D = 256 (169.0 -> 196.0), fp8 V (the fused
+    // softmax 116.4 -> 124.5) and grids that need 16 or more splits (B = 16,
+    // C = 16384, fused softmax: 95.2 -> 95.8; B = 4, C = 32768: 50.1 -> 50.5,
+    // 52.3 -> 53.1).
     int ht = h.kv_tile > 0 ? h.kv_tile : 1;
     const bool bf16_engine = engine == GQA_AV_ENGINE_MFMA_BF16;
     const int64_t wg_per_cu_bf16 =
@@ -415,10 +422,12 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
         const int64_t target = (bf16_engine ? wg_per_cu_bf16 : kTargetWgPerCuValu) * cus;
         const int64_t min_rows = bf16_engine ? kMinRowsPerSplitBf16 : kMinRowsPerSplit;
         for (int cand : {8, 4, 2}) {
-            const bool eight = bf16_engine && !fp8 && !sm && G == 8 && D <= 128 && (h.waves == 0 || h.waves == 8);
+            const bool eight = bf16_engine && !fp8 && !attention && G == 8 && (sm ? D == 128 : D <= 128) &&
+                               (h.waves == 0 || h.waves == 8);
             const bool four = bf16_engine ? !fp8 : (fp8 && 4 * D * es <= 512);
             if ((cand == 8 && !eight) || (cand == 4 && !four) || Hkv % cand != 0) continue;
             const int64_t tiles_w = B * (Hkv / cand) * nsgw;
+            if (cand == 8 && tiles_w * kMaxSplitsBf16Wide < target) continue;
             const int64_t rows_w = cand == 8 ? kMinRowsPerSplitBf16Wide : min_rows;
             if (lanes > 0 && (bf16_engine || cand * lanes <= gqa_av::kThreads) && v_align % 16 == 0 &&
                 tiles_w > 0 &&
@@ -433,10 +442,11 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
             return fail(GQA_AV_ERR_UNSUPPORTED, "kv_tile > 1 needs the VALU or bf16 matrix engine in reuse mode");
         if (Hkv % ht != 0)
             return fail(GQA_AV_ERR_INVALID_ARG, "kv_tile %d does not divide Hkv=%lld", ht, (long long)Hkv);
-        if (bf16_engine && ht != 2 && ht != 4 && !(ht == 8 && !sm))
+        if (bf16_engine && ht != 2 && ht != 4 && !(ht == 8 && !attention))
             return fail(GQA_AV_ERR_UNSUPPORTED,
-                        "the bf16 matrix engine takes 1, 2 or 4 KV heads per tile (8 for the plain product)");
-        if (sm && ht > 4) return fail(GQA_AV_ERR_UNSUPPORTED, "the fused softmax takes at most 4 KV heads per tile");
+                        "the bf16 matrix engine takes 1, 2, 4 or 8 KV heads per tile (fused attention: up to 4)");
+        if (sm && ht > 4 && !bf16_engine)
+            return fail(GQA_AV_ERR_UNSUPPORTED, "the fused softmax on the VALU engine takes at most 4 KV heads per tile");
     }
 
     // Waves per workgroup: four, or eight for the plain product on the bf16
@@ -446,9 +456,9 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
     // when a workgroup streams one KV head (set below, once the KV heads per
     // tile are known).
     if (h.waves > 0 && h.waves != nw) {
-        if (!bf16_engine || sm)
-            return fail(GQA_AV_ERR_UNSUPPORTED, "%d waves per workgroup: only the plain product on the bf16 matrix "
-                        "engine takes eight", h.waves);
+        if (!bf16_engine || (sm && ht != 8))
+            return fail(GQA_AV_ERR_UNSUPPORTED, "%d waves per workgroup: only the bf16 matrix engine takes eight, "
+                        "for the plain product or eight KV heads per tile", h.waves);
         nw = h.waves;
     }
 
@@ -461,7 +471,7 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
         // Hq = 16, Hkv = 1: pass 1 10.4 -> 9.9 us; with four KV heads per
         // workgroup (B = 64, C = 8192, Hq = 64, Hkv = 8) eight waves were
         // slower (176 -> 190 us).
-        if (h.waves == 0 && (ht == 1 || ht == 8) && !sm) nw = 8;
+        if (h.waves == 0 && ((ht == 1 && !sm) || ht == 8)) nw = 8;
         if (ht == 8 && nw != 8)
             return fail(GQA_AV_ERR_UNSUPPORTED, "eight KV heads per tile take eight waves (a wave per KV head)");
         VB = v_dtype == GQA_AV_FP8_E4M3 ? 8 : 16;    // one 8-value piece per lane load

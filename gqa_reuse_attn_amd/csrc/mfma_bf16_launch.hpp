@@ -14,14 +14,14 @@ hipError_t launch_mfma_bf16(const gqa_av::Pass1Args& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Eight waves per workgroup only for the plain product (the fused softmax and
-// fused attention keep four).
+// Eight waves per workgroup for the plain product, and for the fused softmax
+// with eight KV heads (fused attention keeps four).
 template <int VDT, int PR, int NSET, int HT, bool SM, bool PG, bool QK>
 hipError_t launch_mfma_bf16_nw(int nw, const gqa_av::Pass1Args& a, hipStream_t s) {
     if constexpr (HT <= 4) {
         if (nw == 4) return launch_mfma_bf16<VDT, PR, NSET, HT, SM, PG, QK, 4>(a, s);
     }
-    if constexpr (!SM && !QK) {
+    if constexpr (!QK && (!SM || HT == 8)) {
         if (nw == 8) return launch_mfma_bf16<VDT, PR, NSET, HT, SM, PG, QK, 8>(a, s);
     }
     return hipErrorInvalidValue;
@@ -34,8 +34,8 @@ hipError_t launch_mfma_bf16_ht(int ht, int nw, const gqa_av::Pass1Args& a, hipSt
     case 2: return launch_mfma_bf16_nw<VDT, PR, NSET, 2, SM, PG, QK>(nw, a, s);
     case 4: return launch_mfma_bf16_nw<VDT, PR, NSET, 4, SM, PG, QK>(nw, a, s);
     case 8:
-        // Eight KV heads, a wave each: the plain product only.
-        if constexpr (!SM && !QK) return launch_mfma_bf16_nw<VDT, PR, NSET, 8, SM, PG, QK>(nw, a, s);
+        // Eight KV heads, a wave each: not fused attention.
+        if constexpr (!QK) return launch_mfma_bf16_nw<VDT, PR, NSET, 8, SM, PG, QK>(nw, a, s);
         return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
     }

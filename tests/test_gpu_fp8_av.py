@@ -132,8 +132,8 @@ def test_fp8_sweep(B, C, Hq, Hkv, D, std, oracle_lib):
                     plans.append(ga.make_plan(B, C, Hq, Hkv, D, "fp8", "reuse", kv_tile=ht, nsplit=3,
                                               softmax=softmax))
             if Hq // Hkv >= 2 and D in (64, 128, 256):        # the bf16 matrix engine at any G
-                for ht in (1, 2, 8):                      # eight KV heads: the plain product
-                    if Hkv % ht == 0 and not (ht == 8 and softmax):
+                for ht in (1, 2, 8):
+                    if Hkv % ht == 0:
                         plans.append(ga.make_plan(B, C, Hq, Hkv, D, "fp8", "reuse", engine="mfma_bf16", kv_tile=ht,
                                                   nsplit=2, softmax=softmax))
             for plan in plans:

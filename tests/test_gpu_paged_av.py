@@ -155,8 +155,8 @@ def test_paged_sweep(B, C, Hq, Hkv, D, P, dt, oracle_lib):
         plans = [ga.make_plan(B, C, Hq, Hkv, D, dt, mode, nsplit=ns, softmax=softmax, page_size=P)
                  for mode in modes for ns in (0, 1, 7)]
         if dt == "bf16" and Hq // Hkv >= 2:          # the bf16 matrix engine at any G
-            for ht, ns in ((1, 0), (2, 5), (4, 1), (8, 3)):   # eight KV heads: the plain product
-                if Hkv % ht == 0 and (ns != 1 or C <= 1023 * P) and not (ht == 8 and softmax):
+            for ht, ns in ((1, 0), (2, 5), (4, 1), (8, 3)):
+                if Hkv % ht == 0 and (ns != 1 or C <= 1023 * P):
                     plans.append(ga.make_plan(B, C, Hq, Hkv, D, dt, "reuse", engine="mfma_bf16", kv_tile=ht,
                                               nsplit=ns, softmax=softmax, page_size=P))
         for plan in plans:

@@ -117,13 +117,15 @@ def _cases():
                 std = (1.0, 4.0, 0.25)[k % 3]
                 cases.append((1 + k % 2, C, G * Hkv, Hkv, D, dt, std))
                 k += 1
-    return cases
+    # eight KV heads (the bf16 engine's eight-head tiles)
+    return cases + [(2, 700, 64, 8, 128, "bf16", 1.0), (1, 1000, 64, 8, 64, "bf16", 4.0),
+                    (2, 65, 128, 8, 256, "bf16", 0.25)]
 
 
 @pytest.mark.parametrize("B,C,Hq,Hkv,D,dt,std", _cases())
 def test_softmax_sweep(B, C, Hq, Hkv, D, dt, std, oracle_lib):
     """Small shapes: G 1..32, D 32..256, ragged C, all dtypes, every engine that
-    takes the shape, forced splits (1, 2, 7, auto) and 1/2/4 KV heads per tile."""
+    takes the shape, forced splits (1, 2, 7, auto) and 1/2/4/8 KV heads per tile."""
     s, V = make_scores_random(B, C, Hq, Hkv, D, dt, seed=B * 1000 + C + D, score_std=std)
     ref = oracle_lib.softmax_av(s, V, dt)
     modes = ("auto", "per_head") if Hq // Hkv >= 2 else ("auto",)
@@ -137,7 +139,7 @@ def test_softmax_sweep(B, C, Hq, Hkv, D, dt, std, oracle_lib):
             plans.append(p)
     if Hq // Hkv >= 2:
         for eng in ("valu", "mfma_bf16"):
-            for ht in (1, 2, 4):
+            for ht in (1, 2, 4, 8):
                 if Hkv % ht:
                     continue
                 try:

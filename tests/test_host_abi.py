@@ -96,10 +96,10 @@ def _check_plan(p, B, C, Hq, Hkv, D, v_dtype, mode):
         assert p.mode == 1 and v_dtype == "bf16" and D in (64, 128, 256) and ht in (1, 2, 4, 8) and Hkv % ht == 0
         assert p.vec_bytes == 16 and p.lanes_per_row == ht * D // 8 and p.d_tiles == 1
         assert p.row_slots == 32 * (p.threads // 64) // ht
-        # automatic: eight waves for the plain product with one or eight KV
-        # heads per workgroup (eight: a wave per KV head)
-        assert p.threads == 256 or (ht in (1, 8) and not p.softmax)
-        assert ht != 8 or (p.threads == 512 and not p.softmax)
+        # automatic: eight waves for the plain product with one KV head per
+        # workgroup, and with eight (a wave per KV head)
+        assert p.threads == 256 or (ht == 1 and not p.softmax) or ht == 8
+        assert ht != 8 or (p.threads == 512 and not p.attention)
         assert p.heads_per_tile in (16, 32) and p.heads_per_tile * D <= 4096
         tile_out = ht * p.heads_per_tile * D
     else:
@@ -348,7 +348,8 @@ def test_kv_tile():
     for kw, status in [(dict(kv_tile=3), "INVALID_ARG"),                      # does not divide Hkv
                        (dict(kv_tile=2, mode="per_head"), "UNSUPPORTED"),
                        (dict(kv_tile=2, engine="mfma"), "UNSUPPORTED"),
-                       (dict(kv_tile=8, engine="mfma_bf16", softmax=True), "UNSUPPORTED"),  # plain product only
+                       (dict(kv_tile=8, attention=True), "UNSUPPORTED"),                  # not fused attention
+                       (dict(kv_tile=8, engine="valu", softmax=True), "UNSUPPORTED"),     # VALU softmax: up to 4
                        (dict(kv_tile=8, engine="mfma_bf16", waves=4), "UNSUPPORTED")]:     # a wave per KV head
         with pytest.raises(ga.GqaAvError) as ei:
             ga.make_plan(4, 100, 16, 8, 128, "bf16", **kw)
@@ -360,8 +361,9 @@ def test_kv_tile():
 
 def test_eight_kv_heads_rule():
     """The bf16 matrix engine takes eight KV heads per workgroup on its own
-    only for the plain bf16 product at G = 8, D <= 128, while every split
-    keeps 1024 rows; otherwise four (or fewer)."""
+    only for bf16 V at G = 8 (D <= 128; the fused softmax D = 128) while
+    the grid fills with at most 8 splits of at least 1024 rows; otherwise
+    four (or fewer)."""
     def ht(B, C, Hq, Hkv, D, dt="bf16", **kw):
         p = ga.make_plan(B, C, Hq, Hkv, D, dt, engine="mfma_bf16", cu_count=256, **kw)
         if not kw.get("softmax"):
@@ -371,7 +373,12 @@ def test_eight_kv_heads_rule():
     assert ht(64, 8192, 64, 8, 64) == (8, 512, 4)
     assert ht(32, 8192, 128, 16, 128) == (8, 512, 4)
     assert ht(64, 8192, 64, 8, 128, page_size=16) == (8, 512, 4)
-    assert ht(64, 8192, 64, 8, 128, softmax=True)[0] == 4                  # fused softmax
+    assert ht(64, 8192, 64, 8, 128, softmax=True) == (8, 512, 4)           # fused softmax
+    assert ht(64, 8192, 64, 8, 64, softmax=True)[0] == 4                   # fused softmax, D = 64
+    assert ht(16, 16384, 64, 8, 128)[0] == 4                               # 16 splits needed
+    assert ht(32, 8192, 64, 8, 128) == (8, 512, 8)
+    p = ga.make_plan(64, 8192, 64, 8, 128, "bf16", attention=True, cu_count=256)
+    assert p.kv_heads_per_tile <= 4                                        # fused attention
     assert ht(64, 8192, 64, 8, 128, waves=4)[0] == 4                       # four waves asked for
     assert ht(64, 8192, 64, 8, 256)[0] == 4                                # D = 256
     assert ht(4, 32768, 64, 8, 128)[0] == 4                                # splits would be 512 rows

@@ -118,7 +118,7 @@ def _check_plan(p, B, C, Hq, Hkv, D, es=2):
     """es: bytes of a V element (2: bf16; 1: fp8, loaded as 8-byte pieces of 8 values)."""
     assert p.engine == ENGINE_BF16 and p.vec_bytes == 8 * es
     PR, HT, NW = D // 8, p.kv_heads_per_tile, p.threads // 64
-    assert NW in (4, 8) and NW % HT == 0 and (NW == 4 or not p.softmax)
+    assert NW in (4, 8) and NW % HT == 0 and (NW == 4 or not p.softmax or HT == 8)
     RPI, LPI, WPH = 64 // PR, PR // 2, NW // HT
     NSET = p.heads_per_tile // 16
     RSTEP, vrow, G = 32 * WPH, Hkv * D * es, Hq // Hkv
@@ -265,7 +265,7 @@ def test_bf16_engine_plan_bounds(B, C, Hq, Hkv, D):
     for ns in (0, 1, 3, 7):
         for comb, sm in (("kernel", False), ("auto", False), ("kernel", True)):
             for ht in (0, 1, 2, 4, 8):
-                if ht > 1 and Hkv % ht or (ht == 8 and sm):   # eight KV heads: the plain product
+                if ht > 1 and Hkv % ht:
                     continue
                 for dt, es in (("bf16", 2), ("fp8", 1)):
                     for P in (0,) + ((16,) if ht in (0, 2, 8) else ()) + ((1, 256) if ns in (0, 3) and ht == 0 else ()):

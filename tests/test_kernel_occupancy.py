@@ -1,7 +1,7 @@
 """Register budgets of the kernels the decode workloads run (CPU; needs hipcc).
 
 The planner runs two workgroups per CU for the VALU engine (4 waves each), for
-the bf16 matrix engine's eight-wave plan (one workgroup), and for its fp8
+the bf16 matrix engine's eight-wave plans (one workgroup), and for its fp8
 fused softmax and fused attention (4 waves each): two waves per SIMD. A
 kernel whose registers (VGPRs + AGPRs) pass 256 runs one wave per SIMD and
 halves that parallelism without any error (fp8 fused attention at B = 64,
@@ -29,6 +29,7 @@ NEED = {
     "launch_valu_bf16_plain.hip": [(r"av_pass1_valuILi2ELi16ELi[24]ELi4ELb0ELb0E", 2)],
     "launch_valu_f16_plain.hip": [(r"av_pass1_valuILi1ELi16ELi3ELi8ELb0ELb0E", 2)],
     "launch_valu_bf16_sm.hip": [(r"av_pass1_valuILi2ELi16ELi[24]ELi4ELb1ELb0E", 2)],
+    "launch_mfma_bf16_bf16_sm.hip": [(r"av_pass1_mfma_bf16ILi16ELi1ELi1ELi8ELb1ELi2ELb0ELb0ELi8E", 2)],
     "launch_mfma_bf16_bf16_plain.hip": [(r"av_pass1_mfma_bf16ILi16ELi1ELi1ELi[18]ELb0ELi2ELb0ELb0ELi8E", 2),
                                         (r"av_pass1_mfma_bf16ILi16ELi1ELi1ELi4ELb0ELi2ELb0ELb0ELi4E", 1)],
     "launch_mfma_bf16_fp8_attn.hip": [(r"av_pass1_mfma_bf16ILi16ELi1ELi1ELi[124]ELb1ELi3ELb0ELb1ELi4E", 2)],

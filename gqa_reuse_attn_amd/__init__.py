@@ -238,7 +238,8 @@ def make_plan(B: int, C: int, Hq: int, Hkv: int, D: int, v_dtype: str, mode: Uni
     kv_tile: adjacent KV heads per workgroup; softmax: plan the fused softmax product;
     page_size > 0: plan for a paged V cache with that many rows per page;
     attention: plan the fused decode attention (scores from q and K; bf16);
-    waves: waves per workgroup (4, or 8 for the plain product on the bf16 matrix engine);
+    waves: waves per workgroup (4, or 8 on the bf16 matrix engine for the plain product or
+    eight KV heads per workgroup);
     split_order: "auto" | "contiguous" | "interleaved" (how a split context is cut).
     """
     h = Hint()

@@ -134,7 +134,8 @@ def _cases():
                 cases.append((2 + k % 2, C, G * Hkv, Hkv, D, P, dt))
                 k += 1
     # eight KV heads (the bf16 engine's eight-head tiles)
-    return cases + [(2, 1000, 64, 8, 128, 16, "bf16"), (3, 300, 16, 8, 64, 1, "bf16")]
+    return cases + [(2, 1000, 64, 8, 128, 16, "bf16"), (3, 300, 16, 8, 64, 1, "bf16"),
+                    (2, 500, 128, 16, 128, 16, "bf16")]
 
 
 @pytest.mark.parametrize("B,C,Hq,Hkv,D,P,dt", _cases())

@@ -429,7 +429,7 @@ def test_workload_kv_tiles(wname, ht, engine, oracle_lib):
 
 
 @pytest.mark.parametrize("B,C,G,Hkv,D", [(2, 1000, 8, 4, 128), (1, 777, 16, 8, 64), (3, 301, 5, 4, 256),
-                                         (2, 515, 32, 4, 128), (1, 64, 12, 8, 128)])
+                                         (2, 515, 32, 4, 128), (1, 64, 12, 8, 128), (2, 333, 8, 16, 128)])
 @pytest.mark.parametrize("waves", [4, 8])
 def test_bf16_engine_kv_tiles_small(B, C, G, Hkv, D, waves, oracle_lib):
     """bf16 matrix engine with 1, 2, 4 and (eight waves) 8 KV heads per
@@ -438,7 +438,7 @@ def test_bf16_engine_kv_tiles_small(B, C, G, Hkv, D, waves, oracle_lib):
     Hq = G * Hkv
     attn, V = make_random(B, C, Hq, Hkv, D, "bf16", seed=C + G, attn_kind="softmax")
     ref = oracle_lib.full(attn, V, "bf16")
-    for ht in (1, 2, 4) + ((8,) if Hkv == 8 and waves == 8 else ()):
+    for ht in (1, 2, 4) + ((8,) if Hkv % 8 == 0 and waves == 8 else ()):
         for ns, comb in ((1, "auto"), (3, "kernel"), (7, "kernel")):
             plan = ga.make_plan(B, C, Hq, Hkv, D, "bf16", "reuse", engine="mfma_bf16", kv_tile=ht, nsplit=ns,
                                 combine=comb, waves=waves)

@@ -119,7 +119,7 @@ def _cases():
                 k += 1
     # eight KV heads (the bf16 engine's eight-head tiles)
     return cases + [(2, 700, 64, 8, 128, "bf16", 1.0), (1, 1000, 64, 8, 64, "bf16", 4.0),
-                    (2, 65, 128, 8, 256, "bf16", 0.25)]
+                    (2, 65, 128, 8, 256, "bf16", 0.25), (1, 300, 128, 16, 128, "bf16", 1.0)]
 
 
 @pytest.mark.parametrize("B,C,Hq,Hkv,D,dt,std", _cases())

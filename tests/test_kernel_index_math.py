@@ -260,7 +260,7 @@ def _check_plan(p, B, C, Hq, Hkv, D, es=2):
 @pytest.mark.parametrize("B,C,Hq,Hkv,D", [(1, 300, 16, 1, 128), (2, 1000, 16, 2, 64), (2, 130, 40, 2, 64),
                                          (1, 257, 24, 1, 256), (2, 31, 16, 1, 128), (1, 1, 16, 1, 64),
                                          (2, 700, 32, 4, 128), (1, 300, 48, 4, 256), (3, 1500, 16, 2, 64),
-                                         (2, 700, 64, 8, 128), (1, 300, 16, 8, 64)])
+                                         (2, 700, 64, 8, 128), (1, 300, 16, 8, 64), (1, 200, 128, 16, 128)])
 def test_bf16_engine_plan_bounds(B, C, Hq, Hkv, D):
     for ns in (0, 1, 3, 7):
         for comb, sm in (("kernel", False), ("auto", False), ("kernel", True)):

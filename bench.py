@@ -659,7 +659,8 @@ def bench_fp8(args, w, dev, props):
     q_h, scale_h = _quant_fp8(V_h)
     alg = w.B * w.C * w.Hkv * w.D + w.attn_bytes() + w.out_bytes()
     plan = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, "fp8", args.mode, engine=args.engine, nsplit=args.nsplit,
-                        cu_count=props.multi_processor_count, kv_tile=args.kv_tile, softmax=softmax)
+                        cu_count=props.multi_processor_count, kv_tile=args.kv_tile, softmax=softmax,
+                        waves=args.waves)
     nrot = set_count(alg, args.rotate_mb * 2 ** 20)
     sets = DeviceSets([q_h, x_h], [((w.B, w.Hq, w.D), torch.float32)], nrot, dev)
     sc = scale_h.to(dev)
@@ -671,7 +672,7 @@ def bench_fp8(args, w, dev, props):
     torch.cuda.synchronize()
     log(f"fp8 {'softmax ' if softmax else ''}{t['median_us']:.2f} us/call, pass 1 {p1['median_us']:.2f} us; "
         f"{nrot} sets, plan {_plan_dict(plan)}")
-    default_plan = args.nsplit == 0 and args.engine == "auto" and args.kv_tile == 0
+    default_plan = args.nsplit == 0 and args.engine == "auto" and args.kv_tile == 0 and args.waves == 0
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -716,7 +717,8 @@ def bench_paged(args, w, dev, props):
     pages_h, bt_h, lens_h = _shuffled_pages(w, P, V_h)
     bt, lens = bt_h.to(dev), lens_h.to(dev)
     plan = ga.make_plan(w.B, w.C, w.Hq, w.Hkv, w.D, w.v_dtype, args.mode, engine=args.engine, nsplit=args.nsplit,
-                        cu_count=props.multi_processor_count, kv_tile=args.kv_tile, softmax=softmax, page_size=P)
+                        cu_count=props.multi_processor_count, kv_tile=args.kv_tile, softmax=softmax, page_size=P,
+                        waves=args.waves)
     alg = w.algorithmic_bytes()
     nrot = set_count(alg, args.rotate_mb * 2 ** 20)
     sets = DeviceSets([pages_h, x_h], [((w.B, w.Hq, w.D), torch.float32)], nrot, dev)
@@ -728,7 +730,7 @@ def bench_paged(args, w, dev, props):
     torch.cuda.synchronize()
     log(f"paged P={P} {'softmax ' if softmax else ''}{t['median_us']:.2f} us/call, pass 1 {p1['median_us']:.2f} us; "
         f"{nrot} sets, plan {_plan_dict(plan)}")
-    default_plan = args.nsplit == 0 and args.engine == "auto" and args.kv_tile == 0
+    default_plan = args.nsplit == 0 and args.engine == "auto" and args.kv_tile == 0 and args.waves == 0
     cpu = None
     if not args.no_cpu_baseline:
         import oracle

@@ -1103,7 +1103,6 @@ __global__ __launch_bounds__(64 * NW) void av_pass1_mfma_bf16(Pass1Args a) {
     // 256 bytes) and takes one instruction per two values.
     auto to_bf16 = [](const Piece& pc) -> u32x4 {
         if constexpr (FP8) {
-            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
             u32x4 piece;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {

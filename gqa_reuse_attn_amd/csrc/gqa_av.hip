@@ -463,7 +463,7 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
     }
 
     int VB, GT, nsg;
-    int64_t Lc, rps, ndt, rows_per_step, tile_outputs;
+    int64_t Lc, rps, ndt, rows_per_step;
     int64_t heads_major;  // tiles along the head axis per KV head
     if (engine == GQA_AV_ENGINE_MFMA_BF16) {
         // Eight waves when one KV head per workgroup: more rows in flight per
@@ -482,7 +482,6 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
         rps = 32 * nw / ht;             // one 32-row chunk per wave, nw / ht waves per KV head
         ndt = 1;
         rows_per_step = rps * GQA_AV_MFMA_BF16_CHUNKS;
-        tile_outputs = static_cast<int64_t>(ht) * GT * D;
     } else if (engine == GQA_AV_ENGINE_MFMA) {
         const int64_t DE = D / 16;
         VB = static_cast<int>(DE * es);
@@ -493,7 +492,6 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
         rps = 16;                       // 4 waves x 4 rows per MFMA
         ndt = 1;
         rows_per_step = 4 * gqa_av::kWaves * gqa_av::mfma_unroll(VB);
-        tile_outputs = static_cast<int64_t>(GT) * D;
     } else {
         // Widest lane load that divides a D-row and respects V's alignment
         // (fp8: 16 values per lane only for tiles of up to 4 heads, else 8, so
@@ -534,7 +532,6 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
             heads_major = G;
         }
         rows_per_step = rps * gqa_av::valu_unroll(static_cast<int>(GT), v_dtype, h.softmax == 1, paged);
-        tile_outputs = static_cast<int64_t>(GT) * E * Lc;
     }
     const int64_t tiles = B * (Hkv / ht) * heads_major * ndt;
 

@@ -83,7 +83,6 @@ struct QkArgs {
 __device__ inline void fp8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
     // gfx950's packed conversion, scale 1: exact (bf16 holds every E4M3 value;
     // checked on MI355X against the fp32 conversion for all 256 bytes).
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w), 1.0f, false));
     hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w), 1.0f, true));
 }

@@ -83,19 +83,21 @@ def _fresh(x, seed):
 
 
 @pytest.mark.parametrize("softmax", [False, True])
-@pytest.mark.parametrize("shape,engine,combine", [
-    ((2, 3000, 16, 8, 128, "bf16"), "auto", "auto"),     # VALU, split kernel combine
-    ((2, 3000, 64, 8, 128, "bf16"), "auto", "auto"),     # bf16 matrix engine
-    ((2, 3000, 32, 4, 64, "f32"), "mfma", "auto"),       # fp32 matrix engine (plain only)
-    ((2, 3000, 24, 8, 96, "f16"), "valu", "kernel"),     # f16 VALU, G = 3, split kernel combine
-    ((1, 100, 8, 2, 64, "bf16"), "auto", "auto"),        # one split: a single launch
+@pytest.mark.parametrize("shape,engine,combine,kv_tile", [
+    ((2, 3000, 16, 8, 128, "bf16"), "auto", "auto", 0),     # VALU, split kernel combine
+    ((2, 3000, 64, 8, 128, "bf16"), "auto", "auto", 0),     # bf16 matrix engine
+    ((2, 3000, 64, 8, 128, "bf16"), "mfma_bf16", "auto", 8),  # bf16 matrix engine, eight KV heads, eight waves
+    ((2, 3000, 32, 4, 64, "f32"), "mfma", "auto", 0),       # fp32 matrix engine (plain only)
+    ((2, 3000, 24, 8, 96, "f16"), "valu", "kernel", 0),     # f16 VALU, G = 3, split kernel combine
+    ((1, 100, 8, 2, 64, "bf16"), "auto", "auto", 0),        # one split: a single launch
 ])
-def test_graph_dense(shape, engine, combine, softmax):
+def test_graph_dense(shape, engine, combine, kv_tile, softmax):
     if softmax and engine == "mfma":
         pytest.skip("the fused softmax runs on the VALU or bf16 matrix engine")
     B, C, Hq, Hkv, D, dt = shape
     x, V = _weights(B, C, Hq, Hkv, D, dt, seed=C + Hq, softmax=softmax)
-    plan = ga.make_plan(B, C, Hq, Hkv, D, dt, engine=engine, combine=combine, softmax=softmax)
+    plan = ga.make_plan(B, C, Hq, Hkv, D, dt, engine=engine, combine=combine, softmax=softmax, kv_tile=kv_tile)
+    assert plan.kv_heads_per_tile == kv_tile or kv_tile == 0
     bind = ga.bind_softmax if softmax else ga.bind
     _graph_matches_eager(f"dense {shape} {plan.as_dict()}", lambda s: bind(x, V, plan=plan, stream=s), x,
                          _fresh(x, 1))

@@ -817,8 +817,8 @@ __global__ __launch_bounds__(kThreads) void av_pass1_mfma(Pass1Args a) {
 //
 // PR = D / 8 16-byte pieces per row (8, 16 or 32); NSET sets of 16 heads; U
 // chunks of 32 rows per wave and buffer, two buffers in flight; NW waves per
-// workgroup (4 or 8); HT adjacent KV heads per workgroup (1, 2 or 4; 8 for
-// the plain product with eight waves), each streamed by NW / HT waves, so the
+// workgroup (4 or 8); HT adjacent KV heads per workgroup (1, 2 or 4; 8 with
+// eight waves, not in fused attention), each streamed by NW / HT waves, so the
 // workgroup reads HT * 2 D contiguous bytes of every row.
 //
 // SM: fused softmax (see av_pass1_valu). A wave keeps one running maximum per

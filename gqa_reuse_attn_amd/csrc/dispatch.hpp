@@ -21,8 +21,8 @@ hipError_t mfma(int DT, int DE, int nset, const gqa_av::Pass1Args& a, hipStream_
 
 // bf16 matrix engine, V of element type VDT (gqa_av::kBF16 or kFP8), paged V
 // when PG, fused attention (scores from q and K) when QK: D of 64, 128 or
-// 256, nset sets of 16 heads, ht KV heads per tile, nw waves per workgroup
-// (4, or 8 for the plain product).
+// 256, nset sets of 16 heads, ht KV heads per tile (1, 2, 4 or 8), nw waves
+// per workgroup (4, or 8 for the plain product or eight KV heads per tile).
 template <int VDT, bool SM, bool PG = false, bool QK = false>
 hipError_t mfma_bf16(int64_t D, int nset, int ht, int nw, const gqa_av::Pass1Args& a, hipStream_t s);
 

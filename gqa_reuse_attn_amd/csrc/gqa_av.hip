@@ -449,12 +449,13 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
             return fail(GQA_AV_ERR_UNSUPPORTED, "the fused softmax on the VALU engine takes at most 4 KV heads per tile");
     }
 
-    // Waves per workgroup: four, or eight for the plain product on the bf16
-    // matrix engine (more rows in flight per workgroup without more splits).
+    // Waves per workgroup: four, or eight on the bf16 matrix engine for the
+    // plain product or eight KV heads per tile (more rows in flight per
+    // workgroup without more splits).
     int nw = gqa_av::kWaves;
-    // Automatic: eight waves for the plain product on the bf16 matrix engine
-    // when a workgroup streams one KV head (set below, once the KV heads per
-    // tile are known).
+    // Automatic: eight waves on the bf16 matrix engine when a workgroup
+    // streams one KV head of the plain product, or eight KV heads (set below,
+    // once the KV heads per tile are known).
     if (h.waves > 0 && h.waves != nw) {
         if (!bf16_engine || (sm && ht != 8))
             return fail(GQA_AV_ERR_UNSUPPORTED, "%d waves per workgroup: only the bf16 matrix engine takes eight, "
@@ -466,11 +467,12 @@ int plan_impl(int64_t B, int64_t C, int64_t Hq, int64_t Hkv, int64_t D, int v_dt
     int64_t Lc, rps, ndt, rows_per_step;
     int64_t heads_major;  // tiles along the head axis per KV head
     if (engine == GQA_AV_ENGINE_MFMA_BF16) {
-        // Eight waves when one KV head per workgroup: more rows in flight per
-        // CU without more splits. Measured on MI355X, B = 4, C = 32768,
-        // Hq = 16, Hkv = 1: pass 1 10.4 -> 9.9 us; with four KV heads per
-        // workgroup (B = 64, C = 8192, Hq = 64, Hkv = 8) eight waves were
-        // slower (176 -> 190 us).
+        // Eight waves when one KV head per workgroup (plain product): more
+        // rows in flight per CU without more splits. Measured on MI355X,
+        // B = 4, C = 32768, Hq = 16, Hkv = 1: pass 1 10.4 -> 9.9 us; with four
+        // KV heads per workgroup (B = 64, C = 8192, Hq = 64, Hkv = 8) eight
+        // waves were slower (176 -> 190 us). Eight KV heads take eight waves,
+        // one per head.
         if (h.waves == 0 && ((ht == 1 && !sm) || ht == 8)) nw = 8;
         if (ht == 8 && nw != 8)
             return fail(GQA_AV_ERR_UNSUPPORTED, "eight KV heads per tile take eight waves (a wave per KV head)");
